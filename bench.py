@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Benchmark of the multi-head LSTM forward hot path on one MI355X.
+
+A step is one whole forward pass of the workload: the input projection
+(rnn_input_proj, bf16 MFMA contraction over all T*B rows) followed by the
+sequential recurrence (rnn_rec_lstm, persistent kernel with R resident) --
+exactly the two launches rnn_fwd_lstm makes -- on synthetic inputs already
+resident in HBM.  Both launches go to torch's current stream, where HIP
+events bracket each of them, so the recurrence kernel's own average launch
+time is measured over the timed region.
+
+Prints ONE JSON line (see the keys below).  `value` is recurrent TFLOP/s:
+the algorithmic flops of the recurrent products (2*B*H*G*Dh per step, the
+block-diagonal R only) divided by the wall time of the whole step.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+METRIC = "recurrent TFLOP/s and time-steps/s, multi-head LSTM fwd B=16 NH=6 Dh=128"
+HEADLINE = "lstm_mh_b16_nh6_dh128"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
+NUM_CU = 256
+CU_BF16_TFLOPS = PEAK_BF16_TFLOPS / NUM_CU
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "gru_recurrence_amd", "csrc", f)
+                  for f in ("rec_fwd.hip", "common.h", "kernels.h")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recurrent_flops(w: synth.Workload, T=None) -> float:
+    d = w.dims
+    G = synth.gates_of(w.cell)
+    return 2.0 * d.B * d.NH * d.Dh * G * d.Dh * (T if T is not None else d.T)
+
+
+def traffic_per_launch():
+    """HBM bytes per recurrence launch from committed rocprofv3 counter runs,
+    or None when absent or taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w: synth.Workload, c, budget_s: float):
+    """Time the oracle (double-precision scalar C, OpenMP over independent
+    chains) on a T-prefix of the same workload, all chains, and express it in
+    the metric's unit (recurrent TFLOP/s of the whole forward)."""
+    import oracle
+    d = w.dims
+    # one short probe to size the sample to ~budget_s of CPU work
+    Tp = 8
+    x = c.f64("x")
+    args = (c.f64("W"), c.f64("R"), c.f64("b"), c.f64("h0"), c.f64("c0"))
+    t0 = time.perf_counter()
+    oracle.lstm_fwd(x[:Tp], *args, NH=d.NH, Dh=d.Dh)
+    probe = time.perf_counter() - t0
+    Ts = int(min(d.T, max(Tp, Tp * budget_s / max(probe, 1e-6))))
+    reps, el = 0, 0.0
+    while reps == 0 or (el < 0.5 * budget_s and reps < 20):
+        t0 = time.perf_counter()
+        oracle.lstm_fwd(x[:Ts], *args, NH=d.NH, Dh=d.Dh)
+        el += time.perf_counter() - t0
+        reps += 1
+    per = el / reps
+    flops = recurrent_flops(w, Ts)
+    return {"value": flops / per / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "whole forward (input projection + recurrence) of the first %d of %d "
+                      "steps, all %d chains, float64; mean of %d runs, %.3f s each"
+                      % (Ts, d.T, d.B * d.NH, reps, per),
+            "time_steps_per_s": Ts / per}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only; the recurrence shards by heads or "
+              "batch rows with no exchange, but no multi-GPU path is built "
+              "(requested --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gru_recurrence_amd as g
+
+    w = synth.WORKLOADS[args.workload]
+    if w.cell != "lstm" or w.backward:
+        print("bench.py times the LSTM forward workloads only", file=sys.stderr)
+        sys.exit(2)
+    d = w.dims
+    c = synth.workload_case(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(name):
+        if name in c.bits:
+            return torch.from_numpy(c.bits[name].view(np.int16).copy()).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(c.vals[name])).to(dev)
+
+    x, W, R, b = to_dev("x"), to_dev("W"), to_dev("R"), to_dev("b")
+    h0, c0 = to_dev("h0"), to_dev("c0")
+    H, N = d.NH * d.Dh, d.NH * 4 * d.Dh
+    f32 = torch.float32
+    gx = torch.empty((d.T, d.B, N), dtype=f32, device=dev)
+    outs = dict(h_seq=torch.empty((d.T, d.B, H), dtype=f32, device=dev),
+                c_seq=torch.empty((d.T, d.B, H), dtype=f32, device=dev),
+                hT=torch.empty((d.B, H), dtype=f32, device=dev),
+                cT=torch.empty((d.B, H), dtype=f32, device=dev))
+    dims = g.dims_of(x, R)
+    dtc = g.RNN_BF16 if w.dtype == "bf16" else g.RNN_F32
+    ws = torch.empty(g.workspace_size(g.OP_REC_LSTM, dims, dtc), dtype=torch.uint8, device=dev)
+    plan = g.plan_describe(g.OP_REC_LSTM, dims, dtc)
+    stream = torch.cuda.current_stream()
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        g.input_proj(x, W, b, out=gx, stream=stream)
+        if evs is not None:
+            evs[1].record(stream)
+        g.rec_lstm(gx, R, h0, c0, ws=ws, out=outs, stream=stream)
+        if evs is not None:
+            evs[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    proj_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    rec_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    st = g.workspace_status(ws, stream)
+    if st != g.RNN_OK:
+        print("bench.py: kernel reported %s" % g.status_str(st), file=sys.stderr)
+        sys.exit(1)
+
+    ms_step = 1e3 * wall / args.steps
+    rflops = recurrent_flops(w)
+    value = rflops / (ms_step * 1e-3) / 1e12
+    rec_avg = float(np.mean(rec_ms))
+    proj_avg = float(np.mean(proj_ms))
+    achieved = rflops / (rec_avg * 1e-3) / 1e12
+    G = 4
+    gemm_flops = 2.0 * d.T * d.B * d.Din * N
+    ncu_engaged = int(plan.split(" wg=")[1].split()[0])
+    out = {
+        "metric": METRIC if args.workload == HEADLINE else METRIC.split(",")[0] + ", " + w.name,
+        "value": round(value, 4),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded SplitMix64/Box-Muller, bf16 RNE), random-init weights",
+        "config": {"workload": w.name, "cell": w.cell, "T": d.T, "B": d.B, "NH": d.NH,
+                   "Dh": d.Dh, "Din": d.Din, "hidden": H, "parallelism": "single GPU"},
+        "time_steps_per_s": round(d.T / (ms_step * 1e-3), 1),
+        "recurrence": {"avg_launch_ms": round(rec_avg, 4), "tflops": round(achieved, 3),
+                       "ns_per_time_step": round(rec_avg * 1e6 / d.T, 1),
+                       "time_steps_per_s": round(d.T / (rec_avg * 1e-3), 1),
+                       "engaged_cus": ncu_engaged,
+                       "engaged_cu_peak_tflops": round(ncu_engaged * CU_BF16_TFLOPS, 1),
+                       "frac_of_engaged_cu_peak": round(achieved / (ncu_engaged * CU_BF16_TFLOPS), 4),
+                       "plan": plan},
+        "input_projection": {"avg_launch_ms": round(proj_avg, 4),
+                             "tflops": round(gemm_flops / (proj_avg * 1e-3) / 1e12, 2),
+                             "frac_of_peak": round(gemm_flops / (proj_avg * 1e-3) / 1e12
+                                                   / PEAK_BF16_TFLOPS, 4)},
+        "roofline": {"kernel": "rec_fwd_mfma_kernel (recurrence)", "bound": "mfma",
+                     "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 5),
+                     "traffic": traffic_per_launch()},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(w, c, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

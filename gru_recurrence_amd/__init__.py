@@ -1,0 +1,316 @@
+"""gru_recurrence_amd -- Python binding of librnn355 (multi-head LSTM / GRU
+recurrence with block-diagonal R on MI355X).
+
+Argument marshalling only: every step runs in the HIP kernels of
+``librnn355.so`` behind the C ABI declared in ``include/rnn355.h``.  torch
+supplies device memory (inputs, outputs, workspace) and the current stream.
+There is no fallback: if the library is missing, ``load()`` raises.
+
+Shapes (H = NH*Dh, G = 4 for the LSTM, 3 for the GRU, N = NH*G*Dh):
+  x [T,B,Din], W [Din,N], R [NH,Dh,G*Dh] in torch.bfloat16 or torch.float32,
+  b [N] float32, h0/c0 [B,H] float32; outputs float32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librnn355.so")
+
+RNN_OK, RNN_ERR_INVALID_ARG, RNN_ERR_UNSUPPORTED, RNN_ERR_WORKSPACE, RNN_ERR_HIP, \
+    RNN_ERR_BARRIER_TIMEOUT = range(6)
+RNN_F32, RNN_BF16 = 0, 1
+OP_FWD_LSTM, OP_FWD_GRU, OP_BWD_LSTM, OP_BWD_GRU, OP_REC_LSTM, OP_REC_GRU = range(6)
+
+EXPORTS = ("rnn_status_str", "rnn_workspace_size", "rnn_plan_describe", "rnn_input_proj",
+           "rnn_rec_lstm", "rnn_rec_gru", "rnn_fwd_lstm", "rnn_fwd_gru", "rnn_bwd_lstm",
+           "rnn_workspace_status")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int), ("B", ctypes.c_int), ("Din", ctypes.c_int),
+                ("NH", ctypes.c_int), ("Dh", ctypes.c_int)]
+
+
+class RnnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s: %s" % (what, status_str(status)))
+
+
+_lib = None
+
+
+def load(path: Optional[str] = None):
+    """Load librnn355.so (built in-tree by gru_recurrence_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError("librnn355.so not built at %s: run "
+                          "`python -m gru_recurrence_amd.build`" % p)
+    lib = ctypes.CDLL(p)
+    P, I, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    D = ctypes.POINTER(Dims)
+    lib.rnn_status_str.restype = ctypes.c_char_p
+    lib.rnn_status_str.argtypes = [I]
+    lib.rnn_workspace_size.restype = S
+    lib.rnn_workspace_size.argtypes = [I, D, I]
+    lib.rnn_plan_describe.argtypes = [I, D, I, ctypes.c_char_p, S]
+    lib.rnn_input_proj.argtypes = [I, I, I, I, P, P, P, P, P]
+    lib.rnn_rec_lstm.argtypes = [D, I, P, P, P, P, P, P, P, P, P, S, P]
+    lib.rnn_rec_gru.argtypes = [D, I, P, P, P, P, P, P, S, P]
+    lib.rnn_fwd_lstm.argtypes = [D, I, P, P, P, P, P, P, P, P, P, P, P, S, P]
+    lib.rnn_fwd_gru.argtypes = [D, I, P, P, P, P, P, P, P, P, S, P]
+    lib.rnn_bwd_lstm.argtypes = [D, I] + [P] * 17 + [P, S, P]
+    lib.rnn_workspace_status.argtypes = [P, S, P]
+    for f in ("rnn_plan_describe", "rnn_input_proj", "rnn_rec_lstm", "rnn_rec_gru",
+              "rnn_fwd_lstm", "rnn_fwd_gru", "rnn_bwd_lstm", "rnn_workspace_status"):
+        getattr(lib, f).restype = I
+    _lib = lib
+    return lib
+
+
+def status_str(s: int) -> str:
+    return load().rnn_status_str(int(s)).decode()
+
+
+def _check(s: int, what: str):
+    if s != RNN_OK:
+        raise RnnError(s, what)
+
+
+# ----------------------------------------------------------- marshalling
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return RNN_BF16
+    if t.dtype == torch.float32:
+        return RNN_F32
+    raise TypeError("x/W/R must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _ptr(t, name, dtype=None, shape=None, optional=False):
+    if t is None:
+        if optional:
+            return None
+        raise ValueError("%s is required" % name)
+    torch = _torch()
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    del torch
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def dims_of(x, R) -> Dims:
+    T, B, Din = x.shape
+    NH, Dh = R.shape[0], R.shape[1]
+    return Dims(T, B, Din, NH, Dh)
+
+
+def workspace_size(op: int, dims: Dims, dtype_code: int) -> int:
+    return int(load().rnn_workspace_size(op, ctypes.byref(dims), dtype_code))
+
+
+def plan_describe(op: int, dims: Dims, dtype_code: int) -> str:
+    buf = ctypes.create_string_buffer(256)
+    s = load().rnn_plan_describe(op, ctypes.byref(dims), dtype_code, buf, 256)
+    _check(s, "rnn_plan_describe")
+    return buf.value.decode()
+
+
+def _workspace(op, d, dt, device, ws=None):
+    torch = _torch()
+    need = workspace_size(op, d, dt)
+    if need == 0:
+        raise RnnError(RNN_ERR_UNSUPPORTED, "rnn_workspace_size")
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+    return ws
+
+
+def _common(x, W, R, G):
+    torch = _torch()
+    dt = _dtype_code(x)
+    tdt = x.dtype
+    d = dims_of(x, R)
+    N = d.NH * G * d.Dh
+    _ptr(x, "x", tdt)
+    _ptr(W, "W", tdt, (d.Din, N))
+    _ptr(R, "R", tdt, (d.NH, d.Dh, G * d.Dh))
+    del torch
+    return d, dt, N
+
+
+def input_proj(x, W, b=None, out=None, stream=None):
+    """gx = x W + b over all T*B rows (float32 [T,B,N])."""
+    torch = _torch()
+    T, B, Din = x.shape
+    N = W.shape[1]
+    dt = _dtype_code(x)
+    if out is None:
+        out = torch.empty((T, B, N), dtype=torch.float32, device=x.device)
+    s = load().rnn_input_proj(T * B, Din, N, dt, _ptr(x, "x", x.dtype), _ptr(W, "W", x.dtype),
+                              _ptr(b, "b", torch.float32, (N,), optional=True),
+                              _ptr(out, "gx", torch.float32, (T, B, N)), _stream(stream))
+    _check(s, "rnn_input_proj")
+    return out
+
+
+def lstm_fwd(x, W, R, b=None, h0=None, c0=None, *, with_seq: bool = True, ws=None,
+             out=None, stream=None):
+    """Multi-head LSTM forward.  Returns (h_seq, c_seq, hT, cT); the
+    sequences are None when with_seq is False."""
+    torch = _torch()
+    d, dt, N = _common(x, W, R, 4)
+    H = d.NH * d.Dh
+    dev = x.device
+    f32 = torch.float32
+    if out is None:
+        out = {}
+    h_seq = out.get("h_seq") if with_seq else None
+    c_seq = out.get("c_seq") if with_seq else None
+    if with_seq and h_seq is None:
+        h_seq = torch.empty((d.T, d.B, H), dtype=f32, device=dev)
+    if with_seq and c_seq is None:
+        c_seq = torch.empty((d.T, d.B, H), dtype=f32, device=dev)
+    hT = out.get("hT")
+    cT = out.get("cT")
+    hT = torch.empty((d.B, H), dtype=f32, device=dev) if hT is None else hT
+    cT = torch.empty((d.B, H), dtype=f32, device=dev) if cT is None else cT
+    ws = _workspace(OP_FWD_LSTM, d, dt, dev, ws)
+    s = load().rnn_fwd_lstm(ctypes.byref(d), dt, _ptr(x, "x"), _ptr(W, "W"), _ptr(R, "R"),
+                            _ptr(b, "b", f32, (N,), True), _ptr(h0, "h0", f32, (d.B, H), True),
+                            _ptr(c0, "c0", f32, (d.B, H), True),
+                            _ptr(h_seq, "h_seq", f32, None, True),
+                            _ptr(c_seq, "c_seq", f32, None, True),
+                            _ptr(hT, "hT", f32), _ptr(cT, "cT", f32),
+                            _ptr(ws, "ws"), ws.numel(), _stream(stream))
+    _check(s, "rnn_fwd_lstm")
+    return h_seq, c_seq, hT, cT
+
+
+def gru_fwd(x, W, R, b=None, h0=None, *, with_seq: bool = True, ws=None, stream=None):
+    """Multi-head GRU forward (reset-after).  Returns (h_seq, hT)."""
+    torch = _torch()
+    d, dt, N = _common(x, W, R, 3)
+    H = d.NH * d.Dh
+    dev = x.device
+    f32 = torch.float32
+    h_seq = torch.empty((d.T, d.B, H), dtype=f32, device=dev) if with_seq else None
+    hT = torch.empty((d.B, H), dtype=f32, device=dev)
+    ws = _workspace(OP_FWD_GRU, d, dt, dev, ws)
+    s = load().rnn_fwd_gru(ctypes.byref(d), dt, _ptr(x, "x"), _ptr(W, "W"), _ptr(R, "R"),
+                           _ptr(b, "b", f32, (N,), True), _ptr(h0, "h0", f32, (d.B, H), True),
+                           _ptr(h_seq, "h_seq", f32, None, True), _ptr(hT, "hT", f32),
+                           _ptr(ws, "ws"), ws.numel(), _stream(stream))
+    _check(s, "rnn_fwd_gru")
+    return h_seq, hT
+
+
+def rec_lstm(gx, R, h0=None, c0=None, *, with_seq=True, ws=None, out=None, stream=None):
+    """The LSTM recurrence alone on a precomputed gx [T,B,N]."""
+    torch = _torch()
+    T, B, N = gx.shape
+    NH, Dh = R.shape[0], R.shape[1]
+    d = Dims(T, B, 1, NH, Dh)
+    dt = _dtype_code(R)
+    H = NH * Dh
+    f32 = torch.float32
+    dev = gx.device
+    out = out or {}
+    h_seq = out.get("h_seq") if with_seq else None
+    c_seq = out.get("c_seq") if with_seq else None
+    if with_seq and h_seq is None:
+        h_seq = torch.empty((T, B, H), dtype=f32, device=dev)
+    if with_seq and c_seq is None:
+        c_seq = torch.empty((T, B, H), dtype=f32, device=dev)
+    hT = out.get("hT") if out.get("hT") is not None else torch.empty((B, H), dtype=f32, device=dev)
+    cT = out.get("cT") if out.get("cT") is not None else torch.empty((B, H), dtype=f32, device=dev)
+    ws = _workspace(OP_REC_LSTM, d, dt, dev, ws)
+    s = load().rnn_rec_lstm(ctypes.byref(d), dt, _ptr(gx, "gx", f32, (T, B, NH * 4 * Dh)),
+                            _ptr(R, "R", None, (NH, Dh, 4 * Dh)),
+                            _ptr(h0, "h0", f32, (B, H), True), _ptr(c0, "c0", f32, (B, H), True),
+                            _ptr(h_seq, "h_seq", f32, None, True),
+                            _ptr(c_seq, "c_seq", f32, None, True),
+                            _ptr(hT, "hT", f32), _ptr(cT, "cT", f32),
+                            _ptr(ws, "ws"), ws.numel(), _stream(stream))
+    _check(s, "rnn_rec_lstm")
+    return h_seq, c_seq, hT, cT
+
+
+def rec_gru(gx, R, h0=None, *, with_seq=True, ws=None, stream=None):
+    """The GRU recurrence alone on a precomputed gx [T,B,N]."""
+    torch = _torch()
+    T, B, N = gx.shape
+    NH, Dh = R.shape[0], R.shape[1]
+    d = Dims(T, B, 1, NH, Dh)
+    dt = _dtype_code(R)
+    H = NH * Dh
+    f32 = torch.float32
+    dev = gx.device
+    h_seq = torch.empty((T, B, H), dtype=f32, device=dev) if with_seq else None
+    hT = torch.empty((B, H), dtype=f32, device=dev)
+    ws = _workspace(OP_REC_GRU, d, dt, dev, ws)
+    s = load().rnn_rec_gru(ctypes.byref(d), dt, _ptr(gx, "gx", f32, (T, B, NH * 3 * Dh)),
+                           _ptr(R, "R", None, (NH, Dh, 3 * Dh)),
+                           _ptr(h0, "h0", f32, (B, H), True),
+                           _ptr(h_seq, "h_seq", f32, None, True), _ptr(hT, "hT", f32),
+                           _ptr(ws, "ws"), ws.numel(), _stream(stream))
+    _check(s, "rnn_rec_gru")
+    return h_seq, hT
+
+
+def lstm_bwd(x, W, R, b, h0, c0, h_seq, c_seq, dh_seq, dhT=None, dcT=None, *, ws=None,
+             stream=None):
+    """Multi-head LSTM BPTT.  Returns dict dx, dW, dR, db, dh0, dc0."""
+    torch = _torch()
+    d, dt, N = _common(x, W, R, 4)
+    H = d.NH * d.Dh
+    dev = x.device
+    f32 = torch.float32
+    g = dict(dx=torch.empty((d.T, d.B, d.Din), dtype=f32, device=dev),
+             dW=torch.empty((d.Din, N), dtype=f32, device=dev),
+             dR=torch.empty((d.NH, d.Dh, 4 * d.Dh), dtype=f32, device=dev),
+             db=torch.empty((N,), dtype=f32, device=dev),
+             dh0=torch.empty((d.B, H), dtype=f32, device=dev),
+             dc0=torch.empty((d.B, H), dtype=f32, device=dev))
+    ws = _workspace(OP_BWD_LSTM, d, dt, dev, ws)
+    seq = (d.T, d.B, H)
+    s = load().rnn_bwd_lstm(ctypes.byref(d), dt, _ptr(x, "x"), _ptr(W, "W"), _ptr(R, "R"),
+                            _ptr(b, "b", f32, (N,), True), _ptr(h0, "h0", f32, (d.B, H), True),
+                            _ptr(c0, "c0", f32, (d.B, H), True),
+                            _ptr(h_seq, "h_seq", f32, seq), _ptr(c_seq, "c_seq", f32, seq),
+                            _ptr(dh_seq, "dh_seq", f32, seq),
+                            _ptr(dhT, "dhT", f32, (d.B, H), True),
+                            _ptr(dcT, "dcT", f32, (d.B, H), True),
+                            _ptr(g["dx"], "dx"), _ptr(g["dW"], "dW"), _ptr(g["dR"], "dR"),
+                            _ptr(g["db"], "db"), _ptr(g["dh0"], "dh0"), _ptr(g["dc0"], "dc0"),
+                            _ptr(ws, "ws"), ws.numel(), _stream(stream))
+    _check(s, "rnn_bwd_lstm")
+    return g
+
+
+def workspace_status(ws, stream=None) -> int:
+    """Synchronise and report a recorded step-wait timeout (RNN_OK if none)."""
+    return int(load().rnn_workspace_status(_ptr(ws, "ws"), ws.numel(), _stream(stream)))

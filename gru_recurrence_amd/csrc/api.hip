@@ -1,0 +1,245 @@
+// api.hip -- host side of the librnn355 C ABI (include/rnn355.h): argument
+// validation, workspace layout, kernel plans and stream-ordered launches.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/rnn355.h"
+#include "common.h"
+#include "kernels.h"
+
+using namespace rnn355;
+
+namespace {
+
+// Workspace: [0, kHeader) status words and step counters, then the regions
+// of the operation, each 256-byte aligned.
+constexpr size_t kHeader = 4096;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+
+bool aligned16(const void *p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
+
+bool dims_ok(const rnn_dims *d) {
+    return d && d->T > 0 && d->B > 0 && d->Din > 0 && d->NH > 0 && d->Dh > 0 &&
+           (long)d->NH * d->Dh <= (1L << 24) && (long)d->T * d->B <= (1L << 30);
+}
+
+bool dtype_ok(rnn_dtype dt) { return dt == RNN_F32 || dt == RNN_BF16; }
+
+int gates_of_op(rnn_op op) {
+    return (op == RNN_OP_FWD_GRU || op == RNN_OP_BWD_GRU || op == RNN_OP_REC_GRU) ? 3 : 4;
+}
+
+int cell_of_op(rnn_op op) { return gates_of_op(op) == 4 ? kLSTM : kGRU; }
+
+size_t gx_bytes(const rnn_dims *d, int G) {
+    return align_up(sizeof(float) * (size_t)d->T * d->B * d->NH * G * d->Dh);
+}
+
+// Compute-unit count of the current device, cached per device.
+int device_cus() {
+    static std::mutex mu;
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    std::lock_guard<std::mutex> lk(mu);
+    if (cache[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+        cache[dev] = cus;
+    }
+    return cache[dev];
+}
+
+int bt_override() {
+    const char *e = getenv("RNN355_REC_BT");
+    return e ? atoi(e) : 0;
+}
+
+bool gemm_shape_ok(int K, int N, rnn_dtype dt) {
+    if (dt == RNN_BF16) return K % 8 == 0 && N % 8 == 0;
+    return true;
+}
+
+rnn_status input_proj(int M, int K, int N, rnn_dtype dt, const void *x, const void *W,
+                      const float *b, float *gx, uint32_t *clear, hipStream_t s) {
+    hipError_t e;
+    if (dt == RNN_BF16) {
+        GemmArgs g{};
+        g.M = M; g.N = N; g.K = K;
+        g.A = (const uint16_t *)x; g.lda = K; g.strideA = 0;
+        g.B = (const uint16_t *)W; g.ldb = N; g.strideB = 0;
+        g.bias = b; g.C = gx; g.ldc = N; g.strideC = 0;
+        g.accumulate = 0; g.clear_words = clear;
+        e = launch_gemm_bf16(g, true, false, 1, s);
+    } else {
+        GemmF32Args g{};
+        g.M = M; g.N = N; g.K = K;
+        g.A = (const float *)x; g.sam = K; g.sak = 1; g.strideA = 0;
+        g.B = (const float *)W; g.sbk = N; g.sbn = 1; g.strideB = 0;
+        g.bias = b; g.C = gx; g.ldc = N; g.strideC = 0;
+        g.accumulate = 0; g.clear_words = clear;
+        e = launch_gemm_f32(g, 1, s);
+    }
+    return e == hipSuccess ? RNN_OK : RNN_ERR_HIP;
+}
+
+rnn_status rec_fwd(int cell, const rnn_dims *d, rnn_dtype dt, const float *gx, const void *R,
+                   const float *h0, const float *c0, float *h_seq, float *c_seq, float *hT,
+                   float *cT, hipStream_t s) {
+    const RecPlan p = plan_rec(cell, d->T, d->B, d->NH, d->Dh, dt == RNN_BF16, device_cus(),
+                               bt_override());
+    if (p.kind == kRecNone) return RNN_ERR_UNSUPPORTED;
+    RecArgs a{};
+    a.T = d->T; a.B = d->B; a.NH = d->NH; a.Dh = d->Dh; a.BT = p.BT;
+    a.gx = gx;
+    a.Rb = dt == RNN_BF16 ? (const uint16_t *)R : nullptr;
+    a.Rf = dt == RNN_F32 ? (const float *)R : nullptr;
+    a.h0 = h0; a.c0 = c0; a.h_seq = h_seq; a.c_seq = c_seq; a.hT = hT; a.cT = cT;
+    return launch_rec_fwd(cell, p, a, dt == RNN_BF16, s) == hipSuccess ? RNN_OK : RNN_ERR_HIP;
+}
+
+bool rec_supported(int cell, const rnn_dims *d, rnn_dtype dt) {
+    return plan_rec(cell, d->T, d->B, d->NH, d->Dh, dt == RNN_BF16, 256, 0).kind != kRecNone;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *rnn_status_str(rnn_status s) {
+    switch (s) {
+        case RNN_OK: return "RNN_OK";
+        case RNN_ERR_INVALID_ARG: return "RNN_ERR_INVALID_ARG: bad pointer, dimension or enum";
+        case RNN_ERR_UNSUPPORTED: return "RNN_ERR_UNSUPPORTED: no kernel for this shape";
+        case RNN_ERR_WORKSPACE: return "RNN_ERR_WORKSPACE: workspace missing or too small";
+        case RNN_ERR_HIP: return "RNN_ERR_HIP: a HIP runtime call failed";
+        case RNN_ERR_BARRIER_TIMEOUT: return "RNN_ERR_BARRIER_TIMEOUT: a step wait ran out";
+    }
+    return "RNN_ERR_UNKNOWN";
+}
+
+size_t rnn_workspace_size(rnn_op op, const rnn_dims *d, rnn_dtype dt) {
+    if (!dims_ok(d) || !dtype_ok(dt)) return 0;
+    const int G = gates_of_op(op);
+    switch (op) {
+        case RNN_OP_FWD_LSTM:
+        case RNN_OP_FWD_GRU:
+            return kHeader + gx_bytes(d, G);
+        case RNN_OP_REC_LSTM:
+        case RNN_OP_REC_GRU:
+            return kHeader;
+        default:
+            return 0;
+    }
+}
+
+rnn_status rnn_plan_describe(rnn_op op, const rnn_dims *d, rnn_dtype dt, char *buf,
+                             size_t len) {
+    if (!dims_ok(d) || !dtype_ok(dt) || !buf || len == 0) return RNN_ERR_INVALID_ARG;
+    if (op < RNN_OP_FWD_LSTM || op > RNN_OP_REC_GRU) return RNN_ERR_INVALID_ARG;
+    const int cell = cell_of_op(op);
+    const RecPlan p = plan_rec(cell, d->T, d->B, d->NH, d->Dh, dt == RNN_BF16, device_cus(),
+                               bt_override());
+    const char *k = p.kind == kRecMfma ? "mfma_resident_R" : p.kind == kRecSimple ? "lds_simple" : "none";
+    snprintf(buf, len, "rec_kernel=%s rows_per_wg=%d wg=%d threads=%d wg_per_head_row_tile=1 units_per_thread=%d",
+             k, p.BT, p.grid, p.threads, p.upt);
+    return p.kind == kRecNone ? RNN_ERR_UNSUPPORTED : RNN_OK;
+}
+
+rnn_status rnn_input_proj(int M, int K, int N, rnn_dtype dt, const void *x, const void *W,
+                          const float *b, float *gx, hipStream_t stream) {
+    if (M <= 0 || K <= 0 || N <= 0 || !dtype_ok(dt)) return RNN_ERR_INVALID_ARG;
+    if (!x || !W || !gx) return RNN_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(W) || !aligned16(b) || !aligned16(gx))
+        return RNN_ERR_INVALID_ARG;
+    if (!gemm_shape_ok(K, N, dt)) return RNN_ERR_UNSUPPORTED;
+    return input_proj(M, K, N, dt, x, W, b, gx, nullptr, stream);
+}
+
+rnn_status rnn_rec_lstm(const rnn_dims *d, rnn_dtype dt, const float *gx, const void *R,
+                        const float *h0, const float *c0, float *h_seq, float *c_seq,
+                        float *hT, float *cT, void *ws, size_t ws_bytes, hipStream_t stream) {
+    if (!dims_ok(d) || !dtype_ok(dt) || !gx || !R || !hT || !cT) return RNN_ERR_INVALID_ARG;
+    const void *ps[] = {gx, R, h0, c0, h_seq, c_seq, hT, cT, ws};
+    for (const void *p : ps)
+        if (!aligned16(p)) return RNN_ERR_INVALID_ARG;
+    if (!rec_supported(kLSTM, d, dt)) return RNN_ERR_UNSUPPORTED;
+    if (!ws || ws_bytes < rnn_workspace_size(RNN_OP_REC_LSTM, d, dt)) return RNN_ERR_WORKSPACE;
+    return rec_fwd(kLSTM, d, dt, gx, R, h0, c0, h_seq, c_seq, hT, cT, stream);
+}
+
+rnn_status rnn_rec_gru(const rnn_dims *d, rnn_dtype dt, const float *gx, const void *R,
+                       const float *h0, float *h_seq, float *hT, void *ws, size_t ws_bytes,
+                       hipStream_t stream) {
+    if (!dims_ok(d) || !dtype_ok(dt) || !gx || !R || !hT) return RNN_ERR_INVALID_ARG;
+    const void *ps[] = {gx, R, h0, h_seq, hT, ws};
+    for (const void *p : ps)
+        if (!aligned16(p)) return RNN_ERR_INVALID_ARG;
+    if (!rec_supported(kGRU, d, dt)) return RNN_ERR_UNSUPPORTED;
+    if (!ws || ws_bytes < rnn_workspace_size(RNN_OP_REC_GRU, d, dt)) return RNN_ERR_WORKSPACE;
+    return rec_fwd(kGRU, d, dt, gx, R, h0, nullptr, h_seq, nullptr, hT, nullptr, stream);
+}
+
+rnn_status rnn_fwd_lstm(const rnn_dims *d, rnn_dtype dt, const void *x, const void *W,
+                        const void *R, const float *b, const float *h0, const float *c0,
+                        float *h_seq, float *c_seq, float *hT, float *cT, void *ws,
+                        size_t ws_bytes, hipStream_t stream) {
+    if (!dims_ok(d) || !dtype_ok(dt) || !x || !W || !R || !hT || !cT) return RNN_ERR_INVALID_ARG;
+    const void *ps[] = {x, W, R, b, h0, c0, h_seq, c_seq, hT, cT, ws};
+    for (const void *p : ps)
+        if (!aligned16(p)) return RNN_ERR_INVALID_ARG;
+    const int N = d->NH * 4 * d->Dh;
+    if (!gemm_shape_ok(d->Din, N, dt) || !rec_supported(kLSTM, d, dt)) return RNN_ERR_UNSUPPORTED;
+    if (!ws || ws_bytes < rnn_workspace_size(RNN_OP_FWD_LSTM, d, dt)) return RNN_ERR_WORKSPACE;
+    float *gx = (float *)((char *)ws + kHeader);
+    rnn_status st = input_proj(d->T * d->B, d->Din, N, dt, x, W, b, gx, (uint32_t *)ws, stream);
+    if (st != RNN_OK) return st;
+    return rec_fwd(kLSTM, d, dt, gx, R, h0, c0, h_seq, c_seq, hT, cT, stream);
+}
+
+rnn_status rnn_fwd_gru(const rnn_dims *d, rnn_dtype dt, const void *x, const void *W,
+                       const void *R, const float *b, const float *h0, float *h_seq,
+                       float *hT, void *ws, size_t ws_bytes, hipStream_t stream) {
+    if (!dims_ok(d) || !dtype_ok(dt) || !x || !W || !R || !hT) return RNN_ERR_INVALID_ARG;
+    const void *ps[] = {x, W, R, b, h0, h_seq, hT, ws};
+    for (const void *p : ps)
+        if (!aligned16(p)) return RNN_ERR_INVALID_ARG;
+    const int N = d->NH * 3 * d->Dh;
+    if (!gemm_shape_ok(d->Din, N, dt) || !rec_supported(kGRU, d, dt)) return RNN_ERR_UNSUPPORTED;
+    if (!ws || ws_bytes < rnn_workspace_size(RNN_OP_FWD_GRU, d, dt)) return RNN_ERR_WORKSPACE;
+    float *gx = (float *)((char *)ws + kHeader);
+    rnn_status st = input_proj(d->T * d->B, d->Din, N, dt, x, W, b, gx, (uint32_t *)ws, stream);
+    if (st != RNN_OK) return st;
+    return rec_fwd(kGRU, d, dt, gx, R, h0, nullptr, h_seq, nullptr, hT, nullptr, stream);
+}
+
+rnn_status rnn_bwd_lstm(const rnn_dims *d, rnn_dtype dt, const void *x, const void *W,
+                        const void *R, const float *b, const float *h0, const float *c0,
+                        const float *h_seq, const float *c_seq, const float *dh_seq,
+                        const float *dhT, const float *dcT, float *dx, float *dW, float *dR,
+                        float *db, float *dh0, float *dc0, void *ws, size_t ws_bytes,
+                        hipStream_t stream) {
+    (void)x; (void)W; (void)R; (void)b; (void)h0; (void)c0; (void)h_seq; (void)c_seq;
+    (void)dh_seq; (void)dhT; (void)dcT; (void)dx; (void)dW; (void)dR; (void)db; (void)dh0;
+    (void)dc0; (void)ws; (void)ws_bytes; (void)stream;
+    if (!dims_ok(d) || !dtype_ok(dt)) return RNN_ERR_INVALID_ARG;
+    return RNN_ERR_UNSUPPORTED;
+}
+
+rnn_status rnn_workspace_status(const void *ws, size_t ws_bytes, hipStream_t stream) {
+    if (!ws || ws_bytes < kHeader) return RNN_ERR_INVALID_ARG;
+    if (hipStreamSynchronize(stream) != hipSuccess) return RNN_ERR_HIP;
+    uint32_t flag = 0;
+    if (hipMemcpy(&flag, ws, sizeof(flag), hipMemcpyDeviceToHost) != hipSuccess) return RNN_ERR_HIP;
+    return flag ? RNN_ERR_BARRIER_TIMEOUT : RNN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,69 @@
+// common.h -- device types and small helpers shared by the librnn355 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rnn355 {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+enum Cell { kLSTM = 0, kGRU = 1 };
+
+template <int CELL>
+struct CellTraits;
+template <>
+struct CellTraits<kLSTM> { static constexpr int G = 4; };
+template <>
+struct CellTraits<kGRU> { static constexpr int G = 3; };
+
+// float -> bf16 bit pattern, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float(((uint32_t)h) << 16);
+}
+
+// e^x through the hardware base-2 exponential (v_exp_f32) with the argument
+// scaled by log2(e).  Over/underflow saturate to inf / 0 as e^x does.
+__device__ __forceinline__ float exp_fast(float x) {
+    return __builtin_amdgcn_exp2f(x * kLog2e);
+}
+
+// 1/x via v_rcp_f32 (1 ulp).
+__device__ __forceinline__ float rcp_fast(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// logistic sigmoid 1/(1+e^-a); saturates cleanly to 0 and 1.
+__device__ __forceinline__ float sigmoid_f(float a) {
+    return rcp_fast(1.0f + exp_fast(-a));
+}
+
+// tanh(a) = sign(a) * (1 - e^{-2|a|}) / (1 + e^{-2|a|}); e^{-2|a|} lies in
+// (0, 1] so nothing overflows, and the absolute error stays near 1 ulp of 1.
+__device__ __forceinline__ float tanh_f(float a) {
+    const float e = exp_fast(-2.0f * fabsf(a));
+    const float t = (1.0f - e) * rcp_fast(1.0f + e);
+    return copysignf(t, a);
+}
+
+__device__ __forceinline__ f32x4 mfma_16x16x32_bf16(const bf16x8 &a, const bf16x8 &b,
+                                                     const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Select two 16-bit halves: lo half of the result from `lo_src`, hi half
+// from `hi_src`; `hi_parts` picks the upper (true) or lower (false) halves
+// of both sources.  (v_perm_b32 byte select.)
+__device__ __forceinline__ uint32_t pack_halves(uint32_t lo_src, uint32_t hi_src, bool upper) {
+    return __builtin_amdgcn_perm(hi_src, lo_src, upper ? 0x07060302u : 0x05040100u);
+}
+
+}  // namespace rnn355

@@ -1,0 +1,186 @@
+/*
+ * rnn355.h -- C ABI of librnn355: multi-head LSTM / GRU recurrence with a
+ * block-diagonal recurrent matrix on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (FlashRNN, arXiv 2412.07752, abstract; and "Re-examining
+ * RNNs from a GPU programming perspective", blog.hotdry.top 2025-09-21, the
+ * paragraphs on the step dependency, on keeping R resident across steps and
+ * on head-wise splitting):
+ *   a traditional LSTM or GRU whose hidden state of size H = NH*Dh is split
+ *   into NH independent heads, each with its own Dh x G*Dh recurrent block, so
+ *   the recurrent matrix is block-diagonal.  Every call first forms the input
+ *   part of all gates for all T steps at once (Gx = x W + b, a dense
+ *   contraction) and then runs the strictly sequential recurrence
+ *   A_t = Gx_t + h_{t-1} R, followed by the cell's gate update.
+ *
+ * Cells (textbook forms; the pages name the cells but print no equations):
+ *   LSTM, gates i,f,z,o:  i,f,o = sigmoid, z = tanh
+ *       c_t = f*c_{t-1} + i*z,   h_t = o*tanh(c_t)
+ *   GRU (reset-after), gates r,z,n with S = h_{t-1} R:
+ *       r = sigmoid(Gx_r + S_r), u = sigmoid(Gx_z + S_z),
+ *       n = tanh(Gx_n + r*S_n),  h_t = (1-u)*n + u*h_{t-1}
+ *
+ * Layouts (row-major, C order).  H = NH*Dh, G = 4 (LSTM) or 3 (GRU),
+ * N = NH*G*Dh.
+ *   x        [T][B][Din]          dtype of the call (f32 or bf16)
+ *   W        [Din][NH][G][Dh]     dtype of the call; column (n*G+g)*Dh + j
+ *   R        [NH][Dh][G*Dh]       dtype of the call; row m of block n multiplies h_{t-1}[n*Dh+m]
+ *   b        [NH][G][Dh]          float32 (may be NULL = 0)
+ *   h0, c0   [B][H]               float32 (may be NULL = 0)
+ *   h_seq, c_seq, dh_seq [T][B][H] float32, holding h_1..h_T (not h_0)
+ *   hT, cT, dh0, dc0, dhT, dcT [B][H] float32
+ *   gx       [T][B][N]            float32 (the input projection incl. bias)
+ *   dx       [T][B][Din]          float32
+ *   dW, dR, db  shapes of W, R, b  float32
+ * Arithmetic: bf16 calls multiply bf16 operands (x, W, R, and h_{t-1} rounded
+ * to bf16 with round-to-nearest-even) with float32 accumulation; gates, cell
+ * and hidden state, and every gradient stay float32.  f32 calls compute in
+ * float32 throughout.
+ *
+ * Ownership and threading: every tensor pointer is DEVICE memory owned by the
+ * caller; outputs are overwritten, never accumulated.  The library allocates
+ * nothing: scratch comes from the caller's workspace of at least
+ * rnn_workspace_size() bytes.  Calls only enqueue work on `stream` and return
+ * (asynchronous, stream-ordered); they hold no global mutable state apart from
+ * a lazily filled, lock-protected cache of device properties, so they may be
+ * called from several host threads.  Two calls in flight at once must not
+ * share a workspace.
+ *
+ * Errors: every function returns a status; nothing aborts and no C++
+ * exception crosses this boundary.  Arguments are validated before anything
+ * is enqueued (then nothing was enqueued): NULL required pointers, non-positive
+ * dims, pointers not 16-byte aligned, unsupported shapes, a workspace that is
+ * too small.  A failing launch returns RNN_ERR_HIP.  Kernels that span several
+ * compute units per head wait on each other at every step with a bounded
+ * spin; if a wait ever runs out they record it in the workspace and finish,
+ * and rnn_workspace_status() reports RNN_ERR_BARRIER_TIMEOUT.
+ */
+#ifndef RNN355_H
+#define RNN355_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct {
+    int T;    /* time steps (>= 1) */
+    int B;    /* batch rows (>= 1) */
+    int Din;  /* input features (>= 1) */
+    int NH;   /* heads (>= 1) */
+    int Dh;   /* hidden units per head (>= 1) */
+} rnn_dims;
+
+typedef enum { RNN_F32 = 0, RNN_BF16 = 1 } rnn_dtype;
+
+typedef enum {
+    RNN_OK = 0,
+    RNN_ERR_INVALID_ARG = 1,     /* NULL / misaligned pointer, dims <= 0, bad enum */
+    RNN_ERR_UNSUPPORTED = 2,     /* shape this build has no kernel for */
+    RNN_ERR_WORKSPACE = 3,       /* ws NULL or ws_bytes < rnn_workspace_size() */
+    RNN_ERR_HIP = 4,             /* a HIP runtime call failed */
+    RNN_ERR_BARRIER_TIMEOUT = 5  /* a multi-CU step wait ran out (see above) */
+} rnn_status;
+
+typedef enum {
+    RNN_OP_FWD_LSTM = 0,
+    RNN_OP_FWD_GRU = 1,
+    RNN_OP_BWD_LSTM = 2,
+    RNN_OP_BWD_GRU = 3,
+    RNN_OP_REC_LSTM = 4,   /* rnn_rec_lstm alone (no input projection) */
+    RNN_OP_REC_GRU = 5     /* rnn_rec_gru alone */
+} rnn_op;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *rnn_status_str(rnn_status s);
+
+/* Bytes of workspace `op` needs at these dims and dtype; 0 if the arguments
+ * are invalid or unsupported (the call itself then says which).  Pure host
+ * function: touches no device. */
+size_t rnn_workspace_size(rnn_op op, const rnn_dims *d, rnn_dtype dt);
+
+/* Write a one-line description of the kernel plan `op` would use (kernel,
+ * rows per workgroup, workgroups, workgroups per head) into buf.  Pure host
+ * function apart from reading the device's compute-unit count once. */
+rnn_status rnn_plan_describe(rnn_op op, const rnn_dims *d, rnn_dtype dt,
+                             char *buf, size_t len);
+
+/*
+ * Input projection for all steps at once (FlashRNN abstract: the input part
+ * of every gate depends only on x_t, so it is one dense contraction over all
+ * T*B rows; the recurrence then only adds h_{t-1} R):
+ *   gx[m][c] = b[c] + sum_k x[m][k] * W[k][c],   m < M = T*B, c < N
+ * x [M][K], W [K][N] in dtype dt; b [N] float32 or NULL; gx [M][N] float32.
+ * bf16 needs K % 8 == 0 and N % 8 == 0.
+ */
+rnn_status rnn_input_proj(int M, int K, int N, rnn_dtype dt,
+                          const void *x, const void *W, const float *b,
+                          float *gx, hipStream_t stream);
+
+/*
+ * The sequential LSTM recurrence alone, given gx from rnn_input_proj
+ * (blog.hotdry.top 2025-09-21: the per-step dependency is the bottleneck; R
+ * stays resident on chip for all steps):
+ *   A_t = gx_t + h_{t-1} R (block-diagonal), then the LSTM gate update.
+ * gx [T][B][N] float32; R in dtype dt; outputs as in rnn_fwd_lstm.
+ * h_seq, c_seq may be NULL (then only hT, cT are written); hT, cT required.
+ */
+rnn_status rnn_rec_lstm(const rnn_dims *d, rnn_dtype dt, const float *gx,
+                        const void *R, const float *h0, const float *c0,
+                        float *h_seq, float *c_seq, float *hT, float *cT,
+                        void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* The GRU recurrence alone, given gx (bias inside gx).  h_seq may be NULL. */
+rnn_status rnn_rec_gru(const rnn_dims *d, rnn_dtype dt, const float *gx,
+                       const void *R, const float *h0,
+                       float *h_seq, float *hT,
+                       void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Multi-head LSTM forward: rnn_input_proj into the workspace, then
+ * rnn_rec_lstm.  h_seq, c_seq [T][B][H] may be NULL; hT, cT required.
+ */
+rnn_status rnn_fwd_lstm(const rnn_dims *d, rnn_dtype dt,
+                        const void *x, const void *W, const void *R,
+                        const float *b, const float *h0, const float *c0,
+                        float *h_seq, float *c_seq, float *hT, float *cT,
+                        void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Multi-head GRU forward (reset-after).  h_seq may be NULL; hT required. */
+rnn_status rnn_fwd_gru(const rnn_dims *d, rnn_dtype dt,
+                       const void *x, const void *W, const void *R,
+                       const float *b, const float *h0,
+                       float *h_seq, float *hT,
+                       void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Multi-head LSTM backpropagation through time for the loss
+ *   L = sum_t dh_seq[t] . h_t + dhT . h_T + dcT . c_T
+ * given the forward's h_seq and c_seq (from rnn_fwd_lstm on the same inputs).
+ * dhT, dcT may be NULL (= 0).  Writes dx, dW, dR, db, dh0, dc0 (all required).
+ * Gate pre-activations are recomputed from x, W, b, h_seq and R.
+ */
+rnn_status rnn_bwd_lstm(const rnn_dims *d, rnn_dtype dt,
+                        const void *x, const void *W, const void *R,
+                        const float *b, const float *h0, const float *c0,
+                        const float *h_seq, const float *c_seq,
+                        const float *dh_seq, const float *dhT, const float *dcT,
+                        float *dx, float *dW, float *dR, float *db,
+                        float *dh0, float *dc0,
+                        void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Synchronises `stream`, then reports whether a kernel of the last call that
+ * used `ws` recorded a step-wait timeout (RNN_ERR_BARRIER_TIMEOUT) or not
+ * (RNN_OK).  `ws` must be the workspace that call used.
+ */
+rnn_status rnn_workspace_status(const void *ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RNN355_H */

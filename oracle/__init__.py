@@ -49,7 +49,8 @@ def _load():
         lib.oracle_gru_bptt.argtypes = [I] * 5 + [P] * 5 + [P] * 2 + [P] + [P] * 4
         lib.oracle_param_grads.argtypes = [I] * 6 + [P] * 6 + [P] * 4
         lib.oracle_param_grad_entries.argtypes = [I] * 7 + [L, P] + [P] * 6 + [P]
-        for f in (lib.oracle_lstm_fwd, lib.oracle_gru_fwd, lib.oracle_lstm_bptt,
+        lib.oracle_input_proj.argtypes = [L, I, I, P, P, P, L, P, P]
+        for f in (lib.oracle_input_proj, lib.oracle_lstm_fwd, lib.oracle_gru_fwd, lib.oracle_lstm_bptt,
                   lib.oracle_gru_bptt, lib.oracle_param_grads,
                   lib.oracle_param_grad_entries):
             f.restype = I
@@ -85,6 +86,22 @@ def _nan(shape):
 def _check(rc, what):
     if rc != 0:
         raise ValueError("oracle %s rejected its arguments (rc=%d)" % (what, rc))
+
+
+def input_proj(x, W, b=None, rows=None):
+    """gx = x W + b for x [M,K] (or [T,B,K], flattened), W [K,N]; optionally
+    only at the given flat row indices.  Returns [len(rows) or M, N]."""
+    x = _d(x)
+    x = x.reshape(-1, x.shape[-1])
+    W, b = _d(W), _d(b)
+    M, K = x.shape
+    N = W.shape[1]
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int_)
+    out = np.zeros((M if r is None else r.size, N))
+    rc = _load().oracle_input_proj(M, K, N, _p(x), _p(W), _p(b), 0 if r is None else r.size,
+                                   _p(r), _p(out))
+    _check(rc, "input_proj")
+    return out
 
 
 def lstm_fwd(x, W, R, b, h0=None, c0=None, *, NH: int, Dh: int, chain_mask=None):

@@ -469,3 +469,28 @@ int oracle_param_grad_entries(int T, int B, int Din, int NH, int Dh, int G, int 
     }
     return 0;
 }
+
+/* ------------------------------------------------- input projection */
+
+/*
+ * The input projection on its own, at chosen rows (rows = NULL: all M rows):
+ *   gx[e][c] = b[c] + sum_{k=0..K-1} x[rows[e]][k] * W[k][c]
+ * x [M][K], W [K][N], gx [nrows][N].
+ */
+int oracle_input_proj(long M, int K, int N, const double *x, const double *W,
+                      const double *bias, long nrows, const long *rows, double *gx) {
+    if (M <= 0 || K <= 0 || N <= 0) return -1;
+    const long R = rows ? nrows : M;
+#pragma omp parallel for
+    for (long e = 0; e < R; ++e) {
+        const long m = rows ? rows[e] : e;
+        double *o = gx + (size_t)e * N;
+        for (int c = 0; c < N; ++c) o[c] = bias ? bias[c] : 0.0;
+        for (int k = 0; k < K; ++k) {
+            const double xv = x[(size_t)m * K + k];
+            const double *w = W + (size_t)k * N;
+            for (int c = 0; c < N; ++c) o[c] += xv * w[c];
+        }
+    }
+    return 0;
+}

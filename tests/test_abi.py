@@ -1,0 +1,93 @@
+"""The C ABI on the CPU: the library loads, exports every function that
+include/rnn355.h declares, and rejects bad arguments before touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gru_recurrence_amd as g
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rnn355.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(rnn_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = g.load()
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(g.EXPORTS)
+
+
+def test_status_strings():
+    for s in range(6):
+        assert g.status_str(s).startswith("RNN_")
+    assert "UNKNOWN" in g.status_str(99)
+
+
+def test_workspace_size_pure_host():
+    d = g.Dims(1024, 16, 768, 6, 128)
+    fwd = g.workspace_size(g.OP_FWD_LSTM, d, g.RNN_BF16)
+    assert fwd >= 1024 * 16 * 6 * 4 * 128 * 4
+    assert g.workspace_size(g.OP_FWD_GRU, d, g.RNN_BF16) < fwd
+    assert g.workspace_size(g.OP_FWD_LSTM, g.Dims(0, 16, 768, 6, 128), g.RNN_BF16) == 0
+    assert g.workspace_size(g.OP_FWD_LSTM, d, 7) == 0
+
+
+FAKE = 0x7F0000000000  # never dereferenced: validation fails first
+
+
+def _p(v):
+    return ctypes.c_void_p(v)
+
+
+def test_invalid_arguments_are_rejected_before_launch():
+    lib = g.load()
+    d = g.Dims(8, 2, 32, 1, 32)
+    ok = [_p(FAKE + 256 * i) for i in range(11)]
+    # NULL x
+    args = list(ok)
+    args[0] = None
+    s = lib.rnn_fwd_lstm(ctypes.byref(d), g.RNN_BF16, *args[:10], None, 0, None)
+    assert s == g.RNN_ERR_INVALID_ARG
+    # misaligned W
+    args = list(ok)
+    args[1] = _p(FAKE + 2)
+    s = lib.rnn_fwd_lstm(ctypes.byref(d), g.RNN_BF16, *args[:10], _p(FAKE), 1 << 30, None)
+    assert s == g.RNN_ERR_INVALID_ARG
+    # bad dims and dtype
+    bad = g.Dims(8, 0, 32, 1, 32)
+    assert lib.rnn_fwd_lstm(ctypes.byref(bad), g.RNN_BF16, *ok[:10], _p(FAKE), 1 << 30,
+                            None) == g.RNN_ERR_INVALID_ARG
+    assert lib.rnn_fwd_lstm(ctypes.byref(d), 5, *ok[:10], _p(FAKE), 1 << 30,
+                            None) == g.RNN_ERR_INVALID_ARG
+    # missing / too small workspace
+    assert lib.rnn_fwd_lstm(ctypes.byref(d), g.RNN_BF16, *ok[:10], None, 0,
+                            None) == g.RNN_ERR_WORKSPACE
+    assert lib.rnn_fwd_lstm(ctypes.byref(d), g.RNN_BF16, *ok[:10], _p(FAKE), 64,
+                            None) == g.RNN_ERR_WORKSPACE
+    # unsupported: bf16 GEMM needs Din % 8 == 0
+    d2 = g.Dims(8, 2, 30, 1, 32)
+    assert lib.rnn_fwd_lstm(ctypes.byref(d2), g.RNN_BF16, *ok[:10], _p(FAKE), 1 << 30,
+                            None) == g.RNN_ERR_UNSUPPORTED
+    # unsupported: an f32 head too large for the LDS kernel and not MFMA-shaped
+    d3 = g.Dims(8, 2, 32, 1, 256)
+    assert lib.rnn_fwd_lstm(ctypes.byref(d3), g.RNN_F32, *ok[:10], _p(FAKE), 1 << 30,
+                            None) == g.RNN_ERR_UNSUPPORTED
+    # input projection
+    assert lib.rnn_input_proj(0, 8, 8, g.RNN_BF16, ok[0], ok[1], None, ok[2],
+                              None) == g.RNN_ERR_INVALID_ARG
+    assert lib.rnn_input_proj(4, 8, 8, g.RNN_BF16, ok[0], None, None, ok[2],
+                              None) == g.RNN_ERR_INVALID_ARG
+    # recurrence alone
+    assert lib.rnn_rec_gru(ctypes.byref(d), g.RNN_BF16, None, ok[1], None, None, ok[2],
+                           _p(FAKE), 1 << 20, None) == g.RNN_ERR_INVALID_ARG
+    assert lib.rnn_workspace_status(None, 0, None) == g.RNN_ERR_INVALID_ARG

@@ -1,0 +1,199 @@
+"""GPU parity of the forward path (input projection + recurrence) against the
+CPU oracle, through the C ABI.  Bars: normwise error max|y-y*|/max|y*| of at
+most 1e-5 for float32 calls and 2e-2 for bf16 calls (bf16 x, W, R, float32
+accumulation and state); 1e-4 for the input projection alone (exact bf16
+operands, float32 sums of Din products)."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import dev, host, nerr
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import gru_recurrence_amd as g  # noqa: E402
+
+TOL_F32 = 1e-5
+TOL_BF16 = 2e-2
+
+
+@pytest.fixture(autouse=True)
+def _no_plan_override():
+    old = os.environ.pop("RNN355_REC_BT", None)
+    yield
+    os.environ.pop("RNN355_REC_BT", None)
+    if old is not None:
+        os.environ["RNN355_REC_BT"] = old
+
+
+def run_lstm(c, **kw):
+    h_seq, c_seq, hT, cT = g.lstm_fwd(dev(c, "x"), dev(c, "W"), dev(c, "R"), dev(c, "b"),
+                                      dev(c, "h0"), dev(c, "c0"), **kw)
+    torch.cuda.synchronize()
+    return dict(h_seq=host(h_seq), c_seq=host(c_seq), hT=host(hT), cT=host(cT))
+
+
+def run_gru(c, **kw):
+    h_seq, hT = g.gru_fwd(dev(c, "x"), dev(c, "W"), dev(c, "R"), dev(c, "b"), dev(c, "h0"), **kw)
+    torch.cuda.synchronize()
+    return dict(h_seq=host(h_seq), hT=host(hT))
+
+
+def oracle_of(c, mask=None):
+    d = c.dims
+    if c.cell == "lstm":
+        return oracle.lstm_fwd(c.f64("x"), c.f64("W"), c.f64("R"), c.f64("b"), c.f64("h0"),
+                               c.f64("c0"), NH=d.NH, Dh=d.Dh, chain_mask=mask)
+    return oracle.gru_fwd(c.f64("x"), c.f64("W"), c.f64("R"), c.f64("b"), c.f64("h0"),
+                          NH=d.NH, Dh=d.Dh, chain_mask=mask)
+
+
+def compare(got, want, tol, keys):
+    for k in keys:
+        e = nerr(got[k], want[k])
+        print("  %-6s nerr=%.3e" % (k, e), flush=True)
+        assert e <= tol, (k, e)
+
+
+def test_lstm_fp32_tiny_workload_full():
+    """The fp32 tiny LSTM workload (T=64, B=2, NH=1, Dh=32, Din=32) in full."""
+    c = synth.workload_case(synth.WORKLOADS["lstm_fp32_tiny"])
+    compare(run_lstm(c), oracle_of(c), TOL_F32, ("h_seq", "c_seq", "hT", "cT"))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("M,K,N", [(185, 96, 384), (128, 64, 128), (300, 768, 288)])
+def test_input_projection(M, K, N, dtype):
+    d = synth.Dims(T=M, B=1, Din=K, NH=1, Dh=N // 4)
+    c = synth.make_case("lstm", d, dtype, 4242 + M, bias=synth.normal(99, N, 1.0))
+    gx = g.input_proj(dev(c, "x"), dev(c, "W"), dev(c, "b"))
+    torch.cuda.synchronize()
+    want = oracle.input_proj(c.f64("x"), c.f64("W"), c.f64("b"))
+    e = nerr(host(gx).reshape(M, N), want)
+    print("  gx nerr=%.3e" % e, flush=True)
+    assert e <= (1e-4 if dtype == "bf16" else 1e-5)
+
+
+@pytest.mark.parametrize("Dh", [32, 64, 128])
+@pytest.mark.parametrize("bt", [None, 1, 3, 16])
+def test_lstm_bf16_tiles_and_ragged(Dh, bt):
+    """T=37, B=5 (ragged against every batch tile), NH=3, Din=96 (M=185 rows
+    and N=12*Dh columns end in partial GEMM tiles)."""
+    if bt is not None:
+        os.environ["RNN355_REC_BT"] = str(bt)
+    d = synth.Dims(T=37, B=5, Din=96, NH=3, Dh=Dh)
+    c = synth.make_case("lstm", d, "bf16", 5000 + Dh, bias="forget+1", h0_var=0.2, c0_var=0.2)
+    compare(run_lstm(c), oracle_of(c), TOL_BF16, ("h_seq", "c_seq", "hT", "cT"))
+
+
+@pytest.mark.parametrize("Dh", [32, 64, 128])
+@pytest.mark.parametrize("bt", [None, 2, 16])
+def test_gru_bf16_tiles_and_ragged(Dh, bt):
+    if bt is not None:
+        os.environ["RNN355_REC_BT"] = str(bt)
+    d = synth.Dims(T=41, B=6, Din=64, NH=2, Dh=Dh)
+    c = synth.make_case("gru", d, "bf16", 6000 + Dh, h0_var=0.1)
+    compare(run_gru(c), oracle_of(c), TOL_BF16, ("h_seq", "hT"))
+
+
+@pytest.mark.parametrize("cell,dtype,Dh", [("gru", "f32", 32), ("lstm", "f32", 48),
+                                           ("lstm", "bf16", 48), ("gru", "bf16", 16)])
+def test_lds_kernel_shapes(cell, dtype, Dh):
+    """Shapes outside the MFMA kernel run on the LDS kernel (R as float32)."""
+    d = synth.Dims(T=19, B=3, Din=40 if dtype == "bf16" else 20, NH=2, Dh=Dh)
+    c = synth.make_case(cell, d, dtype, 7000 + Dh, h0_var=0.2, c0_var=0.2)
+    got = run_lstm(c) if cell == "lstm" else run_gru(c)
+    keys = ("h_seq", "c_seq", "hT", "cT") if cell == "lstm" else ("h_seq", "hT")
+    compare(got, oracle_of(c), TOL_F32 if dtype == "f32" else TOL_BF16, keys)
+
+
+def test_single_step_single_row_single_head():
+    d = synth.Dims(T=1, B=1, Din=8, NH=1, Dh=32)
+    c = synth.make_case("lstm", d, "bf16", 7100, h0_var=0.5, c0_var=0.5)
+    compare(run_lstm(c), oracle_of(c), TOL_BF16, ("h_seq", "c_seq", "hT", "cT"))
+
+
+def test_run_to_run_bitwise_and_resume():
+    d = synth.Dims(T=30, B=4, Din=64, NH=2, Dh=64)
+    c = synth.make_case("lstm", d, "bf16", 7200, bias="forget+1", h0_var=0.1, c0_var=0.1)
+    a = run_lstm(c)
+    b = run_lstm(c)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+    # two chunks chained through (hT, cT) equal one call, bitwise
+    x, W, R, bb = dev(c, "x"), dev(c, "W"), dev(c, "R"), dev(c, "b")
+    h1, c1, hT1, cT1 = g.lstm_fwd(x[:11].contiguous(), W, R, bb, dev(c, "h0"), dev(c, "c0"))
+    h2, c2, hT2, cT2 = g.lstm_fwd(x[11:].contiguous(), W, R, bb, hT1, cT1)
+    torch.cuda.synchronize()
+    assert np.array_equal(np.concatenate([host(h1), host(h2)]), a["h_seq"])
+    assert np.array_equal(host(cT2), a["cT"])
+
+
+def test_head_and_batch_independence_bitwise():
+    d = synth.Dims(T=20, B=4, Din=64, NH=3, Dh=32)
+    c = synth.make_case("gru", d, "bf16", 7300, h0_var=0.1)
+    base = run_gru(c)
+    c.vals["h0"][:, 32:64] += 0.5      # head 1 state
+    c.vals["h0"][3] -= 0.5             # batch row 3
+    c.bits.pop("R")
+    c.vals["R"] = c.vals["R"].copy()
+    c.vals["R"][1] *= -1.0             # head 1 weights (stays exact in bf16)
+    c.bits["R"] = synth.f32_to_bf16_bits(c.vals["R"])
+    pert = run_gru(c)
+    keep_h = np.r_[0:32, 64:96]
+    assert np.array_equal(pert["h_seq"][:, :3][..., keep_h], base["h_seq"][:, :3][..., keep_h])
+    assert not np.array_equal(pert["h_seq"][:, 3], base["h_seq"][:, 3])
+
+
+def test_recurrence_entry_matches_fused_forward():
+    d = synth.Dims(T=25, B=3, Din=32, NH=2, Dh=64)
+    c = synth.make_case("lstm", d, "bf16", 7400, bias="forget+1")
+    full = run_lstm(c)
+    gx = g.input_proj(dev(c, "x"), dev(c, "W"), dev(c, "b"))
+    h, cs, hT, cT = g.rec_lstm(gx, dev(c, "R"), dev(c, "h0"), dev(c, "c0"))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(h), full["h_seq"])
+    assert np.array_equal(host(cT), full["cT"])
+
+
+def _chain_mask(B, NH, chains):
+    m = np.zeros((B, NH), bool)
+    for b, n in chains:
+        m[b, n] = True
+    return m
+
+
+def _compare_chains(got, want, chains, Dh, tol, keys):
+    for b, n in chains:
+        sl = slice(n * Dh, (n + 1) * Dh)
+        for k in keys:
+            y = got[k][:, b, sl] if got[k].ndim == 3 else got[k][b, sl]
+            r = want[k][:, b, sl] if want[k].ndim == 3 else want[k][b, sl]
+            e = nerr(y, r)
+            print("  chain (b=%d, n=%d) %-6s nerr=%.3e" % (b, n, k, e), flush=True)
+            assert e <= tol, (b, n, k, e)
+
+
+def test_headline_lstm_workload_full_size_sampled_chains():
+    """Multi-head LSTM B=16, NH=6, Dh=128, T=1024, Din=768 at full size in the
+    default launch configuration; the oracle recomputes three whole chains."""
+    w = synth.WORKLOADS["lstm_mh_b16_nh6_dh128"]
+    c = synth.workload_case(w)
+    got = run_lstm(c, )
+    chains = [(0, 0), (7, 3), (15, 5)]
+    want = oracle_of(c, _chain_mask(16, 6, chains))
+    _compare_chains(got, want, chains, 128, TOL_BF16, ("h_seq", "c_seq", "hT", "cT"))
+
+
+def test_gru_small_batch_workload_full_size_sampled_chains():
+    """Multi-head GRU B=4, NH=12, Dh=64, T=2048, Din=768 at full size."""
+    w = synth.WORKLOADS["gru_mh_b4_nh12_dh64"]
+    c = synth.workload_case(w)
+    got = run_gru(c)
+    chains = [(0, 0), (2, 7), (3, 11)]
+    want = oracle_of(c, _chain_mask(4, 12, chains))
+    _compare_chains(got, want, chains, 64, TOL_BF16, ("h_seq", "hT"))
