@@ -54,6 +54,31 @@ __device__ __forceinline__ float tanh_f(float a) {
     return copysignf(t, a);
 }
 
+// Workgroup barrier that orders LDS only: release/acquire fences limited to
+// the local address space, so the barrier never waits on outstanding global
+// loads or stores (a plain __syncthreads() would also drain those).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Cross-row moves of gfx950 (a "row" is 16 lanes).  With x the first and y
+// the second operand:
+//   swap16(x, y) -> { [x0, y0, x2, y2], [x1, y1, x3, y3] }
+//   swap32(x, y) -> { [x0, x1, y0, y1], [x2, x3, y2, y3] }
+struct RowPair {
+    float a, b;
+};
+__device__ __forceinline__ RowPair swap16(float x, float y) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ RowPair swap32(float x, float y) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+
 __device__ __forceinline__ f32x4 mfma_16x16x32_bf16(const bf16x8 &a, const bf16x8 &b,
                                                      const f32x4 &c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);

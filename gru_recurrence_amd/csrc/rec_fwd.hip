@@ -9,20 +9,24 @@
 // and then walks all T steps:
 //     A_t = Gx_t + h_{t-1} R_n,   then the cell's gate update.
 //
-// MFMA kernel (bf16 R, Dh a multiple of 32):
-//   * R_n lives in VGPRs for the whole call as B-operand fragments of
-//     v_mfma_f32_16x16x32_bf16: the G*Dh gate columns are cut into 16-wide
-//     tiles, dealt round-robin to the waves; each wave holds its tiles for all
-//     Dh/32 k-chunks (Dh=128, LSTM: 4 tiles x 4 chunks x 4 VGPRs = 64 VGPRs).
-//   * h_{t-1} is kept in LDS as bf16 (the A operand: 16 rows = batch rows of
-//     the tile, rows beyond the tile are zero).
-//   * per step: one 16-byte LDS read per k-chunk, the MFMA chain, the 16x16
-//     results go to LDS, barrier, then every thread updates its own units
-//     (b, j) in float32 -- gate nonlinearities, c/h update, h_t back to LDS
-//     as bf16 and h_t, c_t streamed to HBM -- barrier.
-//   * Gx_t for a thread's units is prefetched PD steps ahead into registers.
+// MFMA kernel (bf16 R, Dh in {32, 64, 128}):
+//   * Dh/16 waves; wave w owns hidden units [16w, 16w+16) and holds, for all
+//     T steps, the B-operand fragments of v_mfma_f32_16x16x32_bf16 for those
+//     units' G gate columns over all Dh/32 k-chunks (Dh=128 LSTM: 4 gates x
+//     4 chunks x 4 VGPRs = 64 VGPRs of R per wave, R never re-read).
+//   * h_{t-1} sits in LDS as bf16 (A operand; 16 rows = batch rows of the
+//     tile, rows beyond the tile stay zero), double-buffered by step parity.
+//   * per step: Dh/32 16-byte LDS reads, G*Dh/32 MFMAs, then every lane
+//     already holds all G gate sums of its units (lane-local gate update in
+//     float32), writes h_t as bf16 to the other LDS buffer, one barrier.
+//   * HBM traffic is grouped by PD steps: Gx for the next group goes into a
+//     register double buffer and the last group's h/c outputs are stored,
+//     both issued at the first step of a group, so the only wait on HBM sits
+//     at a group start and covers requests issued a full group earlier.
 // Simple kernel (f32, or shapes the MFMA kernel does not cover): R in LDS as
 // float32, one thread per (row, gate column) dot product per step.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -59,21 +63,58 @@ __device__ __forceinline__ void lstm_or_gru_unit(const float *gpre, int DH, cons
     }
 }
 
-template <int CELL, int DH, int NW, int UPT, int PD>
-__global__ __launch_bounds__(NW * 64) void rec_fwd_mfma_kernel(RecArgs a) {
+// Gate update of one unit from its pre-activations.  LSTM: a[g] = Gx + h R
+// for g = i,f,z,o and st = c.  GRU: a[0..1] = Gx + S for r,z, a[2] = S_n,
+// gxn = Gx_n and st = h_{t-1}.
+template <int CELL>
+__device__ __forceinline__ float unit_update(const float *a, float gxn, float &st, float &c_out) {
+    if (CELL == kLSTM) {
+        const float ig = sigmoid_f(a[0]), fg = sigmoid_f(a[1]);
+        const float zg = tanh_f(a[2]), og = sigmoid_f(a[3]);
+        const float c = fmaf(fg, st, ig * zg);
+        st = c;
+        c_out = c;
+        return og * tanh_f(c);
+    } else {
+        const float r = sigmoid_f(a[0]), u = sigmoid_f(a[1]);
+        const float nn = tanh_f(fmaf(r, a[2], gxn));
+        const float h = fmaf(u, st - nn, nn);  // (1-u)*nn + u*h_{t-1}
+        st = h;
+        c_out = 0.f;
+        return h;
+    }
+}
+
+// One workgroup = one head x one tile of up to 16 batch rows; DH/16 waves,
+// wave w owns hidden units [16w, 16w+16) with all G gate tiles, so after the
+// MFMA chain lane l holds every gate sum of unit 16w + l%16 for batch rows
+// 4*(l/16) + r, r < R4 (R4 = register row slots in use).
+//
+// R4 == 1 (one batch row per workgroup) only rows 0 of the accumulators are
+// live, in lanes 0..15.  Three cross-row swaps then lay the G gate sums of a
+// unit out as the 4 rows of one register (gate g in lanes 16g..16g+15), so a
+// single exp + rcp pass activates every gate at once (tanh(x) = 2*sigmoid(2x)
+// - 1 on the z/n row), and three more swaps hand each lane back all gates.
+//
+// Memory traffic is grouped by PD steps: at the first step of each group the
+// Gx values of the NEXT group are loaded into a register double buffer and
+// the h/c outputs of the PREVIOUS group (kept in registers) are stored.  The
+// only wait on HBM then sits at the first step of a group and covers
+// operations issued a whole group earlier.
+template <int CELL, int DH, int R4, int PD>
+__global__ __launch_bounds__(DH / 16 * 64) void rec_fwd_mfma_kernel(RecArgs a) {
     constexpr int G = CellTraits<CELL>::G;
     constexpr int GD = G * DH;
-    constexpr int NT = GD / 16;   // 16-wide gate-column tiles
+    constexpr int NW = DH / 16;   // waves = 16-unit blocks
     constexpr int KC = DH / 32;   // k chunks of one MFMA
-    constexpr int TPW = NT / NW;  // tiles per wave
-    constexpr int NTH = NW * 64;
     constexpr int HLD = DH + 8;   // bf16 per h row in LDS (bank spread)
-    constexpr int GLD = GD + 4;   // floats per gate row in LDS
-    static_assert(NT % NW == 0, "tiles must split evenly over waves");
+    constexpr bool ROWS1 = R4 == 1;
+    constexpr int GL = ROWS1 ? 1 : G;          // Gx values per row slot per lane
+    constexpr int OUT_ROW = CELL == kLSTM ? 0 : 3;  // R4 == 1: lanes that own the result
     static_assert(DH % 32 == 0, "Dh must be a multiple of 32");
+    static_assert(PD % 2 == 0, "groups must keep the h double-buffer parity");
 
-    __shared__ __attribute__((aligned(16))) uint16_t hbuf[16 * HLD];
-    __shared__ __attribute__((aligned(16))) float gbuf[16 * GLD];
+    __shared__ __attribute__((aligned(16))) uint16_t hbuf[2][16 * HLD];
 
     const int n = blockIdx.x % a.NH;
     const int b0 = (blockIdx.x / a.NH) * a.BT;
@@ -82,14 +123,15 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd_mfma_kernel(RecArgs a) {
     const int T = a.T, B = a.B;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
+    const int j = 16 * wave + lr;  // this lane's hidden unit
 
-    // ---- prologue: this wave's R fragments, resident for all T steps
-    bf16x8 rf[TPW][KC];
+    // ---- R_n fragments of this wave's G tiles, resident for all T steps
+    bf16x8 rf[G][KC];
     {
         const uint16_t *Rn = a.Rb + (long)n * DH * GD;
 #pragma unroll
-        for (int p = 0; p < TPW; ++p) {
-            const int col = 16 * (wave + NW * p) + lr;
+        for (int g = 0; g < G; ++g) {
+            const int col = g * DH + j;
 #pragma unroll
             for (int c = 0; c < KC; ++c) {
                 uint32_t w[4];
@@ -100,98 +142,207 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd_mfma_kernel(RecArgs a) {
                     const uint32_t hi = Rn[(long)(k + 1) * GD + col];
                     w[e] = lo | (hi << 16);
                 }
-                uint4 u4 = make_uint4(w[0], w[1], w[2], w[3]);
-                rf[p][c] = __builtin_bit_cast(bf16x8, u4);
+                rf[g][c] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
             }
         }
     }
-    for (int i = tid; i < 16 * DH; i += NTH) {
-        const int b = i / DH, j = i - b * DH;
-        float v = 0.f;
-        if (b < rows && a.h0) v = a.h0[(long)(b0 + b) * H + n * DH + j];
-        hbuf[b * HLD + j] = f32_to_bf16_rne(v);
-    }
-    // ---- per-thread units (b, j): state stays in registers across steps
-    float cst[UPT], hst[UPT];
-    int ub[UPT], uj[UPT];
-    bool uv[UPT];
-#pragma unroll
-    for (int q = 0; q < UPT; ++q) {
-        const int u = tid + NTH * q;
-        ub[q] = u / DH;
-        uj[q] = u - ub[q] * DH;
-        uv[q] = u < rows * DH;
-        const long o = (long)(b0 + ub[q]) * H + n * DH + uj[q];
-        cst[q] = (uv[q] && a.c0) ? a.c0[o] : 0.f;
-        hst[q] = (uv[q] && a.h0) ? a.h0[o] : 0.f;
-    }
-    float ring[PD][UPT][G];
-    auto load_gx = [&](int t, float (&dst)[UPT][G]) {
-#pragma unroll
-        for (int q = 0; q < UPT; ++q) {
-            if (uv[q] && t < T) {
-                const float *src = a.gx + ((long)t * B + b0 + ub[q]) * N + n * GD + uj[q];
-#pragma unroll
-                for (int g = 0; g < G; ++g) dst[q][g] = src[g * DH];
-            }
-        }
-    };
-#pragma unroll
-    for (int s = 0; s < PD; ++s) load_gx(s, ring[s]);
+    for (int i = tid; i < 2 * 16 * HLD; i += NW * 64) (&hbuf[0][0])[i] = 0;
     __syncthreads();
 
-    for (int t0 = 0; t0 < T; t0 += PD) {
+    // Wave-uniform base pointers plus per-lane 32-bit element offsets (B*N <
+    // 2^31 is checked on the host): every global access is SGPR-based.
+    const float *gx_tile = a.gx + (long)b0 * N + n * GD;
+    const long gx_step = (long)B * N, o_step = (long)B * H;
+    const long o_tile = (long)b0 * H + n * DH;
+    const bool has_h = a.h_seq != nullptr, has_c = CELL == kLSTM && a.c_seq != nullptr;
+    // lane roles.  R4 > 1: row slot r is batch row 4*lg + r.  R4 == 1: batch
+    // row 0 only; lane row lg is gate lg for the Gx loads, and the lanes of
+    // row OUT_ROW write results.
+    bool rv[R4], ld[R4], wr[R4];
+    unsigned go[R4], oo[R4];
+    float st[R4], hl[R4];
+#pragma unroll
+    for (int r = 0; r < R4; ++r) {
+        const int b = ROWS1 ? 0 : 4 * lg + r;
+        rv[r] = b < rows;
+        ld[r] = ROWS1 ? lg < G : rv[r];
+        wr[r] = ROWS1 ? lg == OUT_ROW : rv[r];
+        go[r] = (unsigned)(b * N + (ROWS1 ? lg * DH : 0) + j);
+        oo[r] = (unsigned)(b * H + j);
+        const float h0 = (rv[r] && a.h0) ? a.h0[o_tile + oo[r]] : 0.f;
+        const float c0 = (rv[r] && a.c0) ? a.c0[o_tile + oo[r]] : 0.f;
+        st[r] = CELL == kLSTM ? c0 : h0;
+        hl[r] = h0;
+        if (wr[r]) hbuf[0][b * HLD + j] = f32_to_bf16_rne(h0);
+    }
+
+    float bx0[PD][R4][GL], bx1[PD][R4][GL];  // Gx of the current / next group
+    float oh[PD][R4], oc[PD][R4];            // outputs of the current group
+#pragma unroll
+    for (int s = 0; s < PD; ++s)
+#pragma unroll
+        for (int r = 0; r < R4; ++r) {
+            oh[s][r] = oc[s][r] = 0.f;
+#pragma unroll
+            for (int g = 0; g < GL; ++g) bx0[s][r][g] = bx1[s][r][g] = 0.f;
+        }
+    // Gx of steps [tg, tg+PD) into dst (steps at or past T are skipped).
+    auto load_group = [&](int tg, float (&dst)[PD][R4][GL]) {
+        const float *src = gx_tile + (long)tg * gx_step;
 #pragma unroll
         for (int s = 0; s < PD; ++s) {
-            const int t = t0 + s;
-            if (t >= T) break;
-            // ---- h_{t-1} R_n for this wave's tiles
-            bf16x8 af[KC];
+            if (tg + s < T) {
 #pragma unroll
-            for (int c = 0; c < KC; ++c)
-                af[c] = *reinterpret_cast<const bf16x8 *>(hbuf + lr * HLD + 32 * c + 8 * lg);
-            f32x4 acc[TPW];
+                for (int r = 0; r < R4; ++r) {
+                    if (ld[r]) {
 #pragma unroll
-            for (int p = 0; p < TPW; ++p) acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int c = 0; c < KC; ++c)
-#pragma unroll
-                for (int p = 0; p < TPW; ++p) acc[p] = mfma_16x16x32_bf16(af[c], rf[p][c], acc[p]);
-#pragma unroll
-            for (int p = 0; p < TPW; ++p) {
-                const int col = 16 * (wave + NW * p) + lr;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) gbuf[(4 * lg + r) * GLD + col] = acc[p][r];
-            }
-            float cur[UPT][G];
-#pragma unroll
-            for (int q = 0; q < UPT; ++q)
-#pragma unroll
-                for (int g = 0; g < G; ++g) cur[q][g] = ring[s][q][g];
-            load_gx(t + PD, ring[s]);
-            __syncthreads();
-            // ---- gate update of this thread's units
-#pragma unroll
-            for (int q = 0; q < UPT; ++q) {
-                if (uv[q]) {
-                    float h, c;
-                    lstm_or_gru_unit<CELL>(gbuf + ub[q] * GLD + uj[q], DH, cur[q], cst[q],
-                                           hst[q], h, c);
-                    hbuf[ub[q] * HLD + uj[q]] = f32_to_bf16_rne(h);
-                    const long o = ((long)t * B + b0 + ub[q]) * H + n * DH + uj[q];
-                    if (a.h_seq) a.h_seq[o] = h;
-                    if (CELL == kLSTM && a.c_seq) a.c_seq[o] = c;
+                        for (int g = 0; g < GL; ++g) dst[s][r][g] = src[go[r] + g * DH];
+                    }
                 }
             }
-            __syncthreads();
+            src += gx_step;
+        }
+    };
+    // h/c outputs of steps [tg, tg+PD) held in oh/oc.
+    auto store_group = [&](int tg) {
+        float *hs = has_h ? a.h_seq + o_tile + (long)tg * o_step : nullptr;
+        float *cs = has_c ? a.c_seq + o_tile + (long)tg * o_step : nullptr;
+#pragma unroll
+        for (int s = 0; s < PD; ++s) {
+            if (tg + s < T) {
+#pragma unroll
+                for (int r = 0; r < R4; ++r) {
+                    if (wr[r]) {
+                        if (has_h) hs[oo[r]] = oh[s][r];
+                        if (has_c) cs[oo[r]] = oc[s][r];
+                    }
+                }
+            }
+            hs += o_step;
+            cs += o_step;
+        }
+    };
+    // per-lane constants of the one-pass activation (R4 == 1): row 2 of the
+    // LSTM is z (tanh), every other row a sigmoid
+    const bool tanh_row = CELL == kLSTM && lg == 2;
+    const float act_k = tanh_row ? -2.0f * kLog2e : -kLog2e;
+    const float act_m = tanh_row ? 2.0f : 1.0f;
+    const float act_d = tanh_row ? -1.0f : 0.0f;
+
+    // PD steps starting at tg, reading Gx from `use`; at the first step the
+    // previous group's outputs are stored and the next group's Gx requested.
+    // FULL: every step of the group is < T (no per-step bound checks).
+    auto run_group = [&](auto full, int tg, float (&use)[PD][R4][GL],
+                         float (&nxt)[PD][R4][GL]) {
+#pragma unroll
+        for (int s = 0; s < PD; ++s) {
+            if (!decltype(full)::value && tg + s >= T) break;
+            // first step of a group: everything still in flight was issued a
+            // whole group ago; drain it here, before the new group's requests
+            // go out, so no later use of `use` has to wait on those.
+            if (s == 0) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+            const uint16_t *hc = hbuf[s & 1];
+            uint16_t *hn = hbuf[(s + 1) & 1];
+            // A operand: only lanes of live batch rows read LDS
+            bf16x8 af[KC];
+            if (lr < rows) {
+#pragma unroll
+                for (int c = 0; c < KC; ++c)
+                    af[c] = *reinterpret_cast<const bf16x8 *>(hc + lr * HLD + 32 * c + 8 * lg);
+            } else {
+#pragma unroll
+                for (int c = 0; c < KC; ++c)
+                    af[c] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+            }
+            f32x4 acc[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < KC; ++c)
+#pragma unroll
+                for (int g = 0; g < G; ++g) acc[g] = mfma_16x16x32_bf16(af[c], rf[g][c], acc[g]);
+            if (s == 0) {
+                if (tg > 0) store_group(tg - PD);
+                load_group(tg + PD, nxt);
+            }
+            if constexpr (ROWS1) {
+                // gate sums of batch row 0 (row 0 of every accumulator) -> one
+                // register whose row g holds gate g
+                float v;
+                if constexpr (CELL == kLSTM) {
+                    const RowPair p = swap16(acc[0][0], acc[1][0]);
+                    const RowPair q = swap16(acc[2][0], acc[3][0]);
+                    v = swap32(p.a, q.a).a;
+                } else {
+                    const RowPair p = swap16(acc[0][0], acc[1][0]);
+                    v = swap32(p.a, acc[2][0]).a;  // rows r, z, n(S_n), -
+                }
+                const float x = v + use[s][0][0];
+                const float sg = rcp_fast(1.0f + __builtin_amdgcn_exp2f(x * act_k));
+                float h, c = 0.f;
+                if constexpr (CELL == kLSTM) {
+                    const float act = fmaf(sg, act_m, act_d);   // rows i, f, z, o
+                    const RowPair A = swap16(act, act);         // [i,i,z,z] [f,f,o,o]
+                    const RowPair I = swap32(A.a, A.a);         // [i..] [z..]
+                    const RowPair F = swap32(A.b, A.b);         // [f..] [o..]
+                    c = fmaf(F.a, st[0], I.a * I.b);
+                    st[0] = c;
+                    h = F.b * tanh_f(c);
+                    hl[0] = h;
+                } else {
+                    const RowPair W = swap32(sg, sg);           // rows r, u, r, u
+                    const float nn = tanh_f(fmaf(W.a, v, use[s][0][0]));  // row 2: tanh(Gx_n + r S_n)
+                    const float nn3 = swap16(nn, nn).a;         // row 3 <- row 2
+                    h = fmaf(W.a, st[0] - nn3, nn3);            // row 3: (1-u) nn + u h
+                    st[0] = h;
+                }
+                oh[s][0] = h;
+                oc[s][0] = c;
+                if (wr[0]) hn[j] = f32_to_bf16_rne(h);
+            } else {
+#pragma unroll
+                for (int r = 0; r < R4; ++r) {
+                    // A = Gx + h R (the GRU's candidate gate keeps its
+                    // recurrent sum apart: it is scaled by r before Gx_n is added)
+                    float pre[G];
+#pragma unroll
+                    for (int g = 0; g < G; ++g)
+                        pre[g] = (CELL == kGRU && g == 2) ? acc[g][r] : acc[g][r] + use[s][r][g];
+                    float c;
+                    const float h = unit_update<CELL>(pre, CELL == kGRU ? use[s][r][2] : 0.f, st[r], c);
+                    hl[r] = h;
+                    oh[s][r] = h;
+                    oc[s][r] = c;
+                    if (rv[r]) hn[(4 * lg + r) * HLD + j] = f32_to_bf16_rne(h);
+                }
+            }
+            lds_barrier();
+        }
+    };
+
+    load_group(0, bx0);
+    using Full = std::integral_constant<bool, true>;
+    using Part = std::integral_constant<bool, false>;
+    const int tfull = T / (2 * PD) * (2 * PD);
+    for (int tg = 0; tg < tfull; tg += 2 * PD) {
+        run_group(Full{}, tg, bx0, bx1);
+        run_group(Full{}, tg + PD, bx1, bx0);
+    }
+    int tlast = tfull - PD;
+    if (tfull < T) {
+        run_group(Part{}, tfull, bx0, bx1);
+        tlast = tfull;
+        if (tfull + PD < T) {
+            run_group(Part{}, tfull + PD, bx1, bx0);
+            tlast = tfull + PD;
         }
     }
+    store_group(tlast);
 #pragma unroll
-    for (int q = 0; q < UPT; ++q) {
-        if (uv[q]) {
-            const long o = (long)(b0 + ub[q]) * H + n * DH + uj[q];
-            a.hT[o] = hst[q];
-            if (CELL == kLSTM) a.cT[o] = cst[q];
+    for (int r = 0; r < R4; ++r) {
+        if (wr[r]) {
+            a.hT[o_tile + oo[r]] = CELL == kLSTM ? hl[r] : st[r];
+            if (CELL == kLSTM) a.cT[o_tile + oo[r]] = st[r];
         }
     }
 }
@@ -257,32 +408,19 @@ __global__ __launch_bounds__(256) void rec_fwd_simple_kernel(RecArgs a) {
     }
 }
 
-// Gx prefetch distance in steps: 4, or 2 when each thread owns 4 units (the
-// ring would otherwise push the Dh=128 LSTM past 256 VGPRs and spill).
-template <int UPT>
-constexpr int prefetch_steps() { return UPT >= 4 ? 2 : 4; }
-
-int mfma_waves(int cell, int Dh) {
-    if (cell == kLSTM) return 8;                 // NT = Dh/4 tiles: 8, 16, 32
-    if (Dh == 32) return 6;                      // GRU NT = 6
-    if (Dh == 64) return 12;                     // GRU NT = 12
-    return 8;                                    // GRU Dh=128: NT = 24
-}
-
-template <int CELL, int DH, int NW>
-hipError_t launch_mfma_upt(const RecPlan &p, const RecArgs &a, hipStream_t s) {
+// Rows per lane in use and the matching prefetch group length (steps).
+template <int CELL, int DH>
+hipError_t launch_mfma_rows(const RecPlan &p, const RecArgs &a, hipStream_t s) {
+    const dim3 grid(p.grid), blk(DH / 16 * 64);
     switch (p.upt) {
         case 1:
-            hipLaunchKernelGGL((rec_fwd_mfma_kernel<CELL, DH, NW, 1, prefetch_steps<1>()>), dim3(p.grid),
-                               dim3(NW * 64), 0, s, a);
+            hipLaunchKernelGGL((rec_fwd_mfma_kernel<CELL, DH, 1, 8>), grid, blk, 0, s, a);
             break;
         case 2:
-            hipLaunchKernelGGL((rec_fwd_mfma_kernel<CELL, DH, NW, 2, prefetch_steps<2>()>), dim3(p.grid),
-                               dim3(NW * 64), 0, s, a);
+            hipLaunchKernelGGL((rec_fwd_mfma_kernel<CELL, DH, 2, 4>), grid, blk, 0, s, a);
             break;
         default:
-            hipLaunchKernelGGL((rec_fwd_mfma_kernel<CELL, DH, NW, 4, prefetch_steps<4>()>), dim3(p.grid),
-                               dim3(NW * 64), 0, s, a);
+            hipLaunchKernelGGL((rec_fwd_mfma_kernel<CELL, DH, 4, 2>), grid, blk, 0, s, a);
             break;
     }
     return hipGetLastError();
@@ -290,11 +428,10 @@ hipError_t launch_mfma_upt(const RecPlan &p, const RecArgs &a, hipStream_t s) {
 
 template <int CELL>
 hipError_t launch_mfma(const RecPlan &p, const RecArgs &a, hipStream_t s) {
-    constexpr bool L = CELL == kLSTM;
     switch (a.Dh) {
-        case 32: return launch_mfma_upt<CELL, 32, L ? 8 : 6>(p, a, s);
-        case 64: return launch_mfma_upt<CELL, 64, L ? 8 : 12>(p, a, s);
-        case 128: return launch_mfma_upt<CELL, 128, 8>(p, a, s);
+        case 32: return launch_mfma_rows<CELL, 32>(p, a, s);
+        case 64: return launch_mfma_rows<CELL, 64>(p, a, s);
+        case 128: return launch_mfma_rows<CELL, 128>(p, a, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -318,11 +455,9 @@ RecPlan plan_rec(int cell, int T, int B, int NH, int Dh, bool bf16, int num_cu,
         p.BT = bt;
         p.nbt = (B + bt - 1) / bt;
         p.grid = NH * p.nbt;
-        p.waves = mfma_waves(cell, Dh);
+        p.waves = Dh / 16;
         p.threads = p.waves * 64;
-        const int units = bt * Dh;
-        p.upt = (units + p.threads - 1) / p.threads;
-        if (p.upt == 3) p.upt = 4;
+        p.upt = bt >= 4 ? 4 : bt == 3 ? 4 : bt;  // register row slots per lane
         p.lds = 0;
         return p;
     }
