@@ -15,9 +15,11 @@ using namespace rnn355;
 
 namespace {
 
-// Workspace: [0, kHeader) status words and step counters, then the regions
-// of the operation, each 256-byte aligned.
+// Workspace: [0, kHeader) status word (word 0) and per-group step counters
+// (words 64..), then the h exchange slots of the multi-CU kernel, then the
+// operation's own regions, each 256-byte aligned.
 constexpr size_t kHeader = 4096;
+constexpr size_t kCounterWord = 64;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
@@ -36,6 +38,12 @@ int gates_of_op(rnn_op op) {
 }
 
 int cell_of_op(rnn_op op) { return gates_of_op(op) == 4 ? kLSTM : kGRU; }
+
+// Exchange slots: [groups][2][BT][Dh] bf16 with groups = NH * ceil(B/BT) and
+// BT <= 16, so groups * BT <= NH * (B + 15).
+size_t xchg_bytes(const rnn_dims *d) {
+    return align_up(2u * 2u * (size_t)d->NH * (d->B + 15) * d->Dh);
+}
 
 size_t gx_bytes(const rnn_dims *d, int G) {
     return align_up(sizeof(float) * (size_t)d->T * d->B * d->NH * G * d->Dh);
@@ -58,9 +66,48 @@ int device_cus() {
     return cache[dev];
 }
 
-int bt_override() {
-    const char *e = getenv("RNN355_REC_BT");
+// Plan overrides for tile sweeps (rows per workgroup, workgroups per head).
+int env_int(const char *name) {
+    const char *e = getenv(name);
     return e ? atoi(e) : 0;
+}
+int bt_override() { return env_int("RNN355_REC_BT"); }
+int k_override() { return env_int("RNN355_REC_K"); }
+// Polls of a multi-CU step wait before it is declared lost (~4 s by default;
+// tests lower it to force the time-out path).
+unsigned spin_limit() {
+    const int v = env_int("RNN355_SPIN_LIMIT");
+    return v > 0 ? (unsigned)v : (1u << 22);
+}
+
+// Which recurrent kernel serves a shape: the one-CU MFMA kernel (bf16, Dh in
+// {32, 64, 128}), the multi-CU kernel (bf16, Dh >= 256, Dh % 128 == 0), or
+// the LDS kernel (f32, other shapes whose R fits 64 KiB of LDS).
+struct Choice {
+    RecPlan rec;
+    McPlan mc;
+    bool use_mc;
+    bool ok;
+};
+
+Choice choose(int cell, const rnn_dims *d, rnn_dtype dt, int num_cu) {
+    Choice c{};
+    const bool bf16 = dt == RNN_BF16;
+    c.rec = plan_rec(cell, d->T, d->B, d->NH, d->Dh, bf16, num_cu, bt_override());
+    if (c.rec.kind == kRecMfma) {
+        c.ok = true;
+        return c;
+    }
+    if (bf16) {
+        c.mc = plan_mc(cell, d->B, d->NH, d->Dh, num_cu, bt_override(), k_override());
+        if (c.mc.ok) {
+            c.use_mc = true;
+            c.ok = true;
+            return c;
+        }
+    }
+    c.ok = c.rec.kind != kRecNone;
+    return c;
 }
 
 bool gemm_shape_ok(int K, int N, rnn_dtype dt) {
@@ -93,21 +140,35 @@ rnn_status input_proj(int M, int K, int N, rnn_dtype dt, const void *x, const vo
 
 rnn_status rec_fwd(int cell, const rnn_dims *d, rnn_dtype dt, const float *gx, const void *R,
                    const float *h0, const float *c0, float *h_seq, float *c_seq, float *hT,
-                   float *cT, hipStream_t s) {
-    const RecPlan p = plan_rec(cell, d->T, d->B, d->NH, d->Dh, dt == RNN_BF16, device_cus(),
-                               bt_override());
-    if (p.kind == kRecNone) return RNN_ERR_UNSUPPORTED;
+                   float *cT, void *ws, hipStream_t s) {
+    const Choice ch = choose(cell, d, dt, device_cus());
+    if (!ch.ok) return RNN_ERR_UNSUPPORTED;
     RecArgs a{};
-    a.T = d->T; a.B = d->B; a.NH = d->NH; a.Dh = d->Dh; a.BT = p.BT;
+    a.T = d->T; a.B = d->B; a.NH = d->NH; a.Dh = d->Dh;
     a.gx = gx;
     a.Rb = dt == RNN_BF16 ? (const uint16_t *)R : nullptr;
     a.Rf = dt == RNN_F32 ? (const float *)R : nullptr;
     a.h0 = h0; a.c0 = c0; a.h_seq = h_seq; a.c_seq = c_seq; a.hT = hT; a.cT = cT;
-    return launch_rec_fwd(cell, p, a, dt == RNN_BF16, s) == hipSuccess ? RNN_OK : RNN_ERR_HIP;
+    hipError_t e;
+    if (ch.use_mc) {
+        a.BT = ch.mc.BT;
+        McArgs m{};
+        m.r = a;
+        m.K = ch.mc.K; m.KS = ch.mc.ks; m.NB = ch.mc.nb;
+        m.flag = (unsigned *)ws;
+        m.cnt = (unsigned *)ws + kCounterWord;
+        m.xg = (uint16_t *)((char *)ws + kHeader);
+        m.spin_limit = spin_limit();
+        e = launch_rec_mc(cell, ch.mc, m, s);
+    } else {
+        a.BT = ch.rec.BT;
+        e = launch_rec_fwd(cell, ch.rec, a, dt == RNN_BF16, s);
+    }
+    return e == hipSuccess ? RNN_OK : RNN_ERR_HIP;
 }
 
 bool rec_supported(int cell, const rnn_dims *d, rnn_dtype dt) {
-    return plan_rec(cell, d->T, d->B, d->NH, d->Dh, dt == RNN_BF16, 256, 0).kind != kRecNone;
+    return choose(cell, d, dt, device_cus()).ok;
 }
 
 }  // namespace
@@ -132,10 +193,10 @@ size_t rnn_workspace_size(rnn_op op, const rnn_dims *d, rnn_dtype dt) {
     switch (op) {
         case RNN_OP_FWD_LSTM:
         case RNN_OP_FWD_GRU:
-            return kHeader + gx_bytes(d, G);
+            return kHeader + xchg_bytes(d) + gx_bytes(d, G);
         case RNN_OP_REC_LSTM:
         case RNN_OP_REC_GRU:
-            return kHeader;
+            return kHeader + xchg_bytes(d);
         default:
             return 0;
     }
@@ -146,12 +207,24 @@ rnn_status rnn_plan_describe(rnn_op op, const rnn_dims *d, rnn_dtype dt, char *b
     if (!dims_ok(d) || !dtype_ok(dt) || !buf || len == 0) return RNN_ERR_INVALID_ARG;
     if (op < RNN_OP_FWD_LSTM || op > RNN_OP_REC_GRU) return RNN_ERR_INVALID_ARG;
     const int cell = cell_of_op(op);
-    const RecPlan p = plan_rec(cell, d->T, d->B, d->NH, d->Dh, dt == RNN_BF16, device_cus(),
-                               bt_override());
-    const char *k = p.kind == kRecMfma ? "mfma_resident_R" : p.kind == kRecSimple ? "lds_simple" : "none";
-    snprintf(buf, len, "rec_kernel=%s rows_per_wg=%d wg=%d threads=%d wg_per_head_row_tile=1 units_per_thread=%d",
-             k, p.BT, p.grid, p.threads, p.upt);
-    return p.kind == kRecNone ? RNN_ERR_UNSUPPORTED : RNN_OK;
+    const Choice ch = choose(cell, d, dt, device_cus());
+    if (!ch.ok) {
+        snprintf(buf, len, "rec_kernel=none");
+        return RNN_ERR_UNSUPPORTED;
+    }
+    if (ch.use_mc) {
+        const McPlan &p = ch.mc;
+        snprintf(buf, len,
+                 "rec_kernel=mfma_multi_cu rows_per_wg=%d wg=%d threads=%d wg_per_head_row_tile=%d "
+                 "units_per_wg=%d k_splits=%d",
+                 p.BT, p.grid, p.threads, p.K, p.nb * 16, p.ks);
+    } else {
+        const RecPlan &p = ch.rec;
+        snprintf(buf, len,
+                 "rec_kernel=%s rows_per_wg=%d wg=%d threads=%d wg_per_head_row_tile=1 units_per_thread=%d",
+                 p.kind == kRecMfma ? "mfma_resident_R" : "lds_simple", p.BT, p.grid, p.threads, p.upt);
+    }
+    return RNN_OK;
 }
 
 rnn_status rnn_input_proj(int M, int K, int N, rnn_dtype dt, const void *x, const void *W,
@@ -173,7 +246,7 @@ rnn_status rnn_rec_lstm(const rnn_dims *d, rnn_dtype dt, const float *gx, const 
         if (!aligned16(p)) return RNN_ERR_INVALID_ARG;
     if (!rec_supported(kLSTM, d, dt)) return RNN_ERR_UNSUPPORTED;
     if (!ws || ws_bytes < rnn_workspace_size(RNN_OP_REC_LSTM, d, dt)) return RNN_ERR_WORKSPACE;
-    return rec_fwd(kLSTM, d, dt, gx, R, h0, c0, h_seq, c_seq, hT, cT, stream);
+    return rec_fwd(kLSTM, d, dt, gx, R, h0, c0, h_seq, c_seq, hT, cT, ws, stream);
 }
 
 rnn_status rnn_rec_gru(const rnn_dims *d, rnn_dtype dt, const float *gx, const void *R,
@@ -185,7 +258,7 @@ rnn_status rnn_rec_gru(const rnn_dims *d, rnn_dtype dt, const float *gx, const v
         if (!aligned16(p)) return RNN_ERR_INVALID_ARG;
     if (!rec_supported(kGRU, d, dt)) return RNN_ERR_UNSUPPORTED;
     if (!ws || ws_bytes < rnn_workspace_size(RNN_OP_REC_GRU, d, dt)) return RNN_ERR_WORKSPACE;
-    return rec_fwd(kGRU, d, dt, gx, R, h0, nullptr, h_seq, nullptr, hT, nullptr, stream);
+    return rec_fwd(kGRU, d, dt, gx, R, h0, nullptr, h_seq, nullptr, hT, nullptr, ws, stream);
 }
 
 rnn_status rnn_fwd_lstm(const rnn_dims *d, rnn_dtype dt, const void *x, const void *W,
@@ -199,10 +272,10 @@ rnn_status rnn_fwd_lstm(const rnn_dims *d, rnn_dtype dt, const void *x, const vo
     const int N = d->NH * 4 * d->Dh;
     if (!gemm_shape_ok(d->Din, N, dt) || !rec_supported(kLSTM, d, dt)) return RNN_ERR_UNSUPPORTED;
     if (!ws || ws_bytes < rnn_workspace_size(RNN_OP_FWD_LSTM, d, dt)) return RNN_ERR_WORKSPACE;
-    float *gx = (float *)((char *)ws + kHeader);
+    float *gx = (float *)((char *)ws + kHeader + xchg_bytes(d));
     rnn_status st = input_proj(d->T * d->B, d->Din, N, dt, x, W, b, gx, (uint32_t *)ws, stream);
     if (st != RNN_OK) return st;
-    return rec_fwd(kLSTM, d, dt, gx, R, h0, c0, h_seq, c_seq, hT, cT, stream);
+    return rec_fwd(kLSTM, d, dt, gx, R, h0, c0, h_seq, c_seq, hT, cT, ws, stream);
 }
 
 rnn_status rnn_fwd_gru(const rnn_dims *d, rnn_dtype dt, const void *x, const void *W,
@@ -215,10 +288,10 @@ rnn_status rnn_fwd_gru(const rnn_dims *d, rnn_dtype dt, const void *x, const voi
     const int N = d->NH * 3 * d->Dh;
     if (!gemm_shape_ok(d->Din, N, dt) || !rec_supported(kGRU, d, dt)) return RNN_ERR_UNSUPPORTED;
     if (!ws || ws_bytes < rnn_workspace_size(RNN_OP_FWD_GRU, d, dt)) return RNN_ERR_WORKSPACE;
-    float *gx = (float *)((char *)ws + kHeader);
+    float *gx = (float *)((char *)ws + kHeader + xchg_bytes(d));
     rnn_status st = input_proj(d->T * d->B, d->Din, N, dt, x, W, b, gx, (uint32_t *)ws, stream);
     if (st != RNN_OK) return st;
-    return rec_fwd(kGRU, d, dt, gx, R, h0, nullptr, h_seq, nullptr, hT, nullptr, stream);
+    return rec_fwd(kGRU, d, dt, gx, R, h0, nullptr, h_seq, nullptr, hT, nullptr, ws, stream);
 }
 
 rnn_status rnn_bwd_lstm(const rnn_dims *d, rnn_dtype dt, const void *x, const void *W,

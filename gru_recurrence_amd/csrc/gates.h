@@ -1,0 +1,102 @@
+// gates.h -- the cell update of the recurrent kernels (LSTM / GRU), applied
+// to the MFMA accumulators of one wave.
+//
+// Accumulator layout (v_mfma_f32_16x16x32_bf16, one 16-unit block, G gate
+// tiles): acc[g][r] of lane l is the recurrent sum h_{t-1} R of gate g for
+// unit l%16 and batch row 4*(l/16) + r.
+#pragma once
+
+#include "common.h"
+
+namespace rnn355 {
+
+// Gate update of one unit from its pre-activations.  LSTM: a[g] = Gx + h R
+// for g = i,f,z,o and st = c.  GRU: a[0..1] = Gx + S for r,z, a[2] = S_n,
+// gxn = Gx_n and st = h_{t-1}.
+template <int CELL>
+__device__ __forceinline__ float unit_update(const float *a, float gxn, float &st, float &c_out) {
+    if (CELL == kLSTM) {
+        const float ig = sigmoid_f(a[0]), fg = sigmoid_f(a[1]);
+        const float zg = tanh_f(a[2]), og = sigmoid_f(a[3]);
+        const float c = fmaf(fg, st, ig * zg);
+        st = c;
+        c_out = c;
+        return og * tanh_f(c);
+    } else {
+        const float r = sigmoid_f(a[0]), u = sigmoid_f(a[1]);
+        const float nn = tanh_f(fmaf(r, a[2], gxn));
+        const float h = fmaf(u, st - nn, nn);  // (1-u)*nn + u*h_{t-1}
+        st = h;
+        c_out = 0.f;
+        return h;
+    }
+}
+
+// The cell update of all row slots of one lane.
+//   gx[r][.]: for R4 > 1 the G gate inputs Gx of row slot r; for R4 == 1 a
+//             single value, the Gx of gate l/16 (the lane's row, see below).
+//   st[r]:    cell state c (LSTM) or h (GRU), updated in place.
+//   hl[r]:    last h (LSTM only; GRU keeps h in st).
+//   h[r], c[r]: this step's outputs.
+// R4 == 1 (only batch row 0 is live, in lanes 0..15): three cross-row swaps
+// lay the G gate sums of a unit out as the rows of one register (gate g in
+// lanes 16g..16g+15), one exp + rcp pass activates all gates (tanh(x) =
+// 2*sigmoid(2x) - 1 on the LSTM's z row), and swaps hand every lane all the
+// gates back.  The LSTM result is then valid in every row (row 0 writes it),
+// the GRU result in row 3 (row 3 writes it).
+template <int CELL, int R4, int GL>
+__device__ __forceinline__ void gate_update(const f32x4 (&acc)[CellTraits<CELL>::G],
+                                            const float (&gx)[R4][GL], float (&st)[R4],
+                                            float (&hl)[R4], float (&h)[R4], float (&c)[R4]) {
+    constexpr int G = CellTraits<CELL>::G;
+    if constexpr (R4 == 1) {
+        const int row = (threadIdx.x & 63) >> 4;
+        const bool tanh_row = CELL == kLSTM && row == 2;
+        const float act_k = tanh_row ? -2.0f * kLog2e : -kLog2e;
+        float v;
+        if constexpr (CELL == kLSTM) {
+            const RowPair p = swap16(acc[0][0], acc[1][0]);
+            const RowPair q = swap16(acc[2][0], acc[3][0]);
+            v = swap32(p.a, q.a).a;              // rows: i, f, z, o
+        } else {
+            const RowPair p = swap16(acc[0][0], acc[1][0]);
+            v = swap32(p.a, acc[2][0]).a;        // rows: r, z, S_n, -
+        }
+        const float x = v + gx[0][0];
+        const float sg = rcp_fast(1.0f + __builtin_amdgcn_exp2f(x * act_k));
+        if constexpr (CELL == kLSTM) {
+            const float act = tanh_row ? fmaf(sg, 2.0f, -1.0f) : sg;
+            const RowPair A = swap16(act, act);  // [i,i,z,z] [f,f,o,o]
+            const RowPair I = swap32(A.a, A.a);  // [i..] [z..]
+            const RowPair F = swap32(A.b, A.b);  // [f..] [o..]
+            const float cn = fmaf(F.a, st[0], I.a * I.b);
+            st[0] = cn;
+            c[0] = cn;
+            h[0] = F.b * tanh_f(cn);
+            hl[0] = h[0];
+        } else {
+            const RowPair W = swap32(sg, sg);                    // rows r, u, r, u
+            const float nn = tanh_f(fmaf(W.a, v, gx[0][0]));     // row 2: tanh(Gx_n + r S_n)
+            const float nn3 = swap16(nn, nn).a;                  // row 3 <- row 2
+            const float hn = fmaf(W.a, st[0] - nn3, nn3);        // row 3: (1-u) nn + u h
+            st[0] = hn;
+            h[0] = hn;
+            c[0] = 0.f;
+        }
+        (void)G;
+    } else {
+#pragma unroll
+        for (int r = 0; r < R4; ++r) {
+            // A = Gx + h R (the GRU's candidate gate keeps its recurrent sum
+            // apart: it is scaled by r before Gx_n is added)
+            float pre[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+                pre[g] = (CELL == kGRU && g == 2) ? acc[g][r] : acc[g][r] + gx[r][g];
+            h[r] = unit_update<CELL>(pre, CELL == kGRU ? gx[r][2] : 0.f, st[r], c[r]);
+            hl[r] = h[r];
+        }
+    }
+}
+
+}  // namespace rnn355

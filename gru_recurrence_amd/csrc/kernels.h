@@ -73,4 +73,35 @@ RecPlan plan_rec(int cell, int T, int B, int NH, int Dh, bool bf16, int num_cu,
 hipError_t launch_rec_fwd(int cell, const RecPlan &p, const RecArgs &a, bool bf16,
                           hipStream_t s);
 
+// Multi-CU forward recurrence (rec_mc.hip).
+struct McPlan {
+    int ok;
+    int K;        // workgroups per (head, batch tile)
+    int nb;       // 16-unit blocks per workgroup
+    int ks;       // waves per unit block (k-range splits)
+    int kcw;      // k-chunks of 32 per wave (4 or 8)
+    int threads;  // per workgroup
+    int BT;       // batch rows per group
+    int r4;       // register row slots in use
+    int groups;   // (head, batch tile) groups
+    int grid;     // groups * K
+    size_t lds;   // dynamic LDS bytes
+};
+
+struct McArgs {
+    RecArgs r;
+    int K, KS, NB;
+    uint16_t *xg;    // exchange slots [groups][2][BT][Dh] bf16
+    unsigned *cnt;   // per-group step counters (cleared before every launch)
+    unsigned *flag;  // time-out / abort word (cleared before every launch)
+    unsigned spin_limit;  // polls of the group counter before a wait is declared lost
+};
+
+// Plan for heads of Dh >= 256, Dh % 128 == 0; ok == 0 if none fits the
+// chip (every workgroup must be resident at once).  Pure host function.
+McPlan plan_mc(int cell, int B, int NH, int Dh, int num_cu, int bt_override, int k_override);
+
+// Clears the counters and the abort word, then launches cooperatively.
+hipError_t launch_rec_mc(int cell, const McPlan &p, const McArgs &m, hipStream_t s);
+
 }  // namespace rnn355

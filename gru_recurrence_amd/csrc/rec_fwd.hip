@@ -28,6 +28,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "gates.h"
 #include "kernels.h"
 
 namespace rnn355 {
@@ -60,28 +61,6 @@ __device__ __forceinline__ void lstm_or_gru_unit(const float *gpre, int DH, cons
         hst = h;
         h_out = h;
         c_out = 0.f;
-    }
-}
-
-// Gate update of one unit from its pre-activations.  LSTM: a[g] = Gx + h R
-// for g = i,f,z,o and st = c.  GRU: a[0..1] = Gx + S for r,z, a[2] = S_n,
-// gxn = Gx_n and st = h_{t-1}.
-template <int CELL>
-__device__ __forceinline__ float unit_update(const float *a, float gxn, float &st, float &c_out) {
-    if (CELL == kLSTM) {
-        const float ig = sigmoid_f(a[0]), fg = sigmoid_f(a[1]);
-        const float zg = tanh_f(a[2]), og = sigmoid_f(a[3]);
-        const float c = fmaf(fg, st, ig * zg);
-        st = c;
-        c_out = c;
-        return og * tanh_f(c);
-    } else {
-        const float r = sigmoid_f(a[0]), u = sigmoid_f(a[1]);
-        const float nn = tanh_f(fmaf(r, a[2], gxn));
-        const float h = fmaf(u, st - nn, nn);  // (1-u)*nn + u*h_{t-1}
-        st = h;
-        c_out = 0.f;
-        return h;
     }
 }
 
@@ -144,6 +123,9 @@ __global__ __launch_bounds__(DH / 16 * 64) void rec_fwd_mfma_kernel(RecArgs a) {
                 }
                 rf[g][c] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
             }
+            // drain this gate's loads before the next gate's are issued: all
+            // of them in flight at once would need a register each
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         }
     }
     for (int i = tid; i < 2 * 16 * HLD; i += NW * 64) (&hbuf[0][0])[i] = 0;
@@ -222,13 +204,6 @@ __global__ __launch_bounds__(DH / 16 * 64) void rec_fwd_mfma_kernel(RecArgs a) {
             cs += o_step;
         }
     };
-    // per-lane constants of the one-pass activation (R4 == 1): row 2 of the
-    // LSTM is z (tanh), every other row a sigmoid
-    const bool tanh_row = CELL == kLSTM && lg == 2;
-    const float act_k = tanh_row ? -2.0f * kLog2e : -kLog2e;
-    const float act_m = tanh_row ? 2.0f : 1.0f;
-    const float act_d = tanh_row ? -1.0f : 0.0f;
-
     // PD steps starting at tg, reading Gx from `use`; at the first step the
     // previous group's outputs are stored and the next group's Gx requested.
     // FULL: every step of the group is < T (no per-step bound checks).
@@ -265,56 +240,13 @@ __global__ __launch_bounds__(DH / 16 * 64) void rec_fwd_mfma_kernel(RecArgs a) {
                 if (tg > 0) store_group(tg - PD);
                 load_group(tg + PD, nxt);
             }
-            if constexpr (ROWS1) {
-                // gate sums of batch row 0 (row 0 of every accumulator) -> one
-                // register whose row g holds gate g
-                float v;
-                if constexpr (CELL == kLSTM) {
-                    const RowPair p = swap16(acc[0][0], acc[1][0]);
-                    const RowPair q = swap16(acc[2][0], acc[3][0]);
-                    v = swap32(p.a, q.a).a;
-                } else {
-                    const RowPair p = swap16(acc[0][0], acc[1][0]);
-                    v = swap32(p.a, acc[2][0]).a;  // rows r, z, n(S_n), -
-                }
-                const float x = v + use[s][0][0];
-                const float sg = rcp_fast(1.0f + __builtin_amdgcn_exp2f(x * act_k));
-                float h, c = 0.f;
-                if constexpr (CELL == kLSTM) {
-                    const float act = fmaf(sg, act_m, act_d);   // rows i, f, z, o
-                    const RowPair A = swap16(act, act);         // [i,i,z,z] [f,f,o,o]
-                    const RowPair I = swap32(A.a, A.a);         // [i..] [z..]
-                    const RowPair F = swap32(A.b, A.b);         // [f..] [o..]
-                    c = fmaf(F.a, st[0], I.a * I.b);
-                    st[0] = c;
-                    h = F.b * tanh_f(c);
-                    hl[0] = h;
-                } else {
-                    const RowPair W = swap32(sg, sg);           // rows r, u, r, u
-                    const float nn = tanh_f(fmaf(W.a, v, use[s][0][0]));  // row 2: tanh(Gx_n + r S_n)
-                    const float nn3 = swap16(nn, nn).a;         // row 3 <- row 2
-                    h = fmaf(W.a, st[0] - nn3, nn3);            // row 3: (1-u) nn + u h
-                    st[0] = h;
-                }
-                oh[s][0] = h;
-                oc[s][0] = c;
-                if (wr[0]) hn[j] = f32_to_bf16_rne(h);
-            } else {
+            float h[R4], c[R4];
+            gate_update<CELL, R4>(acc, use[s], st, hl, h, c);
 #pragma unroll
-                for (int r = 0; r < R4; ++r) {
-                    // A = Gx + h R (the GRU's candidate gate keeps its
-                    // recurrent sum apart: it is scaled by r before Gx_n is added)
-                    float pre[G];
-#pragma unroll
-                    for (int g = 0; g < G; ++g)
-                        pre[g] = (CELL == kGRU && g == 2) ? acc[g][r] : acc[g][r] + use[s][r][g];
-                    float c;
-                    const float h = unit_update<CELL>(pre, CELL == kGRU ? use[s][r][2] : 0.f, st[r], c);
-                    hl[r] = h;
-                    oh[s][r] = h;
-                    oc[s][r] = c;
-                    if (rv[r]) hn[(4 * lg + r) * HLD + j] = f32_to_bf16_rne(h);
-                }
+            for (int r = 0; r < R4; ++r) {
+                oh[s][r] = h[r];
+                oc[s][r] = c[r];
+                if (wr[r]) hn[(ROWS1 ? 0 : 4 * lg + r) * HLD + j] = f32_to_bf16_rne(h[r]);
             }
             lds_barrier();
         }

@@ -1,0 +1,312 @@
+// rec_mc.hip -- forward recurrence for heads whose R block does not fit one
+// compute unit: the hidden units of one head are split over K workgroups
+// (one per CU, co-resident by cooperative launch) that swap h_t through
+// global memory at every step.
+//
+// FlashRNN (arXiv 2412.07752, abstract) stresses that its CUDA kernels reach
+// much larger hidden sizes than its Triton ones; the blog post
+// (blog.hotdry.top 2025-09-21, the paragraphs on the step dependency and on
+// keeping R in registers) explains the price: R stays on chip, so a large R
+// must be spread over several processors that then meet once per step.
+//
+// Per workgroup: U = Dh/K units, NB = U/16 unit blocks, and KS waves per unit
+// block, each holding KCW = Dh/(32*KS) k-chunks of the MFMA B fragments of
+// its block's G gate tiles (G * KCW * 4 VGPRs, R never re-read).  Per step:
+//   1. A fragments of h_{t-1} (bf16, LDS, full Dh) for the wave's k-range;
+//   2. MFMAs -> partial gate sums; waves with ks > 0 hand theirs to the
+//      ks = 0 wave of the block through LDS;
+//   3. the ks = 0 waves apply the cell update (same code as the one-CU
+//      kernel) and publish h_t (bf16) into the group's exchange slot;
+//   4. group barrier: every wave fences (agent-scope release), thread 0
+//      bumps the group counter and polls it until all K members arrived,
+//      then every wave fences (acquire).  The poll is bounded: on time-out the
+//      workgroup raises the abort word, which stops every member;
+//   5. the h/c outputs of step t are stored and Gx of step t+1 requested --
+//      issued right after the barrier so they drain during the next step --
+//      and the full h_t is copied from the exchange slot into LDS.
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+#include "gates.h"
+#include "kernels.h"
+
+namespace rnn355 {
+
+namespace {
+
+template <int CELL, int KCW, int R4>
+__global__ __launch_bounds__(512) void rec_fwd_mc_kernel(McArgs m) {
+    constexpr int G = CellTraits<CELL>::G;
+    constexpr bool ROWS1 = R4 == 1;
+    constexpr int GL = ROWS1 ? 1 : G;
+    constexpr int OUT_ROW = CELL == kLSTM ? 0 : 3;
+    const RecArgs &a = m.r;
+    const int Dh = a.Dh, K = m.K, KS = m.KS, NB = m.NB;
+    const int U = NB * 16, GD = G * Dh, H = a.NH * Dh, N = a.NH * GD, HLD = Dh + 8;
+    const int T = a.T, B = a.B;
+
+    extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+    uint16_t *hbuf = smem;                                    // [16][HLD] bf16
+    float *red = reinterpret_cast<float *>(smem + 16 * HLD);  // [KS-1][NB][G][16][16]
+    __shared__ int s_abort;
+
+    const int group = blockIdx.x / K, member = blockIdx.x - group * K;
+    const int n = group % a.NH;
+    const int b0 = (group / a.NH) * a.BT;
+    const int rows = min(a.BT, B - b0);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int blk = wave / KS, ks = wave - blk * KS;
+    const bool gate_wave = ks == 0;
+    const int j = member * U + blk * 16 + lr;  // this lane's hidden unit
+    const int kc0 = ks * KCW;                  // first k-chunk of this wave
+
+    bf16x8 rf[G][KCW];
+    {
+        const uint16_t *Rn = a.Rb + (long)n * Dh * GD;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int col = g * Dh + j;
+#pragma unroll
+            for (int c = 0; c < KCW; ++c) {
+                uint32_t w[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int k = 32 * (kc0 + c) + 8 * lg + 2 * e;
+                    const uint32_t lo = Rn[(long)k * GD + col];
+                    const uint32_t hi = Rn[(long)(k + 1) * GD + col];
+                    w[e] = lo | (hi << 16);
+                }
+                rf[g][c] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+            }
+            // drain this gate's loads before the next gate's are issued: all
+            // of them in flight at once would need a register each
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        }
+    }
+    const int nthr = blockDim.x;
+    for (int i = tid; i < 16 * HLD; i += nthr) {
+        const int b = i / HLD, k = i - b * HLD;
+        float v = 0.f;
+        if (b < rows && k < Dh && a.h0) v = a.h0[(long)(b0 + b) * H + n * Dh + k];
+        hbuf[i] = f32_to_bf16_rne(v);
+    }
+    if (tid == 0) s_abort = 0;
+
+    // lanes of the ks = 0 waves own units (same roles as the one-CU kernel)
+    const float *gx_tile = a.gx + (long)b0 * N + n * GD;
+    const long gx_step = (long)B * N, o_step = (long)B * H;
+    const long o_tile = (long)b0 * H + n * Dh;
+    const bool has_h = a.h_seq != nullptr, has_c = CELL == kLSTM && a.c_seq != nullptr;
+    bool rv[R4], ld[R4], wr[R4];
+    unsigned go[R4], oo[R4];
+    float st[R4], hl[R4], gxr[R4][GL], ph[R4], pc[R4];
+#pragma unroll
+    for (int r = 0; r < R4; ++r) {
+        const int b = ROWS1 ? 0 : 4 * lg + r;
+        rv[r] = b < rows;
+        ld[r] = gate_wave && (ROWS1 ? lg < G : rv[r]);
+        wr[r] = gate_wave && (ROWS1 ? lg == OUT_ROW : rv[r]);
+        go[r] = (unsigned)(b * N + (ROWS1 ? lg * Dh : 0) + j);
+        oo[r] = (unsigned)(b * H + j);
+        const float h0 = (rv[r] && a.h0) ? a.h0[o_tile + oo[r]] : 0.f;
+        const float c0 = (rv[r] && a.c0) ? a.c0[o_tile + oo[r]] : 0.f;
+        st[r] = CELL == kLSTM ? c0 : h0;
+        hl[r] = h0;
+        ph[r] = pc[r] = 0.f;
+#pragma unroll
+        for (int g = 0; g < GL; ++g) gxr[r][g] = 0.f;
+    }
+    auto load_gx = [&](int t) {
+        const float *src = gx_tile + (long)t * gx_step;
+#pragma unroll
+        for (int r = 0; r < R4; ++r)
+            if (ld[r])
+#pragma unroll
+                for (int g = 0; g < GL; ++g) gxr[r][g] = src[go[r] + g * Dh];
+    };
+    load_gx(0);
+    __syncthreads();
+
+    uint16_t *xg_group = m.xg + (long)group * 2 * a.BT * Dh;  // [2][BT][Dh]
+    unsigned *cnt = m.cnt + group;
+    int t = 0;
+    for (; t < T; ++t) {
+        bf16x8 af[KCW];
+        if (lr < rows) {
+#pragma unroll
+            for (int c = 0; c < KCW; ++c)
+                af[c] = *reinterpret_cast<const bf16x8 *>(hbuf + lr * HLD + 32 * (kc0 + c) + 8 * lg);
+        } else {
+#pragma unroll
+            for (int c = 0; c < KCW; ++c) af[c] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+        }
+        f32x4 acc[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < KCW; ++c)
+#pragma unroll
+            for (int g = 0; g < G; ++g) acc[g] = mfma_16x16x32_bf16(af[c], rf[g][c], acc[g]);
+
+        if (KS > 1) {
+            // partial sums of the other k-ranges -> the ks = 0 wave of the block
+            if (!gate_wave) {
+                float *dst = red + ((long)(ks - 1) * NB + blk) * G * 256;
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dst[(g * 16 + 4 * lg + r) * 16 + lr] = acc[g][r];
+            }
+            __syncthreads();
+            if (gate_wave) {
+                for (int k2 = 1; k2 < KS; ++k2) {
+                    const float *src = red + ((long)(k2 - 1) * NB + blk) * G * 256;
+#pragma unroll
+                    for (int g = 0; g < G; ++g)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc[g][r] += src[(g * 16 + 4 * lg + r) * 16 + lr];
+                }
+            }
+        }
+        uint16_t *slot = xg_group + (long)(t & 1) * a.BT * Dh;
+        if (gate_wave) {
+            float h[R4], c[R4];
+            gate_update<CELL, R4>(acc, gxr, st, hl, h, c);
+#pragma unroll
+            for (int r = 0; r < R4; ++r) {
+                ph[r] = h[r];
+                pc[r] = c[r];
+                if (wr[r]) slot[(ROWS1 ? 0 : 4 * lg + r) * Dh + j] = f32_to_bf16_rne(h[r]);
+            }
+        }
+        // ---- group barrier (agent scope)
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __syncthreads();
+        if (tid == 0) {
+            __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const unsigned want = (unsigned)K * (unsigned)(t + 1);
+            unsigned spins = 0;
+            while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < want) {
+                if ((++spins & 255u) == 0 &&
+                    __hip_atomic_load(m.flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+                    s_abort = 1;
+                    break;
+                }
+                if (spins >= m.spin_limit) {
+                    __hip_atomic_store(m.flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    s_abort = 1;
+                    break;
+                }
+            }
+        }
+        __syncthreads();
+        if (s_abort) break;
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        // ---- outputs of step t, Gx of step t+1, full h_t into LDS
+        if (gate_wave) {
+            const long base = o_tile + (long)t * o_step;
+#pragma unroll
+            for (int r = 0; r < R4; ++r) {
+                if (wr[r]) {
+                    if (has_h) a.h_seq[base + oo[r]] = ph[r];
+                    if (has_c) a.c_seq[base + oo[r]] = pc[r];
+                }
+            }
+            if (t + 1 < T) load_gx(t + 1);
+        }
+        {
+            const int chunks = rows * (Dh / 8);  // 16-byte pieces of h_t
+            for (int i = tid; i < chunks; i += nthr) {
+                const int b = i / (Dh / 8), k8 = (i - b * (Dh / 8)) * 8;
+                *reinterpret_cast<uint4 *>(hbuf + b * HLD + k8) =
+                    *reinterpret_cast<const uint4 *>(slot + b * Dh + k8);
+            }
+        }
+        __syncthreads();
+    }
+    if (t == T) {
+#pragma unroll
+        for (int r = 0; r < R4; ++r) {
+            if (wr[r]) {
+                a.hT[o_tile + oo[r]] = CELL == kLSTM ? hl[r] : st[r];
+                if (CELL == kLSTM) a.cT[o_tile + oo[r]] = st[r];
+            }
+        }
+    }
+}
+
+__global__ void clear_words_kernel(unsigned *p, int n) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+template <int CELL, int KCW, int R4>
+hipError_t launch_mc_t(const McPlan &p, McArgs m, hipStream_t s) {
+    void *args[] = {&m};
+    return hipLaunchCooperativeKernel(
+        reinterpret_cast<const void *>(&rec_fwd_mc_kernel<CELL, KCW, R4>), dim3(p.grid),
+        dim3(p.threads), args, p.lds, s);
+}
+
+template <int CELL, int KCW>
+hipError_t launch_mc_rows(const McPlan &p, const McArgs &m, hipStream_t s) {
+    switch (p.r4) {
+        case 1: return launch_mc_t<CELL, KCW, 1>(p, m, s);
+        case 2: return launch_mc_t<CELL, KCW, 2>(p, m, s);
+        default: return launch_mc_t<CELL, KCW, 4>(p, m, s);
+    }
+}
+
+}  // namespace
+
+McPlan plan_mc(int cell, int B, int NH, int Dh, int num_cu, int bt_override, int k_override) {
+    McPlan p{};
+    const int G = cell == kLSTM ? 4 : 3;
+    if (Dh < 256 || Dh % 128 != 0) return p;
+    const int KC = Dh / 32;
+    p.kcw = KC % 8 == 0 ? 8 : 4;
+    p.ks = KC / p.kcw;
+    const int nb_max = 8 / p.ks;  // at most 8 waves (512 threads) per workgroup
+    if (nb_max < 1) return p;
+    int K = 0;
+    for (int k = 2; k <= Dh / 16; ++k) {
+        if (Dh % (16 * k) == 0 && Dh / (16 * k) <= nb_max) {
+            K = k;
+            break;
+        }
+    }
+    if (k_override > 0 && Dh % (16 * k_override) == 0 && Dh / (16 * k_override) <= nb_max)
+        K = k_override;
+    if (K == 0) return p;
+    p.K = K;
+    p.nb = Dh / (16 * K);
+    p.threads = p.nb * p.ks * 64;
+    int bt = 16;
+    while (bt > 1 && (long)NH * ((B + bt / 2 - 1) / (bt / 2)) * K <= num_cu) bt /= 2;
+    if (bt_override > 0) bt = bt_override < 16 ? bt_override : 16;
+    if (bt > B) bt = B;
+    const int nbt = (B + bt - 1) / bt;
+    if ((long)NH * nbt * K > num_cu) return p;  // every member must be resident at once
+    p.BT = bt;
+    p.r4 = bt >= 3 ? 4 : bt;
+    p.groups = NH * nbt;
+    p.grid = p.groups * K;
+    p.lds = sizeof(uint16_t) * 16 * (Dh + 8) +
+            sizeof(float) * (size_t)(p.ks - 1) * p.nb * G * 256;
+    p.ok = 1;
+    return p;
+}
+
+hipError_t launch_rec_mc(int cell, const McPlan &p, const McArgs &m, hipStream_t s) {
+    hipLaunchKernelGGL(clear_words_kernel, dim3(1), dim3(256), 0, s, m.flag, 1);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(clear_words_kernel, dim3(4), dim3(256), 0, s, m.cnt, p.groups);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (cell == kLSTM)
+        return p.kcw == 8 ? launch_mc_rows<kLSTM, 8>(p, m, s) : launch_mc_rows<kLSTM, 4>(p, m, s);
+    return p.kcw == 8 ? launch_mc_rows<kGRU, 8>(p, m, s) : launch_mc_rows<kGRU, 4>(p, m, s);
+}
+
+}  // namespace rnn355

@@ -1,0 +1,136 @@
+"""GPU parity of the multi-CU forward recurrence (heads of Dh >= 256 split
+over several workgroups that swap h_t through global memory every step)
+against the oracle, plus its time-out path forced from the host."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import dev, host, nerr
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import gru_recurrence_amd as g  # noqa: E402
+
+TOL_BF16 = 2e-2
+
+
+@pytest.fixture(autouse=True)
+def _clean_env():
+    keys = ("RNN355_REC_BT", "RNN355_REC_K", "RNN355_SPIN_LIMIT")
+    old = {k: os.environ.pop(k, None) for k in keys}
+    yield
+    for k in keys:
+        os.environ.pop(k, None)
+        if old[k] is not None:
+            os.environ[k] = old[k]
+
+
+def run(c, ws=None):
+    if c.cell == "lstm":
+        h_seq, c_seq, hT, cT = g.lstm_fwd(dev(c, "x"), dev(c, "W"), dev(c, "R"), dev(c, "b"),
+                                          dev(c, "h0"), dev(c, "c0"), ws=ws)
+        torch.cuda.synchronize()
+        return dict(h_seq=host(h_seq), c_seq=host(c_seq), hT=host(hT), cT=host(cT))
+    h_seq, hT = g.gru_fwd(dev(c, "x"), dev(c, "W"), dev(c, "R"), dev(c, "b"), dev(c, "h0"), ws=ws)
+    torch.cuda.synchronize()
+    return dict(h_seq=host(h_seq), hT=host(hT))
+
+
+def want(c, mask=None):
+    d = c.dims
+    if c.cell == "lstm":
+        return oracle.lstm_fwd(c.f64("x"), c.f64("W"), c.f64("R"), c.f64("b"), c.f64("h0"),
+                               c.f64("c0"), NH=d.NH, Dh=d.Dh, chain_mask=mask)
+    return oracle.gru_fwd(c.f64("x"), c.f64("W"), c.f64("R"), c.f64("b"), c.f64("h0"),
+                          NH=d.NH, Dh=d.Dh, chain_mask=mask)
+
+
+def plan(c):
+    d = c.dims
+    op = g.OP_FWD_LSTM if c.cell == "lstm" else g.OP_FWD_GRU
+    return g.plan_describe(op, g.Dims(d.T, d.B, d.Din, d.NH, d.Dh), g.RNN_BF16)
+
+
+@pytest.mark.parametrize("cell,Dh,NH,B,bt,k", [
+    ("lstm", 256, 2, 3, None, None),   # 2 workgroups per head, one row each
+    ("lstm", 256, 2, 5, 2, None),      # two row slots, ragged batch
+    ("lstm", 256, 1, 6, 4, 4),         # four row slots, 4 workgroups per head
+    ("gru", 256, 2, 3, None, None),
+    ("gru", 256, 1, 7, 4, None),
+    ("lstm", 384, 1, 2, None, None),   # k split over 3 waves (LDS reduction)
+    ("gru", 384, 1, 3, 2, None),
+    ("lstm", 768, 1, 2, None, None),   # 24 workgroups per head
+])
+def test_multicu_forward(cell, Dh, NH, B, bt, k):
+    if bt is not None:
+        os.environ["RNN355_REC_BT"] = str(bt)
+    if k is not None:
+        os.environ["RNN355_REC_K"] = str(k)
+    d = synth.Dims(T=23, B=B, Din=64, NH=NH, Dh=Dh)
+    c = synth.make_case(cell, d, "bf16", 8000 + Dh + B, bias="forget+1" if cell == "lstm" else "zero",
+                        h0_var=0.2, c0_var=0.2)
+    p = plan(c)
+    print("  plan:", p, flush=True)
+    assert "multi_cu" in p
+    got, ref = run(c), want(c)
+    for key in got:
+        e = nerr(got[key], ref[key])
+        print("  %-6s nerr=%.3e" % (key, e), flush=True)
+        assert e <= TOL_BF16, (key, e)
+
+
+def test_multicu_run_to_run_bitwise():
+    d = synth.Dims(T=17, B=2, Din=32, NH=1, Dh=256)
+    c = synth.make_case("lstm", d, "bf16", 8100, bias="forget+1")
+    a, b = run(c), run(c)
+    for key in a:
+        assert np.array_equal(a[key], b[key]), key
+
+
+def test_step_wait_timeout_is_reported():
+    """A spin limit of one poll (set from the host) makes the first step wait
+    give up: every workgroup stops, the kernel ends normally and the
+    workspace reports the time-out; the next call clears it."""
+    d = synth.Dims(T=64, B=2, Din=32, NH=1, Dh=256)
+    c = synth.make_case("lstm", d, "bf16", 8200, bias="forget+1")
+    need = g.workspace_size(g.OP_FWD_LSTM, g.Dims(d.T, d.B, d.Din, d.NH, d.Dh), g.RNN_BF16)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    os.environ["RNN355_SPIN_LIMIT"] = "1"
+    run(c, ws=ws)
+    assert g.workspace_status(ws) == g.RNN_ERR_BARRIER_TIMEOUT
+    os.environ.pop("RNN355_SPIN_LIMIT")
+    got = run(c, ws=ws)
+    assert g.workspace_status(ws) == g.RNN_OK
+    assert nerr(got["h_seq"], want(c)["h_seq"]) <= TOL_BF16
+
+
+def _mask(B, NH, chains):
+    m = np.zeros((B, NH), bool)
+    for b, n in chains:
+        m[b, n] = True
+    return m
+
+
+@pytest.mark.parametrize("name,chains", [
+    ("lstm_1h_b16_dh768", [(0, 0), (9, 0)]),
+    ("lstm_fwdbwd_b16_nh4_dh256", [(0, 0), (5, 2), (15, 3)]),
+])
+def test_large_head_workloads_full_size_sampled_chains(name, chains):
+    w = synth.WORKLOADS[name]
+    c = synth.workload_case(w)
+    print("  plan:", plan(c), flush=True)
+    got = run(c)
+    ref = want(c, _mask(w.dims.B, w.dims.NH, chains))
+    Dh = w.dims.Dh
+    for b, n in chains:
+        sl = slice(n * Dh, (n + 1) * Dh)
+        for key in ("h_seq", "c_seq", "hT", "cT"):
+            y = got[key][:, b, sl] if got[key].ndim == 3 else got[key][b, sl]
+            r = ref[key][:, b, sl] if ref[key].ndim == 3 else ref[key][b, sl]
+            e = nerr(y, r)
+            print("  chain (b=%d, n=%d) %-6s nerr=%.3e" % (b, n, key, e), flush=True)
+            assert e <= TOL_BF16, (b, n, key, e)
