@@ -120,9 +120,6 @@ def main():
     import gru_recurrence_amd as g
 
     w = synth.WORKLOADS[args.workload]
-    if w.cell != "lstm" or w.backward:
-        print("bench.py times the LSTM forward workloads only", file=sys.stderr)
-        sys.exit(2)
     d = w.dims
     c = synth.workload_case(w)
     dev = torch.device("cuda:0")
@@ -133,9 +130,12 @@ def main():
             return torch.from_numpy(c.bits[name].view(np.int16).copy()).view(torch.bfloat16).to(dev)
         return torch.from_numpy(np.ascontiguousarray(c.vals[name])).to(dev)
 
+    lstm = w.cell == "lstm"
+    G = 4 if lstm else 3
     x, W, R, b = to_dev("x"), to_dev("W"), to_dev("R"), to_dev("b")
-    h0, c0 = to_dev("h0"), to_dev("c0")
-    H, N = d.NH * d.Dh, d.NH * 4 * d.Dh
+    h0 = to_dev("h0")
+    c0 = to_dev("c0") if lstm else None
+    H, N = d.NH * d.Dh, d.NH * G * d.Dh
     f32 = torch.float32
     gx = torch.empty((d.T, d.B, N), dtype=f32, device=dev)
     outs = dict(h_seq=torch.empty((d.T, d.B, H), dtype=f32, device=dev),
@@ -144,8 +144,9 @@ def main():
                 cT=torch.empty((d.B, H), dtype=f32, device=dev))
     dims = g.dims_of(x, R)
     dtc = g.RNN_BF16 if w.dtype == "bf16" else g.RNN_F32
-    ws = torch.empty(g.workspace_size(g.OP_REC_LSTM, dims, dtc), dtype=torch.uint8, device=dev)
-    plan = g.plan_describe(g.OP_REC_LSTM, dims, dtc)
+    op = g.OP_REC_LSTM if lstm else g.OP_REC_GRU
+    ws = torch.empty(g.workspace_size(op, dims, dtc), dtype=torch.uint8, device=dev)
+    plan = g.plan_describe(op, dims, dtc)
     stream = torch.cuda.current_stream()
 
     def step(evs=None):
@@ -154,7 +155,10 @@ def main():
         g.input_proj(x, W, b, out=gx, stream=stream)
         if evs is not None:
             evs[1].record(stream)
-        g.rec_lstm(gx, R, h0, c0, ws=ws, out=outs, stream=stream)
+        if lstm:
+            g.rec_lstm(gx, R, h0, c0, ws=ws, out=outs, stream=stream)
+        else:
+            g.rec_gru(gx, R, h0, ws=ws, out=outs, stream=stream)
         if evs is not None:
             evs[2].record(stream)
 
@@ -181,7 +185,6 @@ def main():
     rec_avg = float(np.mean(rec_ms))
     proj_avg = float(np.mean(proj_ms))
     achieved = rflops / (rec_avg * 1e-3) / 1e12
-    G = 4
     gemm_flops = 2.0 * d.T * d.B * d.Din * N
     ncu_engaged = int(plan.split(" wg=")[1].split()[0])
     out = {
@@ -211,13 +214,14 @@ def main():
                              "tflops": round(gemm_flops / (proj_avg * 1e-3) / 1e12, 2),
                              "frac_of_peak": round(gemm_flops / (proj_avg * 1e-3) / 1e12
                                                    / PEAK_BF16_TFLOPS, 4)},
-        "roofline": {"kernel": "rec_fwd_mfma_kernel (recurrence)", "bound": "mfma",
+        "roofline": {"kernel": ("rec_fwd_mc_kernel" if "multi_cu" in plan else
+                                "rec_fwd_mfma_kernel") + " (recurrence)", "bound": "mfma",
                      "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 5),
                      "traffic": traffic_per_launch()},
         "cpu_baseline": None,
     }
-    if not args.no_cpu:
+    if not args.no_cpu and lstm:
         out["cpu_baseline"] = cpu_baseline(w, c, args.cpu_budget)
     print(json.dumps(out), flush=True)
 

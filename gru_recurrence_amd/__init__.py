@@ -259,7 +259,7 @@ def rec_lstm(gx, R, h0=None, c0=None, *, with_seq=True, ws=None, out=None, strea
     return h_seq, c_seq, hT, cT
 
 
-def rec_gru(gx, R, h0=None, *, with_seq=True, ws=None, stream=None):
+def rec_gru(gx, R, h0=None, *, with_seq=True, ws=None, out=None, stream=None):
     """The GRU recurrence alone on a precomputed gx [T,B,N]."""
     torch = _torch()
     T, B, N = gx.shape
@@ -269,8 +269,11 @@ def rec_gru(gx, R, h0=None, *, with_seq=True, ws=None, stream=None):
     H = NH * Dh
     f32 = torch.float32
     dev = gx.device
-    h_seq = torch.empty((T, B, H), dtype=f32, device=dev) if with_seq else None
-    hT = torch.empty((B, H), dtype=f32, device=dev)
+    out = out or {}
+    h_seq = out.get("h_seq") if with_seq else None
+    if with_seq and h_seq is None:
+        h_seq = torch.empty((T, B, H), dtype=f32, device=dev)
+    hT = out.get("hT") if out.get("hT") is not None else torch.empty((B, H), dtype=f32, device=dev)
     ws = _workspace(OP_REC_GRU, d, dt, dev, ws)
     s = load().rnn_rec_gru(ctypes.byref(d), dt, _ptr(gx, "gx", f32, (T, B, NH * 3 * Dh)),
                            _ptr(R, "R", None, (NH, Dh, 3 * Dh)),

@@ -15,11 +15,10 @@ using namespace rnn355;
 
 namespace {
 
-// Workspace: [0, kHeader) status word (word 0) and per-group step counters
-// (words 64..), then the h exchange slots of the multi-CU kernel, then the
-// operation's own regions, each 256-byte aligned.
+// Workspace: [0, kHeader) status word (word 0), then the h exchange slots
+// of the multi-CU kernel, then the operation's own regions, each 256-byte
+// aligned.
 constexpr size_t kHeader = 4096;
-constexpr size_t kCounterWord = 64;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
@@ -39,10 +38,10 @@ int gates_of_op(rnn_op op) {
 
 int cell_of_op(rnn_op op) { return gates_of_op(op) == 4 ? kLSTM : kGRU; }
 
-// Exchange slots: [groups][2][BT][Dh] bf16 with groups = NH * ceil(B/BT) and
-// BT <= 16, so groups * BT <= NH * (B + 15).
+// Exchange slots: [groups][2][BT][Dh/2] 8-byte words with groups =
+// NH * ceil(B/BT) and BT <= 16, so groups * BT <= NH * (B + 15).
 size_t xchg_bytes(const rnn_dims *d) {
-    return align_up(2u * 2u * (size_t)d->NH * (d->B + 15) * d->Dh);
+    return align_up(2u * 8u * (size_t)d->NH * (d->B + 15) * ((d->Dh + 1) / 2));
 }
 
 size_t gx_bytes(const rnn_dims *d, int G) {
@@ -156,8 +155,7 @@ rnn_status rec_fwd(int cell, const rnn_dims *d, rnn_dtype dt, const float *gx, c
         m.r = a;
         m.K = ch.mc.K; m.KS = ch.mc.ks; m.NB = ch.mc.nb;
         m.flag = (unsigned *)ws;
-        m.cnt = (unsigned *)ws + kCounterWord;
-        m.xg = (uint16_t *)((char *)ws + kHeader);
+        m.xg = (unsigned long long *)((char *)ws + kHeader);
         m.spin_limit = spin_limit();
         e = launch_rec_mc(cell, ch.mc, m, s);
     } else {

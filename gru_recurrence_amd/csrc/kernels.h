@@ -91,9 +91,8 @@ struct McPlan {
 struct McArgs {
     RecArgs r;
     int K, KS, NB;
-    uint16_t *xg;    // exchange slots [groups][2][BT][Dh] bf16
-    unsigned *cnt;   // per-group step counters (cleared before every launch)
-    unsigned *flag;  // time-out / abort word (cleared before every launch)
+    unsigned long long *xg;  // exchange slots [groups][2][BT][Dh/2] (2 bf16 + step)
+    unsigned *flag;          // time-out / abort word (cleared before every launch)
     unsigned spin_limit;  // polls of the group counter before a wait is declared lost
 };
 
@@ -101,7 +100,7 @@ struct McArgs {
 // chip (every workgroup must be resident at once).  Pure host function.
 McPlan plan_mc(int cell, int B, int NH, int Dh, int num_cu, int bt_override, int k_override);
 
-// Clears the counters and the abort word, then launches cooperatively.
+// Clears the exchange slots and the abort word, then launches cooperatively.
 hipError_t launch_rec_mc(int cell, const McPlan &p, const McArgs &m, hipStream_t s);
 
 }  // namespace rnn355

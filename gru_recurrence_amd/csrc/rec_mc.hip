@@ -12,18 +12,23 @@
 // Per workgroup: U = Dh/K units, NB = U/16 unit blocks, and KS waves per unit
 // block, each holding KCW = Dh/(32*KS) k-chunks of the MFMA B fragments of
 // its block's G gate tiles (G * KCW * 4 VGPRs, R never re-read).  Per step:
-//   1. A fragments of h_{t-1} (bf16, LDS, full Dh) for the wave's k-range;
+//   1. A fragments of h_{t-1} (bf16, LDS, full Dh, double-buffered by step
+//      parity) for the wave's k-range;
 //   2. MFMAs -> partial gate sums; waves with ks > 0 hand theirs to the
 //      ks = 0 wave of the block through LDS;
 //   3. the ks = 0 waves apply the cell update (same code as the one-CU
-//      kernel) and publish h_t (bf16) into the group's exchange slot;
-//   4. group barrier: every wave fences (agent-scope release), thread 0
-//      bumps the group counter and polls it until all K members arrived,
-//      then every wave fences (acquire).  The poll is bounded: on time-out the
-//      workgroup raises the abort word, which stops every member;
-//   5. the h/c outputs of step t are stored and Gx of step t+1 requested --
-//      issued right after the barrier so they drain during the next step --
-//      and the full h_t is copied from the exchange slot into LDS.
+//      kernel) and publish h_t into the group's exchange slot: 8-byte words of
+//      two bf16 values plus the step number, written as relaxed agent-scope
+//      atomics (single-copy atomic and coherent across XCDs), so a reader that
+//      sees the step number sees the values with it -- no counter, no fence,
+//      no cache write-back or invalidation (those act on a whole XCD's L2 and
+//      would stall every other group on it);
+//   4. every thread polls its share of the words of the slot until all carry
+//      step t and copies them into LDS.  Polls are bounded: on time-out the
+//      workgroup raises the abort word, which every poller checks, so all
+//      members stop and the kernel ends;
+//   5. the h/c outputs of step t are stored and Gx of step t+1 requested,
+//      so they drain during the next step.
 #include <hip/hip_runtime.h>
 
 #include "common.h"
@@ -46,8 +51,11 @@ __global__ __launch_bounds__(512) void rec_fwd_mc_kernel(McArgs m) {
     const int T = a.T, B = a.B;
 
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-    uint16_t *hbuf = smem;                                    // [16][HLD] bf16
-    float *red = reinterpret_cast<float *>(smem + 16 * HLD);  // [KS-1][NB][G][16][16]
+    // h_{t-1} as bf16, double-buffered by step parity: step t reads buffer
+    // t&1 and fills buffer (t+1)&1, which nobody reads any more (its last
+    // readers finished before the closing barrier of step t-1)
+    uint16_t *hbuf2 = smem;                                       // [2][16][HLD] bf16
+    float *red = reinterpret_cast<float *>(smem + 2 * 16 * HLD);  // [KS-1][NB][G][16][16]
     __shared__ int s_abort;
 
     const int group = blockIdx.x / K, member = blockIdx.x - group * K;
@@ -85,11 +93,11 @@ __global__ __launch_bounds__(512) void rec_fwd_mc_kernel(McArgs m) {
         }
     }
     const int nthr = blockDim.x;
-    for (int i = tid; i < 16 * HLD; i += nthr) {
-        const int b = i / HLD, k = i - b * HLD;
+    for (int i = tid; i < 2 * 16 * HLD; i += nthr) {
+        const int b = (i / HLD) & 15, k = i % HLD;
         float v = 0.f;
-        if (b < rows && k < Dh && a.h0) v = a.h0[(long)(b0 + b) * H + n * Dh + k];
-        hbuf[i] = f32_to_bf16_rne(v);
+        if (i < 16 * HLD && b < rows && k < Dh && a.h0) v = a.h0[(long)(b0 + b) * H + n * Dh + k];
+        hbuf2[i] = f32_to_bf16_rne(v);
     }
     if (tid == 0) s_abort = 0;
 
@@ -128,10 +136,12 @@ __global__ __launch_bounds__(512) void rec_fwd_mc_kernel(McArgs m) {
     load_gx(0);
     __syncthreads();
 
-    uint16_t *xg_group = m.xg + (long)group * 2 * a.BT * Dh;  // [2][BT][Dh]
-    unsigned *cnt = m.cnt + group;
+    // exchange slots of the group: [2 parities][BT rows][Dh/2] words
+    unsigned long long *xs_group = m.xg + (long)group * 2 * a.BT * (Dh / 2);
+    const int wpr = Dh / 2;  // words per row
     int t = 0;
     for (; t < T; ++t) {
+        const uint16_t *hbuf = hbuf2 + (t & 1) * 16 * HLD;
         bf16x8 af[KCW];
         if (lr < rows) {
 #pragma unroll
@@ -169,7 +179,8 @@ __global__ __launch_bounds__(512) void rec_fwd_mc_kernel(McArgs m) {
                 }
             }
         }
-        uint16_t *slot = xg_group + (long)(t & 1) * a.BT * Dh;
+        unsigned long long *slot = xs_group + (long)(t & 1) * a.BT * wpr;
+        const unsigned long long tag = (unsigned long long)(unsigned)(t + 1) << 32;
         if (gate_wave) {
             float h[R4], c[R4];
             gate_update<CELL, R4>(acc, gxr, st, hl, h, c);
@@ -177,33 +188,46 @@ __global__ __launch_bounds__(512) void rec_fwd_mc_kernel(McArgs m) {
             for (int r = 0; r < R4; ++r) {
                 ph[r] = h[r];
                 pc[r] = c[r];
-                if (wr[r]) slot[(ROWS1 ? 0 : 4 * lg + r) * Dh + j] = f32_to_bf16_rne(h[r]);
+                // units j, j+1 live in neighbouring lanes: the even lane
+                // writes both with the step number
+                const unsigned hb = f32_to_bf16_rne(h[r]);
+                const unsigned nb = (unsigned)__shfl_xor((int)hb, 1);
+                if (wr[r] && (lr & 1) == 0)
+                    __hip_atomic_store(slot + (ROWS1 ? 0 : 4 * lg + r) * wpr + (j >> 1),
+                                       tag | (nb << 16) | hb, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
             }
         }
-        // ---- group barrier (agent scope)
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        __syncthreads();
-        if (tid == 0) {
-            __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const unsigned want = (unsigned)K * (unsigned)(t + 1);
-            unsigned spins = 0;
-            while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < want) {
-                if ((++spins & 255u) == 0 &&
-                    __hip_atomic_load(m.flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
-                    s_abort = 1;
-                    break;
+        // ---- collect h_t of every member: poll each word until it carries step t
+        {
+            const int words = rows * wpr;
+            unsigned *hw = reinterpret_cast<unsigned *>(hbuf2 + ((t + 1) & 1) * 16 * HLD);
+            for (int i = tid; i < words; i += nthr) {
+                const int b = i / wpr, k2 = i - b * wpr;
+                unsigned spins = 0;
+                unsigned long long w;
+                for (;;) {
+                    w = __hip_atomic_load(slot + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if ((w & 0xFFFFFFFF00000000ull) == tag) break;
+                    ++spins;
+                    if ((spins & 255u) == 0 &&
+                        __hip_atomic_load(m.flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+                        s_abort = 1;
+                        break;
+                    }
+                    if (spins >= m.spin_limit) {
+                        __hip_atomic_store(m.flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        s_abort = 1;
+                        break;
+                    }
                 }
-                if (spins >= m.spin_limit) {
-                    __hip_atomic_store(m.flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    s_abort = 1;
-                    break;
-                }
+                if (s_abort) break;
+                hw[(b * HLD) / 2 + k2] = (unsigned)w;
             }
         }
         __syncthreads();
         if (s_abort) break;
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        // ---- outputs of step t, Gx of step t+1, full h_t into LDS
+        // ---- outputs of step t, Gx of step t+1
         if (gate_wave) {
             const long base = o_tile + (long)t * o_step;
 #pragma unroll
@@ -215,15 +239,6 @@ __global__ __launch_bounds__(512) void rec_fwd_mc_kernel(McArgs m) {
             }
             if (t + 1 < T) load_gx(t + 1);
         }
-        {
-            const int chunks = rows * (Dh / 8);  // 16-byte pieces of h_t
-            for (int i = tid; i < chunks; i += nthr) {
-                const int b = i / (Dh / 8), k8 = (i - b * (Dh / 8)) * 8;
-                *reinterpret_cast<uint4 *>(hbuf + b * HLD + k8) =
-                    *reinterpret_cast<const uint4 *>(slot + b * Dh + k8);
-            }
-        }
-        __syncthreads();
     }
     if (t == T) {
 #pragma unroll
@@ -291,7 +306,7 @@ McPlan plan_mc(int cell, int B, int NH, int Dh, int num_cu, int bt_override, int
     p.r4 = bt >= 3 ? 4 : bt;
     p.groups = NH * nbt;
     p.grid = p.groups * K;
-    p.lds = sizeof(uint16_t) * 16 * (Dh + 8) +
+    p.lds = sizeof(uint16_t) * 2 * 16 * (Dh + 8) +
             sizeof(float) * (size_t)(p.ks - 1) * p.nb * G * 256;
     p.ok = 1;
     return p;
@@ -301,7 +316,10 @@ hipError_t launch_rec_mc(int cell, const McPlan &p, const McArgs &m, hipStream_t
     hipLaunchKernelGGL(clear_words_kernel, dim3(1), dim3(256), 0, s, m.flag, 1);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(clear_words_kernel, dim3(4), dim3(256), 0, s, m.cnt, p.groups);
+    // step numbers start at 1: cleared slots never match a step
+    const long words = 2L * p.groups * 2 * p.BT * (m.r.Dh / 2);
+    hipLaunchKernelGGL(clear_words_kernel, dim3(64), dim3(256), 0, s,
+                       reinterpret_cast<unsigned *>(m.xg), (int)words);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (cell == kLSTM)
