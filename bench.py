@@ -39,7 +39,7 @@ NUM_CU = 256
 CU_BF16_TFLOPS = PEAK_BF16_TFLOPS / NUM_CU
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "gru_recurrence_amd", "csrc", f)
-                  for f in ("rec_fwd.hip", "common.h", "kernels.h")]
+                  for f in ("rec_fwd.hip", "gates.h", "common.h", "kernels.h")]
 
 
 def kernel_source_hash() -> str:
@@ -107,7 +107,22 @@ def main():
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(synth.WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (5 times) and exit; "
+                         "used to scale the HBM byte counters of a profiler run")
     args = ap.parse_args()
+
+    if args.copy_calibration_mb > 0:
+        import torch
+        n = args.copy_calibration_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_mb": args.copy_calibration_mb,
+                          "bytes_read_per_copy": 4 * n, "bytes_written_per_copy": 4 * n}))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
