@@ -48,6 +48,26 @@ size_t gx_bytes(const rnn_dims *d, int G) {
     return align_up(sizeof(float) * (size_t)d->T * d->B * d->NH * G * d->Dh);
 }
 
+// Backward workspace after the header: dA exchange slots, recomputed
+// pre-activations A (f32), gate gradients dA (bf16), h_{t-1} (bf16) and the
+// per-batch-tile bias-gradient partials.
+struct BwdLayout {
+    size_t xchg, A, dA, hprev, dbp, total;
+};
+BwdLayout bwd_layout(const rnn_dims *d) {
+    BwdLayout L{};
+    const size_t TB = (size_t)d->T * d->B, N = (size_t)d->NH * 4 * d->Dh;
+    const size_t H = (size_t)d->NH * d->Dh;
+    size_t off = 0;
+    L.xchg = off; off += align_up(8u * (size_t)d->NH * (d->B + 15) * 2 * d->Dh * 2);
+    L.A = off;    off += align_up(sizeof(float) * TB * N);
+    L.dA = off;   off += align_up(sizeof(uint16_t) * TB * N);
+    L.hprev = off; off += align_up(sizeof(uint16_t) * TB * H);
+    L.dbp = off;  off += align_up(sizeof(float) * (size_t)d->B * N);
+    L.total = off;
+    return L;
+}
+
 // Compute-unit count of the current device, cached per device.
 int device_cus() {
     static std::mutex mu;
@@ -195,6 +215,8 @@ size_t rnn_workspace_size(rnn_op op, const rnn_dims *d, rnn_dtype dt) {
         case RNN_OP_REC_LSTM:
         case RNN_OP_REC_GRU:
             return kHeader + xchg_bytes(d);
+        case RNN_OP_BWD_LSTM:
+            return kHeader + bwd_layout(d).total;
         default:
             return 0;
     }
@@ -298,11 +320,77 @@ rnn_status rnn_bwd_lstm(const rnn_dims *d, rnn_dtype dt, const void *x, const vo
                         const float *dhT, const float *dcT, float *dx, float *dW, float *dR,
                         float *db, float *dh0, float *dc0, void *ws, size_t ws_bytes,
                         hipStream_t stream) {
-    (void)x; (void)W; (void)R; (void)b; (void)h0; (void)c0; (void)h_seq; (void)c_seq;
-    (void)dh_seq; (void)dhT; (void)dcT; (void)dx; (void)dW; (void)dR; (void)db; (void)dh0;
-    (void)dc0; (void)ws; (void)ws_bytes; (void)stream;
     if (!dims_ok(d) || !dtype_ok(dt)) return RNN_ERR_INVALID_ARG;
-    return RNN_ERR_UNSUPPORTED;
+    if (!x || !W || !R || !h_seq || !c_seq || !dh_seq || !dx || !dW || !dR || !db || !dh0 || !dc0)
+        return RNN_ERR_INVALID_ARG;
+    const void *ps[] = {x, W, R, b, h0, c0, h_seq, c_seq, dh_seq, dhT, dcT,
+                        dx, dW, dR, db, dh0, dc0, ws};
+    for (const void *p : ps)
+        if (!aligned16(p)) return RNN_ERR_INVALID_ARG;
+    if (dt != RNN_BF16) return RNN_ERR_UNSUPPORTED;
+    const int G = 4, Dh = d->Dh, NH = d->NH, T = d->T, B = d->B, Din = d->Din;
+    const int GD = G * Dh, N = NH * GD, H = NH * Dh, M = T * B;
+    if (!gemm_shape_ok(Din, N, dt) || Dh % 16 != 0) return RNN_ERR_UNSUPPORTED;
+    const BwdPlan p = plan_bwd(B, NH, Dh, device_cus(), bt_override(), k_override());
+    if (!p.ok) return RNN_ERR_UNSUPPORTED;
+    if (!ws || ws_bytes < rnn_workspace_size(RNN_OP_BWD_LSTM, d, dt)) return RNN_ERR_WORKSPACE;
+
+    char *base = (char *)ws + kHeader;
+    const BwdLayout L = bwd_layout(d);
+    float *A = (float *)(base + L.A);
+    uint16_t *dA = (uint16_t *)(base + L.dA);
+    uint16_t *hprev = (uint16_t *)(base + L.hprev);
+    float *dbp = (float *)(base + L.dbp);
+    const uint16_t *xb = (const uint16_t *)x, *Wb = (const uint16_t *)W, *Rb = (const uint16_t *)R;
+    auto ok = [](hipError_t e) { return e == hipSuccess; };
+
+    // 1. h_{t-1} as bf16; A = x W + b + h_{t-1} R (block-diagonal), all t at once
+    if (!ok(launch_hprev_bf16(h0, h_seq, hprev, (long)B * H, (long)M * H, stream))) return RNN_ERR_HIP;
+    if (input_proj(M, Din, N, dt, x, W, b, A, (uint32_t *)ws, stream) != RNN_OK) return RNN_ERR_HIP;
+    {
+        GemmArgs g{};
+        g.M = M; g.N = GD; g.K = Dh;
+        g.A = hprev; g.lda = H; g.strideA = Dh;       // row m, k = unit of head n
+        g.B = Rb; g.ldb = GD; g.strideB = (long)Dh * GD;  // R[n][k][c]: r-major
+        g.C = A; g.ldc = N; g.strideC = GD;
+        g.accumulate = 1;
+        if (!ok(launch_gemm_bf16(g, true, false, NH, stream))) return RNN_ERR_HIP;
+    }
+    // 2. the reverse-time sweep
+    {
+        BwdArgs m{};
+        m.T = T; m.B = B; m.NH = NH; m.Dh = Dh; m.BT = p.BT;
+        m.K = p.K; m.KS = p.ks; m.NB = p.nb;
+        m.A = A; m.c_seq = c_seq; m.c0 = c0; m.dh_seq = dh_seq; m.dhT = dhT; m.dcT = dcT;
+        m.Rb = Rb; m.dA = dA; m.db_part = dbp; m.dh0 = dh0; m.dc0 = dc0;
+        m.xg = (unsigned long long *)(base + L.xchg);
+        m.flag = (unsigned *)ws;
+        m.spin_limit = spin_limit();
+        if (!ok(launch_rec_bwd(p, m, stream))) return RNN_ERR_HIP;
+    }
+    // 3. parameter and input gradients from dA
+    if (!ok(launch_db_reduce(dbp, p.nbt, N, db, stream))) return RNN_ERR_HIP;
+    {
+        GemmArgs g{};  // dW[k][c] = sum_m x[m][k] dA[m][c]
+        g.M = Din; g.N = N; g.K = M;
+        g.A = xb; g.lda = Din; g.B = dA; g.ldb = N; g.C = dW; g.ldc = N;
+        if (!ok(launch_gemm_bf16(g, false, false, 1, stream))) return RNN_ERR_HIP;
+    }
+    {
+        GemmArgs g{};  // dx[m][k] = sum_c dA[m][c] W[k][c]
+        g.M = M; g.N = Din; g.K = N;
+        g.A = dA; g.lda = N; g.B = Wb; g.ldb = N; g.C = dx; g.ldc = Din;
+        if (!ok(launch_gemm_bf16(g, true, true, 1, stream))) return RNN_ERR_HIP;
+    }
+    {
+        GemmArgs g{};  // dR[n][i][c] = sum_m h_{t-1}[m][n*Dh+i] dA[m][n*GD+c]
+        g.M = Dh; g.N = GD; g.K = M;
+        g.A = hprev; g.lda = H; g.strideA = Dh;
+        g.B = dA; g.ldb = N; g.strideB = GD;
+        g.C = dR; g.ldc = GD; g.strideC = (long)Dh * GD;
+        if (!ok(launch_gemm_bf16(g, false, false, NH, stream))) return RNN_ERR_HIP;
+    }
+    return RNN_OK;
 }
 
 rnn_status rnn_workspace_status(const void *ws, size_t ws_bytes, hipStream_t stream) {

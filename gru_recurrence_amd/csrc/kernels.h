@@ -103,4 +103,33 @@ McPlan plan_mc(int cell, int B, int NH, int Dh, int num_cu, int bt_override, int
 // Clears the exchange slots and the abort word, then launches cooperatively.
 hipError_t launch_rec_mc(int cell, const McPlan &p, const McArgs &m, hipStream_t s);
 
+// LSTM backward (rec_bwd.hip).
+struct BwdPlan {
+    int ok;
+    int K, nb, ks, kcw, threads, BT, r4, nbt, groups, grid;
+    size_t lds;
+};
+
+struct BwdArgs {
+    int T, B, NH, Dh, BT, K, KS, NB;
+    const float *A;          // recomputed pre-activations [T][B][NH*4*Dh]
+    const float *c_seq;      // [T][B][H]
+    const float *c0;         // [B][H] or null
+    const float *dh_seq;     // [T][B][H]
+    const float *dhT, *dcT;  // [B][H] or null
+    const uint16_t *Rb;      // bf16 R
+    uint16_t *dA;            // bf16 gate gradients [T][B][NH*4*Dh]
+    float *db_part;          // [nbt][NH*4*Dh]
+    float *dh0, *dc0;        // [B][H]
+    unsigned long long *xg;  // exchange slots [groups][2][BT][2*Dh]
+    unsigned *flag;
+    unsigned spin_limit;
+};
+
+BwdPlan plan_bwd(int B, int NH, int Dh, int num_cu, int bt_override, int k_override);
+hipError_t launch_rec_bwd(const BwdPlan &p, const BwdArgs &m, hipStream_t s);
+hipError_t launch_hprev_bf16(const float *h0, const float *h_seq, uint16_t *hprev, long BH,
+                             long total, hipStream_t s);
+hipError_t launch_db_reduce(const float *db_part, int nbt, int N, float *db, hipStream_t s);
+
 }  // namespace rnn355

@@ -1,0 +1,368 @@
+// rec_bwd.hip -- reverse-time recurrence of LSTM backpropagation through
+// time (the sequential part of the backward), plus the small helper kernels
+// of the backward pass.
+//
+// Backward of the recurrence A_t = Gx_t + h_{t-1} R (FlashRNN, arXiv
+// 2412.07752, abstract: traditional RNNs trained through their sequential
+// recurrence; blog.hotdry.top 2025-09-21, the paragraphs on the step
+// dependency and on keeping R resident, which apply to the reverse sweep in
+// the same way).  With the pre-activations A_t recomputed beforehand (fully
+// parallel over t) the reverse sweep is, per step t = T-1 .. 0:
+//     dh   = dL/dh_t (upstream) + dh_carry          tc = tanh(c_t)
+//     dA_o = dh tc o(1-o)                           dc = dc_carry + dh o (1-tc^2)
+//     dA_i = dc z i(1-i)    dA_z = dc i (1-z^2)     dA_f = dc c_{t-1} f(1-f)
+//     dc_carry = dc f       dh_carry = dA_t R^T   (per head, block-diagonal)
+// and after t = 0 the carries are dL/dh_0 and dL/dc_0.
+//
+// Mapping (mirrors the forward kernels): a (head, batch tile) group of K
+// workgroups; workgroup `member` owns output units [member*U, (member+1)*U),
+// wave (blk, ks) the 16-unit block blk and the ks-th range of the G*Dh gate
+// columns (the reduction dimension here), holding the matching fragments of
+// R^T -- lane l of chunk c reads R[n][unit][32c + 8(l/16) .. +8], one 16-byte
+// load, so R's own row layout serves R^T.  The A operand is the row of dA_t
+// (bf16, all G*Dh gate columns) in LDS.  After the MFMAs the lane that holds
+// dh_carry of unit j and row b also computes the cell backward of (b, j), so
+// all per-unit state stays in registers.  dA_t reaches the other members as
+// step-tagged 8-byte words (as in the multi-CU forward) or, with K = 1,
+// directly through LDS.
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace rnn355 {
+
+namespace {
+
+template <int KCW, int R4>
+__global__ __launch_bounds__(512) void rec_bwd_lstm_kernel(BwdArgs m) {
+    constexpr int G = 4;
+    const int Dh = m.Dh, K = m.K, KS = m.KS, NB = m.NB;
+    const int U = NB * 16, GD = G * Dh, H = m.NH * Dh, N = m.NH * GD, ALD = GD + 8;
+    const int T = m.T, B = m.B;
+
+    extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+    uint16_t *dab2 = smem;                                          // [2][BT][ALD] bf16
+    float *red = reinterpret_cast<float *>(smem + 2 * m.BT * ALD);  // [KS-1][NB][16][16]
+    __shared__ int s_abort;
+
+    const int group = blockIdx.x / K, member = blockIdx.x - group * K;
+    const int n = group % m.NH;
+    const int bt = group / m.NH;
+    const int b0 = bt * m.BT;
+    const int rows = min(m.BT, B - b0);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int blk = wave / KS, ks = wave - blk * KS;
+    const bool gate_wave = ks == 0;
+    const int j = member * U + blk * 16 + lr;  // this lane's hidden unit
+    const int kc0 = ks * KCW;
+    const int nthr = blockDim.x;
+
+    // R^T fragments: B[k][col] = R[n][unit][k] for k in this wave's chunks
+    bf16x8 rf[KCW];
+    {
+        const uint16_t *Rrow = m.Rb + ((long)n * Dh + j) * GD;
+#pragma unroll
+        for (int c = 0; c < KCW; ++c)
+            rf[c] = *reinterpret_cast<const bf16x8 *>(Rrow + 32 * (kc0 + c) + 8 * lg);
+    }
+    for (int i = tid; i < 2 * m.BT * ALD; i += nthr) dab2[i] = 0;
+    if (tid == 0) s_abort = 0;
+
+    // per-lane state of the gate waves: row slots r -> batch row 4*lg + r
+    bool rv[R4];
+    unsigned oo[R4];
+    float dhc[R4], dcc[R4], dbs[R4][G];
+    const long o_tile = (long)b0 * H + n * Dh;
+    const long a_tile = (long)b0 * N + n * GD;
+#pragma unroll
+    for (int r = 0; r < R4; ++r) {
+        const int b = 4 * lg + r;
+        rv[r] = gate_wave && b < rows;
+        oo[r] = (unsigned)(b * H + j);
+        dhc[r] = (rv[r] && m.dhT) ? m.dhT[o_tile + oo[r]] : 0.f;
+        dcc[r] = (rv[r] && m.dcT) ? m.dcT[o_tile + oo[r]] : 0.f;
+#pragma unroll
+        for (int g = 0; g < G; ++g) dbs[r][g] = 0.f;
+    }
+    // streamed per step and row slot: pre-activations, c_t, c_{t-1}, dL/dh_t
+    float pa[R4][G], ct[R4], cp[R4], up[R4];
+    auto load_step = [&](int t) {
+#pragma unroll
+        for (int r = 0; r < R4; ++r) {
+            if (rv[r]) {
+                const long ao = a_tile + (long)t * B * N + (long)(4 * lg + r) * N + j;
+#pragma unroll
+                for (int g = 0; g < G; ++g) pa[r][g] = m.A[ao + g * Dh];
+                const long oo_t = o_tile + (long)t * B * H + oo[r];
+                ct[r] = m.c_seq[oo_t];
+                cp[r] = t > 0 ? m.c_seq[oo_t - (long)B * H]
+                              : (m.c0 ? m.c0[o_tile + oo[r]] : 0.f);
+                up[r] = m.dh_seq[oo_t];
+            }
+        }
+    };
+    load_step(T - 1);
+    __syncthreads();
+
+    const int wpr = GD / 2;  // exchange words per row
+    unsigned long long *xs_group = m.xg + (long)group * 2 * m.BT * wpr;
+    int s = 0;  // steps done
+    for (; s < T; ++s) {
+        const int t = T - 1 - s;
+        uint16_t *dab_next = dab2 + (s & 1) * m.BT * ALD;  // filled with dA_t this step
+        unsigned long long *slot = xs_group + (long)(s & 1) * m.BT * wpr;
+        const unsigned long long tag = (unsigned long long)(unsigned)(s + 1) << 32;
+        // ---- cell backward of this lane's units at step t
+        if (gate_wave) {
+#pragma unroll
+            for (int r = 0; r < R4; ++r) {
+                const float ig = sigmoid_f(pa[r][0]), fg = sigmoid_f(pa[r][1]);
+                const float zg = tanh_f(pa[r][2]), og = sigmoid_f(pa[r][3]);
+                const float tc = tanh_f(ct[r]);
+                const float dh = up[r] + dhc[r];
+                const float dc = fmaf(dh * og, 1.0f - tc * tc, dcc[r]);
+                float d[G];
+                d[0] = dc * zg * ig * (1.0f - ig);
+                d[1] = dc * cp[r] * fg * (1.0f - fg);
+                d[2] = dc * ig * (1.0f - zg * zg);
+                d[3] = dh * tc * og * (1.0f - og);
+                dcc[r] = dc * fg;
+                uint16_t db16[G];
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    dbs[r][g] += rv[r] ? d[g] : 0.f;
+                    db16[g] = f32_to_bf16_rne(d[g]);
+                }
+                if (rv[r]) {
+                    uint16_t *dst = m.dA + a_tile + (long)t * B * N + (long)(4 * lg + r) * N + j;
+#pragma unroll
+                    for (int g = 0; g < G; ++g) dst[g * Dh] = db16[g];
+                }
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const unsigned v = db16[g];
+                    const unsigned nb = (unsigned)__shfl_xor((int)v, 1);
+                    if (rv[r]) {
+                        const int row = 4 * lg + r, col = g * Dh + j;
+                        if (K == 1) {
+                            dab_next[row * ALD + col] = (uint16_t)v;
+                        } else if ((lr & 1) == 0) {
+                            __hip_atomic_store(slot + row * wpr + (col >> 1), tag | (nb << 16) | v,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        }
+                    }
+                }
+            }
+        }
+        // ---- dA_t of the whole head row into LDS
+        if (K > 1) {
+            const int words = rows * wpr;
+            unsigned *hw = reinterpret_cast<unsigned *>(dab_next);
+            for (int i = tid; i < words; i += nthr) {
+                const int b = i / wpr, k2 = i - b * wpr;
+                unsigned spins = 0;
+                unsigned long long w;
+                for (;;) {
+                    w = __hip_atomic_load(slot + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if ((w & 0xFFFFFFFF00000000ull) == tag) break;
+                    ++spins;
+                    if ((spins & 255u) == 0 &&
+                        __hip_atomic_load(m.flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+                        s_abort = 1;
+                        break;
+                    }
+                    if (spins >= m.spin_limit) {
+                        __hip_atomic_store(m.flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        s_abort = 1;
+                        break;
+                    }
+                }
+                if (s_abort) break;
+                hw[(b * ALD) / 2 + k2] = (unsigned)w;
+            }
+        }
+        __syncthreads();
+        if (s_abort) break;
+        // next step's streamed inputs, issued now so they land during the MFMAs
+        if (gate_wave && t > 0) load_step(t - 1);
+        // ---- dh_carry = dA_t R^T for this wave's gate-column range
+        bf16x8 af[KCW];
+        if (lr < rows) {
+#pragma unroll
+            for (int c = 0; c < KCW; ++c)
+                af[c] = *reinterpret_cast<const bf16x8 *>(dab_next + lr * ALD + 32 * (kc0 + c) + 8 * lg);
+        } else {
+#pragma unroll
+            for (int c = 0; c < KCW; ++c) af[c] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+        }
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < KCW; ++c) acc = mfma_16x16x32_bf16(af[c], rf[c], acc);
+        if (KS > 1) {
+            if (!gate_wave) {
+                float *dst = red + ((long)(ks - 1) * NB + blk) * 256;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dst[(4 * lg + r) * 16 + lr] = acc[r];
+            }
+            __syncthreads();
+            if (gate_wave) {
+                for (int k2 = 1; k2 < KS; ++k2) {
+                    const float *src = red + ((long)(k2 - 1) * NB + blk) * 256;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[r] += src[(4 * lg + r) * 16 + lr];
+                }
+            }
+            // the next step rewrites `red` only after its own barrier
+        }
+#pragma unroll
+        for (int r = 0; r < R4; ++r) dhc[r] = acc[r];
+    }
+    if (s == T) {
+#pragma unroll
+        for (int r = 0; r < R4; ++r) {
+            if (rv[r]) {
+                m.dh0[o_tile + oo[r]] = dhc[r];
+                m.dc0[o_tile + oo[r]] = dcc[r];
+            }
+        }
+        // db partial of this batch tile: the lane's 4 gate sums over its rows
+        // (row slots are combined by the lanes of one column: lanes lr with
+        // the same unit in the four 16-lane rows, reduced through LDS)
+        float *dbt = m.db_part + (long)bt * N + n * GD;
+        if (gate_wave) {
+            float sg[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                float v = 0.f;
+#pragma unroll
+                for (int r = 0; r < R4; ++r) v += dbs[r][g];
+                sg[g] = v;
+            }
+            // sum over the 4 lane rows (batch rows 4lg..4lg+3) with cross-row
+            // shuffles: lanes l, l^16, l^32, l^48 share the unit
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                float v = sg[g];
+                v += __shfl_xor(v, 16);
+                v += __shfl_xor(v, 32);
+                if (lg == 0) dbt[g * Dh + j] = v;
+            }
+        }
+    }
+}
+
+template <int KCW, int R4>
+hipError_t launch_bwd_t(const BwdPlan &p, BwdArgs m, hipStream_t s) {
+    void *args[] = {&m};
+    return hipLaunchCooperativeKernel(
+        reinterpret_cast<const void *>(&rec_bwd_lstm_kernel<KCW, R4>), dim3(p.grid),
+        dim3(p.threads), args, p.lds, s);
+}
+
+template <int KCW>
+hipError_t launch_bwd_rows(const BwdPlan &p, const BwdArgs &m, hipStream_t s) {
+    switch (p.r4) {
+        case 1: return launch_bwd_t<KCW, 1>(p, m, s);
+        case 2: return launch_bwd_t<KCW, 2>(p, m, s);
+        default: return launch_bwd_t<KCW, 4>(p, m, s);
+    }
+}
+
+__global__ void clear_words_bwd_kernel(unsigned *p, long n) {
+    for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x)
+        p[i] = 0u;
+}
+
+// hprev[t][b][k] = bf16(h_{t-1}[b][k]) with h_{-1} = h0 (the MFMA operand the
+// forward used), as the A operand of the dR and recompute contractions.
+__global__ void hprev_bf16_kernel(const float *h0, const float *h_seq, uint16_t *hprev, long BH,
+                                  long total) {
+    for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < total;
+         i += (long)gridDim.x * blockDim.x) {
+        const float v = i < BH ? (h0 ? h0[i] : 0.f) : h_seq[i - BH];
+        hprev[i] = f32_to_bf16_rne(v);
+    }
+}
+
+// db[c] = sum over batch tiles of db_part[bt][c], in tile order.
+__global__ void db_reduce_kernel(const float *db_part, int nbt, int N, float *db) {
+    const int c = blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= N) return;
+    float v = 0.f;
+    for (int b = 0; b < nbt; ++b) v += db_part[(long)b * N + c];
+    db[c] = v;
+}
+
+}  // namespace
+
+BwdPlan plan_bwd(int B, int NH, int Dh, int num_cu, int bt_override, int k_override) {
+    BwdPlan p{};
+    const int G = 4;
+    if (Dh % 16 != 0 || (G * Dh) % 128 != 0) return p;
+    const int KC = G * Dh / 32;  // reduction chunks of 32 gate columns
+    // at most 16 chunks per wave: its R^T fragments and the A fragments of
+    // one step then take 64 VGPRs each
+    p.kcw = KC % 16 == 0 ? 16 : KC % 8 == 0 ? 8 : 4;
+    p.ks = KC / p.kcw;
+    const int nb_max = 8 / p.ks;
+    if (nb_max < 1) return p;
+    int K = 0;
+    for (int k = 1; k <= Dh / 16; ++k) {
+        if (Dh % (16 * k) == 0 && Dh / (16 * k) <= nb_max) {
+            K = k;
+            break;
+        }
+    }
+    if (k_override > 0 && Dh % (16 * k_override) == 0 && Dh / (16 * k_override) <= nb_max)
+        K = k_override;
+    if (K == 0) return p;
+    p.K = K;
+    p.nb = Dh / (16 * K);
+    p.threads = p.nb * p.ks * 64;
+    int bt = 16;
+    while (bt > 1 && (long)NH * ((B + bt / 2 - 1) / (bt / 2)) * K <= num_cu) bt /= 2;
+    if (bt_override > 0) bt = bt_override < 16 ? bt_override : 16;
+    if (bt > B) bt = B;
+    p.nbt = (B + bt - 1) / bt;
+    if ((long)NH * p.nbt * K > num_cu) return p;
+    p.BT = bt;
+    p.r4 = bt >= 3 ? 4 : bt;
+    p.groups = NH * p.nbt;
+    p.grid = p.groups * K;
+    p.lds = sizeof(uint16_t) * 2 * (size_t)bt * (G * Dh + 8) + sizeof(float) * (size_t)(p.ks - 1) * p.nb * 256;
+    p.ok = 1;
+    return p;
+}
+
+hipError_t launch_rec_bwd(const BwdPlan &p, const BwdArgs &m, hipStream_t s) {
+    hipLaunchKernelGGL(clear_words_bwd_kernel, dim3(1), dim3(64), 0, s, m.flag, 1L);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (p.K > 1) {
+        const long words = 2L * p.groups * 2 * p.BT * (4 * m.Dh / 2);
+        hipLaunchKernelGGL(clear_words_bwd_kernel, dim3(64), dim3(256), 0, s,
+                           reinterpret_cast<unsigned *>(m.xg), words);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    switch (p.kcw) {
+        case 16: return launch_bwd_rows<16>(p, m, s);
+        case 8: return launch_bwd_rows<8>(p, m, s);
+        default: return launch_bwd_rows<4>(p, m, s);
+    }
+}
+
+hipError_t launch_hprev_bf16(const float *h0, const float *h_seq, uint16_t *hprev, long BH,
+                             long total, hipStream_t s) {
+    hipLaunchKernelGGL(hprev_bf16_kernel, dim3(1024), dim3(256), 0, s, h0, h_seq, hprev, BH, total);
+    return hipGetLastError();
+}
+
+hipError_t launch_db_reduce(const float *db_part, int nbt, int N, float *db, hipStream_t s) {
+    hipLaunchKernelGGL(db_reduce_kernel, dim3((N + 255) / 256), dim3(256), 0, s, db_part, nbt, N, db);
+    return hipGetLastError();
+}
+
+}  // namespace rnn355

@@ -91,3 +91,22 @@ def test_invalid_arguments_are_rejected_before_launch():
     assert lib.rnn_rec_gru(ctypes.byref(d), g.RNN_BF16, None, ok[1], None, None, ok[2],
                            _p(FAKE), 1 << 20, None) == g.RNN_ERR_INVALID_ARG
     assert lib.rnn_workspace_status(None, 0, None) == g.RNN_ERR_INVALID_ARG
+
+
+def test_backward_rejects_unsupported_and_invalid_before_launch():
+    lib = g.load()
+    d = g.Dims(8, 2, 32, 2, 64)
+    ptrs = [_p(FAKE + 256 * i) for i in range(17)]
+    # f32 backward has no kernel in this build
+    assert lib.rnn_bwd_lstm(ctypes.byref(d), g.RNN_F32, *ptrs, _p(FAKE), 1 << 30,
+                            None) == g.RNN_ERR_UNSUPPORTED
+    # a required gradient output missing
+    bad = list(ptrs)
+    bad[11] = None  # dx
+    assert lib.rnn_bwd_lstm(ctypes.byref(d), g.RNN_BF16, *bad, _p(FAKE), 1 << 30,
+                            None) == g.RNN_ERR_INVALID_ARG
+    # workspace too small
+    assert lib.rnn_bwd_lstm(ctypes.byref(d), g.RNN_BF16, *ptrs, _p(FAKE), 64,
+                            None) == g.RNN_ERR_WORKSPACE
+    need = g.workspace_size(g.OP_BWD_LSTM, d, g.RNN_BF16)
+    assert need > 8 * 2 * (2 * 4 * 64) * 4  # holds at least the recomputed pre-activations

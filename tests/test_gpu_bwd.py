@@ -1,0 +1,124 @@
+"""GPU parity of the LSTM backward (BPTT) against the oracle.
+
+The GPU backward runs on the GPU forward's h_seq / c_seq; the oracle runs
+its own forward.  Bar: normwise 2e-2 on every gradient (bf16 operands, f32
+accumulation; dA is rounded to bf16 only as the operand of the dx, dW, dR
+contractions)."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import dev, host, nerr
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import gru_recurrence_amd as g  # noqa: E402
+
+TOL = 2e-2
+
+
+@pytest.fixture(autouse=True)
+def _clean_env():
+    keys = ("RNN355_REC_BT", "RNN355_REC_K")
+    old = {k: os.environ.pop(k, None) for k in keys}
+    yield
+    for k in keys:
+        os.environ.pop(k, None)
+        if old[k] is not None:
+            os.environ[k] = old[k]
+
+
+def gpu_bwd(c, final=False):
+    x, W, R, b = dev(c, "x"), dev(c, "W"), dev(c, "R"), dev(c, "b")
+    h0, c0 = dev(c, "h0"), dev(c, "c0")
+    h_seq, c_seq, _, _ = g.lstm_fwd(x, W, R, b, h0, c0)
+    grads = g.lstm_bwd(x, W, R, b, h0, c0, h_seq, c_seq, dev(c, "dH"),
+                       dev(c, "dhT") if final else None, dev(c, "dcT") if final else None)
+    torch.cuda.synchronize()
+    return {k: host(v) for k, v in grads.items()}
+
+
+@pytest.mark.parametrize("Dh,B,bt,final", [
+    (32, 3, None, False),     # one workgroup per head, dA through LDS
+    (64, 5, 2, True),         # two row slots, ragged, final-state gradients
+    (128, 3, 4, False),       # four row slots
+    (128, 2, None, True),
+    (256, 3, None, True),     # several workgroups per head, dA as tagged words
+    (256, 5, 4, False),
+])
+def test_lstm_backward_small(Dh, B, bt, final):
+    if bt is not None:
+        os.environ["RNN355_REC_BT"] = str(bt)
+    d = synth.Dims(T=19, B=B, Din=64, NH=2, Dh=Dh)
+    c = synth.make_case("lstm", d, "bf16", 9000 + Dh + B, bias="forget+1", h0_var=0.2,
+                        c0_var=0.2, backward=True, final_grads=final)
+    got = gpu_bwd(c, final)
+    ref = oracle.lstm_bwd(c.f64("x"), c.f64("W"), c.f64("R"), c.f64("b"), c.f64("h0"),
+                          c.f64("c0"), c.f64("dH"), c.f64("dhT") if final else None,
+                          c.f64("dcT") if final else None, NH=d.NH, Dh=d.Dh)
+    for k in ("dx", "dW", "dR", "db", "dh0", "dc0"):
+        e = nerr(got[k], ref[k])
+        print("  %-4s nerr=%.3e" % (k, e), flush=True)
+        assert e <= TOL, (k, e)
+
+
+def test_lstm_backward_bitwise_repeatable():
+    d = synth.Dims(T=11, B=2, Din=32, NH=2, Dh=256)
+    c = synth.make_case("lstm", d, "bf16", 9100, bias="forget+1", backward=True)
+    a, b = gpu_bwd(c), gpu_bwd(c)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_backward_workload_full_size_sampled():
+    """LSTM forward+BPTT, B=16, NH=4, Dh=256, T=1024, Din=1024 at full size.
+    The oracle recomputes 19 whole chains: every batch row of head 1 and
+    every head of batch row 3.  Compared: dh0/dc0 of those chains, db, dW
+    and dR entries of head 1's columns, dx entries of batch row 3."""
+    w = synth.WORKLOADS["lstm_fwdbwd_b16_nh4_dh256"]
+    c = synth.workload_case(w)
+    d = w.dims
+    got = gpu_bwd(c)
+    n1, b3 = 1, 3
+    mask = np.zeros((d.B, d.NH), bool)
+    mask[:, n1] = True
+    mask[b3, :] = True
+    ref = oracle.lstm_bwd(c.f64("x"), c.f64("W"), c.f64("R"), c.f64("b"), c.f64("h0"),
+                          c.f64("c0"), c.f64("dH"), NH=d.NH, Dh=d.Dh, chain_mask=mask, grads=())
+    H, GD = d.NH * d.Dh, 4 * d.Dh
+    for b, n in [(0, n1), (15, n1), (b3, 0), (b3, 3)]:
+        sl = slice(n * d.Dh, (n + 1) * d.Dh)
+        for k in ("dh0", "dc0"):
+            e = nerr(got[k][b, sl], ref[k][b, sl])
+            print("  chain (b=%d,n=%d) %s nerr=%.3e" % (b, n, k, e), flush=True)
+            assert e <= TOL, (b, n, k, e)
+    rng = np.random.default_rng(5)
+    args = (c.f64("x"), c.f64("W"), c.f64("h0"), ref["h_seq"], ref["dA"], ref["dA"])
+    kw = dict(NH=d.NH, Dh=d.Dh, G=4)
+    cols = n1 * GD + np.arange(GD)
+    db_ref = oracle.param_grad_entries("db", cols[:, None], *args, **kw)
+    e = nerr(got["db"][cols], db_ref)
+    print("  db (head %d) nerr=%.3e" % (n1, e), flush=True)
+    assert e <= TOL
+    kk = rng.integers(0, d.Din, 256)
+    cc = n1 * GD + rng.integers(0, GD, 256)
+    dW_ref = oracle.param_grad_entries("dW", np.stack([kk, cc], 1), *args, **kw)
+    e = nerr(got["dW"][kk, cc], dW_ref)
+    print("  dW entries nerr=%.3e" % e, flush=True)
+    assert e <= TOL
+    ii = rng.integers(0, d.Dh, 256)
+    jj = rng.integers(0, GD, 256)
+    dR_ref = oracle.param_grad_entries("dR", np.stack([np.full(256, n1), ii, jj], 1), *args, **kw)
+    e = nerr(got["dR"][n1, ii, jj], dR_ref)
+    print("  dR entries nerr=%.3e" % e, flush=True)
+    assert e <= TOL
+    tt = rng.integers(0, d.T, 256)
+    kx = rng.integers(0, d.Din, 256)
+    dx_ref = oracle.param_grad_entries("dx", np.stack([tt * d.B + b3, kx], 1), *args, **kw)
+    e = nerr(got["dx"][tt, b3, kx], dx_ref)
+    print("  dx entries (row %d) nerr=%.3e" % (b3, e), flush=True)
+    assert e <= TOL
