@@ -164,6 +164,17 @@ def main():
     plan = g.plan_describe(op, dims, dtc)
     stream = torch.cuda.current_stream()
 
+    backward = w.backward
+    if backward:
+        dH = to_dev("dH")
+        ws_b = torch.empty(g.workspace_size(g.OP_BWD_LSTM, dims, dtc), dtype=torch.uint8, device=dev)
+        grads = dict(dx=torch.empty((d.T, d.B, d.Din), dtype=f32, device=dev),
+                     dW=torch.empty((d.Din, N), dtype=f32, device=dev),
+                     dR=torch.empty((d.NH, d.Dh, 4 * d.Dh), dtype=f32, device=dev),
+                     db=torch.empty((N,), dtype=f32, device=dev),
+                     dh0=torch.empty((d.B, H), dtype=f32, device=dev),
+                     dc0=torch.empty((d.B, H), dtype=f32, device=dev))
+
     def step(evs=None):
         if evs is not None:
             evs[0].record(stream)
@@ -176,11 +187,16 @@ def main():
             g.rec_gru(gx, R, h0, ws=ws, out=outs, stream=stream)
         if evs is not None:
             evs[2].record(stream)
+        if backward:
+            g.lstm_bwd(x, W, R, b, h0, c0, outs["h_seq"], outs["c_seq"], dH, ws=ws_b,
+                       out=grads, stream=stream)
+            if evs is not None:
+                evs[3].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -195,11 +211,13 @@ def main():
         sys.exit(1)
 
     ms_step = 1e3 * wall / args.steps
-    rflops = recurrent_flops(w)
+    # forward + backward: the reverse sweep's dA R^T products add the same
+    # recurrent flops again
+    rflops = recurrent_flops(w) * (2 if backward else 1)
     value = rflops / (ms_step * 1e-3) / 1e12
     rec_avg = float(np.mean(rec_ms))
     proj_avg = float(np.mean(proj_ms))
-    achieved = rflops / (rec_avg * 1e-3) / 1e12
+    achieved = recurrent_flops(w) / (rec_avg * 1e-3) / 1e12
     gemm_flops = 2.0 * d.T * d.B * d.Din * N
     ncu_engaged = int(plan.split(" wg=")[1].split()[0])
     out = {
@@ -236,6 +254,10 @@ def main():
                      "traffic": traffic_per_launch()},
         "cpu_baseline": None,
     }
+    if backward:
+        bwd_ms = [e[2].elapsed_time(e[3]) for e in evs]
+        out["backward"] = {"avg_call_ms": round(float(np.mean(bwd_ms)), 4),
+                           "note": "rnn_bwd_lstm: recompute GEMMs, reverse sweep, dx/dW/dR GEMMs"}
     if not args.no_cpu and lstm:
         out["cpu_baseline"] = cpu_baseline(w, c, args.cpu_budget)
     print(json.dumps(out), flush=True)

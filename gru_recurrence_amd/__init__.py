@@ -285,19 +285,19 @@ def rec_gru(gx, R, h0=None, *, with_seq=True, ws=None, out=None, stream=None):
 
 
 def lstm_bwd(x, W, R, b, h0, c0, h_seq, c_seq, dh_seq, dhT=None, dcT=None, *, ws=None,
-             stream=None):
-    """Multi-head LSTM BPTT.  Returns dict dx, dW, dR, db, dh0, dc0."""
+             out=None, stream=None):
+    """Multi-head LSTM BPTT.  Returns dict dx, dW, dR, db, dh0, dc0 (taken
+    from ``out`` where given, else allocated)."""
     torch = _torch()
     d, dt, N = _common(x, W, R, 4)
     H = d.NH * d.Dh
     dev = x.device
     f32 = torch.float32
-    g = dict(dx=torch.empty((d.T, d.B, d.Din), dtype=f32, device=dev),
-             dW=torch.empty((d.Din, N), dtype=f32, device=dev),
-             dR=torch.empty((d.NH, d.Dh, 4 * d.Dh), dtype=f32, device=dev),
-             db=torch.empty((N,), dtype=f32, device=dev),
-             dh0=torch.empty((d.B, H), dtype=f32, device=dev),
-             dc0=torch.empty((d.B, H), dtype=f32, device=dev))
+    shapes = dict(dx=(d.T, d.B, d.Din), dW=(d.Din, N), dR=(d.NH, d.Dh, 4 * d.Dh), db=(N,),
+                  dh0=(d.B, H), dc0=(d.B, H))
+    out = out or {}
+    g = {k: out[k] if out.get(k) is not None else torch.empty(v, dtype=f32, device=dev)
+         for k, v in shapes.items()}
     ws = _workspace(OP_BWD_LSTM, d, dt, dev, ws)
     seq = (d.T, d.B, H)
     s = load().rnn_bwd_lstm(ctypes.byref(d), dt, _ptr(x, "x"), _ptr(W, "W"), _ptr(R, "R"),
@@ -307,8 +307,10 @@ def lstm_bwd(x, W, R, b, h0, c0, h_seq, c_seq, dh_seq, dhT=None, dcT=None, *, ws
                             _ptr(dh_seq, "dh_seq", f32, seq),
                             _ptr(dhT, "dhT", f32, (d.B, H), True),
                             _ptr(dcT, "dcT", f32, (d.B, H), True),
-                            _ptr(g["dx"], "dx"), _ptr(g["dW"], "dW"), _ptr(g["dR"], "dR"),
-                            _ptr(g["db"], "db"), _ptr(g["dh0"], "dh0"), _ptr(g["dc0"], "dc0"),
+                            _ptr(g["dx"], "dx", f32, shapes["dx"]), _ptr(g["dW"], "dW", f32, shapes["dW"]),
+                            _ptr(g["dR"], "dR", f32, shapes["dR"]), _ptr(g["db"], "db", f32, shapes["db"]),
+                            _ptr(g["dh0"], "dh0", f32, shapes["dh0"]),
+                            _ptr(g["dc0"], "dc0", f32, shapes["dc0"]),
                             _ptr(ws, "ws"), ws.numel(), _stream(stream))
     _check(s, "rnn_bwd_lstm")
     return g

@@ -5,6 +5,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <algorithm>
 #include <mutex>
 
 #include "../../include/rnn355.h"
@@ -52,7 +53,7 @@ size_t gx_bytes(const rnn_dims *d, int G) {
 // pre-activations A (f32), gate gradients dA (bf16), h_{t-1} (bf16) and the
 // per-batch-tile bias-gradient partials.
 struct BwdLayout {
-    size_t xchg, A, dA, hprev, dbp, total;
+    size_t xchg, A, dA, hprev, dbp, part, total;
 };
 BwdLayout bwd_layout(const rnn_dims *d) {
     BwdLayout L{};
@@ -64,6 +65,10 @@ BwdLayout bwd_layout(const rnn_dims *d) {
     L.dA = off;   off += align_up(sizeof(uint16_t) * TB * N);
     L.hprev = off; off += align_up(sizeof(uint16_t) * TB * H);
     L.dbp = off;  off += align_up(sizeof(float) * (size_t)d->B * N);
+    // split-K partials of the dW and dR contractions (used one after the other)
+    const size_t pw = gemm_partial_bytes(d->Din, (int)N, 1, kMaxSplitK);
+    const size_t pr = gemm_partial_bytes(d->Dh, 4 * d->Dh, d->NH, kMaxSplitK);
+    L.part = off; off += align_up(pw > pr ? pw : pr);
     L.total = off;
     return L;
 }
@@ -370,10 +375,14 @@ rnn_status rnn_bwd_lstm(const rnn_dims *d, rnn_dtype dt, const void *x, const vo
     }
     // 3. parameter and input gradients from dA
     if (!ok(launch_db_reduce(dbp, p.nbt, N, db, stream))) return RNN_ERR_HIP;
+    float *part = (float *)(base + L.part);
+    const int cus = device_cus();
     {
         GemmArgs g{};  // dW[k][c] = sum_m x[m][k] dA[m][c]
         g.M = Din; g.N = N; g.K = M;
         g.A = xb; g.lda = Din; g.B = dA; g.ldb = N; g.C = dW; g.ldc = N;
+        g.ksplit = std::min(gemm_splitk_for(Din, N, M, 1, cus), kMaxSplitK);
+        g.partial = part;
         if (!ok(launch_gemm_bf16(g, false, false, 1, stream))) return RNN_ERR_HIP;
     }
     {
@@ -388,6 +397,8 @@ rnn_status rnn_bwd_lstm(const rnn_dims *d, rnn_dtype dt, const void *x, const vo
         g.A = hprev; g.lda = H; g.strideA = Dh;
         g.B = dA; g.ldb = N; g.strideB = GD;
         g.C = dR; g.ldc = GD; g.strideC = (long)Dh * GD;
+        g.ksplit = std::min(gemm_splitk_for(Dh, GD, M, NH, cus), kMaxSplitK);
+        g.partial = part;
         if (!ok(launch_gemm_bf16(g, false, false, NH, stream))) return RNN_ERR_HIP;
     }
     return RNN_OK;

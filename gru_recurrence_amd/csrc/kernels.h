@@ -21,7 +21,15 @@ struct GemmArgs {
     long ldc, strideC;
     int accumulate;           // C += product
     uint32_t *clear_words;    // if set, block 0 zeroes 64 words (status header)
+    int ksplit;               // K slices (0 or 1: none); > 1 needs `partial`
+    float *partial;           // [batch][ksplit][M][N] slice partials (workspace)
 };
+
+// Largest useful K split (a power of two <= what fills num_cu CUs, keeping
+// >= 8 K tiles per slice) and the partial-buffer bytes it needs.
+int gemm_splitk_for(int M, int N, int K, int batch, int num_cu);
+size_t gemm_partial_bytes(int M, int N, int batch, int ksplit);
+constexpr int kMaxSplitK = 8;
 
 // float32 contraction with explicit strides: A(m,k) = A[m*sam + k*sak],
 // B(k,n) = B[k*sbk + n*sbn].
