@@ -210,15 +210,21 @@ def lstm_fwd(x, W, R, b=None, h0=None, c0=None, *, with_seq: bool = True, ws=Non
     return h_seq, c_seq, hT, cT
 
 
-def gru_fwd(x, W, R, b=None, h0=None, *, with_seq: bool = True, ws=None, stream=None):
+def gru_fwd(x, W, R, b=None, h0=None, *, with_seq: bool = True, ws=None, out=None,
+            stream=None):
     """Multi-head GRU forward (reset-after).  Returns (h_seq, hT)."""
     torch = _torch()
     d, dt, N = _common(x, W, R, 3)
     H = d.NH * d.Dh
     dev = x.device
     f32 = torch.float32
-    h_seq = torch.empty((d.T, d.B, H), dtype=f32, device=dev) if with_seq else None
-    hT = torch.empty((d.B, H), dtype=f32, device=dev)
+    if out is None:
+        out = {}
+    h_seq = out.get("h_seq") if with_seq else None
+    if with_seq and h_seq is None:
+        h_seq = torch.empty((d.T, d.B, H), dtype=f32, device=dev)
+    hT = out.get("hT")
+    hT = torch.empty((d.B, H), dtype=f32, device=dev) if hT is None else hT
     ws = _workspace(OP_FWD_GRU, d, dt, dev, ws)
     s = load().rnn_fwd_gru(ctypes.byref(d), dt, _ptr(x, "x"), _ptr(W, "W"), _ptr(R, "R"),
                            _ptr(b, "b", f32, (N,), True), _ptr(h0, "h0", f32, (d.B, H), True),

@@ -39,6 +39,8 @@ int gates_of_op(rnn_op op) {
 
 int cell_of_op(rnn_op op) { return gates_of_op(op) == 4 ? kLSTM : kGRU; }
 
+int gates_of_cell(int cell) { return cell == kLSTM ? 4 : 3; }
+
 // Exchange slots: [groups][2][BT][Dh/2] 8-byte words with groups =
 // NH * ceil(B/BT) and BT <= 16, so groups * BT <= NH * (B + 15).
 size_t xchg_bytes(const rnn_dims *d) {
@@ -48,6 +50,13 @@ size_t xchg_bytes(const rnn_dims *d) {
 size_t gx_bytes(const rnn_dims *d, int G) {
     return align_up(sizeof(float) * (size_t)d->T * d->B * d->NH * G * d->Dh);
 }
+
+// Row-panel counters of the pipelined forward (one word per kGemmRowTile
+// rows of gx), after gx in the forward workspace.
+long gx_panels(const rnn_dims *d) {
+    return ((long)d->T * d->B + kGemmRowTile - 1) / kGemmRowTile;
+}
+size_t ready_bytes(const rnn_dims *d) { return align_up(sizeof(unsigned) * (size_t)gx_panels(d)); }
 
 // Backward workspace after the header: dA exchange slots, recomputed
 // pre-activations A (f32), gate gradients dA (bf16), h_{t-1} (bf16) and the
@@ -96,6 +105,12 @@ int env_int(const char *name) {
     return e ? atoi(e) : 0;
 }
 int bt_override() { return env_int("RNN355_REC_BT"); }
+// RNN355_PIPELINE=0 runs the forward's two phases one after the other;
+// =1 overlaps them wherever that is safe, also where the plan would not.
+int pipeline_override() {
+    const char *e = getenv("RNN355_PIPELINE");
+    return !e || !e[0] ? -1 : e[0] == '0' ? 0 : 1;
+}
 int k_override() { return env_int("RNN355_REC_K"); }
 // Polls of a multi-CU step wait before it is declared lost (~4 s by default;
 // tests lower it to force the time-out path).
@@ -108,6 +123,7 @@ unsigned spin_limit() {
 // {32, 64, 128}), the multi-CU kernel (bf16, Dh >= 256, Dh % 128 == 0), or
 // the LDS kernel (f32, other shapes whose R fits 64 KiB of LDS).
 struct Choice {
+    int cell;
     RecPlan rec;
     McPlan mc;
     bool use_mc;
@@ -116,6 +132,7 @@ struct Choice {
 
 Choice choose(int cell, const rnn_dims *d, rnn_dtype dt, int num_cu) {
     Choice c{};
+    c.cell = cell;
     const bool bf16 = dt == RNN_BF16;
     c.rec = plan_rec(cell, d->T, d->B, d->NH, d->Dh, bf16, num_cu, bt_override());
     if (c.rec.kind == kRecMfma) {
@@ -140,7 +157,8 @@ bool gemm_shape_ok(int K, int N, rnn_dtype dt) {
 }
 
 rnn_status input_proj(int M, int K, int N, rnn_dtype dt, const void *x, const void *W,
-                      const float *b, float *gx, uint32_t *clear, hipStream_t s) {
+                      const float *b, float *gx, uint32_t *clear, hipStream_t s,
+                      unsigned *ready = nullptr) {
     hipError_t e;
     if (dt == RNN_BF16) {
         GemmArgs g{};
@@ -149,6 +167,7 @@ rnn_status input_proj(int M, int K, int N, rnn_dtype dt, const void *x, const vo
         g.B = (const uint16_t *)W; g.ldb = N; g.strideB = 0;
         g.bias = b; g.C = gx; g.ldc = N; g.strideC = 0;
         g.accumulate = 0; g.clear_words = clear;
+        g.ready = ready;
         e = launch_gemm_bf16(g, true, false, 1, s);
     } else {
         GemmF32Args g{};
@@ -194,6 +213,99 @@ bool rec_supported(int cell, const rnn_dims *d, rnn_dtype dt) {
     return choose(cell, d, dt, device_cus()).ok;
 }
 
+// Whether the forward overlaps its two phases (see forward()): the
+// recurrence must leave at least half the CUs free, and the projection must
+// take more than two waves of output tiles on those CUs -- otherwise the
+// first row panel is ready about when the whole projection would be, and
+// the overlap only adds the cost of running the two side by side.
+bool pipelined(const Choice &ch, const rnn_dims *d, rnn_dtype dt, int cus) {
+    const int force = pipeline_override();
+    if (dt != RNN_BF16 || ch.use_mc || ch.rec.kind != kRecMfma || 2 * ch.rec.grid > cus ||
+        force == 0 || gx_panels(d) < 2)
+        return false;
+    if (force == 1) return true;
+    const int G = gates_of_cell(ch.cell);
+    const long tiles = gx_panels(d) * (((long)d->NH * G * d->Dh + kGemmColTile - 1) / kGemmColTile);
+    return tiles > 2L * (cus - ch.rec.grid);
+}
+
+// Side stream and fork/join events of the pipelined forward, one set per
+// device, created on first use and kept for the life of the process.  The
+// side stream is non-blocking (no implicit order with the legacy default
+// stream) and has the default priority.
+struct Pipe {
+    std::mutex mu;
+    bool tried = false;
+    hipStream_t side = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+
+Pipe *pipe_of_current_device() {
+    static Pipe pipes[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    return &pipes[dev];
+}
+
+// Forward = input projection + recurrence.  Pipelined when the recurrence is
+// the one-CU MFMA kernel and leaves at least half the CUs free: the
+// projection runs on the side stream in time order and publishes finished
+// row panels; the recurrence, on the caller's stream, waits for the panels
+// of each group of steps before loading them.  The projection never waits,
+// and the recurrence's workgroups leave CUs free for it, so both finish
+// however the two grids are placed.  The caller's stream joins the side
+// stream before returning, so stream order is as for one kernel.
+rnn_status forward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, const void *W,
+                   const void *R, const float *b, const float *h0, const float *c0,
+                   float *h_seq, float *c_seq, float *hT, float *cT, void *ws, hipStream_t s) {
+    const int G = cell == kLSTM ? 4 : 3;
+    const int N = d->NH * G * d->Dh, M = d->T * d->B;
+    float *gx = (float *)((char *)ws + kHeader + xchg_bytes(d));
+    unsigned *ready = (unsigned *)((char *)gx + gx_bytes(d, G));
+    const int cus = device_cus();
+    const Choice ch = choose(cell, d, dt, cus);
+    if (!ch.ok) return RNN_ERR_UNSUPPORTED;
+    const long panels = gx_panels(d);
+    Pipe *pp = pipelined(ch, d, dt, cus) ? pipe_of_current_device() : nullptr;
+    if (pp) {
+        std::lock_guard<std::mutex> lk(pp->mu);
+        if (!pp->tried) {
+            pp->tried = true;
+            if (hipStreamCreateWithFlags(&pp->side, hipStreamNonBlocking) != hipSuccess ||
+                hipEventCreateWithFlags(&pp->fork, hipEventDisableTiming) != hipSuccess ||
+                hipEventCreateWithFlags(&pp->join, hipEventDisableTiming) != hipSuccess)
+                pp->side = nullptr;
+        }
+        if (pp->side) {
+            auto ok = [](hipError_t e) { return e == hipSuccess; };
+            if (!ok(launch_clear_u32((unsigned *)ws, 64, ready, panels, s)) ||
+                !ok(hipEventRecord(pp->fork, s)) ||
+                !ok(hipStreamWaitEvent(pp->side, pp->fork, 0)))
+                return RNN_ERR_HIP;
+            if (input_proj(M, d->Din, N, dt, x, W, b, gx, nullptr, pp->side, ready) != RNN_OK)
+                return RNN_ERR_HIP;
+            if (!ok(hipEventRecord(pp->join, pp->side))) return RNN_ERR_HIP;
+            RecArgs a{};
+            a.T = d->T; a.B = d->B; a.NH = d->NH; a.Dh = d->Dh; a.BT = ch.rec.BT;
+            a.gx = gx;
+            a.Rb = (const uint16_t *)R;
+            a.h0 = h0; a.c0 = c0; a.h_seq = h_seq; a.c_seq = c_seq; a.hT = hT; a.cT = cT;
+            a.ready = ready;
+            a.ready_target = (unsigned)((N + kGemmColTile - 1) / kGemmColTile);  // tiles per panel
+            a.panels = (int)panels;
+            a.flag = (unsigned *)ws;
+            a.spin_limit = spin_limit();
+            const hipError_t e = launch_rec_fwd(cell, ch.rec, a, true, s);
+            // join even after a failed launch: the side stream's work is queued
+            const hipError_t ej = hipStreamWaitEvent(s, pp->join, 0);
+            return (e == hipSuccess && ej == hipSuccess) ? RNN_OK : RNN_ERR_HIP;
+        }
+    }
+    rnn_status st = input_proj(M, d->Din, N, dt, x, W, b, gx, (uint32_t *)ws, s);
+    if (st != RNN_OK) return st;
+    return rec_fwd(cell, d, dt, gx, R, h0, c0, h_seq, c_seq, hT, cT, ws, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -216,7 +328,7 @@ size_t rnn_workspace_size(rnn_op op, const rnn_dims *d, rnn_dtype dt) {
     switch (op) {
         case RNN_OP_FWD_LSTM:
         case RNN_OP_FWD_GRU:
-            return kHeader + xchg_bytes(d) + gx_bytes(d, G);
+            return kHeader + xchg_bytes(d) + gx_bytes(d, G) + ready_bytes(d);
         case RNN_OP_REC_LSTM:
         case RNN_OP_REC_GRU:
             return kHeader + xchg_bytes(d);
@@ -237,17 +349,22 @@ rnn_status rnn_plan_describe(rnn_op op, const rnn_dims *d, rnn_dtype dt, char *b
         snprintf(buf, len, "rec_kernel=none");
         return RNN_ERR_UNSUPPORTED;
     }
+    const bool fwd = op == RNN_OP_FWD_LSTM || op == RNN_OP_FWD_GRU;
+    const char *proj = !fwd ? "" : pipelined(ch, d, dt, device_cus()) ? " input_proj=pipelined"
+                                                                        : " input_proj=serial";
     if (ch.use_mc) {
         const McPlan &p = ch.mc;
         snprintf(buf, len,
                  "rec_kernel=mfma_multi_cu rows_per_wg=%d wg=%d threads=%d wg_per_head_row_tile=%d "
-                 "units_per_wg=%d k_splits=%d",
-                 p.BT, p.grid, p.threads, p.K, p.nb * 16, p.ks);
+                 "units_per_wg=%d k_splits=%d%s",
+                 p.BT, p.grid, p.threads, p.K, p.nb * 16, p.ks, proj);
     } else {
         const RecPlan &p = ch.rec;
         snprintf(buf, len,
-                 "rec_kernel=%s rows_per_wg=%d wg=%d threads=%d wg_per_head_row_tile=1 units_per_thread=%d",
-                 p.kind == kRecMfma ? "mfma_resident_R" : "lds_simple", p.BT, p.grid, p.threads, p.upt);
+                 "rec_kernel=%s rows_per_wg=%d wg=%d threads=%d wg_per_head_row_tile=1 "
+                 "units_per_thread=%d%s",
+                 p.kind == kRecMfma ? "mfma_resident_R" : "lds_simple", p.BT, p.grid, p.threads,
+                 p.upt, proj);
     }
     return RNN_OK;
 }
@@ -297,10 +414,7 @@ rnn_status rnn_fwd_lstm(const rnn_dims *d, rnn_dtype dt, const void *x, const vo
     const int N = d->NH * 4 * d->Dh;
     if (!gemm_shape_ok(d->Din, N, dt) || !rec_supported(kLSTM, d, dt)) return RNN_ERR_UNSUPPORTED;
     if (!ws || ws_bytes < rnn_workspace_size(RNN_OP_FWD_LSTM, d, dt)) return RNN_ERR_WORKSPACE;
-    float *gx = (float *)((char *)ws + kHeader + xchg_bytes(d));
-    rnn_status st = input_proj(d->T * d->B, d->Din, N, dt, x, W, b, gx, (uint32_t *)ws, stream);
-    if (st != RNN_OK) return st;
-    return rec_fwd(kLSTM, d, dt, gx, R, h0, c0, h_seq, c_seq, hT, cT, ws, stream);
+    return forward(kLSTM, d, dt, x, W, R, b, h0, c0, h_seq, c_seq, hT, cT, ws, stream);
 }
 
 rnn_status rnn_fwd_gru(const rnn_dims *d, rnn_dtype dt, const void *x, const void *W,
@@ -313,10 +427,7 @@ rnn_status rnn_fwd_gru(const rnn_dims *d, rnn_dtype dt, const void *x, const voi
     const int N = d->NH * 3 * d->Dh;
     if (!gemm_shape_ok(d->Din, N, dt) || !rec_supported(kGRU, d, dt)) return RNN_ERR_UNSUPPORTED;
     if (!ws || ws_bytes < rnn_workspace_size(RNN_OP_FWD_GRU, d, dt)) return RNN_ERR_WORKSPACE;
-    float *gx = (float *)((char *)ws + kHeader + xchg_bytes(d));
-    rnn_status st = input_proj(d->T * d->B, d->Din, N, dt, x, W, b, gx, (uint32_t *)ws, stream);
-    if (st != RNN_OK) return st;
-    return rec_fwd(kGRU, d, dt, gx, R, h0, nullptr, h_seq, nullptr, hT, nullptr, ws, stream);
+    return forward(kGRU, d, dt, x, W, R, b, h0, nullptr, h_seq, nullptr, hT, nullptr, ws, stream);
 }
 
 rnn_status rnn_bwd_lstm(const rnn_dims *d, rnn_dtype dt, const void *x, const void *W,

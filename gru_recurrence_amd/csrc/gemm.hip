@@ -40,6 +40,7 @@ namespace {
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 constexpr int BM = 256, BN = 256, BK = 64;
+static_assert(BM == kGemmRowTile && BN == kGemmColTile, "row-panel counters assume the output tile");
 constexpr int LDS_LD = BK + 8;  // bf16 per LDS row: 144 bytes (bank spread, 16-byte aligned)
 constexpr int NTHR = 512;
 constexpr int STAGE = (BM + BN) * LDS_LD;  // bf16 per LDS stage
@@ -127,13 +128,26 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(GemmArgs g) {
     const uint16_t *A = g.A + (long)bz * g.strideA;
     const uint16_t *B = g.B + (long)bz * g.strideB;
 
-    // XCD-contiguous tile order
+    // Tile order: runs of 8 row tiles, row tile 8q + x of a run on XCD x
+    // (workgroup i runs on XCD i % 8) with all its column tiles, so an XCD's
+    // L2 shares that row panel of A, and row tiles finish roughly in order
+    // (a consumer of the rows, e.g. the time steps of a recurrence, can
+    // start on the first ones).  Rows past the last whole run go in order.
     const int tiles_n = (g.N + BN - 1) / BN;
-    const int nt = gridDim.x;
+    const int tiles_m = (g.M + BM - 1) / BM;
     const int bid = blockIdx.x;
-    int t = bid;
-    if ((nt & 7) == 0) t = (bid & 7) * (nt >> 3) + (bid >> 3);
-    const int m0 = (t / tiles_n) * BM, n0 = (t % tiles_n) * BN;
+    const int run = 8 * tiles_n, full = (tiles_m >> 3) * run;
+    int mt, nt;
+    if (bid < full) {
+        const int q = bid / run, i = bid - q * run;
+        mt = 8 * q + (i & 7);
+        nt = i >> 3;
+    } else {
+        const int i = bid - full;
+        mt = (tiles_m & ~7) + i / tiles_n;
+        nt = i % tiles_n;
+    }
+    const int m0 = mt * BM, n0 = nt * BN;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 2, wn = wave & 3;
@@ -235,6 +249,19 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(GemmArgs g) {
             }
         }
     }
+    if (g.ready) {
+        // publish the finished tile: every wave waits until its stores have
+        // reached the XCD's L2 (vmcnt 0), then, after the barrier, one
+        // thread writes the L2 back to memory (device-scope release) and
+        // counts the tile of its row panel.  One write-back per tile rather
+        // than one per wave: each write-back stalls every wave of the XCD.
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        __syncthreads();
+        if (tid == 0) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            __hip_atomic_fetch_add(g.ready + mt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
 }
 
 // C = sum over slices of the partials (+ bias) (+ old C), slices in order.
@@ -322,6 +349,7 @@ hipError_t launch_gemm_bf16(const GemmArgs &g0, bool a_kmajor, bool b_kmajor, in
     GemmArgs g = g0;
     if (g.ksplit < 1) g.ksplit = 1;
     if (g.ksplit > 1 && !g.partial) return hipErrorInvalidValue;
+    if (g.ready && (g.ksplit > 1 || batch != 1)) return hipErrorInvalidValue;
     hipError_t e;
     if (a_kmajor && !b_kmajor) e = launch_t<true, false>(g, batch, s);
     else if (a_kmajor && b_kmajor) e = launch_t<true, true>(g, batch, s);

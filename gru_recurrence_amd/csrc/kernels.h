@@ -23,7 +23,12 @@ struct GemmArgs {
     uint32_t *clear_words;    // if set, block 0 zeroes 64 words (status header)
     int ksplit;               // K slices (0 or 1: none); > 1 needs `partial`
     float *partial;           // [batch][ksplit][M][N] slice partials (workspace)
+    unsigned *ready;          // if set (ksplit 1, batch 1): per 256-row panel, +1 per
+                              // finished column tile, released at device scope
 };
+constexpr int kGemmRowTile = 256;  // rows per output tile of the bf16 contraction
+constexpr int kGemmColTile = 256;  // columns per output tile
+
 
 // Largest useful K split (a power of two <= what fills num_cu CUs, keeping
 // >= 8 K tiles per slice) and the partial-buffer bytes it needs.
@@ -58,6 +63,14 @@ struct RecArgs {
     const float *Rf;          // f32 R (f32 simple kernel)
     const float *h0, *c0;
     float *h_seq, *c_seq, *hT, *cT;
+    // Pipelined forward: gx is still being written by the input projection.
+    // ready[p] counts the finished column tiles of row panel p (kGemmRowTile
+    // rows of gx); a panel is complete at ready_target.  Null: gx complete.
+    const unsigned *ready;
+    unsigned ready_target;
+    int panels;
+    unsigned *flag;       // abort word, set when a wait runs out
+    unsigned spin_limit;  // polls before a wait is declared lost
 };
 
 enum RecKind { kRecNone = 0, kRecMfma = 1, kRecSimple = 2 };
@@ -78,6 +91,11 @@ struct RecPlan {
 RecPlan plan_rec(int cell, int T, int B, int NH, int Dh, bool bf16, int num_cu,
                  int bt_override);
 
+// Zeroes p[0, n) and q[0, nq) on stream s in one launch (a kernel, so it
+// may sit in a captured graph).
+hipError_t launch_clear_u32(unsigned *p, long n, unsigned *q, long nq, hipStream_t s);
+
+// a.ready set: only the MFMA kernel waits on row panels (kRecMfma plans).
 hipError_t launch_rec_fwd(int cell, const RecPlan &p, const RecArgs &a, bool bf16,
                           hipStream_t s);
 

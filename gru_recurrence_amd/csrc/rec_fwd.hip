@@ -25,6 +25,7 @@
 //     at a group start and covers requests issued a full group earlier.
 // Simple kernel (f32, or shapes the MFMA kernel does not cover): R in LDS as
 // float32, one thread per (row, gate column) dot product per step.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -80,7 +81,18 @@ __device__ __forceinline__ void lstm_or_gru_unit(const float *gpre, int DH, cons
 // the h/c outputs of the PREVIOUS group (kept in registers) are stored.  The
 // only wait on HBM then sits at the first step of a group and covers
 // operations issued a whole group earlier.
-template <int CELL, int DH, int R4, int PD>
+//
+// WAIT (pipelined forward): Gx is written by the input projection while this
+// kernel runs.  Before Gx of a step is requested, the wave checks that every
+// row panel holding rows up to that step is complete (one counter word per
+// panel, read 64 panels per poll).  The projection writes a panel's tiles
+// back to memory before it counts them, and the Gx loads here are
+// device-scope loads issued after the count was seen, which miss in this
+// CU's L1 and the XCD's L2; so no cache invalidation is needed (an acquire
+// fence would drop every cached line of the XCD, the projection's operand
+// panels included).  Panels found complete are remembered; once the
+// projection is ahead, a check costs a compare.
+template <int CELL, int DH, int R4, int PD, bool WAIT>
 __global__ __launch_bounds__(DH / 16 * 64) void rec_fwd_mfma_kernel(RecArgs a) {
     constexpr int G = CellTraits<CELL>::G;
     constexpr int GD = G * DH;
@@ -168,6 +180,35 @@ __global__ __launch_bounds__(DH / 16 * 64) void rec_fwd_mfma_kernel(RecArgs a) {
 #pragma unroll
             for (int g = 0; g < GL; ++g) bx0[s][r][g] = bx1[s][r][g] = 0.f;
         }
+    // Gx of steps [0, avail) is known complete and acquired (WAIT only).
+    int avail = WAIT ? 0 : T, panels_ok = 0;
+    auto wait_ready = [&](int tend) {
+        if constexpr (WAIT) {
+            tend = min(tend, T);
+            if (tend <= avail) return;
+            const int need = (int)(((long)tend * B + kGemmRowTile - 1) / kGemmRowTile);
+            unsigned spins = 0;
+            for (;;) {
+                const int p = panels_ok + lane;
+                const unsigned v = p < a.panels ? __hip_atomic_load(a.ready + p, __ATOMIC_RELAXED,
+                                                                    __HIP_MEMORY_SCOPE_AGENT)
+                                                : a.ready_target;
+                const unsigned long long done = __ballot(v >= a.ready_target);
+                const int run = ~done == 0ull ? 64 : __builtin_ctzll(~done);
+                panels_ok = min(panels_ok + run, a.panels);
+                if (panels_ok >= need) break;
+                if (++spins >= a.spin_limit) {
+                    if (lane == 0)
+                        __hip_atomic_store(a.flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    panels_ok = a.panels;  // give up waiting; the results are void
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(8);
+            }
+            avail = panels_ok >= a.panels ? T
+                                          : (int)min((long)T, (long)panels_ok * kGemmRowTile / B);
+        }
+    };
     // Gx of steps [tg, tg+PD) into dst (steps at or past T are skipped).
     auto load_group = [&](int tg, float (&dst)[PD][R4][GL]) {
         const float *src = gx_tile + (long)tg * gx_step;
@@ -178,7 +219,13 @@ __global__ __launch_bounds__(DH / 16 * 64) void rec_fwd_mfma_kernel(RecArgs a) {
                 for (int r = 0; r < R4; ++r) {
                     if (ld[r]) {
 #pragma unroll
-                        for (int g = 0; g < GL; ++g) dst[s][r][g] = src[go[r] + g * DH];
+                        for (int g = 0; g < GL; ++g) {
+                            if constexpr (WAIT)
+                                dst[s][r][g] = __hip_atomic_load(src + go[r] + g * DH, __ATOMIC_RELAXED,
+                                                                 __HIP_MEMORY_SCOPE_AGENT);
+                            else
+                                dst[s][r][g] = src[go[r] + g * DH];
+                        }
                     }
                 }
             }
@@ -238,6 +285,7 @@ __global__ __launch_bounds__(DH / 16 * 64) void rec_fwd_mfma_kernel(RecArgs a) {
                 for (int g = 0; g < G; ++g) acc[g] = mfma_16x16x32_bf16(af[c], rf[g][c], acc[g]);
             if (s == 0) {
                 if (tg > 0) store_group(tg - PD);
+                wait_ready(tg + 2 * PD);
                 load_group(tg + PD, nxt);
             }
             float h[R4], c[R4];
@@ -252,6 +300,7 @@ __global__ __launch_bounds__(DH / 16 * 64) void rec_fwd_mfma_kernel(RecArgs a) {
         }
     };
 
+    wait_ready(PD);
     load_group(0, bx0);
     using Full = std::integral_constant<bool, true>;
     using Part = std::integral_constant<bool, false>;
@@ -341,21 +390,35 @@ __global__ __launch_bounds__(256) void rec_fwd_simple_kernel(RecArgs a) {
 }
 
 // Rows per lane in use and the matching prefetch group length (steps).
-template <int CELL, int DH>
-hipError_t launch_mfma_rows(const RecPlan &p, const RecArgs &a, hipStream_t s) {
+template <int CELL, int DH, bool WAIT>
+void launch_mfma_rows_w(const RecPlan &p, const RecArgs &a, hipStream_t s) {
     const dim3 grid(p.grid), blk(DH / 16 * 64);
     switch (p.upt) {
         case 1:
-            hipLaunchKernelGGL((rec_fwd_mfma_kernel<CELL, DH, 1, 8>), grid, blk, 0, s, a);
+            hipLaunchKernelGGL((rec_fwd_mfma_kernel<CELL, DH, 1, 8, WAIT>), grid, blk, 0, s, a);
             break;
         case 2:
-            hipLaunchKernelGGL((rec_fwd_mfma_kernel<CELL, DH, 2, 4>), grid, blk, 0, s, a);
+            hipLaunchKernelGGL((rec_fwd_mfma_kernel<CELL, DH, 2, 4, WAIT>), grid, blk, 0, s, a);
             break;
         default:
-            hipLaunchKernelGGL((rec_fwd_mfma_kernel<CELL, DH, 4, 2>), grid, blk, 0, s, a);
+            hipLaunchKernelGGL((rec_fwd_mfma_kernel<CELL, DH, 4, 2, WAIT>), grid, blk, 0, s, a);
             break;
     }
+}
+
+template <int CELL, int DH>
+hipError_t launch_mfma_rows(const RecPlan &p, const RecArgs &a, hipStream_t s) {
+    if (a.ready) launch_mfma_rows_w<CELL, DH, true>(p, a, s);
+    else launch_mfma_rows_w<CELL, DH, false>(p, a, s);
     return hipGetLastError();
+}
+
+__global__ void clear_u32_kernel(unsigned *p, long n, unsigned *q, long nq) {
+    const long stride = (long)gridDim.x * blockDim.x;
+    for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n + nq; i += stride) {
+        if (i < n) p[i] = 0u;
+        else q[i - n] = 0u;
+    }
 }
 
 template <int CELL>
@@ -416,8 +479,16 @@ RecPlan plan_rec(int cell, int T, int B, int NH, int Dh, bool bf16, int num_cu,
     return p;
 }
 
+hipError_t launch_clear_u32(unsigned *p, long n, unsigned *q, long nq, hipStream_t s) {
+    if (n < 0 || nq < 0 || n + nq == 0) return hipSuccess;
+    const long blocks = std::min<long>(1024, (n + nq + 255) / 256);
+    hipLaunchKernelGGL(clear_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n, q, nq);
+    return hipGetLastError();
+}
+
 hipError_t launch_rec_fwd(int cell, const RecPlan &p, const RecArgs &a, bool bf16,
                           hipStream_t s) {
+    if (a.ready && p.kind != kRecMfma) return hipErrorInvalidValue;
     if (p.kind == kRecMfma) {
         return cell == kLSTM ? launch_mfma<kLSTM>(p, a, s) : launch_mfma<kGRU>(p, a, s);
     }

@@ -110,3 +110,34 @@ def test_backward_rejects_unsupported_and_invalid_before_launch():
                             None) == g.RNN_ERR_WORKSPACE
     need = g.workspace_size(g.OP_BWD_LSTM, d, g.RNN_BF16)
     assert need > 8 * 2 * (2 * 4 * 64) * 4  # holds at least the recomputed pre-activations
+
+
+def test_plans_of_the_workloads(monkeypatch):
+    """Kernel plans are pure host decisions (256 compute units assumed when
+    no device is visible): one-CU resident-R kernel for Dh <= 128, multi-CU
+    split above; the forward overlaps projection and recurrence only when
+    the recurrence leaves half the chip free and the projection is large."""
+    monkeypatch.delenv("RNN355_PIPELINE", raising=False)
+    monkeypatch.delenv("RNN355_REC_BT", raising=False)
+    monkeypatch.delenv("RNN355_REC_K", raising=False)
+    if g.plan_describe(g.OP_REC_LSTM, g.Dims(8, 16, 8, 6, 128), g.RNN_BF16).find(" wg=96 ") < 0:
+        pytest.skip("a device with other than 256 compute units is visible")
+    head = g.Dims(1024, 16, 768, 6, 128)
+    p = g.plan_describe(g.OP_FWD_LSTM, head, g.RNN_BF16)
+    assert "mfma_resident_R" in p and " wg=96 " in p and "input_proj=pipelined" in p
+    p = g.plan_describe(g.OP_FWD_GRU, g.Dims(2048, 4, 768, 12, 64), g.RNN_BF16)
+    assert "mfma_resident_R" in p and " wg=48 " in p and "input_proj=serial" in p
+    p = g.plan_describe(g.OP_FWD_LSTM, g.Dims(1024, 16, 768, 1, 768), g.RNN_BF16)
+    assert "mfma_multi_cu" in p and "input_proj=serial" in p
+    p = g.plan_describe(g.OP_FWD_LSTM, g.Dims(64, 2, 32, 1, 32), g.RNN_F32)
+    assert "lds_simple" in p and "input_proj=serial" in p
+    assert "input_proj" not in g.plan_describe(g.OP_REC_LSTM, head, g.RNN_BF16)
+    monkeypatch.setenv("RNN355_PIPELINE", "0")
+    assert "input_proj=serial" in g.plan_describe(g.OP_FWD_LSTM, head, g.RNN_BF16)
+    monkeypatch.setenv("RNN355_PIPELINE", "1")
+    small = g.Dims(233, 5, 96, 2, 64)
+    assert "input_proj=pipelined" in g.plan_describe(g.OP_FWD_LSTM, small, g.RNN_BF16)
+    # never when the recurrence would hold more than half the units
+    big = g.Dims(64, 16, 64, 16, 128)
+    p = g.plan_describe(g.OP_FWD_LSTM, big, g.RNN_BF16)
+    assert " wg=256 " in p and "input_proj=serial" in p

@@ -23,11 +23,13 @@ TOL_BF16 = 2e-2
 
 @pytest.fixture(autouse=True)
 def _no_plan_override():
-    old = os.environ.pop("RNN355_REC_BT", None)
+    keys = ("RNN355_REC_BT", "RNN355_PIPELINE")
+    old = {k: os.environ.pop(k, None) for k in keys}
     yield
-    os.environ.pop("RNN355_REC_BT", None)
-    if old is not None:
-        os.environ["RNN355_REC_BT"] = old
+    for k in keys:
+        os.environ.pop(k, None)
+        if old[k] is not None:
+            os.environ[k] = old[k]
 
 
 def run_lstm(c, **kw):
@@ -197,3 +199,88 @@ def test_gru_small_batch_workload_full_size_sampled_chains():
     chains = [(0, 0), (2, 7), (3, 11)]
     want = oracle_of(c, _chain_mask(4, 12, chains))
     _compare_chains(got, want, chains, 64, TOL_BF16, ("h_seq", "hT"))
+
+
+def _with_env(key, val, fn):
+    old = os.environ.get(key)
+    os.environ[key] = val
+    try:
+        return fn()
+    finally:
+        if old is None:
+            os.environ.pop(key, None)
+        else:
+            os.environ[key] = old
+
+
+@pytest.mark.parametrize("cell,T,B,NH,Dh,Din", [
+    ("lstm", 233, 5, 2, 64, 96),     # 1165 rows: 5 row panels, the last one ragged
+    ("gru", 300, 16, 3, 128, 64),    # 19 row panels, 16 rows per step
+    ("lstm", 96, 11, 4, 32, 32),     # 1056 rows, steps straddle panel edges
+])
+def test_pipelined_forward_matches_serial_bitwise_and_oracle(cell, T, B, NH, Dh, Din):
+    """The forward that overlaps the input projection with the recurrence
+    (row panels published by the projection, waited on by the recurrence)
+    gives bitwise the serial result, and that result matches the oracle."""
+    d = synth.Dims(T=T, B=B, Din=Din, NH=NH, Dh=Dh)
+    op = g.OP_FWD_LSTM if cell == "lstm" else g.OP_FWD_GRU
+    gd = g.Dims(T, B, Din, NH, Dh)
+    assert "input_proj=serial" in g.plan_describe(op, gd, g.RNN_BF16)   # too small to pay
+    assert "input_proj=pipelined" in _with_env("RNN355_PIPELINE", "1",
+                                               lambda: g.plan_describe(op, gd, g.RNN_BF16))
+    c = synth.make_case(cell, d, "bf16", 7500 + T, bias="forget+1" if cell == "lstm" else "zero",
+                        h0_var=0.1, c0_var=0.1 if cell == "lstm" else 0.0)
+    run = run_lstm if cell == "lstm" else run_gru
+    piped = _with_env("RNN355_PIPELINE", "1", lambda: run(c))
+    serial = _with_env("RNN355_PIPELINE", "0", lambda: run(c))
+    for k in piped:
+        assert np.array_equal(piped[k], serial[k]), k
+    keys = ("h_seq", "c_seq", "hT", "cT") if cell == "lstm" else ("h_seq", "hT")
+    compare(piped, oracle_of(c), TOL_BF16, keys)
+
+
+def test_pipelined_headline_forward_repeatable_and_equal_to_serial():
+    """Full-size multi-head LSTM (B=16, NH=6, Dh=128, T=1024): three pipelined
+    calls on one workspace (panel counters reused) and one serial call agree
+    bitwise."""
+    w = synth.WORKLOADS["lstm_mh_b16_nh6_dh128"]
+    c = synth.workload_case(w)
+    x, W, R, b = dev(c, "x"), dev(c, "W"), dev(c, "R"), dev(c, "b")
+    wd = w.dims
+    d = g.Dims(wd.T, wd.B, wd.Din, wd.NH, wd.Dh)
+    assert "input_proj=pipelined" in g.plan_describe(g.OP_FWD_LSTM, d, g.RNN_BF16)
+    ws = torch.empty(g.workspace_size(g.OP_FWD_LSTM, d, g.RNN_BF16), dtype=torch.uint8,
+                     device="cuda")
+    outs = []
+    for _ in range(3):
+        h_seq, _, hT, cT = g.lstm_fwd(x, W, R, b, ws=ws)
+        outs.append((h_seq.clone(), hT.clone(), cT.clone()))
+    assert g.workspace_status(ws) == g.RNN_OK
+    serial = _with_env("RNN355_PIPELINE", "0", lambda: g.lstm_fwd(x, W, R, b, ws=ws))
+    torch.cuda.synchronize()
+    for o in outs[1:] + [(serial[0], serial[2], serial[3])]:
+        for a, e in zip(outs[0], o):
+            assert torch.equal(a, e)
+
+
+def test_pipelined_forward_reads_fresh_projection_after_reuse():
+    """Two pipelined calls on one workspace with different inputs: the second
+    call's projection overwrites gx (2 MiB, small enough to stay cached) while
+    its recurrence reads it; the result must be the serial one for the second
+    inputs, never the first call's cached values."""
+    d = synth.Dims(T=256, B=4, Din=64, NH=2, Dh=64)
+    gd = g.Dims(d.T, d.B, d.Din, d.NH, d.Dh)
+    os.environ["RNN355_PIPELINE"] = "1"   # removed by the fixture
+    assert "input_proj=pipelined" in g.plan_describe(g.OP_FWD_LSTM, gd, g.RNN_BF16)
+    ws = torch.empty(g.workspace_size(g.OP_FWD_LSTM, gd, g.RNN_BF16), dtype=torch.uint8,
+                     device="cuda")
+    c1 = synth.make_case("lstm", d, "bf16", 7600, bias="forget+1")
+    c2 = synth.make_case("lstm", d, "bf16", 7700, bias="forget+1")
+    ins = [tuple(dev(c, k) for k in ("x", "W", "R", "b")) for c in (c1, c2)]
+    for _ in range(3):
+        g.lstm_fwd(*ins[0], ws=ws)
+        h2, _, _, cT2 = g.lstm_fwd(*ins[1], ws=ws)
+        h2, cT2 = h2.clone(), cT2.clone()
+    serial = _with_env("RNN355_PIPELINE", "0", lambda: g.lstm_fwd(*ins[1]))
+    torch.cuda.synchronize()
+    assert torch.equal(h2, serial[0]) and torch.equal(cT2, serial[3])
