@@ -32,58 +32,69 @@ __device__ __forceinline__ float unit_update(const float *a, float gxn, float &s
     }
 }
 
+// R4 == 1 (only batch row 0 is live, in lanes 0..15): three cross-row swaps
+// lay the G gate sums of a unit out as the rows of one register: gate g of
+// unit l%16 in lane l = 16g + l%16 (LSTM rows i, f, z, o; GRU rows r, z,
+// S_n and an unused row 3).
+template <int CELL>
+__device__ __forceinline__ float gate_rows_of(const f32x4 (&acc)[CellTraits<CELL>::G]) {
+    if constexpr (CELL == kLSTM) {
+        const RowPair p = swap16(acc[0][0], acc[1][0]);
+        const RowPair q = swap16(acc[2][0], acc[3][0]);
+        return swap32(p.a, q.a).a;
+    } else {
+        const RowPair p = swap16(acc[0][0], acc[1][0]);
+        return swap32(p.a, acc[2][0]).a;
+    }
+}
+
+// Cell update from the gate-row layout above, v = this lane's recurrent
+// sum and gx = the Gx of the lane's gate row.  One exp + rcp pass activates
+// every gate at once (tanh(x) = 2*sigmoid(2x) - 1 on the LSTM's z row), and
+// swaps hand every lane all the gates back.  The LSTM result is then valid
+// in every row (row 0 writes it), the GRU result in row 3 (row 3 writes it).
+template <int CELL>
+__device__ __forceinline__ void gate_rows_update(float v, float gx, float &st, float &hl,
+                                                 float &h, float &c) {
+    const int row = (threadIdx.x & 63) >> 4;
+    const bool tanh_row = CELL == kLSTM && row == 2;
+    const float act_k = tanh_row ? -2.0f * kLog2e : -kLog2e;
+    const float x = v + gx;
+    const float sg = rcp_fast(1.0f + __builtin_amdgcn_exp2f(x * act_k));
+    if constexpr (CELL == kLSTM) {
+        const float act = tanh_row ? fmaf(sg, 2.0f, -1.0f) : sg;
+        const RowPair A = swap16(act, act);  // [i,i,z,z] [f,f,o,o]
+        const RowPair I = swap32(A.a, A.a);  // [i..] [z..]
+        const RowPair F = swap32(A.b, A.b);  // [f..] [o..]
+        const float cn = fmaf(F.a, st, I.a * I.b);
+        st = cn;
+        c = cn;
+        h = F.b * tanh_f(cn);
+        hl = h;
+    } else {
+        const RowPair W = swap32(sg, sg);                 // rows r, u, r, u
+        const float nn = tanh_f(fmaf(W.a, v, gx));        // row 2: tanh(Gx_n + r S_n)
+        const float nn3 = swap16(nn, nn).a;               // row 3 <- row 2
+        const float hn = fmaf(W.a, st - nn3, nn3);        // row 3: (1-u) nn + u h
+        st = hn;
+        h = hn;
+        c = 0.f;
+    }
+}
+
 // The cell update of all row slots of one lane.
 //   gx[r][.]: for R4 > 1 the G gate inputs Gx of row slot r; for R4 == 1 a
-//             single value, the Gx of gate l/16 (the lane's row, see below).
+//             single value, the Gx of gate l/16 (the lane's row, see above).
 //   st[r]:    cell state c (LSTM) or h (GRU), updated in place.
 //   hl[r]:    last h (LSTM only; GRU keeps h in st).
 //   h[r], c[r]: this step's outputs.
-// R4 == 1 (only batch row 0 is live, in lanes 0..15): three cross-row swaps
-// lay the G gate sums of a unit out as the rows of one register (gate g in
-// lanes 16g..16g+15), one exp + rcp pass activates all gates (tanh(x) =
-// 2*sigmoid(2x) - 1 on the LSTM's z row), and swaps hand every lane all the
-// gates back.  The LSTM result is then valid in every row (row 0 writes it),
-// the GRU result in row 3 (row 3 writes it).
 template <int CELL, int R4, int GL>
 __device__ __forceinline__ void gate_update(const f32x4 (&acc)[CellTraits<CELL>::G],
                                             const float (&gx)[R4][GL], float (&st)[R4],
                                             float (&hl)[R4], float (&h)[R4], float (&c)[R4]) {
     constexpr int G = CellTraits<CELL>::G;
     if constexpr (R4 == 1) {
-        const int row = (threadIdx.x & 63) >> 4;
-        const bool tanh_row = CELL == kLSTM && row == 2;
-        const float act_k = tanh_row ? -2.0f * kLog2e : -kLog2e;
-        float v;
-        if constexpr (CELL == kLSTM) {
-            const RowPair p = swap16(acc[0][0], acc[1][0]);
-            const RowPair q = swap16(acc[2][0], acc[3][0]);
-            v = swap32(p.a, q.a).a;              // rows: i, f, z, o
-        } else {
-            const RowPair p = swap16(acc[0][0], acc[1][0]);
-            v = swap32(p.a, acc[2][0]).a;        // rows: r, z, S_n, -
-        }
-        const float x = v + gx[0][0];
-        const float sg = rcp_fast(1.0f + __builtin_amdgcn_exp2f(x * act_k));
-        if constexpr (CELL == kLSTM) {
-            const float act = tanh_row ? fmaf(sg, 2.0f, -1.0f) : sg;
-            const RowPair A = swap16(act, act);  // [i,i,z,z] [f,f,o,o]
-            const RowPair I = swap32(A.a, A.a);  // [i..] [z..]
-            const RowPair F = swap32(A.b, A.b);  // [f..] [o..]
-            const float cn = fmaf(F.a, st[0], I.a * I.b);
-            st[0] = cn;
-            c[0] = cn;
-            h[0] = F.b * tanh_f(cn);
-            hl[0] = h[0];
-        } else {
-            const RowPair W = swap32(sg, sg);                    // rows r, u, r, u
-            const float nn = tanh_f(fmaf(W.a, v, gx[0][0]));     // row 2: tanh(Gx_n + r S_n)
-            const float nn3 = swap16(nn, nn).a;                  // row 3 <- row 2
-            const float hn = fmaf(W.a, st[0] - nn3, nn3);        // row 3: (1-u) nn + u h
-            st[0] = hn;
-            h[0] = hn;
-            c[0] = 0.f;
-        }
-        (void)G;
+        gate_rows_update<CELL>(gate_rows_of<CELL>(acc), gx[0][0], st[0], hl[0], h[0], c[0]);
     } else {
 #pragma unroll
         for (int r = 0; r < R4; ++r) {

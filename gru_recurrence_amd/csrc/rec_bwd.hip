@@ -108,6 +108,13 @@ __global__ __launch_bounds__(512) void rec_bwd_lstm_kernel(BwdArgs m) {
 
     const int wpr = GD / 2;  // exchange words per row
     unsigned long long *xs_group = m.xg + (long)group * 2 * m.BT * wpr;
+    // A operand: lanes of live batch rows load it every step.  With one row
+    // slot the other lanes keep the zeros they start with (rewriting them
+    // every step costs a dozen moves on the step's critical path); with more
+    // they are rewritten (keeping them would spill).
+    bf16x8 af[KCW];
+#pragma unroll
+    for (int c = 0; c < KCW; ++c) af[c] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
     int s = 0;  // steps done
     for (; s < T; ++s) {
         const int t = T - 1 - s;
@@ -188,12 +195,11 @@ __global__ __launch_bounds__(512) void rec_bwd_lstm_kernel(BwdArgs m) {
         // next step's streamed inputs, issued now so they land during the MFMAs
         if (gate_wave && t > 0) load_step(t - 1);
         // ---- dh_carry = dA_t R^T for this wave's gate-column range
-        bf16x8 af[KCW];
         if (lr < rows) {
 #pragma unroll
             for (int c = 0; c < KCW; ++c)
                 af[c] = *reinterpret_cast<const bf16x8 *>(dab_next + lr * ALD + 32 * (kc0 + c) + 8 * lg);
-        } else {
+        } else if (R4 > 1) {
 #pragma unroll
             for (int c = 0; c < KCW; ++c) af[c] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
         }

@@ -251,6 +251,12 @@ __global__ __launch_bounds__(DH / 16 * 64) void rec_fwd_mfma_kernel(RecArgs a) {
             cs += o_step;
         }
     };
+    // A operand: lanes of live batch rows load it from LDS every step; the
+    // other lanes keep the zeros they start with (rewriting them every step
+    // would cost a dozen moves on the step's critical path).
+    bf16x8 af[KC];
+#pragma unroll
+    for (int c = 0; c < KC; ++c) af[c] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
     // PD steps starting at tg, reading Gx from `use`; at the first step the
     // previous group's outputs are stored and the next group's Gx requested.
     // FULL: every step of the group is < T (no per-step bound checks).
@@ -265,16 +271,10 @@ __global__ __launch_bounds__(DH / 16 * 64) void rec_fwd_mfma_kernel(RecArgs a) {
             if (s == 0) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
             const uint16_t *hc = hbuf[s & 1];
             uint16_t *hn = hbuf[(s + 1) & 1];
-            // A operand: only lanes of live batch rows read LDS
-            bf16x8 af[KC];
             if (lr < rows) {
 #pragma unroll
                 for (int c = 0; c < KC; ++c)
                     af[c] = *reinterpret_cast<const bf16x8 *>(hc + lr * HLD + 32 * c + 8 * lg);
-            } else {
-#pragma unroll
-                for (int c = 0; c < KC; ++c)
-                    af[c] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
             }
             f32x4 acc[G];
 #pragma unroll

@@ -139,15 +139,21 @@ __global__ __launch_bounds__(512) void rec_fwd_mc_kernel(McArgs m) {
     // exchange slots of the group: [2 parities][BT rows][Dh/2] words
     unsigned long long *xs_group = m.xg + (long)group * 2 * a.BT * (Dh / 2);
     const int wpr = Dh / 2;  // words per row
+    // A operand: lanes of live batch rows load it every step.  With one row
+    // slot the other lanes keep the zeros they start with (rewriting them
+    // every step costs a dozen moves on the step's critical path); with more
+    // they are rewritten (keeping them would spill).
+    bf16x8 af[KCW];
+#pragma unroll
+    for (int c = 0; c < KCW; ++c) af[c] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
     int t = 0;
     for (; t < T; ++t) {
         const uint16_t *hbuf = hbuf2 + (t & 1) * 16 * HLD;
-        bf16x8 af[KCW];
         if (lr < rows) {
 #pragma unroll
             for (int c = 0; c < KCW; ++c)
                 af[c] = *reinterpret_cast<const bf16x8 *>(hbuf + lr * HLD + 32 * (kc0 + c) + 8 * lg);
-        } else {
+        } else if (R4 > 1) {
 #pragma unroll
             for (int c = 0; c < KCW; ++c) af[c] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
         }
