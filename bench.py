@@ -239,9 +239,16 @@ def main():
             print("bench.py: kernel reported %s" % g.status_str(st), file=sys.stderr)
             sys.exit(1)
 
-    # the two kernels of the forward, each on its own
-    def proj():
-        g.input_proj(x, W, b, out=gx, stream=stream)
+    # the two kernels of the forward, each on its own (the forward stages W
+    # transposed and runs the k-major contraction; here W^T is made once)
+    if dtc == g.RNN_BF16 and d.Din % 32 == 0:
+        Wt = W.t().contiguous()
+
+        def proj():
+            g.input_proj_t(x, Wt, b, out=gx, stream=stream)
+    else:
+        def proj():
+            g.input_proj(x, W, b, out=gx, stream=stream)
 
     def rec():
         if lstm:

@@ -25,6 +25,7 @@ RNN_F32, RNN_BF16 = 0, 1
 OP_FWD_LSTM, OP_FWD_GRU, OP_BWD_LSTM, OP_BWD_GRU, OP_REC_LSTM, OP_REC_GRU = range(6)
 
 EXPORTS = ("rnn_status_str", "rnn_workspace_size", "rnn_plan_describe", "rnn_input_proj",
+           "rnn_input_proj_t",
            "rnn_rec_lstm", "rnn_rec_gru", "rnn_fwd_lstm", "rnn_fwd_gru", "rnn_bwd_lstm",
            "rnn_workspace_status")
 
@@ -61,13 +62,14 @@ def load(path: Optional[str] = None):
     lib.rnn_workspace_size.argtypes = [I, D, I]
     lib.rnn_plan_describe.argtypes = [I, D, I, ctypes.c_char_p, S]
     lib.rnn_input_proj.argtypes = [I, I, I, I, P, P, P, P, P]
+    lib.rnn_input_proj_t.argtypes = [I, I, I, I, P, P, P, P, P]
     lib.rnn_rec_lstm.argtypes = [D, I, P, P, P, P, P, P, P, P, P, S, P]
     lib.rnn_rec_gru.argtypes = [D, I, P, P, P, P, P, P, S, P]
     lib.rnn_fwd_lstm.argtypes = [D, I, P, P, P, P, P, P, P, P, P, P, P, S, P]
     lib.rnn_fwd_gru.argtypes = [D, I, P, P, P, P, P, P, P, P, S, P]
     lib.rnn_bwd_lstm.argtypes = [D, I] + [P] * 17 + [P, S, P]
     lib.rnn_workspace_status.argtypes = [P, S, P]
-    for f in ("rnn_plan_describe", "rnn_input_proj", "rnn_rec_lstm", "rnn_rec_gru",
+    for f in ("rnn_plan_describe", "rnn_input_proj", "rnn_input_proj_t", "rnn_rec_lstm", "rnn_rec_gru",
               "rnn_fwd_lstm", "rnn_fwd_gru", "rnn_bwd_lstm", "rnn_workspace_status"):
         getattr(lib, f).restype = I
     _lib = lib
@@ -174,6 +176,23 @@ def input_proj(x, W, b=None, out=None, stream=None):
                               _ptr(b, "b", torch.float32, (N,), optional=True),
                               _ptr(out, "gx", torch.float32, (T, B, N)), _stream(stream))
     _check(s, "rnn_input_proj")
+    return out
+
+
+def input_proj_t(x, Wt, b=None, out=None, stream=None):
+    """gx = x Wt^T + b with the weights given transposed, Wt [N, Din] (bf16,
+    Din % 32 == 0): the fused forward's contraction (float32 [T,B,N])."""
+    torch = _torch()
+    T, B, Din = x.shape
+    N = Wt.shape[0]
+    dt = _dtype_code(x)
+    if out is None:
+        out = torch.empty((T, B, N), dtype=torch.float32, device=x.device)
+    s = load().rnn_input_proj_t(T * B, Din, N, dt, _ptr(x, "x", x.dtype),
+                                _ptr(Wt, "Wt", x.dtype, (N, Din)),
+                                _ptr(b, "b", torch.float32, (N,), optional=True),
+                                _ptr(out, "gx", torch.float32, (T, B, N)), _stream(stream))
+    _check(s, "rnn_input_proj_t")
     return out
 
 

@@ -58,11 +58,16 @@ long gx_panels(const rnn_dims *d) {
 }
 size_t ready_bytes(const rnn_dims *d) { return align_up(sizeof(unsigned) * (size_t)gx_panels(d)); }
 
+// W staged transposed ([N][Din] bf16) for the k-major contraction.
+size_t wt_bytes(const rnn_dims *d, int G) {
+    return align_up(sizeof(uint16_t) * (size_t)d->Din * d->NH * G * d->Dh);
+}
+
 // Backward workspace after the header: dA exchange slots, recomputed
 // pre-activations A (f32), gate gradients dA (bf16), h_{t-1} (bf16) and the
 // per-batch-tile bias-gradient partials.
 struct BwdLayout {
-    size_t xchg, A, dA, hprev, dbp, part, total;
+    size_t xchg, A, dA, hprev, dbp, part, wt, rt, total;
 };
 BwdLayout bwd_layout(const rnn_dims *d) {
     BwdLayout L{};
@@ -78,6 +83,8 @@ BwdLayout bwd_layout(const rnn_dims *d) {
     const size_t pw = gemm_partial_bytes(d->Din, (int)N, 1, kMaxSplitK);
     const size_t pr = gemm_partial_bytes(d->Dh, 4 * d->Dh, d->NH, kMaxSplitK);
     L.part = off; off += align_up(pw > pr ? pw : pr);
+    L.wt = off;   off += wt_bytes(d, 4);                                     // W^T [N][Din]
+    L.rt = off;   off += align_up(sizeof(uint16_t) * (size_t)d->NH * 4 * d->Dh * d->Dh);  // R^T per head
     L.total = off;
     return L;
 }
@@ -156,11 +163,25 @@ bool gemm_shape_ok(int K, int N, rnn_dtype dt) {
     return true;
 }
 
+// gx = x W + b.  With `wt` (bf16, K % 32 == 0) W is first transposed into
+// wt and both operands stream k-major through the direct-to-LDS kernel;
+// otherwise the register-staged kernel reads W as it is.
 rnn_status input_proj(int M, int K, int N, rnn_dtype dt, const void *x, const void *W,
                       const float *b, float *gx, uint32_t *clear, hipStream_t s,
-                      unsigned *ready = nullptr) {
+                      unsigned *ready = nullptr, uint16_t *wt = nullptr) {
     hipError_t e;
-    if (dt == RNN_BF16) {
+    if (dt == RNN_BF16 && wt && gemm_dma_ok(K)) {
+        e = launch_transpose_bf16((const uint16_t *)W, wt, K, N, 1, s);
+        if (e != hipSuccess) return RNN_ERR_HIP;
+        GemmArgs g{};
+        g.M = M; g.N = N; g.K = K;
+        g.A = (const uint16_t *)x; g.lda = K;
+        g.B = wt; g.ldb = K;
+        g.bias = b; g.C = gx; g.ldc = N;
+        g.clear_words = clear;
+        g.ready = ready;
+        e = launch_gemm_dma(g, 1, s);
+    } else if (dt == RNN_BF16) {
         GemmArgs g{};
         g.M = M; g.N = N; g.K = K;
         g.A = (const uint16_t *)x; g.lda = K; g.strideA = 0;
@@ -262,6 +283,7 @@ rnn_status forward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, con
     const int N = d->NH * G * d->Dh, M = d->T * d->B;
     float *gx = (float *)((char *)ws + kHeader + xchg_bytes(d));
     unsigned *ready = (unsigned *)((char *)gx + gx_bytes(d, G));
+    uint16_t *wt = (uint16_t *)((char *)ready + ready_bytes(d));
     const int cus = device_cus();
     const Choice ch = choose(cell, d, dt, cus);
     if (!ch.ok) return RNN_ERR_UNSUPPORTED;
@@ -282,7 +304,7 @@ rnn_status forward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, con
                 !ok(hipEventRecord(pp->fork, s)) ||
                 !ok(hipStreamWaitEvent(pp->side, pp->fork, 0)))
                 return RNN_ERR_HIP;
-            if (input_proj(M, d->Din, N, dt, x, W, b, gx, nullptr, pp->side, ready) != RNN_OK)
+            if (input_proj(M, d->Din, N, dt, x, W, b, gx, nullptr, pp->side, ready, wt) != RNN_OK)
                 return RNN_ERR_HIP;
             if (!ok(hipEventRecord(pp->join, pp->side))) return RNN_ERR_HIP;
             RecArgs a{};
@@ -301,7 +323,7 @@ rnn_status forward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, con
             return (e == hipSuccess && ej == hipSuccess) ? RNN_OK : RNN_ERR_HIP;
         }
     }
-    rnn_status st = input_proj(M, d->Din, N, dt, x, W, b, gx, (uint32_t *)ws, s);
+    rnn_status st = input_proj(M, d->Din, N, dt, x, W, b, gx, (uint32_t *)ws, s, nullptr, wt);
     if (st != RNN_OK) return st;
     return rec_fwd(cell, d, dt, gx, R, h0, c0, h_seq, c_seq, hT, cT, ws, s);
 }
@@ -328,7 +350,7 @@ size_t rnn_workspace_size(rnn_op op, const rnn_dims *d, rnn_dtype dt) {
     switch (op) {
         case RNN_OP_FWD_LSTM:
         case RNN_OP_FWD_GRU:
-            return kHeader + xchg_bytes(d) + gx_bytes(d, G) + ready_bytes(d);
+            return kHeader + xchg_bytes(d) + gx_bytes(d, G) + ready_bytes(d) + wt_bytes(d, G);
         case RNN_OP_REC_LSTM:
         case RNN_OP_REC_GRU:
             return kHeader + xchg_bytes(d);
@@ -377,6 +399,21 @@ rnn_status rnn_input_proj(int M, int K, int N, rnn_dtype dt, const void *x, cons
         return RNN_ERR_INVALID_ARG;
     if (!gemm_shape_ok(K, N, dt)) return RNN_ERR_UNSUPPORTED;
     return input_proj(M, K, N, dt, x, W, b, gx, nullptr, stream);
+}
+
+rnn_status rnn_input_proj_t(int M, int K, int N, rnn_dtype dt, const void *x, const void *Wt,
+                            const float *b, float *gx, hipStream_t stream) {
+    if (M <= 0 || K <= 0 || N <= 0 || !dtype_ok(dt)) return RNN_ERR_INVALID_ARG;
+    if (!x || !Wt || !gx) return RNN_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(Wt) || !aligned16(b) || !aligned16(gx))
+        return RNN_ERR_INVALID_ARG;
+    if (dt != RNN_BF16 || !gemm_dma_ok(K)) return RNN_ERR_UNSUPPORTED;
+    GemmArgs g{};
+    g.M = M; g.N = N; g.K = K;
+    g.A = (const uint16_t *)x; g.lda = K;
+    g.B = (const uint16_t *)Wt; g.ldb = K;
+    g.bias = b; g.C = gx; g.ldc = N;
+    return launch_gemm_dma(g, 1, stream) == hipSuccess ? RNN_OK : RNN_ERR_HIP;
 }
 
 rnn_status rnn_rec_lstm(const rnn_dims *d, rnn_dtype dt, const float *gx, const void *R,
@@ -457,20 +494,30 @@ rnn_status rnn_bwd_lstm(const rnn_dims *d, rnn_dtype dt, const void *x, const vo
     uint16_t *dA = (uint16_t *)(base + L.dA);
     uint16_t *hprev = (uint16_t *)(base + L.hprev);
     float *dbp = (float *)(base + L.dbp);
+    uint16_t *wt = (uint16_t *)(base + L.wt);
+    uint16_t *rt = (uint16_t *)(base + L.rt);
     const uint16_t *xb = (const uint16_t *)x, *Wb = (const uint16_t *)W, *Rb = (const uint16_t *)R;
     auto ok = [](hipError_t e) { return e == hipSuccess; };
 
     // 1. h_{t-1} as bf16; A = x W + b + h_{t-1} R (block-diagonal), all t at once
     if (!ok(launch_hprev_bf16(h0, h_seq, hprev, (long)B * H, (long)M * H, stream))) return RNN_ERR_HIP;
-    if (input_proj(M, Din, N, dt, x, W, b, A, (uint32_t *)ws, stream) != RNN_OK) return RNN_ERR_HIP;
+    if (input_proj(M, Din, N, dt, x, W, b, A, (uint32_t *)ws, stream, nullptr, wt) != RNN_OK)
+        return RNN_ERR_HIP;
     {
         GemmArgs g{};
         g.M = M; g.N = GD; g.K = Dh;
         g.A = hprev; g.lda = H; g.strideA = Dh;       // row m, k = unit of head n
-        g.B = Rb; g.ldb = GD; g.strideB = (long)Dh * GD;  // R[n][k][c]: r-major
         g.C = A; g.ldc = N; g.strideC = GD;
         g.accumulate = 1;
-        if (!ok(launch_gemm_bf16(g, true, false, NH, stream))) return RNN_ERR_HIP;
+        if (gemm_dma_ok(Dh)) {
+            // R^T per head: B(c, k) = R[n][k][c] at rt[n][c][k]
+            if (!ok(launch_transpose_bf16(Rb, rt, Dh, GD, NH, stream))) return RNN_ERR_HIP;
+            g.B = rt; g.ldb = Dh; g.strideB = (long)GD * Dh;
+            if (!ok(launch_gemm_dma(g, NH, stream))) return RNN_ERR_HIP;
+        } else {
+            g.B = Rb; g.ldb = GD; g.strideB = (long)Dh * GD;  // R[n][k][c]: r-major
+            if (!ok(launch_gemm_bf16(g, true, false, NH, stream))) return RNN_ERR_HIP;
+        }
     }
     // 2. the reverse-time sweep
     {
@@ -500,7 +547,9 @@ rnn_status rnn_bwd_lstm(const rnn_dims *d, rnn_dtype dt, const void *x, const vo
         GemmArgs g{};  // dx[m][k] = sum_c dA[m][c] W[k][c]
         g.M = M; g.N = Din; g.K = N;
         g.A = dA; g.lda = N; g.B = Wb; g.ldb = N; g.C = dx; g.ldc = Din;
-        if (!ok(launch_gemm_bf16(g, true, true, 1, stream))) return RNN_ERR_HIP;
+        const hipError_t e = gemm_dma_ok(N) ? launch_gemm_dma(g, 1, stream)
+                                            : launch_gemm_bf16(g, true, true, 1, stream);
+        if (!ok(e)) return RNN_ERR_HIP;
     }
     {
         GemmArgs g{};  // dR[n][i][c] = sum_m h_{t-1}[m][n*Dh+i] dA[m][n*GD+c]

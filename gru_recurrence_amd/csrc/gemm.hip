@@ -356,6 +356,10 @@ hipError_t launch_gemm_bf16(const GemmArgs &g0, bool a_kmajor, bool b_kmajor, in
     else if (!a_kmajor && !b_kmajor) e = launch_t<false, false>(g, batch, s);
     else e = launch_t<false, true>(g, batch, s);
     if (e != hipSuccess || g.ksplit == 1) return e;
+    return launch_splitk_reduce(g, batch, s);
+}
+
+hipError_t launch_splitk_reduce(const GemmArgs &g, int batch, hipStream_t s) {
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3(1024, batch), dim3(256), 0, s, g);
     return hipGetLastError();
 }

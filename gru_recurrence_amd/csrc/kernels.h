@@ -53,6 +53,16 @@ struct GemmF32Args {
 
 hipError_t launch_gemm_bf16(const GemmArgs &g, bool a_kmajor, bool b_kmajor, int batch,
                             hipStream_t s);
+// Sums the split-K partials of g into g.C (after a launch with ksplit > 1).
+hipError_t launch_splitk_reduce(const GemmArgs &g, int batch, hipStream_t s);
+
+// Both operands k-major, K % 32 == 0: tiles streamed into LDS by direct
+// global-to-LDS loads (gemm_dma.hip).  B(n,k) = B[n*ldb + k].
+bool gemm_dma_ok(int K);
+hipError_t launch_gemm_dma(const GemmArgs &g, int batch, hipStream_t s);
+// dst[b][c][r] = src[b][r][c], bf16 [R][C] matrices, `batch` of them.
+hipError_t launch_transpose_bf16(const uint16_t *src, uint16_t *dst, int R, int C, int batch,
+                                 hipStream_t s);
 hipError_t launch_gemm_f32(const GemmF32Args &g, int batch, hipStream_t s);
 
 // Forward recurrence (rec_fwd.hip).

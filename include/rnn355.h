@@ -121,6 +121,18 @@ rnn_status rnn_input_proj(int M, int K, int N, rnn_dtype dt,
                           float *gx, hipStream_t stream);
 
 /*
+ * The same contraction with the weights given transposed, Wt [N][K] (k
+ * contiguous, as a layer would keep them): gx[m][c] = b[c] + sum_k x[m][k]
+ * Wt[c][k].  bf16 only, K % 32 == 0 (else RNN_ERR_UNSUPPORTED).  Both
+ * operands are then read k-major straight into LDS; this is the kernel the
+ * fused forward uses after staging W transposed in its workspace, and its
+ * sums are bitwise those of rnn_input_proj (same k order).
+ */
+rnn_status rnn_input_proj_t(int M, int K, int N, rnn_dtype dt,
+                            const void *x, const void *Wt, const float *b,
+                            float *gx, hipStream_t stream);
+
+/*
  * The sequential LSTM recurrence alone, given gx from rnn_input_proj
  * (blog.hotdry.top 2025-09-21: the per-step dependency is the bottleneck; R
  * stays resident on chip for all steps):

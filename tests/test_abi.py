@@ -87,6 +87,15 @@ def test_invalid_arguments_are_rejected_before_launch():
                               None) == g.RNN_ERR_INVALID_ARG
     assert lib.rnn_input_proj(4, 8, 8, g.RNN_BF16, ok[0], None, None, ok[2],
                               None) == g.RNN_ERR_INVALID_ARG
+    # transposed-weights projection: bf16 with K % 32 == 0 only
+    assert lib.rnn_input_proj_t(4, 32, 8, g.RNN_BF16, ok[0], None, None, ok[2],
+                                None) == g.RNN_ERR_INVALID_ARG
+    assert lib.rnn_input_proj_t(4, 48, 8, g.RNN_BF16, ok[0], ok[1], None, ok[2],
+                                None) == g.RNN_ERR_UNSUPPORTED
+    assert lib.rnn_input_proj_t(4, 32, 8, g.RNN_F32, ok[0], ok[1], None, ok[2],
+                                None) == g.RNN_ERR_UNSUPPORTED
+    assert lib.rnn_input_proj_t(4, 32, 8, g.RNN_BF16, _p(FAKE + 8), ok[1], None, ok[2],
+                                None) == g.RNN_ERR_INVALID_ARG
     # recurrence alone
     assert lib.rnn_rec_gru(ctypes.byref(d), g.RNN_BF16, None, ok[1], None, None, ok[2],
                            _p(FAKE), 1 << 20, None) == g.RNN_ERR_INVALID_ARG

@@ -80,6 +80,31 @@ def test_input_projection(M, K, N, dtype):
     assert e <= (1e-4 if dtype == "bf16" else 1e-5)
 
 
+@pytest.mark.parametrize("M,K,N", [(185, 96, 384), (300, 768, 288), (2048, 64, 1000),
+                                   (1, 32, 8), (4096, 1024, 4096)])
+def test_input_projection_transposed_weights(M, K, N):
+    """k-major contraction (weights given transposed, tiles loaded straight
+    into LDS): matches the oracle, and bitwise the contraction on W as it is
+    (same k order).  Covers ragged row and column tiles, a single row, and a
+    K of 32 k-tiles in flight through the four-stage ring."""
+    d = synth.Dims(T=M, B=1, Din=K, NH=1, Dh=max(N // 4, 1))
+    c = synth.make_case("lstm", d, "bf16", 4300 + M, w_var=1.0 / K)
+    x = dev(c, "x")
+    Wf = torch.from_numpy(synth.normal(4400 + N, K * N, 1.0 / K).reshape(K, N))
+    W = Wf.to(torch.bfloat16).to("cuda")
+    b = torch.from_numpy(synth.normal(4500 + N, N, 1.0)).float().to("cuda")
+    gt = g.input_proj_t(x, W.t().contiguous(), b)
+    gr = g.input_proj(x, W, b)
+    torch.cuda.synchronize()
+    assert torch.equal(gt, gr)
+    rows = np.unique(np.r_[0, M - 1, np.arange(0, M, max(1, M // 37))])
+    want = oracle.input_proj(c.f64("x"), W.float().cpu().numpy().astype(np.float64),
+                             b.cpu().numpy().astype(np.float64), rows=rows)
+    e = nerr(host(gt).reshape(M, N)[rows], want)
+    print("  gx nerr=%.3e (%d rows)" % (e, len(rows)), flush=True)
+    assert e <= 1e-4
+
+
 @pytest.mark.parametrize("Dh", [32, 64, 128])
 @pytest.mark.parametrize("bt", [None, 1, 3, 16])
 def test_lstm_bf16_tiles_and_ragged(Dh, bt):
