@@ -234,15 +234,16 @@ bool rec_supported(int cell, const rnn_dims *d, rnn_dtype dt) {
     return choose(cell, d, dt, device_cus()).ok;
 }
 
-// Whether the forward overlaps its two phases (see forward()): the
-// recurrence must leave at least half the CUs free, and the projection must
-// take more than two waves of output tiles on those CUs -- otherwise the
-// first row panel is ready about when the whole projection would be, and
-// the overlap only adds the cost of running the two side by side.
+// Whether the forward overlaps its two phases (see forward()): the one-CU
+// recurrence at Dh = 128 must leave at least half the CUs free, and the
+// projection (bf16, Din % 32 == 0) must take more than two waves of output
+// tiles on those CUs -- otherwise the first row panel is ready about when
+// the whole projection would be, and the overlap only adds the cost of
+// running the two side by side.
 bool pipelined(const Choice &ch, const rnn_dims *d, rnn_dtype dt, int cus) {
     const int force = pipeline_override();
-    if (dt != RNN_BF16 || ch.use_mc || ch.rec.kind != kRecMfma || 2 * ch.rec.grid > cus ||
-        force == 0 || gx_panels(d) < 2)
+    if (dt != RNN_BF16 || ch.use_mc || ch.rec.kind != kRecMfma || d->Dh != 128 ||
+        !gemm_dma_ok(d->Din) || 2 * ch.rec.grid > cus || force == 0 || gx_panels(d) < 2)
         return false;
     if (force == 1) return true;
     const int G = gates_of_cell(ch.cell);
@@ -250,32 +251,11 @@ bool pipelined(const Choice &ch, const rnn_dims *d, rnn_dtype dt, int cus) {
     return tiles > 2L * (cus - ch.rec.grid);
 }
 
-// Side stream and fork/join events of the pipelined forward, one set per
-// device, created on first use and kept for the life of the process.  The
-// side stream is non-blocking (no implicit order with the legacy default
-// stream) and has the default priority.
-struct Pipe {
-    std::mutex mu;
-    bool tried = false;
-    hipStream_t side = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
-};
-
-Pipe *pipe_of_current_device() {
-    static Pipe pipes[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-    return &pipes[dev];
-}
-
-// Forward = input projection + recurrence.  Pipelined when the recurrence is
-// the one-CU MFMA kernel and leaves at least half the CUs free: the
-// projection runs on the side stream in time order and publishes finished
-// row panels; the recurrence, on the caller's stream, waits for the panels
-// of each group of steps before loading them.  The projection never waits,
-// and the recurrence's workgroups leave CUs free for it, so both finish
-// however the two grids are placed.  The caller's stream joins the side
-// stream before returning, so stream order is as for one kernel.
+// Forward = input projection + recurrence.  Pipelined (see pipelined()): one
+// launch whose first workgroups compute the projection in time order and
+// count finished 256-row panels of gx, while the recurrence's workgroups
+// wait for the panels of their next steps (launch_fwd_fused).  Otherwise the
+// projection, then the recurrence.  Results are bitwise the same.
 rnn_status forward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, const void *W,
                    const void *R, const float *b, const float *h0, const float *c0,
                    float *h_seq, float *c_seq, float *hT, float *cT, void *ws, hipStream_t s) {
@@ -288,40 +268,36 @@ rnn_status forward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, con
     const Choice ch = choose(cell, d, dt, cus);
     if (!ch.ok) return RNN_ERR_UNSUPPORTED;
     const long panels = gx_panels(d);
-    Pipe *pp = pipelined(ch, d, dt, cus) ? pipe_of_current_device() : nullptr;
-    if (pp) {
-        std::lock_guard<std::mutex> lk(pp->mu);
-        if (!pp->tried) {
-            pp->tried = true;
-            if (hipStreamCreateWithFlags(&pp->side, hipStreamNonBlocking) != hipSuccess ||
-                hipEventCreateWithFlags(&pp->fork, hipEventDisableTiming) != hipSuccess ||
-                hipEventCreateWithFlags(&pp->join, hipEventDisableTiming) != hipSuccess)
-                pp->side = nullptr;
-        }
-        if (pp->side) {
-            auto ok = [](hipError_t e) { return e == hipSuccess; };
-            if (!ok(launch_clear_u32((unsigned *)ws, 64, ready, panels, s)) ||
-                !ok(hipEventRecord(pp->fork, s)) ||
-                !ok(hipStreamWaitEvent(pp->side, pp->fork, 0)))
-                return RNN_ERR_HIP;
-            if (input_proj(M, d->Din, N, dt, x, W, b, gx, nullptr, pp->side, ready, wt) != RNN_OK)
-                return RNN_ERR_HIP;
-            if (!ok(hipEventRecord(pp->join, pp->side))) return RNN_ERR_HIP;
-            RecArgs a{};
-            a.T = d->T; a.B = d->B; a.NH = d->NH; a.Dh = d->Dh; a.BT = ch.rec.BT;
-            a.gx = gx;
-            a.Rb = (const uint16_t *)R;
-            a.h0 = h0; a.c0 = c0; a.h_seq = h_seq; a.c_seq = c_seq; a.hT = hT; a.cT = cT;
-            a.ready = ready;
-            a.ready_target = (unsigned)((N + kGemmColTile - 1) / kGemmColTile);  // tiles per panel
-            a.panels = (int)panels;
-            a.flag = (unsigned *)ws;
-            a.spin_limit = spin_limit();
-            const hipError_t e = launch_rec_fwd(cell, ch.rec, a, true, s);
-            // join even after a failed launch: the side stream's work is queued
-            const hipError_t ej = hipStreamWaitEvent(s, pp->join, 0);
-            return (e == hipSuccess && ej == hipSuccess) ? RNN_OK : RNN_ERR_HIP;
-        }
+    if (pipelined(ch, d, dt, cus)) {
+        auto ok = [](hipError_t e) { return e == hipSuccess; };
+        // W^T for the k-major contraction; status word and panel counters zeroed
+        if (!ok(launch_transpose_bf16((const uint16_t *)W, wt, d->Din, N, 1, s)) ||
+            !ok(launch_clear_u32((unsigned *)ws, 64, ready, panels, s)))
+            return RNN_ERR_HIP;
+        GemmArgs g{};
+        g.M = M; g.N = N; g.K = d->Din;
+        g.A = (const uint16_t *)x; g.lda = d->Din;
+        g.B = wt; g.ldb = d->Din;
+        g.bias = b; g.C = gx; g.ldc = N;
+        g.ksplit = 1;
+        g.ready = ready;
+        RecArgs a{};
+        a.T = d->T; a.B = d->B; a.NH = d->NH; a.Dh = d->Dh; a.BT = ch.rec.BT;
+        a.gx = gx;
+        a.Rb = (const uint16_t *)R;
+        a.h0 = h0; a.c0 = c0; a.h_seq = h_seq; a.c_seq = c_seq; a.hT = hT; a.cT = cT;
+        a.ready = ready;
+        a.ready_target = (unsigned)((N + kGemmColTile - 1) / kGemmColTile);  // tiles per panel
+        a.panels = (int)panels;
+        a.flag = (unsigned *)ws;
+        a.spin_limit = spin_limit();
+        // projection workgroups: the CUs the recurrence leaves, a multiple of
+        // 8 (whole XCD rounds), at most one per tile
+        const long tiles = panels * a.ready_target;
+        int n_gemm = ((cus - ch.rec.grid) / 8) * 8;
+        if (n_gemm > tiles) n_gemm = (int)tiles;
+        if (n_gemm < 8) n_gemm = (int)std::min<long>(8, tiles);
+        return ok(launch_fwd_fused(cell, ch.rec, a, g, n_gemm, s)) ? RNN_OK : RNN_ERR_HIP;
     }
     rnn_status st = input_proj(M, d->Din, N, dt, x, W, b, gx, (uint32_t *)ws, s, nullptr, wt);
     if (st != RNN_OK) return st;

@@ -1,0 +1,202 @@
+// gemm_dma.h -- device body of the bf16 MFMA contraction with both operands
+// k-major and tiles streamed into LDS by the direct global-to-LDS loads of
+// gfx950 (see gemm_dma.hip for the kernel and the design notes).  A header
+// so that the fused forward kernel can run the same body in some of its
+// workgroups.
+#pragma once
+
+#include "common.h"
+#include "kernels.h"
+
+namespace rnn355 {
+namespace dma {
+
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((address_space(3))) char lds_char;
+
+constexpr int BM = 256, BN = 256, BK = 32, NST = 4, NTHR = 512;
+constexpr int ROWB = BK * 2;                 // bytes per LDS row
+constexpr int OPB = BM * ROWB;               // bytes per operand per stage (16 KiB)
+constexpr int STB = 2 * OPB;                 // bytes per stage (32 KiB)
+constexpr size_t LDS_BYTES = (size_t)NST * STB;
+static_assert(BM == kGemmRowTile && BN == kGemmColTile, "row-panel counters assume the output tile");
+
+// Issue the loads of one operand tile (256 rows x 32 k) into `dst`: 1024
+// chunks of 16 bytes, two per thread; chunk q goes to LDS byte 16q, i.e.
+// row q/4, slot q%4, holding k chunk (q%4) ^ ((row >> 1) & 3).  Rows past R
+// read row R-1 (their products only reach outputs that are not stored).
+__device__ __forceinline__ void dma_tile(const uint16_t *__restrict__ P, long ld, int r0, int k0,
+                                         int R, lds_char *dst, int tid, int wave) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int q = tid + NTHR * i;
+        const int r = q >> 2, slot = q & 3;
+        const int chunk = slot ^ ((r >> 1) & 3);
+        const int gr = min(r0 + r, R - 1);
+        const uint16_t *src = P + (long)gr * ld + k0 + chunk * 8;
+        __builtin_amdgcn_global_load_lds(src, dst + (64 * wave + NTHR * i) * 16, 16, 0, 0);
+    }
+}
+
+// vmcnt(n) for n in {0, 4, 8}: loads of later tiles may stay in flight.
+__device__ __forceinline__ void wait_tiles_after(int later) {
+    if (later >= 2) __builtin_amdgcn_s_waitcnt(0x0F78);       // vmcnt(8)
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+    else __builtin_amdgcn_s_waitcnt(0x0F70);                  // vmcnt(0)
+}
+
+// The contraction's work for workgroup `wg` of `nwg`: output tiles wg,
+// wg + nwg, ... of batch / split slice blockIdx.z (a persistent loop when
+// nwg is smaller than the tile count).  `lds` is LDS_BYTES of dynamic LDS.
+__device__ __forceinline__ void gemm_dma_tiles(const GemmArgs &g, int wg, int nwg, lds_char *lds) {
+    const uint32_t lbase = (uint32_t)(uintptr_t)lds;
+
+    const int slice = blockIdx.z % g.ksplit, bz = blockIdx.z / g.ksplit;
+    const uint16_t *A = g.A + (long)bz * g.strideA;
+    const uint16_t *B = g.B + (long)bz * g.strideB;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 2, wn = wave & 3;
+    const int l32 = lane & 31, lh = lane >> 5;
+
+    if (g.clear_words && wg == 0 && blockIdx.z == 0 && tid < 64) g.clear_words[tid] = 0u;
+
+    const int ktiles = g.K / BK;
+    const int per = (ktiles + g.ksplit - 1) / g.ksplit;
+    const int kt0 = slice * per, kt1 = min(ktiles, kt0 + per);
+
+    // this lane's fragment byte offsets inside a stage, for the two 16-deep
+    // k steps of a tile: row l32 of the wave's first A / B tile, chunk
+    // 2*kc + lh in its swizzled slot (rows of the other tiles: +32 rows)
+    const int sw = (l32 >> 1) & 3;
+    uint32_t offA[2], offB[2];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+        const int slot = (2 * kc + lh) ^ sw;
+        offA[kc] = (uint32_t)((wm * 128 + l32) * ROWB + slot * 16);
+        offB[kc] = (uint32_t)(OPB + (wn * 64 + l32) * ROWB + slot * 16);
+    }
+
+    // runs of 8 row tiles, row tile 8q + x of a run on XCD x (workgroup i
+    // runs on XCD i % 8; nwg is a multiple of 8 or the tile count), all its
+    // column tiles there; rows past the last whole run in order
+    const int tiles_n = (g.N + BN - 1) / BN;
+    const int tiles_m = (g.M + BM - 1) / BM;
+    const int tiles = tiles_m * tiles_n;
+    const int run = 8 * tiles_n, full = (tiles_m >> 3) * run;
+    for (int t = wg; t < tiles; t += nwg) {
+    int mt, nt;
+    if (t < full) {
+        const int q = t / run, i = t - q * run;
+        mt = 8 * q + (i & 7);
+        nt = i >> 3;
+    } else {
+        const int i = t - full;
+        mt = (tiles_m & ~7) + i / tiles_n;
+        nt = i % tiles_n;
+    }
+    const int m0 = mt * BM, n0 = nt * BN;
+    // a new tile refills the ring: every wave is past the last tile's reads
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    auto issue = [&](int kt) {
+        lds_char *st = lds + ((kt - kt0) & (NST - 1)) * STB;
+        dma_tile(A, g.lda, m0, kt * BK, g.M, st, tid, wave);
+        dma_tile(B, g.ldb, n0, kt * BK, g.N, st + OPB, tid, wave);
+    };
+#pragma unroll
+    for (int p = 0; p < NST - 1; ++p)
+        if (kt0 + p < kt1) issue(kt0 + p);
+
+    for (int kt = kt0; kt < kt1; ++kt) {
+        // this thread's loads of tile kt have landed; after the barrier,
+        // everyone's have, and every wave is done with tile kt-1's stage
+        wait_tiles_after(min(2, kt1 - 1 - kt));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        const uint32_t sb = lbase + (uint32_t)(((kt - kt0) & (NST - 1)) * STB);
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+            bf16x8 a0, a1, a2, a3, b0, b1;
+            asm volatile(
+                "ds_read_b128 %0, %6\n\t"
+                "ds_read_b128 %1, %6 offset:2048\n\t"
+                "ds_read_b128 %2, %6 offset:4096\n\t"
+                "ds_read_b128 %3, %6 offset:6144\n\t"
+                "ds_read_b128 %4, %7\n\t"
+                "ds_read_b128 %5, %7 offset:2048\n\t"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(b0), "=&v"(b1)
+                : "v"(sb + offA[kc]), "v"(sb + offB[kc])
+                : "memory");
+            const bf16x8 af[4] = {a0, a1, a2, a3}, bfr[2] = {b0, b1};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+        asm volatile("" ::: "memory");
+        // refill the stage that tile kt-1 used (every wave has passed this
+        // iteration's barrier, so none still reads it)
+        if (kt + NST - 1 < kt1) issue(kt + NST - 1);
+    }
+
+    // epilogue: register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4, column l%32
+    float *C;
+    long ldc;
+    bool direct;
+    if (g.ksplit == 1) {
+        C = g.C + (long)bz * g.strideC;
+        ldc = g.ldc;
+        direct = true;
+    } else {
+        C = g.partial + ((long)bz * g.ksplit + slice) * (long)g.M * g.N;
+        ldc = g.N;
+        direct = false;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int n = n0 + wn * 64 + j * 32 + l32;
+        if (n >= g.N) continue;
+        const float bv = (direct && g.bias) ? g.bias[n] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                if (m < g.M) {
+                    float v = acc[i][j][r] + bv;
+                    float *dst = C + (long)m * ldc + n;
+                    if (direct && g.accumulate) v += *dst;
+                    *dst = v;
+                }
+            }
+        }
+    }
+    if (g.ready) {
+        // publish the finished tile (see gemm.hip): stores reach L2, one
+        // device-scope release per tile, then the panel count
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        __syncthreads();
+        if (tid == 0) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            __hip_atomic_fetch_add(g.ready + mt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    }  // tiles
+}
+
+}  // namespace dma
+}  // namespace rnn355

@@ -105,9 +105,16 @@ RecPlan plan_rec(int cell, int T, int B, int NH, int Dh, bool bf16, int num_cu,
 // may sit in a captured graph).
 hipError_t launch_clear_u32(unsigned *p, long n, unsigned *q, long nq, hipStream_t s);
 
-// a.ready set: only the MFMA kernel waits on row panels (kRecMfma plans).
+// The recurrence on a finished gx (a.ready must be null).
 hipError_t launch_rec_fwd(int cell, const RecPlan &p, const RecArgs &a, bool bf16,
                           hipStream_t s);
+
+// Pipelined forward in one launch (MFMA plan, Dh = 128, bf16, Din % 32 ==
+// 0): n_gemm workgroups run the k-major input projection g (with g.ready),
+// p.grid more run the recurrence a waiting on a.ready.  Dynamic LDS of the
+// contraction is set up here.
+hipError_t launch_fwd_fused(int cell, const RecPlan &p, const RecArgs &a, const GemmArgs &g,
+                            int n_gemm, hipStream_t s);
 
 // Multi-CU forward recurrence (rec_mc.hip).
 struct McPlan {

@@ -26,10 +26,12 @@
 // Simple kernel (f32, or shapes the MFMA kernel does not cover): R in LDS as
 // float32, one thread per (row, gate column) dot product per step.
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
 #include "gates.h"
+#include "gemm_dma.h"
 #include "kernels.h"
 
 namespace rnn355 {
@@ -93,7 +95,7 @@ __device__ __forceinline__ void lstm_or_gru_unit(const float *gpre, int DH, cons
 // panels included).  Panels found complete are remembered; once the
 // projection is ahead, a check costs a compare.
 template <int CELL, int DH, int R4, int PD, bool WAIT>
-__global__ __launch_bounds__(DH / 16 * 64) void rec_fwd_mfma_kernel(RecArgs a) {
+__device__ __forceinline__ void rec_fwd_mfma_body(const RecArgs &a, const int blk) {
     constexpr int G = CellTraits<CELL>::G;
     constexpr int GD = G * DH;
     constexpr int NW = DH / 16;   // waves = 16-unit blocks
@@ -107,8 +109,8 @@ __global__ __launch_bounds__(DH / 16 * 64) void rec_fwd_mfma_kernel(RecArgs a) {
 
     __shared__ __attribute__((aligned(16))) uint16_t hbuf[2][16 * HLD];
 
-    const int n = blockIdx.x % a.NH;
-    const int b0 = (blockIdx.x / a.NH) * a.BT;
+    const int n = blk % a.NH;
+    const int b0 = (blk / a.NH) * a.BT;
     const int rows = min(a.BT, a.B - b0);
     const int H = a.NH * DH, N = a.NH * GD;
     const int T = a.T, B = a.B;
@@ -328,6 +330,30 @@ __global__ __launch_bounds__(DH / 16 * 64) void rec_fwd_mfma_kernel(RecArgs a) {
     }
 }
 
+template <int CELL, int DH, int R4, int PD, bool WAIT>
+__global__ __launch_bounds__(DH / 16 * 64) void rec_fwd_mfma_kernel(RecArgs a) {
+    rec_fwd_mfma_body<CELL, DH, R4, PD, WAIT>(a, blockIdx.x);
+}
+
+// The pipelined forward as one launch (Dh = 128: both roles run 512
+// threads): workgroups [0, n_gemm) compute the input projection, output
+// tiles in time order and each finished tile counted on its row panel;
+// the rest run the recurrence, waiting for the panels of their next steps.
+// Workgroups are dispatched in index order, so every projection workgroup
+// is resident before any recurrence workgroup starts to wait, and the
+// projection waits on nothing: the launch cannot stall on itself, whatever
+// else shares the chip.
+template <int CELL, int DH, int R4, int PD>
+__global__ __launch_bounds__(512) void fwd_fused_kernel(RecArgs a, GemmArgs g, int n_gemm) {
+    static_assert(DH / 16 * 64 == 512, "both roles run 512 threads");
+    extern __shared__ __attribute__((aligned(16))) char fused_lds[];
+    if ((int)blockIdx.x < n_gemm) {
+        dma::gemm_dma_tiles(g, blockIdx.x, n_gemm, (dma::lds_char *)fused_lds);
+        return;
+    }
+    rec_fwd_mfma_body<CELL, DH, R4, PD, true>(a, blockIdx.x - n_gemm);
+}
+
 // Simple kernel: dynamic LDS = R [Dh][G*Dh] f32 | h operand [BT][Dh] |
 // c state [BT][Dh] | h state [BT][Dh] | gate pre-activations [BT][G*Dh].
 template <int CELL, bool BF16>
@@ -408,8 +434,7 @@ void launch_mfma_rows_w(const RecPlan &p, const RecArgs &a, hipStream_t s) {
 
 template <int CELL, int DH>
 hipError_t launch_mfma_rows(const RecPlan &p, const RecArgs &a, hipStream_t s) {
-    if (a.ready) launch_mfma_rows_w<CELL, DH, true>(p, a, s);
-    else launch_mfma_rows_w<CELL, DH, false>(p, a, s);
+    launch_mfma_rows_w<CELL, DH, false>(p, a, s);
     return hipGetLastError();
 }
 
@@ -479,6 +504,21 @@ RecPlan plan_rec(int cell, int T, int B, int NH, int Dh, bool bf16, int num_cu,
     return p;
 }
 
+template <int CELL, int R4, int PD>
+hipError_t launch_fused_t(const RecPlan &p, const RecArgs &a, const GemmArgs &g, int n_gemm,
+                          hipStream_t s) {
+    static std::once_flag once;
+    static hipError_t attr = hipSuccess;
+    std::call_once(once, [] {
+        attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&fwd_fused_kernel<CELL, 128, R4, PD>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)dma::LDS_BYTES);
+    });
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((fwd_fused_kernel<CELL, 128, R4, PD>), dim3(n_gemm + p.grid), dim3(512),
+                       dma::LDS_BYTES, s, a, g, n_gemm);
+    return hipGetLastError();
+}
+
 hipError_t launch_clear_u32(unsigned *p, long n, unsigned *q, long nq, hipStream_t s) {
     if (n < 0 || nq < 0 || n + nq == 0) return hipSuccess;
     const long blocks = std::min<long>(1024, (n + nq + 255) / 256);
@@ -486,9 +526,24 @@ hipError_t launch_clear_u32(unsigned *p, long n, unsigned *q, long nq, hipStream
     return hipGetLastError();
 }
 
+hipError_t launch_fwd_fused(int cell, const RecPlan &p, const RecArgs &a, const GemmArgs &g,
+                            int n_gemm, hipStream_t s) {
+    if (p.kind != kRecMfma || a.Dh != 128 || !a.ready || !g.ready || n_gemm <= 0 ||
+        !gemm_dma_ok(g.K))
+        return hipErrorInvalidValue;
+    switch (p.upt) {
+        case 1: return cell == kLSTM ? launch_fused_t<kLSTM, 1, 8>(p, a, g, n_gemm, s)
+                                     : launch_fused_t<kGRU, 1, 8>(p, a, g, n_gemm, s);
+        case 2: return cell == kLSTM ? launch_fused_t<kLSTM, 2, 4>(p, a, g, n_gemm, s)
+                                     : launch_fused_t<kGRU, 2, 4>(p, a, g, n_gemm, s);
+        default: return cell == kLSTM ? launch_fused_t<kLSTM, 4, 2>(p, a, g, n_gemm, s)
+                                      : launch_fused_t<kGRU, 4, 2>(p, a, g, n_gemm, s);
+    }
+}
+
 hipError_t launch_rec_fwd(int cell, const RecPlan &p, const RecArgs &a, bool bf16,
                           hipStream_t s) {
-    if (a.ready && p.kind != kRecMfma) return hipErrorInvalidValue;
+    if (a.ready) return hipErrorInvalidValue;  // waiting recurrences run fused
     if (p.kind == kRecMfma) {
         return cell == kLSTM ? launch_mfma<kLSTM>(p, a, s) : launch_mfma<kGRU>(p, a, s);
     }

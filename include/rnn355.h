@@ -156,19 +156,18 @@ rnn_status rnn_rec_gru(const rnn_dims *d, rnn_dtype dt, const float *gx,
  * rnn_rec_lstm.  h_seq, c_seq [T][B][H] may be NULL; hT, cT required.
  *
  * When the recurrence runs one workgroup per (head, batch tile) on at most
- * half the compute units (bf16, Dh in {32, 64, 128}) and the projection has
- * more than two waves of 256x256 output tiles for the remaining units, the
- * two phases overlap: the projection runs on a side stream the library owns
- * (one per device, default priority, created on first use) in time order
- * and marks finished 256-row panels of gx; the recurrence waits for the
- * panels of its next steps.  Results are bitwise those of the serial order.
- * The environment variable RNN355_PIPELINE=0 forces the serial order, =1
- * the overlap wherever the first condition holds.  `stream` waits for the
- * side stream before the call's work is complete, so stream order and graph
- * capture see one fork and one join.  Calls that overlap on one device
- * serialise their projections on the shared side stream.  A panel wait that
- * runs out (RNN355_SPIN_LIMIT polls) sets the workspace's timeout word
- * instead of hanging (rnn_workspace_status).
+ * half the compute units (bf16, Dh = 128, Din % 32 == 0) and the projection
+ * has more than two waves of 256x256 output tiles for the remaining units,
+ * the two phases run as one launch: its first workgroups compute the
+ * projection in time order and mark finished 256-row panels of gx, the rest
+ * run the recurrence and wait for the panels of their next steps.
+ * Workgroups start in index order, so the projection never waits behind the
+ * recurrence, also when kernels are serialised (profilers).  Results are
+ * bitwise those of the serial order.  The environment variable
+ * RNN355_PIPELINE=0 forces the serial order, =1 the single launch wherever
+ * the first condition holds.  A panel wait that runs out (RNN355_SPIN_LIMIT
+ * polls) sets the workspace's timeout word instead of hanging
+ * (rnn_workspace_status).
  */
 rnn_status rnn_fwd_lstm(const rnn_dims *d, rnn_dtype dt,
                         const void *x, const void *W, const void *R,

@@ -124,8 +124,9 @@ def test_backward_rejects_unsupported_and_invalid_before_launch():
 def test_plans_of_the_workloads(monkeypatch):
     """Kernel plans are pure host decisions (256 compute units assumed when
     no device is visible): one-CU resident-R kernel for Dh <= 128, multi-CU
-    split above; the forward overlaps projection and recurrence only when
-    the recurrence leaves half the chip free and the projection is large."""
+    split above; the forward overlaps projection and recurrence (one fused
+    launch, Dh = 128) only when the recurrence leaves half the chip free and
+    the projection is large."""
     monkeypatch.delenv("RNN355_PIPELINE", raising=False)
     monkeypatch.delenv("RNN355_REC_BT", raising=False)
     monkeypatch.delenv("RNN355_REC_K", raising=False)
@@ -144,8 +145,14 @@ def test_plans_of_the_workloads(monkeypatch):
     monkeypatch.setenv("RNN355_PIPELINE", "0")
     assert "input_proj=serial" in g.plan_describe(g.OP_FWD_LSTM, head, g.RNN_BF16)
     monkeypatch.setenv("RNN355_PIPELINE", "1")
-    small = g.Dims(233, 5, 96, 2, 64)
+    small = g.Dims(233, 5, 96, 2, 128)
     assert "input_proj=pipelined" in g.plan_describe(g.OP_FWD_LSTM, small, g.RNN_BF16)
+    # only the Dh = 128 one-CU kernel runs fused with the projection, and only
+    # with Din % 32 == 0
+    assert "input_proj=serial" in g.plan_describe(g.OP_FWD_LSTM, g.Dims(233, 5, 96, 2, 64),
+                                                  g.RNN_BF16)
+    assert "input_proj=serial" in g.plan_describe(g.OP_FWD_LSTM, g.Dims(233, 5, 40, 2, 128),
+                                                  g.RNN_BF16)
     # never when the recurrence would hold more than half the units
     big = g.Dims(64, 16, 64, 16, 128)
     p = g.plan_describe(g.OP_FWD_LSTM, big, g.RNN_BF16)

@@ -239,14 +239,15 @@ def _with_env(key, val, fn):
 
 
 @pytest.mark.parametrize("cell,T,B,NH,Dh,Din", [
-    ("lstm", 233, 5, 2, 64, 96),     # 1165 rows: 5 row panels, the last one ragged
+    ("lstm", 233, 5, 2, 128, 96),    # 1165 rows: 5 row panels, the last one ragged
     ("gru", 300, 16, 3, 128, 64),    # 19 row panels, 16 rows per step
-    ("lstm", 96, 11, 4, 32, 32),     # 1056 rows, steps straddle panel edges
+    ("lstm", 96, 11, 4, 128, 32),    # 1056 rows, steps straddle panel edges
 ])
 def test_pipelined_forward_matches_serial_bitwise_and_oracle(cell, T, B, NH, Dh, Din):
-    """The forward that overlaps the input projection with the recurrence
-    (row panels published by the projection, waited on by the recurrence)
-    gives bitwise the serial result, and that result matches the oracle."""
+    """The forward that overlaps the input projection with the recurrence in
+    one launch (row panels published by the projection's workgroups, waited
+    on by the recurrence's) gives bitwise the serial result, and that result
+    matches the oracle."""
     d = synth.Dims(T=T, B=B, Din=Din, NH=NH, Dh=Dh)
     op = g.OP_FWD_LSTM if cell == "lstm" else g.OP_FWD_GRU
     gd = g.Dims(T, B, Din, NH, Dh)
@@ -290,10 +291,10 @@ def test_pipelined_headline_forward_repeatable_and_equal_to_serial():
 
 def test_pipelined_forward_reads_fresh_projection_after_reuse():
     """Two pipelined calls on one workspace with different inputs: the second
-    call's projection overwrites gx (2 MiB, small enough to stay cached) while
+    call's projection overwrites gx (4 MiB, about what an XCD's L2 holds) while
     its recurrence reads it; the result must be the serial one for the second
     inputs, never the first call's cached values."""
-    d = synth.Dims(T=256, B=4, Din=64, NH=2, Dh=64)
+    d = synth.Dims(T=256, B=4, Din=64, NH=2, Dh=128)
     gd = g.Dims(d.T, d.B, d.Din, d.NH, d.Dh)
     os.environ["RNN355_PIPELINE"] = "1"   # removed by the fixture
     assert "input_proj=pipelined" in g.plan_describe(g.OP_FWD_LSTM, gd, g.RNN_BF16)
