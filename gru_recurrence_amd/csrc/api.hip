@@ -270,9 +270,10 @@ rnn_status forward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, con
     const long panels = gx_panels(d);
     if (pipelined(ch, d, dt, cus)) {
         auto ok = [](hipError_t e) { return e == hipSuccess; };
-        // W^T for the k-major contraction; status word and panel counters zeroed
-        if (!ok(launch_transpose_bf16((const uint16_t *)W, wt, d->Din, N, 1, s)) ||
-            !ok(launch_clear_u32((unsigned *)ws, 64, ready, panels, s)))
+        // W^T for the k-major contraction; the same launch zeroes the status
+        // words of the header and the panel counters
+        if (!ok(launch_transpose_bf16((const uint16_t *)W, wt, d->Din, N, 1, s, (unsigned *)ws, 64,
+                                      ready, panels)))
             return RNN_ERR_HIP;
         GemmArgs g{};
         g.M = M; g.N = N; g.K = d->Din;

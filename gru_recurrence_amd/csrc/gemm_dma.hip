@@ -41,23 +41,64 @@ __global__ __launch_bounds__(NTHR) void gemm_dma_kernel(GemmArgs g) {
 }
 
 // dst[b][c][r] = src[b][r][c] for bf16 matrices [R][C] (row pitch C), in
-// 64x64 tiles through LDS; grid (ceil(C/64), ceil(R/64), batch).
+// 64x64 tiles through LDS with 16-byte loads and stores where a row of the
+// tile is whole and aligned (C % 8 == 0 for loads, R % 8 == 0 for stores);
+// grid (ceil(C/64), ceil(R/64), batch).  Block (0,0,0) also zeroes the
+// `nclear` words at `clear` and the `nclear2` at `clear2` (the status words
+// and panel counters of the forward that follows), saving a launch.
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t *__restrict__ src,
                                                              uint16_t *__restrict__ dst, int R,
-                                                             int C, long bstride) {
-    __shared__ uint16_t t[64][66];
+                                                             int C, long bstride, unsigned *clear,
+                                                             long nclear, unsigned *clear2,
+                                                             long nclear2) {
+    __shared__ __attribute__((aligned(16))) uint16_t t[64][72];
     const uint16_t *S = src + blockIdx.z * bstride;
     uint16_t *D = dst + blockIdx.z * bstride;
     const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
-    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-    for (int i = ty; i < 64; i += 4) {
-        const int r = r0 + i, c = c0 + tx;
-        t[i][tx] = (r < R && c < C) ? S[(long)r * C + c] : (uint16_t)0;
+    const int tid = threadIdx.x;
+    if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) {
+        if (clear)
+            for (long i = tid; i < nclear; i += 256) clear[i] = 0u;
+        if (clear2)
+            for (long i = tid; i < nclear2; i += 256) clear2[i] = 0u;
+    }
+    // load: 64 rows x 8 chunks of 8 columns, two chunks per thread
+    for (int q = tid; q < 512; q += 256) {
+        const int i = q >> 3, cc = (q & 7) * 8;
+        const int r = r0 + i, c = c0 + cc;
+        uint16_t v[8];
+        if (r < R && c + 8 <= C && (C & 7) == 0) {
+            const uint4 w = *reinterpret_cast<const uint4 *>(S + (long)r * C + c);
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[2 * e] = (uint16_t)ws[e];
+                v[2 * e + 1] = (uint16_t)(ws[e] >> 16);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = (r < R && c + e < C) ? S[(long)r * C + c + e] : (uint16_t)0;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t[i][cc + e] = v[e];
     }
     __syncthreads();
-    for (int i = ty; i < 64; i += 4) {
-        const int c = c0 + i, r = r0 + tx;
-        if (c < C && r < R) D[(long)c * R + r] = t[tx][i];
+    // store: 64 output rows (c) x 8 chunks of 8 source rows (r)
+    for (int q = tid; q < 512; q += 256) {
+        const int i = q >> 3, rr = (q & 7) * 8;
+        const int c = c0 + i, r = r0 + rr;
+        if (c >= C) continue;
+        if (r + 8 <= R && (R & 7) == 0) {
+            uint32_t ws[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                ws[e] = (uint32_t)t[rr + 2 * e][i] | ((uint32_t)t[rr + 2 * e + 1][i] << 16);
+            *reinterpret_cast<uint4 *>(D + (long)c * R + r) = make_uint4(ws[0], ws[1], ws[2], ws[3]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (r + e < R) D[(long)c * R + r + e] = t[rr + e][i];
+        }
     }
 }
 
@@ -86,9 +127,11 @@ hipError_t launch_gemm_dma(const GemmArgs &g0, int batch, hipStream_t s) {
 }
 
 hipError_t launch_transpose_bf16(const uint16_t *src, uint16_t *dst, int R, int C, int batch,
-                                 hipStream_t s) {
+                                 hipStream_t s, unsigned *clear, long nclear, unsigned *clear2,
+                                 long nclear2) {
     dim3 grid((C + 63) / 64, (R + 63) / 64, batch);
-    hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, s, src, dst, R, C, (long)R * C);
+    hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, s, src, dst, R, C, (long)R * C,
+                       clear, nclear, clear2, nclear2);
     return hipGetLastError();
 }
 

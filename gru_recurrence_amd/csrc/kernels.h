@@ -60,9 +60,11 @@ hipError_t launch_splitk_reduce(const GemmArgs &g, int batch, hipStream_t s);
 // global-to-LDS loads (gemm_dma.hip).  B(n,k) = B[n*ldb + k].
 bool gemm_dma_ok(int K);
 hipError_t launch_gemm_dma(const GemmArgs &g, int batch, hipStream_t s);
-// dst[b][c][r] = src[b][r][c], bf16 [R][C] matrices, `batch` of them.
+// dst[b][c][r] = src[b][r][c], bf16 [R][C] matrices, `batch` of them; the
+// same launch zeroes nclear words at `clear` and nclear2 at `clear2` (if set).
 hipError_t launch_transpose_bf16(const uint16_t *src, uint16_t *dst, int R, int C, int batch,
-                                 hipStream_t s);
+                                 hipStream_t s, unsigned *clear = nullptr, long nclear = 0,
+                                 unsigned *clear2 = nullptr, long nclear2 = 0);
 hipError_t launch_gemm_f32(const GemmF32Args &g, int batch, hipStream_t s);
 
 // Forward recurrence (rec_fwd.hip).
@@ -101,9 +103,6 @@ struct RecPlan {
 RecPlan plan_rec(int cell, int T, int B, int NH, int Dh, bool bf16, int num_cu,
                  int bt_override);
 
-// Zeroes p[0, n) and q[0, nq) on stream s in one launch (a kernel, so it
-// may sit in a captured graph).
-hipError_t launch_clear_u32(unsigned *p, long n, unsigned *q, long nq, hipStream_t s);
 
 // The recurrence on a finished gx (a.ready must be null).
 hipError_t launch_rec_fwd(int cell, const RecPlan &p, const RecArgs &a, bool bf16,

@@ -438,13 +438,6 @@ hipError_t launch_mfma_rows(const RecPlan &p, const RecArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-__global__ void clear_u32_kernel(unsigned *p, long n, unsigned *q, long nq) {
-    const long stride = (long)gridDim.x * blockDim.x;
-    for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n + nq; i += stride) {
-        if (i < n) p[i] = 0u;
-        else q[i - n] = 0u;
-    }
-}
 
 template <int CELL>
 hipError_t launch_mfma(const RecPlan &p, const RecArgs &a, hipStream_t s) {
@@ -519,12 +512,6 @@ hipError_t launch_fused_t(const RecPlan &p, const RecArgs &a, const GemmArgs &g,
     return hipGetLastError();
 }
 
-hipError_t launch_clear_u32(unsigned *p, long n, unsigned *q, long nq, hipStream_t s) {
-    if (n < 0 || nq < 0 || n + nq == 0) return hipSuccess;
-    const long blocks = std::min<long>(1024, (n + nq + 255) / 256);
-    hipLaunchKernelGGL(clear_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n, q, nq);
-    return hipGetLastError();
-}
 
 hipError_t launch_fwd_fused(int cell, const RecPlan &p, const RecArgs &a, const GemmArgs &g,
                             int n_gemm, hipStream_t s) {
