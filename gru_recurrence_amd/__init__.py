@@ -27,6 +27,7 @@ OP_FWD_LSTM, OP_FWD_GRU, OP_BWD_LSTM, OP_BWD_GRU, OP_REC_LSTM, OP_REC_GRU = rang
 EXPORTS = ("rnn_status_str", "rnn_workspace_size", "rnn_plan_describe", "rnn_input_proj",
            "rnn_input_proj_t",
            "rnn_rec_lstm", "rnn_rec_gru", "rnn_fwd_lstm", "rnn_fwd_gru", "rnn_bwd_lstm",
+           "rnn_bwd_gru",
            "rnn_workspace_status")
 
 
@@ -68,9 +69,11 @@ def load(path: Optional[str] = None):
     lib.rnn_fwd_lstm.argtypes = [D, I, P, P, P, P, P, P, P, P, P, P, P, S, P]
     lib.rnn_fwd_gru.argtypes = [D, I, P, P, P, P, P, P, P, P, S, P]
     lib.rnn_bwd_lstm.argtypes = [D, I] + [P] * 17 + [P, S, P]
+    lib.rnn_bwd_gru.argtypes = [D, I] + [P] * 13 + [P, S, P]
     lib.rnn_workspace_status.argtypes = [P, S, P]
     for f in ("rnn_plan_describe", "rnn_input_proj", "rnn_input_proj_t", "rnn_rec_lstm", "rnn_rec_gru",
-              "rnn_fwd_lstm", "rnn_fwd_gru", "rnn_bwd_lstm", "rnn_workspace_status"):
+              "rnn_fwd_lstm", "rnn_fwd_gru", "rnn_bwd_lstm", "rnn_bwd_gru",
+              "rnn_workspace_status"):
         getattr(lib, f).restype = I
     _lib = lib
     return lib
@@ -338,6 +341,33 @@ def lstm_bwd(x, W, R, b, h0, c0, h_seq, c_seq, dh_seq, dhT=None, dcT=None, *, ws
                             _ptr(g["dc0"], "dc0", f32, shapes["dc0"]),
                             _ptr(ws, "ws"), ws.numel(), _stream(stream))
     _check(s, "rnn_bwd_lstm")
+    return g
+
+
+def gru_bwd(x, W, R, b, h0, h_seq, dh_seq, dhT=None, *, ws=None, out=None, stream=None):
+    """Multi-head GRU BPTT.  Returns dict dx, dW, dR, db, dh0 (taken from
+    ``out`` where given, else allocated)."""
+    torch = _torch()
+    d, dt, N = _common(x, W, R, 3)
+    H = d.NH * d.Dh
+    dev = x.device
+    f32 = torch.float32
+    shapes = dict(dx=(d.T, d.B, d.Din), dW=(d.Din, N), dR=(d.NH, d.Dh, 3 * d.Dh), db=(N,),
+                  dh0=(d.B, H))
+    out = out or {}
+    g = {k: out[k] if out.get(k) is not None else torch.empty(v, dtype=f32, device=dev)
+         for k, v in shapes.items()}
+    ws = _workspace(OP_BWD_GRU, d, dt, dev, ws)
+    seq = (d.T, d.B, H)
+    s = load().rnn_bwd_gru(ctypes.byref(d), dt, _ptr(x, "x"), _ptr(W, "W"), _ptr(R, "R"),
+                           _ptr(b, "b", f32, (N,), True), _ptr(h0, "h0", f32, (d.B, H), True),
+                           _ptr(h_seq, "h_seq", f32, seq), _ptr(dh_seq, "dh_seq", f32, seq),
+                           _ptr(dhT, "dhT", f32, (d.B, H), True),
+                           _ptr(g["dx"], "dx", f32, shapes["dx"]), _ptr(g["dW"], "dW", f32, shapes["dW"]),
+                           _ptr(g["dR"], "dR", f32, shapes["dR"]), _ptr(g["db"], "db", f32, shapes["db"]),
+                           _ptr(g["dh0"], "dh0", f32, shapes["dh0"]),
+                           _ptr(ws, "ws"), ws.numel(), _stream(stream))
+    _check(s, "rnn_bwd_gru")
     return g
 
 

@@ -63,28 +63,33 @@ size_t wt_bytes(const rnn_dims *d, int G) {
     return align_up(sizeof(uint16_t) * (size_t)d->Din * d->NH * G * d->Dh);
 }
 
-// Backward workspace after the header: dA exchange slots, recomputed
-// pre-activations A (f32), gate gradients dA (bf16), h_{t-1} (bf16) and the
-// per-batch-tile bias-gradient partials.
+// Backward workspace after the header: the exchange slots of the sweep, the
+// recomputed pre-activations A (LSTM: Gx + h_{t-1} R; GRU: Gx alone) and the
+// GRU's recurrent sums S (f32), the gate-input gradients dA and the GRU's
+// recurrent-sum gradients dS (bf16), h_{t-1} (bf16), the per-batch-tile bias
+// partials, split-K partials, W^T and R^T per head.
 struct BwdLayout {
-    size_t xchg, A, dA, hprev, dbp, part, wt, rt, total;
+    size_t xchg, A, S, dA, dS, hprev, dbp, part, wt, rt, total;
 };
-BwdLayout bwd_layout(const rnn_dims *d) {
+BwdLayout bwd_layout(const rnn_dims *d, int G) {
     BwdLayout L{};
-    const size_t TB = (size_t)d->T * d->B, N = (size_t)d->NH * 4 * d->Dh;
+    const bool gru = G == 3;
+    const size_t TB = (size_t)d->T * d->B, N = (size_t)d->NH * G * d->Dh;
     const size_t H = (size_t)d->NH * d->Dh;
     size_t off = 0;
-    L.xchg = off; off += align_up(8u * (size_t)d->NH * (d->B + 15) * 2 * d->Dh * 2);
+    L.xchg = off; off += align_up(8u * (size_t)d->NH * (d->B + 15) * 2 * ((size_t)G * d->Dh / 2));
     L.A = off;    off += align_up(sizeof(float) * TB * N);
+    L.S = off;    off += gru ? align_up(sizeof(float) * TB * N) : 0;
     L.dA = off;   off += align_up(sizeof(uint16_t) * TB * N);
+    L.dS = off;   off += gru ? align_up(sizeof(uint16_t) * TB * N) : 0;
     L.hprev = off; off += align_up(sizeof(uint16_t) * TB * H);
     L.dbp = off;  off += align_up(sizeof(float) * (size_t)d->B * N);
     // split-K partials of the dW and dR contractions (used one after the other)
     const size_t pw = gemm_partial_bytes(d->Din, (int)N, 1, kMaxSplitK);
-    const size_t pr = gemm_partial_bytes(d->Dh, 4 * d->Dh, d->NH, kMaxSplitK);
+    const size_t pr = gemm_partial_bytes(d->Dh, G * d->Dh, d->NH, kMaxSplitK);
     L.part = off; off += align_up(pw > pr ? pw : pr);
-    L.wt = off;   off += wt_bytes(d, 4);                                     // W^T [N][Din]
-    L.rt = off;   off += align_up(sizeof(uint16_t) * (size_t)d->NH * 4 * d->Dh * d->Dh);  // R^T per head
+    L.wt = off;   off += wt_bytes(d, G);                                     // W^T [N][Din]
+    L.rt = off;   off += align_up(sizeof(uint16_t) * (size_t)d->NH * G * d->Dh * d->Dh);  // R^T per head
     L.total = off;
     return L;
 }
@@ -305,6 +310,109 @@ rnn_status forward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, con
     return rec_fwd(cell, d, dt, gx, R, h0, c0, h_seq, c_seq, hT, cT, ws, s);
 }
 
+// Backpropagation through time (pointers validated by the entry points).
+// 1. h_{t-1} as bf16, the gate inputs recomputed for all t at once: LSTM A =
+//    x W + b + h_{t-1} R; GRU Gx = x W + b and S = h_{t-1} R apart.
+// 2. The reverse sweep (rec_bwd.hip) -> dA (and the GRU's dS), db partials,
+//    dh0 (dc0).
+// 3. db, dW = x^T dA, dx = dA W^T, dR = h_{t-1}^T dS (dS = dA for the LSTM).
+rnn_status backward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, const void *W,
+                    const void *R, const float *b, const float *h0, const float *c0,
+                    const float *h_seq, const float *c_seq, const float *dh_seq,
+                    const float *dhT, const float *dcT, float *dx, float *dW, float *dR,
+                    float *db, float *dh0, float *dc0, void *ws, size_t ws_bytes,
+                    hipStream_t stream) {
+    if (dt != RNN_BF16) return RNN_ERR_UNSUPPORTED;
+    const bool lstm = cell == kLSTM;
+    const int G = lstm ? 4 : 3, Dh = d->Dh, NH = d->NH, T = d->T, B = d->B, Din = d->Din;
+    const int GD = G * Dh, N = NH * GD, H = NH * Dh, M = T * B;
+    if (!gemm_shape_ok(Din, N, dt) || Dh % 16 != 0) return RNN_ERR_UNSUPPORTED;
+    const BwdPlan p = plan_bwd(cell, B, NH, Dh, device_cus(), bt_override(), k_override());
+    if (!p.ok) return RNN_ERR_UNSUPPORTED;
+    const rnn_op op = lstm ? RNN_OP_BWD_LSTM : RNN_OP_BWD_GRU;
+    if (!ws || ws_bytes < rnn_workspace_size(op, d, dt)) return RNN_ERR_WORKSPACE;
+
+    char *base = (char *)ws + kHeader;
+    const BwdLayout L = bwd_layout(d, G);
+    float *A = (float *)(base + L.A);
+    float *S = lstm ? A : (float *)(base + L.S);
+    uint16_t *dA = (uint16_t *)(base + L.dA);
+    uint16_t *dS = lstm ? dA : (uint16_t *)(base + L.dS);
+    uint16_t *hprev = (uint16_t *)(base + L.hprev);
+    float *dbp = (float *)(base + L.dbp);
+    uint16_t *wt = (uint16_t *)(base + L.wt);
+    uint16_t *rt = (uint16_t *)(base + L.rt);
+    const uint16_t *xb = (const uint16_t *)x, *Wb = (const uint16_t *)W, *Rb = (const uint16_t *)R;
+    auto ok = [](hipError_t e) { return e == hipSuccess; };
+
+    // 1. h_{t-1} as bf16; gate inputs for all t at once
+    if (!ok(launch_hprev_bf16(h0, h_seq, hprev, (long)B * H, (long)M * H, stream))) return RNN_ERR_HIP;
+    if (input_proj(M, Din, N, dt, x, W, b, A, (uint32_t *)ws, stream, nullptr, wt) != RNN_OK)
+        return RNN_ERR_HIP;
+    {
+        GemmArgs g{};  // h_{t-1} R per head: added to A (LSTM) or into S (GRU)
+        g.M = M; g.N = GD; g.K = Dh;
+        g.A = hprev; g.lda = H; g.strideA = Dh;       // row m, k = unit of head n
+        g.C = S; g.ldc = N; g.strideC = GD;
+        g.accumulate = lstm ? 1 : 0;
+        if (gemm_dma_ok(Dh)) {
+            // R^T per head: B(c, k) = R[n][k][c] at rt[n][c][k]
+            if (!ok(launch_transpose_bf16(Rb, rt, Dh, GD, NH, stream))) return RNN_ERR_HIP;
+            g.B = rt; g.ldb = Dh; g.strideB = (long)GD * Dh;
+            if (!ok(launch_gemm_dma(g, NH, stream))) return RNN_ERR_HIP;
+        } else {
+            g.B = Rb; g.ldb = GD; g.strideB = (long)Dh * GD;  // R[n][k][c]: r-major
+            if (!ok(launch_gemm_bf16(g, true, false, NH, stream))) return RNN_ERR_HIP;
+        }
+    }
+    // 2. the reverse-time sweep
+    {
+        BwdArgs m{};
+        m.T = T; m.B = B; m.NH = NH; m.Dh = Dh; m.BT = p.BT;
+        m.K = p.K; m.KS = p.ks; m.NB = p.nb;
+        m.A = A; m.S = lstm ? nullptr : S;
+        m.c_seq = c_seq; m.c0 = c0; m.h_seq = h_seq; m.h0 = h0;
+        m.dh_seq = dh_seq; m.dhT = dhT; m.dcT = dcT;
+        m.Rb = Rb; m.dA = dA; m.dS = lstm ? nullptr : dS;
+        m.db_part = dbp; m.dh0 = dh0; m.dc0 = dc0;
+        m.xg = (unsigned long long *)(base + L.xchg);
+        m.flag = (unsigned *)ws;
+        m.spin_limit = spin_limit();
+        if (!ok(launch_rec_bwd(cell, p, m, stream))) return RNN_ERR_HIP;
+    }
+    // 3. parameter and input gradients
+    if (!ok(launch_db_reduce(dbp, p.nbt, N, db, stream))) return RNN_ERR_HIP;
+    float *part = (float *)(base + L.part);
+    const int cus = device_cus();
+    {
+        GemmArgs g{};  // dW[k][c] = sum_m x[m][k] dA[m][c]
+        g.M = Din; g.N = N; g.K = M;
+        g.A = xb; g.lda = Din; g.B = dA; g.ldb = N; g.C = dW; g.ldc = N;
+        g.ksplit = std::min(gemm_splitk_for(Din, N, M, 1, cus), kMaxSplitK);
+        g.partial = part;
+        if (!ok(launch_gemm_bf16(g, false, false, 1, stream))) return RNN_ERR_HIP;
+    }
+    {
+        GemmArgs g{};  // dx[m][k] = sum_c dA[m][c] W[k][c]
+        g.M = M; g.N = Din; g.K = N;
+        g.A = dA; g.lda = N; g.B = Wb; g.ldb = N; g.C = dx; g.ldc = Din;
+        const hipError_t e = gemm_dma_ok(N) ? launch_gemm_dma(g, 1, stream)
+                                            : launch_gemm_bf16(g, true, true, 1, stream);
+        if (!ok(e)) return RNN_ERR_HIP;
+    }
+    {
+        GemmArgs g{};  // dR[n][i][c] = sum_m h_{t-1}[m][n*Dh+i] dS[m][n*GD+c]
+        g.M = Dh; g.N = GD; g.K = M;
+        g.A = hprev; g.lda = H; g.strideA = Dh;
+        g.B = dS; g.ldb = N; g.strideB = GD;
+        g.C = dR; g.ldc = GD; g.strideC = (long)Dh * GD;
+        g.ksplit = std::min(gemm_splitk_for(Dh, GD, M, NH, cus), kMaxSplitK);
+        g.partial = part;
+        if (!ok(launch_gemm_bf16(g, false, false, NH, stream))) return RNN_ERR_HIP;
+    }
+    return RNN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -332,7 +440,8 @@ size_t rnn_workspace_size(rnn_op op, const rnn_dims *d, rnn_dtype dt) {
         case RNN_OP_REC_GRU:
             return kHeader + xchg_bytes(d);
         case RNN_OP_BWD_LSTM:
-            return kHeader + bwd_layout(d).total;
+        case RNN_OP_BWD_GRU:
+            return kHeader + bwd_layout(d, G).total;
         default:
             return 0;
     }
@@ -457,88 +566,22 @@ rnn_status rnn_bwd_lstm(const rnn_dims *d, rnn_dtype dt, const void *x, const vo
                         dx, dW, dR, db, dh0, dc0, ws};
     for (const void *p : ps)
         if (!aligned16(p)) return RNN_ERR_INVALID_ARG;
-    if (dt != RNN_BF16) return RNN_ERR_UNSUPPORTED;
-    const int G = 4, Dh = d->Dh, NH = d->NH, T = d->T, B = d->B, Din = d->Din;
-    const int GD = G * Dh, N = NH * GD, H = NH * Dh, M = T * B;
-    if (!gemm_shape_ok(Din, N, dt) || Dh % 16 != 0) return RNN_ERR_UNSUPPORTED;
-    const BwdPlan p = plan_bwd(B, NH, Dh, device_cus(), bt_override(), k_override());
-    if (!p.ok) return RNN_ERR_UNSUPPORTED;
-    if (!ws || ws_bytes < rnn_workspace_size(RNN_OP_BWD_LSTM, d, dt)) return RNN_ERR_WORKSPACE;
+    return backward(kLSTM, d, dt, x, W, R, b, h0, c0, h_seq, c_seq, dh_seq, dhT, dcT, dx, dW, dR,
+                    db, dh0, dc0, ws, ws_bytes, stream);
+}
 
-    char *base = (char *)ws + kHeader;
-    const BwdLayout L = bwd_layout(d);
-    float *A = (float *)(base + L.A);
-    uint16_t *dA = (uint16_t *)(base + L.dA);
-    uint16_t *hprev = (uint16_t *)(base + L.hprev);
-    float *dbp = (float *)(base + L.dbp);
-    uint16_t *wt = (uint16_t *)(base + L.wt);
-    uint16_t *rt = (uint16_t *)(base + L.rt);
-    const uint16_t *xb = (const uint16_t *)x, *Wb = (const uint16_t *)W, *Rb = (const uint16_t *)R;
-    auto ok = [](hipError_t e) { return e == hipSuccess; };
-
-    // 1. h_{t-1} as bf16; A = x W + b + h_{t-1} R (block-diagonal), all t at once
-    if (!ok(launch_hprev_bf16(h0, h_seq, hprev, (long)B * H, (long)M * H, stream))) return RNN_ERR_HIP;
-    if (input_proj(M, Din, N, dt, x, W, b, A, (uint32_t *)ws, stream, nullptr, wt) != RNN_OK)
-        return RNN_ERR_HIP;
-    {
-        GemmArgs g{};
-        g.M = M; g.N = GD; g.K = Dh;
-        g.A = hprev; g.lda = H; g.strideA = Dh;       // row m, k = unit of head n
-        g.C = A; g.ldc = N; g.strideC = GD;
-        g.accumulate = 1;
-        if (gemm_dma_ok(Dh)) {
-            // R^T per head: B(c, k) = R[n][k][c] at rt[n][c][k]
-            if (!ok(launch_transpose_bf16(Rb, rt, Dh, GD, NH, stream))) return RNN_ERR_HIP;
-            g.B = rt; g.ldb = Dh; g.strideB = (long)GD * Dh;
-            if (!ok(launch_gemm_dma(g, NH, stream))) return RNN_ERR_HIP;
-        } else {
-            g.B = Rb; g.ldb = GD; g.strideB = (long)Dh * GD;  // R[n][k][c]: r-major
-            if (!ok(launch_gemm_bf16(g, true, false, NH, stream))) return RNN_ERR_HIP;
-        }
-    }
-    // 2. the reverse-time sweep
-    {
-        BwdArgs m{};
-        m.T = T; m.B = B; m.NH = NH; m.Dh = Dh; m.BT = p.BT;
-        m.K = p.K; m.KS = p.ks; m.NB = p.nb;
-        m.A = A; m.c_seq = c_seq; m.c0 = c0; m.dh_seq = dh_seq; m.dhT = dhT; m.dcT = dcT;
-        m.Rb = Rb; m.dA = dA; m.db_part = dbp; m.dh0 = dh0; m.dc0 = dc0;
-        m.xg = (unsigned long long *)(base + L.xchg);
-        m.flag = (unsigned *)ws;
-        m.spin_limit = spin_limit();
-        if (!ok(launch_rec_bwd(p, m, stream))) return RNN_ERR_HIP;
-    }
-    // 3. parameter and input gradients from dA
-    if (!ok(launch_db_reduce(dbp, p.nbt, N, db, stream))) return RNN_ERR_HIP;
-    float *part = (float *)(base + L.part);
-    const int cus = device_cus();
-    {
-        GemmArgs g{};  // dW[k][c] = sum_m x[m][k] dA[m][c]
-        g.M = Din; g.N = N; g.K = M;
-        g.A = xb; g.lda = Din; g.B = dA; g.ldb = N; g.C = dW; g.ldc = N;
-        g.ksplit = std::min(gemm_splitk_for(Din, N, M, 1, cus), kMaxSplitK);
-        g.partial = part;
-        if (!ok(launch_gemm_bf16(g, false, false, 1, stream))) return RNN_ERR_HIP;
-    }
-    {
-        GemmArgs g{};  // dx[m][k] = sum_c dA[m][c] W[k][c]
-        g.M = M; g.N = Din; g.K = N;
-        g.A = dA; g.lda = N; g.B = Wb; g.ldb = N; g.C = dx; g.ldc = Din;
-        const hipError_t e = gemm_dma_ok(N) ? launch_gemm_dma(g, 1, stream)
-                                            : launch_gemm_bf16(g, true, true, 1, stream);
-        if (!ok(e)) return RNN_ERR_HIP;
-    }
-    {
-        GemmArgs g{};  // dR[n][i][c] = sum_m h_{t-1}[m][n*Dh+i] dA[m][n*GD+c]
-        g.M = Dh; g.N = GD; g.K = M;
-        g.A = hprev; g.lda = H; g.strideA = Dh;
-        g.B = dA; g.ldb = N; g.strideB = GD;
-        g.C = dR; g.ldc = GD; g.strideC = (long)Dh * GD;
-        g.ksplit = std::min(gemm_splitk_for(Dh, GD, M, NH, cus), kMaxSplitK);
-        g.partial = part;
-        if (!ok(launch_gemm_bf16(g, false, false, NH, stream))) return RNN_ERR_HIP;
-    }
-    return RNN_OK;
+rnn_status rnn_bwd_gru(const rnn_dims *d, rnn_dtype dt, const void *x, const void *W,
+                       const void *R, const float *b, const float *h0, const float *h_seq,
+                       const float *dh_seq, const float *dhT, float *dx, float *dW, float *dR,
+                       float *db, float *dh0, void *ws, size_t ws_bytes, hipStream_t stream) {
+    if (!dims_ok(d) || !dtype_ok(dt)) return RNN_ERR_INVALID_ARG;
+    if (!x || !W || !R || !h_seq || !dh_seq || !dx || !dW || !dR || !db || !dh0)
+        return RNN_ERR_INVALID_ARG;
+    const void *ps[] = {x, W, R, b, h0, h_seq, dh_seq, dhT, dx, dW, dR, db, dh0, ws};
+    for (const void *p : ps)
+        if (!aligned16(p)) return RNN_ERR_INVALID_ARG;
+    return backward(kGRU, d, dt, x, W, R, b, h0, nullptr, h_seq, nullptr, dh_seq, dhT, nullptr, dx,
+                    dW, dR, db, dh0, nullptr, ws, ws_bytes, stream);
 }
 
 rnn_status rnn_workspace_status(const void *ws, size_t ws_bytes, hipStream_t stream) {

@@ -79,6 +79,17 @@ __device__ __forceinline__ RowPair swap32(float x, float y) {
     return {__uint_as_float(r[0]), __uint_as_float(r[1])};
 }
 
+// Eight wait states pinned right after an MFMA chain.  A vector instruction
+// that reads or overwrites an MFMA destination needs them (the compiler
+// spaces such pairs inside a basic block, but across a branch it has been
+// seen to place a read one instruction after the MFMA, which then saw a
+// stale value); with the pad in place every path after the chain is safe.
+__device__ __forceinline__ void mfma_chain_end() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 __device__ __forceinline__ f32x4 mfma_16x16x32_bf16(const bf16x8 &a, const bf16x8 &b,
                                                      const f32x4 &c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);

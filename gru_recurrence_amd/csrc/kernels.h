@@ -154,22 +154,28 @@ struct BwdPlan {
 
 struct BwdArgs {
     int T, B, NH, Dh, BT, K, KS, NB;
-    const float *A;          // recomputed pre-activations [T][B][NH*4*Dh]
-    const float *c_seq;      // [T][B][H]
-    const float *c0;         // [B][H] or null
+    // LSTM: recomputed pre-activations A = Gx + h_{t-1} R [T][B][NH*4*Dh].
+    // GRU: Gx (x W + b) alone [T][B][NH*3*Dh], the recurrent sums in S.
+    const float *A;
+    const float *S;          // GRU: h_{t-1} R [T][B][NH*3*Dh]
+    const float *c_seq;      // LSTM: [T][B][H]
+    const float *c0;         // LSTM: [B][H] or null
+    const float *h_seq;      // GRU: [T][B][H] (h_{t-1} of the update gate)
+    const float *h0;         // GRU: [B][H] or null
     const float *dh_seq;     // [T][B][H]
-    const float *dhT, *dcT;  // [B][H] or null
+    const float *dhT, *dcT;  // [B][H] or null (dcT: LSTM)
     const uint16_t *Rb;      // bf16 R
-    uint16_t *dA;            // bf16 gate gradients [T][B][NH*4*Dh]
-    float *db_part;          // [nbt][NH*4*Dh]
-    float *dh0, *dc0;        // [B][H]
-    unsigned long long *xg;  // exchange slots [groups][2][BT][2*Dh]
+    uint16_t *dA;            // bf16 gradients of the gate inputs Gx [T][B][N]
+    uint16_t *dS;            // GRU: bf16 gradients of the recurrent sums (dR, carry)
+    float *db_part;          // [nbt][N]
+    float *dh0, *dc0;        // [B][H] (dc0: LSTM)
+    unsigned long long *xg;  // exchange slots [groups][2][BT][G*Dh/2]
     unsigned *flag;
     unsigned spin_limit;
 };
 
-BwdPlan plan_bwd(int B, int NH, int Dh, int num_cu, int bt_override, int k_override);
-hipError_t launch_rec_bwd(const BwdPlan &p, const BwdArgs &m, hipStream_t s);
+BwdPlan plan_bwd(int cell, int B, int NH, int Dh, int num_cu, int bt_override, int k_override);
+hipError_t launch_rec_bwd(int cell, const BwdPlan &p, const BwdArgs &m, hipStream_t s);
 hipError_t launch_hprev_bf16(const float *h0, const float *h_seq, uint16_t *hprev, long BH,
                              long total, hipStream_t s);
 hipError_t launch_db_reduce(const float *db_part, int nbt, int N, float *db, hipStream_t s);

@@ -1,6 +1,6 @@
-// rec_bwd.hip -- reverse-time recurrence of LSTM backpropagation through
-// time (the sequential part of the backward), plus the small helper kernels
-// of the backward pass.
+// rec_bwd.hip -- reverse-time recurrence of LSTM and GRU backpropagation
+// through time (the sequential part of the backward), plus the small helper
+// kernels of the backward pass.
 //
 // Backward of the recurrence A_t = Gx_t + h_{t-1} R (FlashRNN, arXiv
 // 2412.07752, abstract: traditional RNNs trained through their sequential
@@ -13,6 +13,15 @@
 //     dA_i = dc z i(1-i)    dA_z = dc i (1-z^2)     dA_f = dc c_{t-1} f(1-f)
 //     dc_carry = dc f       dh_carry = dA_t R^T   (per head, block-diagonal)
 // and after t = 0 the carries are dL/dh_0 and dL/dc_0.
+//
+// GRU (reset-after: A_r = Gx_r + S_r, A_z = Gx_z + S_z, A_n = Gx_n + r S_n
+// with S = h_{t-1} R, h_t = (1-u) n + u h_{t-1}), from Gx and S kept apart:
+//     dh   = dL/dh_t + dh_carry
+//     dA_n = dh (1-u)(1-n^2)    dA_z = dh (h_{t-1} - n) u(1-u)
+//     dA_r = dA_n S_n r(1-r)
+//     dGx  = (dA_r, dA_z, dA_n)          (-> dW, dx, db)
+//     dS   = (dA_r, dA_z, dA_n r)        (-> dR and the carry)
+//     dh_carry = dh u + dS R^T.
 //
 // Mapping (mirrors the forward kernels): a (head, batch tile) group of K
 // workgroups; workgroup `member` owns output units [member*U, (member+1)*U),
@@ -34,9 +43,10 @@ namespace rnn355 {
 
 namespace {
 
-template <int KCW, int R4>
-__global__ __launch_bounds__(512) void rec_bwd_lstm_kernel(BwdArgs m) {
-    constexpr int G = 4;
+template <int CELL, int KCW, int R4>
+__global__ __launch_bounds__(512) void rec_bwd_kernel(BwdArgs m) {
+    constexpr int G = CellTraits<CELL>::G;
+    constexpr bool LSTM = CELL == kLSTM;
     const int Dh = m.Dh, K = m.K, KS = m.KS, NB = m.NB;
     const int U = NB * 16, GD = G * Dh, H = m.NH * Dh, N = m.NH * GD, ALD = GD + 8;
     const int T = m.T, B = m.B;
@@ -73,7 +83,7 @@ __global__ __launch_bounds__(512) void rec_bwd_lstm_kernel(BwdArgs m) {
     // per-lane state of the gate waves: row slots r -> batch row 4*lg + r
     bool rv[R4];
     unsigned oo[R4];
-    float dhc[R4], dcc[R4], dbs[R4][G];
+    float dhc[R4], dcc[R4], dir[R4], dbs[R4][G];
     const long o_tile = (long)b0 * H + n * Dh;
     const long a_tile = (long)b0 * N + n * GD;
 #pragma unroll
@@ -82,12 +92,14 @@ __global__ __launch_bounds__(512) void rec_bwd_lstm_kernel(BwdArgs m) {
         rv[r] = gate_wave && b < rows;
         oo[r] = (unsigned)(b * H + j);
         dhc[r] = (rv[r] && m.dhT) ? m.dhT[o_tile + oo[r]] : 0.f;
-        dcc[r] = (rv[r] && m.dcT) ? m.dcT[o_tile + oo[r]] : 0.f;
+        dcc[r] = (LSTM && rv[r] && m.dcT) ? m.dcT[o_tile + oo[r]] : 0.f;
+        dir[r] = 0.f;
 #pragma unroll
         for (int g = 0; g < G; ++g) dbs[r][g] = 0.f;
     }
-    // streamed per step and row slot: pre-activations, c_t, c_{t-1}, dL/dh_t
-    float pa[R4][G], ct[R4], cp[R4], up[R4];
+    // streamed per step and row slot.  LSTM: pre-activations, c_t, c_{t-1},
+    // dL/dh_t.  GRU: Gx (pa), S (sv), h_{t-1} (cp), dL/dh_t.
+    float pa[R4][G], sv[R4][G], ct[R4], cp[R4], up[R4];
     auto load_step = [&](int t) {
 #pragma unroll
         for (int r = 0; r < R4; ++r) {
@@ -96,9 +108,16 @@ __global__ __launch_bounds__(512) void rec_bwd_lstm_kernel(BwdArgs m) {
 #pragma unroll
                 for (int g = 0; g < G; ++g) pa[r][g] = m.A[ao + g * Dh];
                 const long oo_t = o_tile + (long)t * B * H + oo[r];
-                ct[r] = m.c_seq[oo_t];
-                cp[r] = t > 0 ? m.c_seq[oo_t - (long)B * H]
-                              : (m.c0 ? m.c0[o_tile + oo[r]] : 0.f);
+                if constexpr (LSTM) {
+                    ct[r] = m.c_seq[oo_t];
+                    cp[r] = t > 0 ? m.c_seq[oo_t - (long)B * H]
+                                  : (m.c0 ? m.c0[o_tile + oo[r]] : 0.f);
+                } else {
+#pragma unroll
+                    for (int g = 0; g < G; ++g) sv[r][g] = m.S[ao + g * Dh];
+                    cp[r] = t > 0 ? m.h_seq[oo_t - (long)B * H]
+                                  : (m.h0 ? m.h0[o_tile + oo[r]] : 0.f);
+                }
                 up[r] = m.dh_seq[oo_t];
             }
         }
@@ -125,31 +144,54 @@ __global__ __launch_bounds__(512) void rec_bwd_lstm_kernel(BwdArgs m) {
         if (gate_wave) {
 #pragma unroll
             for (int r = 0; r < R4; ++r) {
-                const float ig = sigmoid_f(pa[r][0]), fg = sigmoid_f(pa[r][1]);
-                const float zg = tanh_f(pa[r][2]), og = sigmoid_f(pa[r][3]);
-                const float tc = tanh_f(ct[r]);
-                const float dh = up[r] + dhc[r];
-                const float dc = fmaf(dh * og, 1.0f - tc * tc, dcc[r]);
-                float d[G];
-                d[0] = dc * zg * ig * (1.0f - ig);
-                d[1] = dc * cp[r] * fg * (1.0f - fg);
-                d[2] = dc * ig * (1.0f - zg * zg);
-                d[3] = dh * tc * og * (1.0f - og);
-                dcc[r] = dc * fg;
-                uint16_t db16[G];
+                // d: gradients of the gate inputs Gx; e: of the recurrent
+                // sums S (the same for the LSTM), exchanged for the carry
+                float d[G], e[G];
+                if constexpr (LSTM) {
+                    const float ig = sigmoid_f(pa[r][0]), fg = sigmoid_f(pa[r][1]);
+                    const float zg = tanh_f(pa[r][2]), og = sigmoid_f(pa[r][3]);
+                    const float tc = tanh_f(ct[r]);
+                    const float dh = up[r] + dhc[r];
+                    const float dc = fmaf(dh * og, 1.0f - tc * tc, dcc[r]);
+                    d[0] = dc * zg * ig * (1.0f - ig);
+                    d[1] = dc * cp[r] * fg * (1.0f - fg);
+                    d[2] = dc * ig * (1.0f - zg * zg);
+                    d[3] = dh * tc * og * (1.0f - og);
+                    dcc[r] = dc * fg;
+#pragma unroll
+                    for (int g = 0; g < G; ++g) e[g] = d[g];
+                } else {
+                    const float rg = sigmoid_f(pa[r][0] + sv[r][0]);
+                    const float ug = sigmoid_f(pa[r][1] + sv[r][1]);
+                    const float ng = tanh_f(fmaf(rg, sv[r][2], pa[r][2]));
+                    const float dh = up[r] + dhc[r];
+                    d[2] = dh * (1.0f - ug) * (1.0f - ng * ng);
+                    d[1] = dh * (cp[r] - ng) * ug * (1.0f - ug);
+                    d[0] = d[2] * sv[r][2] * rg * (1.0f - rg);
+                    e[0] = d[0];
+                    e[1] = d[1];
+                    e[2] = d[2] * rg;
+                    dir[r] = dh * ug;
+                }
+                uint16_t db16[G], de16[G];
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
                     dbs[r][g] += rv[r] ? d[g] : 0.f;
                     db16[g] = f32_to_bf16_rne(d[g]);
+                    de16[g] = LSTM ? db16[g] : f32_to_bf16_rne(e[g]);
                 }
                 if (rv[r]) {
-                    uint16_t *dst = m.dA + a_tile + (long)t * B * N + (long)(4 * lg + r) * N + j;
+                    const long o = a_tile + (long)t * B * N + (long)(4 * lg + r) * N + j;
 #pragma unroll
-                    for (int g = 0; g < G; ++g) dst[g * Dh] = db16[g];
+                    for (int g = 0; g < G; ++g) m.dA[o + g * Dh] = db16[g];
+                    if constexpr (!LSTM) {
+#pragma unroll
+                        for (int g = 0; g < G; ++g) m.dS[o + g * Dh] = de16[g];
+                    }
                 }
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
-                    const unsigned v = db16[g];
+                    const unsigned v = de16[g];
                     const unsigned nb = (unsigned)__shfl_xor((int)v, 1);
                     if (rv[r]) {
                         const int row = 4 * lg + r, col = g * Dh + j;
@@ -203,9 +245,18 @@ __global__ __launch_bounds__(512) void rec_bwd_lstm_kernel(BwdArgs m) {
 #pragma unroll
             for (int c = 0; c < KCW; ++c) af[c] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
         }
+        // the GRU's direct term dh u enters as the chain's initial value, so no
+        // vector instruction reads the MFMA result right after the chain (a
+        // read across the branch below came without the wait states an MFMA
+        // result needs and saw stale values)
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (!LSTM) {
+#pragma unroll
+            for (int r = 0; r < R4; ++r) acc[r] = dir[r];
+        }
 #pragma unroll
         for (int c = 0; c < KCW; ++c) acc = mfma_16x16x32_bf16(af[c], rf[c], acc);
+        mfma_chain_end();
         if (KS > 1) {
             if (!gate_wave) {
                 float *dst = red + ((long)(ks - 1) * NB + blk) * 256;
@@ -230,7 +281,7 @@ __global__ __launch_bounds__(512) void rec_bwd_lstm_kernel(BwdArgs m) {
         for (int r = 0; r < R4; ++r) {
             if (rv[r]) {
                 m.dh0[o_tile + oo[r]] = dhc[r];
-                m.dc0[o_tile + oo[r]] = dcc[r];
+                if (LSTM) m.dc0[o_tile + oo[r]] = dcc[r];
             }
         }
         // db partial of this batch tile: the lane's 4 gate sums over its rows
@@ -259,20 +310,32 @@ __global__ __launch_bounds__(512) void rec_bwd_lstm_kernel(BwdArgs m) {
     }
 }
 
-template <int KCW, int R4>
+template <int CELL, int KCW, int R4>
 hipError_t launch_bwd_t(const BwdPlan &p, BwdArgs m, hipStream_t s) {
     void *args[] = {&m};
     return hipLaunchCooperativeKernel(
-        reinterpret_cast<const void *>(&rec_bwd_lstm_kernel<KCW, R4>), dim3(p.grid),
+        reinterpret_cast<const void *>(&rec_bwd_kernel<CELL, KCW, R4>), dim3(p.grid),
         dim3(p.threads), args, p.lds, s);
 }
 
-template <int KCW>
+template <int CELL, int KCW>
 hipError_t launch_bwd_rows(const BwdPlan &p, const BwdArgs &m, hipStream_t s) {
     switch (p.r4) {
-        case 1: return launch_bwd_t<KCW, 1>(p, m, s);
-        case 2: return launch_bwd_t<KCW, 2>(p, m, s);
-        default: return launch_bwd_t<KCW, 4>(p, m, s);
+        case 1: return launch_bwd_t<CELL, KCW, 1>(p, m, s);
+        case 2: return launch_bwd_t<CELL, KCW, 2>(p, m, s);
+        default: return launch_bwd_t<CELL, KCW, 4>(p, m, s);
+    }
+}
+
+template <int CELL>
+hipError_t launch_bwd_cell(const BwdPlan &p, const BwdArgs &m, hipStream_t s) {
+    switch (p.kcw) {
+        case 16: return launch_bwd_rows<CELL, 16>(p, m, s);
+        case 12: return launch_bwd_rows<CELL, 12>(p, m, s);
+        case 8: return launch_bwd_rows<CELL, 8>(p, m, s);
+        case 6: return launch_bwd_rows<CELL, 6>(p, m, s);
+        case 4: return launch_bwd_rows<CELL, 4>(p, m, s);
+        default: return hipErrorInvalidValue;
     }
 }
 
@@ -303,14 +366,22 @@ __global__ void db_reduce_kernel(const float *db_part, int nbt, int N, float *db
 
 }  // namespace
 
-BwdPlan plan_bwd(int B, int NH, int Dh, int num_cu, int bt_override, int k_override) {
+BwdPlan plan_bwd(int cell, int B, int NH, int Dh, int num_cu, int bt_override, int k_override) {
     BwdPlan p{};
-    const int G = 4;
-    if (Dh % 16 != 0 || (G * Dh) % 128 != 0) return p;
+    const int G = cell == kLSTM ? 4 : 3;
+    if (Dh % 16 != 0 || (G * Dh) % 32 != 0) return p;
     const int KC = G * Dh / 32;  // reduction chunks of 32 gate columns
-    // at most 16 chunks per wave: its R^T fragments and the A fragments of
-    // one step then take 64 VGPRs each
-    p.kcw = KC % 16 == 0 ? 16 : KC % 8 == 0 ? 8 : 4;
+    // at most 16 chunks per wave (its R^T fragments and the A fragments of
+    // one step then take 64 VGPRs each): the largest of 16, 12, 8, 6, 4
+    // that divides the chunk count
+    p.kcw = 0;
+    for (const int c : {16, 12, 8, 6, 4}) {
+        if (KC % c == 0) {
+            p.kcw = c;
+            break;
+        }
+    }
+    if (p.kcw == 0) return p;
     p.ks = KC / p.kcw;
     const int nb_max = 8 / p.ks;
     if (nb_max < 1) return p;
@@ -342,22 +413,19 @@ BwdPlan plan_bwd(int B, int NH, int Dh, int num_cu, int bt_override, int k_overr
     return p;
 }
 
-hipError_t launch_rec_bwd(const BwdPlan &p, const BwdArgs &m, hipStream_t s) {
+hipError_t launch_rec_bwd(int cell, const BwdPlan &p, const BwdArgs &m, hipStream_t s) {
+    const int G = cell == kLSTM ? 4 : 3;
     hipLaunchKernelGGL(clear_words_bwd_kernel, dim3(1), dim3(64), 0, s, m.flag, 1L);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (p.K > 1) {
-        const long words = 2L * p.groups * 2 * p.BT * (4 * m.Dh / 2);
+        const long words = 2L * p.groups * 2 * p.BT * (G * m.Dh / 2);
         hipLaunchKernelGGL(clear_words_bwd_kernel, dim3(64), dim3(256), 0, s,
                            reinterpret_cast<unsigned *>(m.xg), words);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    switch (p.kcw) {
-        case 16: return launch_bwd_rows<16>(p, m, s);
-        case 8: return launch_bwd_rows<8>(p, m, s);
-        default: return launch_bwd_rows<4>(p, m, s);
-    }
+    return cell == kLSTM ? launch_bwd_cell<kLSTM>(p, m, s) : launch_bwd_cell<kGRU>(p, m, s);
 }
 
 hipError_t launch_hprev_bf16(const float *h0, const float *h_seq, uint16_t *hprev, long BH,

@@ -285,6 +285,10 @@ __device__ __forceinline__ void rec_fwd_mfma_body(const RecArgs &a, const int bl
             for (int c = 0; c < KC; ++c)
 #pragma unroll
                 for (int g = 0; g < G; ++g) acc[g] = mfma_16x16x32_bf16(af[c], rf[g][c], acc[g]);
+            // steps are unrolled: only a group's first step branches right
+            // after the chain (the HBM traffic of the group), so only it needs
+            // the pinned wait states
+            if (s == 0) mfma_chain_end();
             if (s == 0) {
                 if (tg > 0) store_group(tg - PD);
                 wait_ready(tg + 2 * PD);

@@ -164,6 +164,7 @@ __global__ __launch_bounds__(512) void rec_fwd_mc_kernel(McArgs m) {
         for (int c = 0; c < KCW; ++c)
 #pragma unroll
             for (int g = 0; g < G; ++g) acc[g] = mfma_16x16x32_bf16(af[c], rf[g][c], acc[g]);
+        mfma_chain_end();
 
         if (KS > 1) {
             // partial sums of the other k-ranges -> the ks = 0 wave of the block

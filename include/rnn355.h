@@ -187,7 +187,10 @@ rnn_status rnn_fwd_gru(const rnn_dims *d, rnn_dtype dt,
  *   L = sum_t dh_seq[t] . h_t + dhT . h_T + dcT . c_T
  * given the forward's h_seq and c_seq (from rnn_fwd_lstm on the same inputs).
  * dhT, dcT may be NULL (= 0).  Writes dx, dW, dR, db, dh0, dc0 (all required).
- * Gate pre-activations are recomputed from x, W, b, h_seq and R.
+ * Gate pre-activations are recomputed from x, W, b, h_seq and R.  (FlashRNN
+ * card, abstract: the LSTM trained through its sequential recurrence; the
+ * backward is the reverse-time recurrence of the same cell, with the same
+ * block-diagonal R, held resident as R^T.)
  */
 rnn_status rnn_bwd_lstm(const rnn_dims *d, rnn_dtype dt,
                         const void *x, const void *W, const void *R,
@@ -197,6 +200,29 @@ rnn_status rnn_bwd_lstm(const rnn_dims *d, rnn_dtype dt,
                         float *dx, float *dW, float *dR, float *db,
                         float *dh0, float *dc0,
                         void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Multi-head GRU (reset-after) backpropagation through time (FlashRNN card,
+ * abstract: GRU among the cells the kernels cover) for the loss
+ *   L = sum_t dh_seq[t] . h_t + dhT . h_T
+ * given the forward's h_seq (from rnn_fwd_gru on the same inputs).  dhT may
+ * be NULL (= 0).  Writes dx, dW, dR, db, dh0 (all required).  The gate
+ * inputs Gx = x W + b and the recurrent sums S = h_{t-1} R are recomputed
+ * apart (the candidate gate scales S_n by r); per step t = T-1 .. 0, with
+ * dh = dh_seq[t] + the carry:
+ *   dA_n = dh (1-u)(1-n^2),  dA_z = dh (h_{t-1} - n) u(1-u),
+ *   dA_r = dA_n S_n r(1-r),
+ *   dGx = (dA_r, dA_z, dA_n) -> dW, dx, db;  dS = (dA_r, dA_z, dA_n r) -> dR,
+ *   carry = dh u + dS R^T (block-diagonal R).
+ * bf16 only (f32 returns RNN_ERR_UNSUPPORTED); Dh % 16 == 0 and 3*Dh % 32
+ * == 0.  Same workspace and stream rules as rnn_bwd_lstm.
+ */
+rnn_status rnn_bwd_gru(const rnn_dims *d, rnn_dtype dt,
+                       const void *x, const void *W, const void *R,
+                       const float *b, const float *h0, const float *h_seq,
+                       const float *dh_seq, const float *dhT,
+                       float *dx, float *dW, float *dR, float *db, float *dh0,
+                       void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Synchronises `stream`, then reports whether a kernel of the last call that

@@ -119,6 +119,23 @@ def test_backward_rejects_unsupported_and_invalid_before_launch():
                             None) == g.RNN_ERR_WORKSPACE
     need = g.workspace_size(g.OP_BWD_LSTM, d, g.RNN_BF16)
     assert need > 8 * 2 * (2 * 4 * 64) * 4  # holds at least the recomputed pre-activations
+    # GRU: 13 pointers (no c0, c_seq, dcT, dc0)
+    gp = [_p(FAKE + 256 * i) for i in range(13)]
+    assert lib.rnn_bwd_gru(ctypes.byref(d), g.RNN_F32, *gp, _p(FAKE), 1 << 30,
+                           None) == g.RNN_ERR_UNSUPPORTED
+    bad = list(gp)
+    bad[12] = None  # dh0
+    assert lib.rnn_bwd_gru(ctypes.byref(d), g.RNN_BF16, *bad, _p(FAKE), 1 << 30,
+                           None) == g.RNN_ERR_INVALID_ARG
+    bad = list(gp)
+    bad[5] = _p(FAKE + 4)  # misaligned h_seq
+    assert lib.rnn_bwd_gru(ctypes.byref(d), g.RNN_BF16, *bad, _p(FAKE), 1 << 30,
+                           None) == g.RNN_ERR_INVALID_ARG
+    assert lib.rnn_bwd_gru(ctypes.byref(d), g.RNN_BF16, *gp, _p(FAKE), 64,
+                           None) == g.RNN_ERR_WORKSPACE
+    # the GRU workspace keeps Gx and S apart, so it is larger per gate column
+    gneed = g.workspace_size(g.OP_BWD_GRU, d, g.RNN_BF16)
+    assert gneed > 8 * 2 * (2 * 3 * 64) * 4 * 2
 
 
 def test_plans_of_the_workloads(monkeypatch):

@@ -1,4 +1,4 @@
-"""GPU parity of the LSTM backward (BPTT) against the oracle.
+"""GPU parity of the LSTM and GRU backward (BPTT) against the oracle.
 
 The GPU backward runs on the GPU forward's h_seq / c_seq; the oracle runs
 its own forward.  Bar: normwise 2e-2 on every gradient (bf16 operands, f32
@@ -121,4 +121,82 @@ def test_backward_workload_full_size_sampled():
     dx_ref = oracle.param_grad_entries("dx", np.stack([tt * d.B + b3, kx], 1), *args, **kw)
     e = nerr(got["dx"][tt, b3, kx], dx_ref)
     print("  dx entries (row %d) nerr=%.3e" % (b3, e), flush=True)
+    assert e <= TOL
+
+
+def gpu_bwd_gru(c, final=False):
+    x, W, R, b = dev(c, "x"), dev(c, "W"), dev(c, "R"), dev(c, "b")
+    h0 = dev(c, "h0")
+    h_seq, _ = g.gru_fwd(x, W, R, b, h0)
+    grads = g.gru_bwd(x, W, R, b, h0, h_seq, dev(c, "dH"), dev(c, "dhT") if final else None)
+    torch.cuda.synchronize()
+    return {k: host(v) for k, v in grads.items()}
+
+
+@pytest.mark.parametrize("Dh,B,bt,final", [
+    (64, 3, None, False),     # one workgroup per (head, row): 6 chunks per wave, dS through LDS
+    (64, 5, 2, True),         # two row slots, ragged, final-state gradient
+    (128, 2, None, True),     # 12 chunks per wave, one workgroup
+    (128, 5, 4, False),       # four row slots
+    (256, 3, None, True),     # two k-splits, four workgroups per head: dS as tagged words
+    (256, 5, 2, False),
+])
+def test_gru_backward_small(Dh, B, bt, final):
+    if bt is not None:
+        os.environ["RNN355_REC_BT"] = str(bt)
+    d = synth.Dims(T=17, B=B, Din=64, NH=2, Dh=Dh)
+    c = synth.make_case("gru", d, "bf16", 9500 + Dh + B,
+                        bias=synth.normal(9400 + Dh, d.NH * 3 * Dh, 0.25), h0_var=0.3,
+                        backward=True, final_grads=final)
+    got = gpu_bwd_gru(c, final)
+    ref = oracle.gru_bwd(c.f64("x"), c.f64("W"), c.f64("R"), c.f64("b"), c.f64("h0"),
+                         c.f64("dH"), c.f64("dhT") if final else None, NH=d.NH, Dh=d.Dh)
+    for k in ("dx", "dW", "dR", "db", "dh0"):
+        e = nerr(got[k], ref[k])
+        print("  %-4s nerr=%.3e" % (k, e), flush=True)
+        assert e <= TOL, (k, e)
+
+
+def test_gru_backward_bitwise_repeatable():
+    d = synth.Dims(T=13, B=3, Din=32, NH=2, Dh=256)
+    c = synth.make_case("gru", d, "bf16", 9600, h0_var=0.2, backward=True)
+    a, b = gpu_bwd_gru(c), gpu_bwd_gru(c)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_gru_backward_small_batch_workload_shape_sampled():
+    """GRU BPTT at the shape of the small-batch GRU workload (B=4, NH=12,
+    Dh=64, T=2048, Din=768; dL/dh_t ~ N(0,1) for all t).  The oracle
+    recomputes 4 whole chains (head 5 of every batch row); compared: dh0 of
+    those chains, db and dW / dR entries of head 5's columns, dx entries."""
+    w = synth.WORKLOADS["gru_mh_b4_nh12_dh64"]
+    d = w.dims
+    c = synth.make_case("gru", d, "bf16", 9000, h0_var=0.1, backward=True)
+    got = gpu_bwd_gru(c)
+    n5 = 5
+    mask = np.zeros((d.B, d.NH), bool)
+    mask[:, n5] = True
+    ref = oracle.gru_bwd(c.f64("x"), c.f64("W"), c.f64("R"), c.f64("b"), c.f64("h0"),
+                         c.f64("dH"), NH=d.NH, Dh=d.Dh, chain_mask=mask, grads=())
+    GD = 3 * d.Dh
+    sl = slice(n5 * d.Dh, (n5 + 1) * d.Dh)
+    e = nerr(got["dh0"][:, sl], ref["dh0"][:, sl])
+    print("  dh0 (head %d) nerr=%.3e" % (n5, e), flush=True)
+    assert e <= TOL
+    args = (c.f64("x"), c.f64("W"), c.f64("h0"), ref["h_seq"], ref["dGx"], ref["dS"])
+    kw = dict(NH=d.NH, Dh=d.Dh, G=3)
+    cols = n5 * GD + np.arange(GD)
+    e = nerr(got["db"][cols], oracle.param_grad_entries("db", cols[:, None], *args, **kw))
+    print("  db nerr=%.3e" % e, flush=True)
+    assert e <= TOL
+    rng = np.random.default_rng(7)
+    kk, cc = rng.integers(0, d.Din, 256), n5 * GD + rng.integers(0, GD, 256)
+    e = nerr(got["dW"][kk, cc], oracle.param_grad_entries("dW", np.stack([kk, cc], 1), *args, **kw))
+    print("  dW entries nerr=%.3e" % e, flush=True)
+    assert e <= TOL
+    ii, jj = rng.integers(0, d.Dh, 256), rng.integers(0, GD, 256)
+    e = nerr(got["dR"][n5, ii, jj],
+             oracle.param_grad_entries("dR", np.stack([np.full(256, n5), ii, jj], 1), *args, **kw))
+    print("  dR entries nerr=%.3e" % e, flush=True)
     assert e <= TOL
