@@ -205,6 +205,9 @@ __global__ __launch_bounds__(512) void rec_bwd_kernel(BwdArgs m) {
                 }
             }
         }
+        // next step's streamed inputs, issued as soon as this step's cell
+        // update has used them: they land during the exchange and the MFMAs
+        if (gate_wave && t > 0) load_step(t - 1);
         // ---- dA_t of the whole head row into LDS
         if (K > 1) {
             const int words = rows * wpr;
@@ -234,8 +237,6 @@ __global__ __launch_bounds__(512) void rec_bwd_kernel(BwdArgs m) {
         }
         __syncthreads();
         if (s_abort) break;
-        // next step's streamed inputs, issued now so they land during the MFMAs
-        if (gate_wave && t > 0) load_step(t - 1);
         // ---- dh_carry = dA_t R^T for this wave's gate-column range
         if (lr < rows) {
 #pragma unroll
