@@ -66,6 +66,8 @@ def rec_kernel_name(w: synth.Workload, plan: str) -> str:
     it (template arguments: cell, Dh, row slots, steps per group, waits)."""
     if "multi_cu" in plan:
         return "rec_fwd_mc_kernel"
+    if "split_R" in plan:
+        return "rec_fwd_wide_kernel<%d>" % (0 if w.cell == "lstm" else 1)
     if "mfma" not in plan:
         return "rec_fwd_simple_kernel"
     upt = int(plan.split("units_per_thread=")[1].split()[0])

@@ -63,6 +63,13 @@ size_t wt_bytes(const rnn_dims *d, int G) {
     return align_up(sizeof(uint16_t) * (size_t)d->Din * d->NH * G * d->Dh);
 }
 
+// R staged transposed per head ([NH][G*Dh][Dh] bf16) for the Dh = 256
+// one-CU recurrence; sized for every bf16 shape with Dh = 256.
+size_t rt_fwd_bytes(const rnn_dims *d, rnn_dtype dt, int G) {
+    if (dt != RNN_BF16 || d->Dh != 256) return 0;
+    return align_up(sizeof(uint16_t) * (size_t)d->NH * G * d->Dh * d->Dh);
+}
+
 // Backward workspace after the header: the exchange slots of the sweep, the
 // recomputed pre-activations A (LSTM: Gx + h_{t-1} R; GRU: Gx alone) and the
 // GRU's recurrent sums S (f32), the gate-input gradients dA and the GRU's
@@ -124,6 +131,12 @@ int pipeline_override() {
     return !e || !e[0] ? -1 : e[0] == '0' ? 0 : 1;
 }
 int k_override() { return env_int("RNN355_REC_K"); }
+// RNN355_REC_WIDE=0 serves Dh = 256 with the multi-CU kernel instead of the
+// one-CU kernel with split R.
+bool wide_enabled() {
+    const char *e = getenv("RNN355_REC_WIDE");
+    return !(e && e[0] == '0');
+}
 // Polls of a multi-CU step wait before it is declared lost (~4 s by default;
 // tests lower it to force the time-out path).
 unsigned spin_limit() {
@@ -132,12 +145,15 @@ unsigned spin_limit() {
 }
 
 // Which recurrent kernel serves a shape: the one-CU MFMA kernel (bf16, Dh in
-// {32, 64, 128}), the multi-CU kernel (bf16, Dh >= 256, Dh % 128 == 0), or
-// the LDS kernel (f32, other shapes whose R fits 64 KiB of LDS).
+// {32, 64, 128}), the one-CU kernel with R split over registers and LDS
+// (bf16, Dh = 256), the multi-CU kernel (bf16, Dh >= 256, Dh % 128 == 0),
+// or the LDS kernel (f32, other shapes whose R fits 64 KiB of LDS).
 struct Choice {
     int cell;
     RecPlan rec;
+    WidePlan wide;
     McPlan mc;
+    bool use_wide;
     bool use_mc;
     bool ok;
 };
@@ -150,6 +166,14 @@ Choice choose(int cell, const rnn_dims *d, rnn_dtype dt, int num_cu) {
     if (c.rec.kind == kRecMfma) {
         c.ok = true;
         return c;
+    }
+    if (bf16 && wide_enabled()) {
+        c.wide = plan_wide(cell, d->B, d->NH, d->Dh, bf16);
+        if (c.wide.ok) {
+            c.use_wide = true;
+            c.ok = true;
+            return c;
+        }
     }
     if (bf16) {
         c.mc = plan_mc(cell, d->B, d->NH, d->Dh, num_cu, bt_override(), k_override());
@@ -207,9 +231,10 @@ rnn_status input_proj(int M, int K, int N, rnn_dtype dt, const void *x, const vo
     return e == hipSuccess ? RNN_OK : RNN_ERR_HIP;
 }
 
+// rt: workspace region for R^T (rt_fwd_bytes), used by the Dh = 256 kernel.
 rnn_status rec_fwd(int cell, const rnn_dims *d, rnn_dtype dt, const float *gx, const void *R,
                    const float *h0, const float *c0, float *h_seq, float *c_seq, float *hT,
-                   float *cT, void *ws, hipStream_t s) {
+                   float *cT, void *ws, uint16_t *rt, hipStream_t s) {
     const Choice ch = choose(cell, d, dt, device_cus());
     if (!ch.ok) return RNN_ERR_UNSUPPORTED;
     RecArgs a{};
@@ -219,7 +244,15 @@ rnn_status rec_fwd(int cell, const rnn_dims *d, rnn_dtype dt, const float *gx, c
     a.Rf = dt == RNN_F32 ? (const float *)R : nullptr;
     a.h0 = h0; a.c0 = c0; a.h_seq = h_seq; a.c_seq = c_seq; a.hT = hT; a.cT = cT;
     hipError_t e;
-    if (ch.use_mc) {
+    if (ch.use_wide) {
+        // R^T per head; the same launch clears the status words
+        const int G = gates_of_cell(cell);
+        e = launch_transpose_bf16((const uint16_t *)R, rt, d->Dh, G * d->Dh, d->NH, s,
+                                  (unsigned *)ws, 64);
+        if (e != hipSuccess) return RNN_ERR_HIP;
+        a.BT = 1;
+        e = launch_rec_wide(cell, ch.wide, a, rt, s);
+    } else if (ch.use_mc) {
         a.BT = ch.mc.BT;
         McArgs m{};
         m.r = a;
@@ -247,7 +280,7 @@ bool rec_supported(int cell, const rnn_dims *d, rnn_dtype dt) {
 // running the two side by side.
 bool pipelined(const Choice &ch, const rnn_dims *d, rnn_dtype dt, int cus) {
     const int force = pipeline_override();
-    if (dt != RNN_BF16 || ch.use_mc || ch.rec.kind != kRecMfma || d->Dh != 128 ||
+    if (dt != RNN_BF16 || ch.use_mc || ch.use_wide || ch.rec.kind != kRecMfma || d->Dh != 128 ||
         !gemm_dma_ok(d->Din) || 2 * ch.rec.grid > cus || force == 0 || gx_panels(d) < 2)
         return false;
     if (force == 1) return true;
@@ -307,7 +340,8 @@ rnn_status forward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, con
     }
     rnn_status st = input_proj(M, d->Din, N, dt, x, W, b, gx, (uint32_t *)ws, s, nullptr, wt);
     if (st != RNN_OK) return st;
-    return rec_fwd(cell, d, dt, gx, R, h0, c0, h_seq, c_seq, hT, cT, ws, s);
+    uint16_t *rt = (uint16_t *)((char *)wt + wt_bytes(d, G));
+    return rec_fwd(cell, d, dt, gx, R, h0, c0, h_seq, c_seq, hT, cT, ws, rt, s);
 }
 
 // Backpropagation through time (pointers validated by the entry points).
@@ -435,10 +469,11 @@ size_t rnn_workspace_size(rnn_op op, const rnn_dims *d, rnn_dtype dt) {
     switch (op) {
         case RNN_OP_FWD_LSTM:
         case RNN_OP_FWD_GRU:
-            return kHeader + xchg_bytes(d) + gx_bytes(d, G) + ready_bytes(d) + wt_bytes(d, G);
+            return kHeader + xchg_bytes(d) + gx_bytes(d, G) + ready_bytes(d) + wt_bytes(d, G) +
+                   rt_fwd_bytes(d, dt, G);
         case RNN_OP_REC_LSTM:
         case RNN_OP_REC_GRU:
-            return kHeader + xchg_bytes(d);
+            return kHeader + xchg_bytes(d) + rt_fwd_bytes(d, dt, G);
         case RNN_OP_BWD_LSTM:
         case RNN_OP_BWD_GRU:
             return kHeader + bwd_layout(d, G).total;
@@ -460,7 +495,13 @@ rnn_status rnn_plan_describe(rnn_op op, const rnn_dims *d, rnn_dtype dt, char *b
     const bool fwd = op == RNN_OP_FWD_LSTM || op == RNN_OP_FWD_GRU;
     const char *proj = !fwd ? "" : pipelined(ch, d, dt, device_cus()) ? " input_proj=pipelined"
                                                                         : " input_proj=serial";
-    if (ch.use_mc) {
+    if (ch.use_wide) {
+        const WidePlan &p = ch.wide;
+        snprintf(buf, len,
+                 "rec_kernel=mfma_split_R rows_per_wg=1 wg=%d threads=%d wg_per_head_row_tile=1 "
+                 "r_lds_bytes=%zu%s",
+                 p.grid, p.threads, p.lds, proj);
+    } else if (ch.use_mc) {
         const McPlan &p = ch.mc;
         snprintf(buf, len,
                  "rec_kernel=mfma_multi_cu rows_per_wg=%d wg=%d threads=%d wg_per_head_row_tile=%d "
@@ -511,7 +552,8 @@ rnn_status rnn_rec_lstm(const rnn_dims *d, rnn_dtype dt, const float *gx, const 
         if (!aligned16(p)) return RNN_ERR_INVALID_ARG;
     if (!rec_supported(kLSTM, d, dt)) return RNN_ERR_UNSUPPORTED;
     if (!ws || ws_bytes < rnn_workspace_size(RNN_OP_REC_LSTM, d, dt)) return RNN_ERR_WORKSPACE;
-    return rec_fwd(kLSTM, d, dt, gx, R, h0, c0, h_seq, c_seq, hT, cT, ws, stream);
+    uint16_t *rt = (uint16_t *)((char *)ws + kHeader + xchg_bytes(d));
+    return rec_fwd(kLSTM, d, dt, gx, R, h0, c0, h_seq, c_seq, hT, cT, ws, rt, stream);
 }
 
 rnn_status rnn_rec_gru(const rnn_dims *d, rnn_dtype dt, const float *gx, const void *R,
@@ -523,7 +565,8 @@ rnn_status rnn_rec_gru(const rnn_dims *d, rnn_dtype dt, const float *gx, const v
         if (!aligned16(p)) return RNN_ERR_INVALID_ARG;
     if (!rec_supported(kGRU, d, dt)) return RNN_ERR_UNSUPPORTED;
     if (!ws || ws_bytes < rnn_workspace_size(RNN_OP_REC_GRU, d, dt)) return RNN_ERR_WORKSPACE;
-    return rec_fwd(kGRU, d, dt, gx, R, h0, nullptr, h_seq, nullptr, hT, nullptr, ws, stream);
+    uint16_t *rt = (uint16_t *)((char *)ws + kHeader + xchg_bytes(d));
+    return rec_fwd(kGRU, d, dt, gx, R, h0, nullptr, h_seq, nullptr, hT, nullptr, ws, rt, stream);
 }
 
 rnn_status rnn_fwd_lstm(const rnn_dims *d, rnn_dtype dt, const void *x, const void *W,

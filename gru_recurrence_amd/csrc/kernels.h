@@ -115,6 +115,19 @@ hipError_t launch_rec_fwd(int cell, const RecPlan &p, const RecArgs &a, bool bf1
 hipError_t launch_fwd_fused(int cell, const RecPlan &p, const RecArgs &a, const GemmArgs &g,
                             int n_gemm, hipStream_t s);
 
+// Forward recurrence for Dh = 256 on one compute unit per (head, batch row),
+// R split over AGPRs, VGPRs and LDS (rec_wide.hip).  Rt holds R transposed
+// per head, [NH][G*Dh][Dh] bf16.
+struct WidePlan {
+    int ok;
+    int grid;     // NH * B workgroups (one batch row each)
+    int threads;  // 256: one wave per SIMD
+    size_t lds;   // dynamic LDS bytes (R chunks read every step)
+};
+WidePlan plan_wide(int cell, int B, int NH, int Dh, bool bf16);
+hipError_t launch_rec_wide(int cell, const WidePlan &p, const RecArgs &a, const uint16_t *Rt,
+                           hipStream_t s);
+
 // Multi-CU forward recurrence (rec_mc.hip).
 struct McPlan {
     int ok;

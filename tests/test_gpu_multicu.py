@@ -1,6 +1,8 @@
 """GPU parity of the multi-CU forward recurrence (heads of Dh >= 256 split
 over several workgroups that swap h_t through global memory every step)
-against the oracle, plus its time-out path forced from the host."""
+against the oracle, plus its time-out path forced from the host.  At Dh =
+256 the plan prefers the one-CU kernel with split R; RNN355_REC_WIDE=0
+selects the multi-CU kernel there."""
 import os
 
 import numpy as np
@@ -20,8 +22,9 @@ TOL_BF16 = 2e-2
 
 @pytest.fixture(autouse=True)
 def _clean_env():
-    keys = ("RNN355_REC_BT", "RNN355_REC_K", "RNN355_SPIN_LIMIT")
+    keys = ("RNN355_REC_BT", "RNN355_REC_K", "RNN355_SPIN_LIMIT", "RNN355_REC_WIDE")
     old = {k: os.environ.pop(k, None) for k in keys}
+    os.environ["RNN355_REC_WIDE"] = "0"
     yield
     for k in keys:
         os.environ.pop(k, None)
@@ -118,8 +121,12 @@ def _mask(B, NH, chains):
 @pytest.mark.parametrize("name,chains", [
     ("lstm_1h_b16_dh768", [(0, 0), (9, 0)]),
     ("lstm_fwdbwd_b16_nh4_dh256", [(0, 0), (5, 2), (15, 3)]),
+    ("lstm_fwdbwd_b16_nh4_dh256/split_R", [(0, 0), (6, 1), (15, 3)]),
 ])
 def test_large_head_workloads_full_size_sampled_chains(name, chains):
+    if name.endswith("/split_R"):
+        name = name.split("/")[0]
+        os.environ.pop("RNN355_REC_WIDE")
     w = synth.WORKLOADS[name]
     c = synth.workload_case(w)
     print("  plan:", plan(c), flush=True)
