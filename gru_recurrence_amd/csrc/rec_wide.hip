@@ -10,37 +10,37 @@
 // for the GRU): as large as the whole register file of a compute unit
 // (4 SIMDs x 128 KiB).  Splitting the head over several compute units costs
 // a cross-unit exchange of h_t at every step (about a microsecond through
-// the device-coherent memory side); here it stays on one unit instead:
-//   * 4 waves, one per SIMD (so each wave may hold 512 registers); wave w
-//     owns hidden units [64w, 64w+64) = 4 blocks of 16 units, with all G
-//     gate columns of each;
-//   * the B fragments of v_mfma_f32_16x16x32_bf16 (k-chunks of 32) sit in
-//     the accumulation registers (AGPRs: chunks 0..3 of the LSTM, 0..4 of
-//     the GRU), in vector registers (LSTM 4..5, GRU 5..7), and the LSTM's
-//     chunks 6..7 in LDS (128 KiB), read again at every step;
-//   * one batch row per workgroup: the MFMA A operand holds h_{t-1} in row
-//     0 only, the gate sums of a 16-unit block come out in row 0 of G
-//     accumulator tiles, and the cell update runs as in the one-CU kernel
-//     (cross-row swaps put the G gates of a unit in the 4 rows of one
-//     register, one exp + rcp pass activates them all).  The other rows of
-//     the A operand stay zero (MFMA rows are independent; the rows they
-//     produce are never read).
+// the device-coherent memory side); here it stays on one unit instead.
+//
+// One workgroup per (head, batch row), 4 waves, one per SIMD (so each wave
+// may hold 512 registers).  The reduction dimension is split over the waves:
+// wave w multiplies h_{t-1}[64w, 64w+64) (two k-chunks of 32) with the
+// matching 64 rows of R for ALL G*256 gate columns, i.e. NT = G*16 output
+// tiles of v_mfma_f32_16x16x32_bf16, 2*NT MFMAs per step.  Its 2*NT B
+// fragments sit 64 in the AGPRs, 32 in VGPRs and (LSTM) the last 32 in LDS,
+// read again at every step.  Per step:
+//   1. tile groups of 4: MFMAs, then row 0 of the 4 tiles (the only live
+//      batch row) packed into one register with cross-row swaps and written
+//      to LDS as this wave's partial gate sums;
+//   2. barrier; thread u sums the 4 waves' partials of unit u's G gates and
+//      runs the whole cell update of unit u lane-locally;
+//   3. barrier (the partial sums may be rewritten); the A operand of the
+//      next step: wave w's k range is exactly the units its own threads
+//      updated, so h_t goes through a per-wave LDS slot with no barrier.
 // The MFMAs are inline assembly so that their B operand can be an AGPR:
 // compiled from the builtin, every AGPR fragment was first copied to vector
 // registers (four moves per MFMA, which a single wave per SIMD cannot hide).
 // The compiler does not see these as MFMAs, so it inserts no wait states
-// for their results; every read of an accumulator goes through
-// `chain_end`, which carries the wait states of the MFMA-result hazard
-// (16, twice what the compiler keeps for this instruction).  Their source
-// operands come from memory loads (R fragments, h from LDS); each asm also
-// carries the wait states that a VALU write of a source would need.
+// for them: every read of an accumulator goes through `chain_end` (16 wait
+// states, twice what the compiler keeps for this instruction), and each
+// MFMA starts with the two wait states a VALU write of one of its sources
+// would need.  They are volatile, so they keep the order written here.
 //
-// HBM traffic per step: Gx_t (G*256 floats) read, h_t and c_t written, all
-// in coalesced 16- or 4-byte lane accesses.  Steps go in groups of PD: at
-// the start of group g the single wait on memory completes the Gx of group
-// g+1 (requested at the start of g-1), which goes into an LDS ring slot; the
-// Gx of group g+2 is requested into the same 8 registers; and the outputs
-// of group g-1, staged in LDS, are written back.
+// HBM traffic per step: Gx_t (G*256 floats) read, h_t and c_t written, by
+// thread u for unit u (coalesced).  Steps go in groups of PD: the Gx of the
+// next group is requested at the start of a group into registers, and the
+// outputs of the previous group (also kept in registers) are stored right
+// after the group's single wait on memory.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -54,265 +54,335 @@ namespace rnn355 {
 namespace {
 
 constexpr int kWideDh = 256;
+// global-memory float (address space 1): a pointer that went through an
+// empty asm is otherwise treated as generic (flat)
+typedef __attribute__((address_space(1))) float gfloat;
 constexpr int kWideWaves = 4;
 
 template <int CELL>
 struct WideCfg {
     static constexpr int G = CellTraits<CELL>::G;
-    static constexpr int KC = kWideDh / 32;            // k-chunks
-    static constexpr int KA = CELL == kLSTM ? 4 : 5;   // chunks in AGPRs (256 / 240)
-    static constexpr int KV = CELL == kLSTM ? 2 : 3;   // chunks in VGPRs (128 / 144)
-    static constexpr int KL = KC - KA - KV;            // chunks in LDS
-    static constexpr int NQ = kWideDh / 16 / kWideWaves;  // 16-unit blocks per wave
-    static constexpr size_t kLdsR = (size_t)KL * (kWideDh / 16) * G * 64 * 16;
+    static constexpr int NT = G * kWideDh / 16;   // output tiles (16 gate columns each)
+    static constexpr int NF = 2 * NT;             // B fragments per wave (2 k-chunks per tile)
+    static constexpr int FA = 64;                 // fragments in AGPRs (256 registers)
+    static constexpr int FV = 32;                 // fragments in VGPRs (128 registers)
+    static constexpr int FL = NF - FA - FV;       // fragments in LDS (LSTM 32, GRU 0)
+    static constexpr int TG = 4;                  // tiles per group
+    static constexpr int NG = NT / TG;            // groups per step
+    static constexpr size_t kLdsR = (size_t)FL * kWideWaves * 64 * 16;
+    static_assert(FL >= 0 && NT % TG == 0, "fragment split");
 };
 
 // acc = A . B (+ acc): v_mfma_f32_16x16x32_bf16 with B in an AGPR ("a") or a
-// VGPR ("v").  The first MFMA of a chain takes 0 as its addend.  Each one
-// starts with the two wait states an MFMA needs after a VALU write of one
-// of its sources (the compiler may place a register copy right before the
-// asm, not knowing it is an MFMA); inside a chain the nop overlaps the wait
-// for the matrix pipe.
+// VGPR ("v"); the *_first forms take 0 as the addend.
 __device__ __forceinline__ void mfma_b_agpr_first(f32x4 &d, const bf16x8 &a, const bf16x8 &b) {
-    asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+    asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
 }
 __device__ __forceinline__ void mfma_b_agpr(f32x4 &d, const bf16x8 &a, const bf16x8 &b) {
-    asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+    asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_b_vgpr_first(f32x4 &d, const bf16x8 &a, const bf16x8 &b) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma_b_vgpr(f32x4 &d, const bf16x8 &a, const bf16x8 &b) {
-    asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+    asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+
+// LDS fragment reads issued where they are written (the compiler would
+// move its own loads next to their uses and wait there), completed by
+// lds_wait, through which the values pass so nothing reads them earlier.
+// The compiler does not count these loads; its own waits on LDS only get
+// stricter (LDS operations complete in order).
+__device__ __forceinline__ bf16x8 lds_frag(const uint4 *p) {
+    bf16x8 v;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"((unsigned)(uintptr_t)p));
+    return v;
+}
+template <int NV>
+__device__ __forceinline__ void lds_wait(bf16x8 (&v)[NV]) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < NV; ++i) asm volatile("" : "+v"(v[i]));
 }
 
 // 16 wait states between the last MFMA writing the accumulators and any
 // instruction that reads them; the accumulators pass through the asm, so
 // every reader depends on it.
-template <int G>
-__device__ __forceinline__ void chain_end(f32x4 (&acc)[G]) {
-    if constexpr (G == 4)
-        asm volatile("s_nop 7\n\ts_nop 7" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]));
-    else
-        asm volatile("s_nop 7\n\ts_nop 7" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]));
+__device__ __forceinline__ void chain_end(f32x4 (&acc)[4]) {
+    asm volatile("s_nop 7\n\ts_nop 7" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]));
+}
+
+// The same packing as inline assembly, for interleaving with the MFMAs
+// (swap16(x, y): x <- [x0, y0, x2, y2], y <- [x1, y1, x3, y3] by 16-lane
+// rows; swap32(x, y): x <- [x0, x1, y0, y1]), and an LDS store the compiler
+// does not reorder against them.  The barrier that follows waits for it.
+__device__ __forceinline__ void swap16_asm(float &x, float &y) {
+    asm volatile("v_permlane16_swap_b32 %0, %1" : "+v"(x), "+v"(y));
+}
+__device__ __forceinline__ void swap32_asm(float &x, float &y) {
+    asm volatile("v_permlane32_swap_b32 %0, %1" : "+v"(x), "+v"(y));
+}
+__device__ __forceinline__ void lds_store_asm(float *p, float v) {
+    asm volatile("ds_write_b32 %0, %1" ::"v"((unsigned)(uintptr_t)p), "v"(v) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void tie(f32x4 &x, f32x4 &y) {
+    asm volatile("" : "+v"(x), "+v"(y));
+}
+
+// Row 0 of four tiles in one register: tile i in lanes 16i .. 16i+15.
+__device__ __forceinline__ float pack_row0(const f32x4 (&acc)[4]) {
+    const RowPair p = swap16(acc[0][0], acc[1][0]);  // [t0, t1, ., .]
+    const RowPair q = swap16(acc[2][0], acc[3][0]);  // [t2, t3, ., .]
+    return swap32(p.a, q.a).a;                       // [t0, t1, t2, t3]
 }
 
 template <int CELL>
 __global__ __launch_bounds__(kWideWaves * 64, 1) void rec_fwd_wide_kernel(RecArgs a,
                                                                           const uint16_t *Rt) {
     using C = WideCfg<CELL>;
-    constexpr int DH = kWideDh, G = C::G, GD = G * DH, KC = C::KC, KA = C::KA, KV = C::KV;
-    constexpr int KL = C::KL, KR = KA + KV, NQ = C::NQ;
-    constexpr int PD = 2;                                   // steps per Gx group
-    constexpr int OUT_ROW = CELL == kLSTM ? 0 : 3;          // lanes that hold the result
-    constexpr int NOUT = CELL == kLSTM ? 2 : 1;             // h (and c) outputs
+    constexpr int DH = kWideDh, G = C::G, GD = G * DH, NT = C::NT;
+    constexpr int FA = C::FA, FV = C::FV, FL = C::FL, TG = C::TG, NG = C::NG;
+    constexpr int PD = 1;  // steps per Gx group
+    constexpr bool LSTM = CELL == kLSTM;
 
-    extern __shared__ __attribute__((aligned(16))) uint4 rl[];  // [KL][16 blocks][G][64 lanes]
-    __shared__ __attribute__((aligned(16))) uint16_t hbuf[2][DH];     // h_{t-1}, step parity
-    __shared__ __attribute__((aligned(16))) float obuf[2][PD][NOUT][DH];  // outputs, group parity
-    // Gx ring, group parity; gate rows padded by 16 floats so the four lane
-    // rows of a wave (one gate each) read distinct banks
-    constexpr int GXP = DH + 16;
-    __shared__ __attribute__((aligned(16))) float gxs[2][PD][G][GXP];
+    extern __shared__ __attribute__((aligned(16))) uint4 rl[];        // [waves][FL][64 lanes]
+    __shared__ __attribute__((aligned(16))) float part[kWideWaves][NT * 16];  // partial sums
+    __shared__ __attribute__((aligned(16))) uint16_t hst[kWideWaves][64];     // A operand slot
 
     const int n = blockIdx.x % a.NH, b = blockIdx.x / a.NH;
     const int H = a.NH * DH, N = a.NH * GD, T = a.T, B = a.B;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
 
-    // ---- R^T fragments: lane (lr, lg) of fragment (gate column col, chunk
-    // c) holds R[k][col] for k = 32c + 8lg .. +8, 16 contiguous bytes of R^T
+    // ---- R^T fragments.  Fragment f = 2*tile + kc: gate columns
+    // [16 tile, +16), k-chunk 2w + kc; lane (lr, lg) holds
+    // R[64w + 32kc + 8lg .. +8][16 tile + lr], 16 contiguous bytes of R^T.
     const uint4 *Rn = reinterpret_cast<const uint4 *>(Rt + (long)n * GD * DH);
-    bf16x8 ra[NQ][G][KA], rv[NQ][G][KV];
+    auto frag_src = [&](int f) {
+        const int col = 16 * (f >> 1) + lr, k = 64 * w + 32 * (f & 1) + 8 * lg;
+        return Rn[(col * DH + k) / 8];
+    };
+    bf16x8 ra[FA], rv[FV];
 #pragma unroll
-    for (int q = 0; q < NQ; ++q)
+    for (int f = 0; f < FA; ++f) ra[f] = __builtin_bit_cast(bf16x8, frag_src(f));
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const int col = g * DH + 64 * w + 16 * q + lr;
-#pragma unroll
-            for (int c = 0; c < KA; ++c)
-                ra[q][g][c] = __builtin_bit_cast(bf16x8, Rn[(col * DH + 32 * c + 8 * lg) / 8]);
-#pragma unroll
-            for (int c = 0; c < KV; ++c)
-                rv[q][g][c] = __builtin_bit_cast(bf16x8, Rn[(col * DH + 32 * (KA + c) + 8 * lg) / 8]);
-        }
-    for (int i = tid; i < KL * 16 * G * 64; i += kWideWaves * 64) {
-        const int l = i & 63, f = i >> 6;
-        const int g = f % G, ub = (f / G) % 16, c = KR + f / (16 * G);
-        const int col = g * DH + 16 * ub + (l & 15);
-        rl[i] = Rn[(col * DH + 32 * c + 8 * (l >> 4)) / 8];
-    }
-    const long o_row = (long)b * H + n * DH;  // this row's h/c in an output step
-    for (int i = tid; i < 2 * DH; i += kWideWaves * 64) {
-        const float v = (i < DH && a.h0) ? a.h0[o_row + i] : 0.f;
-        (&hbuf[0][0])[i] = f32_to_bf16_rne(v);
-    }
+    for (int f = 0; f < FV; ++f) rv[f] = __builtin_bit_cast(bf16x8, frag_src(FA + f));
+    for (int f = 0; f < FL; ++f) rl[(w * FL + f) * 64 + lane] = frag_src(FA + FV + f);
 
-    // ---- lane roles: lane row lg takes Gx of gate lg (the GRU's fourth row
-    // reads gate 2, unused); lanes of row OUT_ROW hold the results
-    const bool wr = lg == OUT_ROW;
-    const int lgx = lg < G ? lg : G - 1;
+    // ---- thread tid owns unit u = tid: state, Gx, outputs
+    const int u = tid;
+    const long o_row = (long)b * H + n * DH;
     const float *gx_row = a.gx + (long)b * N + n * GD;
     const long gx_step = (long)B * N, o_step = (long)B * H;
-    float st[NQ], hl[NQ];
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-        const int j = 64 * w + 16 * q + lr;
-        const float h0 = a.h0 ? a.h0[o_row + j] : 0.f;
-        const float c0 = (CELL == kLSTM && a.c0) ? a.c0[o_row + j] : 0.f;
-        st[q] = CELL == kLSTM ? c0 : h0;
-        hl[q] = h0;
-    }
-    const bool has_h = a.h_seq != nullptr, has_c = CELL == kLSTM && a.c_seq != nullptr;
+    const float h0 = a.h0 ? a.h0[o_row + u] : 0.f;
+    float st = LSTM ? (a.c0 ? a.c0[o_row + u] : 0.f) : h0;  // c (LSTM) or h (GRU)
+    float hl = h0;
+    // (scalar flags: kept in SGPRs rather than as per-lane values)
+    const bool has_h = __builtin_amdgcn_readfirstlane(a.h_seq != nullptr ? 1 : 0) != 0;
+    const bool has_c = LSTM && __builtin_amdgcn_readfirstlane(a.c_seq != nullptr ? 1 : 0) != 0;
 
-    // Gx of a group in flight: PD rows of GD floats, 16 bytes per lane
-    constexpr int GX4 = PD * GD / 4;                       // float4 per group
-    constexpr int GXI = (GX4 + kWideWaves * 64 - 1) / (kWideWaves * 64);
-    float4 gxr[GXI];
+    float bx0[PD][G], bx1[PD][G], oh[PD], oc[PD];
 #pragma unroll
-    for (int i = 0; i < GXI; ++i) gxr[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    auto load_group = [&](int tg) {
+    for (int s = 0; s < PD; ++s) {
+        oh[s] = oc[s] = 0.f;
 #pragma unroll
-        for (int i = 0; i < GXI; ++i) {
-            const int v = tid + i * kWideWaves * 64, s = v / (GD / 4), c4 = v % (GD / 4);
-            if (v < GX4 && tg + s < T) {
-                const float4 *src = reinterpret_cast<const float4 *>(gx_row + (long)(tg + s) * gx_step);
-                gxr[i] = src[(unsigned)c4];
+        for (int g = 0; g < G; ++g) bx0[s][g] = bx1[s][g] = 0.f;
+    }
+    auto load_group = [&](int tg, float (&dst)[PD][G]) {
+#pragma unroll
+        for (int s = 0; s < PD; ++s) {
+            if (tg + s < T) {
+                // wave-uniform row base kept in SGPRs (through an empty asm,
+                // so no per-lane 64-bit pointer is hoisted out of the loop)
+                const float *src = gx_row + (long)(tg + s) * gx_step;
+                asm volatile("" : "+s"(src));
+                const gfloat *gsrc = (const gfloat *)src;
+#pragma unroll
+                for (int g = 0; g < G; ++g) dst[s][g] = gsrc[(unsigned)(g * DH + u)];
             }
         }
     };
-    auto stage_group = [&](int tg) {
-        const int par = (tg / PD) & 1;
-#pragma unroll
-        for (int i = 0; i < GXI; ++i) {
-            const int v = tid + i * kWideWaves * 64, s = v / (GD / 4), c4 = v % (GD / 4);
-            if (v < GX4) {
-                const int col = 4 * c4, g = col / DH, j = col % DH;
-                *reinterpret_cast<float4 *>(&gxs[par][s][g][j]) = gxr[i];
-            }
-        }
-    };
-    // outputs of steps [tg, tg+PD) from the LDS stage of that group: thread
-    // i writes unit i, so each step's row is one coalesced 1 KiB store
     auto store_group = [&](int tg) {
-        const int par = (tg / PD) & 1;
 #pragma unroll
         for (int s = 0; s < PD; ++s) {
             if (tg + s >= T) break;
-            // wave-uniform row base (kept in SGPRs through an empty asm, so
-            // the compiler does not hoist a per-lane 64-bit pointer out of
-            // the loop) plus a 32-bit lane offset
             const long o = (long)(tg + s) * o_step + o_row;
             float *hp = a.h_seq + o, *cp = has_c ? a.c_seq + o : hp;
             asm volatile("" : "+s"(hp), "+s"(cp));
-            if (has_h) hp[(unsigned)tid] = obuf[par][s][0][tid];
-            if (has_c) cp[(unsigned)tid] = obuf[par][s][NOUT - 1][tid];
+            if (has_h) ((gfloat *)hp)[(unsigned)u] = oh[s];
+            if (has_c) ((gfloat *)cp)[(unsigned)u] = oc[s];
         }
     };
-
-    // Gx of group 0 staged, group 1 in flight
-    load_group(0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    stage_group(0);
-    load_group(PD);
+    // A operand: this wave's two k-chunks of h (rows all equal: every lane
+    // of a row group reads the same 16 bytes), through the wave's own slot
+    bf16x8 af[2];
+    auto stage_a = [&](float hv) {
+        hst[w][lane] = f32_to_bf16_rne(hv);
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) af[kc] = *reinterpret_cast<const bf16x8 *>(&hst[w][32 * kc + 8 * lg]);
+    };
+    stage_a(h0);
     __syncthreads();
 
-    bf16x8 af[KC];
+    // MFMAs of tile group g into acc; groups whose fragments sit in LDS take
+    // them from lb (read beforehand by fetch)
+    constexpr int GA = FA / (2 * TG), GV = FV / (2 * TG), GL = FL / (2 * TG);
+    static_assert(FA % (2 * TG) == 0 && FV % (2 * TG) == 0 && FL % (2 * TG) == 0, "group split");
+    // fill(j) runs after the j-th MFMA of the group (work interleaved with
+    // the matrix pipe's latency)
+    auto chain = [&](int g, f32x4 (&acc)[TG], const bf16x8 (&lb)[2 * TG], auto &&fill) {
 #pragma unroll
-    for (int c = 0; c < KC; ++c) af[c] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
-    auto run_group = [&](auto full, int tg) {
-        const int par = (tg / PD) & 1;
+        for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
-        for (int s = 0; s < PD; ++s) {
-            const int t = tg + s;
-            if (!decltype(full)::value && t >= T) break;
-            if (s == 0) {
-                // the next group's Gx (requested a group ago) and the stores
-                // issued then are complete after this single wait.  Its ring
-                // slot was last read in the previous group, before the
-                // barrier that closed it.
-                __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-                stage_group(tg + PD);
-                if (tg > 0) store_group(tg - PD);
-                load_group(tg + 2 * PD);
-            }
-            const uint16_t *hc = hbuf[t & 1];
-            uint16_t *hn = hbuf[(t + 1) & 1];
-            // h_{t-1} as the A operand of all four blocks: row 0 only (4
-            // lanes); the LDS is the LSTM's busiest unit (its R chunks are
-            // read from it at every step), so the other rows are not filled
-            if (lr == 0) {
-#pragma unroll
-                for (int c = 0; c < KC; ++c)
-                    af[c] = *reinterpret_cast<const bf16x8 *>(hc + 32 * c + 8 * lg);
-            }
-            // Chain of block q: the LDS fragments are requested first and
-            // used after the AGPR chunks, so their reads land meanwhile.
-            auto chain = [&](int q, f32x4 (&acc)[G]) {
-                bf16x8 lb[KL > 0 ? KL : 1][G];
-#pragma unroll
-                for (int c = 0; c < KL; ++c)
-#pragma unroll
-                    for (int g = 0; g < G; ++g)
-                        lb[c][g] = __builtin_bit_cast(bf16x8, rl[((c * 16 + 4 * w + q) * G + g) * 64 + lane]);
-#pragma unroll
-                for (int c = 0; c < KA; ++c)
-#pragma unroll
-                    for (int g = 0; g < G; ++g) {
-                        if (c == 0)
-                            mfma_b_agpr_first(acc[g], af[c], ra[q][g][c]);
-                        else
-                            mfma_b_agpr(acc[g], af[c], ra[q][g][c]);
-                    }
-#pragma unroll
-                for (int c = 0; c < KL; ++c)
-#pragma unroll
-                    for (int g = 0; g < G; ++g)
-                        mfma_b_vgpr(acc[g], af[KR + c], lb[c][g]);
-#pragma unroll
-                for (int c = 0; c < KV; ++c)
-#pragma unroll
-                    for (int g = 0; g < G; ++g) mfma_b_vgpr(acc[g], af[KA + c], rv[q][g][c]);
-                chain_end<G>(acc);
-            };
-            // Gate update of block q.  (Written after the chain of block q+1,
-            // the two did not overlap: the compiler ran out of registers.)
-            auto gates = [&](int q, f32x4 (&acc)[G]) {
-                float h, cc;
-                const int j = 64 * w + 16 * q + lr;
-                gate_rows_update<CELL>(gate_rows_of<CELL>(acc), gxs[par][s][lgx][j], st[q], hl[q], h,
-                                       cc);
-                if (wr) {
-                    hn[j] = f32_to_bf16_rne(h);
-                    obuf[par][s][0][j] = h;
-                    if (CELL == kLSTM) obuf[par][s][NOUT - 1][j] = cc;
+            for (int i = 0; i < TG; ++i) {
+                const int f = 2 * (TG * g + i) + kc;
+                if (g < GA) {
+                    if (kc == 0) mfma_b_agpr_first(acc[i], af[kc], ra[f]);
+                    else mfma_b_agpr(acc[i], af[kc], ra[f]);
+                } else {
+                    const bf16x8 &bf = g < GA + GV ? rv[g < GA + GV ? f - FA : 0] : lb[2 * i + kc];
+                    if (kc == 0) mfma_b_vgpr_first(acc[i], af[kc], bf);
+                    else mfma_b_vgpr(acc[i], af[kc], bf);
                 }
-            };
-#pragma unroll
-            for (int q = 0; q < NQ; ++q) {
-                f32x4 acc[G];
-                chain(q, acc);
-                gates(q, acc);
+                fill(kc * TG + i);
             }
-            lds_barrier();
+    };
+    // one LDS fragment of group g (j-th of 8) into lb
+    auto fetch1 = [&](int g, int j, bf16x8 (&lb)[2 * TG]) {
+        const int f = 2 * TG * g + j;
+        lb[j] = lds_frag(&rl[(w * FL + (f - FA - FV)) * 64 + lane]);
+    };
+    // The previous group's publication after the next group's eight MFMAs
+    // (at least sixteen wait states since its last MFMA, as below); the tie
+    // keeps the reads behind them.  Used where the interleaved form below
+    // would need more registers than there are (the LSTM, which also holds
+    // LDS fragments in flight).
+    auto publish_after = [&](int g, f32x4 (&acc)[TG]) {
+        tie<0>(acc[0], acc[1]);
+        tie<1>(acc[2], acc[3]);
+        part[w][(TG * g) * 16 + lane] = pack_row0(acc);
+    };
+    constexpr bool kPieces = FL == 0;
+    // row 0 of the last group of a step -> this wave's partial sums
+    auto publish_last = [&](int g, f32x4 (&acc)[TG]) {
+        chain_end(acc);
+        part[w][(TG * g) * 16 + lane] = pack_row0(acc);
+    };
+    // The previous group's publication, interleaved with the next group's
+    // MFMAs: a tile's last MFMA is at index 4..7 of its group, and its row 0
+    // is read after at least six more MFMAs (each with two wait states of its
+    // own, so at least eighteen: more than the sixteen the result hazard
+    // needs).  The ties keep the reads behind those MFMAs.
+    auto publish_piece = [&](int j, int gp, f32x4 (&acc)[TG], float (&x)[4]) {
+        if (j == 3) {
+            tie<0>(acc[0], acc[1]);
+            x[0] = acc[0][0];
+            x[1] = acc[1][0];
+            swap16_asm(x[0], x[1]);
+        } else if (j == 5) {
+            tie<1>(acc[2], acc[3]);
+            x[2] = acc[2][0];
+            x[3] = acc[3][0];
+            swap16_asm(x[2], x[3]);
+        } else if (j == 6) {
+            swap32_asm(x[0], x[2]);
+        } else if (j == 7) {
+            lds_store_asm(&part[w][(TG * gp) * 16 + lane], x[0]);
         }
     };
 
+    auto run_group = [&](auto full, int tg, float (&use)[PD][G], float (&nxt)[PD][G]) {
+#pragma unroll
+        for (int s = 0; s < PD; ++s) {
+            if (!decltype(full)::value && tg + s >= T) break;
+            if (s == 0) {
+                // everything in flight was issued a whole group ago
+                __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+                if (tg > 0) store_group(tg - PD);
+                load_group(tg + PD, nxt);
+            }
+            // 1. partial gate sums of this wave's k range, all tiles; the
+            // next group's MFMAs go out before this group's results are read
+            // order: each LDS group comes after two AGPR groups, during whose
+            // MFMAs its fragments arrive
+            f32x4 acc0[TG], acc1[TG];
+            bf16x8 lb[2 * TG];
+            float px[4];
+            int prev = -1, k = 0;
+            auto step_group = [&](int g) {
+                f32x4 (&cur)[TG] = (k & 1) ? acc1 : acc0;
+                f32x4 (&old)[TG] = (k & 1) ? acc0 : acc1;
+                const int gp = prev;
+                if constexpr (kPieces) {
+                    chain(g, cur, lb, [&](int j) {
+                        if (gp >= 0) publish_piece(j, gp, old, px);
+                    });
+                } else {
+                    chain(g, cur, lb, [](int) {});
+                    if (gp >= 0) publish_after(gp, old);
+                }
+                prev = g;
+                ++k;
+            };
+            static_assert(GA >= 2 * GL, "two AGPR groups per LDS group");
+#pragma unroll
+            for (int i = 0; i < GA / 2; ++i) {
+                if (i < GL) {
+#pragma unroll
+                    for (int j = 0; j < 2 * TG; ++j) fetch1(GA + GV + i, j, lb);
+                }
+                step_group(2 * i);
+                step_group(2 * i + 1);
+                if (i < GL) {
+                    lds_wait(lb);
+                    step_group(GA + GV + i);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < GV; ++i) step_group(GA + i);
+            publish_last(prev, (k & 1) ? acc0 : acc1);
+            lds_barrier();
+            // 2. unit u: sum over the waves, cell update
+            float pre[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                float v = 0.f;
+#pragma unroll
+                for (int ww = 0; ww < kWideWaves; ++ww) v += part[ww][g * DH + u];
+                pre[g] = (CELL == kGRU && g == 2) ? v : v + use[s][g];
+            }
+            float c;
+            const float h = unit_update<CELL>(pre, CELL == kGRU ? use[s][2] : 0.f, st, c);
+            hl = h;
+            oh[s] = h;
+            oc[s] = c;
+            lds_barrier();
+            // 3. next A operand
+            stage_a(h);
+        }
+    };
+
+    load_group(0, bx0);
     using Full = std::integral_constant<bool, true>;
     using Part = std::integral_constant<bool, false>;
-    const int tfull = T / PD * PD;
-    for (int tg = 0; tg < tfull; tg += PD) run_group(Full{}, tg);
+    const int tfull = T / (2 * PD) * (2 * PD);
+    for (int tg = 0; tg < tfull; tg += 2 * PD) {
+        run_group(Full{}, tg, bx0, bx1);
+        run_group(Full{}, tg + PD, bx1, bx0);
+    }
     int tlast = tfull - PD;
     if (tfull < T) {
-        run_group(Part{}, tfull);
+        run_group(Part{}, tfull, bx0, bx1);
         tlast = tfull;
-    }
-    store_group(tlast);
-    if (wr) {
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            const long o = o_row + 64 * w + 16 * q + lr;
-            a.hT[o] = CELL == kLSTM ? hl[q] : st[q];
-            if (CELL == kLSTM) a.cT[o] = st[q];
+        if (tfull + PD < T) {
+            run_group(Part{}, tfull + PD, bx1, bx0);
+            tlast = tfull + PD;
         }
     }
+    store_group(tlast);
+    a.hT[o_row + u] = LSTM ? hl : st;
+    if (LSTM) a.cT[o_row + u] = st;
 }
 
 template <int CELL>
