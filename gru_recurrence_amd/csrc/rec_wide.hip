@@ -17,11 +17,14 @@
 // wave w multiplies h_{t-1}[64w, 64w+64) (two k-chunks of 32) with the
 // matching 64 rows of R for ALL G*256 gate columns, i.e. NT = G*16 output
 // tiles of v_mfma_f32_16x16x32_bf16, 2*NT MFMAs per step.  Its 2*NT B
-// fragments sit 64 in the AGPRs, 32 in VGPRs and (LSTM) the last 32 in LDS,
-// read again at every step.  Per step:
-//   1. tile groups of 4: MFMAs, then row 0 of the 4 tiles (the only live
-//      batch row) packed into one register with cross-row swaps and written
-//      to LDS as this wave's partial gate sums;
+// fragments sit 64 in the AGPRs, 32 in VGPRs and (LSTM) 32 in LDS, read
+// again at every step; in the LSTM every group of 8 MFMAs takes 4 B operands
+// from AGPRs, 2 from VGPRs and 2 from LDS, so the LDS reads (each issued two
+// groups before its use) are spread evenly over the step.  Per step:
+//   1. tile groups of 4: MFMAs, and interleaved with the next group's MFMAs
+//      row 0 of the 4 tiles (the only live batch row) packed into one
+//      register with cross-row swaps and written to LDS as this wave's
+//      partial gate sums;
 //   2. barrier; thread u sums the 4 waves' partials of unit u's G gates and
 //      runs the whole cell update of unit u lane-locally;
 //   3. barrier (the partial sums may be rewritten); the A operand of the
@@ -37,10 +40,10 @@
 // would need.  They are volatile, so they keep the order written here.
 //
 // HBM traffic per step: Gx_t (G*256 floats) read, h_t and c_t written, by
-// thread u for unit u (coalesced).  Steps go in groups of PD: the Gx of the
-// next group is requested at the start of a group into registers, and the
-// outputs of the previous group (also kept in registers) are stored right
-// after the group's single wait on memory.
+// thread u for unit u (coalesced).  At the start of step t the Gx of step
+// t+1 is requested into registers and then the outputs of step t-1 (kept in
+// registers) are stored; the only wait on memory, at the start of the next
+// step, leaves those stores in flight.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -54,6 +57,16 @@ namespace rnn355 {
 namespace {
 
 constexpr int kWideDh = 256;
+
+// f(integral_constant<int, i>) for i in [B, E): loop indices usable as
+// template arguments (immediate LDS offsets)
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
 // global-memory float (address space 1): a pointer that went through an
 // empty asm is otherwise treated as generic (flat)
 typedef __attribute__((address_space(1))) float gfloat;
@@ -93,16 +106,19 @@ __device__ __forceinline__ void mfma_b_vgpr(f32x4 &d, const bf16x8 &a, const bf1
 // lds_wait, through which the values pass so nothing reads them earlier.
 // The compiler does not count these loads; its own waits on LDS only get
 // stricter (LDS operations complete in order).
-__device__ __forceinline__ bf16x8 lds_frag(const uint4 *p) {
+// (base register + immediate byte offset, so the fragments of a wave share
+// one address register)
+template <int OFF>
+__device__ __forceinline__ bf16x8 lds_frag(unsigned base) {
     bf16x8 v;
-    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"((unsigned)(uintptr_t)p));
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(base), "n"(OFF));
     return v;
 }
-template <int NV>
-__device__ __forceinline__ void lds_wait(bf16x8 (&v)[NV]) {
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-    for (int i = 0; i < NV; ++i) asm volatile("" : "+v"(v[i]));
+// Completes a fragment read with at most three LDS operations issued after
+// it still in flight (LDS operations complete in order; loads the compiler
+// adds in between only make the wait stricter).
+__device__ __forceinline__ void lds_wait3(bf16x8 &v) {
+    asm volatile("s_waitcnt lgkmcnt(3)" : "+v"(v) :: "memory");
 }
 
 // 16 wait states between the last MFMA writing the accumulators and any
@@ -122,8 +138,9 @@ __device__ __forceinline__ void swap16_asm(float &x, float &y) {
 __device__ __forceinline__ void swap32_asm(float &x, float &y) {
     asm volatile("v_permlane32_swap_b32 %0, %1" : "+v"(x), "+v"(y));
 }
-__device__ __forceinline__ void lds_store_asm(float *p, float v) {
-    asm volatile("ds_write_b32 %0, %1" ::"v"((unsigned)(uintptr_t)p), "v"(v) : "memory");
+template <int OFF>
+__device__ __forceinline__ void lds_store_asm(unsigned base, float v) {
+    asm volatile("ds_write_b32 %0, %1 offset:%2" ::"v"(base), "v"(v), "n"(OFF) : "memory");
 }
 template <int N>
 __device__ __forceinline__ void tie(f32x4 &x, f32x4 &y) {
@@ -164,11 +181,6 @@ __global__ __launch_bounds__(kWideWaves * 64, 1) void rec_fwd_wide_kernel(RecArg
         return Rn[(col * DH + k) / 8];
     };
     bf16x8 ra[FA], rv[FV];
-#pragma unroll
-    for (int f = 0; f < FA; ++f) ra[f] = __builtin_bit_cast(bf16x8, frag_src(f));
-#pragma unroll
-    for (int f = 0; f < FV; ++f) rv[f] = __builtin_bit_cast(bf16x8, frag_src(FA + f));
-    for (int f = 0; f < FL; ++f) rl[(w * FL + f) * 64 + lane] = frag_src(FA + FV + f);
 
     // ---- thread tid owns unit u = tid: state, Gx, outputs
     const int u = tid;
@@ -182,6 +194,9 @@ __global__ __launch_bounds__(kWideWaves * 64, 1) void rec_fwd_wide_kernel(RecArg
     const bool has_h = __builtin_amdgcn_readfirstlane(a.h_seq != nullptr ? 1 : 0) != 0;
     const bool has_c = LSTM && __builtin_amdgcn_readfirstlane(a.c_seq != nullptr ? 1 : 0) != 0;
 
+    // store instructions per group (issued after the group's loads)
+    const int nst = PD * ((has_h ? 1 : 0) + (has_c ? 1 : 0));
+    static_assert(PD == 1, "the waits below count one step of stores");
     float bx0[PD][G], bx1[PD][G], oh[PD], oc[PD];
 #pragma unroll
     for (int s = 0; s < PD; ++s) {
@@ -225,45 +240,62 @@ __global__ __launch_bounds__(kWideWaves * 64, 1) void rec_fwd_wide_kernel(RecArg
     stage_a(h0);
     __syncthreads();
 
-    // MFMAs of tile group g into acc; groups whose fragments sit in LDS take
-    // them from lb (read beforehand by fetch)
-    constexpr int GA = FA / (2 * TG), GV = FV / (2 * TG), GL = FL / (2 * TG);
-    static_assert(FA % (2 * TG) == 0 && FV % (2 * TG) == 0 && FL % (2 * TG) == 0, "group split");
+    // Where the B fragment of MFMA j of group g lives (j = kc*TG + i: tile
+    // TG*g + i, k-chunk kc).  LSTM: j%4 in {0,1} AGPR, 2 VGPR, 3 LDS; GRU:
+    // the first 8 groups AGPR, the rest VGPR.
+    enum { kA = 0, kV = 1, kL = 2 };
+    constexpr auto cls = [](int g, int j) { return LSTM ? ((j & 3) < 2 ? kA : (j & 3) == 2 ? kV : kL) : (g < 8 ? kA : kV); };
+    constexpr auto idx = [](int g, int j) {
+        return LSTM ? ((j & 3) < 2 ? 4 * g + 2 * (j >> 2) + (j & 3) : 2 * g + (j >> 2))
+                    : (g < 8 ? 8 * g + j : 8 * (g - 8) + j);
+    };
+    static_assert(FL == 0 || FL == 2 * NG, "two LDS fragments per group");
+    // R^T fragments, placed by class
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int j = 0; j < 2 * TG; ++j) {
+            const int tile = TG * g + (j % TG), kc = j / TG;
+            const uint4 v = frag_src(2 * tile + kc);
+            if (cls(g, j) == kA) ra[idx(g, j)] = __builtin_bit_cast(bf16x8, v);
+            else if (cls(g, j) == kV) rv[idx(g, j)] = __builtin_bit_cast(bf16x8, v);
+            else rl[(w * FL + idx(g, j)) * 64 + lane] = v;
+        }
+    // LDS fragments in flight: slot (g & 1)*2 + j/4, read two groups ahead
+    bf16x8 lb[4];
+    const unsigned rl_base = (unsigned)(uintptr_t)&rl[(w * FL) * 64 + lane];
+    auto fetch = [&](auto gc, auto jc) {
+        constexpr int g = decltype(gc)::value, j = decltype(jc)::value;
+        lb[(g & 1) * 2 + (j >> 2)] = lds_frag<idx(g, j) * 1024>(rl_base);
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I3 = std::integral_constant<int, 3>;
+    using I7 = std::integral_constant<int, 7>;
+    if constexpr (FL > 0) {
+        fetch(I0{}, I3{}); fetch(I0{}, I7{}); fetch(I1{}, I3{}); fetch(I1{}, I7{});
+    }
     // fill(j) runs after the j-th MFMA of the group (work interleaved with
     // the matrix pipe's latency)
-    auto chain = [&](int g, f32x4 (&acc)[TG], const bf16x8 (&lb)[2 * TG], auto &&fill) {
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-            for (int i = 0; i < TG; ++i) {
-                const int f = 2 * (TG * g + i) + kc;
-                if (g < GA) {
-                    if (kc == 0) mfma_b_agpr_first(acc[i], af[kc], ra[f]);
-                    else mfma_b_agpr(acc[i], af[kc], ra[f]);
-                } else {
-                    const bf16x8 &bf = g < GA + GV ? rv[g < GA + GV ? f - FA : 0] : lb[2 * i + kc];
-                    if (kc == 0) mfma_b_vgpr_first(acc[i], af[kc], bf);
-                    else mfma_b_vgpr(acc[i], af[kc], bf);
-                }
-                fill(kc * TG + i);
+    auto chain = [&](auto gc, f32x4 (&acc)[TG], auto &&fill) {
+        constexpr int g = decltype(gc)::value;
+        static_for<0, 2 * TG>([&](auto jc) {
+            constexpr int j = decltype(jc)::value, i = j % TG, kc = j / TG;
+            constexpr int c = cls(g, j);
+            if constexpr (c == kA) {
+                if constexpr (kc == 0) mfma_b_agpr_first(acc[i], af[kc], ra[idx(g, j)]);
+                else mfma_b_agpr(acc[i], af[kc], ra[idx(g, j)]);
+            } else {
+                bf16x8 &bf = c == kV ? rv[c == kV ? idx(g, j) : 0] : lb[(g & 1) * 2 + (j >> 2)];
+                if constexpr (c == kL) lds_wait3(bf);
+                if constexpr (kc == 0) mfma_b_vgpr_first(acc[i], af[kc], bf);
+                else mfma_b_vgpr(acc[i], af[kc], bf);
+                // the same slot, two groups on
+                if constexpr (c == kL) fetch(std::integral_constant<int, (g + 2) % NG>{}, jc);
             }
+            fill(jc);
+        });
     };
-    // one LDS fragment of group g (j-th of 8) into lb
-    auto fetch1 = [&](int g, int j, bf16x8 (&lb)[2 * TG]) {
-        const int f = 2 * TG * g + j;
-        lb[j] = lds_frag(&rl[(w * FL + (f - FA - FV)) * 64 + lane]);
-    };
-    // The previous group's publication after the next group's eight MFMAs
-    // (at least sixteen wait states since its last MFMA, as below); the tie
-    // keeps the reads behind them.  Used where the interleaved form below
-    // would need more registers than there are (the LSTM, which also holds
-    // LDS fragments in flight).
-    auto publish_after = [&](int g, f32x4 (&acc)[TG]) {
-        tie<0>(acc[0], acc[1]);
-        tie<1>(acc[2], acc[3]);
-        part[w][(TG * g) * 16 + lane] = pack_row0(acc);
-    };
-    constexpr bool kPieces = FL == 0;
     // row 0 of the last group of a step -> this wave's partial sums
     auto publish_last = [&](int g, f32x4 (&acc)[TG]) {
         chain_end(acc);
@@ -274,21 +306,23 @@ __global__ __launch_bounds__(kWideWaves * 64, 1) void rec_fwd_wide_kernel(RecArg
     // is read after at least six more MFMAs (each with two wait states of its
     // own, so at least eighteen: more than the sixteen the result hazard
     // needs).  The ties keep the reads behind those MFMAs.
-    auto publish_piece = [&](int j, int gp, f32x4 (&acc)[TG], float (&x)[4]) {
-        if (j == 3) {
+    const unsigned part_base = (unsigned)(uintptr_t)&part[w][lane];
+    auto publish_piece = [&](auto jc, auto gpc, f32x4 (&acc)[TG], float (&x)[4]) {
+        constexpr int j = decltype(jc)::value, gp = decltype(gpc)::value;
+        if constexpr (j == 3) {
             tie<0>(acc[0], acc[1]);
             x[0] = acc[0][0];
             x[1] = acc[1][0];
             swap16_asm(x[0], x[1]);
-        } else if (j == 5) {
+        } else if constexpr (j == 5) {
             tie<1>(acc[2], acc[3]);
             x[2] = acc[2][0];
             x[3] = acc[3][0];
             swap16_asm(x[2], x[3]);
-        } else if (j == 6) {
+        } else if constexpr (j == 6) {
             swap32_asm(x[0], x[2]);
-        } else if (j == 7) {
-            lds_store_asm(&part[w][(TG * gp) * 16 + lane], x[0]);
+        } else if constexpr (j == 7) {
+            lds_store_asm<(TG * gp) * 16 * 4>(part_base, x[0]);
         }
     };
 
@@ -297,51 +331,27 @@ __global__ __launch_bounds__(kWideWaves * 64, 1) void rec_fwd_wide_kernel(RecArg
         for (int s = 0; s < PD; ++s) {
             if (!decltype(full)::value && tg + s >= T) break;
             if (s == 0) {
-                // everything in flight was issued a whole group ago
-                __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-                if (tg > 0) store_group(tg - PD);
+                // this group's Gx, requested a group ago; the stores issued
+                // after it (nst of them) may still be in flight
+                if (tg <= PD || nst == 0) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+                else if (nst == 1) __builtin_amdgcn_s_waitcnt(0x0F71);       // vmcnt(1)
+                else __builtin_amdgcn_s_waitcnt(0x0F72);                     // vmcnt(2)
                 load_group(tg + PD, nxt);
+                if (tg > 0) store_group(tg - PD);
             }
             // 1. partial gate sums of this wave's k range, all tiles; the
             // next group's MFMAs go out before this group's results are read
-            // order: each LDS group comes after two AGPR groups, during whose
-            // MFMAs its fragments arrive
             f32x4 acc0[TG], acc1[TG];
-            bf16x8 lb[2 * TG];
             float px[4];
-            int prev = -1, k = 0;
-            auto step_group = [&](int g) {
-                f32x4 (&cur)[TG] = (k & 1) ? acc1 : acc0;
-                f32x4 (&old)[TG] = (k & 1) ? acc0 : acc1;
-                const int gp = prev;
-                if constexpr (kPieces) {
-                    chain(g, cur, lb, [&](int j) {
-                        if (gp >= 0) publish_piece(j, gp, old, px);
-                    });
-                } else {
-                    chain(g, cur, lb, [](int) {});
-                    if (gp >= 0) publish_after(gp, old);
-                }
-                prev = g;
-                ++k;
-            };
-            static_assert(GA >= 2 * GL, "two AGPR groups per LDS group");
-#pragma unroll
-            for (int i = 0; i < GA / 2; ++i) {
-                if (i < GL) {
-#pragma unroll
-                    for (int j = 0; j < 2 * TG; ++j) fetch1(GA + GV + i, j, lb);
-                }
-                step_group(2 * i);
-                step_group(2 * i + 1);
-                if (i < GL) {
-                    lds_wait(lb);
-                    step_group(GA + GV + i);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < GV; ++i) step_group(GA + i);
-            publish_last(prev, (k & 1) ? acc0 : acc1);
+            static_for<0, NG>([&](auto gc) {
+                constexpr int g = decltype(gc)::value;
+                f32x4 (&cur)[TG] = (g & 1) ? acc1 : acc0;
+                f32x4 (&old)[TG] = (g & 1) ? acc0 : acc1;
+                chain(gc, cur, [&](auto jc) {
+                    if constexpr (g > 0) publish_piece(jc, std::integral_constant<int, g - 1>{}, old, px);
+                });
+            });
+            publish_last(NG - 1, (NG & 1) ? acc0 : acc1);
             lds_barrier();
             // 2. unit u: sum over the waves, cell update
             float pre[G];
