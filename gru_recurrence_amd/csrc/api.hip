@@ -361,8 +361,13 @@ rnn_status backward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, co
     const int G = lstm ? 4 : 3, Dh = d->Dh, NH = d->NH, T = d->T, B = d->B, Din = d->Din;
     const int GD = G * Dh, N = NH * GD, H = NH * Dh, M = T * B;
     if (!gemm_shape_ok(Din, N, dt) || Dh % 16 != 0) return RNN_ERR_UNSUPPORTED;
-    const BwdPlan p = plan_bwd(cell, B, NH, Dh, device_cus(), bt_override(), k_override());
-    if (!p.ok) return RNN_ERR_UNSUPPORTED;
+    // Dh = 256: one workgroup per (head, batch row) with R split over
+    // registers and LDS; otherwise the exchange-based sweep
+    const WidePlan pw = wide_enabled() ? plan_wide(cell, B, NH, Dh, true) : WidePlan{};
+    const BwdPlan p = pw.ok ? BwdPlan{} : plan_bwd(cell, B, NH, Dh, device_cus(), bt_override(),
+                                                   k_override());
+    if (!pw.ok && !p.ok) return RNN_ERR_UNSUPPORTED;
+    const int nbt = pw.ok ? B : p.nbt;  // rows of db partials
     const rnn_op op = lstm ? RNN_OP_BWD_LSTM : RNN_OP_BWD_GRU;
     if (!ws || ws_bytes < rnn_workspace_size(op, d, dt)) return RNN_ERR_WORKSPACE;
 
@@ -412,10 +417,12 @@ rnn_status backward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, co
         m.xg = (unsigned long long *)(base + L.xchg);
         m.flag = (unsigned *)ws;
         m.spin_limit = spin_limit();
-        if (!ok(launch_rec_bwd(cell, p, m, stream))) return RNN_ERR_HIP;
+        const hipError_t e = pw.ok ? launch_rec_bwd_wide(cell, pw, m, stream)
+                                   : launch_rec_bwd(cell, p, m, stream);
+        if (!ok(e)) return RNN_ERR_HIP;
     }
     // 3. parameter and input gradients
-    if (!ok(launch_db_reduce(dbp, p.nbt, N, db, stream))) return RNN_ERR_HIP;
+    if (!ok(launch_db_reduce(dbp, nbt, N, db, stream))) return RNN_ERR_HIP;
     float *part = (float *)(base + L.part);
     const int cus = device_cus();
     {

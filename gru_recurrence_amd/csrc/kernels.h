@@ -189,6 +189,12 @@ struct BwdArgs {
 
 BwdPlan plan_bwd(int cell, int B, int NH, int Dh, int num_cu, int bt_override, int k_override);
 hipError_t launch_rec_bwd(int cell, const BwdPlan &p, const BwdArgs &m, hipStream_t s);
+// Reverse sweep of the backward for Dh = 256 on the same layout (one
+// workgroup per (head, batch row); db partials per batch row).  Uses the
+// fields of BwdArgs that the cell backward reads; K, KS, NB, BT, xg, flag
+// and spin_limit are ignored.  The plan is plan_wide's (its lds is the
+// forward's; the launcher sets its own).
+hipError_t launch_rec_bwd_wide(int cell, const WidePlan &p, const BwdArgs &m, hipStream_t s);
 hipError_t launch_hprev_bf16(const float *h0, const float *h_seq, uint16_t *hprev, long BH,
                              long total, hipStream_t s);
 hipError_t launch_db_reduce(const float *db_part, int nbt, int N, float *db, hipStream_t s);

@@ -395,6 +395,290 @@ __global__ __launch_bounds__(kWideWaves * 64, 1) void rec_fwd_wide_kernel(RecArg
     if (LSTM) a.cT[o_row + u] = st;
 }
 
+// ---------------------------------------------------------------------------
+// Reverse-time sweep of backpropagation through time for Dh = 256 on one
+// compute unit per (head, batch row), the same split of R.  Per step t
+// (T-1 .. 0), thread u owns unit u:
+//   1. the cell backward of unit u (from the recomputed gate inputs, the
+//      streamed c_t, c_{t-1} / h_{t-1} and dL/dh_t, and the carries), which
+//      writes dGx_t (and the GRU's dS_t) as bf16 and accumulates db;
+//   2. the carry dh = e_t R^T with e = dGx (LSTM) or dS (GRU): wave w holds
+//      the gate columns of units [64w, 64w+64) of every gate -- exactly the
+//      e values its own threads produced, so the A operand needs no barrier
+//      -- and multiplies them with the matching columns of R for all 256
+//      output units (16 tiles), publishing row 0 of its partial sums;
+//   3. barrier, each thread sums the four partials of its unit (plus the
+//      GRU's direct term dh u), barrier.
+// B fragment (tile of units [16i, 16i+16), chunk (g, half) of the wave's
+// columns): lane (lr, lg) holds R[16i + lr][g*256 + 64w + 32 half + 8lg ..
+// +8], 16 contiguous bytes of R's own rows.
+template <int CELL>
+struct WideBwdCfg {
+    static constexpr int G = CellTraits<CELL>::G;
+    static constexpr int NCH = 2 * G;            // k-chunks per wave
+    static constexpr int NT = kWideDh / 16;      // output tiles
+    static constexpr int TG = 4;                 // tiles per group
+    static constexpr int NG = NT / TG;           // groups per step
+    static constexpr int MPG = TG * NCH;         // MFMAs per group
+    static constexpr int NF = NT * NCH;          // B fragments per wave
+    static constexpr int FA = 64, FV = 32, FL = NF - FA - FV;
+    static constexpr size_t kLdsR = (size_t)FL * kWideWaves * 64 * 16;
+    static_assert(FL == 0 || FL == NG * NCH, "one LDS fragment per chunk and group");
+};
+
+template <int CELL>
+__global__ __launch_bounds__(kWideWaves * 64, 1) void rec_bwd_wide_kernel(BwdArgs m) {
+    using C = WideBwdCfg<CELL>;
+    constexpr int DH = kWideDh, G = C::G, GD = G * DH, NCH = C::NCH, TG = C::TG, NG = C::NG;
+    constexpr int MPG = C::MPG, FA = C::FA, FV = C::FV, FL = C::FL;
+    constexpr bool LSTM = CELL == kLSTM;
+    constexpr int NIN = LSTM ? G + 3 : 2 * G + 2;  // streamed floats per step and unit
+    constexpr int NST = LSTM ? G : 2 * G;          // bf16 stores per step
+
+    extern __shared__ __attribute__((aligned(16))) uint4 rl[];        // [waves][FL][64 lanes]
+    __shared__ __attribute__((aligned(16))) float part[kWideWaves][DH];       // partial carries
+    __shared__ __attribute__((aligned(16))) uint16_t hs[kWideWaves][G][64];   // A operand slot
+
+    const int n = blockIdx.x % m.NH, b = blockIdx.x / m.NH;
+    const int H = m.NH * DH, N = m.NH * GD, T = m.T, B = m.B;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int u = tid;
+
+    // ---- R fragments by class (LSTM: tiles i%4 in {0,1} AGPR, 2 VGPR, 3
+    // LDS; GRU: the first 64 in MFMA order AGPR, the rest VGPR)
+    enum { kA = 0, kV = 1, kL = 2 };
+    constexpr auto cls = [](int gi, int j) {
+        return LSTM ? ((j % TG) < 2 ? kA : (j % TG) == 2 ? kV : kL) : (gi * MPG + j < FA ? kA : kV);
+    };
+    constexpr auto idx = [](int gi, int j) {
+        const int c = j / TG, i = j % TG;
+        return LSTM ? (i < 2 ? (gi * NCH + c) * 2 + i : gi * NCH + c)
+                    : (gi * MPG + j < FA ? gi * MPG + j : gi * MPG + j - FA);
+    };
+    const uint16_t *Rn = m.Rb + (long)n * DH * GD;
+    bf16x8 ra[FA], rv[FV];
+    static_for<0, NG>([&](auto gc) {
+        constexpr int gi = decltype(gc)::value;
+        static_for<0, MPG>([&](auto jc) {
+            constexpr int j = decltype(jc)::value, c = j / TG, i = j % TG;
+            const int row = 16 * (TG * gi + i) + lr;
+            const int col = (c >> 1) * DH + 64 * w + 32 * (c & 1) + 8 * lg;
+            const uint4 v = *reinterpret_cast<const uint4 *>(Rn + (long)row * GD + col);
+            if constexpr (cls(gi, j) == kA) ra[idx(gi, j)] = __builtin_bit_cast(bf16x8, v);
+            else if constexpr (cls(gi, j) == kV) rv[idx(gi, j)] = __builtin_bit_cast(bf16x8, v);
+            else rl[(w * FL + idx(gi, j)) * 64 + lane] = v;
+        });
+    });
+    // LDS fragments in flight: use q (= gi*NCH + c) in slot q % 4, read four
+    // uses ahead (continuing into the next step)
+    bf16x8 lb[4];
+    const unsigned rl_base = (unsigned)(uintptr_t)&rl[(w * FL) * 64 + lane];
+    auto fetch = [&](auto qc) {
+        constexpr int q = decltype(qc)::value % (FL > 0 ? FL : 1);
+        lb[q & 3] = lds_frag<q * 1024>(rl_base);
+    };
+    if constexpr (FL > 0)
+        static_for<0, 4>([&](auto qc) { fetch(qc); });
+
+    // ---- per-unit state and streamed inputs
+    const long o_row = (long)b * H + n * DH, a_row = (long)b * N + n * GD;
+    const long a_step = (long)B * N, o_step = (long)B * H;
+    float dhc = m.dhT ? m.dhT[o_row + u] : 0.f;
+    float dcc = (LSTM && m.dcT) ? m.dcT[o_row + u] : 0.f;
+    float dir = 0.f, dbs[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) dbs[g] = 0.f;
+    // in[]: LSTM pa[0..3], c_t, c_{t-1}, dL/dh_t; GRU pa[0..2], sv[0..2],
+    // h_{t-1}, dL/dh_t
+    float in0[NIN], in1[NIN];
+#pragma unroll
+    for (int i = 0; i < NIN; ++i) in0[i] = in1[i] = 0.f;
+    auto gptr = [](const float *p) {
+        asm volatile("" : "+s"(p));
+        return (const gfloat *)p;
+    };
+    auto load_in = [&](int t, float (&d)[NIN]) {
+        const gfloat *pa = gptr(m.A + a_row + (long)t * a_step);
+#pragma unroll
+        for (int g = 0; g < G; ++g) d[g] = pa[(unsigned)(g * DH + u)];
+        const gfloat *up = gptr(m.dh_seq + o_row + (long)t * o_step);
+        d[NIN - 1] = up[(unsigned)u];
+        if constexpr (LSTM) {
+            const gfloat *ct = gptr(m.c_seq + o_row + (long)t * o_step);
+            d[G] = ct[(unsigned)u];
+            if (t > 0) d[G + 1] = gptr(m.c_seq + o_row + (long)(t - 1) * o_step)[(unsigned)u];
+            else d[G + 1] = m.c0 ? m.c0[o_row + u] : 0.f;
+        } else {
+            const gfloat *sv = gptr(m.S + a_row + (long)t * a_step);
+#pragma unroll
+            for (int g = 0; g < G; ++g) d[G + g] = sv[(unsigned)(g * DH + u)];
+            if (t > 0) d[2 * G] = gptr(m.h_seq + o_row + (long)(t - 1) * o_step)[(unsigned)u];
+            else d[2 * G] = m.h0 ? m.h0[o_row + u] : 0.f;
+        }
+    };
+    auto store_d = [&](int t, const uint16_t (&dd)[G], const uint16_t (&de)[G]) {
+        uint16_t *pa = m.dA + a_row + (long)t * a_step;
+        asm volatile("" : "+s"(pa));
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            ((__attribute__((address_space(1))) uint16_t *)pa)[(unsigned)(g * DH + u)] = dd[g];
+        if constexpr (!LSTM) {
+            uint16_t *ps = m.dS + a_row + (long)t * a_step;
+            asm volatile("" : "+s"(ps));
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+                ((__attribute__((address_space(1))) uint16_t *)ps)[(unsigned)(g * DH + u)] = de[g];
+        }
+    };
+
+    // ---- the MFMA part of a step (A operand: this wave's e values)
+    bf16x8 af[NCH];
+    auto chain = [&](auto gc, f32x4 (&acc)[TG], auto &&fill) {
+        constexpr int gi = decltype(gc)::value;
+        static_for<0, MPG>([&](auto jc) {
+            constexpr int j = decltype(jc)::value, c = j / TG, i = j % TG;
+            constexpr int k = cls(gi, j);
+            if constexpr (k == kA) {
+                if constexpr (c == 0) mfma_b_agpr_first(acc[i], af[c], ra[idx(gi, j)]);
+                else mfma_b_agpr(acc[i], af[c], ra[idx(gi, j)]);
+            } else {
+                constexpr int q = gi * NCH + c;  // LDS use index (LSTM)
+                bf16x8 &bf = k == kV ? rv[k == kV ? idx(gi, j) : 0] : lb[q & 3];
+                if constexpr (k == kL) lds_wait3(bf);
+                if constexpr (c == 0) mfma_b_vgpr_first(acc[i], af[c], bf);
+                else mfma_b_vgpr(acc[i], af[c], bf);
+                if constexpr (k == kL) fetch(std::integral_constant<int, q + 4>{});
+            }
+            fill(jc);
+        });
+    };
+    const unsigned part_base = (unsigned)(uintptr_t)&part[w][lane];
+    // the previous group's publication within the next group's MFMAs: a
+    // tile's last MFMA is among the last four of its group, and its row 0 is
+    // read after at least eight more (with their own wait states, well over
+    // the sixteen the result hazard needs)
+    auto publish_piece = [&](auto jc, auto gpc, f32x4 (&acc)[TG], float (&x)[4]) {
+        constexpr int j = decltype(jc)::value, gp = decltype(gpc)::value;
+        if constexpr (j == 5) {
+            tie<0>(acc[0], acc[1]);
+            x[0] = acc[0][0];
+            x[1] = acc[1][0];
+            swap16_asm(x[0], x[1]);
+        } else if constexpr (j == 7) {
+            tie<1>(acc[2], acc[3]);
+            x[2] = acc[2][0];
+            x[3] = acc[3][0];
+            swap16_asm(x[2], x[3]);
+        } else if constexpr (j == 8) {
+            swap32_asm(x[0], x[2]);
+        } else if constexpr (j == 9) {
+            lds_store_asm<(TG * gp) * 16 * 4>(part_base, x[0]);
+        }
+    };
+    static_assert(MPG >= 10, "publication pieces fit in a group");
+
+    load_in(T - 1, in0);
+    __syncthreads();
+
+    auto step = [&](int s, float (&cur)[NIN], float (&nxt)[NIN]) {
+        const int t = T - 1 - s;
+        // this step's inputs (requested a step ago); the previous step's
+        // stores may still be in flight
+        if (s == 0) __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0)
+        else if (NST == 4) __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+        else __builtin_amdgcn_s_waitcnt(0x0F76);                // vmcnt(6)
+        if (t > 0) load_in(t - 1, nxt);
+        // 1. cell backward of unit u
+        float d[G], e[G];
+        const float dh = cur[NIN - 1] + dhc;
+        if constexpr (LSTM) {
+            const float ig = sigmoid_f(cur[0]), fg = sigmoid_f(cur[1]);
+            const float zg = tanh_f(cur[2]), og = sigmoid_f(cur[3]);
+            const float tc = tanh_f(cur[G]);
+            const float dc = fmaf(dh * og, 1.0f - tc * tc, dcc);
+            d[0] = dc * zg * ig * (1.0f - ig);
+            d[1] = dc * cur[G + 1] * fg * (1.0f - fg);
+            d[2] = dc * ig * (1.0f - zg * zg);
+            d[3] = dh * tc * og * (1.0f - og);
+            dcc = dc * fg;
+#pragma unroll
+            for (int g = 0; g < G; ++g) e[g] = d[g];
+        } else {
+            const float rg = sigmoid_f(cur[0] + cur[G]);
+            const float ug = sigmoid_f(cur[1] + cur[G + 1]);
+            const float ng = tanh_f(fmaf(rg, cur[G + 2], cur[2]));
+            d[2] = dh * (1.0f - ug) * (1.0f - ng * ng);
+            d[1] = dh * (cur[2 * G] - ng) * ug * (1.0f - ug);
+            d[0] = d[2] * cur[G + 2] * rg * (1.0f - rg);
+            e[0] = d[0];
+            e[1] = d[1];
+            e[2] = d[2] * rg;
+            dir = dh * ug;
+        }
+        uint16_t dd[G], de[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            dbs[g] += d[g];
+            dd[g] = f32_to_bf16_rne(d[g]);
+            de[g] = LSTM ? dd[g] : f32_to_bf16_rne(e[g]);
+            hs[w][g][lane] = de[g];
+        }
+        store_d(t, dd, de);
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+            af[c] = *reinterpret_cast<const bf16x8 *>(&hs[w][c >> 1][32 * (c & 1) + 8 * lg]);
+        // 2. partial carries of this wave's columns
+        f32x4 acc0[TG], acc1[TG];
+        float px[4];
+        static_for<0, NG>([&](auto gc) {
+            constexpr int gi = decltype(gc)::value;
+            f32x4 (&cu)[TG] = (gi & 1) ? acc1 : acc0;
+            f32x4 (&old)[TG] = (gi & 1) ? acc0 : acc1;
+            chain(gc, cu, [&](auto jc) {
+                if constexpr (gi > 0) publish_piece(jc, std::integral_constant<int, gi - 1>{}, old, px);
+            });
+        });
+        {
+            f32x4 (&last)[TG] = ((NG - 1) & 1) ? acc1 : acc0;
+            chain_end(last);
+            part[w][(TG * (NG - 1)) * 16 + lane] = pack_row0(last);
+        }
+        lds_barrier();
+        // 3. carry of unit u
+        float v = LSTM ? 0.f : dir;
+#pragma unroll
+        for (int ww = 0; ww < kWideWaves; ++ww) v += part[ww][u];
+        dhc = v;
+        lds_barrier();
+    };
+    int s = 0;
+    for (; s + 1 < T; s += 2) {
+        step(s, in0, in1);
+        step(s + 1, in1, in0);
+    }
+    if (s < T) step(s, in0, in1);
+    if constexpr (FL > 0) __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): prefetches done
+    m.dh0[o_row + u] = dhc;
+    if (LSTM) m.dc0[o_row + u] = dcc;
+    float *dbt = m.db_part + (long)b * N + n * GD;
+#pragma unroll
+    for (int g = 0; g < G; ++g) dbt[g * DH + u] = dbs[g];
+}
+
+template <int CELL>
+hipError_t launch_bwd_wide_t(const WidePlan &p, const BwdArgs &m, hipStream_t s) {
+    if (WideBwdCfg<CELL>::kLdsR > 0) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&rec_bwd_wide_kernel<CELL>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)WideBwdCfg<CELL>::kLdsR);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(rec_bwd_wide_kernel<CELL>, dim3(p.grid), dim3(p.threads),
+                       WideBwdCfg<CELL>::kLdsR, s, m);
+    return hipGetLastError();
+}
+
 template <int CELL>
 hipError_t launch_wide_t(const WidePlan &p, const RecArgs &a, const uint16_t *Rt, hipStream_t s) {
     if (WideCfg<CELL>::kLdsR > 0) {
@@ -418,6 +702,11 @@ WidePlan plan_wide(int cell, int B, int NH, int Dh, bool bf16) {
     p.threads = kWideWaves * 64;
     p.lds = cell == kLSTM ? WideCfg<kLSTM>::kLdsR : WideCfg<kGRU>::kLdsR;
     return p;
+}
+
+hipError_t launch_rec_bwd_wide(int cell, const WidePlan &p, const BwdArgs &m, hipStream_t s) {
+    if (!p.ok || m.Dh != kWideDh) return hipErrorInvalidValue;
+    return cell == kLSTM ? launch_bwd_wide_t<kLSTM>(p, m, s) : launch_bwd_wide_t<kGRU>(p, m, s);
 }
 
 hipError_t launch_rec_wide(int cell, const WidePlan &p, const RecArgs &a, const uint16_t *Rt,

@@ -23,7 +23,7 @@ TOL = 2e-2
 
 @pytest.fixture(autouse=True)
 def _clean_env():
-    keys = ("RNN355_REC_BT", "RNN355_REC_K")
+    keys = ("RNN355_REC_BT", "RNN355_REC_K", "RNN355_REC_WIDE")
     old = {k: os.environ.pop(k, None) for k in keys}
     yield
     for k in keys:
@@ -42,15 +42,23 @@ def gpu_bwd(c, final=False):
     return {k: host(v) for k, v in grads.items()}
 
 
+# bt "x": RNN355_REC_WIDE=0, the exchange-based sweep at Dh = 256 (the
+# default there is one workgroup per (head, row) with R split over
+# registers and LDS)
 @pytest.mark.parametrize("Dh,B,bt,final", [
     (32, 3, None, False),     # one workgroup per head, dA through LDS
     (64, 5, 2, True),         # two row slots, ragged, final-state gradients
     (128, 3, 4, False),       # four row slots
     (128, 2, None, True),
-    (256, 3, None, True),     # several workgroups per head, dA as tagged words
-    (256, 5, 4, False),
+    (256, 3, None, True),     # split R, one workgroup per (head, row)
+    (256, 5, None, False),
+    (256, 3, "x", True),      # several workgroups per head, dA as tagged words
+    (256, 5, "x4", False),
 ])
 def test_lstm_backward_small(Dh, B, bt, final):
+    if isinstance(bt, str):
+        os.environ["RNN355_REC_WIDE"] = "0"
+        bt = int(bt[1:]) if len(bt) > 1 else None
     if bt is not None:
         os.environ["RNN355_REC_BT"] = str(bt)
     d = synth.Dims(T=19, B=B, Din=64, NH=2, Dh=Dh)
@@ -66,7 +74,9 @@ def test_lstm_backward_small(Dh, B, bt, final):
         assert e <= TOL, (k, e)
 
 
-def test_lstm_backward_bitwise_repeatable():
+@pytest.mark.parametrize("wide", ["1", "0"])
+def test_lstm_backward_bitwise_repeatable(wide):
+    os.environ["RNN355_REC_WIDE"] = wide
     d = synth.Dims(T=11, B=2, Din=32, NH=2, Dh=256)
     c = synth.make_case("lstm", d, "bf16", 9100, bias="forget+1", backward=True)
     a, b = gpu_bwd(c), gpu_bwd(c)
@@ -138,10 +148,15 @@ def gpu_bwd_gru(c, final=False):
     (64, 5, 2, True),         # two row slots, ragged, final-state gradient
     (128, 2, None, True),     # 12 chunks per wave, one workgroup
     (128, 5, 4, False),       # four row slots
-    (256, 3, None, True),     # two k-splits, four workgroups per head: dS as tagged words
-    (256, 5, 2, False),
+    (256, 3, None, True),     # split R, one workgroup per (head, row)
+    (256, 5, None, False),
+    (256, 3, "x", True),      # two k-splits, four workgroups per head: dS as tagged words
+    (256, 5, "x2", False),
 ])
 def test_gru_backward_small(Dh, B, bt, final):
+    if isinstance(bt, str):
+        os.environ["RNN355_REC_WIDE"] = "0"
+        bt = int(bt[1:]) if len(bt) > 1 else None
     if bt is not None:
         os.environ["RNN355_REC_BT"] = str(bt)
     d = synth.Dims(T=17, B=B, Din=64, NH=2, Dh=Dh)
@@ -157,7 +172,9 @@ def test_gru_backward_small(Dh, B, bt, final):
         assert e <= TOL, (k, e)
 
 
-def test_gru_backward_bitwise_repeatable():
+@pytest.mark.parametrize("wide", ["1", "0"])
+def test_gru_backward_bitwise_repeatable(wide):
+    os.environ["RNN355_REC_WIDE"] = wide
     d = synth.Dims(T=13, B=3, Din=32, NH=2, Dh=256)
     c = synth.make_case("gru", d, "bf16", 9600, h0_var=0.2, backward=True)
     a, b = gpu_bwd_gru(c), gpu_bwd_gru(c)
