@@ -44,14 +44,22 @@ NUM_CU = 256
 CU_BF16_TFLOPS = PEAK_BF16_TFLOPS / NUM_CU
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "gru_recurrence_amd", "csrc", f)
-                  for f in ("rec_fwd.hip", "gates.h", "common.h", "kernels.h")]
+                  for f in ("rec_fwd.hip", "gates.h", "common.h")]
+KERNEL_ARGS_HEADER = os.path.join(ROOT, "gru_recurrence_amd", "csrc", "kernels.h")
 
 
 def kernel_source_hash() -> str:
+    """Hash of what the recurrence kernel is compiled from: its source file,
+    the device helpers it includes and its argument block (struct RecArgs);
+    other declarations in the kernels header do not change its code."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
         with open(p, "rb") as f:
             h.update(f.read())
+    with open(KERNEL_ARGS_HEADER) as f:
+        hdr = f.read()
+    i = hdr.index("struct RecArgs {")
+    h.update(hdr[i:hdr.index("};", i) + 2].encode())
     return h.hexdigest()[:16]
 
 
