@@ -133,6 +133,61 @@ def gru_fwd(x, W, R, b, h0=None, *, NH: int, Dh: int, chain_mask=None):
     return out
 
 
+def round_bf16(a):
+    """Round to bfloat16 (nearest, ties to even) and widen back to float64:
+    first to float32 (numpy rounds to nearest even), then the float32 bit
+    pattern to its top 16 bits with the same rule.  NaN is not expected."""
+    f = np.ascontiguousarray(np.asarray(a, np.float64).astype(np.float32))
+    u = f.view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def _stack(cell, x, Ws, Rs, bs, h0s, c0s, NH, Dh, bf16_between, chain_mask):
+    L = len(Ws)
+    inp = _d(x)
+    hT, cT, last = [], [], None
+    for layer in range(L):
+        h0 = None if h0s is None else h0s[layer]
+        if cell == "lstm":
+            c0 = None if c0s is None else c0s[layer]
+            r = lstm_fwd(inp, Ws[layer], Rs[layer], bs[layer], h0, c0, NH=NH, Dh=Dh,
+                         chain_mask=chain_mask)
+            cT.append(r["cT"])
+        else:
+            r = gru_fwd(inp, Ws[layer], Rs[layer], bs[layer], h0, NH=NH, Dh=Dh,
+                        chain_mask=chain_mask)
+        hT.append(r["hT"])
+        last = r
+        if layer + 1 < L:
+            inp = round_bf16(r["h_seq"]) if bf16_between else r["h_seq"]
+    out = dict(h_seq=last["h_seq"], hT=np.stack(hT))
+    if cell == "lstm":
+        out["c_seq"] = last["c_seq"]
+        out["cT"] = np.stack(cT)
+    return out
+
+
+def lstm_stack_fwd(x, Ws, Rs, bs, h0=None, c0=None, *, NH: int, Dh: int,
+                   bf16_between: bool = False, chain_mask=None):
+    """Stacked multi-head LSTM: layer l > 0 takes layer l-1's sequence h_1..h_T
+    as its input (Ws[l] is [NH*Dh][NH*4*Dh]); every layer has its own W, R, b
+    and initial state (h0, c0: [L][B][H] or None).  With bf16_between the
+    layer input is rounded to bfloat16 as the first layer's x is in a bf16
+    run.  Returns the last layer's h_seq, c_seq and every layer's hT, cT
+    ([L][B][H]).  A chain_mask must keep whole batch rows (all heads), since a
+    layer's input row depends on every head of the layer below.
+    Inter-layer parallelism of multi-layer RNNs: blog.hotdry.top 2025-09-21,
+    the list of framework-level optimisations, first item."""
+    return _stack("lstm", x, Ws, Rs, bs, h0, c0, NH, Dh, bf16_between, chain_mask)
+
+
+def gru_stack_fwd(x, Ws, Rs, bs, h0=None, *, NH: int, Dh: int, bf16_between: bool = False,
+                  chain_mask=None):
+    """Stacked multi-head GRU, as lstm_stack_fwd (no cell state)."""
+    return _stack("gru", x, Ws, Rs, bs, h0, None, NH, Dh, bf16_between, chain_mask)
+
+
 def param_grads(x, W, h0, h_seq, dG, dS, *, NH: int, Dh: int, G: int,
                 want=("dx", "dW", "dR", "db")):
     """dx, dW, dR, db from the per-step gate gradients (see oracle.c)."""
