@@ -164,7 +164,9 @@ def main():
 
     w = synth.WORKLOADS[args.workload]
     d = w.dims
-    c = synth.workload_case(w)
+    stacked = w.layers > 1
+    cs = synth.workload_stack_case(w) if stacked else [synth.workload_case(w)]
+    c = cs[0]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
@@ -206,11 +208,33 @@ def main():
     fop = g.OP_FWD_LSTM if lstm else g.OP_FWD_GRU
     ws_f = torch.empty(g.workspace_size(fop, dims, dtc), dtype=torch.uint8, device=dev)
     fplan = g.plan_describe(fop, dims, dtc)
+    if stacked:
+        # every layer's weights; layer 0 takes x, layer l > 0 the h of layer l-1
+        def layer_dev(ci, name):
+            if name in ci.bits:
+                return torch.from_numpy(ci.bits[name].view(np.int16).copy()).view(
+                    torch.bfloat16).to(dev)
+            return torch.from_numpy(np.ascontiguousarray(ci.vals[name])).to(dev)
+        L = w.layers
+        Ws = [layer_dev(ci, "W") for ci in cs]
+        Rs = [layer_dev(ci, "R") for ci in cs]
+        bs = [layer_dev(ci, "b") for ci in cs]
+        h0s = torch.stack([layer_dev(ci, "h0") for ci in cs])
+        c0s = torch.stack([layer_dev(ci, "c0") for ci in cs]) if lstm else None
+        outs_s = dict(h_seq=outs["h_seq"], c_seq=outs["c_seq"],
+                      hT=torch.empty((L, d.B, H), dtype=f32, device=dev),
+                      cT=torch.empty((L, d.B, H), dtype=f32, device=dev))
+        ws_f = torch.empty(g.workspace_size_stack(fop, dims, L, dtc), dtype=torch.uint8,
+                           device=dev)
 
     def step(evs=None):
         if evs is not None:
             evs[0].record(stream)
-        if lstm:
+        if stacked and lstm:
+            g.lstm_stack_fwd(x, Ws, Rs, bs, h0s, c0s, ws=ws_f, out=outs_s, stream=stream)
+        elif stacked:
+            g.gru_stack_fwd(x, Ws, Rs, bs, h0s, ws=ws_f, out=outs_s, stream=stream)
+        elif lstm:
             g.lstm_fwd(x, W, R, b, h0, c0, ws=ws_f, out=outs, stream=stream)
         else:
             g.gru_fwd(x, W, R, b, h0, ws=ws_f, out=outs, stream=stream)
@@ -278,7 +302,7 @@ def main():
     ms_step = 1e3 * wall / args.steps
     # forward + backward: the reverse sweep's dA R^T products add the same
     # recurrent flops again
-    rflops = recurrent_flops(w) * (2 if backward else 1)
+    rflops = recurrent_flops(w) * (2 if backward else 1) * w.layers
     value = rflops / (ms_step * 1e-3) / 1e12
     achieved = recurrent_flops(w) / (rec_avg * 1e-3) / 1e12
     gemm_flops = 2.0 * d.T * d.B * d.Din * N
@@ -297,7 +321,8 @@ def main():
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic (seeded SplitMix64/Box-Muller, bf16 RNE), random-init weights",
         "config": {"workload": w.name, "cell": w.cell, "T": d.T, "B": d.B, "NH": d.NH,
-                   "Dh": d.Dh, "Din": d.Din, "hidden": H, "parallelism": "single GPU"},
+                   "Dh": d.Dh, "Din": d.Din, "hidden": H, "layers": w.layers,
+                   "parallelism": "single GPU"},
         "time_steps_per_s": round(d.T / (ms_step * 1e-3), 1),
         "forward_call": {"avg_ms": round(float(np.mean(fwd_ms)), 4), "plan": fplan},
         "recurrence": {"avg_launch_ms": round(rec_avg, 4), "tflops": round(achieved, 3),
@@ -321,7 +346,11 @@ def main():
         bwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
         out["backward"] = {"avg_call_ms": round(float(np.mean(bwd_ms)), 4),
                            "note": "rnn_bwd_lstm: recompute GEMMs, reverse sweep, dx/dW/dR GEMMs"}
-    if not args.no_cpu and lstm:
+    if stacked:
+        out["forward_call"]["note"] = ("rnn_fwd_%s_stack over %d layers; the recurrence and "
+                                       "input projection entries time layer 0's kernels"
+                                       % (w.cell, w.layers))
+    if not args.no_cpu and lstm and not stacked:
         out["cpu_baseline"] = cpu_baseline(w, c, args.cpu_budget)
     print(json.dumps(out), flush=True)
 

@@ -27,7 +27,7 @@ OP_FWD_LSTM, OP_FWD_GRU, OP_BWD_LSTM, OP_BWD_GRU, OP_REC_LSTM, OP_REC_GRU = rang
 EXPORTS = ("rnn_status_str", "rnn_workspace_size", "rnn_plan_describe", "rnn_input_proj",
            "rnn_input_proj_t",
            "rnn_rec_lstm", "rnn_rec_gru", "rnn_fwd_lstm", "rnn_fwd_gru", "rnn_bwd_lstm",
-           "rnn_bwd_gru",
+           "rnn_bwd_gru", "rnn_workspace_size_stack", "rnn_fwd_lstm_stack", "rnn_fwd_gru_stack",
            "rnn_workspace_status")
 
 
@@ -71,9 +71,13 @@ def load(path: Optional[str] = None):
     lib.rnn_bwd_lstm.argtypes = [D, I] + [P] * 17 + [P, S, P]
     lib.rnn_bwd_gru.argtypes = [D, I] + [P] * 13 + [P, S, P]
     lib.rnn_workspace_status.argtypes = [P, S, P]
+    lib.rnn_workspace_size_stack.restype = S
+    lib.rnn_workspace_size_stack.argtypes = [I, D, I, I]
+    lib.rnn_fwd_lstm_stack.argtypes = [D, I, I, P, P, P, P, P, P, P, P, P, P, P, S, P]
+    lib.rnn_fwd_gru_stack.argtypes = [D, I, I, P, P, P, P, P, P, P, P, S, P]
     for f in ("rnn_plan_describe", "rnn_input_proj", "rnn_input_proj_t", "rnn_rec_lstm", "rnn_rec_gru",
               "rnn_fwd_lstm", "rnn_fwd_gru", "rnn_bwd_lstm", "rnn_bwd_gru",
-              "rnn_workspace_status"):
+              "rnn_fwd_lstm_stack", "rnn_fwd_gru_stack", "rnn_workspace_status"):
         getattr(lib, f).restype = I
     _lib = lib
     return lib
@@ -254,6 +258,79 @@ def gru_fwd(x, W, R, b=None, h0=None, *, with_seq: bool = True, ws=None, out=Non
                            _ptr(ws, "ws"), ws.numel(), _stream(stream))
     _check(s, "rnn_fwd_gru")
     return h_seq, hT
+
+
+def workspace_size_stack(op: int, dims: Dims, L: int, dtype_code: int) -> int:
+    return int(load().rnn_workspace_size_stack(op, ctypes.byref(dims), int(L), dtype_code))
+
+
+def _stack(cell, x, Ws, Rs, bs, h0, c0, with_seq, ws, out, stream):
+    torch = _torch()
+    L = len(Ws)
+    if len(Rs) != L or (bs is not None and len(bs) != L):
+        raise ValueError("Ws, Rs and bs need one entry per layer")
+    G = 4 if cell == "lstm" else 3
+    d, dt, N = _common(x, Ws[0], Rs[0], G)
+    H = d.NH * d.Dh
+    f32 = torch.float32
+    dev = x.device
+    for layer in range(1, L):
+        if tuple(Ws[layer].shape) != (H, N) or Ws[layer].dtype != Ws[0].dtype:
+            raise ValueError("W[%d] must be [%d, %d] %s" % (layer, H, N, Ws[0].dtype))
+        if tuple(Rs[layer].shape) != tuple(Rs[0].shape) or Rs[layer].dtype != Rs[0].dtype:
+            raise ValueError("R[%d] must match R[0]" % layer)
+    P = ctypes.c_void_p
+    Wp = (P * L)(*[_ptr(w, "W[%d]" % i) for i, w in enumerate(Ws)])
+    Rp = (P * L)(*[_ptr(r, "R[%d]" % i) for i, r in enumerate(Rs)])
+    bp = None if bs is None else (P * L)(*[_ptr(v, "b[%d]" % i, f32, (N,), True)
+                                          for i, v in enumerate(bs)])
+    out = {} if out is None else out
+    h_seq = out.get("h_seq") if with_seq else None
+    if with_seq and h_seq is None:
+        h_seq = torch.empty((d.T, d.B, H), dtype=f32, device=dev)
+    hT = out.get("hT")
+    hT = torch.empty((L, d.B, H), dtype=f32, device=dev) if hT is None else hT
+    op = OP_FWD_LSTM if cell == "lstm" else OP_FWD_GRU
+    need = workspace_size_stack(op, d, L, dt)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    if cell == "lstm":
+        c_seq = out.get("c_seq") if with_seq else None
+        if with_seq and c_seq is None:
+            c_seq = torch.empty((d.T, d.B, H), dtype=f32, device=dev)
+        cT = out.get("cT")
+        cT = torch.empty((L, d.B, H), dtype=f32, device=dev) if cT is None else cT
+        s = load().rnn_fwd_lstm_stack(ctypes.byref(d), L, dt, _ptr(x, "x"), Wp, Rp, bp,
+                                      _ptr(h0, "h0", f32, (L, d.B, H), True),
+                                      _ptr(c0, "c0", f32, (L, d.B, H), True),
+                                      _ptr(h_seq, "h_seq", f32, None, True),
+                                      _ptr(c_seq, "c_seq", f32, None, True),
+                                      _ptr(hT, "hT", f32, (L, d.B, H)),
+                                      _ptr(cT, "cT", f32, (L, d.B, H)),
+                                      _ptr(ws, "ws"), ws.numel(), _stream(stream))
+        _check(s, "rnn_fwd_lstm_stack")
+        return h_seq, c_seq, hT, cT
+    s = load().rnn_fwd_gru_stack(ctypes.byref(d), L, dt, _ptr(x, "x"), Wp, Rp, bp,
+                                 _ptr(h0, "h0", f32, (L, d.B, H), True),
+                                 _ptr(h_seq, "h_seq", f32, None, True),
+                                 _ptr(hT, "hT", f32, (L, d.B, H)),
+                                 _ptr(ws, "ws"), ws.numel(), _stream(stream))
+    _check(s, "rnn_fwd_gru_stack")
+    return h_seq, hT
+
+
+def lstm_stack_fwd(x, Ws, Rs, bs=None, h0=None, c0=None, *, with_seq: bool = True, ws=None,
+                   out=None, stream=None):
+    """Stacked multi-head LSTM: Ws, Rs, bs are per-layer lists (Ws[0] [Din,N],
+    Ws[l>0] [H,N]); h0, c0 [L,B,H].  Returns (h_seq, c_seq) of the last layer
+    and hT, cT [L,B,H] of every layer."""
+    return _stack("lstm", x, Ws, Rs, bs, h0, c0, with_seq, ws, out, stream)
+
+
+def gru_stack_fwd(x, Ws, Rs, bs=None, h0=None, *, with_seq: bool = True, ws=None, out=None,
+                  stream=None):
+    """Stacked multi-head GRU.  Returns (h_seq of the last layer, hT [L,B,H])."""
+    return _stack("gru", x, Ws, Rs, bs, h0, None, with_seq, ws, out, stream)
 
 
 def rec_lstm(gx, R, h0=None, c0=None, *, with_seq=True, ws=None, out=None, stream=None):

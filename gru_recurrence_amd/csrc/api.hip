@@ -20,6 +20,7 @@ namespace {
 // of the multi-CU kernel, then the operation's own regions, each 256-byte
 // aligned.
 constexpr size_t kHeader = 4096;
+constexpr int kMaxLayers = 64;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
@@ -344,6 +345,61 @@ rnn_status forward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, con
     return rec_fwd(cell, d, dt, gx, R, h0, c0, h_seq, c_seq, hT, cT, ws, rt, s);
 }
 
+// Stacked layers: layer l > 0 reads layer l-1's h_1..h_T (rounded to bf16
+// in bf16 runs, as x is).  Workspace: one forward workspace sized for the
+// larger input width, two float32 sequence buffers the layers alternate
+// between, and the bf16 copy of the layer input.
+struct StackLayout {
+    size_t fwd, hbuf, xb, total;
+};
+StackLayout stack_layout(const rnn_dims *d, int G, rnn_dtype dt) {
+    StackLayout L{};
+    rnn_dims dm = *d;
+    const int H = d->NH * d->Dh;
+    if (H > dm.Din) dm.Din = H;
+    const size_t seq = (size_t)d->T * d->B * H;
+    L.fwd = align_up(kHeader + xchg_bytes(&dm) + gx_bytes(&dm, G) + ready_bytes(&dm) +
+                     wt_bytes(&dm, G) + rt_fwd_bytes(&dm, dt, G));
+    L.hbuf = L.fwd;
+    L.xb = L.hbuf + 2 * align_up(sizeof(float) * seq);
+    L.total = L.xb + (dt == RNN_BF16 ? align_up(sizeof(uint16_t) * seq) : 0);
+    return L;
+}
+
+rnn_status forward_stack(int cell, const rnn_dims *d, int L, rnn_dtype dt, const void *x,
+                         const void *const *W, const void *const *R, const float *const *b,
+                         const float *h0, const float *c0, float *h_seq, float *c_seq,
+                         float *hT, float *cT, void *ws, hipStream_t s) {
+    const int G = gates_of_cell(cell), H = d->NH * d->Dh;
+    const long BH = (long)d->B * H, seq = (long)d->T * BH;
+    const StackLayout SL = stack_layout(d, G, dt);
+    char *base = (char *)ws;
+    float *hb[2] = {(float *)(base + SL.hbuf),
+                    (float *)(base + SL.hbuf + align_up(sizeof(float) * seq))};
+    uint16_t *xb = dt == RNN_BF16 ? (uint16_t *)(base + SL.xb) : nullptr;
+    const void *xin = x;
+    for (int l = 0; l < L; ++l) {
+        rnn_dims dl = *d;
+        if (l > 0) dl.Din = H;
+        const bool last = l == L - 1;
+        float *hs = last ? h_seq : hb[l & 1];
+        float *cs = last ? c_seq : nullptr;
+        rnn_status st = forward(cell, &dl, dt, xin, W[l], R[l], b ? b[l] : nullptr,
+                                h0 ? h0 + l * BH : nullptr, c0 ? c0 + l * BH : nullptr, hs, cs,
+                                hT + l * BH, cT ? cT + l * BH : nullptr, ws, s);
+        if (st != RNN_OK) return st;
+        if (!last) {
+            if (xb) {
+                if (launch_hprev_bf16(nullptr, hs, xb, 0, seq, s) != hipSuccess) return RNN_ERR_HIP;
+                xin = xb;
+            } else {
+                xin = hs;
+            }
+        }
+    }
+    return RNN_OK;
+}
+
 // Backpropagation through time (pointers validated by the entry points).
 // 1. h_{t-1} as bf16, the gate inputs recomputed for all t at once: LSTM A =
 //    x W + b + h_{t-1} R; GRU Gx = x W + b and S = h_{t-1} R apart.
@@ -601,6 +657,61 @@ rnn_status rnn_fwd_gru(const rnn_dims *d, rnn_dtype dt, const void *x, const voi
     if (!gemm_shape_ok(d->Din, N, dt) || !rec_supported(kGRU, d, dt)) return RNN_ERR_UNSUPPORTED;
     if (!ws || ws_bytes < rnn_workspace_size(RNN_OP_FWD_GRU, d, dt)) return RNN_ERR_WORKSPACE;
     return forward(kGRU, d, dt, x, W, R, b, h0, nullptr, h_seq, nullptr, hT, nullptr, ws, stream);
+}
+
+size_t rnn_workspace_size_stack(rnn_op op, const rnn_dims *d, int L, rnn_dtype dt) {
+    if (!dims_ok(d) || !dtype_ok(dt) || L < 1 || L > kMaxLayers) return 0;
+    if (op != RNN_OP_FWD_LSTM && op != RNN_OP_FWD_GRU) return 0;
+    return stack_layout(d, gates_of_op(op), dt).total;
+}
+
+// Common checks of the stack entry points.  W, R, b are host arrays of L
+// device pointers (b may be NULL, or hold NULLs).
+static rnn_status stack_args_ok(int cell, const rnn_dims *d, int L, rnn_dtype dt, const void *x,
+                                const void *const *W, const void *const *R,
+                                const float *const *b, const void *const *more, int nmore,
+                                void *ws, size_t ws_bytes) {
+    if (!dims_ok(d) || !dtype_ok(dt) || L < 1 || L > kMaxLayers || !x || !W || !R)
+        return RNN_ERR_INVALID_ARG;
+    for (int i = 0; i < nmore; ++i)
+        if (!aligned16(more[i])) return RNN_ERR_INVALID_ARG;
+    if (!aligned16(x)) return RNN_ERR_INVALID_ARG;
+    const int G = gates_of_cell(cell), H = d->NH * d->Dh, N = d->NH * G * d->Dh;
+    for (int l = 0; l < L; ++l) {
+        if (!W[l] || !R[l] || !aligned16(W[l]) || !aligned16(R[l])) return RNN_ERR_INVALID_ARG;
+        if (b && !aligned16(b[l])) return RNN_ERR_INVALID_ARG;
+        if (!gemm_shape_ok(l == 0 ? d->Din : H, N, dt)) return RNN_ERR_UNSUPPORTED;
+    }
+    rnn_dims dh = *d;
+    dh.Din = H;
+    if (!rec_supported(cell, d, dt) || !rec_supported(cell, &dh, dt)) return RNN_ERR_UNSUPPORTED;
+    const rnn_op op = cell == kLSTM ? RNN_OP_FWD_LSTM : RNN_OP_FWD_GRU;
+    if (!ws || ws_bytes < rnn_workspace_size_stack(op, d, L, dt)) return RNN_ERR_WORKSPACE;
+    return RNN_OK;
+}
+
+rnn_status rnn_fwd_lstm_stack(const rnn_dims *d, int L, rnn_dtype dt, const void *x,
+                              const void *const *W, const void *const *R, const float *const *b,
+                              const float *h0, const float *c0, float *h_seq, float *c_seq,
+                              float *hT, float *cT, void *ws, size_t ws_bytes,
+                              hipStream_t stream) {
+    if (!hT || !cT) return RNN_ERR_INVALID_ARG;
+    const void *more[] = {h0, c0, h_seq, c_seq, hT, cT, ws};
+    const rnn_status st = stack_args_ok(kLSTM, d, L, dt, x, W, R, b, more, 7, ws, ws_bytes);
+    if (st != RNN_OK) return st;
+    return forward_stack(kLSTM, d, L, dt, x, W, R, b, h0, c0, h_seq, c_seq, hT, cT, ws, stream);
+}
+
+rnn_status rnn_fwd_gru_stack(const rnn_dims *d, int L, rnn_dtype dt, const void *x,
+                             const void *const *W, const void *const *R, const float *const *b,
+                             const float *h0, float *h_seq, float *hT, void *ws,
+                             size_t ws_bytes, hipStream_t stream) {
+    if (!hT) return RNN_ERR_INVALID_ARG;
+    const void *more[] = {h0, h_seq, hT, ws};
+    const rnn_status st = stack_args_ok(kGRU, d, L, dt, x, W, R, b, more, 4, ws, ws_bytes);
+    if (st != RNN_OK) return st;
+    return forward_stack(kGRU, d, L, dt, x, W, R, b, h0, nullptr, h_seq, nullptr, hT, nullptr, ws,
+                         stream);
 }
 
 rnn_status rnn_bwd_lstm(const rnn_dims *d, rnn_dtype dt, const void *x, const void *W,

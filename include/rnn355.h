@@ -183,6 +183,35 @@ rnn_status rnn_fwd_gru(const rnn_dims *d, rnn_dtype dt,
                        void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Stacked layers (blog.hotdry.top 2025-09-21, the list of framework-level
+ * optimisations, first item: multi-layer RNNs).  Layer l > 0 takes layer
+ * l-1's output sequence h_1..h_T as its input x (width H = NH*Dh; in bf16
+ * runs rounded to bf16, nearest-even, as x is); every layer has its own
+ * weights and initial state:
+ *   W, R, b: host arrays of L device pointers; W[0] is [Din][N], W[l>0] is
+ *            [H][N]; R[l] as in rnn_fwd_lstm; b itself or any b[l] may be NULL.
+ *   h0, c0:  [L][B][H] float32 or NULL (zeros).
+ *   h_seq, c_seq: the last layer's [T][B][H], may be NULL.
+ *   hT, cT:  every layer's final states, [L][B][H], required.
+ * 1 <= L <= 64.  The layers run one after the other on `stream`, each as
+ * rnn_fwd_lstm would (same kernels and plans); intermediate sequences live
+ * in the workspace (rnn_workspace_size_stack).  Errors as rnn_fwd_lstm.
+ */
+size_t rnn_workspace_size_stack(rnn_op op /* RNN_OP_FWD_LSTM or RNN_OP_FWD_GRU */,
+                                const rnn_dims *d, int L, rnn_dtype dt);
+rnn_status rnn_fwd_lstm_stack(const rnn_dims *d, int L, rnn_dtype dt, const void *x,
+                              const void *const *W, const void *const *R,
+                              const float *const *b, const float *h0, const float *c0,
+                              float *h_seq, float *c_seq, float *hT, float *cT,
+                              void *ws, size_t ws_bytes, hipStream_t stream);
+/* Stacked GRU layers, as rnn_fwd_lstm_stack without cell states. */
+rnn_status rnn_fwd_gru_stack(const rnn_dims *d, int L, rnn_dtype dt, const void *x,
+                             const void *const *W, const void *const *R,
+                             const float *const *b, const float *h0,
+                             float *h_seq, float *hT,
+                             void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Multi-head LSTM backpropagation through time for the loss
  *   L = sum_t dh_seq[t] . h_t + dhT . h_T + dcT . c_T
  * given the forward's h_seq and c_seq (from rnn_fwd_lstm on the same inputs).

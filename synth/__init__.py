@@ -121,6 +121,7 @@ class Workload:
     c0_var: float = 0.0
     backward: bool = False
     dH_var: float = 1.0
+    layers: int = 1              # stacked layers (layer l > 0 reads layer l-1's h)
     note: str = ""
 
 
@@ -144,6 +145,10 @@ WORKLOADS: Dict[str, Workload] = {
         5, "lstm_fwdbwd_b16_nh4_dh256", "lstm", Dims(T=1024, B=16, Din=1024, NH=4, Dh=256), "bf16",
         bias="forget+1", backward=True,
         note="multi-head LSTM forward plus BPTT backward"),
+    "lstm_stack2_b16_nh6_dh128": Workload(
+        6, "lstm_stack2_b16_nh6_dh128", "lstm", Dims(T=1024, B=16, Din=768, NH=6, Dh=128), "bf16",
+        bias="forget+1", layers=2,
+        note="two stacked layers of the multi-head LSTM (second layer's W is [H][N])"),
 }
 
 BY_ID = {w.wid: w for w in WORKLOADS.values()}
@@ -227,6 +232,20 @@ def make_case(cell: str, dims: Dims, dtype: str, seed_base: int, *,
     return c
 
 
+def make_stack_case(cell: str, dims: Dims, layers: int, dtype: str, seed_base: int,
+                    **kw) -> list:
+    """Inputs of a stack of ``layers`` layers: one Case per layer.  Layer 0 is
+    make_case(dims); layer l > 0 has input width H (its x is never used) and
+    seeds seed_base + 100*l; its W variance defaults to 1/H."""
+    out = [make_case(cell, dims, dtype, seed_base, **kw)]
+    for layer in range(1, layers):
+        d = Dims(dims.T, dims.B, dims.H, dims.NH, dims.Dh)
+        kl = dict(kw)
+        kl.pop("w_var", None)
+        out.append(make_case(cell, d, dtype, seed_base + 100 * layer, **kl))
+    return out
+
+
 def workload_case(w: Workload, dims: Optional[Dims] = None) -> Case:
     """Inputs of a named workload, optionally at other dims (same recipe)."""
     d = dims or w.dims
@@ -234,3 +253,10 @@ def workload_case(w: Workload, dims: Optional[Dims] = None) -> Case:
                      w_var=w.w_var, r_var=w.r_var, bias=w.bias,
                      h0_var=w.h0_var, c0_var=w.c0_var, backward=w.backward,
                      dH_var=w.dH_var)
+
+
+def workload_stack_case(w: Workload) -> list:
+    """Per-layer inputs of a stacked workload (same recipe per layer)."""
+    return make_stack_case(w.cell, w.dims, w.layers, w.dtype, 1000 * w.wid, x_var=w.x_var,
+                           w_var=w.w_var, r_var=w.r_var, bias=w.bias, h0_var=w.h0_var,
+                           c0_var=w.c0_var)

@@ -189,3 +189,39 @@ def test_plans_of_the_workloads(monkeypatch):
     big = g.Dims(64, 16, 64, 16, 128)
     p = g.plan_describe(g.OP_FWD_LSTM, big, g.RNN_BF16)
     assert " wg=256 " in p and "input_proj=serial" in p
+
+
+def test_stack_entry_points_reject_before_launch():
+    lib = g.load()
+    d = g.Dims(8, 2, 32, 1, 32)
+    P3 = ctypes.c_void_p * 3
+    W, R = P3(*[FAKE + 256 * i for i in range(3)]), P3(*[FAKE + 4096 + 256 * i for i in range(3)])
+    ok = [_p(FAKE + 65536 + 256 * i) for i in range(8)]
+    big = 1 << 30
+    ws1 = g.workspace_size_stack(g.OP_FWD_LSTM, d, 1, g.RNN_BF16)
+    ws3 = g.workspace_size_stack(g.OP_FWD_LSTM, d, 3, g.RNN_BF16)
+    assert ws1 > 0 and ws3 == ws1  # the buffers are reused layer after layer
+    assert g.workspace_size_stack(g.OP_FWD_LSTM, d, 0, g.RNN_BF16) == 0
+    assert g.workspace_size_stack(g.OP_FWD_LSTM, d, 65, g.RNN_BF16) == 0
+    assert g.workspace_size_stack(g.OP_BWD_LSTM, d, 2, g.RNN_BF16) == 0
+
+    def lstm(dd, L, W_, R_, hT=ok[4], ws=_p(FAKE), nb=big, x=ok[0]):
+        return lib.rnn_fwd_lstm_stack(ctypes.byref(dd), L, g.RNN_BF16, x, W_, R_, None, None,
+                                      None, ok[2], ok[3], hT, ok[5], ws, nb, None)
+
+    assert lstm(d, 0, W, R) == g.RNN_ERR_INVALID_ARG
+    assert lstm(d, 65, W, R) == g.RNN_ERR_INVALID_ARG
+    assert lstm(d, 3, W, R, x=None) == g.RNN_ERR_INVALID_ARG
+    assert lstm(d, 3, None, R) == g.RNN_ERR_INVALID_ARG
+    assert lstm(d, 3, W, R, hT=None) == g.RNN_ERR_INVALID_ARG
+    holed = P3(FAKE, 0, FAKE + 512)
+    assert lstm(d, 3, holed, R) == g.RNN_ERR_INVALID_ARG
+    assert lstm(d, 2, holed, R) == g.RNN_ERR_INVALID_ARG
+    misal = P3(FAKE, FAKE + 6, FAKE + 512)
+    assert lstm(d, 3, misal, R) == g.RNN_ERR_INVALID_ARG
+    assert lstm(d, 3, W, R, ws=None, nb=0) == g.RNN_ERR_WORKSPACE
+    assert lstm(d, 3, W, R, nb=ws3 - 1) == g.RNN_ERR_WORKSPACE
+    # Din % 8 != 0 rejects layer 0's projection
+    assert lstm(g.Dims(8, 2, 30, 1, 32), 2, W, R) == g.RNN_ERR_UNSUPPORTED
+    assert lib.rnn_fwd_gru_stack(ctypes.byref(d), 2, g.RNN_BF16, ok[0], W, R, None, None, None,
+                                 None, _p(FAKE), big, None) == g.RNN_ERR_INVALID_ARG
