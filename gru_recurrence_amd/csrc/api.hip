@@ -233,9 +233,11 @@ rnn_status input_proj(int M, int K, int N, rnn_dtype dt, const void *x, const vo
 }
 
 // rt: workspace region for R^T (rt_fwd_bytes), used by the Dh = 256 kernel.
+// clear_status: zero the status word first (a stacked layer after the
+// first keeps what earlier layers reported).
 rnn_status rec_fwd(int cell, const rnn_dims *d, rnn_dtype dt, const float *gx, const void *R,
                    const float *h0, const float *c0, float *h_seq, float *c_seq, float *hT,
-                   float *cT, void *ws, uint16_t *rt, hipStream_t s) {
+                   float *cT, void *ws, uint16_t *rt, hipStream_t s, bool clear_status = true) {
     const Choice ch = choose(cell, d, dt, device_cus());
     if (!ch.ok) return RNN_ERR_UNSUPPORTED;
     RecArgs a{};
@@ -249,7 +251,7 @@ rnn_status rec_fwd(int cell, const rnn_dims *d, rnn_dtype dt, const float *gx, c
         // R^T per head; the same launch clears the status words
         const int G = gates_of_cell(cell);
         e = launch_transpose_bf16((const uint16_t *)R, rt, d->Dh, G * d->Dh, d->NH, s,
-                                  (unsigned *)ws, 64);
+                                  clear_status ? (unsigned *)ws : nullptr, 64);
         if (e != hipSuccess) return RNN_ERR_HIP;
         a.BT = 1;
         e = launch_rec_wide(cell, ch.wide, a, rt, s);
@@ -261,7 +263,7 @@ rnn_status rec_fwd(int cell, const rnn_dims *d, rnn_dtype dt, const float *gx, c
         m.flag = (unsigned *)ws;
         m.xg = (unsigned long long *)((char *)ws + kHeader);
         m.spin_limit = spin_limit();
-        e = launch_rec_mc(cell, ch.mc, m, s);
+        e = launch_rec_mc(cell, ch.mc, m, s, clear_status);
     } else {
         a.BT = ch.rec.BT;
         e = launch_rec_fwd(cell, ch.rec, a, dt == RNN_BF16, s);
@@ -297,7 +299,8 @@ bool pipelined(const Choice &ch, const rnn_dims *d, rnn_dtype dt, int cus) {
 // projection, then the recurrence.  Results are bitwise the same.
 rnn_status forward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, const void *W,
                    const void *R, const float *b, const float *h0, const float *c0,
-                   float *h_seq, float *c_seq, float *hT, float *cT, void *ws, hipStream_t s) {
+                   float *h_seq, float *c_seq, float *hT, float *cT, void *ws, hipStream_t s,
+                   bool clear_status = true) {
     const int G = cell == kLSTM ? 4 : 3;
     const int N = d->NH * G * d->Dh, M = d->T * d->B;
     float *gx = (float *)((char *)ws + kHeader + xchg_bytes(d));
@@ -311,8 +314,8 @@ rnn_status forward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, con
         auto ok = [](hipError_t e) { return e == hipSuccess; };
         // W^T for the k-major contraction; the same launch zeroes the status
         // words of the header and the panel counters
-        if (!ok(launch_transpose_bf16((const uint16_t *)W, wt, d->Din, N, 1, s, (unsigned *)ws, 64,
-                                      ready, panels)))
+        if (!ok(launch_transpose_bf16((const uint16_t *)W, wt, d->Din, N, 1, s,
+                                      clear_status ? (unsigned *)ws : nullptr, 64, ready, panels)))
             return RNN_ERR_HIP;
         GemmArgs g{};
         g.M = M; g.N = N; g.K = d->Din;
@@ -339,18 +342,44 @@ rnn_status forward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, con
         if (n_gemm < 8) n_gemm = (int)std::min<long>(8, tiles);
         return ok(launch_fwd_fused(cell, ch.rec, a, g, n_gemm, s)) ? RNN_OK : RNN_ERR_HIP;
     }
-    rnn_status st = input_proj(M, d->Din, N, dt, x, W, b, gx, (uint32_t *)ws, s, nullptr, wt);
+    rnn_status st = input_proj(M, d->Din, N, dt, x, W, b, gx,
+                               clear_status ? (uint32_t *)ws : nullptr, s, nullptr, wt);
     if (st != RNN_OK) return st;
     uint16_t *rt = (uint16_t *)((char *)wt + wt_bytes(d, G));
-    return rec_fwd(cell, d, dt, gx, R, h0, c0, h_seq, c_seq, hT, cT, ws, rt, s);
+    return rec_fwd(cell, d, dt, gx, R, h0, c0, h_seq, c_seq, hT, cT, ws, rt, s, clear_status);
 }
 
 // Stacked layers: layer l > 0 reads layer l-1's h_1..h_T (rounded to bf16
-// in bf16 runs, as x is).  Workspace: one forward workspace sized for the
-// larger input width, two float32 sequence buffers the layers alternate
-// between, and the bf16 copy of the layer input.
+// in bf16 runs, as x is).
+//
+// Two layers at a time share one launch (launch_fwd_stack2) where the
+// one-row MFMA recurrence at Dh = 128 leaves at least 32 CUs beside two
+// copies of itself: layer l's projection runs first on the whole chip, then
+// layer l's recurrence, layer l+1's projection (on the CUs left) and layer
+// l+1's recurrence run side by side, each 256-row tile of the projection
+// starting once layer l has produced its steps.  Otherwise the layers run
+// in turn.  RNN355_STACK_OVERLAP=0 turns the overlap off.  Both ways give
+// the same bits: the same kernels sum in the same order.
+int stack_overlap_wgs(const Choice &ch, const rnn_dims *dh, rnn_dtype dt, int cus) {
+    const char *e = getenv("RNN355_STACK_OVERLAP");
+    if (e && e[0] == '0') return 0;
+    if (dt != RNN_BF16 || !ch.ok || ch.use_mc || ch.use_wide || ch.rec.kind != kRecMfma ||
+        ch.rec.upt != 1 || ch.rec.BT != 1 || dh->Dh != 128 || !gemm_dma_ok(dh->Din))
+        return 0;
+    const int free = cus - 2 * ch.rec.grid;
+    if (free < 32) return 0;
+    const int G = gates_of_cell(ch.cell);
+    const long tiles = gx_panels(dh) * (((long)dh->NH * G * dh->Dh + kGemmColTile - 1) /
+                                        kGemmColTile);
+    return (int)std::min<long>(free / 8 * 8, tiles);
+}
+
+// Workspace: one forward workspace sized for the larger input width, two
+// float32 sequence buffers (layers that run in turn), two bf16 sequence
+// buffers (layer inputs), a second gx and the step counters (overlapped
+// pairs).
 struct StackLayout {
-    size_t fwd, hbuf, xb, total;
+    size_t fwd, hbuf, hbf, gx2, done, total;
 };
 StackLayout stack_layout(const rnn_dims *d, int G, rnn_dtype dt) {
     StackLayout L{};
@@ -358,11 +387,14 @@ StackLayout stack_layout(const rnn_dims *d, int G, rnn_dtype dt) {
     const int H = d->NH * d->Dh;
     if (H > dm.Din) dm.Din = H;
     const size_t seq = (size_t)d->T * d->B * H;
+    const bool bf = dt == RNN_BF16;
     L.fwd = align_up(kHeader + xchg_bytes(&dm) + gx_bytes(&dm, G) + ready_bytes(&dm) +
                      wt_bytes(&dm, G) + rt_fwd_bytes(&dm, dt, G));
     L.hbuf = L.fwd;
-    L.xb = L.hbuf + 2 * align_up(sizeof(float) * seq);
-    L.total = L.xb + (dt == RNN_BF16 ? align_up(sizeof(uint16_t) * seq) : 0);
+    L.hbf = L.hbuf + 2 * align_up(sizeof(float) * seq);
+    L.gx2 = L.hbf + (bf ? 2 * align_up(sizeof(uint16_t) * seq) : 0);
+    L.done = L.gx2 + (bf ? gx_bytes(&dm, G) : 0);
+    L.total = L.done + (bf ? align_up(sizeof(unsigned) * (size_t)d->T) : 0);
     return L;
 }
 
@@ -370,32 +402,103 @@ rnn_status forward_stack(int cell, const rnn_dims *d, int L, rnn_dtype dt, const
                          const void *const *W, const void *const *R, const float *const *b,
                          const float *h0, const float *c0, float *h_seq, float *c_seq,
                          float *hT, float *cT, void *ws, hipStream_t s) {
-    const int G = gates_of_cell(cell), H = d->NH * d->Dh;
+    const int G = gates_of_cell(cell), H = d->NH * d->Dh, N = d->NH * G * d->Dh;
     const long BH = (long)d->B * H, seq = (long)d->T * BH;
     const StackLayout SL = stack_layout(d, G, dt);
     char *base = (char *)ws;
     float *hb[2] = {(float *)(base + SL.hbuf),
                     (float *)(base + SL.hbuf + align_up(sizeof(float) * seq))};
-    uint16_t *xb = dt == RNN_BF16 ? (uint16_t *)(base + SL.xb) : nullptr;
+    uint16_t *hbf[2] = {nullptr, nullptr};
+    if (dt == RNN_BF16) {
+        hbf[0] = (uint16_t *)(base + SL.hbf);
+        hbf[1] = (uint16_t *)(base + SL.hbf + align_up(sizeof(uint16_t) * seq));
+    }
+    // the forward workspace's regions (as forward() lays them out)
+    float *gx = (float *)(base + kHeader + xchg_bytes(d));
+    unsigned *ready = (unsigned *)((char *)gx + gx_bytes(d, G));
+    uint16_t *wt = (uint16_t *)((char *)ready + ready_bytes(d));
+    float *gx2 = (float *)(base + SL.gx2);
+    unsigned *done = (unsigned *)(base + SL.done);
+
+    rnn_dims dh = *d;
+    dh.Din = H;
+    const int cus = device_cus();
+    const Choice chh = choose(cell, &dh, dt, cus);
+    const int n_gemm = stack_overlap_wgs(chh, &dh, dt, cus);
+    const long panels = gx_panels(d);
+    const int M = d->T * d->B;
+    auto hip_ok = [](hipError_t e) { return e == hipSuccess; };
+
     const void *xin = x;
-    for (int l = 0; l < L; ++l) {
+    for (int l = 0; l < L;) {
         rnn_dims dl = *d;
         if (l > 0) dl.Din = H;
+        const bool first = l == 0;
+        const float *h0l = h0 ? h0 + l * BH : nullptr, *c0l = c0 ? c0 + l * BH : nullptr;
+        if (n_gemm > 0 && l + 1 < L) {
+            const bool last = l + 2 == L;
+            // layer l's projection on the whole chip
+            rnn_status st = input_proj(M, dl.Din, N, dt, xin, W[l], b ? b[l] : nullptr, gx,
+                                       first ? (uint32_t *)ws : nullptr, s, nullptr, wt);
+            if (st != RNN_OK) return st;
+            // W[l+1]^T; the same launch zeroes the step and panel counters
+            if (!hip_ok(launch_transpose_bf16((const uint16_t *)W[l + 1], wt, H, N, 1, s, done,
+                                              d->T, ready, panels)))
+                return RNN_ERR_HIP;
+            RecArgs a0{}, a1{};
+            a0.T = a1.T = d->T; a0.B = a1.B = d->B; a0.NH = a1.NH = d->NH;
+            a0.Dh = a1.Dh = d->Dh; a0.BT = a1.BT = 1;
+            a0.flag = a1.flag = (unsigned *)ws;
+            a0.spin_limit = a1.spin_limit = spin_limit();
+            a0.gx = gx;
+            a0.Rb = (const uint16_t *)R[l];
+            a0.h0 = h0l; a0.c0 = c0l;
+            a0.hT = hT + l * BH; a0.cT = cT ? cT + l * BH : nullptr;
+            a1.gx = gx2;
+            a1.Rb = (const uint16_t *)R[l + 1];
+            a1.h0 = h0 ? h0 + (l + 1) * BH : nullptr;
+            a1.c0 = c0 ? c0 + (l + 1) * BH : nullptr;
+            a1.h_seq = last ? h_seq : nullptr;
+            a1.c_seq = last ? c_seq : nullptr;
+            a1.hT = hT + (l + 1) * BH; a1.cT = cT ? cT + (l + 1) * BH : nullptr;
+            a1.ready = ready;
+            a1.ready_target = (unsigned)((N + kGemmColTile - 1) / kGemmColTile);
+            a1.panels = (int)panels;
+            GemmArgs g{};
+            g.M = M; g.N = N; g.K = H;
+            g.A = hbf[0]; g.lda = H;
+            g.B = wt; g.ldb = H;
+            g.bias = b ? b[l + 1] : nullptr;
+            g.C = gx2; g.ldc = N;
+            g.ksplit = 1;
+            g.ready = ready;
+            StackSync y{};
+            y.h_bf0 = hbf[0];
+            y.h_bf1 = last ? nullptr : hbf[1];
+            y.done = done;
+            y.rec_grid = chh.rec.grid;
+            y.done_target = (unsigned)chh.rec.grid;
+            y.n_gemm = n_gemm;
+            if (!hip_ok(launch_fwd_stack2(cell, chh.rec, a0, a1, g, y, s))) return RNN_ERR_HIP;
+            xin = hbf[1];
+            l += 2;
+            continue;
+        }
         const bool last = l == L - 1;
         float *hs = last ? h_seq : hb[l & 1];
         float *cs = last ? c_seq : nullptr;
-        rnn_status st = forward(cell, &dl, dt, xin, W[l], R[l], b ? b[l] : nullptr,
-                                h0 ? h0 + l * BH : nullptr, c0 ? c0 + l * BH : nullptr, hs, cs,
-                                hT + l * BH, cT ? cT + l * BH : nullptr, ws, s);
+        rnn_status st = forward(cell, &dl, dt, xin, W[l], R[l], b ? b[l] : nullptr, h0l, c0l, hs,
+                                cs, hT + l * BH, cT ? cT + l * BH : nullptr, ws, s, first);
         if (st != RNN_OK) return st;
         if (!last) {
-            if (xb) {
-                if (launch_hprev_bf16(nullptr, hs, xb, 0, seq, s) != hipSuccess) return RNN_ERR_HIP;
-                xin = xb;
+            if (hbf[0]) {
+                if (!hip_ok(launch_hprev_bf16(nullptr, hs, hbf[0], 0, seq, s))) return RNN_ERR_HIP;
+                xin = hbf[0];
             } else {
                 xin = hs;
             }
         }
+        ++l;
     }
     return RNN_OK;
 }

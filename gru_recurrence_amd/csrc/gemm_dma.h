@@ -25,6 +25,9 @@ static_assert(BM == kGemmRowTile && BN == kGemmColTile, "row-panel counters assu
 // chunks of 16 bytes, two per thread; chunk q goes to LDS byte 16q, i.e.
 // row q/4, slot q%4, holding k chunk (q%4) ^ ((row >> 1) & 3).  Rows past R
 // read row R-1 (their products only reach outputs that are not stored).
+// AUX is the loads' cache policy (16: device scope, for operands that other
+// workgroups of the same launch write).
+template <int AUX = 0>
 __device__ __forceinline__ void dma_tile(const uint16_t *__restrict__ P, long ld, int r0, int k0,
                                          int R, lds_char *dst, int tid, int wave) {
 #pragma unroll
@@ -34,7 +37,7 @@ __device__ __forceinline__ void dma_tile(const uint16_t *__restrict__ P, long ld
         const int chunk = slot ^ ((r >> 1) & 3);
         const int gr = min(r0 + r, R - 1);
         const uint16_t *src = P + (long)gr * ld + k0 + chunk * 8;
-        __builtin_amdgcn_global_load_lds(src, dst + (64 * wave + NTHR * i) * 16, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(src, dst + (64 * wave + NTHR * i) * 16, 16, 0, AUX);
     }
 }
 
@@ -48,7 +51,12 @@ __device__ __forceinline__ void wait_tiles_after(int later) {
 // The contraction's work for workgroup `wg` of `nwg`: output tiles wg,
 // wg + nwg, ... of batch / split slice blockIdx.z (a persistent loop when
 // nwg is smaller than the tile count).  `lds` is LDS_BYTES of dynamic LDS.
-__device__ __forceinline__ void gemm_dma_tiles(const GemmArgs &g, int wg, int nwg, lds_char *lds) {
+// Before each tile every thread calls pre(row tile), ahead of the barrier
+// that starts the tile (a wait for A's rows goes there); A_AUX is the cache
+// policy of A's loads.
+template <int A_AUX, class PreTile>
+__device__ __forceinline__ void gemm_dma_tiles_pre(const GemmArgs &g, int wg, int nwg,
+                                                   lds_char *lds, PreTile &&pre) {
     const uint32_t lbase = (uint32_t)(uintptr_t)lds;
 
     const int slice = blockIdx.z % g.ksplit, bz = blockIdx.z / g.ksplit;
@@ -96,6 +104,7 @@ __device__ __forceinline__ void gemm_dma_tiles(const GemmArgs &g, int wg, int nw
         nt = i % tiles_n;
     }
     const int m0 = mt * BM, n0 = nt * BN;
+    pre(mt);
     // a new tile refills the ring: every wave is past the last tile's reads
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -111,7 +120,7 @@ __device__ __forceinline__ void gemm_dma_tiles(const GemmArgs &g, int wg, int nw
 
     auto issue = [&](int kt) {
         lds_char *st = lds + ((kt - kt0) & (NST - 1)) * STB;
-        dma_tile(A, g.lda, m0, kt * BK, g.M, st, tid, wave);
+        dma_tile<A_AUX>(A, g.lda, m0, kt * BK, g.M, st, tid, wave);
         dma_tile(B, g.ldb, n0, kt * BK, g.N, st + OPB, tid, wave);
     };
 #pragma unroll
@@ -196,6 +205,10 @@ __device__ __forceinline__ void gemm_dma_tiles(const GemmArgs &g, int wg, int nw
         }
     }
     }  // tiles
+}
+
+__device__ __forceinline__ void gemm_dma_tiles(const GemmArgs &g, int wg, int nwg, lds_char *lds) {
+    gemm_dma_tiles_pre<0>(g, wg, nwg, lds, [](int) {});
 }
 
 }  // namespace dma

@@ -115,6 +115,24 @@ hipError_t launch_rec_fwd(int cell, const RecPlan &p, const RecArgs &a, bool bf1
 hipError_t launch_fwd_fused(int cell, const RecPlan &p, const RecArgs &a, const GemmArgs &g,
                             int n_gemm, hipStream_t s);
 
+// Two stacked layers l, l+1 in one launch (MFMA plan with one batch row per
+// workgroup, Dh = 128, bf16): rec_grid workgroups run layer l on a finished
+// gx (a0), storing h_t as bf16 in h_bf0 and counting each finished step on
+// done[t] (one count per workgroup, done_target = rec_grid); n_gemm workgroups
+// compute layer l+1's input projection g from h_bf0 (g.A), each 256-row
+// tile once the steps of its rows are counted, and count finished tiles on
+// g.ready; the last rec_grid
+// workgroups run layer l+1 (a1, a1.ready = g.ready) and, if h_bf1 is set,
+// also store its h_t as bf16 there.  done and g.ready start at zero.
+struct StackSync {
+    uint16_t *h_bf0, *h_bf1;
+    unsigned *done;       // [T]
+    unsigned done_target;  // counts of a finished step: rec_grid
+    int rec_grid, n_gemm;
+};
+hipError_t launch_fwd_stack2(int cell, const RecPlan &p, const RecArgs &a0, const RecArgs &a1,
+                             const GemmArgs &g, const StackSync &y, hipStream_t s);
+
 // Forward recurrence for Dh = 256 on one compute unit per (head, batch row),
 // R split over AGPRs, VGPRs and LDS (rec_wide.hip).  Rt holds R transposed
 // per head, [NH][G*Dh][Dh] bf16.
@@ -155,8 +173,10 @@ struct McArgs {
 // chip (every workgroup must be resident at once).  Pure host function.
 McPlan plan_mc(int cell, int B, int NH, int Dh, int num_cu, int bt_override, int k_override);
 
-// Clears the exchange slots and the abort word, then launches cooperatively.
-hipError_t launch_rec_mc(int cell, const McPlan &p, const McArgs &m, hipStream_t s);
+// Clears the exchange slots and (if clear_flag) the abort word, then
+// launches cooperatively.
+hipError_t launch_rec_mc(int cell, const McPlan &p, const McArgs &m, hipStream_t s,
+                         bool clear_flag = true);
 
 // LSTM backward (rec_bwd.hip).
 struct BwdPlan {

@@ -94,8 +94,26 @@ __device__ __forceinline__ void lstm_or_gru_unit(const float *gpre, int DH, cons
 // fence would drop every cached line of the XCD, the projection's operand
 // panels included).  Panels found complete are remembered; once the
 // projection is ahead, a check costs a compare.
-template <int CELL, int DH, int R4, int PD, bool WAIT>
-__device__ __forceinline__ void rec_fwd_mfma_body(const RecArgs &a, const int blk) {
+//
+// HB (a stacked layer feeding the next one): h_t is also stored as bf16 at
+// h_bf ([T][B][H]), with device-scope stores (written through the XCD's
+// L2), and with `done` the workgroup counts a step on done[t] once every
+// wave's stores of that step are complete.  No cache write-back is needed
+// (one per group from every workgroup slowed the contraction running
+// beside it by more than half).  Written-through stores take long to
+// complete, so at a group start the Gx loads go out before the previous
+// group's stores, and the next group start waits for all but those stores
+// and the count that follows them: each wave's stores issued a group
+// earlier are then complete.  After the barrier of that step every wave
+// has passed its wait, and at the group's second step wave 0 counts the
+// steps those stores hold (the group three back).
+// s_waitcnt immediate for vmcnt(n), n < 64, other counters not waited on.
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+template <int CELL, int DH, int R4, int PD, bool WAIT, bool HB = false>
+__device__ __forceinline__ void rec_fwd_mfma_body(const RecArgs &a, const int blk,
+                                                  uint16_t *h_bf = nullptr,
+                                                  unsigned *done = nullptr) {
     constexpr int G = CellTraits<CELL>::G;
     constexpr int GD = G * DH;
     constexpr int NW = DH / 16;   // waves = 16-unit blocks
@@ -106,6 +124,7 @@ __device__ __forceinline__ void rec_fwd_mfma_body(const RecArgs &a, const int bl
     constexpr int OUT_ROW = CELL == kLSTM ? 0 : 3;  // R4 == 1: lanes that own the result
     static_assert(DH % 32 == 0, "Dh must be a multiple of 32");
     static_assert(PD % 2 == 0, "groups must keep the h double-buffer parity");
+    static_assert(3 * PD < 64, "a group's stores must fit the vmcnt field");
 
     __shared__ __attribute__((aligned(16))) uint16_t hbuf[2][16 * HLD];
 
@@ -238,6 +257,7 @@ __device__ __forceinline__ void rec_fwd_mfma_body(const RecArgs &a, const int bl
     auto store_group = [&](int tg) {
         float *hs = has_h ? a.h_seq + o_tile + (long)tg * o_step : nullptr;
         float *cs = has_c ? a.c_seq + o_tile + (long)tg * o_step : nullptr;
+        uint16_t *hb = HB ? h_bf + o_tile + (long)tg * o_step : nullptr;
 #pragma unroll
         for (int s = 0; s < PD; ++s) {
             if (tg + s < T) {
@@ -246,11 +266,39 @@ __device__ __forceinline__ void rec_fwd_mfma_body(const RecArgs &a, const int bl
                     if (wr[r]) {
                         if (has_h) hs[oo[r]] = oh[s][r];
                         if (has_c) cs[oo[r]] = oc[s][r];
+                        if constexpr (HB)
+                            __hip_atomic_store(hb + oo[r], f32_to_bf16_rne(oh[s][r]),
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     }
                 }
             }
             hs += o_step;
             cs += o_step;
+            if constexpr (HB) hb += o_step;
+        }
+    };
+    // HB: a full group's stores (PD steps of h, c and the bf16 h) and the
+    // count after them are the last vector-memory instructions of a group;
+    // wait for all older ones.
+    const int nst = (has_h ? 1 : 0) + (has_c ? 1 : 0) + 1;
+    auto wait_but_stores = [&]() {
+        if (nst == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PD + 1));
+        else if (nst == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PD + 1));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * PD + 1));
+    };
+    // HB with `done`, wave 0 at the second step of group tg: every wave's
+    // stores of steps [tg - 3PD, tg - 2PD) are complete; count them.
+    int counted = 0;  // steps [0, counted) counted (wave 0)
+    auto publish = [&](int tg) {
+        if constexpr (HB) {
+            if (done == nullptr || wave != 0) return;
+            const int t0 = tg - 3 * PD;
+            if (t0 >= 0) {
+                if (lane < PD)
+                    __hip_atomic_fetch_add(done + t0 + lane, 1u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                counted = t0 + PD;
+            }
         }
     };
     // A operand: lanes of live batch rows load it from LDS every step; the
@@ -270,7 +318,12 @@ __device__ __forceinline__ void rec_fwd_mfma_body(const RecArgs &a, const int bl
             // first step of a group: everything still in flight was issued a
             // whole group ago; drain it here, before the new group's requests
             // go out, so no later use of `use` has to wait on those.
-            if (s == 0) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+            if constexpr (HB) {
+                if (s == 0) wait_but_stores();
+                if (s == 1) publish(tg);
+            } else {
+                if (s == 0) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+            }
             const uint16_t *hc = hbuf[s & 1];
             uint16_t *hn = hbuf[(s + 1) & 1];
             if (lr < rows) {
@@ -290,9 +343,15 @@ __device__ __forceinline__ void rec_fwd_mfma_body(const RecArgs &a, const int bl
             // the pinned wait states
             if (s == 0) mfma_chain_end();
             if (s == 0) {
-                if (tg > 0) store_group(tg - PD);
-                wait_ready(tg + 2 * PD);
-                load_group(tg + PD, nxt);
+                if constexpr (HB) {
+                    wait_ready(tg + 2 * PD);
+                    load_group(tg + PD, nxt);
+                    if (tg > 0) store_group(tg - PD);
+                } else {
+                    if (tg > 0) store_group(tg - PD);
+                    wait_ready(tg + 2 * PD);
+                    load_group(tg + PD, nxt);
+                }
             }
             float h[R4], c[R4];
             gate_update<CELL, R4>(acc, use[s], st, hl, h, c);
@@ -332,6 +391,17 @@ __device__ __forceinline__ void rec_fwd_mfma_body(const RecArgs &a, const int bl
             if (CELL == kLSTM) a.cT[o_tile + oo[r]] = st[r];
         }
     }
+    if constexpr (HB) {
+        if (done != nullptr) {
+            // the steps not counted yet, once every wave's stores are done
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+            __syncthreads();
+            if (wave == 0)
+                for (int t = counted + lane; t < T; t += 64)
+                    __hip_atomic_fetch_add(done + t, 1u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
 }
 
 template <int CELL, int DH, int R4, int PD, bool WAIT>
@@ -356,6 +426,62 @@ __global__ __launch_bounds__(512) void fwd_fused_kernel(RecArgs a, GemmArgs g, i
         return;
     }
     rec_fwd_mfma_body<CELL, DH, R4, PD, true>(a, blockIdx.x - n_gemm);
+}
+
+// Two stacked layers in one launch (see StackSync): [0, R) layer l's
+// recurrence, [R, R + n_gemm) layer l+1's input projection, then layer
+// l+1's recurrence.  Every role waits only on workgroups of lower index,
+// which are dispatched first, so the launch cannot stall on itself; each
+// wait is bounded by a.spin_limit and then sets the abort word.
+//
+// A tile of the projection covers rows [256 mt, 256 mt + 256) of the
+// [T*B] rows of h_bf0, i.e. the steps up to (256 mt + 255) / B; wave 0
+// polls the step counters (64 per poll) until those steps are counted by
+// every workgroup of layer l (y.done_target), then the tile's barrier releases
+// the other waves.  A's loads are device-scope (they miss in the XCD's L2,
+// like the stores that wrote them); the weights load as usual.
+template <int CELL, int PD, bool HB1>
+__global__ __launch_bounds__(512) void fwd_stack2_kernel(RecArgs a0, RecArgs a1, GemmArgs g,
+                                                         StackSync y) {
+    extern __shared__ __attribute__((aligned(16))) char stack_lds[];
+    const int blk = blockIdx.x;
+    if (blk < y.rec_grid) {
+        rec_fwd_mfma_body<CELL, 128, 1, PD, false, true>(a0, blk, y.h_bf0, y.done);
+        return;
+    }
+    const int gb = blk - y.rec_grid;
+    if (gb < y.n_gemm) {
+        const int T = a0.T, B = a0.B, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const unsigned target = y.done_target;
+        const long rows = (long)T * B;
+        int steps_ok = 0;
+        auto wait_rows = [&](int mt) {
+            if (wave != 0) return;
+            const long last = min((long)(mt + 1) * kGemmRowTile, rows) - 1;
+            const int need = (int)(last / B) + 1;
+            unsigned spins = 0;
+            while (steps_ok < need) {
+                const int t = steps_ok + lane;
+                const unsigned v = t < T ? __hip_atomic_load(y.done + t, __ATOMIC_RELAXED,
+                                                             __HIP_MEMORY_SCOPE_AGENT)
+                                         : target;
+                const unsigned long long ok = __ballot(v >= target);
+                const int run = ~ok == 0ull ? 64 : __builtin_ctzll(~ok);
+                steps_ok = min(steps_ok + run, T);
+                if (steps_ok >= need) break;
+                if (++spins >= a0.spin_limit) {
+                    if (lane == 0)
+                        __hip_atomic_store(a0.flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    steps_ok = T;  // give up waiting; the results are void
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(8);
+            }
+        };
+        dma::gemm_dma_tiles_pre<16>(g, gb, y.n_gemm, (dma::lds_char *)stack_lds, wait_rows);
+        return;
+    }
+    rec_fwd_mfma_body<CELL, 128, 1, PD, true, HB1>(a1, gb - y.n_gemm, y.h_bf1, nullptr);
 }
 
 // Simple kernel: dynamic LDS = R [Dh][G*Dh] f32 | h operand [BT][Dh] |
@@ -530,6 +656,36 @@ hipError_t launch_fwd_fused(int cell, const RecPlan &p, const RecArgs &a, const 
         default: return cell == kLSTM ? launch_fused_t<kLSTM, 4, 2>(p, a, g, n_gemm, s)
                                       : launch_fused_t<kGRU, 4, 2>(p, a, g, n_gemm, s);
     }
+}
+
+template <int CELL, bool HB1>
+hipError_t launch_stack2_t(const RecArgs &a0, const RecArgs &a1, const GemmArgs &g,
+                           const StackSync &y, hipStream_t s) {
+    static std::once_flag once;
+    static hipError_t attr = hipSuccess;
+    std::call_once(once, [] {
+        attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&fwd_stack2_kernel<CELL, 8, HB1>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)dma::LDS_BYTES);
+    });
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((fwd_stack2_kernel<CELL, 8, HB1>), dim3(2 * y.rec_grid + y.n_gemm),
+                       dim3(512), dma::LDS_BYTES, s, a0, a1, g, y);
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd_stack2(int cell, const RecPlan &p, const RecArgs &a0, const RecArgs &a1,
+                             const GemmArgs &g, const StackSync &y, hipStream_t s) {
+    if (p.kind != kRecMfma || p.upt != 1 || p.BT != 1 || a0.Dh != 128 || a1.Dh != 128 ||
+        a0.ready || !a1.ready || a1.ready != g.ready || !y.done || !y.h_bf0 || y.n_gemm <= 0 ||
+        y.rec_grid != p.grid || y.done_target != (unsigned)p.grid ||
+        g.A != y.h_bf0 || !gemm_dma_ok(g.K) || g.ksplit != 1)
+        return hipErrorInvalidValue;
+    const bool hb1 = y.h_bf1 != nullptr;
+    if (cell == kLSTM)
+        return hb1 ? launch_stack2_t<kLSTM, true>(a0, a1, g, y, s)
+                   : launch_stack2_t<kLSTM, false>(a0, a1, g, y, s);
+    return hb1 ? launch_stack2_t<kGRU, true>(a0, a1, g, y, s)
+               : launch_stack2_t<kGRU, false>(a0, a1, g, y, s);
 }
 
 hipError_t launch_rec_fwd(int cell, const RecPlan &p, const RecArgs &a, bool bf16,

@@ -319,10 +319,14 @@ McPlan plan_mc(int cell, int B, int NH, int Dh, int num_cu, int bt_override, int
     return p;
 }
 
-hipError_t launch_rec_mc(int cell, const McPlan &p, const McArgs &m, hipStream_t s) {
-    hipLaunchKernelGGL(clear_words_kernel, dim3(1), dim3(256), 0, s, m.flag, 1);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+hipError_t launch_rec_mc(int cell, const McPlan &p, const McArgs &m, hipStream_t s,
+                         bool clear_flag) {
+    hipError_t e;
+    if (clear_flag) {
+        hipLaunchKernelGGL(clear_words_kernel, dim3(1), dim3(256), 0, s, m.flag, 1);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     // step numbers start at 1: cleared slots never match a step
     const long words = 2L * p.groups * 2 * p.BT * (m.r.Dh / 2);
     hipLaunchKernelGGL(clear_words_kernel, dim3(64), dim3(256), 0, s,

@@ -193,9 +193,16 @@ rnn_status rnn_fwd_gru(const rnn_dims *d, rnn_dtype dt,
  *   h0, c0:  [L][B][H] float32 or NULL (zeros).
  *   h_seq, c_seq: the last layer's [T][B][H], may be NULL.
  *   hT, cT:  every layer's final states, [L][B][H], required.
- * 1 <= L <= 64.  The layers run one after the other on `stream`, each as
- * rnn_fwd_lstm would (same kernels and plans); intermediate sequences live
- * in the workspace (rnn_workspace_size_stack).  Errors as rnn_fwd_lstm.
+ * 1 <= L <= 64.  Where the recurrence runs one batch row per workgroup
+ * (bf16, Dh = 128, 2*NH*B + 32 <= compute units), layers run two at a time
+ * in one launch: layer l+1's input projection and recurrence start on each
+ * block of 256 rows of (t, b) as soon as layer l has produced it, on the
+ * compute units layer l leaves free.  Other layers run one after the other
+ * on `stream`, each as rnn_fwd_lstm would.  The results are the same bits
+ * either way (RNN355_STACK_OVERLAP=0 forces the second).  Intermediate
+ * sequences live in the workspace (rnn_workspace_size_stack, independent of
+ * L); a bounded wait that gave up in any layer is reported by
+ * rnn_workspace_status.  Errors as rnn_fwd_lstm.
  */
 size_t rnn_workspace_size_stack(rnn_op op /* RNN_OP_FWD_LSTM or RNN_OP_FWD_GRU */,
                                 const rnn_dims *d, int L, rnn_dtype dt);

@@ -2,6 +2,8 @@
 against the stacked oracle: layer l > 0 reads layer l-1's h sequence,
 rounded to bf16 in bf16 runs.  Bar: normwise 2e-2 (bf16) / 1e-5 (f32) on
 the last layer's sequences and every layer's final states."""
+import os
+
 import numpy as np
 import pytest
 
@@ -13,6 +15,16 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 import gru_recurrence_amd as g  # noqa: E402
+
+
+@pytest.fixture
+def overlap_env():
+    old = {k: os.environ.pop(k, None) for k in ("RNN355_STACK_OVERLAP", "RNN355_SPIN_LIMIT")}
+    yield
+    for k, v in old.items():
+        os.environ.pop(k, None)
+        if v is not None:
+            os.environ[k] = v
 
 
 def run(cs, **kw):
@@ -89,9 +101,11 @@ def test_stack_final_states_only():
     assert np.array_equal(a["hT"], b["hT"]) and "h_seq" not in b
 
 
-def test_two_layer_headline_stack_full_size_sampled_rows():
+@pytest.mark.parametrize("overlap", ["1", "0"])
+def test_two_layer_headline_stack_full_size_sampled_rows(overlap_env, overlap):
     """Two stacked layers at the headline shape (B=16, NH=6, Dh=128, T=1024,
     Din=768); the oracle computes whole batch rows 0 and 9 (every head)."""
+    os.environ["RNN355_STACK_OVERLAP"] = overlap
     w = synth.WORKLOADS["lstm_stack2_b16_nh6_dh128"]
     cs = synth.workload_stack_case(w)
     got = run(cs)
@@ -107,3 +121,48 @@ def test_two_layer_headline_stack_full_size_sampled_rows():
         e = nerr(got[k][:, rows], ref[k][:, rows])
         print("  %-6s nerr=%.3e" % (k, e), flush=True)
         assert e <= 2e-2, (k, e)
+
+
+@pytest.mark.parametrize("cell,L,T,B,NH,Din", [
+    ("lstm", 2, 21, 3, 2, 96),      # one row panel
+    ("lstm", 3, 100, 5, 1, 64),     # two panels, ragged; the third layer runs alone
+    ("lstm", 4, 37, 8, 3, 128),     # two overlapped pairs
+    ("gru", 2, 70, 4, 2, 32),
+    ("gru", 3, 9, 2, 1, 128),
+])
+def test_overlapped_pairs_match_oracle_and_layers_in_turn(overlap_env, cell, L, T, B, NH, Din):
+    """Dh = 128 bf16 stacks run two layers per launch (layer l+1's projection
+    and recurrence beside layer l's); RNN355_STACK_OVERLAP=0 runs them in
+    turn.  Same kernels, same summation order: equal bits."""
+    d = synth.Dims(T=T, B=B, Din=Din, NH=NH, Dh=128)
+    cs = synth.make_stack_case(cell, d, L, "bf16", 9700 + 7 * T + L,
+                               bias="forget+1" if cell == "lstm" else "zero",
+                               h0_var=0.2, c0_var=0.2)
+    got = run(cs)
+    os.environ["RNN355_STACK_OVERLAP"] = "0"
+    seq = run(cs)
+    ref = want(cs)
+    for k in got:
+        e = nerr(got[k], ref[k])
+        print("  %-6s nerr=%.3e" % (k, e), flush=True)
+        assert e <= 2e-2, (k, e)
+        assert np.array_equal(got[k], seq[k]), k
+
+
+def test_overlapped_pair_timeout_is_reported_and_cleared(overlap_env):
+    """A spin limit of one poll (set from the host) makes the projection's
+    wait for layer 0's steps give up: every workgroup stops, the launch ends
+    normally and the workspace reports the time-out; the next call clears
+    it and is right again."""
+    d = synth.Dims(T=64, B=4, Din=64, NH=2, Dh=128)
+    cs = synth.make_stack_case("lstm", d, 2, "bf16", 9800, bias="forget+1")
+    need = g.workspace_size_stack(g.OP_FWD_LSTM, g.Dims(d.T, d.B, d.Din, d.NH, d.Dh), 2,
+                                  g.RNN_BF16)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    os.environ["RNN355_SPIN_LIMIT"] = "1"
+    run(cs, ws=ws)
+    assert g.workspace_status(ws) == g.RNN_ERR_BARRIER_TIMEOUT
+    os.environ.pop("RNN355_SPIN_LIMIT")
+    got = run(cs, ws=ws)
+    assert g.workspace_status(ws) == g.RNN_OK
+    assert nerr(got["h_seq"], want(cs)["h_seq"]) <= 2e-2
