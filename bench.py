@@ -227,9 +227,34 @@ def main():
         ws_f = torch.empty(g.workspace_size_stack(fop, dims, L, dtc), dtype=torch.uint8,
                            device=dev)
 
+    chunked = w.chunk > 0
+    if chunked:
+        # the forward in chunks (checkpoints at the chunk ends when the
+        # backward follows, which then recomputes each segment from them)
+        ws_f = torch.empty(g.workspace_size_chunked(fop, dims, w.chunk, dtc), dtype=torch.uint8,
+                           device=dev)
+        nck = (d.T + w.chunk - 1) // w.chunk
+        outs_c = dict(outs)
+        if backward:
+            outs_c["h_ckpt"] = torch.empty((nck, d.B, H), dtype=f32, device=dev)
+            outs_c["c_ckpt"] = torch.empty((nck, d.B, H), dtype=f32, device=dev)
+            ws_b = torch.empty(g.workspace_size_chunked(g.OP_BWD_LSTM, dims, w.chunk, dtc),
+                               dtype=torch.uint8, device=dev)
+
     def step(evs=None):
         if evs is not None:
             evs[0].record(stream)
+        if chunked:
+            g.lstm_fwd_chunked(x, W, R, b, h0, c0, chunk=w.chunk, with_seq=not backward,
+                               ckpt=backward, ws=ws_f, out=outs_c, stream=stream)
+            if evs is not None:
+                evs[1].record(stream)
+            if backward:
+                g.lstm_bwd_ckpt(x, W, R, b, h0, c0, outs_c["h_ckpt"], outs_c["c_ckpt"], dH,
+                                chunk=w.chunk, ws=ws_b, out=grads, stream=stream)
+                if evs is not None:
+                    evs[2].record(stream)
+            return
         if stacked and lstm:
             g.lstm_stack_fwd(x, Ws, Rs, bs, h0s, c0s, ws=ws_f, out=outs_s, stream=stream)
         elif stacked:
@@ -346,11 +371,25 @@ def main():
         bwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
         out["backward"] = {"avg_call_ms": round(float(np.mean(bwd_ms)), 4),
                            "note": "rnn_bwd_lstm: recompute GEMMs, reverse sweep, dx/dW/dR GEMMs"}
+    if chunked:
+        out["config"]["chunk"] = w.chunk
+        out["workspace_bytes"] = {
+            "forward_chunked": int(ws_f.numel()),
+            "forward_one_piece": int(g.workspace_size(fop, dims, dtc))}
+        if backward:
+            out["workspace_bytes"]["backward_checkpointed"] = int(ws_b.numel())
+            out["workspace_bytes"]["backward_one_piece"] = int(
+                g.workspace_size(g.OP_BWD_LSTM, dims, dtc))
+            out["backward"]["note"] = ("rnn_bwd_lstm_ckpt: per segment of %d steps, the forward "
+                                       "recomputed from the checkpoint, then BPTT" % w.chunk)
+        out["forward_call"]["note"] = ("rnn_fwd_lstm_chunked in chunks of %d steps; the recurrence "
+                                       "and input projection entries time one-piece kernels"
+                                       % w.chunk)
     if stacked:
         out["forward_call"]["note"] = ("rnn_fwd_%s_stack over %d layers; the recurrence and "
                                        "input projection entries time layer 0's kernels"
                                        % (w.cell, w.layers))
-    if not args.no_cpu and lstm and not stacked:
+    if not args.no_cpu and lstm and not stacked and not chunked:
         out["cpu_baseline"] = cpu_baseline(w, c, args.cpu_budget)
     print(json.dumps(out), flush=True)
 

@@ -28,7 +28,8 @@ EXPORTS = ("rnn_status_str", "rnn_workspace_size", "rnn_plan_describe", "rnn_inp
            "rnn_input_proj_t",
            "rnn_rec_lstm", "rnn_rec_gru", "rnn_fwd_lstm", "rnn_fwd_gru", "rnn_bwd_lstm",
            "rnn_bwd_gru", "rnn_workspace_size_stack", "rnn_fwd_lstm_stack", "rnn_fwd_gru_stack",
-           "rnn_workspace_status")
+           "rnn_workspace_size_chunked", "rnn_fwd_lstm_chunked", "rnn_fwd_gru_chunked",
+           "rnn_bwd_lstm_ckpt", "rnn_bwd_gru_ckpt", "rnn_workspace_status")
 
 
 class Dims(ctypes.Structure):
@@ -75,9 +76,17 @@ def load(path: Optional[str] = None):
     lib.rnn_workspace_size_stack.argtypes = [I, D, I, I]
     lib.rnn_fwd_lstm_stack.argtypes = [D, I, I, P, P, P, P, P, P, P, P, P, P, P, S, P]
     lib.rnn_fwd_gru_stack.argtypes = [D, I, I, P, P, P, P, P, P, P, P, S, P]
+    lib.rnn_workspace_size_chunked.restype = S
+    lib.rnn_workspace_size_chunked.argtypes = [I, D, I, I]
+    lib.rnn_fwd_lstm_chunked.argtypes = [D, I, I] + [P] * 13 + [S, P]
+    lib.rnn_fwd_gru_chunked.argtypes = [D, I, I] + [P] * 9 + [S, P]
+    lib.rnn_bwd_lstm_ckpt.argtypes = [D, I, I] + [P] * 18 + [S, P]
+    lib.rnn_bwd_gru_ckpt.argtypes = [D, I, I] + [P] * 14 + [S, P]
     for f in ("rnn_plan_describe", "rnn_input_proj", "rnn_input_proj_t", "rnn_rec_lstm", "rnn_rec_gru",
               "rnn_fwd_lstm", "rnn_fwd_gru", "rnn_bwd_lstm", "rnn_bwd_gru",
-              "rnn_fwd_lstm_stack", "rnn_fwd_gru_stack", "rnn_workspace_status"):
+              "rnn_fwd_lstm_stack", "rnn_fwd_gru_stack", "rnn_fwd_lstm_chunked",
+              "rnn_fwd_gru_chunked", "rnn_bwd_lstm_ckpt", "rnn_bwd_gru_ckpt",
+              "rnn_workspace_status"):
         getattr(lib, f).restype = I
     _lib = lib
     return lib
@@ -445,6 +454,135 @@ def gru_bwd(x, W, R, b, h0, h_seq, dh_seq, dhT=None, *, ws=None, out=None, strea
                            _ptr(g["dh0"], "dh0", f32, shapes["dh0"]),
                            _ptr(ws, "ws"), ws.numel(), _stream(stream))
     _check(s, "rnn_bwd_gru")
+    return g
+
+
+def workspace_size_chunked(op: int, dims: Dims, chunk: int, dtype_code: int) -> int:
+    return int(load().rnn_workspace_size_chunked(op, ctypes.byref(dims), int(chunk), dtype_code))
+
+
+def _chunk_ws(op, d, chunk, dt, dev, ws):
+    torch = _torch()
+    need = workspace_size_chunked(op, d, chunk, dt)
+    if need == 0:
+        raise RnnError(RNN_ERR_INVALID_ARG, "rnn_workspace_size_chunked")
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    return ws
+
+
+def lstm_fwd_chunked(x, W, R, b=None, h0=None, c0=None, *, chunk: int, with_seq: bool = True,
+                     ckpt: bool = True, ws=None, out=None, stream=None):
+    """The LSTM forward in chunks of `chunk` steps (workspace independent of
+    T).  Returns (h_seq, c_seq, hT, cT, h_ckpt, c_ckpt); the checkpoints are
+    [ceil(T/chunk), B, H] (None unless ckpt)."""
+    torch = _torch()
+    d, dt, N = _common(x, W, R, 4)
+    H = d.NH * d.Dh
+    dev, f32 = x.device, torch.float32
+    out = out or {}
+    nck = (d.T + chunk - 1) // chunk
+
+    def get(k, shape, want=True):
+        if not want:
+            return None
+        v = out.get(k)
+        return torch.empty(shape, dtype=f32, device=dev) if v is None else v
+    h_seq, c_seq = get("h_seq", (d.T, d.B, H), with_seq), get("c_seq", (d.T, d.B, H), with_seq)
+    hT, cT = get("hT", (d.B, H)), get("cT", (d.B, H))
+    h_ck, c_ck = get("h_ckpt", (nck, d.B, H), ckpt), get("c_ckpt", (nck, d.B, H), ckpt)
+    ws = _chunk_ws(OP_FWD_LSTM, d, chunk, dt, dev, ws)
+    s = load().rnn_fwd_lstm_chunked(
+        ctypes.byref(d), dt, int(chunk), _ptr(x, "x"), _ptr(W, "W"), _ptr(R, "R"),
+        _ptr(b, "b", f32, (N,), True), _ptr(h0, "h0", f32, (d.B, H), True),
+        _ptr(c0, "c0", f32, (d.B, H), True), _ptr(h_seq, "h_seq", f32, None, True),
+        _ptr(c_seq, "c_seq", f32, None, True), _ptr(hT, "hT", f32, (d.B, H)),
+        _ptr(cT, "cT", f32, (d.B, H)), _ptr(h_ck, "h_ckpt", f32, (nck, d.B, H), True),
+        _ptr(c_ck, "c_ckpt", f32, (nck, d.B, H), True), _ptr(ws, "ws"), ws.numel(),
+        _stream(stream))
+    _check(s, "rnn_fwd_lstm_chunked")
+    return h_seq, c_seq, hT, cT, h_ck, c_ck
+
+
+def gru_fwd_chunked(x, W, R, b=None, h0=None, *, chunk: int, with_seq: bool = True,
+                    ckpt: bool = True, ws=None, out=None, stream=None):
+    """The GRU forward in chunks.  Returns (h_seq, hT, h_ckpt)."""
+    torch = _torch()
+    d, dt, N = _common(x, W, R, 3)
+    H = d.NH * d.Dh
+    dev, f32 = x.device, torch.float32
+    out = out or {}
+    nck = (d.T + chunk - 1) // chunk
+
+    def get(k, shape, want=True):
+        if not want:
+            return None
+        v = out.get(k)
+        return torch.empty(shape, dtype=f32, device=dev) if v is None else v
+    h_seq, hT = get("h_seq", (d.T, d.B, H), with_seq), get("hT", (d.B, H))
+    h_ck = get("h_ckpt", (nck, d.B, H), ckpt)
+    ws = _chunk_ws(OP_FWD_GRU, d, chunk, dt, dev, ws)
+    s = load().rnn_fwd_gru_chunked(
+        ctypes.byref(d), dt, int(chunk), _ptr(x, "x"), _ptr(W, "W"), _ptr(R, "R"),
+        _ptr(b, "b", f32, (N,), True), _ptr(h0, "h0", f32, (d.B, H), True),
+        _ptr(h_seq, "h_seq", f32, None, True), _ptr(hT, "hT", f32, (d.B, H)),
+        _ptr(h_ck, "h_ckpt", f32, (nck, d.B, H), True), _ptr(ws, "ws"), ws.numel(),
+        _stream(stream))
+    _check(s, "rnn_fwd_gru_chunked")
+    return h_seq, hT, h_ck
+
+
+def lstm_bwd_ckpt(x, W, R, b, h0, c0, h_ckpt, c_ckpt, dh_seq, dhT=None, dcT=None, *,
+                  chunk: int, ws=None, out=None, stream=None):
+    """LSTM BPTT from the checkpoints of lstm_fwd_chunked (same chunk).
+    Returns dict dx, dW, dR, db, dh0, dc0."""
+    torch = _torch()
+    d, dt, N = _common(x, W, R, 4)
+    H = d.NH * d.Dh
+    dev, f32 = x.device, torch.float32
+    nck = (d.T + chunk - 1) // chunk
+    shapes = dict(dx=(d.T, d.B, d.Din), dW=(d.Din, N), dR=(d.NH, d.Dh, 4 * d.Dh), db=(N,),
+                  dh0=(d.B, H), dc0=(d.B, H))
+    out = out or {}
+    g = {k: out[k] if out.get(k) is not None else torch.empty(v, dtype=f32, device=dev)
+         for k, v in shapes.items()}
+    ws = _chunk_ws(OP_BWD_LSTM, d, chunk, dt, dev, ws)
+    s = load().rnn_bwd_lstm_ckpt(
+        ctypes.byref(d), dt, int(chunk), _ptr(x, "x"), _ptr(W, "W"), _ptr(R, "R"),
+        _ptr(b, "b", f32, (N,), True), _ptr(h0, "h0", f32, (d.B, H), True),
+        _ptr(c0, "c0", f32, (d.B, H), True), _ptr(h_ckpt, "h_ckpt", f32, (nck, d.B, H), True),
+        _ptr(c_ckpt, "c_ckpt", f32, (nck, d.B, H), True),
+        _ptr(dh_seq, "dh_seq", f32, (d.T, d.B, H)), _ptr(dhT, "dhT", f32, (d.B, H), True),
+        _ptr(dcT, "dcT", f32, (d.B, H), True),
+        *[_ptr(g[k], k, f32, shapes[k]) for k in ("dx", "dW", "dR", "db", "dh0", "dc0")],
+        _ptr(ws, "ws"), ws.numel(), _stream(stream))
+    _check(s, "rnn_bwd_lstm_ckpt")
+    return g
+
+
+def gru_bwd_ckpt(x, W, R, b, h0, h_ckpt, dh_seq, dhT=None, *, chunk: int, ws=None, out=None,
+                 stream=None):
+    """GRU BPTT from the checkpoints of gru_fwd_chunked (same chunk).
+    Returns dict dx, dW, dR, db, dh0."""
+    torch = _torch()
+    d, dt, N = _common(x, W, R, 3)
+    H = d.NH * d.Dh
+    dev, f32 = x.device, torch.float32
+    nck = (d.T + chunk - 1) // chunk
+    shapes = dict(dx=(d.T, d.B, d.Din), dW=(d.Din, N), dR=(d.NH, d.Dh, 3 * d.Dh), db=(N,),
+                  dh0=(d.B, H))
+    out = out or {}
+    g = {k: out[k] if out.get(k) is not None else torch.empty(v, dtype=f32, device=dev)
+         for k, v in shapes.items()}
+    ws = _chunk_ws(OP_BWD_GRU, d, chunk, dt, dev, ws)
+    s = load().rnn_bwd_gru_ckpt(
+        ctypes.byref(d), dt, int(chunk), _ptr(x, "x"), _ptr(W, "W"), _ptr(R, "R"),
+        _ptr(b, "b", f32, (N,), True), _ptr(h0, "h0", f32, (d.B, H), True),
+        _ptr(h_ckpt, "h_ckpt", f32, (nck, d.B, H), True),
+        _ptr(dh_seq, "dh_seq", f32, (d.T, d.B, H)), _ptr(dhT, "dhT", f32, (d.B, H), True),
+        *[_ptr(g[k], k, f32, shapes[k]) for k in ("dx", "dW", "dR", "db", "dh0")],
+        _ptr(ws, "ws"), ws.numel(), _stream(stream))
+    _check(s, "rnn_bwd_gru_ckpt")
     return g
 
 

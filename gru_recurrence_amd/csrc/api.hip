@@ -509,12 +509,14 @@ rnn_status forward_stack(int cell, const rnn_dims *d, int L, rnn_dtype dt, const
 // 2. The reverse sweep (rec_bwd.hip) -> dA (and the GRU's dS), db partials,
 //    dh0 (dc0).
 // 3. db, dW = x^T dA, dx = dA W^T, dR = h_{t-1}^T dS (dS = dA for the LSTM).
+// accumulate: add dW, dR and db to what they hold (a later segment of a
+// checkpointed backward); clear_status: zero the status word first.
 rnn_status backward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, const void *W,
                     const void *R, const float *b, const float *h0, const float *c0,
                     const float *h_seq, const float *c_seq, const float *dh_seq,
                     const float *dhT, const float *dcT, float *dx, float *dW, float *dR,
                     float *db, float *dh0, float *dc0, void *ws, size_t ws_bytes,
-                    hipStream_t stream) {
+                    hipStream_t stream, bool accumulate = false, bool clear_status = true) {
     if (dt != RNN_BF16) return RNN_ERR_UNSUPPORTED;
     const bool lstm = cell == kLSTM;
     const int G = lstm ? 4 : 3, Dh = d->Dh, NH = d->NH, T = d->T, B = d->B, Din = d->Din;
@@ -545,7 +547,8 @@ rnn_status backward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, co
 
     // 1. h_{t-1} as bf16; gate inputs for all t at once
     if (!ok(launch_hprev_bf16(h0, h_seq, hprev, (long)B * H, (long)M * H, stream))) return RNN_ERR_HIP;
-    if (input_proj(M, Din, N, dt, x, W, b, A, (uint32_t *)ws, stream, nullptr, wt) != RNN_OK)
+    if (input_proj(M, Din, N, dt, x, W, b, A, clear_status ? (uint32_t *)ws : nullptr, stream,
+                   nullptr, wt) != RNN_OK)
         return RNN_ERR_HIP;
     {
         GemmArgs g{};  // h_{t-1} R per head: added to A (LSTM) or into S (GRU)
@@ -581,13 +584,14 @@ rnn_status backward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, co
         if (!ok(e)) return RNN_ERR_HIP;
     }
     // 3. parameter and input gradients
-    if (!ok(launch_db_reduce(dbp, nbt, N, db, stream))) return RNN_ERR_HIP;
+    if (!ok(launch_db_reduce(dbp, nbt, N, db, stream, accumulate))) return RNN_ERR_HIP;
     float *part = (float *)(base + L.part);
     const int cus = device_cus();
     {
         GemmArgs g{};  // dW[k][c] = sum_m x[m][k] dA[m][c]
         g.M = Din; g.N = N; g.K = M;
         g.A = xb; g.lda = Din; g.B = dA; g.ldb = N; g.C = dW; g.ldc = N;
+        g.accumulate = accumulate ? 1 : 0;
         g.ksplit = std::min(gemm_splitk_for(Din, N, M, 1, cus), kMaxSplitK);
         g.partial = part;
         if (!ok(launch_gemm_bf16(g, false, false, 1, stream))) return RNN_ERR_HIP;
@@ -606,9 +610,226 @@ rnn_status backward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, co
         g.A = hprev; g.lda = H; g.strideA = Dh;
         g.B = dS; g.ldb = N; g.strideB = GD;
         g.C = dR; g.ldc = GD; g.strideC = (long)Dh * GD;
+        g.accumulate = accumulate ? 1 : 0;
         g.ksplit = std::min(gemm_splitk_for(Dh, GD, M, NH, cus), kMaxSplitK);
         g.partial = part;
         if (!ok(launch_gemm_bf16(g, false, false, NH, stream))) return RNN_ERR_HIP;
+    }
+    return RNN_OK;
+}
+
+// A second stream of the current device (default priority) for work that
+// runs beside the caller's stream; created on first use.
+hipStream_t side_stream() {
+    static std::mutex mu;
+    static hipStream_t st[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> lk(mu);
+    if (!st[dev] && hipStreamCreateWithFlags(&st[dev], hipStreamNonBlocking) != hipSuccess)
+        st[dev] = nullptr;
+    return st[dev];
+}
+
+// Events of one call, destroyed when the call returns (the runtime keeps
+// a recorded event alive until its work is done).
+struct CallEvents {
+    hipEvent_t e[5] = {};
+    bool ok = true;
+    CallEvents() {
+        for (hipEvent_t &v : e)
+            if (hipEventCreateWithFlags(&v, hipEventDisableTiming) != hipSuccess) ok = false;
+    }
+    ~CallEvents() {
+        for (hipEvent_t v : e)
+            if (v) hipEventDestroy(v);
+    }
+};
+
+// Long sequences in chunks of `chunk` steps (blog.hotdry.top 2025-09-21,
+// the list of framework-level optimisations, third item: memory for long
+// sequences).  The recurrence runs chunk after chunk on the caller's
+// stream, each from the previous chunk's final state (the same kernels as
+// an unchunked call, hence the same bits); the input projection of chunk
+// k+2 runs on a second stream into the gx slot chunk k read, once chunk k's
+// recurrence is done, so each chunk's projection is ready before its
+// recurrence starts and runs beside the previous one, on the compute units
+// that recurrence leaves.  Workspace: two gx slots of `chunk` steps in
+// place of T, W^T, R^T, the exchange slots and the state between chunks.
+struct ChunkLayout {
+    size_t gx0, gx1, wt, rt, st, total;
+};
+ChunkLayout chunk_layout(const rnn_dims *d, int chunk, int G, rnn_dtype dt) {
+    ChunkLayout L{};
+    rnn_dims dc = *d;
+    dc.T = std::min(chunk, d->T);
+    const size_t bh = align_up(sizeof(float) * (size_t)d->B * d->NH * d->Dh);
+    L.gx0 = kHeader + xchg_bytes(&dc);
+    L.gx1 = L.gx0 + gx_bytes(&dc, G);
+    L.wt = L.gx1 + gx_bytes(&dc, G);
+    L.rt = L.wt + wt_bytes(d, G);
+    L.st = L.rt + rt_fwd_bytes(d, dt, G);
+    L.total = L.st + 4 * bh;
+    return L;
+}
+
+rnn_status forward_chunked(int cell, const rnn_dims *d, rnn_dtype dt, int chunk, const void *x,
+                           const void *W, const void *R, const float *b, const float *h0,
+                           const float *c0, float *h_seq, float *c_seq, float *hT, float *cT,
+                           float *h_ck, float *c_ck, void *ws, hipStream_t s) {
+    const bool lstm = cell == kLSTM;
+    const int G = gates_of_cell(cell), T = d->T, B = d->B, Din = d->Din;
+    const int H = d->NH * d->Dh, N = d->NH * G * d->Dh;
+    const long BH = (long)B * H;
+    chunk = std::min(chunk, T);
+    const int nck = (T + chunk - 1) / chunk;
+    const ChunkLayout CL = chunk_layout(d, chunk, G, dt);
+    char *base = (char *)ws;
+    float *gx[2] = {(float *)(base + CL.gx0), (float *)(base + CL.gx1)};
+    uint16_t *wt = (uint16_t *)(base + CL.wt), *rt = (uint16_t *)(base + CL.rt);
+    const size_t bh = align_up(sizeof(float) * (size_t)BH);
+    float *sth[2] = {(float *)(base + CL.st), (float *)(base + CL.st + bh)};
+    float *stc[2] = {(float *)(base + CL.st + 2 * bh), (float *)(base + CL.st + 3 * bh)};
+    const size_t esz = dt == RNN_BF16 ? 2 : 4;
+
+    const int cus = device_cus();
+    rnn_dims dc = *d;
+    dc.T = chunk;
+    const Choice ch = choose(cell, &dc, dt, cus);
+    if (!ch.ok) return RNN_ERR_UNSUPPORTED;
+    const int rec_grid = ch.use_wide ? ch.wide.grid : ch.use_mc ? ch.mc.grid : ch.rec.grid;
+    const bool dma = dt == RNN_BF16 && gemm_dma_ok(Din);
+    const int gemm_wg = std::max(8, (cus - rec_grid) / 8 * 8);
+    hipStream_t s2 = side_stream();
+    CallEvents ev;
+    if (!s2 || !ev.ok) return RNN_ERR_HIP;
+    hipEvent_t fork = ev.e[0], eg[2] = {ev.e[1], ev.e[2]}, er[2] = {ev.e[3], ev.e[4]};
+    auto ok = [](hipError_t e) { return e == hipSuccess; };
+
+    auto proj = [&](int k) -> rnn_status {
+        const int t0 = k * chunk, tk = std::min(chunk, T - t0);
+        const void *xk = (const char *)x + (size_t)t0 * B * Din * esz;
+        if (dma) {
+            GemmArgs g{};
+            g.M = tk * B; g.N = N; g.K = Din;
+            g.A = (const uint16_t *)xk; g.lda = Din;
+            g.B = wt; g.ldb = Din;
+            g.bias = b; g.C = gx[k & 1]; g.ldc = N;
+            g.ksplit = 1;
+            return ok(launch_gemm_dma(g, 1, s2, gemm_wg)) ? RNN_OK : RNN_ERR_HIP;
+        }
+        return input_proj(tk * B, Din, N, dt, xk, W, b, gx[k & 1],
+                          k == 0 ? (uint32_t *)ws : nullptr, s2);
+    };
+    // fork: the second stream starts after what the caller queued
+    if (!ok(hipEventRecord(fork, s)) || !ok(hipStreamWaitEvent(s2, fork, 0))) return RNN_ERR_HIP;
+    // W^T once; the same launch zeroes the status words
+    if (dma && !ok(launch_transpose_bf16((const uint16_t *)W, wt, Din, N, 1, s2, (unsigned *)ws, 64)))
+        return RNN_ERR_HIP;
+    for (int k = 0; k < std::min(2, nck); ++k) {
+        const rnn_status st = proj(k);
+        if (st != RNN_OK) return st;
+        if (!ok(hipEventRecord(eg[k & 1], s2))) return RNN_ERR_HIP;
+    }
+    for (int k = 0; k < nck; ++k) {
+        const int t0 = k * chunk;
+        rnn_dims dk = *d;
+        dk.T = std::min(chunk, T - t0);
+        const bool last = k == nck - 1;
+        const float *hin = k == 0 ? h0 : (h_ck ? h_ck + (k - 1) * BH : sth[(k - 1) & 1]);
+        const float *cin = !lstm ? nullptr
+                                 : k == 0 ? c0 : (c_ck ? c_ck + (k - 1) * BH : stc[(k - 1) & 1]);
+        float *hout = last ? hT : (h_ck ? h_ck + k * BH : sth[k & 1]);
+        float *cout = !lstm ? nullptr : last ? cT : (c_ck ? c_ck + k * BH : stc[k & 1]);
+        if (!ok(hipStreamWaitEvent(s, eg[k & 1], 0))) return RNN_ERR_HIP;
+        const rnn_status st = rec_fwd(cell, &dk, dt, gx[k & 1], R, hin, cin,
+                                      h_seq ? h_seq + t0 * BH : nullptr,
+                                      c_seq ? c_seq + t0 * BH : nullptr, hout, cout, ws, rt, s,
+                                      false);
+        if (st != RNN_OK) return st;
+        if (!ok(hipEventRecord(er[k & 1], s))) return RNN_ERR_HIP;
+        if (k + 2 < nck) {
+            if (!ok(hipStreamWaitEvent(s2, er[k & 1], 0))) return RNN_ERR_HIP;
+            const rnn_status sp = proj(k + 2);
+            if (sp != RNN_OK) return sp;
+            if (!ok(hipEventRecord(eg[k & 1], s2))) return RNN_ERR_HIP;
+        }
+    }
+    if (h_ck) {
+        const size_t bytes = sizeof(float) * (size_t)BH;
+        if (!ok(hipMemcpyAsync(h_ck + (nck - 1) * BH, hT, bytes, hipMemcpyDeviceToDevice, s)))
+            return RNN_ERR_HIP;
+        if (lstm && !ok(hipMemcpyAsync(c_ck + (nck - 1) * BH, cT, bytes, hipMemcpyDeviceToDevice, s)))
+            return RNN_ERR_HIP;
+    }
+    return RNN_OK;
+}
+
+// Checkpointed backpropagation through time (blog.hotdry.top 2025-09-21,
+// the list of framework-level optimisations, third item: checkpointing
+// trades compute for memory).  Segments of `chunk` steps from the last to
+// the first: the segment's h and c are recomputed by the forward from the
+// state before it (h0/c0, else the checkpoint of the previous segment),
+// then BPTT runs over the segment with the carries dh, dc that the later
+// segment left, adding to dW, dR and db.  Workspace: one forward or
+// backward workspace of `chunk` steps, the segment's h and c, the carries.
+struct CkptLayout {
+    size_t hseg, cseg, car, scr, total;
+};
+CkptLayout ckpt_layout(const rnn_dims *d, int chunk, int G, rnn_dtype dt) {
+    CkptLayout L{};
+    rnn_dims dc = *d;
+    dc.T = std::min(chunk, d->T);
+    const bool lstm = G == 4;
+    const size_t work = std::max(rnn_workspace_size(lstm ? RNN_OP_FWD_LSTM : RNN_OP_FWD_GRU, &dc, dt),
+                                 rnn_workspace_size(lstm ? RNN_OP_BWD_LSTM : RNN_OP_BWD_GRU, &dc, dt));
+    const size_t seg = align_up(sizeof(float) * (size_t)dc.T * d->B * d->NH * d->Dh);
+    const size_t bh = align_up(sizeof(float) * (size_t)d->B * d->NH * d->Dh);
+    L.hseg = align_up(work);
+    L.cseg = L.hseg + seg;
+    L.car = L.cseg + (lstm ? seg : 0);
+    L.scr = L.car + 4 * bh;
+    L.total = L.scr + 2 * bh;
+    return L;
+}
+
+rnn_status backward_ckpt(int cell, const rnn_dims *d, rnn_dtype dt, int chunk, const void *x,
+                         const void *W, const void *R, const float *b, const float *h0,
+                         const float *c0, const float *h_ck, const float *c_ck,
+                         const float *dh_seq, const float *dhT, const float *dcT, float *dx,
+                         float *dW, float *dR, float *db, float *dh0, float *dc0, void *ws,
+                         hipStream_t s) {
+    const bool lstm = cell == kLSTM;
+    const int G = gates_of_cell(cell), T = d->T, B = d->B, Din = d->Din;
+    const long BH = (long)B * d->NH * d->Dh;
+    chunk = std::min(chunk, T);
+    const int nseg = (T + chunk - 1) / chunk;
+    const CkptLayout CL = ckpt_layout(d, chunk, G, dt);
+    char *base = (char *)ws;
+    float *hseg = (float *)(base + CL.hseg), *cseg = lstm ? (float *)(base + CL.cseg) : nullptr;
+    const size_t bh = align_up(sizeof(float) * (size_t)BH);
+    float *car_h[2] = {(float *)(base + CL.car), (float *)(base + CL.car + bh)};
+    float *car_c[2] = {(float *)(base + CL.car + 2 * bh), (float *)(base + CL.car + 3 * bh)};
+    float *scr_h = (float *)(base + CL.scr), *scr_c = (float *)(base + CL.scr + bh);
+    for (int j = nseg - 1; j >= 0; --j) {
+        const int t0 = j * chunk;
+        rnn_dims dj = *d;
+        dj.T = std::min(chunk, T - t0);
+        const bool later = j == nseg - 1;  // the last segment, run first
+        const float *hin = j == 0 ? h0 : h_ck + (j - 1) * BH;
+        const float *cin = !lstm ? nullptr : j == 0 ? c0 : c_ck + (j - 1) * BH;
+        const void *xj = (const char *)x + (size_t)t0 * B * Din * sizeof(uint16_t);
+        rnn_status st = forward(cell, &dj, dt, xj, W, R, b, hin, cin, hseg, cseg, scr_h,
+                                lstm ? scr_c : nullptr, ws, s, later);
+        if (st != RNN_OK) return st;
+        const float *dhTj = later ? dhT : car_h[(j + 1) & 1];
+        const float *dcTj = !lstm ? nullptr : later ? dcT : car_c[(j + 1) & 1];
+        float *dh0j = j == 0 ? dh0 : car_h[j & 1];
+        float *dc0j = !lstm ? nullptr : j == 0 ? dc0 : car_c[j & 1];
+        st = backward(cell, &dj, dt, xj, W, R, b, hin, cin, hseg, cseg, dh_seq + t0 * BH, dhTj,
+                      dcTj, dx + (size_t)t0 * B * Din, dW, dR, db, dh0j, dc0j, ws, CL.hseg, s,
+                      !later, false);
+        if (st != RNN_OK) return st;
     }
     return RNN_OK;
 }
@@ -815,6 +1036,100 @@ rnn_status rnn_fwd_gru_stack(const rnn_dims *d, int L, rnn_dtype dt, const void 
     if (st != RNN_OK) return st;
     return forward_stack(kGRU, d, L, dt, x, W, R, b, h0, nullptr, h_seq, nullptr, hT, nullptr, ws,
                          stream);
+}
+
+size_t rnn_workspace_size_chunked(rnn_op op, const rnn_dims *d, int chunk, rnn_dtype dt) {
+    if (!dims_ok(d) || !dtype_ok(dt) || chunk < 1) return 0;
+    const int G = gates_of_op(op);
+    if (op == RNN_OP_FWD_LSTM || op == RNN_OP_FWD_GRU) return chunk_layout(d, chunk, G, dt).total;
+    if (op == RNN_OP_BWD_LSTM || op == RNN_OP_BWD_GRU) return ckpt_layout(d, chunk, G, dt).total;
+    return 0;
+}
+
+rnn_status rnn_fwd_lstm_chunked(const rnn_dims *d, rnn_dtype dt, int chunk, const void *x,
+                                const void *W, const void *R, const float *b, const float *h0,
+                                const float *c0, float *h_seq, float *c_seq, float *hT,
+                                float *cT, float *h_ckpt, float *c_ckpt, void *ws,
+                                size_t ws_bytes, hipStream_t stream) {
+    if (!dims_ok(d) || !dtype_ok(dt) || chunk < 1 || !x || !W || !R || !hT || !cT ||
+        (h_ckpt == nullptr) != (c_ckpt == nullptr))
+        return RNN_ERR_INVALID_ARG;
+    const void *ps[] = {x, W, R, b, h0, c0, h_seq, c_seq, hT, cT, h_ckpt, c_ckpt, ws};
+    for (const void *p : ps)
+        if (!aligned16(p)) return RNN_ERR_INVALID_ARG;
+    const int N = d->NH * 4 * d->Dh;
+    if (!gemm_shape_ok(d->Din, N, dt) || !rec_supported(kLSTM, d, dt)) return RNN_ERR_UNSUPPORTED;
+    if (!ws || ws_bytes < rnn_workspace_size_chunked(RNN_OP_FWD_LSTM, d, chunk, dt))
+        return RNN_ERR_WORKSPACE;
+    return forward_chunked(kLSTM, d, dt, chunk, x, W, R, b, h0, c0, h_seq, c_seq, hT, cT, h_ckpt,
+                           c_ckpt, ws, stream);
+}
+
+rnn_status rnn_fwd_gru_chunked(const rnn_dims *d, rnn_dtype dt, int chunk, const void *x,
+                               const void *W, const void *R, const float *b, const float *h0,
+                               float *h_seq, float *hT, float *h_ckpt, void *ws,
+                               size_t ws_bytes, hipStream_t stream) {
+    if (!dims_ok(d) || !dtype_ok(dt) || chunk < 1 || !x || !W || !R || !hT)
+        return RNN_ERR_INVALID_ARG;
+    const void *ps[] = {x, W, R, b, h0, h_seq, hT, h_ckpt, ws};
+    for (const void *p : ps)
+        if (!aligned16(p)) return RNN_ERR_INVALID_ARG;
+    const int N = d->NH * 3 * d->Dh;
+    if (!gemm_shape_ok(d->Din, N, dt) || !rec_supported(kGRU, d, dt)) return RNN_ERR_UNSUPPORTED;
+    if (!ws || ws_bytes < rnn_workspace_size_chunked(RNN_OP_FWD_GRU, d, chunk, dt))
+        return RNN_ERR_WORKSPACE;
+    return forward_chunked(kGRU, d, dt, chunk, x, W, R, b, h0, nullptr, h_seq, nullptr, hT,
+                           nullptr, h_ckpt, nullptr, ws, stream);
+}
+
+// Common checks of the checkpointed backward entry points.
+static rnn_status ckpt_args_ok(int cell, const rnn_dims *d, rnn_dtype dt, int chunk,
+                               const void *const *req, int nreq, const void *const *all, int nall,
+                               const void *h_ckpt, const void *c_ckpt, void *ws,
+                               size_t ws_bytes) {
+    if (!dims_ok(d) || !dtype_ok(dt) || chunk < 1) return RNN_ERR_INVALID_ARG;
+    for (int i = 0; i < nreq; ++i)
+        if (!req[i]) return RNN_ERR_INVALID_ARG;
+    for (int i = 0; i < nall; ++i)
+        if (!aligned16(all[i])) return RNN_ERR_INVALID_ARG;
+    if (chunk < d->T && (!h_ckpt || (cell == kLSTM && !c_ckpt))) return RNN_ERR_INVALID_ARG;
+    const int G = gates_of_cell(cell);
+    if (dt != RNN_BF16 || !gemm_shape_ok(d->Din, d->NH * G * d->Dh, dt) || d->Dh % 16 != 0 ||
+        !rec_supported(cell, d, dt))
+        return RNN_ERR_UNSUPPORTED;
+    const rnn_op op = cell == kLSTM ? RNN_OP_BWD_LSTM : RNN_OP_BWD_GRU;
+    if (!ws || ws_bytes < rnn_workspace_size_chunked(op, d, chunk, dt)) return RNN_ERR_WORKSPACE;
+    return RNN_OK;
+}
+
+rnn_status rnn_bwd_lstm_ckpt(const rnn_dims *d, rnn_dtype dt, int chunk, const void *x,
+                             const void *W, const void *R, const float *b, const float *h0,
+                             const float *c0, const float *h_ckpt, const float *c_ckpt,
+                             const float *dh_seq, const float *dhT, const float *dcT, float *dx,
+                             float *dW, float *dR, float *db, float *dh0, float *dc0, void *ws,
+                             size_t ws_bytes, hipStream_t stream) {
+    const void *req[] = {x, W, R, dh_seq, dx, dW, dR, db, dh0, dc0};
+    const void *all[] = {x, W, R, b, h0, c0, h_ckpt, c_ckpt, dh_seq, dhT, dcT,
+                         dx, dW, dR, db, dh0, dc0, ws};
+    const rnn_status st = ckpt_args_ok(kLSTM, d, dt, chunk, req, 10, all, 18, h_ckpt, c_ckpt, ws,
+                                       ws_bytes);
+    if (st != RNN_OK) return st;
+    return backward_ckpt(kLSTM, d, dt, chunk, x, W, R, b, h0, c0, h_ckpt, c_ckpt, dh_seq, dhT,
+                         dcT, dx, dW, dR, db, dh0, dc0, ws, stream);
+}
+
+rnn_status rnn_bwd_gru_ckpt(const rnn_dims *d, rnn_dtype dt, int chunk, const void *x,
+                            const void *W, const void *R, const float *b, const float *h0,
+                            const float *h_ckpt, const float *dh_seq, const float *dhT,
+                            float *dx, float *dW, float *dR, float *db, float *dh0, void *ws,
+                            size_t ws_bytes, hipStream_t stream) {
+    const void *req[] = {x, W, R, dh_seq, dx, dW, dR, db, dh0};
+    const void *all[] = {x, W, R, b, h0, h_ckpt, dh_seq, dhT, dx, dW, dR, db, dh0, ws};
+    const rnn_status st = ckpt_args_ok(kGRU, d, dt, chunk, req, 9, all, 14, h_ckpt, nullptr, ws,
+                                       ws_bytes);
+    if (st != RNN_OK) return st;
+    return backward_ckpt(kGRU, d, dt, chunk, x, W, R, b, h0, nullptr, h_ckpt, nullptr, dh_seq,
+                         dhT, nullptr, dx, dW, dR, db, dh0, nullptr, ws, stream);
 }
 
 rnn_status rnn_bwd_lstm(const rnn_dims *d, rnn_dtype dt, const void *x, const void *W,

@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t *__r
 
 bool gemm_dma_ok(int K) { return K % BK == 0 && K > 0; }
 
-hipError_t launch_gemm_dma(const GemmArgs &g0, int batch, hipStream_t s) {
+hipError_t launch_gemm_dma(const GemmArgs &g0, int batch, hipStream_t s, int max_wg) {
     GemmArgs g = g0;
     if (g.ksplit < 1) g.ksplit = 1;
     if (!gemm_dma_ok(g.K)) return hipErrorInvalidValue;
@@ -120,7 +120,8 @@ hipError_t launch_gemm_dma(const GemmArgs &g0, int batch, hipStream_t s) {
     });
     if (attr != hipSuccess) return attr;
     const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-    hipLaunchKernelGGL(gemm_dma_kernel, dim3(tiles, 1, batch * g.ksplit), dim3(NTHR), LDS_BYTES, s, g);
+    const int wgs = max_wg > 0 && max_wg < tiles ? max_wg : tiles;
+    hipLaunchKernelGGL(gemm_dma_kernel, dim3(wgs, 1, batch * g.ksplit), dim3(NTHR), LDS_BYTES, s, g);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || g.ksplit == 1) return e;
     return launch_splitk_reduce(g, batch, s);

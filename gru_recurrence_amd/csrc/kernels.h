@@ -59,7 +59,10 @@ hipError_t launch_splitk_reduce(const GemmArgs &g, int batch, hipStream_t s);
 // Both operands k-major, K % 32 == 0: tiles streamed into LDS by direct
 // global-to-LDS loads (gemm_dma.hip).  B(n,k) = B[n*ldb + k].
 bool gemm_dma_ok(int K);
-hipError_t launch_gemm_dma(const GemmArgs &g, int batch, hipStream_t s);
+// max_wg > 0: at most that many workgroups, each looping over output tiles
+// (leaves compute units to a kernel running beside it; a multiple of 8
+// keeps a row tile's column tiles on one XCD).
+hipError_t launch_gemm_dma(const GemmArgs &g, int batch, hipStream_t s, int max_wg = 0);
 // dst[b][c][r] = src[b][r][c], bf16 [R][C] matrices, `batch` of them; the
 // same launch zeroes nclear words at `clear` and nclear2 at `clear2` (if set).
 hipError_t launch_transpose_bf16(const uint16_t *src, uint16_t *dst, int R, int C, int batch,
@@ -217,6 +220,8 @@ hipError_t launch_rec_bwd(int cell, const BwdPlan &p, const BwdArgs &m, hipStrea
 hipError_t launch_rec_bwd_wide(int cell, const WidePlan &p, const BwdArgs &m, hipStream_t s);
 hipError_t launch_hprev_bf16(const float *h0, const float *h_seq, uint16_t *hprev, long BH,
                              long total, hipStream_t s);
-hipError_t launch_db_reduce(const float *db_part, int nbt, int N, float *db, hipStream_t s);
+// db = (db if accumulate) + sum over batch tiles of db_part.
+hipError_t launch_db_reduce(const float *db_part, int nbt, int N, float *db, hipStream_t s,
+                            bool accumulate = false);
 
 }  // namespace rnn355

@@ -356,13 +356,14 @@ __global__ void hprev_bf16_kernel(const float *h0, const float *h_seq, uint16_t 
     }
 }
 
-// db[c] = sum over batch tiles of db_part[bt][c], in tile order.
-__global__ void db_reduce_kernel(const float *db_part, int nbt, int N, float *db) {
+// db[c] = sum over batch tiles of db_part[bt][c], in tile order (added to
+// the old db[c] if accumulate).
+__global__ void db_reduce_kernel(const float *db_part, int nbt, int N, float *db, int accumulate) {
     const int c = blockIdx.x * blockDim.x + threadIdx.x;
     if (c >= N) return;
     float v = 0.f;
     for (int b = 0; b < nbt; ++b) v += db_part[(long)b * N + c];
-    db[c] = v;
+    db[c] = accumulate ? db[c] + v : v;
 }
 
 }  // namespace
@@ -435,8 +436,10 @@ hipError_t launch_hprev_bf16(const float *h0, const float *h_seq, uint16_t *hpre
     return hipGetLastError();
 }
 
-hipError_t launch_db_reduce(const float *db_part, int nbt, int N, float *db, hipStream_t s) {
-    hipLaunchKernelGGL(db_reduce_kernel, dim3((N + 255) / 256), dim3(256), 0, s, db_part, nbt, N, db);
+hipError_t launch_db_reduce(const float *db_part, int nbt, int N, float *db, hipStream_t s,
+                            bool accumulate) {
+    hipLaunchKernelGGL(db_reduce_kernel, dim3((N + 255) / 256), dim3(256), 0, s, db_part, nbt, N, db,
+                       accumulate ? 1 : 0);
     return hipGetLastError();
 }
 

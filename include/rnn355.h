@@ -219,6 +219,62 @@ rnn_status rnn_fwd_gru_stack(const rnn_dims *d, int L, rnn_dtype dt, const void 
                              void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Long sequences (blog.hotdry.top 2025-09-21, the list of framework-level
+ * optimisations, third item: memory use for long sequences and trading
+ * compute for it by checkpointing).  Both calls work on chunks of `chunk`
+ * time steps (chunk >= 1; the last chunk may be shorter; chunk >= T is one
+ * chunk), so their workspace (rnn_workspace_size_chunked) grows with chunk,
+ * not with T.
+ *
+ * rnn_fwd_lstm_chunked: the forward of rnn_fwd_lstm, chunk after chunk,
+ * each chunk starting from the previous one's final state; the input
+ * projection of a later chunk runs beside the recurrence of the current
+ * one (on a second stream of the library's that joins `stream`).  Results
+ * are the same bits as rnn_fwd_lstm.  h_ckpt, c_ckpt: NULL (both), or
+ * [ceil(T/chunk)][B][H] float32 receiving the state at the last step of
+ * every chunk (h_{k*chunk-1} for k = 1, 2, ...; the last entry equals hT).
+ * Arguments otherwise as rnn_fwd_lstm.
+ *
+ * rnn_bwd_lstm_ckpt: the gradients of rnn_bwd_lstm without h_seq and c_seq:
+ * segments of `chunk` steps are processed from the last to the first; each
+ * segment's h and c are recomputed from the state before it (h0, c0 for
+ * the first segment, else the previous segment's checkpoint, as
+ * rnn_fwd_lstm_chunked with the same chunk writes them), then BPTT runs
+ * over the segment with the gradients the later segment passes back.  dx,
+ * dh0 and dc0 are the same bits as rnn_bwd_lstm; dW, dR and db are summed
+ * segment by segment (float32 rounding differs).  h_ckpt and c_ckpt are
+ * required when chunk < T.  bf16 only, like rnn_bwd_lstm.
+ */
+size_t rnn_workspace_size_chunked(rnn_op op /* RNN_OP_FWD_* or RNN_OP_BWD_* */,
+                                  const rnn_dims *d, int chunk, rnn_dtype dt);
+rnn_status rnn_fwd_lstm_chunked(const rnn_dims *d, rnn_dtype dt, int chunk, const void *x,
+                                const void *W, const void *R, const float *b,
+                                const float *h0, const float *c0,
+                                float *h_seq, float *c_seq, float *hT, float *cT,
+                                float *h_ckpt, float *c_ckpt,
+                                void *ws, size_t ws_bytes, hipStream_t stream);
+/* GRU forward in chunks, as rnn_fwd_lstm_chunked without cell states. */
+rnn_status rnn_fwd_gru_chunked(const rnn_dims *d, rnn_dtype dt, int chunk, const void *x,
+                               const void *W, const void *R, const float *b,
+                               const float *h0, float *h_seq, float *hT, float *h_ckpt,
+                               void *ws, size_t ws_bytes, hipStream_t stream);
+rnn_status rnn_bwd_lstm_ckpt(const rnn_dims *d, rnn_dtype dt, int chunk, const void *x,
+                             const void *W, const void *R, const float *b,
+                             const float *h0, const float *c0,
+                             const float *h_ckpt, const float *c_ckpt,
+                             const float *dh_seq, const float *dhT, const float *dcT,
+                             float *dx, float *dW, float *dR, float *db,
+                             float *dh0, float *dc0,
+                             void *ws, size_t ws_bytes, hipStream_t stream);
+/* GRU BPTT from checkpoints, as rnn_bwd_lstm_ckpt without cell states. */
+rnn_status rnn_bwd_gru_ckpt(const rnn_dims *d, rnn_dtype dt, int chunk, const void *x,
+                            const void *W, const void *R, const float *b,
+                            const float *h0, const float *h_ckpt,
+                            const float *dh_seq, const float *dhT,
+                            float *dx, float *dW, float *dR, float *db, float *dh0,
+                            void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Multi-head LSTM backpropagation through time for the loss
  *   L = sum_t dh_seq[t] . h_t + dhT . h_T + dcT . c_T
  * given the forward's h_seq and c_seq (from rnn_fwd_lstm on the same inputs).

@@ -122,6 +122,8 @@ class Workload:
     backward: bool = False
     dH_var: float = 1.0
     layers: int = 1              # stacked layers (layer l > 0 reads layer l-1's h)
+    chunk: int = 0               # > 0: forward in chunks of this many steps, BPTT from
+                                 # checkpoints at the chunk ends
     note: str = ""
 
 
@@ -149,6 +151,14 @@ WORKLOADS: Dict[str, Workload] = {
         6, "lstm_stack2_b16_nh6_dh128", "lstm", Dims(T=1024, B=16, Din=768, NH=6, Dh=128), "bf16",
         bias="forget+1", layers=2,
         note="two stacked layers of the multi-head LSTM (second layer's W is [H][N])"),
+    "lstm_long_t8k_b16_nh6_dh128": Workload(
+        7, "lstm_long_t8k_b16_nh6_dh128", "lstm", Dims(T=8192, B=16, Din=768, NH=6, Dh=128),
+        "bf16", bias="forget+1", chunk=1024,
+        note="the headline LSTM over a sequence 8x longer, forward in chunks of 1024 steps"),
+    "lstm_fwdbwd_ckpt_b16_nh4_dh256": Workload(
+        8, "lstm_fwdbwd_ckpt_b16_nh4_dh256", "lstm", Dims(T=1024, B=16, Din=1024, NH=4, Dh=256),
+        "bf16", bias="forget+1", backward=True, chunk=256,
+        note="forward plus BPTT of the Dh=256 workload with checkpoints every 256 steps"),
 }
 
 BY_ID = {w.wid: w for w in WORKLOADS.values()}

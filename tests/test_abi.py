@@ -225,3 +225,41 @@ def test_stack_entry_points_reject_before_launch():
     assert lstm(g.Dims(8, 2, 30, 1, 32), 2, W, R) == g.RNN_ERR_UNSUPPORTED
     assert lib.rnn_fwd_gru_stack(ctypes.byref(d), 2, g.RNN_BF16, ok[0], W, R, None, None, None,
                                  None, _p(FAKE), big, None) == g.RNN_ERR_INVALID_ARG
+
+
+def test_chunked_and_checkpointed_entry_points_reject_before_launch():
+    lib = g.load()
+    d = g.Dims(64, 2, 32, 1, 64)
+    ok = [_p(FAKE + 256 * i) for i in range(24)]
+    big = 1 << 30
+    f = g.workspace_size_chunked(g.OP_FWD_LSTM, d, 16, g.RNN_BF16)
+    d2 = g.Dims(6400, 2, 32, 1, 64)
+    assert f > 0 and g.workspace_size_chunked(g.OP_FWD_LSTM, d2, 16, g.RNN_BF16) == f
+    bk = g.workspace_size_chunked(g.OP_BWD_LSTM, d, 16, g.RNN_BF16)
+    assert bk > 0 and g.workspace_size_chunked(g.OP_BWD_LSTM, d2, 16, g.RNN_BF16) == bk
+    assert bk < g.workspace_size(g.OP_BWD_LSTM, d2, g.RNN_BF16)
+    assert g.workspace_size_chunked(g.OP_FWD_LSTM, d, 0, g.RNN_BF16) == 0
+    assert g.workspace_size_chunked(g.OP_REC_LSTM, d, 16, g.RNN_BF16) == 0
+
+    def fwd(chunk, hck=ok[11], cck=ok[12], ws=_p(FAKE), nb=big):
+        return lib.rnn_fwd_lstm_chunked(ctypes.byref(d), g.RNN_BF16, chunk, *ok[:10], hck, cck, ws,
+                                        nb, None)
+    assert fwd(0) == g.RNN_ERR_INVALID_ARG
+    assert fwd(16, cck=None) == g.RNN_ERR_INVALID_ARG       # h and c checkpoints go together
+    assert fwd(16, ws=None, nb=0) == g.RNN_ERR_WORKSPACE
+    assert fwd(16, nb=f - 1) == g.RNN_ERR_WORKSPACE
+    assert fwd(16, hck=_p(FAKE + 8), cck=_p(FAKE + 8)) == g.RNN_ERR_INVALID_ARG
+    assert lib.rnn_fwd_gru_chunked(ctypes.byref(d), g.RNN_BF16, -1, *ok[:8], _p(FAKE), big,
+                                   None) == g.RNN_ERR_INVALID_ARG
+
+    def bwd(chunk, dt=g.RNN_BF16, hck=ok[6], cck=ok[7], nb=big):
+        a = list(ok[:17])
+        a[6], a[7] = hck, cck
+        return lib.rnn_bwd_lstm_ckpt(ctypes.byref(d), dt, chunk, *a, _p(FAKE), nb, None)
+    assert bwd(0) == g.RNN_ERR_INVALID_ARG
+    assert bwd(16, hck=None) == g.RNN_ERR_INVALID_ARG       # checkpoints needed when chunk < T
+    assert bwd(16, cck=None) == g.RNN_ERR_INVALID_ARG
+    assert bwd(16, dt=g.RNN_F32) == g.RNN_ERR_UNSUPPORTED
+    assert bwd(16, nb=bk - 1) == g.RNN_ERR_WORKSPACE
+    assert lib.rnn_bwd_gru_ckpt(ctypes.byref(d), g.RNN_BF16, 16, *ok[:5], None, *ok[6:13],
+                                _p(FAKE), big, None) == g.RNN_ERR_INVALID_ARG
