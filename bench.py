@@ -332,6 +332,8 @@ def main():
     achieved = recurrent_flops(w) / (rec_avg * 1e-3) / 1e12
     gemm_flops = 2.0 * d.T * d.B * d.Din * N
     ncu_engaged = int(plan.split(" wg=")[1].split()[0])
+    cands, best = g.plan_search(op, dims, dtc)
+    predicted = float(plan.split("predicted_ns_per_step=")[1].split()[0])
     out = {
         "metric": METRIC if args.workload == HEADLINE else METRIC.split(",")[0] + ", " + w.name,
         "value": round(value, 4),
@@ -356,7 +358,11 @@ def main():
                        "engaged_cus": ncu_engaged,
                        "engaged_cu_peak_tflops": round(ncu_engaged * CU_BF16_TFLOPS, 1),
                        "frac_of_engaged_cu_peak": round(achieved / (ncu_engaged * CU_BF16_TFLOPS), 4),
-                       "plan": plan},
+                       "plan": plan,
+                       "plan_search": {"candidates": len(cands),
+                                       "feasible": sum(1 for c in cands if c["feasible"]),
+                                       "predicted_ns_per_step": predicted,
+                                       "measured_ns_per_step": round(rec_avg * 1e6 / d.T, 1)}},
         "input_projection": {"avg_launch_ms": round(proj_avg, 4),
                              "tflops": round(gemm_flops / (proj_avg * 1e-3) / 1e12, 2),
                              "frac_of_peak": round(gemm_flops / (proj_avg * 1e-3) / 1e12

@@ -29,12 +29,25 @@ EXPORTS = ("rnn_status_str", "rnn_workspace_size", "rnn_plan_describe", "rnn_inp
            "rnn_rec_lstm", "rnn_rec_gru", "rnn_fwd_lstm", "rnn_fwd_gru", "rnn_bwd_lstm",
            "rnn_bwd_gru", "rnn_workspace_size_stack", "rnn_fwd_lstm_stack", "rnn_fwd_gru_stack",
            "rnn_workspace_size_chunked", "rnn_fwd_lstm_chunked", "rnn_fwd_gru_chunked",
-           "rnn_bwd_lstm_ckpt", "rnn_bwd_gru_ckpt", "rnn_workspace_status")
+           "rnn_bwd_lstm_ckpt", "rnn_bwd_gru_ckpt", "rnn_plan_search", "rnn_workspace_status")
 
 
 class Dims(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int), ("B", ctypes.c_int), ("Din", ctypes.c_int),
                 ("NH", ctypes.c_int), ("Dh", ctypes.c_int)]
+
+
+class PlanCandidate(ctypes.Structure):
+    """One assignment of the recurrence plan's variables (rnn_plan_candidate)."""
+    _fields_ = [(n, ctypes.c_int) for n in (
+        "family", "rows_per_wg", "wg_per_head", "blocks_per_wg", "k_splits",
+        "kchunks_per_wave", "row_slots", "frags_agpr", "frags_vgpr", "frags_lds", "waves",
+        "grid", "r_vgpr", "wg_per_cu")] + [("lds_bytes", ctypes.c_longlong), ("feasible", ctypes.c_int),
+                              ("violated", ctypes.c_int), ("ns_per_step", ctypes.c_double),
+                              ("ns_total", ctypes.c_double)]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
 
 
 class RnnError(RuntimeError):
@@ -82,11 +95,13 @@ def load(path: Optional[str] = None):
     lib.rnn_fwd_gru_chunked.argtypes = [D, I, I] + [P] * 9 + [S, P]
     lib.rnn_bwd_lstm_ckpt.argtypes = [D, I, I] + [P] * 18 + [S, P]
     lib.rnn_bwd_gru_ckpt.argtypes = [D, I, I] + [P] * 14 + [S, P]
+    lib.rnn_plan_search.argtypes = [I, D, I, I, ctypes.POINTER(PlanCandidate), I,
+                                    ctypes.POINTER(I), ctypes.POINTER(I)]
     for f in ("rnn_plan_describe", "rnn_input_proj", "rnn_input_proj_t", "rnn_rec_lstm", "rnn_rec_gru",
               "rnn_fwd_lstm", "rnn_fwd_gru", "rnn_bwd_lstm", "rnn_bwd_gru",
               "rnn_fwd_lstm_stack", "rnn_fwd_gru_stack", "rnn_fwd_lstm_chunked",
               "rnn_fwd_gru_chunked", "rnn_bwd_lstm_ckpt", "rnn_bwd_gru_ckpt",
-              "rnn_workspace_status"):
+              "rnn_plan_search", "rnn_workspace_status"):
         getattr(lib, f).restype = I
     _lib = lib
     return lib
@@ -455,6 +470,18 @@ def gru_bwd(x, W, R, b, h0, h_seq, dh_seq, dhT=None, *, ws=None, out=None, strea
                            _ptr(ws, "ws"), ws.numel(), _stream(stream))
     _check(s, "rnn_bwd_gru")
     return g
+
+
+def plan_search(op: int, dims: Dims, dtype_code: int, num_cu: int = 0):
+    """Every candidate plan of the recurrence (list of dicts) and the index
+    of the chosen one (-1 if none is feasible)."""
+    buf = (PlanCandidate * 512)()
+    n, best = ctypes.c_int(0), ctypes.c_int(-1)
+    s = load().rnn_plan_search(op, ctypes.byref(dims), dtype_code, int(num_cu), buf, 512,
+                               ctypes.byref(n), ctypes.byref(best))
+    if s not in (RNN_OK, RNN_ERR_UNSUPPORTED):
+        _check(s, "rnn_plan_search")
+    return [buf[i].as_dict() for i in range(n.value)], best.value
 
 
 def workspace_size_chunked(op: int, dims: Dims, chunk: int, dtype_code: int) -> int:

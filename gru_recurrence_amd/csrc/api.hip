@@ -132,6 +132,8 @@ int pipeline_override() {
     return !e || !e[0] ? -1 : e[0] == '0' ? 0 : 1;
 }
 int k_override() { return env_int("RNN355_REC_K"); }
+// RNN355_REC_KCW=4|8: k-chunks per wave of the multi-CU kernel.
+int kcw_override() { return env_int("RNN355_REC_KCW"); }
 // RNN355_REC_WIDE=0 serves Dh = 256 with the multi-CU kernel instead of the
 // one-CU kernel with split R.
 bool wide_enabled() {
@@ -145,15 +147,19 @@ unsigned spin_limit() {
     return v > 0 ? (unsigned)v : (1u << 22);
 }
 
-// Which recurrent kernel serves a shape: the one-CU MFMA kernel (bf16, Dh in
-// {32, 64, 128}), the one-CU kernel with R split over registers and LDS
-// (bf16, Dh = 256), the multi-CU kernel (bf16, Dh >= 256, Dh % 128 == 0),
-// or the LDS kernel (f32, other shapes whose R fits 64 KiB of LDS).
+// Which recurrent kernel serves a shape, and with which tiling: the fastest
+// feasible plan of the constraint search (plan_search.hip) over the
+// one-CU MFMA kernel (bf16, Dh in {32, 64, 128}), the one-CU kernel with R
+// split over registers and LDS (bf16, Dh = 256), the multi-CU kernel (bf16,
+// Dh >= 256, Dh % 128 == 0) and the LDS kernel (R of at most 64 KiB in
+// f32).  The environment overrides (RNN355_REC_BT, _K, _KCW, _WIDE=0) fix
+// or exclude variables of the search.
 struct Choice {
     int cell;
     RecPlan rec;
     WidePlan wide;
     McPlan mc;
+    PlanCand cand;
     bool use_wide;
     bool use_mc;
     bool ok;
@@ -163,28 +169,32 @@ Choice choose(int cell, const rnn_dims *d, rnn_dtype dt, int num_cu) {
     Choice c{};
     c.cell = cell;
     const bool bf16 = dt == RNN_BF16;
-    c.rec = plan_rec(cell, d->T, d->B, d->NH, d->Dh, bf16, num_cu, bt_override());
-    if (c.rec.kind == kRecMfma) {
-        c.ok = true;
-        return c;
+    const PlanFix fix{bt_override(), k_override(), kcw_override(), !wide_enabled()};
+    static thread_local PlanCand buf[kPlanMaxCands];
+    int best = -1;
+    plan_search(cell, d->T, d->B, d->NH, d->Dh, bf16, num_cu, fix, buf, kPlanMaxCands, &best);
+    if (best < 0) return c;
+    const PlanCand &p = buf[best];
+    c.cand = p;
+    switch (p.family) {
+        case kFamResident:
+            c.rec = plan_rec(cell, d->T, d->B, d->NH, d->Dh, true, num_cu, p.BT);
+            c.ok = c.rec.kind == kRecMfma && c.rec.BT == p.BT;
+            break;
+        case kFamLds:
+            // the LDS kernel's geometry (the launcher picks its bf16 or f32 variant)
+            c.rec = plan_rec(cell, d->T, d->B, d->NH, d->Dh, false, num_cu, p.BT);
+            c.ok = c.rec.kind == kRecSimple && c.rec.BT == p.BT;
+            break;
+        case kFamWide:
+            c.wide = plan_wide(cell, d->B, d->NH, d->Dh, bf16);
+            c.use_wide = c.ok = c.wide.ok != 0;
+            break;
+        case kFamMultiCu:
+            c.mc = plan_mc(cell, d->B, d->NH, d->Dh, num_cu, p.BT, p.K, p.kcw);
+            c.use_mc = c.ok = c.mc.ok && c.mc.K == p.K && c.mc.BT == p.BT && c.mc.kcw == p.kcw;
+            break;
     }
-    if (bf16 && wide_enabled()) {
-        c.wide = plan_wide(cell, d->B, d->NH, d->Dh, bf16);
-        if (c.wide.ok) {
-            c.use_wide = true;
-            c.ok = true;
-            return c;
-        }
-    }
-    if (bf16) {
-        c.mc = plan_mc(cell, d->B, d->NH, d->Dh, num_cu, bt_override(), k_override());
-        if (c.mc.ok) {
-            c.use_mc = true;
-            c.ok = true;
-            return c;
-        }
-    }
-    c.ok = c.rec.kind != kRecNone;
     return c;
 }
 
@@ -880,8 +890,10 @@ rnn_status rnn_plan_describe(rnn_op op, const rnn_dims *d, rnn_dtype dt, char *b
         return RNN_ERR_UNSUPPORTED;
     }
     const bool fwd = op == RNN_OP_FWD_LSTM || op == RNN_OP_FWD_GRU;
-    const char *proj = !fwd ? "" : pipelined(ch, d, dt, device_cus()) ? " input_proj=pipelined"
-                                                                        : " input_proj=serial";
+    char proj[96];
+    snprintf(proj, sizeof proj, " predicted_ns_per_step=%.0f%s", ch.cand.ns_total / d->T,
+             !fwd ? "" : pipelined(ch, d, dt, device_cus()) ? " input_proj=pipelined"
+                                                            : " input_proj=serial");
     if (ch.use_wide) {
         const WidePlan &p = ch.wide;
         snprintf(buf, len,
@@ -903,6 +915,46 @@ rnn_status rnn_plan_describe(rnn_op op, const rnn_dims *d, rnn_dtype dt, char *b
                  p.upt, proj);
     }
     return RNN_OK;
+}
+
+rnn_status rnn_plan_search(rnn_op op, const rnn_dims *d, rnn_dtype dt, int num_cu,
+                           rnn_plan_candidate *out, int max_out, int *n_out, int *chosen) {
+    if (!dims_ok(d) || !dtype_ok(dt) || max_out < 0 || (max_out > 0 && !out) || !n_out || !chosen)
+        return RNN_ERR_INVALID_ARG;
+    if (op < RNN_OP_FWD_LSTM || op > RNN_OP_REC_GRU) return RNN_ERR_INVALID_ARG;
+    const int cus = num_cu > 0 ? num_cu : device_cus();
+    const PlanFix fix{bt_override(), k_override(), kcw_override(), !wide_enabled()};
+    static thread_local PlanCand buf[kPlanMaxCands];
+    int best = -1;
+    const int n = plan_search(cell_of_op(op), d->T, d->B, d->NH, d->Dh, dt == RNN_BF16, cus, fix,
+                              buf, kPlanMaxCands, &best);
+    const int kept = std::min(n, kPlanMaxCands);
+    for (int i = 0; i < kept && i < max_out; ++i) {
+        const PlanCand &c = buf[i];
+        rnn_plan_candidate &o = out[i];
+        o.family = c.family;
+        o.rows_per_wg = c.BT;
+        o.wg_per_head = c.K;
+        o.blocks_per_wg = c.nb;
+        o.k_splits = c.ks;
+        o.kchunks_per_wave = c.kcw;
+        o.row_slots = c.r4;
+        o.frags_agpr = c.fa;
+        o.frags_vgpr = c.fv;
+        o.frags_lds = c.fl;
+        o.waves = c.waves;
+        o.grid = c.grid;
+        o.r_vgpr = c.r_vgpr;
+        o.wg_per_cu = c.wg_per_cu;
+        o.lds_bytes = c.lds;
+        o.feasible = c.feasible;
+        o.violated = c.violated;
+        o.ns_per_step = c.ns_step;
+        o.ns_total = c.ns_total;
+    }
+    *n_out = kept;
+    *chosen = best;
+    return best >= 0 ? RNN_OK : RNN_ERR_UNSUPPORTED;
 }
 
 rnn_status rnn_input_proj(int M, int K, int N, rnn_dtype dt, const void *x, const void *W,

@@ -173,13 +173,52 @@ struct McArgs {
 };
 
 // Plan for heads of Dh >= 256, Dh % 128 == 0; ok == 0 if none fits the
-// chip (every workgroup must be resident at once).  Pure host function.
-McPlan plan_mc(int cell, int B, int NH, int Dh, int num_cu, int bt_override, int k_override);
+// chip (every workgroup must be resident at once).  kcw: k-chunks of 32
+// per wave (4 or 8; 0: 8 where it divides Dh/32).  Pure host function.
+McPlan plan_mc(int cell, int B, int NH, int Dh, int num_cu, int bt_override, int k_override,
+               int kcw = 0);
 
 // Clears the exchange slots and (if clear_flag) the abort word, then
 // launches cooperatively.
 hipError_t launch_rec_mc(int cell, const McPlan &p, const McArgs &m, hipStream_t s,
                          bool clear_flag = true);
+
+// The recurrence's plan as an integer constraint problem (plan_search.hip):
+// every assignment of the plan variables, the first constraint it breaks
+// (kPlanOk if none) and the predicted time.  Pure host function.
+enum PlanFamily { kFamResident = 1, kFamWide = 2, kFamMultiCu = 3, kFamLds = 4 };
+enum PlanViolation {
+    kPlanOk = 0,
+    kPlanNotInstantiated = 1,  // no compiled kernel for these values
+    kPlanDivisibility = 2,
+    kPlanRegisters = 3,
+    kPlanLds = 4,
+    kPlanResidency = 5,        // not every workgroup resident at once
+    kPlanBatch = 6,            // more rows per workgroup than the batch or the MFMA holds
+    kPlanFixed = 7,            // excluded by an override
+};
+struct PlanCand {
+    int family;
+    int BT, K, nb, ks, kcw, r4;  // rows, workgroups per head tile, 16-unit blocks, k splits,
+                                 // k-chunks per wave, row slots per lane
+    int fa, fv, fl;              // split R: fragments per wave in AGPRs, VGPRs, LDS
+    int waves, grid, r_vgpr;     // waves per workgroup, workgroups, VGPRs per wave holding R
+    int wg_per_cu;               // workgroups that fit on one CU at once
+    long lds;                    // LDS bytes per workgroup
+    int feasible, violated;
+    double ns_step, ns_total;    // predicted per-step latency, T steps
+};
+// Overrides (0: free): rows per workgroup, workgroups per head tile, k-chunks
+// per wave; no_wide excludes the split-R family.
+struct PlanFix {
+    int bt, k, kcw;
+    bool no_wide;
+};
+constexpr int kPlanMaxCands = 512;
+// Writes up to cap candidates to buf, the fastest feasible one's index to
+// *best (-1 if none); returns the number enumerated.
+int plan_search(int cell, int T, int B, int NH, int Dh, bool bf16, int cus, const PlanFix &fix,
+                PlanCand *buf, int cap, int *best);
 
 // LSTM backward (rec_bwd.hip).
 struct BwdPlan {

@@ -281,12 +281,13 @@ hipError_t launch_mc_rows(const McPlan &p, const McArgs &m, hipStream_t s) {
 
 }  // namespace
 
-McPlan plan_mc(int cell, int B, int NH, int Dh, int num_cu, int bt_override, int k_override) {
+McPlan plan_mc(int cell, int B, int NH, int Dh, int num_cu, int bt_override, int k_override,
+               int kcw) {
     McPlan p{};
     const int G = cell == kLSTM ? 4 : 3;
     if (Dh < 256 || Dh % 128 != 0) return p;
     const int KC = Dh / 32;
-    p.kcw = KC % 8 == 0 ? 8 : 4;
+    p.kcw = (kcw == 4 && KC % 4 == 0) || (kcw == 8 && KC % 8 == 0) ? kcw : KC % 8 == 0 ? 8 : 4;
     p.ks = KC / p.kcw;
     const int nb_max = 8 / p.ks;  // at most 8 waves (512 threads) per workgroup
     if (nb_max < 1) return p;

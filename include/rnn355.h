@@ -183,6 +183,46 @@ rnn_status rnn_fwd_gru(const rnn_dims *d, rnn_dtype dt,
                        void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * The recurrence's plan as an integer constraint problem (FlashRNN card,
+ * paperdance.org/p/2412.07752, abstract: tiling from polyhedral-like
+ * integer constraints with divisibility, solved as an integer CSP; blog.
+ * hotdry.top 2025-09-21, paragraph on hardware-aware auto-tuning: register
+ * total, SRAM size and matrix-unit tile in, tiling out).  Every assignment
+ * of the plan variables for the recurrence of `op` on d: its family, its
+ * integers, the first constraint it breaks (0 if none) and the predicted
+ * time.  The forward and recurrence calls run the candidate *chosen
+ * returns.  num_cu <= 0: the current device's compute units.  The
+ * RNN355_REC_BT / _K / _KCW / _WIDE=0 overrides act as fixed variables.
+ * Writes min(n, max_out) candidates to out (out may be NULL with max_out
+ * 0), the number enumerated to *n_out and the chosen index to *chosen (-1
+ * and RNN_ERR_UNSUPPORTED if no candidate is feasible).  Host only.
+ */
+typedef struct rnn_plan_candidate {
+    int family;           /* 1 one CU per (head, rows), R in VGPRs; 2 one CU per (head,
+                             row), R split over AGPRs, VGPRs, LDS; 3 several CUs per head;
+                             4 R in LDS */
+    int rows_per_wg;      /* BT */
+    int wg_per_head;      /* workgroups per (head, row tile) */
+    int blocks_per_wg;    /* 16-unit blocks */
+    int k_splits;         /* waves per block (k-range splits) */
+    int kchunks_per_wave; /* 32-deep k-chunks per wave */
+    int row_slots;        /* register row slots per lane */
+    int frags_agpr, frags_vgpr, frags_lds;  /* family 2: R fragments per wave */
+    int waves;            /* per workgroup */
+    int grid;             /* workgroups */
+    int r_vgpr;           /* VGPRs per wave holding R */
+    int wg_per_cu;        /* workgroups that fit on one CU at once */
+    long long lds_bytes;  /* per workgroup */
+    int feasible;
+    int violated;         /* 1 not compiled, 2 divisibility, 3 registers, 4 LDS,
+                             5 residency, 6 batch, 7 override */
+    double ns_per_step;   /* predicted */
+    double ns_total;      /* predicted, T steps */
+} rnn_plan_candidate;
+rnn_status rnn_plan_search(rnn_op op, const rnn_dims *d, rnn_dtype dt, int num_cu,
+                           rnn_plan_candidate *out, int max_out, int *n_out, int *chosen);
+
+/*
  * Stacked layers (blog.hotdry.top 2025-09-21, the list of framework-level
  * optimisations, first item: multi-layer RNNs).  Layer l > 0 takes layer
  * l-1's output sequence h_1..h_T as its input x (width H = NH*Dh; in bf16
