@@ -19,12 +19,19 @@ constexpr int ROWB = BK * 2;                 // bytes per LDS row
 constexpr int OPB = BM * ROWB;               // bytes per operand per stage (16 KiB)
 constexpr int STB = 2 * OPB;                 // bytes per stage (32 KiB)
 constexpr size_t LDS_BYTES = (size_t)NST * STB;
+constexpr int NST_ALONE = 5;  // the stand-alone kernel: the whole 160 KiB
+constexpr size_t LDS_BYTES_ALONE = (size_t)NST_ALONE * STB;
 static_assert(BM == kGemmRowTile && BN == kGemmColTile, "row-panel counters assume the output tile");
+
+// Row r of a tile keeps its k chunk c (16 bytes) in slot c ^ swz(r): any 16
+// consecutive rows (or 8) read at one chunk then hit 16 (or 8) different
+// 16-byte bank groups of a 256-byte (128-byte) LDS access phase.
+__device__ __forceinline__ int swz(int r) { return ((r >> 2) & 3) ^ (r & 2); }
 
 // Issue the loads of one operand tile (256 rows x 32 k) into `dst`: 1024
 // chunks of 16 bytes, two per thread; chunk q goes to LDS byte 16q, i.e.
-// row q/4, slot q%4, holding k chunk (q%4) ^ ((row >> 1) & 3).  Rows past R
-// read row R-1 (their products only reach outputs that are not stored).
+// row q/4, slot q%4, holding k chunk (q%4) ^ swz(row).  Rows past R read
+// row R-1 (their products only reach outputs that are not stored).
 // AUX is the loads' cache policy (16: device scope, for operands that other
 // workgroups of the same launch write).
 template <int AUX = 0>
@@ -34,27 +41,28 @@ __device__ __forceinline__ void dma_tile(const uint16_t *__restrict__ P, long ld
     for (int i = 0; i < 2; ++i) {
         const int q = tid + NTHR * i;
         const int r = q >> 2, slot = q & 3;
-        const int chunk = slot ^ ((r >> 1) & 3);
+        const int chunk = slot ^ swz(r);
         const int gr = min(r0 + r, R - 1);
         const uint16_t *src = P + (long)gr * ld + k0 + chunk * 8;
         __builtin_amdgcn_global_load_lds(src, dst + (64 * wave + NTHR * i) * 16, 16, 0, AUX);
     }
 }
 
-// vmcnt(n) for n in {0, 4, 8}: loads of later tiles may stay in flight.
+// vmcnt(4 * later): the loads of `later` later tiles may stay in flight.
 __device__ __forceinline__ void wait_tiles_after(int later) {
-    if (later >= 2) __builtin_amdgcn_s_waitcnt(0x0F78);       // vmcnt(8)
+    if (later >= 3) __builtin_amdgcn_s_waitcnt(0x0F7C);       // vmcnt(12)
+    else if (later == 2) __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
     else if (later == 1) __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
     else __builtin_amdgcn_s_waitcnt(0x0F70);                  // vmcnt(0)
 }
 
 // The contraction's work for workgroup `wg` of `nwg`: output tiles wg,
 // wg + nwg, ... of batch / split slice blockIdx.z (a persistent loop when
-// nwg is smaller than the tile count).  `lds` is LDS_BYTES of dynamic LDS.
-// Before each tile every thread calls pre(row tile), ahead of the barrier
-// that starts the tile (a wait for A's rows goes there); A_AUX is the cache
-// policy of A's loads.
-template <int A_AUX, class PreTile>
+// nwg is smaller than the tile count).  `lds` is NS * STB bytes of dynamic
+// LDS: a ring of NS K tiles (NS - 1 in flight).  Before each tile every
+// thread calls pre(row tile), ahead of the barrier that starts the tile (a
+// wait for A's rows goes there); A_AUX is the cache policy of A's loads.
+template <int A_AUX, int NS = NST, class PreTile>
 __device__ __forceinline__ void gemm_dma_tiles_pre(const GemmArgs &g, int wg, int nwg,
                                                    lds_char *lds, PreTile &&pre) {
     const uint32_t lbase = (uint32_t)(uintptr_t)lds;
@@ -76,7 +84,7 @@ __device__ __forceinline__ void gemm_dma_tiles_pre(const GemmArgs &g, int wg, in
     // this lane's fragment byte offsets inside a stage, for the two 16-deep
     // k steps of a tile: row l32 of the wave's first A / B tile, chunk
     // 2*kc + lh in its swizzled slot (rows of the other tiles: +32 rows)
-    const int sw = (l32 >> 1) & 3;
+    const int sw = swz(l32);  // the tiles' row bases are multiples of 32
     uint32_t offA[2], offB[2];
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
@@ -119,36 +127,50 @@ __device__ __forceinline__ void gemm_dma_tiles_pre(const GemmArgs &g, int wg, in
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     auto issue = [&](int kt) {
-        lds_char *st = lds + ((kt - kt0) & (NST - 1)) * STB;
+        lds_char *st = lds + ((kt - kt0) % NS) * STB;
         dma_tile<A_AUX>(A, g.lda, m0, kt * BK, g.M, st, tid, wave);
         dma_tile(B, g.ldb, n0, kt * BK, g.N, st + OPB, tid, wave);
     };
 #pragma unroll
-    for (int p = 0; p < NST - 1; ++p)
+    for (int p = 0; p < NS - 1; ++p)
         if (kt0 + p < kt1) issue(kt0 + p);
 
     for (int kt = kt0; kt < kt1; ++kt) {
         // this thread's loads of tile kt have landed; after the barrier,
         // everyone's have, and every wave is done with tile kt-1's stage
-        wait_tiles_after(min(2, kt1 - 1 - kt));
+        wait_tiles_after(min(NS - 2, kt1 - 1 - kt));
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        const uint32_t sb = lbase + (uint32_t)(((kt - kt0) & (NST - 1)) * STB);
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-            bf16x8 a0, a1, a2, a3, b0, b1;
-            asm volatile(
-                "ds_read_b128 %0, %6\n\t"
-                "ds_read_b128 %1, %6 offset:2048\n\t"
-                "ds_read_b128 %2, %6 offset:4096\n\t"
-                "ds_read_b128 %3, %6 offset:6144\n\t"
-                "ds_read_b128 %4, %7\n\t"
-                "ds_read_b128 %5, %7 offset:2048\n\t"
-                "s_waitcnt lgkmcnt(0)"
-                : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(b0), "=&v"(b1)
-                : "v"(sb + offA[kc]), "v"(sb + offB[kc])
-                : "memory");
+        // refill the stage that tile kt-1 used at once (no wave reads it any
+        // more): the loads then have the whole tile's work to land
+        if (kt + NS - 1 < kt1) issue(kt + NS - 1);
+        const uint32_t sb = lbase + (uint32_t)(((kt - kt0) % NS) * STB);
+        // both k-steps' fragments requested at once; the first k-step's
+        // MFMAs start when its six reads are in (lgkmcnt(6)) and run while
+        // the second's land.  The waits are tied to the fragment registers
+        // so that no use moves above them.
+        bf16x8 a0, a1, a2, a3, b0, b1, c0, c1, c2, c3, d0, d1;
+        asm volatile(
+            "ds_read_b128 %0, %12\n\t"
+            "ds_read_b128 %1, %12 offset:2048\n\t"
+            "ds_read_b128 %2, %12 offset:4096\n\t"
+            "ds_read_b128 %3, %12 offset:6144\n\t"
+            "ds_read_b128 %4, %13\n\t"
+            "ds_read_b128 %5, %13 offset:2048\n\t"
+            "ds_read_b128 %6, %14\n\t"
+            "ds_read_b128 %7, %14 offset:2048\n\t"
+            "ds_read_b128 %8, %14 offset:4096\n\t"
+            "ds_read_b128 %9, %14 offset:6144\n\t"
+            "ds_read_b128 %10, %15\n\t"
+            "ds_read_b128 %11, %15 offset:2048"
+            : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(b0), "=&v"(b1), "=&v"(c0),
+              "=&v"(c1), "=&v"(c2), "=&v"(c3), "=&v"(d0), "=&v"(d1)
+            : "v"(sb + offA[0]), "v"(sb + offB[0]), "v"(sb + offA[1]), "v"(sb + offB[1])
+            : "memory");
+        asm volatile("s_waitcnt lgkmcnt(6)"
+                     : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3), "+v"(b0), "+v"(b1));
+        {
             const bf16x8 af[4] = {a0, a1, a2, a3}, bfr[2] = {b0, b1};
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -156,10 +178,19 @@ __device__ __forceinline__ void gemm_dma_tiles_pre(const GemmArgs &g, int wg, in
                 for (int j = 0; j < 2; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
         }
+        // keep the first k-step's MFMAs above the second wait
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(c0), "+v"(c1), "+v"(c2), "+v"(c3), "+v"(d0), "+v"(d1));
+        {
+            const bf16x8 af[4] = {c0, c1, c2, c3}, bfr[2] = {d0, d1};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
         asm volatile("" ::: "memory");
-        // refill the stage that tile kt-1 used (every wave has passed this
-        // iteration's barrier, so none still reads it)
-        if (kt + NST - 1 < kt1) issue(kt + NST - 1);
     }
 
     // epilogue: register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4, column l%32
@@ -175,21 +206,43 @@ __device__ __forceinline__ void gemm_dma_tiles_pre(const GemmArgs &g, int wg, in
         ldc = g.N;
         direct = false;
     }
+    const bool acc_old = direct && g.accumulate;
+    // the bias of this lane's two columns, loaded before any store
+    float bv[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int n = n0 + wn * 64 + j * 32 + l32;
-        if (n >= g.N) continue;
-        const float bv = (direct && g.bias) ? g.bias[n] : 0.f;
+        bv[j] = (direct && g.bias && n < g.N) ? g.bias[n] : 0.f;
+    }
+    if (m0 + BM <= g.M && n0 + BN <= g.N && !acc_old) {
+        // a whole tile and nothing to read back: stores only, without bounds
+        // checks or loads between them (with either, the compiler waits for
+        // every earlier store before the next -- a round trip per store)
+        float *base = C + (long)(m0 + wm * 128 + 4 * lh) * ldc + n0 + wn * 64 + l32;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int m = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-                if (m < g.M) {
-                    float v = acc[i][j][r] + bv;
-                    float *dst = C + (long)m * ldc + n;
-                    if (direct && g.accumulate) v += *dst;
-                    *dst = v;
+                float *row = base + (long)(i * 32 + 8 * (r >> 2) + (r & 3)) * ldc;
+#pragma unroll
+                for (int j = 0; j < 2; ++j) row[j * 32] = acc[i][j][r] + bv[j];
+            }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int n = n0 + wn * 64 + j * 32 + l32;
+            if (n >= g.N) continue;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                    if (m < g.M) {
+                        float v = acc[i][j][r] + bv[j];
+                        float *dst = C + (long)m * ldc + n;
+                        if (acc_old) v += *dst;
+                        *dst = v;
+                    }
                 }
             }
         }
@@ -207,8 +260,10 @@ __device__ __forceinline__ void gemm_dma_tiles_pre(const GemmArgs &g, int wg, in
     }  // tiles
 }
 
+// The ring of NST stages (LDS_BYTES): the kernels that share a CU's LDS
+// with a recurrence.
 __device__ __forceinline__ void gemm_dma_tiles(const GemmArgs &g, int wg, int nwg, lds_char *lds) {
-    gemm_dma_tiles_pre<0>(g, wg, nwg, lds, [](int) {});
+    gemm_dma_tiles_pre<0, NST>(g, wg, nwg, lds, [](int) {});
 }
 
 }  // namespace dma

@@ -10,13 +10,15 @@
 //
 // Block tile 256x256, K in tiles of 32, 512 threads = 8 waves in a 2 (m) x 4
 // (n) grid, each wave 128x64 = 4x2 tiles of v_mfma_f32_32x32x16_bf16.  LDS
-// holds a ring of four K tiles (4 x 32 KiB); the loads of tile kt+3 are
-// issued while tile kt is multiplied, so three tiles are in flight and no
-// register is spent on staging.  A load instruction moves 16 bytes per lane
-// and writes the wave's 64 lanes as one contiguous KiB of LDS, so a tile is
-// stored without padding: 64-byte rows (32 k), and in row r the 16-byte
-// chunk c of the k range sits in slot c ^ ((r >> 1) & 3).  The fragment
-// reads of an MFMA (32 rows, one chunk) then touch every bank group equally.
+// holds a ring of K tiles (32 KiB each: five in this kernel, the whole 160
+// KiB; four where a recurrence shares the CU); the loads of tile kt+4 (kt+3)
+// are issued right after the barrier that starts tile kt, so four (three)
+// tiles are in flight and no register is spent on staging.  A load
+// instruction moves 16 bytes per lane and writes the wave's 64 lanes as one
+// contiguous KiB of LDS, so a tile is stored without padding: 64-byte rows
+// (32 k), and in row r the 16-byte chunk c of the k range sits in slot
+// c ^ swz(r) (gemm_dma.h): the 16 lanes of one access phase of a fragment
+// read (16 rows, one chunk) touch 16 different bank groups.
 //
 // The fragment reads are inline assembly on purpose: the compiler tracks
 // loads into LDS only coarsely and would otherwise wait for every load in
@@ -37,7 +39,7 @@ namespace {
 
 __global__ __launch_bounds__(NTHR) void gemm_dma_kernel(GemmArgs g) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    gemm_dma_tiles(g, blockIdx.x, gridDim.x, (lds_char *)smem);
+    gemm_dma_tiles_pre<0, NST_ALONE>(g, blockIdx.x, gridDim.x, (lds_char *)smem, [](int) {});
 }
 
 // dst[b][c][r] = src[b][r][c] for bf16 matrices [R][C] (row pitch C), in
@@ -116,12 +118,13 @@ hipError_t launch_gemm_dma(const GemmArgs &g0, int batch, hipStream_t s, int max
     static hipError_t attr = hipSuccess;
     std::call_once(once, [] {
         attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_dma_kernel),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES_ALONE);
     });
     if (attr != hipSuccess) return attr;
     const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
     const int wgs = max_wg > 0 && max_wg < tiles ? max_wg : tiles;
-    hipLaunchKernelGGL(gemm_dma_kernel, dim3(wgs, 1, batch * g.ksplit), dim3(NTHR), LDS_BYTES, s, g);
+    hipLaunchKernelGGL(gemm_dma_kernel, dim3(wgs, 1, batch * g.ksplit), dim3(NTHR), LDS_BYTES_ALONE, s,
+                       g);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || g.ksplit == 1) return e;
     return launch_splitk_reduce(g, batch, s);
