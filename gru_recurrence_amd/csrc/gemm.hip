@@ -230,21 +230,43 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(GemmArgs g) {
         ldc = g.N;
         direct = false;
     }
+    const bool acc_old = direct && g.accumulate;
+    // the bias of this lane's two columns, loaded before any store
+    float bv[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int n = n0 + wn * 64 + j * 32 + l32;
-        if (n >= g.N) continue;
-        const float bv = (direct && g.bias) ? g.bias[n] : 0.f;
+        bv[j] = (direct && g.bias && n < g.N) ? g.bias[n] : 0.f;
+    }
+    if (m0 + BM <= g.M && n0 + BN <= g.N && !acc_old) {
+        // a whole tile and nothing to read back: stores only, without bounds
+        // checks or loads between them (with either, the compiler waits for
+        // every earlier store before the next -- a round trip per store)
+        float *base = C + (long)(m0 + wm * 128 + 4 * lh) * ldc + n0 + wn * 64 + l32;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int m = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-                if (m < g.M) {
-                    float v = acc[i][j][r] + bv;
-                    float *dst = C + (long)m * ldc + n;
-                    if (direct && g.accumulate) v += *dst;
-                    *dst = v;
+                float *row = base + (long)(i * 32 + 8 * (r >> 2) + (r & 3)) * ldc;
+#pragma unroll
+                for (int j = 0; j < 2; ++j) row[j * 32] = acc[i][j][r] + bv[j];
+            }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int n = n0 + wn * 64 + j * 32 + l32;
+            if (n >= g.N) continue;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                    if (m < g.M) {
+                        float v = acc[i][j][r] + bv[j];
+                        float *dst = C + (long)m * ldc + n;
+                        if (acc_old) v += *dst;
+                        *dst = v;
+                    }
                 }
             }
         }
