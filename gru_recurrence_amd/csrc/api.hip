@@ -348,6 +348,8 @@ rnn_status forward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, con
         // 8 (whole XCD rounds), at most one per tile
         const long tiles = panels * a.ready_target;
         int n_gemm = ((cus - ch.rec.grid) / 8) * 8;
+        const int want = env_int("RNN355_FUSED_GEMM_WGS");
+        if (want >= 8 && want / 8 * 8 < n_gemm) n_gemm = want / 8 * 8;
         if (n_gemm > tiles) n_gemm = (int)tiles;
         if (n_gemm < 8) n_gemm = (int)std::min<long>(8, tiles);
         return ok(launch_fwd_fused(cell, ch.rec, a, g, n_gemm, s)) ? RNN_OK : RNN_ERR_HIP;

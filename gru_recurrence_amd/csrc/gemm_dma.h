@@ -93,16 +93,27 @@ __device__ __forceinline__ void gemm_dma_tiles_pre(const GemmArgs &g, int wg, in
         offB[kc] = (uint32_t)(OPB + (wn * 64 + l32) * ROWB + slot * 16);
     }
 
-    // runs of 8 row tiles, row tile 8q + x of a run on XCD x (workgroup i
-    // runs on XCD i % 8; nwg is a multiple of 8 or the tile count), all its
-    // column tiles there; rows past the last whole run in order
+    // Workgroup i runs on XCD i % 8 (nwg is a multiple of 8 or the tile
+    // count), so tile t goes to XCD t % 8.  Where the tile counts divide,
+    // XCD x = 2 xr + xc takes the row tiles xr, xr + 4, ... in order and the
+    // column tiles of half xc: its share of W^T (half the columns) stays in its L2 while the row panels stream.  Otherwise runs
+    // of 8 row tiles, row tile 8q + x of a run on XCD x with all its column
+    // tiles, rows past the last whole run in order.  Either way each XCD
+    // finishes its row panels in time order.
     const int tiles_n = (g.N + BN - 1) / BN;
     const int tiles_m = (g.M + BM - 1) / BM;
     const int tiles = tiles_m * tiles_n;
     const int run = 8 * tiles_n, full = (tiles_m >> 3) * run;
+    const bool split = (tiles_m & 3) == 0 && (tiles_n & 1) == 0 && (nwg & 7) == 0;
+    const int half_n = tiles_n >> 1;
     for (int t = wg; t < tiles; t += nwg) {
     int mt, nt;
-    if (t < full) {
+    if (split) {
+        const int x = t & 7, k = t >> 3;
+        const int p = k / half_n, c = k - p * half_n;
+        mt = (x >> 1) + 4 * p;
+        nt = (x & 1) * half_n + c;
+    } else if (t < full) {
         const int q = t / run, i = t - q * run;
         mt = 8 * q + (i & 7);
         nt = i >> 3;
@@ -135,63 +146,74 @@ __device__ __forceinline__ void gemm_dma_tiles_pre(const GemmArgs &g, int wg, in
     for (int p = 0; p < NS - 1; ++p)
         if (kt0 + p < kt1) issue(kt0 + p);
 
+    // Pipelined at k-step granularity (two 16-deep k-steps per tile): the
+    // reads of the next k-step are in flight while the current one's MFMAs
+    // run, and the barrier that makes tile kt+1 visible sits between tile
+    // kt's two k-steps, so its wait overlaps MFMAs already issued.  The
+    // stage refilled at that barrier is the one tile kt-1 used: every wave's
+    // reads of it completed before its MFMAs of kt-1, i.e. before the barrier.
+#define RNN355_READ_HALF(kt, kc, a0, a1, a2, a3, b0, b1)                                     \
+    do {                                                                                     \
+        const uint32_t sb_ = lbase + (uint32_t)((((kt) - kt0) % NS) * STB);                  \
+        asm volatile("ds_read_b128 %0, %6\n\t"                                              \
+                     "ds_read_b128 %1, %6 offset:2048\n\t"                                  \
+                     "ds_read_b128 %2, %6 offset:4096\n\t"                                  \
+                     "ds_read_b128 %3, %6 offset:6144\n\t"                                  \
+                     "ds_read_b128 %4, %7\n\t"                                              \
+                     "ds_read_b128 %5, %7 offset:2048"                                       \
+                     : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(b0), "=&v"(b1)      \
+                     : "v"(sb_ + offA[kc]), "v"(sb_ + offB[kc])                              \
+                     : "memory");                                                            \
+    } while (0)
+// the 8 MFMAs of one k-step once its reads are in (WAIT: the lgkmcnt that
+// leaves the six reads issued after them in flight, or 0); the wait is tied
+// to the fragment registers so that no use moves above it
+#define RNN355_MFMA_HALF(WAIT, a0, a1, a2, a3, b0, b1)                                       \
+    do {                                                                                     \
+        asm volatile("s_waitcnt lgkmcnt(" #WAIT ")"                                          \
+                     : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3), "+v"(b0), "+v"(b1));          \
+        acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0][0], 0, 0, 0);     \
+        acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[0][1], 0, 0, 0);     \
+        acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc[1][0], 0, 0, 0);     \
+        acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[1][1], 0, 0, 0);     \
+        acc[2][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, b0, acc[2][0], 0, 0, 0);     \
+        acc[2][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, b1, acc[2][1], 0, 0, 0);     \
+        acc[3][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a3, b0, acc[3][0], 0, 0, 0);     \
+        acc[3][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a3, b1, acc[3][1], 0, 0, 0);     \
+                                                                                             \
+    } while (0)
+
+    // tile kt0: landed for everyone
+    wait_tiles_after(min(NS - 2, kt1 - 1 - kt0));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    bf16x8 x0, x1, x2, x3, x4, x5, y0, y1, y2, y3, y4, y5;
+    RNN355_READ_HALF(kt0, 0, x0, x1, x2, x3, x4, x5);
     for (int kt = kt0; kt < kt1; ++kt) {
-        // this thread's loads of tile kt have landed; after the barrier,
-        // everyone's have, and every wave is done with tile kt-1's stage
-        wait_tiles_after(min(NS - 2, kt1 - 1 - kt));
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        // refill the stage that tile kt-1 used at once (no wave reads it any
-        // more): the loads then have the whole tile's work to land
-        if (kt + NS - 1 < kt1) issue(kt + NS - 1);
-        const uint32_t sb = lbase + (uint32_t)(((kt - kt0) % NS) * STB);
-        // both k-steps' fragments requested at once; the first k-step's
-        // MFMAs start when its six reads are in (lgkmcnt(6)) and run while
-        // the second's land.  The waits are tied to the fragment registers
-        // so that no use moves above them.
-        bf16x8 a0, a1, a2, a3, b0, b1, c0, c1, c2, c3, d0, d1;
-        asm volatile(
-            "ds_read_b128 %0, %12\n\t"
-            "ds_read_b128 %1, %12 offset:2048\n\t"
-            "ds_read_b128 %2, %12 offset:4096\n\t"
-            "ds_read_b128 %3, %12 offset:6144\n\t"
-            "ds_read_b128 %4, %13\n\t"
-            "ds_read_b128 %5, %13 offset:2048\n\t"
-            "ds_read_b128 %6, %14\n\t"
-            "ds_read_b128 %7, %14 offset:2048\n\t"
-            "ds_read_b128 %8, %14 offset:4096\n\t"
-            "ds_read_b128 %9, %14 offset:6144\n\t"
-            "ds_read_b128 %10, %15\n\t"
-            "ds_read_b128 %11, %15 offset:2048"
-            : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(b0), "=&v"(b1), "=&v"(c0),
-              "=&v"(c1), "=&v"(c2), "=&v"(c3), "=&v"(d0), "=&v"(d1)
-            : "v"(sb + offA[0]), "v"(sb + offB[0]), "v"(sb + offA[1]), "v"(sb + offB[1])
-            : "memory");
-        asm volatile("s_waitcnt lgkmcnt(6)"
-                     : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3), "+v"(b0), "+v"(b1));
-        {
-            const bf16x8 af[4] = {a0, a1, a2, a3}, bfr[2] = {b0, b1};
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        RNN355_READ_HALF(kt, 1, y0, y1, y2, y3, y4, y5);
+        RNN355_MFMA_HALF(6, x0, x1, x2, x3, x4, x5);
+        const bool more = kt + 1 < kt1;
+        if (more) {
+            // this thread's loads of tile kt+1 landed (later tiles may fly);
+            // after the barrier everyone's have
+            const int later = min(NS - 3, kt1 - 2 - kt);
+            wait_tiles_after(later < 0 ? 0 : later);
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
         }
-        // keep the first k-step's MFMAs above the second wait
-        __builtin_amdgcn_sched_barrier(0);
-        asm volatile("s_waitcnt lgkmcnt(0)"
-                     : "+v"(c0), "+v"(c1), "+v"(c2), "+v"(c3), "+v"(d0), "+v"(d1));
-        {
-            const bf16x8 af[4] = {c0, c1, c2, c3}, bfr[2] = {d0, d1};
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-        }
-        asm volatile("" ::: "memory");
+        // the next tile's first k-step (the last tile re-reads its own, unused,
+        // so that the count of reads behind y stays six on every path)
+        RNN355_READ_HALF(more ? kt + 1 : kt, 0, x0, x1, x2, x3, x4, x5);
+        RNN355_MFMA_HALF(6, y0, y1, y2, y3, y4, y5);
+        // refill the stage of tile kt-1 (at kt0: the stage the prologue
+        // left empty) with tile kt-1+NS
+        if (more && kt - 1 + NS < kt1) issue(kt - 1 + NS);
     }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the unused reads
+#undef RNN355_READ_HALF
+#undef RNN355_MFMA_HALF
 
     // epilogue: register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4, column l%32
     float *C;
