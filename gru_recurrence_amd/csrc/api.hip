@@ -559,10 +559,24 @@ rnn_status backward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, co
 
     // 1. h_{t-1} as bf16; gate inputs for all t at once
     if (!ok(launch_hprev_bf16(h0, h_seq, hprev, (long)B * H, (long)M * H, stream))) return RNN_ERR_HIP;
-    if (input_proj(M, Din, N, dt, x, W, b, A, clear_status ? (uint32_t *)ws : nullptr, stream,
-                   nullptr, wt) != RNN_OK)
-        return RNN_ERR_HIP;
-    {
+    uint32_t *clear = clear_status ? (uint32_t *)ws : nullptr;
+    if (lstm && GD % kGemmColTile == 0 && gemm_dma_ok(Din) && gemm_dma_ok(Dh)) {
+        // one contraction: the K tiles of x W^T, then for the column tiles of
+        // head n those of h_{t-1}[:, n Dh:(n+1) Dh] R_n (R^T per head)
+        if (!ok(launch_transpose_bf16(Wb, wt, Din, N, 1, stream))) return RNN_ERR_HIP;
+        if (!ok(launch_transpose_bf16(Rb, rt, Dh, GD, NH, stream))) return RNN_ERR_HIP;
+        GemmArgs g{};
+        g.M = M; g.N = N; g.K = Din;
+        g.A = xb; g.lda = Din;
+        g.B = wt; g.ldb = Din;
+        g.bias = b; g.C = A; g.ldc = N;
+        g.clear_words = clear;
+        g.A2 = hprev; g.lda2 = H; g.K2 = Dh; g.seg_n = GD;
+        g.B2 = rt; g.ldb2 = Dh;  // row n = head n/GD's gate column n%GD
+        if (!ok(launch_gemm_dma(g, 1, stream))) return RNN_ERR_HIP;
+    } else {
+        if (input_proj(M, Din, N, dt, x, W, b, A, clear, stream, nullptr, wt) != RNN_OK)
+            return RNN_ERR_HIP;
         GemmArgs g{};  // h_{t-1} R per head: added to A (LSTM) or into S (GRU)
         g.M = M; g.N = GD; g.K = Dh;
         g.A = hprev; g.lda = H; g.strideA = Dh;       // row m, k = unit of head n
@@ -654,7 +668,7 @@ struct CallEvents {
     }
     ~CallEvents() {
         for (hipEvent_t v : e)
-            if (v) hipEventDestroy(v);
+            if (v) (void)hipEventDestroy(v);
     }
 };
 

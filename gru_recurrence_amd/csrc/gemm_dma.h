@@ -62,7 +62,8 @@ __device__ __forceinline__ void wait_tiles_after(int later) {
 // LDS: a ring of NS K tiles (NS - 1 in flight).  Before each tile every
 // thread calls pre(row tile), ahead of the barrier that starts the tile (a
 // wait for A's rows goes there); A_AUX is the cache policy of A's loads.
-template <int A_AUX, int NS = NST, class PreTile>
+// SEG2: the K tiles of the second segment (A2, B2) follow those of A, B.
+template <int A_AUX, int NS = NST, bool SEG2 = false, class PreTile>
 __device__ __forceinline__ void gemm_dma_tiles_pre(const GemmArgs &g, int wg, int nwg,
                                                    lds_char *lds, PreTile &&pre) {
     const uint32_t lbase = (uint32_t)(uintptr_t)lds;
@@ -77,7 +78,8 @@ __device__ __forceinline__ void gemm_dma_tiles_pre(const GemmArgs &g, int wg, in
 
     if (g.clear_words && wg == 0 && blockIdx.z == 0 && tid < 64) g.clear_words[tid] = 0u;
 
-    const int ktiles = g.K / BK;
+    const int ktiles1 = g.K / BK;
+    const int ktiles = SEG2 ? ktiles1 + g.K2 / BK : ktiles1;
     const int per = (ktiles + g.ksplit - 1) / g.ksplit;
     const int kt0 = slice * per, kt1 = min(ktiles, kt0 + per);
 
@@ -137,10 +139,18 @@ __device__ __forceinline__ void gemm_dma_tiles_pre(const GemmArgs &g, int wg, in
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+    // the second segment's A columns of this tile's column block
+    const uint16_t *A2 = SEG2 ? g.A2 + (long)(n0 / g.seg_n) * g.K2 : nullptr;
     auto issue = [&](int kt) {
         lds_char *st = lds + ((kt - kt0) % NS) * STB;
-        dma_tile<A_AUX>(A, g.lda, m0, kt * BK, g.M, st, tid, wave);
-        dma_tile(B, g.ldb, n0, kt * BK, g.N, st + OPB, tid, wave);
+        if (!SEG2 || kt < ktiles1) {
+            dma_tile<A_AUX>(A, g.lda, m0, kt * BK, g.M, st, tid, wave);
+            dma_tile(B, g.ldb, n0, kt * BK, g.N, st + OPB, tid, wave);
+        } else {
+            const int k2 = (kt - ktiles1) * BK;
+            dma_tile<A_AUX>(A2, g.lda2, m0, k2, g.M, st, tid, wave);
+            dma_tile(g.B2, g.ldb2, n0, k2, g.N, st + OPB, tid, wave);
+        }
     };
 #pragma unroll
     for (int p = 0; p < NS - 1; ++p)

@@ -42,6 +42,13 @@ __global__ __launch_bounds__(NTHR) void gemm_dma_kernel(GemmArgs g) {
     gemm_dma_tiles_pre<0, NST_ALONE>(g, blockIdx.x, gridDim.x, (lds_char *)smem, [](int) {});
 }
 
+// The same with a second K segment per column block (GemmArgs::A2, B2).
+__global__ __launch_bounds__(NTHR) void gemm_dma_seg2_kernel(GemmArgs g) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    gemm_dma_tiles_pre<0, NST_ALONE, true>(g, blockIdx.x, gridDim.x, (lds_char *)smem,
+                                           [](int) {});
+}
+
 // dst[b][c][r] = src[b][r][c] for bf16 matrices [R][C] (row pitch C), in
 // 64x64 tiles through LDS with 16-byte loads and stores where a row of the
 // tile is whole and aligned (C % 8 == 0 for loads, R % 8 == 0 for stores);
@@ -114,17 +121,28 @@ hipError_t launch_gemm_dma(const GemmArgs &g0, int batch, hipStream_t s, int max
     if (!gemm_dma_ok(g.K)) return hipErrorInvalidValue;
     if (g.ksplit > 1 && !g.partial) return hipErrorInvalidValue;
     if (g.ready && (g.ksplit > 1 || batch != 1)) return hipErrorInvalidValue;
+    const bool seg2 = g.A2 != nullptr;
+    if (seg2 && (!g.B2 || batch != 1 || g.ksplit != 1 || g.accumulate || !gemm_dma_ok(g.K2) ||
+                 g.seg_n <= 0 || g.seg_n % BN != 0 || g.N % g.seg_n != 0))
+        return hipErrorInvalidValue;
     static std::once_flag once;
     static hipError_t attr = hipSuccess;
     std::call_once(once, [] {
         attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_dma_kernel),
                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES_ALONE);
+        if (attr == hipSuccess)
+            attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_dma_seg2_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)LDS_BYTES_ALONE);
     });
     if (attr != hipSuccess) return attr;
     const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
     const int wgs = max_wg > 0 && max_wg < tiles ? max_wg : tiles;
-    hipLaunchKernelGGL(gemm_dma_kernel, dim3(wgs, 1, batch * g.ksplit), dim3(NTHR), LDS_BYTES_ALONE, s,
-                       g);
+    if (seg2)
+        hipLaunchKernelGGL(gemm_dma_seg2_kernel, dim3(wgs, 1, 1), dim3(NTHR), LDS_BYTES_ALONE, s, g);
+    else
+        hipLaunchKernelGGL(gemm_dma_kernel, dim3(wgs, 1, batch * g.ksplit), dim3(NTHR),
+                           LDS_BYTES_ALONE, s, g);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || g.ksplit == 1) return e;
     return launch_splitk_reduce(g, batch, s);

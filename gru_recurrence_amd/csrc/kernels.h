@@ -25,6 +25,13 @@ struct GemmArgs {
     float *partial;           // [batch][ksplit][M][N] slice partials (workspace)
     unsigned *ready;          // if set (ksplit 1, batch 1): per 256-row panel, +1 per
                               // finished column tile, released at device scope
+    // Optional second K segment (k-major kernel, batch 1, no split): C(m, n)
+    // also gets sum_{k < K2} A2[m*lda2 + (n/seg_n)*K2 + k] * B2[n*ldb2 + k],
+    // i.e. column block n/seg_n of the output takes its own K2 columns of A2
+    // (a block-diagonal right operand).  seg_n is a multiple of the column tile.
+    const uint16_t *A2, *B2;
+    long lda2, ldb2;
+    int K2, seg_n;
 };
 constexpr int kGemmRowTile = 256;  // rows per output tile of the bf16 contraction
 constexpr int kGemmColTile = 256;  // columns per output tile
