@@ -42,7 +42,8 @@ class PlanCandidate(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in (
         "family", "rows_per_wg", "wg_per_head", "blocks_per_wg", "k_splits",
         "kchunks_per_wave", "row_slots", "frags_agpr", "frags_vgpr", "frags_lds", "waves",
-        "grid", "r_vgpr", "wg_per_cu")] + [("lds_bytes", ctypes.c_longlong), ("feasible", ctypes.c_int),
+        "grid", "r_vgpr", "wg_per_cu", "xcd_local")] + [("lds_bytes", ctypes.c_longlong),
+                                                          ("feasible", ctypes.c_int),
                               ("violated", ctypes.c_int), ("ns_per_step", ctypes.c_double),
                               ("ns_total", ctypes.c_double)]
 

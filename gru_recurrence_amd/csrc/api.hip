@@ -16,10 +16,15 @@ using namespace rnn355;
 
 namespace {
 
-// Workspace: [0, kHeader) status word (word 0), then the h exchange slots
+// Workspace: [0, kHeader) status word (word 0) and the multi-CU kernel's
+// XCD table (from byte kXccOffset), then the h exchange slots
 // of the multi-CU kernel, then the operation's own regions, each 256-byte
 // aligned.
 constexpr size_t kHeader = 4096;
+// header words [256, 1024): the multi-CU kernel's table of workgroup XCDs
+constexpr size_t kXccOffset = 1024;
+constexpr int kXccWords = (int)((kHeader - kXccOffset) / sizeof(unsigned));
+static_assert(kXccWords >= kMcXcdMaxGrid, "the XCD table holds one word per workgroup");
 constexpr int kMaxLayers = 64;
 constexpr size_t kAlign = 256;
 
@@ -125,6 +130,12 @@ int env_int(const char *name) {
     return e ? atoi(e) : 0;
 }
 int bt_override() { return env_int("RNN355_REC_BT"); }
+// RNN355_MC_XCD=0: the multi-CU kernel numbers its workgroups group by
+// group and exchanges through memory even where a group could share an L2.
+bool mc_xcd_enabled() {
+    const char *e = getenv("RNN355_MC_XCD");
+    return !e || atoi(e) != 0;
+}
 // RNN355_PIPELINE=0 runs the forward's two phases one after the other;
 // =1 overlaps them wherever that is safe, also where the plan would not.
 int pipeline_override() {
@@ -169,7 +180,8 @@ Choice choose(int cell, const rnn_dims *d, rnn_dtype dt, int num_cu) {
     Choice c{};
     c.cell = cell;
     const bool bf16 = dt == RNN_BF16;
-    const PlanFix fix{bt_override(), k_override(), kcw_override(), !wide_enabled()};
+    const PlanFix fix{bt_override(), k_override(), kcw_override(), !wide_enabled(),
+                      !mc_xcd_enabled()};
     static thread_local PlanCand buf[kPlanMaxCands];
     int best = -1;
     plan_search(cell, d->T, d->B, d->NH, d->Dh, bf16, num_cu, fix, buf, kPlanMaxCands, &best);
@@ -273,6 +285,10 @@ rnn_status rec_fwd(int cell, const rnn_dims *d, rnn_dtype dt, const float *gx, c
         m.flag = (unsigned *)ws;
         m.xg = (unsigned long long *)((char *)ws + kHeader);
         m.spin_limit = spin_limit();
+        if (mc_xcd_enabled() && mc_xcd_grouping(ch.mc.groups, ch.mc.grid)) {
+            m.xcd_map = 1;
+            m.xcc = (unsigned *)((char *)ws + kXccOffset);
+        }
         e = launch_rec_mc(cell, ch.mc, m, s, clear_status);
     } else {
         a.BT = ch.rec.BT;
@@ -699,6 +715,10 @@ ChunkLayout chunk_layout(const rnn_dims *d, int chunk, int G, rnn_dtype dt) {
     return L;
 }
 
+// Fewest free compute units for which a chunk's projection runs beside the
+// previous chunk's recurrence.
+constexpr int kChunkMinFreeCus = 64;
+
 rnn_status forward_chunked(int cell, const rnn_dims *d, rnn_dtype dt, int chunk, const void *x,
                            const void *W, const void *R, const float *b, const float *h0,
                            const float *c0, float *h_seq, float *c_seq, float *hT, float *cT,
@@ -725,10 +745,15 @@ rnn_status forward_chunked(int cell, const rnn_dims *d, rnn_dtype dt, int chunk,
     if (!ch.ok) return RNN_ERR_UNSUPPORTED;
     const int rec_grid = ch.use_wide ? ch.wide.grid : ch.use_mc ? ch.mc.grid : ch.rec.grid;
     const bool dma = dt == RNN_BF16 && gemm_dma_ok(Din);
-    const int gemm_wg = std::max(8, (cus - rec_grid) / 8 * 8);
-    hipStream_t s2 = side_stream();
+    // the projection runs beside the recurrence on the CUs it leaves; where
+    // it leaves few (the multi-CU plans take them all), a capped projection
+    // would take longer than the chunk it feeds, so every chunk's projection
+    // runs on the whole chip, in order on the caller's stream
+    const bool beside = cus - rec_grid >= kChunkMinFreeCus;
+    const int gemm_wg = beside ? (cus - rec_grid) / 8 * 8 : 0;
+    hipStream_t s2 = beside ? side_stream() : s;  // s may be the null stream
     CallEvents ev;
-    if (!s2 || !ev.ok) return RNN_ERR_HIP;
+    if ((beside && !s2) || !ev.ok) return RNN_ERR_HIP;
     hipEvent_t fork = ev.e[0], eg[2] = {ev.e[1], ev.e[2]}, er[2] = {ev.e[3], ev.e[4]};
     auto ok = [](hipError_t e) { return e == hipSuccess; };
 
@@ -920,8 +945,9 @@ rnn_status rnn_plan_describe(rnn_op op, const rnn_dims *d, rnn_dtype dt, char *b
         const McPlan &p = ch.mc;
         snprintf(buf, len,
                  "rec_kernel=mfma_multi_cu rows_per_wg=%d wg=%d threads=%d wg_per_head_row_tile=%d "
-                 "units_per_wg=%d k_splits=%d%s",
-                 p.BT, p.grid, p.threads, p.K, p.nb * 16, p.ks, proj);
+                 "units_per_wg=%d k_splits=%d exchange=%s%s",
+                 p.BT, p.grid, p.threads, p.K, p.nb * 16, p.ks,
+                 ch.cand.xcd_local ? "xcd_l2" : "memory", proj);
     } else {
         const RecPlan &p = ch.rec;
         snprintf(buf, len,
@@ -939,7 +965,8 @@ rnn_status rnn_plan_search(rnn_op op, const rnn_dims *d, rnn_dtype dt, int num_c
         return RNN_ERR_INVALID_ARG;
     if (op < RNN_OP_FWD_LSTM || op > RNN_OP_REC_GRU) return RNN_ERR_INVALID_ARG;
     const int cus = num_cu > 0 ? num_cu : device_cus();
-    const PlanFix fix{bt_override(), k_override(), kcw_override(), !wide_enabled()};
+    const PlanFix fix{bt_override(), k_override(), kcw_override(), !wide_enabled(),
+                      !mc_xcd_enabled()};
     static thread_local PlanCand buf[kPlanMaxCands];
     int best = -1;
     const int n = plan_search(cell_of_op(op), d->T, d->B, d->NH, d->Dh, dt == RNN_BF16, cus, fix,
@@ -962,6 +989,7 @@ rnn_status rnn_plan_search(rnn_op op, const rnn_dims *d, rnn_dtype dt, int num_c
         o.grid = c.grid;
         o.r_vgpr = c.r_vgpr;
         o.wg_per_cu = c.wg_per_cu;
+        o.xcd_local = c.xcd_local;
         o.lds_bytes = c.lds;
         o.feasible = c.feasible;
         o.violated = c.violated;

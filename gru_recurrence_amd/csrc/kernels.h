@@ -177,7 +177,20 @@ struct McArgs {
     unsigned long long *xg;  // exchange slots [groups][2][BT][Dh/2] (2 bf16 + step)
     unsigned *flag;          // time-out / abort word (cleared before every launch)
     unsigned spin_limit;  // polls of the group counter before a wait is declared lost
+    // xcd_map: workgroup i serves group (i % 8) + 8 * ((i / 8) / K), member
+    // (i / 8) % K (needs groups % 8 == 0), so that the members of a group are
+    // the workgroups the dispatcher deals to one XCD; `xcc` ([grid] words,
+    // zero before the launch) lets the members check that placement.
+    unsigned *xcc;
+    int xcd_map;
 };
+// The multi-CU kernel numbers its workgroups by XCD (McArgs::xcd_map) where
+// the groups divide over the 8 XCDs and the id table fits the workspace
+// header.
+constexpr int kMcXcdMaxGrid = 768;
+inline bool mc_xcd_grouping(int groups, int grid) {
+    return groups > 0 && groups % 8 == 0 && grid <= kMcXcdMaxGrid;
+}
 
 // Plan for heads of Dh >= 256, Dh % 128 == 0; ok == 0 if none fits the
 // chip (every workgroup must be resident at once).  kcw: k-chunks of 32
@@ -211,15 +224,18 @@ struct PlanCand {
     int fa, fv, fl;              // split R: fragments per wave in AGPRs, VGPRs, LDS
     int waves, grid, r_vgpr;     // waves per workgroup, workgroups, VGPRs per wave holding R
     int wg_per_cu;               // workgroups that fit on one CU at once
+    int xcd_local;               // multi-CU: groups exchange through one XCD's L2
     long lds;                    // LDS bytes per workgroup
     int feasible, violated;
     double ns_step, ns_total;    // predicted per-step latency, T steps
 };
 // Overrides (0: free): rows per workgroup, workgroups per head tile, k-chunks
-// per wave; no_wide excludes the split-R family.
+// per wave; no_wide excludes the split-R family; no_xcd prices the multi-CU
+// exchange through memory everywhere.
 struct PlanFix {
     int bt, k, kcw;
     bool no_wide;
+    bool no_xcd;  // multi-CU groups exchange through memory even where they could share an L2
 };
 constexpr int kPlanMaxCands = 512;
 // Writes up to cap candidates to buf, the fastest feasible one's index to

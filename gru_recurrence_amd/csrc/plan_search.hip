@@ -59,6 +59,7 @@ constexpr double kMfmaNs = 7.95;          // one 16x16x32 bf16 MFMA issued per S
 constexpr double kGateNs[3] = {61.5, 136.5, 261.5};  // cell update per gate, 1/2/4 row slots
 constexpr double kWideRowsNs = 250.0;     // more than 8 rows of a tile: second row half
 constexpr double kExchangeNs = 1480.0;    // cross-CU step exchange (flag-in-data words)
+constexpr double kExchangeLocalNs = 580.0; // ... base when a group's members share one XCD's L2
 constexpr double kExchangePerWgNs = 10.0; // ... per workgroup of the head
 constexpr double kExchangePerValNs = 0.05; // ... per h value gathered (Dh x BT)
 constexpr double kSplitBaseNs = 350.0;    // k-split partial sums through LDS + barrier
@@ -197,8 +198,9 @@ void family_wide(int cell, int T, int B, int NH, int Dh, bool bf16, int cus, con
     }
 }
 
-// Several CUs per (head, row tile) exchanging h through memory every step
-// (rec_mc.hip), all resident at once.
+// Several CUs per (head, row tile) exchanging h every step (rec_mc.hip), all
+// resident at once; through one XCD's L2 where the groups divide over the 8
+// XCDs (measured: 25-40% shorter steps than through memory).
 void family_multicu(int cell, int T, int B, int NH, int Dh, bool bf16, int cus,
                     const PlanFix &fix, Sink &out) {
     const int G = cell == kLSTM ? 4 : 3;
@@ -233,8 +235,10 @@ void family_multicu(int cell, int T, int B, int NH, int Dh, bool bf16, int cus,
                 if (fix.k > 0 && c.K != fix.k) fail(c, kPlanFixed);
                 if (fix.kcw > 0 && kcw != fix.kcw) fail(c, kPlanFixed);
                 const int per_simd = ceil_div(c.waves, kSimds);
+                c.xcd_local = !fix.no_xcd && mc_xcd_grouping(NH * ceil_div(B, bt), c.grid);
                 c.ns_step = kMfmaNs * G * kcw * per_simd + G * kGateNs[r4_index(c.r4)] +
-                            kExchangeNs + kExchangePerWgNs * std::max(c.K, 1) +
+                            (c.xcd_local ? kExchangeLocalNs : kExchangeNs) +
+                            kExchangePerWgNs * std::max(c.K, 1) +
                             kExchangePerValNs * Dh * bt +
                             (c.ks > 1 ? kSplitBaseNs + kSplitPerWaveNs * c.ks : 0.0) +
                             (cell == kLSTM && kcw == 8 && c.r4 == 4 ? kSpillBoundNs : 0.0);

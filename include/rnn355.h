@@ -212,6 +212,9 @@ typedef struct rnn_plan_candidate {
     int grid;             /* workgroups */
     int r_vgpr;           /* VGPRs per wave holding R */
     int wg_per_cu;        /* workgroups that fit on one CU at once */
+    int xcd_local;        /* family 3: the head tile's workgroups are numbered to run on
+                             one XCD and exchange through its L2 (each launch checks
+                             the placement; a spread group exchanges through memory) */
     long long lds_bytes;  /* per workgroup */
     int feasible;
     int violated;         /* 1 not compiled, 2 divisibility, 3 registers, 4 LDS,

@@ -140,14 +140,17 @@ def test_backward_rejects_unsupported_and_invalid_before_launch():
 
 def test_plans_of_the_workloads(monkeypatch):
     """Kernel plans are pure host decisions (256 compute units assumed when
-    no device is visible): one-CU resident-R kernel for Dh <= 128, one CU
-    with R split over registers and LDS at Dh = 256, multi-CU split above; the forward overlaps projection and recurrence (one fused
+    no device is visible): one-CU resident-R kernel for Dh <= 128, at Dh =
+    256 four CUs per chain exchanging through an XCD's L2 (or one CU with R
+    split over registers and LDS), multi-CU split above; the forward
+    overlaps projection and recurrence (one fused
     launch, Dh = 128) only when the recurrence leaves half the chip free and
     the projection is large."""
     monkeypatch.delenv("RNN355_PIPELINE", raising=False)
     monkeypatch.delenv("RNN355_REC_BT", raising=False)
     monkeypatch.delenv("RNN355_REC_K", raising=False)
     monkeypatch.delenv("RNN355_REC_WIDE", raising=False)
+    monkeypatch.delenv("RNN355_MC_XCD", raising=False)
     if g.plan_describe(g.OP_REC_LSTM, g.Dims(8, 16, 8, 6, 128), g.RNN_BF16).find(" wg=96 ") < 0:
         pytest.skip("a device with other than 256 compute units is visible")
     head = g.Dims(1024, 16, 768, 6, 128)
@@ -157,16 +160,24 @@ def test_plans_of_the_workloads(monkeypatch):
     assert "mfma_resident_R" in p and " wg=48 " in p and "input_proj=serial" in p
     p = g.plan_describe(g.OP_FWD_LSTM, g.Dims(1024, 16, 768, 1, 768), g.RNN_BF16)
     assert "mfma_multi_cu" in p and "input_proj=serial" in p
-    # Dh = 256: one CU per (head, row) with R split over registers and LDS,
-    # or (RNN355_REC_WIDE=0) the multi-CU kernel
+    # Dh = 256, 64 (head, row) chains: four CUs per chain, the 64 groups
+    # numbered so that each group's four run on one XCD and exchange h
+    # through its L2; with that exchange through memory (RNN355_MC_XCD=0),
+    # one CU per (head, row) with R split over registers and LDS
     c5 = g.Dims(1024, 16, 1024, 4, 256)
+    for op in (g.OP_FWD_LSTM, g.OP_FWD_GRU):
+        p = g.plan_describe(op, c5, g.RNN_BF16)
+        assert "mfma_multi_cu" in p and " wg=256 " in p and "exchange=xcd_l2" in p
+    monkeypatch.setenv("RNN355_MC_XCD", "0")
     p = g.plan_describe(g.OP_FWD_LSTM, c5, g.RNN_BF16)
     assert "split_R" in p and " wg=64 " in p and " threads=256 " in p and "r_lds_bytes=131072" in p
     p = g.plan_describe(g.OP_FWD_GRU, c5, g.RNN_BF16)
     assert "split_R" in p and "r_lds_bytes=0" in p
     monkeypatch.setenv("RNN355_REC_WIDE", "0")
-    assert "mfma_multi_cu" in g.plan_describe(g.OP_FWD_LSTM, c5, g.RNN_BF16)
+    p = g.plan_describe(g.OP_FWD_LSTM, c5, g.RNN_BF16)
+    assert "mfma_multi_cu" in p and "exchange=memory" in p
     monkeypatch.delenv("RNN355_REC_WIDE")
+    monkeypatch.delenv("RNN355_MC_XCD")
     # the recurrence-only workspace holds R^T for it (bf16 only)
     rec_f = g.workspace_size(g.OP_REC_LSTM, c5, g.RNN_F32)
     rec_b = g.workspace_size(g.OP_REC_LSTM, c5, g.RNN_BF16)

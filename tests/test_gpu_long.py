@@ -63,6 +63,10 @@ def chunked(c, chunk):
     ("gru", 33, 4, 2, 64, 64, "bf16", 11, None),
     ("gru", 5, 2, 1, 128, 32, "bf16", 1, None),       # one step per chunk
     ("gru", 20, 3, 1, 256, 64, "bf16", 6, None),
+    # 64 chains at Dh = 256: the multi-CU plan takes every CU, so each
+    # chunk's projection runs on the whole chip in order on the caller's stream
+    ("lstm", 21, 16, 4, 256, 64, "bf16", 8, None),
+    ("gru", 19, 16, 4, 256, 32, "bf16", 7, None),
 ])
 def test_chunked_forward_is_the_forward_bitwise(cell, T, B, NH, Dh, Din, dtype, chunk, env):
     if env is not None:
@@ -122,6 +126,7 @@ def _bwd_both(c, chunk, final):
     ("lstm", 24, 2, 2, 64, 24, True),      # one segment
     ("gru", 31, 4, 2, 64, 8, True),
     ("gru", 17, 3, 1, 256, 6, False),
+    ("lstm", 19, 16, 4, 256, 8, True),     # multi-CU forward recompute (every CU)
 ])
 def test_checkpointed_backward(cell, T, B, NH, Dh, chunk, final):
     d = synth.Dims(T=T, B=B, Din=64, NH=NH, Dh=Dh)

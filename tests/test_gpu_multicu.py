@@ -22,7 +22,8 @@ TOL_BF16 = 2e-2
 
 @pytest.fixture(autouse=True)
 def _clean_env():
-    keys = ("RNN355_REC_BT", "RNN355_REC_K", "RNN355_SPIN_LIMIT", "RNN355_REC_WIDE")
+    keys = ("RNN355_REC_BT", "RNN355_REC_K", "RNN355_SPIN_LIMIT", "RNN355_REC_WIDE",
+            "RNN355_MC_XCD")
     old = {k: os.environ.pop(k, None) for k in keys}
     os.environ["RNN355_REC_WIDE"] = "0"
     yield
@@ -86,6 +87,42 @@ def test_multicu_forward(cell, Dh, NH, B, bt, k):
         assert e <= TOL_BF16, (key, e)
 
 
+# groups (heads x batch tiles) a multiple of 8: the members of a group are
+# numbered so that they run on one XCD and exchange h_t through its L2 when
+# every member finds itself there; RNN355_MC_XCD=0 keeps the exchange
+# through memory.  Same sums either way: the outputs must be the same bits.
+@pytest.mark.parametrize("cell,Dh,NH,B,bt", [
+    ("lstm", 256, 2, 8, 2),     # 8 groups of 2 workgroups
+    ("gru", 256, 4, 4, 2),      # 8 groups, GRU
+    ("lstm", 384, 1, 16, 2),    # 8 groups, k split over waves
+    ("lstm", 768, 1, 16, None), # the Dh = 768 plan: 8 groups of 24
+])
+def test_multicu_xcd_grouped_exchange(cell, Dh, NH, B, bt):
+    if bt is not None:
+        os.environ["RNN355_REC_BT"] = str(bt)
+    d = synth.Dims(T=21, B=B, Din=64, NH=NH, Dh=Dh)
+    c = synth.make_case(cell, d, "bf16", 8300 + Dh + B, bias="forget+1" if cell == "lstm" else "zero",
+                        h0_var=0.2, c0_var=0.2)
+    p = plan(c)
+    print("  plan:", p, flush=True)
+    assert "multi_cu" in p
+    op = g.OP_FWD_LSTM if cell == "lstm" else g.OP_FWD_GRU
+    need = g.workspace_size(op, g.Dims(d.T, d.B, d.Din, d.NH, d.Dh), g.RNN_BF16)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    got = run(c, ws=ws)
+    assert g.workspace_status(ws) == g.RNN_OK
+    os.environ["RNN355_MC_XCD"] = "0"
+    mem = run(c, ws=ws)
+    assert g.workspace_status(ws) == g.RNN_OK
+    for key in got:
+        assert np.array_equal(got[key], mem[key]), key
+    ref = want(c)
+    for key in got:
+        e = nerr(got[key], ref[key])
+        print("  %-6s nerr=%.3e" % (key, e), flush=True)
+        assert e <= TOL_BF16, (key, e)
+
+
 def test_multicu_run_to_run_bitwise():
     d = synth.Dims(T=17, B=2, Din=32, NH=1, Dh=256)
     c = synth.make_case("lstm", d, "bf16", 8100, bias="forget+1")
@@ -118,19 +155,36 @@ def _mask(B, NH, chains):
     return m
 
 
+# Full-size workloads in the plans they run by default (multi-CU, h through
+# one XCD's L2), with the exchange through memory (RNN355_MC_XCD=0), and at
+# Dh = 256 in the split-R plan the default takes where groups cannot share
+# an L2.
 @pytest.mark.parametrize("name,chains", [
     ("lstm_1h_b16_dh768", [(0, 0), (9, 0)]),
+    ("lstm_1h_b16_dh768/memory", [(3, 0), (14, 0)]),
     ("lstm_fwdbwd_b16_nh4_dh256", [(0, 0), (5, 2), (15, 3)]),
+    ("lstm_fwdbwd_b16_nh4_dh256/memory", [(1, 0), (7, 3)]),
     ("lstm_fwdbwd_b16_nh4_dh256/split_R", [(0, 0), (6, 1), (15, 3)]),
 ])
 def test_large_head_workloads_full_size_sampled_chains(name, chains):
-    if name.endswith("/split_R"):
-        name = name.split("/")[0]
-        os.environ.pop("RNN355_REC_WIDE")
+    name, _, variant = name.partition("/")
+    os.environ.pop("RNN355_REC_WIDE")
+    if variant == "memory":
+        os.environ["RNN355_MC_XCD"] = "0"
+        os.environ["RNN355_REC_WIDE"] = "0"
+    elif variant == "split_R":
+        os.environ["RNN355_MC_XCD"] = "0"
     w = synth.WORKLOADS[name]
     c = synth.workload_case(w)
-    print("  plan:", plan(c), flush=True)
-    got = run(c)
+    p = plan(c)
+    print("  plan:", p, flush=True)
+    assert ("split_R" if variant == "split_R" else
+            "exchange=memory" if variant == "memory" else "exchange=xcd_l2") in p
+    need = g.workspace_size(g.OP_FWD_LSTM, g.Dims(*(getattr(w.dims, k) for k in
+                                                      ("T", "B", "Din", "NH", "Dh"))), g.RNN_BF16)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    got = run(c, ws=ws)
+    assert g.workspace_status(ws) == g.RNN_OK
     ref = want(c, _mask(w.dims.B, w.dims.NH, chains))
     Dh = w.dims.Dh
     for b, n in chains:

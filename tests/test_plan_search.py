@@ -15,7 +15,7 @@ import gru_recurrence_amd as g
 HERE = os.path.dirname(os.path.abspath(__file__))
 POINTS = json.load(open(os.path.join(HERE, "golden", "plan_measurements.json")))["points"]
 CUS = 256
-ENV = ("RNN355_REC_BT", "RNN355_REC_K", "RNN355_REC_KCW", "RNN355_REC_WIDE")
+ENV = ("RNN355_REC_BT", "RNN355_REC_K", "RNN355_REC_KCW", "RNN355_REC_WIDE", "RNN355_MC_XCD")
 
 
 @pytest.fixture(autouse=True)
@@ -44,6 +44,7 @@ def plan_vars(plan, Dh):
         v["blocks_per_wg"] = int(kv["units_per_wg"]) // 16
         v["k_splits"] = int(kv["k_splits"])
         v["kchunks_per_wave"] = Dh // 32 // v["k_splits"]
+        v["xcd_local"] = int(kv.get("exchange", "memory") == "xcd_l2")
     return v
 
 
@@ -106,7 +107,9 @@ def _check_all(cell, B, Dh, dtype, cands, best, cus=CUS):
 def test_split_r_fragment_split_follows_from_the_budgets(cell, fl):
     """Among the split-R splits that the register and LDS budgets allow
     (feasible, or only not compiled), the cheapest is the compiled one:
-    every AGPR used, then VGPRs, the rest in LDS."""
+    every AGPR used, then VGPRs, the rest in LDS; it is the choice where the
+    multi-CU exchange goes through memory."""
+    os.environ["RNN355_MC_XCD"] = "0"
     cands, best = search(cell, 1024, 16, 4, 256)
     ok = [c for c in cands if c["family"] == 2 and c["violated"] in (0, 1)]
     top = min(ok, key=lambda c: c["ns_total"])
@@ -125,6 +128,10 @@ def test_overrides_fix_variables():
     os.environ["RNN355_REC_K"] = "2"
     cands, best = search("lstm", 1024, 16, 4, 256)
     assert cands[best]["family"] == 3 and cands[best]["wg_per_head"] == 2
+    assert cands[best]["xcd_local"] == 1
+    os.environ["RNN355_MC_XCD"] = "0"
+    cands, best = search("lstm", 1024, 16, 4, 256)
+    assert cands[best]["family"] == 3 and cands[best]["xcd_local"] == 0
 
 
 @pytest.mark.parametrize("shape,want", [
@@ -132,7 +139,9 @@ def test_overrides_fix_variables():
     (("gru", 2048, 4, 12, 64, "bf16"), dict(family=1, rows_per_wg=1, grid=48)),
     (("lstm", 1024, 16, 1, 768, "bf16"), dict(family=3, rows_per_wg=2, wg_per_head=24,
                                              kchunks_per_wave=8)),
-    (("lstm", 1024, 16, 4, 256, "bf16"), dict(family=2, frags_lds=32)),
+    (("lstm", 1024, 16, 4, 256, "bf16"), dict(family=3, wg_per_head=4, rows_per_wg=1,
+                                             xcd_local=1)),
+    (("lstm", 64, 2, 1, 384, "bf16"), dict(family=3, xcd_local=0)),   # 2 groups: memory
     (("lstm", 64, 2, 1, 32, "f32"), dict(family=4, rows_per_wg=2)),
 ])
 def test_workload_plans(shape, want):
@@ -142,7 +151,14 @@ def test_workload_plans(shape, want):
 
 
 def _predicted(p):
-    cands, _ = search(p["cell"], p["T"], p["B"], p["NH"], p["Dh"], p["dtype"])
+    """The model's time for the measured plan (under the point's exchange
+    setting: RNN355_MC_XCD=0 prices the multi-CU exchange through memory)."""
+    if "RNN355_MC_XCD" in p["env"]:
+        os.environ["RNN355_MC_XCD"] = p["env"]["RNN355_MC_XCD"]
+    try:
+        cands, _ = search(p["cell"], p["T"], p["B"], p["NH"], p["Dh"], p["dtype"])
+    finally:
+        os.environ.pop("RNN355_MC_XCD", None)
     c = match(cands, plan_vars(p["plan"], p["Dh"]))
     return c["ns_total"] / p["T"], c
 
@@ -190,6 +206,8 @@ def test_default_choice_is_the_best_measured_plan():
         chosen = {k: cands[best][k] for k in ("family", "rows_per_wg", "wg_per_head")}
         meas = {}
         for p in ps:
+            if "RNN355_MC_XCD" in p["env"]:
+                continue  # the default keeps the XCD-grouped exchange on
             v = plan_vars(p["plan"], key[4])
             meas[(v["family"], v["rows_per_wg"], v.get("wg_per_head", 1))] = p["ns_step"]
         k = (chosen["family"], chosen["rows_per_wg"], chosen["wg_per_head"])
