@@ -620,6 +620,10 @@ rnn_status backward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, co
         m.db_part = dbp; m.dh0 = dh0; m.dc0 = dc0;
         m.xg = (unsigned long long *)(base + L.xchg);
         m.flag = (unsigned *)ws;
+        if (!pw.ok && p.K > 1 && mc_xcd_enabled() && mc_xcd_grouping(p.groups, p.grid)) {
+            m.xcd_map = 1;
+            m.xcc = (unsigned *)((char *)ws + kXccOffset);
+        }
         m.spin_limit = spin_limit();
         const hipError_t e = pw.ok ? launch_rec_bwd_wide(cell, pw, m, stream)
                                    : launch_rec_bwd(cell, p, m, stream);

@@ -270,6 +270,8 @@ struct BwdArgs {
     unsigned long long *xg;  // exchange slots [groups][2][BT][G*Dh/2]
     unsigned *flag;
     unsigned spin_limit;
+    unsigned *xcc;  // as McArgs: members of a group numbered by XCD, checked
+    int xcd_map;    // through this table of workgroup XCDs ([grid] words)
 };
 
 BwdPlan plan_bwd(int cell, int B, int NH, int Dh, int num_cu, int bt_override, int k_override);

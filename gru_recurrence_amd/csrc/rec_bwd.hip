@@ -38,6 +38,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "xcd.h"
 
 namespace rnn355 {
 
@@ -54,9 +55,10 @@ __global__ __launch_bounds__(512) void rec_bwd_kernel(BwdArgs m) {
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
     uint16_t *dab2 = smem;                                          // [2][BT][ALD] bf16
     float *red = reinterpret_cast<float *>(smem + 2 * m.BT * ALD);  // [KS-1][NB][16][16]
-    __shared__ int s_abort;
+    __shared__ int s_abort, s_local;
 
-    const int group = blockIdx.x / K, member = blockIdx.x - group * K;
+    int group, member;
+    group_member(m.xcd_map != 0, K, group, member);
     const int n = group % m.NH;
     const int bt = group / m.NH;
     const int b0 = bt * m.BT;
@@ -78,7 +80,11 @@ __global__ __launch_bounds__(512) void rec_bwd_kernel(BwdArgs m) {
             rf[c] = *reinterpret_cast<const bf16x8 *>(Rrow + 32 * (kc0 + c) + 8 * lg);
     }
     for (int i = tid; i < 2 * m.BT * ALD; i += nthr) dab2[i] = 0;
-    if (tid == 0) s_abort = 0;
+    if (tid == 0) {
+        s_abort = 0;
+        s_local = 0;
+    }
+    if (m.xcd_map) xcd_publish(m.xcc);
 
     // per-lane state of the gate waves: row slots r -> batch row 4*lg + r
     bool rv[R4];
@@ -124,6 +130,17 @@ __global__ __launch_bounds__(512) void rec_bwd_kernel(BwdArgs m) {
     };
     load_step(T - 1);
     __syncthreads();
+    if (m.xcd_map && wave == 0) {
+        const int v = xcd_members_agree(m.xcc, m.flag, m.spin_limit, group, K);
+        if (lane == 0) {
+            s_local = v > 0;
+            if (v < 0) s_abort = 1;
+        }
+    }
+    __syncthreads();
+    // the group's members on one XCD: dA words stay in its L2 (see the
+    // forward's multi-CU kernel), polled at device scope either way
+    const bool local = s_local != 0;
 
     const int wpr = GD / 2;  // exchange words per row
     unsigned long long *xs_group = m.xg + (long)group * 2 * m.BT * wpr;
@@ -134,7 +151,7 @@ __global__ __launch_bounds__(512) void rec_bwd_kernel(BwdArgs m) {
     bf16x8 af[KCW];
 #pragma unroll
     for (int c = 0; c < KCW; ++c) af[c] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
-    int s = 0;  // steps done
+    int s = s_abort ? T + 1 : 0;  // steps done
     for (; s < T; ++s) {
         const int t = T - 1 - s;
         uint16_t *dab_next = dab2 + (s & 1) * m.BT * ALD;  // filled with dA_t this step
@@ -198,8 +215,14 @@ __global__ __launch_bounds__(512) void rec_bwd_kernel(BwdArgs m) {
                         if (K == 1) {
                             dab_next[row * ALD + col] = (uint16_t)v;
                         } else if ((lr & 1) == 0) {
-                            __hip_atomic_store(slot + row * wpr + (col >> 1), tag | (nb << 16) | v,
-                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            unsigned long long *dst = slot + row * wpr + (col >> 1);
+                            const unsigned long long w = tag | (nb << 16) | v;
+                            if (local)
+                                __hip_atomic_store(dst, w, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+                            else
+                                __hip_atomic_store(dst, w, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
                         }
                     }
                 }
@@ -210,15 +233,25 @@ __global__ __launch_bounds__(512) void rec_bwd_kernel(BwdArgs m) {
         if (gate_wave && t > 0) load_step(t - 1);
         // ---- dA_t of the whole head row into LDS
         if (K > 1) {
+            // PW words of a thread per poll, their loads in flight together
+            constexpr int PW = 4;
             const int words = rows * wpr;
             unsigned *hw = reinterpret_cast<unsigned *>(dab_next);
-            for (int i = tid; i < words; i += nthr) {
-                const int b = i / wpr, k2 = i - b * wpr;
+            for (int i0 = tid; i0 < words; i0 += PW * nthr) {
                 unsigned spins = 0;
-                unsigned long long w;
+                unsigned long long w[PW];
                 for (;;) {
-                    w = __hip_atomic_load(slot + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    if ((w & 0xFFFFFFFF00000000ull) == tag) break;
+                    bool all = true;
+#pragma unroll
+                    for (int q = 0; q < PW; ++q) {
+                        const int i = i0 + q * nthr;
+                        w[q] = i < words ? __hip_atomic_load(slot + i, __ATOMIC_RELAXED,
+                                                             __HIP_MEMORY_SCOPE_AGENT)
+                                         : tag;
+                    }
+#pragma unroll
+                    for (int q = 0; q < PW; ++q) all = all && (w[q] & 0xFFFFFFFF00000000ull) == tag;
+                    if (all) break;
                     ++spins;
                     if ((spins & 255u) == 0 &&
                         __hip_atomic_load(m.flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
@@ -232,7 +265,14 @@ __global__ __launch_bounds__(512) void rec_bwd_kernel(BwdArgs m) {
                     }
                 }
                 if (s_abort) break;
-                hw[(b * ALD) / 2 + k2] = (unsigned)w;
+#pragma unroll
+                for (int q = 0; q < PW; ++q) {
+                    const int i = i0 + q * nthr;
+                    if (i < words) {
+                        const int b = i / wpr, k2 = i - b * wpr;
+                        hw[(b * ALD) / 2 + k2] = (unsigned)w[q];
+                    }
+                }
             }
         }
         __syncthreads();
@@ -417,9 +457,15 @@ BwdPlan plan_bwd(int cell, int B, int NH, int Dh, int num_cu, int bt_override, i
 
 hipError_t launch_rec_bwd(int cell, const BwdPlan &p, const BwdArgs &m, hipStream_t s) {
     const int G = cell == kLSTM ? 4 : 3;
+    if (m.xcd_map && (!m.xcc || p.groups % 8 != 0)) return hipErrorInvalidValue;
     hipLaunchKernelGGL(clear_words_bwd_kernel, dim3(1), dim3(64), 0, s, m.flag, 1L);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (m.xcd_map) {
+        hipLaunchKernelGGL(clear_words_bwd_kernel, dim3(1), dim3(256), 0, s, m.xcc, (long)p.grid);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     if (p.K > 1) {
         const long words = 2L * p.groups * 2 * p.BT * (G * m.Dh / 2);
         hipLaunchKernelGGL(clear_words_bwd_kernel, dim3(64), dim3(256), 0, s,

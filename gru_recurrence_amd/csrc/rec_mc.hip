@@ -29,32 +29,24 @@
 //      members stop and the kernel ends;
 //   5. the h/c outputs of step t are stored and Gx of step t+1 requested,
 //      so they drain during the next step.
-// XCD-local exchange: workgroups are dealt to the 8 XCDs in turn, so with
-// the xcd_map numbering all members of a group land on one XCD and share its
-// L2.  Each workgroup publishes the XCD it runs on (hardware register
-// XCC_ID) and reads its members'; if all match, the group's words are
+// XCD-local exchange (xcd.h): with the xcd_map numbering the members of a
+// group run on one XCD, which each launch checks.  Then the group's words are
 // stored into the shared L2 without the write-through to memory (sc0
-// stores), which the members' device-scope polls (sc1 loads, served by
-// that L2) see at once: measured between two CUs, a 421 ns round trip
-// against 673 ns (same XCD) and 773 ns (two XCDs) with write-through
-// stores.  Such a store is not seen from another XCD, so the path needs
-// the check: every member reads the same ids and takes the same path, and a
-// group whose members are spread keeps the write-through stores.
+// stores), which the members' device-scope polls (sc1 loads, served by that
+// L2) see at once: measured between two CUs, a 421 ns round trip against
+// 673 ns (same XCD) and 773 ns (two XCDs) with write-through stores.  Such a
+// store is not seen from another XCD, so only a group found on one XCD takes
+// that path; the others keep the write-through stores.
 #include <hip/hip_runtime.h>
 
 #include "common.h"
 #include "gates.h"
 #include "kernels.h"
+#include "xcd.h"
 
 namespace rnn355 {
 
 namespace {
-
-// The XCD (accelerator complex die) this wave runs on: hardware register
-// XCC_ID, bits [3:0].
-__device__ __forceinline__ unsigned xcc_id() {
-    return (unsigned)__builtin_amdgcn_s_getreg((3 << 11) | 20) & 15u;
-}
 
 template <int CELL, int KCW, int R4>
 __global__ __launch_bounds__(512) void rec_fwd_mc_kernel(McArgs m) {
@@ -76,14 +68,7 @@ __global__ __launch_bounds__(512) void rec_fwd_mc_kernel(McArgs m) {
     __shared__ int s_abort, s_local;
 
     int group, member;
-    if (m.xcd_map) {
-        const int slot = blockIdx.x >> 3;
-        group = (blockIdx.x & 7) + 8 * (slot / K);
-        member = slot % K;
-    } else {
-        group = blockIdx.x / K;
-        member = blockIdx.x - group * K;
-    }
+    group_member(m.xcd_map != 0, K, group, member);
     const int n = group % a.NH;
     const int b0 = (group / a.NH) * a.BT;
     const int rows = min(a.BT, B - b0);
@@ -127,9 +112,8 @@ __global__ __launch_bounds__(512) void rec_fwd_mc_kernel(McArgs m) {
     if (tid == 0) {
         s_abort = 0;
         s_local = 0;
-        if (m.xcd_map) __hip_atomic_store(m.xcc + blockIdx.x, xcc_id() + 1u, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT);
     }
+    if (m.xcd_map) xcd_publish(m.xcc);
 
     // lanes of the ks = 0 waves own units (same roles as the one-CU kernel)
     const float *gx_tile = a.gx + (long)b0 * N + n * GD;
@@ -166,24 +150,11 @@ __global__ __launch_bounds__(512) void rec_fwd_mc_kernel(McArgs m) {
     load_gx(0);
     __syncthreads();
     if (m.xcd_map && wave == 0) {
-        // the members' XCDs (published above; every member is resident)
-        const unsigned mine = xcc_id() + 1u;
-        bool same = true;
-        for (int mm = lane; mm < K; mm += 64) {
-            const int bid = ((((group >> 3) * K) + mm) << 3) | (group & 7);
-            unsigned v, spins = 0;
-            while ((v = __hip_atomic_load(m.xcc + bid, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT)) == 0u) {
-                if (++spins >= m.spin_limit) {
-                    __hip_atomic_store(m.flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    s_abort = 1;
-                    break;
-                }
-            }
-            if (v != mine) same = false;
+        const int v = xcd_members_agree(m.xcc, m.flag, m.spin_limit, group, K);
+        if (lane == 0) {
+            s_local = v > 0;
+            if (v < 0) s_abort = 1;
         }
-        const bool all = __all(same);
-        if (lane == 0) s_local = all ? 1 : 0;
     }
     __syncthreads();
     const bool local = s_local != 0;

@@ -23,7 +23,7 @@ TOL = 2e-2
 
 @pytest.fixture(autouse=True)
 def _clean_env():
-    keys = ("RNN355_REC_BT", "RNN355_REC_K", "RNN355_REC_WIDE")
+    keys = ("RNN355_REC_BT", "RNN355_REC_K", "RNN355_REC_WIDE", "RNN355_MC_XCD")
     old = {k: os.environ.pop(k, None) for k in keys}
     yield
     for k in keys:
@@ -217,3 +217,51 @@ def test_gru_backward_small_batch_workload_shape_sampled():
              oracle.param_grad_entries("dR", np.stack([np.full(256, n5), ii, jj], 1), *args, **kw))
     print("  dR entries nerr=%.3e" % e, flush=True)
     assert e <= TOL
+
+
+# 8 (head, row) groups of four workgroups in the exchange-based sweep
+# (RNN355_REC_WIDE=0): numbered so that each group runs on one XCD and swaps
+# dA through its L2 (each launch checks the placement); RNN355_MC_XCD=0 swaps
+# through memory.  Same sums either way: the gradients must be the same bits.
+@pytest.mark.parametrize("cell", ["lstm", "gru"])
+def test_backward_xcd_grouped_exchange(cell):
+    os.environ["RNN355_REC_WIDE"] = "0"
+    d = synth.Dims(T=15, B=4, Din=64, NH=2, Dh=256)
+    lstm = cell == "lstm"
+    c = synth.make_case(cell, d, "bf16", 9700 + (0 if lstm else 1),
+                        bias="forget+1" if lstm else "zero", h0_var=0.2, c0_var=0.2,
+                        backward=True, final_grads=True)
+    x, W, R, b, h0 = dev(c, "x"), dev(c, "W"), dev(c, "R"), dev(c, "b"), dev(c, "h0")
+    op = g.OP_BWD_LSTM if lstm else g.OP_BWD_GRU
+    ws = torch.empty(g.workspace_size(op, g.Dims(d.T, d.B, d.Din, d.NH, d.Dh), g.RNN_BF16),
+                     dtype=torch.uint8, device="cuda")
+
+    def once():
+        if lstm:
+            c0 = dev(c, "c0")
+            h_seq, c_seq, _, _ = g.lstm_fwd(x, W, R, b, h0, c0)
+            grads = g.lstm_bwd(x, W, R, b, h0, c0, h_seq, c_seq, dev(c, "dH"), dev(c, "dhT"),
+                               dev(c, "dcT"), ws=ws)
+        else:
+            h_seq, _ = g.gru_fwd(x, W, R, b, h0)
+            grads = g.gru_bwd(x, W, R, b, h0, h_seq, dev(c, "dH"), dev(c, "dhT"), ws=ws)
+        torch.cuda.synchronize()
+        assert g.workspace_status(ws) == g.RNN_OK
+        return {k: host(v) for k, v in grads.items()}
+
+    got = once()
+    os.environ["RNN355_MC_XCD"] = "0"
+    mem = once()
+    for k in got:
+        assert np.array_equal(got[k], mem[k]), k
+    if lstm:
+        ref = oracle.lstm_bwd(c.f64("x"), c.f64("W"), c.f64("R"), c.f64("b"), c.f64("h0"),
+                              c.f64("c0"), c.f64("dH"), c.f64("dhT"), c.f64("dcT"),
+                              NH=d.NH, Dh=d.Dh)
+    else:
+        ref = oracle.gru_bwd(c.f64("x"), c.f64("W"), c.f64("R"), c.f64("b"), c.f64("h0"),
+                             c.f64("dH"), c.f64("dhT"), NH=d.NH, Dh=d.Dh)
+    for k in got:
+        e = nerr(got[k], ref[k])
+        print("  %-4s nerr=%.3e" % (k, e), flush=True)
+        assert e <= TOL, (k, e)
