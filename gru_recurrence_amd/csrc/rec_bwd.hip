@@ -380,9 +380,16 @@ hipError_t launch_bwd_cell(const BwdPlan &p, const BwdArgs &m, hipStream_t s) {
     }
 }
 
-__global__ void clear_words_bwd_kernel(unsigned *p, long n) {
-    for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x)
-        p[i] = 0u;
+// Zeroes up to three word ranges (null pointers skipped) in one launch.
+__global__ void clear_words_bwd_kernel(unsigned *p, long n, unsigned *p2, long n2, unsigned *p3,
+                                       long n3) {
+    const long i0 = blockIdx.x * (long)blockDim.x + threadIdx.x, step = (long)gridDim.x * blockDim.x;
+    if (p)
+        for (long i = i0; i < n; i += step) p[i] = 0u;
+    if (p2)
+        for (long i = i0; i < n2; i += step) p2[i] = 0u;
+    if (p3)
+        for (long i = i0; i < n3; i += step) p3[i] = 0u;
 }
 
 // hprev[t][b][k] = bf16(h_{t-1}[b][k]) with h_{-1} = h0 (the MFMA operand the
@@ -393,6 +400,22 @@ __global__ void hprev_bf16_kernel(const float *h0, const float *h_seq, uint16_t 
          i += (long)gridDim.x * blockDim.x) {
         const float v = i < BH ? (h0 ? h0[i] : 0.f) : h_seq[i - BH];
         hprev[i] = f32_to_bf16_rne(v);
+    }
+}
+
+// The same, four elements per thread (16-byte loads, 8-byte stores): BH and
+// total multiples of 4, h0, h_seq 16-byte and hprev 8-byte aligned.
+__global__ void hprev_bf16_x4_kernel(const float *h0, const float *h_seq, uint16_t *hprev, long BH,
+                                     long total) {
+    for (long q = blockIdx.x * (long)blockDim.x + threadIdx.x; 4 * q < total;
+         q += (long)gridDim.x * blockDim.x) {
+        const long i = 4 * q;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (i >= BH) v = *reinterpret_cast<const float4 *>(h_seq + (i - BH));
+        else if (h0) v = *reinterpret_cast<const float4 *>(h0 + i);
+        const uint2 w = make_uint2((unsigned)f32_to_bf16_rne(v.x) | ((unsigned)f32_to_bf16_rne(v.y) << 16),
+                                   (unsigned)f32_to_bf16_rne(v.z) | ((unsigned)f32_to_bf16_rne(v.w) << 16));
+        *reinterpret_cast<uint2 *>(hprev + i) = w;
     }
 }
 
@@ -458,27 +481,26 @@ BwdPlan plan_bwd(int cell, int B, int NH, int Dh, int num_cu, int bt_override, i
 hipError_t launch_rec_bwd(int cell, const BwdPlan &p, const BwdArgs &m, hipStream_t s) {
     const int G = cell == kLSTM ? 4 : 3;
     if (m.xcd_map && (!m.xcc || p.groups % 8 != 0)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(clear_words_bwd_kernel, dim3(1), dim3(64), 0, s, m.flag, 1L);
-    hipError_t e = hipGetLastError();
+    // one launch: the status word, the XCD table, the exchange slots
+    const long words = p.K > 1 ? 2L * p.groups * 2 * p.BT * (G * m.Dh / 2) : 0;
+    hipLaunchKernelGGL(clear_words_bwd_kernel, dim3(64), dim3(256), 0, s, m.flag, 1L,
+                       m.xcd_map ? m.xcc : (unsigned *)nullptr, m.xcd_map ? (long)p.grid : 0L,
+                       p.K > 1 ? reinterpret_cast<unsigned *>(m.xg) : (unsigned *)nullptr, words);
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (m.xcd_map) {
-        hipLaunchKernelGGL(clear_words_bwd_kernel, dim3(1), dim3(256), 0, s, m.xcc, (long)p.grid);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    if (p.K > 1) {
-        const long words = 2L * p.groups * 2 * p.BT * (G * m.Dh / 2);
-        hipLaunchKernelGGL(clear_words_bwd_kernel, dim3(64), dim3(256), 0, s,
-                           reinterpret_cast<unsigned *>(m.xg), words);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
     return cell == kLSTM ? launch_bwd_cell<kLSTM>(p, m, s) : launch_bwd_cell<kGRU>(p, m, s);
 }
 
 hipError_t launch_hprev_bf16(const float *h0, const float *h_seq, uint16_t *hprev, long BH,
                              long total, hipStream_t s) {
-    hipLaunchKernelGGL(hprev_bf16_kernel, dim3(1024), dim3(256), 0, s, h0, h_seq, hprev, BH, total);
+    const bool x4 = BH % 4 == 0 && total % 4 == 0 && ((uintptr_t)h0 & 15) == 0 &&
+                    ((uintptr_t)h_seq & 15) == 0 && ((uintptr_t)hprev & 7) == 0;
+    if (x4)
+        hipLaunchKernelGGL(hprev_bf16_x4_kernel, dim3(2048), dim3(256), 0, s, h0, h_seq, hprev, BH,
+                           total);
+    else
+        hipLaunchKernelGGL(hprev_bf16_kernel, dim3(1024), dim3(256), 0, s, h0, h_seq, hprev, BH,
+                           total);
     return hipGetLastError();
 }
 

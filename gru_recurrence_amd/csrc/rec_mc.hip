@@ -304,11 +304,15 @@ __global__ __launch_bounds__(512) void rec_fwd_mc_kernel(McArgs m) {
     }
 }
 
-__global__ void clear_words_kernel(unsigned *p, int n, unsigned *p2, int n2) {
-    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+// Zeroes up to three word ranges (null pointers skipped) in one launch.
+__global__ void clear_words_kernel(unsigned *p, int n, unsigned *p2, int n2, unsigned *p3, int n3) {
+    const int i0 = blockIdx.x * blockDim.x + threadIdx.x, step = gridDim.x * blockDim.x;
+    if (p)
+        for (int i = i0; i < n; i += step) p[i] = 0u;
     if (p2)
-        for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n2; i += gridDim.x * blockDim.x)
-            p2[i] = 0u;
+        for (int i = i0; i < n2; i += step) p2[i] = 0u;
+    if (p3)
+        for (int i = i0; i < n3; i += step) p3[i] = 0u;
 }
 
 template <int CELL, int KCW, int R4>
@@ -373,18 +377,14 @@ hipError_t launch_rec_mc(int cell, const McPlan &p, const McArgs &m, hipStream_t
                          bool clear_flag) {
     hipError_t e;
     if (m.xcd_map && (!m.xcc || p.groups % 8 != 0)) return hipErrorInvalidValue;
-    if (clear_flag) {
-        hipLaunchKernelGGL(clear_words_kernel, dim3(1), dim3(256), 0, s, m.flag, 1,
-                           (unsigned *)nullptr, 0);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    // step numbers start at 1: cleared slots never match a step; XCD ids
-    // are published as id + 1
+    // one launch: the status word (clear_flag), the exchange slots (step
+    // numbers start at 1: cleared slots never match a step) and the XCD table
+    // (ids are published as id + 1)
     const long words = 2L * p.groups * 2 * p.BT * (m.r.Dh / 2);
     hipLaunchKernelGGL(clear_words_kernel, dim3(64), dim3(256), 0, s,
                        reinterpret_cast<unsigned *>(m.xg), (int)words,
-                       m.xcd_map ? m.xcc : (unsigned *)nullptr, m.xcd_map ? p.grid : 0);
+                       m.xcd_map ? m.xcc : (unsigned *)nullptr, m.xcd_map ? p.grid : 0,
+                       clear_flag ? m.flag : (unsigned *)nullptr, 1);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (cell == kLSTM)
