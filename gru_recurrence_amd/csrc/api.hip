@@ -318,6 +318,23 @@ bool pipelined(const Choice &ch, const rnn_dims *d, rnn_dtype dt, int cus) {
     return tiles > 2L * (cus - ch.rec.grid);
 }
 
+// Workgroups for an input projection that runs beside the recurrence: enough
+// to produce row panels 2.5 times as fast as the recurrence consumes them (a
+// 256x256 tile takes about 40 ns per unit of K on a busy chip; the recurrence
+// spends kGemmRowTile / B steps of the plan's predicted step time on a panel),
+// at most the `free` CUs, a multiple of 8 (whole XCD rounds).  More than
+// needed only slows the recurrence beside them (measured on the headline
+// shape: 112 workgroups 0.578 ms per fused call, 160 0.587).
+// RNN355_FUSED_GEMM_WGS overrides (sweeps).
+int proj_workgroups(const rnn_dims *d, const Choice &ch, int tiles_per_panel, int free) {
+    const int cap = std::max(8, free / 8 * 8);
+    const int want = env_int("RNN355_FUSED_GEMM_WGS");
+    if (want >= 8) return std::min(want / 8 * 8, cap);
+    const double panel_ns = (double)kGemmRowTile / d->B * std::max(ch.cand.ns_step, 1.0);
+    const double need = 2.5 * 40.0 * d->Din * tiles_per_panel / panel_ns;
+    return std::max(8, std::min(cap, (int)((need + 4) / 8) * 8));
+}
+
 // Forward = input projection + recurrence.  Pipelined (see pipelined()): one
 // launch whose first workgroups compute the projection in time order and
 // count finished 256-row panels of gx, while the recurrence's workgroups
@@ -360,18 +377,9 @@ rnn_status forward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, con
         a.panels = (int)panels;
         a.flag = (unsigned *)ws;
         a.spin_limit = spin_limit();
-        // projection workgroups: enough to produce row panels 2.5 times as
-        // fast as the recurrence consumes them (a 256x256 tile takes about
-        // 40 ns per unit of K on a busy chip), at most the CUs the recurrence
-        // leaves, a multiple of 8 (whole XCD rounds), at most one per tile.
-        // More than needed only slows the recurrence (measured on the
-        // headline shape: 112 workgroups 0.578 ms per call, 160 0.587)
+        // projection workgroups by rate (proj_workgroups), at most one per tile
         const long tiles = panels * a.ready_target;
-        const double panel_ns = (double)kGemmRowTile / d->B * std::max(ch.cand.ns_step, 1.0);
-        const double need = 2.5 * 40.0 * d->Din * a.ready_target / panel_ns;
-        int n_gemm = std::min(((cus - ch.rec.grid) / 8) * 8, (int)((need + 4) / 8) * 8);
-        const int want = env_int("RNN355_FUSED_GEMM_WGS");
-        if (want >= 8) n_gemm = std::min(want / 8 * 8, ((cus - ch.rec.grid) / 8) * 8);
+        int n_gemm = proj_workgroups(d, ch, (int)a.ready_target, cus - ch.rec.grid);
         if (n_gemm > tiles) n_gemm = (int)tiles;
         if (n_gemm < 8) n_gemm = (int)std::min<long>(8, tiles);
         return ok(launch_fwd_fused(cell, ch.rec, a, g, n_gemm, s)) ? RNN_OK : RNN_ERR_HIP;
@@ -760,6 +768,9 @@ rnn_status forward_chunked(int cell, const rnn_dims *d, rnn_dtype dt, int chunk,
     // would take longer than the chunk it feeds, so every chunk's projection
     // runs on the whole chip, in order on the caller's stream
     const bool beside = cus - rec_grid >= kChunkMinFreeCus;
+    // (all the free CUs: measured on the T = 8192 headline shape in chunks of
+    // 1024, 160 workgroups 4.29 ms, 112 4.33, 64 4.44 -- unlike the fused
+    // launch, a chunk's projection is done long before the chunk it feeds)
     const int gemm_wg = beside ? (cus - rec_grid) / 8 * 8 : 0;
     hipStream_t s2 = beside ? side_stream() : s;  // s may be the null stream
     CallEvents ev;
