@@ -21,6 +21,10 @@ namespace {
 // of the multi-CU kernel, then the operation's own regions, each 256-byte
 // aligned.
 constexpr size_t kHeader = 4096;
+// dR = h_{t-1}^T dS per head has few output tiles (Dh x G Dh each) and a tall
+// K (T B): up to 16 K slices so that it fills the chip (B16 NH4 Dh256: 256
+// workgroups instead of 128)
+constexpr int kMaxSplitKdR = 16;
 // header words [256, 1024): the multi-CU kernel's table of workgroup XCDs
 constexpr size_t kXccOffset = 1024;
 constexpr int kXccWords = (int)((kHeader - kXccOffset) / sizeof(unsigned));
@@ -99,7 +103,7 @@ BwdLayout bwd_layout(const rnn_dims *d, int G) {
     L.dbp = off;  off += align_up(sizeof(float) * (size_t)d->B * N);
     // split-K partials of the dW and dR contractions (used one after the other)
     const size_t pw = gemm_partial_bytes(d->Din, (int)N, 1, kMaxSplitK);
-    const size_t pr = gemm_partial_bytes(d->Dh, G * d->Dh, d->NH, kMaxSplitK);
+    const size_t pr = gemm_partial_bytes(d->Dh, G * d->Dh, d->NH, kMaxSplitKdR);
     L.part = off; off += align_up(pw > pr ? pw : pr);
     L.wt = off;   off += wt_bytes(d, G);                                     // W^T [N][Din]
     L.rt = off;   off += align_up(sizeof(uint16_t) * (size_t)d->NH * G * d->Dh * d->Dh);  // R^T per head
@@ -671,7 +675,7 @@ rnn_status backward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, co
         g.B = dS; g.ldb = N; g.strideB = GD;
         g.C = dR; g.ldc = GD; g.strideC = (long)Dh * GD;
         g.accumulate = accumulate ? 1 : 0;
-        g.ksplit = std::min(gemm_splitk_for(Dh, GD, M, NH, cus), kMaxSplitK);
+        g.ksplit = std::min(gemm_splitk_for(Dh, GD, M, NH, cus), kMaxSplitKdR);
         g.partial = part;
         if (!ok(launch_gemm_bf16(g, false, false, NH, stream))) return RNN_ERR_HIP;
     }
