@@ -134,6 +134,10 @@ int env_int(const char *name) {
     return e ? atoi(e) : 0;
 }
 int bt_override() { return env_int("RNN355_REC_BT"); }
+int env_int_or(const char *name, int dflt) {
+    const char *e = getenv(name);
+    return e ? atoi(e) : dflt;
+}
 // RNN355_MC_XCD=0: the multi-CU kernel numbers its workgroups group by
 // group and exchanges through memory even where a group could share an L2.
 bool mc_xcd_enabled() {
@@ -642,9 +646,19 @@ rnn_status backward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, co
             m.xcd_map = 1;
             m.xcc = (unsigned *)((char *)ws + kXccOffset);
         }
+        // Dh = 256 on two CUs per (head, row) where the pairs can share an
+        // XCD's L2 and all of them fit the chip at once
+        const bool two = pw.ok && env_int_or("RNN355_BWD_WIDE2", 1) != 0 && mc_xcd_enabled() &&
+                         mc_xcd_grouping(NH * B, 2 * NH * B) && 2 * NH * B <= device_cus();
         m.spin_limit = spin_limit();
-        const hipError_t e = pw.ok ? launch_rec_bwd_wide(cell, pw, m, stream)
-                                   : launch_rec_bwd(cell, p, m, stream);
+        hipError_t e;
+        if (two) {
+            m.xcd_map = 1;
+            m.xcc = (unsigned *)((char *)ws + kXccOffset);
+            e = launch_rec_bwd_wide2(cell, m, stream);
+        } else {
+            e = pw.ok ? launch_rec_bwd_wide(cell, pw, m, stream) : launch_rec_bwd(cell, p, m, stream);
+        }
         if (!ok(e)) return RNN_ERR_HIP;
     }
     // 3. parameter and input gradients

@@ -282,6 +282,10 @@ hipError_t launch_rec_bwd(int cell, const BwdPlan &p, const BwdArgs &m, hipStrea
 // and spin_limit are ignored.  The plan is plan_wide's (its lds is the
 // forward's; the launcher sets its own).
 hipError_t launch_rec_bwd_wide(int cell, const WidePlan &p, const BwdArgs &m, hipStream_t s);
+// The Dh = 256 reverse sweep on two CUs per (head, batch row) (2 NH B
+// workgroups, all resident; m.xcd_map needs NH B % 8 == 0): each holds half
+// of R in AGPRs and the two swap partial carries every step.
+hipError_t launch_rec_bwd_wide2(int cell, const BwdArgs &m, hipStream_t s);
 hipError_t launch_hprev_bf16(const float *h0, const float *h_seq, uint16_t *hprev, long BH,
                              long total, hipStream_t s);
 // db = (db if accumulate) + sum over batch tiles of db_part.

@@ -51,6 +51,7 @@
 #include "common.h"
 #include "gates.h"
 #include "kernels.h"
+#include "xcd.h"
 
 namespace rnn355 {
 
@@ -666,6 +667,289 @@ __global__ __launch_bounds__(kWideWaves * 64, 1) void rec_bwd_wide_kernel(BwdArg
     for (int g = 0; g < G; ++g) dbt[g * DH + u] = dbs[g];
 }
 
+// ---------------------------------------------------------------------------
+// The reverse sweep on two compute units per (head, batch row).  CU c owns
+// units [128c, 128c + 128): it runs their cell backward and multiplies their
+// G*128 gradient values (this step's dA, or dS for the GRU) with the matching
+// R columns for all 256 output units; the two CUs' partial carries are then
+// swapped (each sends the 128 partials of the other's units) and summed in a
+// fixed order (CU 0's first), so each CU has the carry of its own units.
+// Half of R per CU (256 KiB for the LSTM) fits the AGPRs: wave w multiplies
+// its G k-chunks of 32 gradient columns with 16 output tiles, every B
+// fragment in an AGPR (64 for the LSTM), no LDS fragments.  The two CUs of a
+// row are numbered onto one XCD and swap the partials through its L2 when
+// the launch finds them there (xcd.h), else through memory.  Per step the
+// other CU's 8 output tiles come first: their partials are summed over the
+// waves and sent while the waves multiply this CU's own 8 tiles, so the swap
+// travels during those MFMAs.  The swap is done by the two waves that run no
+// cell update: a poll waits for every earlier load and store of its thread,
+// and the cell threads' next inputs and gradient stores are in flight.
+template <int CELL>
+__global__ __launch_bounds__(kWideWaves * 64, 1) void rec_bwd_wide2_kernel(BwdArgs m) {
+    constexpr int DH = kWideDh, G = CellTraits<CELL>::G, GD = G * DH;
+    constexpr int U = DH / 2;       // units per CU
+    constexpr int NT = DH / 16;     // output tiles
+    constexpr int NCHW = G;         // k-chunks of 32 per wave (4G per CU)
+    constexpr int TG = 4, NG = NT / TG;
+    constexpr bool LSTM = CELL == kLSTM;
+    constexpr int NIN = LSTM ? G + 3 : 2 * G + 2;
+
+    __shared__ __attribute__((aligned(16))) float part[kWideWaves][DH];  // partial carries
+    __shared__ __attribute__((aligned(16))) uint16_t hs[G][U];           // this step's gradients
+    __shared__ float dhs[U];                                             // own units' carries
+    __shared__ int s_abort, s_local;
+
+    int group, c;
+    group_member(m.xcd_map != 0, 2, group, c);
+    const int n = group % m.NH, b = group / m.NH;
+    const int H = m.NH * DH, N = m.NH * GD, T = m.T, B = m.B;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    const bool cell_thread = tid < U;
+    const int u = 128 * c + (tid & (U - 1));  // the unit of a cell thread
+
+    // ---- R fragments: wave w, k-chunk i is gradient chunk q = G w + i of
+    // this CU (gate q / 4, units 128c + 32 (q % 4) ..); register slot jj holds
+    // output tile tile_of(jj) (units 16 tile ..): slots 0-7 the other CU's
+    // units, 8-15 this CU's
+    const int tile_off = 8 * (1 - c);
+    auto tile_of = [&](int jj) { return (jj + tile_off) & (NT - 1); };
+    const uint16_t *Rn = m.Rb + (long)n * DH * GD;
+    bf16x8 ra[NT * NCHW];
+    static_for<0, NT>([&](auto jc) {
+        constexpr int jj = decltype(jc)::value;
+        static_for<0, NCHW>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            const int q = G * w + i;
+            const int col = (q >> 2) * DH + 128 * c + 32 * (q & 3) + 8 * lg;
+            const uint4 v =
+                *reinterpret_cast<const uint4 *>(Rn + (long)(16 * tile_of(jj) + lr) * GD + col);
+            ra[jj * NCHW + i] = __builtin_bit_cast(bf16x8, v);
+        });
+    });
+
+    if (tid == 0) {
+        s_abort = 0;
+        s_local = 0;
+    }
+    if (m.xcd_map) xcd_publish(m.xcc);
+
+    const long o_row = (long)b * H + n * DH, a_row = (long)b * N + n * GD;
+    const long a_step = (long)B * N, o_step = (long)B * H;
+    float dhc = (cell_thread && m.dhT) ? m.dhT[o_row + u] : 0.f;
+    float dcc = (LSTM && cell_thread && m.dcT) ? m.dcT[o_row + u] : 0.f;
+    float dir = 0.f, dbs[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) dbs[g] = 0.f;
+    float in0[NIN], in1[NIN];
+#pragma unroll
+    for (int i = 0; i < NIN; ++i) in0[i] = in1[i] = 0.f;
+    auto load_in = [&](int t, float (&d)[NIN]) {
+        const float *pa = m.A + a_row + (long)t * a_step;
+#pragma unroll
+        for (int g = 0; g < G; ++g) d[g] = pa[g * DH + u];
+        d[NIN - 1] = m.dh_seq[o_row + (long)t * o_step + u];
+        if constexpr (LSTM) {
+            d[G] = m.c_seq[o_row + (long)t * o_step + u];
+            d[G + 1] = t > 0 ? m.c_seq[o_row + (long)(t - 1) * o_step + u]
+                             : (m.c0 ? m.c0[o_row + u] : 0.f);
+        } else {
+            const float *sv = m.S + a_row + (long)t * a_step;
+#pragma unroll
+            for (int g = 0; g < G; ++g) d[G + g] = sv[g * DH + u];
+            d[2 * G] = t > 0 ? m.h_seq[o_row + (long)(t - 1) * o_step + u]
+                             : (m.h0 ? m.h0[o_row + u] : 0.f);
+        }
+    };
+    if (cell_thread) load_in(T - 1, in0);
+    __syncthreads();
+    if (m.xcd_map && w == 0) {
+        const int v = xcd_members_agree(m.xcc, m.flag, m.spin_limit, group, 2);
+        if (lane == 0) {
+            s_local = v > 0;
+            if (v < 0) s_abort = 1;
+        }
+    }
+    __syncthreads();
+    const bool local = s_local != 0;
+    // exchange words [2 parities][2 senders][U]: sender c's partials of the
+    // other CU's units, tagged with the step
+    unsigned long long *xs = m.xg + (long)group * 2 * 2 * U;
+
+    auto step = [&](int s, float (&cur)[NIN], float (&nxt)[NIN]) -> bool {
+        const int t = T - 1 - s;
+        // 1. cell backward of this CU's units
+        if (cell_thread) {
+            if (s > 0) dhc = LSTM ? dhs[tid] : dir + dhs[tid];  // the previous step's carry
+            float d[G], e[G];
+            const float dh = cur[NIN - 1] + dhc;
+            if constexpr (LSTM) {
+                const float ig = sigmoid_f(cur[0]), fg = sigmoid_f(cur[1]);
+                const float zg = tanh_f(cur[2]), og = sigmoid_f(cur[3]);
+                const float tc = tanh_f(cur[G]);
+                const float dc = fmaf(dh * og, 1.0f - tc * tc, dcc);
+                d[0] = dc * zg * ig * (1.0f - ig);
+                d[1] = dc * cur[G + 1] * fg * (1.0f - fg);
+                d[2] = dc * ig * (1.0f - zg * zg);
+                d[3] = dh * tc * og * (1.0f - og);
+                dcc = dc * fg;
+#pragma unroll
+                for (int g = 0; g < G; ++g) e[g] = d[g];
+            } else {
+                const float rg = sigmoid_f(cur[0] + cur[G]);
+                const float ug = sigmoid_f(cur[1] + cur[G + 1]);
+                const float ng = tanh_f(fmaf(rg, cur[G + 2], cur[2]));
+                d[2] = dh * (1.0f - ug) * (1.0f - ng * ng);
+                d[1] = dh * (cur[2 * G] - ng) * ug * (1.0f - ug);
+                d[0] = d[2] * cur[G + 2] * rg * (1.0f - rg);
+                e[0] = d[0];
+                e[1] = d[1];
+                e[2] = d[2] * rg;
+                dir = dh * ug;
+            }
+            uint16_t *pa = m.dA + a_row + (long)t * a_step;
+            uint16_t *ps = LSTM ? nullptr : m.dS + a_row + (long)t * a_step;
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                dbs[g] += d[g];
+                const uint16_t dd = f32_to_bf16_rne(d[g]);
+                const uint16_t de = LSTM ? dd : f32_to_bf16_rne(e[g]);
+                pa[g * DH + u] = dd;
+                if constexpr (!LSTM) ps[g * DH + u] = de;
+                hs[g][tid] = de;
+            }
+            // the next step's inputs, once this step's are used (requested
+            // earlier, a wait for this step's would also wait for them)
+            if (t > 0) load_in(t - 1, nxt);
+        }
+        __syncthreads();
+        if (s_abort) return false;
+        // 2. partial carries of this CU's gradient columns, all 256 units
+        bf16x8 af[NCHW];
+#pragma unroll
+        for (int i = 0; i < NCHW; ++i) {
+            const int q = G * w + i;
+            af[i] = *reinterpret_cast<const bf16x8 *>(&hs[q >> 2][32 * (q & 3) + 8 * lg]);
+        }
+        auto tiles = [&](auto gc) {
+            constexpr int gi = decltype(gc)::value;
+            f32x4 acc[TG];
+            static_for<0, NCHW>([&](auto ic) {
+                constexpr int i = decltype(ic)::value;
+                static_for<0, TG>([&](auto kc) {
+                    constexpr int k = decltype(kc)::value;
+                    if constexpr (i == 0) mfma_b_agpr_first(acc[k], af[i], ra[(TG * gi + k) * NCHW + i]);
+                    else mfma_b_agpr(acc[k], af[i], ra[(TG * gi + k) * NCHW + i]);
+                });
+            });
+            chain_end(acc);
+            if (lg == 0) {
+#pragma unroll
+                for (int k = 0; k < TG; ++k) part[w][16 * tile_of(TG * gi + k) + lr] = acc[k][0];
+            }
+        };
+        // the other CU's tiles, summed over the waves and sent (by the
+        // threads that run no cell update) while the own tiles are multiplied
+        static_for<0, NG / 2>(tiles);
+        __syncthreads();
+        const int j = (tid + 128 * c) & (DH - 1);  // own units on the cell threads
+        unsigned long long *slot = xs + (long)(s & 1) * 2 * U;
+        const unsigned long long tag = (unsigned long long)(unsigned)(s + 1) << 32;
+        if (!cell_thread) {
+            float p = part[0][j];
+#pragma unroll
+            for (int ww = 1; ww < kWideWaves; ++ww) p += part[ww][j];
+            unsigned long long *dst = slot + c * U + (j & (U - 1));
+            const unsigned long long wv = tag | __float_as_uint(p);
+            if (local)
+                __hip_atomic_store(dst, wv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            else
+                __hip_atomic_store(dst, wv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        // the first poll of the other CU's partials goes out between the own
+        // tile groups, so that by the barrier it has usually returned with them
+        const unsigned long long *src = slot + (1 - c) * U + (tid & (U - 1));
+        unsigned long long wv = 0;
+        static_for<NG / 2, NG / 2 + 1>(tiles);
+        // (as volatile asm, kept in place among the MFMAs' asm: a device-scope
+        // load the compiler does not track, completed by the wait below)
+        if (!cell_thread)
+            asm volatile("global_load_dwordx2 %0, %1, off sc1" : "=v"(wv) : "v"(src) : "memory");
+        static_for<NG / 2 + 1, NG>(tiles);
+        __syncthreads();
+        if (!cell_thread) asm volatile("s_waitcnt vmcnt(0)" : "+v"(wv)::"memory");
+        // 3. own units (unit 128c + k on non-cell thread 128 + k): this CU's
+        // partial, completed with the other CU's, handed to the cell thread
+        if (!cell_thread) {
+            const int k = tid - U;
+            const int jo = 128 * c + k;
+            float p = part[0][jo];
+#pragma unroll
+            for (int ww = 1; ww < kWideWaves; ++ww) p += part[ww][jo];
+            unsigned spins = 0;
+            for (;;) {
+                if ((wv & 0xFFFFFFFF00000000ull) == tag) break;
+                ++spins;
+                if ((spins & 255u) == 0 &&
+                    __hip_atomic_load(m.flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+                    s_abort = 1;
+                    break;
+                }
+                if (spins >= m.spin_limit) {
+                    __hip_atomic_store(m.flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    s_abort = 1;
+                    break;
+                }
+                wv = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            const float q = __uint_as_float((unsigned)wv);
+            dhs[k] = c == 0 ? p + q : q + p;  // CU 0's partial first in both
+        }
+        __syncthreads();
+        return true;
+    };
+    int s = s_abort ? T + 1 : 0;
+    bool ok = s <= T;
+    for (; ok && s + 1 < T; s += 2) {
+        ok = step(s, in0, in1);
+        if (ok) ok = step(s + 1, in1, in0);
+    }
+    if (ok && s < T) ok = step(s, in0, in1), ++s;
+    if (!ok || s < T || !cell_thread) return;
+    if (T > 0) dhc = LSTM ? dhs[tid] : dir + dhs[tid];  // the last step's carry
+    m.dh0[o_row + u] = dhc;
+    if (LSTM) m.dc0[o_row + u] = dcc;
+    float *dbt = m.db_part + (long)b * N + n * GD;
+#pragma unroll
+    for (int g = 0; g < G; ++g) dbt[g * DH + u] = dbs[g];
+}
+
+__global__ void clear_words_wide_kernel(unsigned *p, long n, unsigned *p2, long n2, unsigned *p3,
+                                        long n3) {
+    const long i0 = blockIdx.x * (long)blockDim.x + threadIdx.x, step = (long)gridDim.x * blockDim.x;
+    if (p)
+        for (long i = i0; i < n; i += step) p[i] = 0u;
+    if (p2)
+        for (long i = i0; i < n2; i += step) p2[i] = 0u;
+    if (p3)
+        for (long i = i0; i < n3; i += step) p3[i] = 0u;
+}
+
+template <int CELL>
+hipError_t launch_bwd_wide2_t(const BwdArgs &m0, hipStream_t s) {
+    BwdArgs m = m0;
+    const int grid = 2 * m.NH * m.B;
+    const long words = (long)m.NH * m.B * 2 * 2 * (kWideDh / 2) * 2;  // as 32-bit words
+    hipLaunchKernelGGL(clear_words_wide_kernel, dim3(64), dim3(256), 0, s, m.flag, 1L,
+                       m.xcd_map ? m.xcc : (unsigned *)nullptr, m.xcd_map ? (long)grid : 0L,
+                       reinterpret_cast<unsigned *>(m.xg), words);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    void *args[] = {&m};
+    return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(&rec_bwd_wide2_kernel<CELL>),
+                                      dim3(grid), dim3(kWideWaves * 64), args, 0, s);
+}
+
 template <int CELL>
 hipError_t launch_bwd_wide_t(const WidePlan &p, const BwdArgs &m, hipStream_t s) {
     if (WideBwdCfg<CELL>::kLdsR > 0) {
@@ -702,6 +986,12 @@ WidePlan plan_wide(int cell, int B, int NH, int Dh, bool bf16) {
     p.threads = kWideWaves * 64;
     p.lds = cell == kLSTM ? WideCfg<kLSTM>::kLdsR : WideCfg<kGRU>::kLdsR;
     return p;
+}
+
+hipError_t launch_rec_bwd_wide2(int cell, const BwdArgs &m, hipStream_t s) {
+    if (m.Dh != kWideDh || m.T < 1 || (m.xcd_map && (!m.xcc || (m.NH * m.B) % 8 != 0)))
+        return hipErrorInvalidValue;
+    return cell == kLSTM ? launch_bwd_wide2_t<kLSTM>(m, s) : launch_bwd_wide2_t<kGRU>(m, s);
 }
 
 hipError_t launch_rec_bwd_wide(int cell, const WidePlan &p, const BwdArgs &m, hipStream_t s) {

@@ -23,7 +23,8 @@ TOL = 2e-2
 
 @pytest.fixture(autouse=True)
 def _clean_env():
-    keys = ("RNN355_REC_BT", "RNN355_REC_K", "RNN355_REC_WIDE", "RNN355_MC_XCD")
+    keys = ("RNN355_REC_BT", "RNN355_REC_K", "RNN355_REC_WIDE", "RNN355_MC_XCD",
+            "RNN355_BWD_WIDE2", "RNN355_SPIN_LIMIT")
     old = {k: os.environ.pop(k, None) for k in keys}
     yield
     for k in keys:
@@ -265,3 +266,78 @@ def test_backward_xcd_grouped_exchange(cell):
         e = nerr(got[k], ref[k])
         print("  %-4s nerr=%.3e" % (k, e), flush=True)
         assert e <= TOL, (k, e)
+
+
+def _bwd_with_ws(c, ws, final=True):
+    lstm = c.cell == "lstm"
+    x, W, R, b, h0 = dev(c, "x"), dev(c, "W"), dev(c, "R"), dev(c, "b"), dev(c, "h0")
+    if lstm:
+        c0 = dev(c, "c0")
+        h_seq, c_seq, _, _ = g.lstm_fwd(x, W, R, b, h0, c0)
+        grads = g.lstm_bwd(x, W, R, b, h0, c0, h_seq, c_seq, dev(c, "dH"),
+                           dev(c, "dhT") if final else None, dev(c, "dcT") if final else None,
+                           ws=ws)
+    else:
+        h_seq, _ = g.gru_fwd(x, W, R, b, h0)
+        grads = g.gru_bwd(x, W, R, b, h0, h_seq, dev(c, "dH"), dev(c, "dhT") if final else None,
+                          ws=ws)
+    torch.cuda.synchronize()
+    return {k: host(v) for k, v in grads.items()}
+
+
+# Dh = 256 with (heads x rows) a multiple of 8: the sweep runs on two CUs per
+# (head, row), each holding half of R in AGPRs and swapping partial carries
+# (RNN355_BWD_WIDE2=0: one CU with R split over AGPRs, VGPRs and LDS).  The
+# two sum the carries in different orders, so they agree to rounding.
+@pytest.mark.parametrize("cell", ["lstm", "gru"])
+def test_backward_two_cu_split_r(cell):
+    d = synth.Dims(T=17, B=4, Din=64, NH=2, Dh=256)
+    lstm = cell == "lstm"
+    c = synth.make_case(cell, d, "bf16", 9800 + (0 if lstm else 1),
+                        bias="forget+1" if lstm else "zero", h0_var=0.2, c0_var=0.2,
+                        backward=True, final_grads=True)
+    op = g.OP_BWD_LSTM if lstm else g.OP_BWD_GRU
+    ws = torch.empty(g.workspace_size(op, g.Dims(d.T, d.B, d.Din, d.NH, d.Dh), g.RNN_BF16),
+                     dtype=torch.uint8, device="cuda")
+    got = _bwd_with_ws(c, ws)
+    assert g.workspace_status(ws) == g.RNN_OK
+    again = _bwd_with_ws(c, ws)
+    for k in got:
+        assert np.array_equal(got[k], again[k]), k
+    if lstm:
+        ref = oracle.lstm_bwd(c.f64("x"), c.f64("W"), c.f64("R"), c.f64("b"), c.f64("h0"),
+                              c.f64("c0"), c.f64("dH"), c.f64("dhT"), c.f64("dcT"),
+                              NH=d.NH, Dh=d.Dh)
+    else:
+        ref = oracle.gru_bwd(c.f64("x"), c.f64("W"), c.f64("R"), c.f64("b"), c.f64("h0"),
+                             c.f64("dH"), c.f64("dhT"), NH=d.NH, Dh=d.Dh)
+    for k in got:
+        e = nerr(got[k], ref[k])
+        print("  %-4s nerr=%.3e" % (k, e), flush=True)
+        assert e <= TOL, (k, e)
+    os.environ["RNN355_BWD_WIDE2"] = "0"
+    one = _bwd_with_ws(c, ws)
+    for k in got:
+        e = nerr(got[k], one[k])
+        print("  %-4s two-CU vs one-CU nerr=%.3e" % (k, e), flush=True)
+        assert e <= 1e-2, (k, e)
+
+
+def test_backward_two_cu_timeout_is_reported():
+    """A spin limit of one poll (set from the host) makes the first swap of
+    partial carries give up: both CUs stop, the kernel ends normally and the
+    workspace reports the time-out; the next call clears it."""
+    d = synth.Dims(T=24, B=4, Din=32, NH=2, Dh=256)
+    c = synth.make_case("lstm", d, "bf16", 9900, bias="forget+1", backward=True,
+                        final_grads=True)
+    ws = torch.empty(g.workspace_size(g.OP_BWD_LSTM, g.Dims(d.T, d.B, d.Din, d.NH, d.Dh),
+                                      g.RNN_BF16), dtype=torch.uint8, device="cuda")
+    os.environ["RNN355_SPIN_LIMIT"] = "1"
+    _bwd_with_ws(c, ws)
+    assert g.workspace_status(ws) == g.RNN_ERR_BARRIER_TIMEOUT
+    os.environ.pop("RNN355_SPIN_LIMIT")
+    got = _bwd_with_ws(c, ws)
+    assert g.workspace_status(ws) == g.RNN_OK
+    ref = oracle.lstm_bwd(c.f64("x"), c.f64("W"), c.f64("R"), c.f64("b"), c.f64("h0"),
+                          c.f64("c0"), c.f64("dH"), c.f64("dhT"), c.f64("dcT"), NH=d.NH, Dh=d.Dh)
+    assert nerr(got["dh0"], ref["dh0"]) <= TOL
