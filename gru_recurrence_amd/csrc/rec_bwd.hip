@@ -376,6 +376,8 @@ hipError_t launch_bwd_cell(const BwdPlan &p, const BwdArgs &m, hipStream_t s) {
         case 8: return launch_bwd_rows<CELL, 8>(p, m, s);
         case 6: return launch_bwd_rows<CELL, 6>(p, m, s);
         case 4: return launch_bwd_rows<CELL, 4>(p, m, s);
+        case 3: return launch_bwd_rows<CELL, 3>(p, m, s);
+        case 2: return launch_bwd_rows<CELL, 2>(p, m, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -437,10 +439,11 @@ BwdPlan plan_bwd(int cell, int B, int NH, int Dh, int num_cu, int bt_override, i
     if (Dh % 16 != 0 || (G * Dh) % 32 != 0) return p;
     const int KC = G * Dh / 32;  // reduction chunks of 32 gate columns
     // at most 16 chunks per wave (its R^T fragments and the A fragments of
-    // one step then take 64 VGPRs each): the largest of 16, 12, 8, 6, 4
-    // that divides the chunk count
+    // one step then take 64 VGPRs each): the largest of 16, 12, 8, 6, 4, 3, 2
+    // that divides the chunk count (GRU counts are multiples of 3, LSTM
+    // counts even, so one always does)
     p.kcw = 0;
-    for (const int c : {16, 12, 8, 6, 4}) {
+    for (const int c : {16, 12, 8, 6, 4, 3, 2}) {
         if (KC % c == 0) {
             p.kcw = c;
             break;

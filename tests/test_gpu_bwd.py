@@ -47,6 +47,7 @@ def gpu_bwd(c, final=False):
 # default there is one workgroup per (head, row) with R split over
 # registers and LDS)
 @pytest.mark.parametrize("Dh,B,bt,final", [
+    (16, 3, None, True),      # two gate-column chunks per head (two per wave)
     (32, 3, None, False),     # one workgroup per head, dA through LDS
     (64, 5, 2, True),         # two row slots, ragged, final-state gradients
     (128, 3, 4, False),       # four row slots
@@ -145,6 +146,7 @@ def gpu_bwd_gru(c, final=False):
 
 
 @pytest.mark.parametrize("Dh,B,bt,final", [
+    (32, 3, None, True),      # three gate-column chunks per head (three per wave)
     (64, 3, None, False),     # one workgroup per (head, row): 6 chunks per wave, dS through LDS
     (64, 5, 2, True),         # two row slots, ragged, final-state gradient
     (128, 2, None, True),     # 12 chunks per wave, one workgroup
