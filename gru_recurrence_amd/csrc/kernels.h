@@ -2,6 +2,8 @@
 // (internal; the public interface is include/rnn355.h).
 #pragma once
 
+#include <cstdlib>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -188,6 +190,15 @@ struct McArgs {
 // the groups divide over the 8 XCDs and the id table fits the workspace
 // header.
 constexpr int kMcXcdMaxGrid = 768;
+// 2..4 batch rows per multi-CU workgroup run the cell update with row q in
+// lane group q (one pass for all rows) unless RNN355_MC_ROWLANES=0 keeps
+// them in register slots (one pass per row).
+inline bool mc_row_lanes(int bt) {
+    if (bt < 2 || bt > 4) return false;
+    const char *e = getenv("RNN355_MC_ROWLANES");
+    return !e || atoi(e) != 0;
+}
+
 inline bool mc_xcd_grouping(int groups, int grid) {
     return groups > 0 && groups % 8 == 0 && grid <= kMcXcdMaxGrid;
 }

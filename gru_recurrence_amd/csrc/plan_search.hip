@@ -57,6 +57,7 @@ namespace {
 // kernels; see the calibration in the design notes).
 constexpr double kMfmaNs = 7.95;          // one 16x16x32 bf16 MFMA issued per SIMD
 constexpr double kGateNs[3] = {61.5, 136.5, 261.5};  // cell update per gate, 1/2/4 row slots
+constexpr double kGateLanesNs = 100.0;    // ... 2-4 rows in lane groups (multi-CU), per gate
 constexpr double kWideRowsNs = 250.0;     // more than 8 rows of a tile: second row half
 constexpr double kExchangeNs = 1480.0;    // cross-CU step exchange (flag-in-data words)
 constexpr double kExchangeLocalNs = 580.0; // ... base when a group's members share one XCD's L2
@@ -236,7 +237,11 @@ void family_multicu(int cell, int T, int B, int NH, int Dh, bool bf16, int cus,
                 if (fix.kcw > 0 && kcw != fix.kcw) fail(c, kPlanFixed);
                 const int per_simd = ceil_div(c.waves, kSimds);
                 c.xcd_local = !fix.no_xcd && mc_xcd_grouping(NH * ceil_div(B, bt), c.grid);
-                c.ns_step = kMfmaNs * G * kcw * per_simd + G * kGateNs[r4_index(c.r4)] +
+                // 2..4 rows in lane groups: one cell update pass, no row slots
+                const bool lanes = mc_row_lanes(bt);
+                if (lanes) c.r4 = 1;
+                c.ns_step = kMfmaNs * G * kcw * per_simd +
+                            G * (lanes ? kGateLanesNs : kGateNs[r4_index(c.r4)]) +
                             (c.xcd_local ? kExchangeLocalNs : kExchangeNs) +
                             kExchangePerWgNs * std::max(c.K, 1) +
                             kExchangePerValNs * Dh * bt +

@@ -48,10 +48,15 @@ namespace rnn355 {
 
 namespace {
 
-template <int CELL, int KCW, int R4>
+// RL: 2..4 batch rows per workgroup with row q of the tile in lane group q
+// (16 lanes) instead of register slot q: the MFMA's rows are moved there by
+// three cross-row swaps per gate, and one cell update per lane serves every
+// row at once (the slot layout runs the update once per row).
+template <int CELL, int KCW, int R4, bool RL = false>
 __global__ __launch_bounds__(512) void rec_fwd_mc_kernel(McArgs m) {
     constexpr int G = CellTraits<CELL>::G;
-    constexpr bool ROWS1 = R4 == 1;
+    constexpr bool ROWS1 = R4 == 1 && !RL;
+    static_assert(!RL || R4 == 1, "RL keeps one state slot per lane");
     constexpr int GL = ROWS1 ? 1 : G;
     constexpr int OUT_ROW = CELL == kLSTM ? 0 : 3;
     const RecArgs &a = m.r;
@@ -125,7 +130,7 @@ __global__ __launch_bounds__(512) void rec_fwd_mc_kernel(McArgs m) {
     float st[R4], hl[R4], gxr[R4][GL], ph[R4], pc[R4];
 #pragma unroll
     for (int r = 0; r < R4; ++r) {
-        const int b = ROWS1 ? 0 : 4 * lg + r;
+        const int b = RL ? lg : ROWS1 ? 0 : 4 * lg + r;
         rv[r] = b < rows;
         ld[r] = gate_wave && (ROWS1 ? lg < G : rv[r]);
         wr[r] = gate_wave && (ROWS1 ? lg == OUT_ROW : rv[r]);
@@ -213,7 +218,21 @@ __global__ __launch_bounds__(512) void rec_fwd_mc_kernel(McArgs m) {
         const unsigned long long tag = (unsigned long long)(unsigned)(t + 1) << 32;
         if (gate_wave) {
             float h[R4], c[R4];
-            gate_update<CELL, R4>(acc, gxr, st, hl, h, c);
+            if constexpr (RL) {
+                // lane group q <- register slot q of lane group 0 (batch row q)
+                float pre[G];
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const RowPair p = swap16(acc[g][0], acc[g][1]);
+                    const RowPair q = swap16(acc[g][2], acc[g][3]);
+                    const float v = swap32(p.a, q.a).a;
+                    pre[g] = (CELL == kGRU && g == 2) ? v : v + gxr[0][g];
+                }
+                h[0] = unit_update<CELL>(pre, CELL == kGRU ? gxr[0][2] : 0.f, st[0], c[0]);
+                hl[0] = h[0];
+            } else {
+                gate_update<CELL, R4>(acc, gxr, st, hl, h, c);
+            }
 #pragma unroll
             for (int r = 0; r < R4; ++r) {
                 ph[r] = h[r];
@@ -223,7 +242,8 @@ __global__ __launch_bounds__(512) void rec_fwd_mc_kernel(McArgs m) {
                 const unsigned hb = f32_to_bf16_rne(h[r]);
                 const unsigned nb = (unsigned)__shfl_xor((int)hb, 1);
                 if (wr[r] && (lr & 1) == 0) {
-                    unsigned long long *dst = slot + (ROWS1 ? 0 : 4 * lg + r) * wpr + (j >> 1);
+                    unsigned long long *dst =
+                        slot + (RL ? lg : ROWS1 ? 0 : 4 * lg + r) * wpr + (j >> 1);
                     const unsigned long long w = tag | (nb << 16) | hb;
                     if (local)
                         __hip_atomic_store(dst, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -315,16 +335,18 @@ __global__ void clear_words_kernel(unsigned *p, int n, unsigned *p2, int n2, uns
         for (int i = i0; i < n3; i += step) p3[i] = 0u;
 }
 
-template <int CELL, int KCW, int R4>
+template <int CELL, int KCW, int R4, bool RL = false>
 hipError_t launch_mc_t(const McPlan &p, McArgs m, hipStream_t s) {
     void *args[] = {&m};
     return hipLaunchCooperativeKernel(
-        reinterpret_cast<const void *>(&rec_fwd_mc_kernel<CELL, KCW, R4>), dim3(p.grid),
+        reinterpret_cast<const void *>(&rec_fwd_mc_kernel<CELL, KCW, R4, RL>), dim3(p.grid),
         dim3(p.threads), args, p.lds, s);
 }
 
+
 template <int CELL, int KCW>
 hipError_t launch_mc_rows(const McPlan &p, const McArgs &m, hipStream_t s) {
+    if (mc_row_lanes(p.BT)) return launch_mc_t<CELL, KCW, 1, true>(p, m, s);
     switch (p.r4) {
         case 1: return launch_mc_t<CELL, KCW, 1>(p, m, s);
         case 2: return launch_mc_t<CELL, KCW, 2>(p, m, s);

@@ -23,7 +23,7 @@ TOL_BF16 = 2e-2
 @pytest.fixture(autouse=True)
 def _clean_env():
     keys = ("RNN355_REC_BT", "RNN355_REC_K", "RNN355_SPIN_LIMIT", "RNN355_REC_WIDE",
-            "RNN355_MC_XCD")
+            "RNN355_MC_XCD", "RNN355_MC_ROWLANES")
     old = {k: os.environ.pop(k, None) for k in keys}
     os.environ["RNN355_REC_WIDE"] = "0"
     yield
@@ -116,6 +116,38 @@ def test_multicu_xcd_grouped_exchange(cell, Dh, NH, B, bt):
     assert g.workspace_status(ws) == g.RNN_OK
     for key in got:
         assert np.array_equal(got[key], mem[key]), key
+    ref = want(c)
+    for key in got:
+        e = nerr(got[key], ref[key])
+        print("  %-6s nerr=%.3e" % (key, e), flush=True)
+        assert e <= TOL_BF16, (key, e)
+
+
+# 2..4 batch rows per workgroup: by default the gate wave moves row q of the
+# MFMA tile into lane group q and runs the cell update once for all rows;
+# RNN355_MC_ROWLANES=0 runs it once per row from the register slots.  The
+# sums and the cell arithmetic are the same, so the outputs are the same bits.
+@pytest.mark.parametrize("cell,Dh,NH,B,bt", [
+    ("lstm", 256, 2, 5, 2),     # ragged: the last tile holds one row
+    ("lstm", 256, 1, 7, 4),     # four rows, ragged (3 in the last tile)
+    ("gru", 256, 2, 6, 3),
+    ("gru", 384, 1, 4, 4),      # k split over waves
+    ("lstm", 768, 1, 16, None), # the Dh = 768 plan (two rows per tile)
+])
+def test_multicu_rows_in_lane_groups_bitwise(cell, Dh, NH, B, bt):
+    if bt is not None:
+        os.environ["RNN355_REC_BT"] = str(bt)
+    d = synth.Dims(T=17, B=B, Din=64, NH=NH, Dh=Dh)
+    c = synth.make_case(cell, d, "bf16", 8700 + Dh + B, bias="forget+1" if cell == "lstm" else "zero",
+                        h0_var=0.2, c0_var=0.2)
+    p = plan(c)
+    print("  plan:", p, flush=True)
+    assert "multi_cu" in p and "rows_per_wg=1 " not in p
+    got = run(c)
+    os.environ["RNN355_MC_ROWLANES"] = "0"
+    slots = run(c)
+    for key in got:
+        assert np.array_equal(got[key], slots[key]), key
     ref = want(c)
     for key in got:
         e = nerr(got[key], ref[key])
