@@ -190,11 +190,11 @@ struct McArgs {
 // the groups divide over the 8 XCDs and the id table fits the workspace
 // header.
 constexpr int kMcXcdMaxGrid = 768;
-// 2..4 batch rows per multi-CU workgroup run the cell update with row q in
-// lane group q (one pass for all rows) unless RNN355_MC_ROWLANES=0 keeps
-// them in register slots (one pass per row).
+// 2..16 batch rows per multi-CU workgroup run the cell update with rows in
+// lane groups (one pass per four rows) unless RNN355_MC_ROWLANES=0 keeps
+// them in register slots (one pass per register slot).
 inline bool mc_row_lanes(int bt) {
-    if (bt < 2 || bt > 4) return false;
+    if (bt < 2 || bt > 16) return false;
     const char *e = getenv("RNN355_MC_ROWLANES");
     return !e || atoi(e) != 0;
 }

@@ -57,7 +57,9 @@ namespace {
 // kernels; see the calibration in the design notes).
 constexpr double kMfmaNs = 7.95;          // one 16x16x32 bf16 MFMA issued per SIMD
 constexpr double kGateNs[3] = {61.5, 136.5, 261.5};  // cell update per gate, 1/2/4 row slots
-constexpr double kGateLanesNs = 100.0;    // ... 2-4 rows in lane groups (multi-CU), per gate
+constexpr double kGateLanesNs = 100.0;    // ... rows in lane groups (multi-CU), per gate
+constexpr double kGateLanesPassNs = 120.0; // ... per further pass of four rows
+constexpr double kGatherRoundNs = 400.0;  // multi-CU: per further poll round of the gather
 constexpr double kWideRowsNs = 250.0;     // more than 8 rows of a tile: second row half
 constexpr double kExchangeNs = 1480.0;    // cross-CU step exchange (flag-in-data words)
 constexpr double kExchangeLocalNs = 580.0; // ... base when a group's members share one XCD's L2
@@ -71,9 +73,11 @@ constexpr double kLdsBaseNs = 415.0;      // LDS kernel: barriers and cell updat
 constexpr double kLdsDotNs = 37.6;        // ... per k of a dot product pass
 constexpr double kShareSlowdown = 0.35;   // per extra workgroup sharing a CU
 // The one variant whose spills sit in the step loop (compiler report: 223
-// VGPRs spilled; measured 7.0 us per step against 3.5-4.0 for its
-// neighbours): LSTM, several CUs per head, kcw 8, four row slots.
-constexpr double kSpillBoundNs = 3000.0;
+// VGPRs spilled): LSTM, several CUs per head, kcw 8, four row slots in the
+// register-slot layout (the lane-group layout keeps only a few reloads).
+// Fitted to 1.5-3.0 us per step more than the lane-group layout measured at
+// the same shapes.
+constexpr double kSpillBoundNs = 2000.0;
 
 constexpr int kVgprWave = 256, kAgprWave = 256, kRegsSimd = 512, kSimds = 4;
 constexpr int kRVgprMax = 128;
@@ -237,16 +241,20 @@ void family_multicu(int cell, int T, int B, int NH, int Dh, bool bf16, int cus,
                 if (fix.kcw > 0 && kcw != fix.kcw) fail(c, kPlanFixed);
                 const int per_simd = ceil_div(c.waves, kSimds);
                 c.xcd_local = !fix.no_xcd && mc_xcd_grouping(NH * ceil_div(B, bt), c.grid);
-                // 2..4 rows in lane groups: one cell update pass, no row slots
+                // rows in lane groups: one cell update pass per four rows (1, 2
+                // or 4 passes as compiled); the gather polls 4 words a thread
                 const bool lanes = mc_row_lanes(bt);
-                if (lanes) c.r4 = 1;
+                if (lanes) c.r4 = bt <= 4 ? 1 : bt <= 8 ? 2 : 4;
+                const int rounds = ceil_div(bt * (Dh / 2), 4 * 64 * c.waves);
                 c.ns_step = kMfmaNs * G * kcw * per_simd +
-                            G * (lanes ? kGateLanesNs : kGateNs[r4_index(c.r4)]) +
+                            G * (lanes ? kGateLanesNs + kGateLanesPassNs * (c.r4 - 1)
+                                       : kGateNs[r4_index(c.r4)]) +
+                            kGatherRoundNs * std::max(rounds - 1, 0) +
                             (c.xcd_local ? kExchangeLocalNs : kExchangeNs) +
                             kExchangePerWgNs * std::max(c.K, 1) +
                             kExchangePerValNs * Dh * bt +
                             (c.ks > 1 ? kSplitBaseNs + kSplitPerWaveNs * c.ks : 0.0) +
-                            (cell == kLSTM && kcw == 8 && c.r4 == 4 ? kSpillBoundNs : 0.0);
+                            (cell == kLSTM && kcw == 8 && c.r4 == 4 && !lanes ? kSpillBoundNs : 0.0);
                 finish(c, T, cus);
                 out.add(c);
             }

@@ -48,15 +48,16 @@ namespace rnn355 {
 
 namespace {
 
-// RL: 2..4 batch rows per workgroup with row q of the tile in lane group q
-// (16 lanes) instead of register slot q: the MFMA's rows are moved there by
-// three cross-row swaps per gate, and one cell update per lane serves every
-// row at once (the slot layout runs the update once per row).
+// RL: batch rows in lane groups.  The MFMA leaves row 4p + r of the tile in
+// register r of lane group p; RL transposes that 4 x 4 block per gate (two
+// 16-lane and two 32-lane swaps) so that pass p holds row 4p + q in lane
+// group q, and each cell update pass serves four rows at once: R4 passes
+// cover 4 R4 rows (the slot layout runs one pass per register, four passes
+// for any tile of more than two rows).
 template <int CELL, int KCW, int R4, bool RL = false>
 __global__ __launch_bounds__(512) void rec_fwd_mc_kernel(McArgs m) {
     constexpr int G = CellTraits<CELL>::G;
     constexpr bool ROWS1 = R4 == 1 && !RL;
-    static_assert(!RL || R4 == 1, "RL keeps one state slot per lane");
     constexpr int GL = ROWS1 ? 1 : G;
     constexpr int OUT_ROW = CELL == kLSTM ? 0 : 3;
     const RecArgs &a = m.r;
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(512) void rec_fwd_mc_kernel(McArgs m) {
     float st[R4], hl[R4], gxr[R4][GL], ph[R4], pc[R4];
 #pragma unroll
     for (int r = 0; r < R4; ++r) {
-        const int b = RL ? lg : ROWS1 ? 0 : 4 * lg + r;
+        const int b = RL ? 4 * r + lg : ROWS1 ? 0 : 4 * lg + r;
         rv[r] = b < rows;
         ld[r] = gate_wave && (ROWS1 ? lg < G : rv[r]);
         wr[r] = gate_wave && (ROWS1 ? lg == OUT_ROW : rv[r]);
@@ -219,17 +220,32 @@ __global__ __launch_bounds__(512) void rec_fwd_mc_kernel(McArgs m) {
         if (gate_wave) {
             float h[R4], c[R4];
             if constexpr (RL) {
-                // lane group q <- register slot q of lane group 0 (batch row q)
-                float pre[G];
+                // pass p, lane group q <- register q of lane group p (row 4p + q)
+                float v[R4][G];
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
                     const RowPair p = swap16(acc[g][0], acc[g][1]);
                     const RowPair q = swap16(acc[g][2], acc[g][3]);
-                    const float v = swap32(p.a, q.a).a;
-                    pre[g] = (CELL == kGRU && g == 2) ? v : v + gxr[0][g];
+                    const RowPair x = swap32(p.a, q.a);  // passes 0, 2
+                    v[0][g] = x.a;
+                    if constexpr (R4 > 1) {
+                        const RowPair y = swap32(p.b, q.b);  // passes 1, 3
+                        v[1][g] = y.a;
+                        if constexpr (R4 > 2) {
+                            v[2][g] = x.b;
+                            v[3][g] = y.b;
+                        }
+                    }
                 }
-                h[0] = unit_update<CELL>(pre, CELL == kGRU ? gxr[0][2] : 0.f, st[0], c[0]);
-                hl[0] = h[0];
+#pragma unroll
+                for (int r = 0; r < R4; ++r) {
+                    float pre[G];
+#pragma unroll
+                    for (int g = 0; g < G; ++g)
+                        pre[g] = (CELL == kGRU && g == 2) ? v[r][g] : v[r][g] + gxr[r][g];
+                    h[r] = unit_update<CELL>(pre, CELL == kGRU ? gxr[r][2] : 0.f, st[r], c[r]);
+                    hl[r] = h[r];
+                }
             } else {
                 gate_update<CELL, R4>(acc, gxr, st, hl, h, c);
             }
@@ -243,7 +259,7 @@ __global__ __launch_bounds__(512) void rec_fwd_mc_kernel(McArgs m) {
                 const unsigned nb = (unsigned)__shfl_xor((int)hb, 1);
                 if (wr[r] && (lr & 1) == 0) {
                     unsigned long long *dst =
-                        slot + (RL ? lg : ROWS1 ? 0 : 4 * lg + r) * wpr + (j >> 1);
+                        slot + (RL ? 4 * r + lg : ROWS1 ? 0 : 4 * lg + r) * wpr + (j >> 1);
                     const unsigned long long w = tag | (nb << 16) | hb;
                     if (local)
                         __hip_atomic_store(dst, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -346,7 +362,11 @@ hipError_t launch_mc_t(const McPlan &p, McArgs m, hipStream_t s) {
 
 template <int CELL, int KCW>
 hipError_t launch_mc_rows(const McPlan &p, const McArgs &m, hipStream_t s) {
-    if (mc_row_lanes(p.BT)) return launch_mc_t<CELL, KCW, 1, true>(p, m, s);
+    if (mc_row_lanes(p.BT)) {
+        if (p.BT <= 4) return launch_mc_t<CELL, KCW, 1, true>(p, m, s);
+        if (p.BT <= 8) return launch_mc_t<CELL, KCW, 2, true>(p, m, s);
+        return launch_mc_t<CELL, KCW, 4, true>(p, m, s);
+    }
     switch (p.r4) {
         case 1: return launch_mc_t<CELL, KCW, 1>(p, m, s);
         case 2: return launch_mc_t<CELL, KCW, 2>(p, m, s);

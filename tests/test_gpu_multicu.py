@@ -123,9 +123,9 @@ def test_multicu_xcd_grouped_exchange(cell, Dh, NH, B, bt):
         assert e <= TOL_BF16, (key, e)
 
 
-# 2..4 batch rows per workgroup: by default the gate wave moves row q of the
-# MFMA tile into lane group q and runs the cell update once for all rows;
-# RNN355_MC_ROWLANES=0 runs it once per row from the register slots.  The
+# 2..16 batch rows per workgroup: by default the gate wave transposes the
+# MFMA tile so that each cell update pass covers four rows (row 4p + q in lane
+# group q); RNN355_MC_ROWLANES=0 runs one pass per register slot.  The
 # sums and the cell arithmetic are the same, so the outputs are the same bits.
 @pytest.mark.parametrize("cell,Dh,NH,B,bt", [
     ("lstm", 256, 2, 5, 2),     # ragged: the last tile holds one row
@@ -133,6 +133,10 @@ def test_multicu_xcd_grouped_exchange(cell, Dh, NH, B, bt):
     ("gru", 256, 2, 6, 3),
     ("gru", 384, 1, 4, 4),      # k split over waves
     ("lstm", 768, 1, 16, None), # the Dh = 768 plan (two rows per tile)
+    ("lstm", 384, 2, 13, 6),    # two passes (rows 0-3, 4-5), ragged (tiles 6, 6, 1)
+    ("gru", 256, 1, 16, 8),     # two passes, 8 k-chunks per wave
+    ("lstm", 256, 1, 11, 12),   # four passes, one ragged tile of 11 rows
+    ("lstm", 512, 1, 16, 16),   # four passes, a full 16-row tile
 ])
 def test_multicu_rows_in_lane_groups_bitwise(cell, Dh, NH, B, bt):
     if bt is not None:

@@ -151,14 +151,18 @@ def test_workload_plans(shape, want):
 
 
 def _predicted(p):
-    """The model's time for the measured plan (under the point's exchange
-    setting: RNN355_MC_XCD=0 prices the multi-CU exchange through memory)."""
-    if "RNN355_MC_XCD" in p["env"]:
-        os.environ["RNN355_MC_XCD"] = p["env"]["RNN355_MC_XCD"]
+    """The model's time for the measured plan (under the point's exchange and
+    row layout settings: RNN355_MC_XCD=0 prices the multi-CU exchange through
+    memory, RNN355_MC_ROWLANES=0 the cell update over register slots)."""
+    keys = ("RNN355_MC_XCD", "RNN355_MC_ROWLANES")
+    for k in keys:
+        if k in p["env"]:
+            os.environ[k] = p["env"][k]
     try:
         cands, _ = search(p["cell"], p["T"], p["B"], p["NH"], p["Dh"], p["dtype"])
     finally:
-        os.environ.pop("RNN355_MC_XCD", None)
+        for k in keys:
+            os.environ.pop(k, None)
     c = match(cands, plan_vars(p["plan"], p["Dh"]))
     return c["ns_total"] / p["T"], c
 
@@ -206,8 +210,8 @@ def test_default_choice_is_the_best_measured_plan():
         chosen = {k: cands[best][k] for k in ("family", "rows_per_wg", "wg_per_head")}
         meas = {}
         for p in ps:
-            if "RNN355_MC_XCD" in p["env"]:
-                continue  # the default keeps the XCD-grouped exchange on
+            if "RNN355_MC_XCD" in p["env"] or "RNN355_MC_ROWLANES" in p["env"]:
+                continue  # the defaults keep the XCD grouping and row lanes on
             v = plan_vars(p["plan"], key[4])
             meas[(v["family"], v["rows_per_wg"], v.get("wg_per_head", 1))] = p["ns_step"]
         k = (chosen["family"], chosen["rows_per_wg"], chosen["wg_per_head"])
