@@ -481,6 +481,9 @@ int oracle_input_proj(long M, int K, int N, const double *x, const double *W,
                       const double *bias, long nrows, const long *rows, double *gx) {
     if (M <= 0 || K <= 0 || N <= 0) return -1;
     const long R = rows ? nrows : M;
+    if (rows)
+        for (long e = 0; e < nrows; ++e)
+            if (rows[e] < 0 || rows[e] >= M) return -1;
 #pragma omp parallel for
     for (long e = 0; e < R; ++e) {
         const long m = rows ? rows[e] : e;
