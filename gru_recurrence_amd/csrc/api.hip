@@ -926,6 +926,54 @@ rnn_status backward_ckpt(int cell, const rnn_dims *d, rnn_dtype dt, int chunk, c
 
 }  // namespace
 
+namespace rnn355 {
+
+// A grid whose workgroups wait on one another every step (bounded polls of
+// step-tagged words, no grid-wide barrier) needs all of them on the chip at
+// once.  The host checks that it fits (resident workgroups per CU from the
+// kernel's registers and LDS, times the CU count) and then dispatches it as
+// an ordinary launch; workgroups are dispatched in index order, and a member
+// that never arrived would end its partners' polls at the spin limit with
+// RNN_ERR_BARRIER_TIMEOUT, not a hang.  (A cooperative launch gives the same
+// residency guarantee but goes through a second device queue of the runtime,
+// whose teardown at process exit outlived a profiler's interception tables.)
+hipError_t launch_all_resident(const void *fn, int grid, int threads, void **args, size_t lds,
+                               hipStream_t s) {
+    struct Key {
+        int dev;
+        const void *fn;
+        int threads;
+        size_t lds;
+        int per_cu;
+    };
+    static std::mutex mu;
+    static Key cache[64];
+    static int ncache = 0;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    int per_cu = -1;
+    {
+        std::lock_guard<std::mutex> lk(mu);
+        for (int i = 0; i < ncache; ++i)
+            if (cache[i].dev == dev && cache[i].fn == fn && cache[i].threads == threads &&
+                cache[i].lds == lds)
+                per_cu = cache[i].per_cu;
+    }
+    if (per_cu < 0) {
+        int nb = 0;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, threads, lds);
+        if (e != hipSuccess) return e;
+        per_cu = nb;
+        std::lock_guard<std::mutex> lk(mu);
+        if (ncache < 64) cache[ncache++] = Key{dev, fn, threads, lds, per_cu};
+    }
+    if ((long)per_cu * device_cus() < grid) return hipErrorCooperativeLaunchTooLarge;
+    return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, lds, s);
+}
+
+}  // namespace rnn355
+
 extern "C" {
 
 const char *rnn_status_str(rnn_status s) {

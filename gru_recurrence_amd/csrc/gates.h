@@ -69,11 +69,11 @@ __device__ __forceinline__ void gate_rows_update(float v, float gx, float &st, f
         const float cn = fmaf(F.a, st, I.a * I.b);
         st = cn;
         c = cn;
-        h = F.b * tanh_f(cn);
+        h = F.b * tanh_abs(cn);
         hl = h;
     } else {
         const RowPair W = swap32(sg, sg);                 // rows r, u, r, u
-        const float nn = tanh_f(fmaf(W.a, v, gx));        // row 2: tanh(Gx_n + r S_n)
+        const float nn = tanh_abs(fmaf(W.a, v, gx));      // row 2: tanh(Gx_n + r S_n)
         const float nn3 = swap16(nn, nn).a;               // row 3 <- row 2
         const float hn = fmaf(W.a, st - nn3, nn3);        // row 3: (1-u) nn + u h
         st = hn;

@@ -209,8 +209,14 @@ inline bool mc_xcd_grouping(int groups, int grid) {
 McPlan plan_mc(int cell, int B, int NH, int Dh, int num_cu, int bt_override, int k_override,
                int kcw = 0);
 
+// Ordinary launch of a grid whose workgroups wait on one another, after a
+// host check that the whole grid is resident at once (api.hip); returns
+// hipErrorCooperativeLaunchTooLarge if it is not.
+hipError_t launch_all_resident(const void *fn, int grid, int threads, void **args, size_t lds,
+                               hipStream_t s);
+
 // Clears the exchange slots and (if clear_flag) the abort word, then
-// launches cooperatively.
+// launches the grid with every workgroup resident.
 hipError_t launch_rec_mc(int cell, const McPlan &p, const McArgs &m, hipStream_t s,
                          bool clear_flag = true);
 

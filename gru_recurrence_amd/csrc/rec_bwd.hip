@@ -354,9 +354,8 @@ __global__ __launch_bounds__(512) void rec_bwd_kernel(BwdArgs m) {
 template <int CELL, int KCW, int R4>
 hipError_t launch_bwd_t(const BwdPlan &p, BwdArgs m, hipStream_t s) {
     void *args[] = {&m};
-    return hipLaunchCooperativeKernel(
-        reinterpret_cast<const void *>(&rec_bwd_kernel<CELL, KCW, R4>), dim3(p.grid),
-        dim3(p.threads), args, p.lds, s);
+    return launch_all_resident(reinterpret_cast<const void *>(&rec_bwd_kernel<CELL, KCW, R4>),
+                               p.grid, p.threads, args, p.lds, s);
 }
 
 template <int CELL, int KCW>

@@ -1,6 +1,6 @@
 // rec_mc.hip -- forward recurrence for heads whose R block does not fit one
 // compute unit: the hidden units of one head are split over K workgroups
-// (one per CU, co-resident by cooperative launch) that swap h_t through
+// (one per CU, all resident at once, checked on the host) that swap h_t through
 // global memory at every step.
 //
 // FlashRNN (arXiv 2412.07752, abstract) stresses that its CUDA kernels reach
@@ -354,9 +354,8 @@ __global__ void clear_words_kernel(unsigned *p, int n, unsigned *p2, int n2, uns
 template <int CELL, int KCW, int R4, bool RL = false>
 hipError_t launch_mc_t(const McPlan &p, McArgs m, hipStream_t s) {
     void *args[] = {&m};
-    return hipLaunchCooperativeKernel(
-        reinterpret_cast<const void *>(&rec_fwd_mc_kernel<CELL, KCW, R4, RL>), dim3(p.grid),
-        dim3(p.threads), args, p.lds, s);
+    return launch_all_resident(reinterpret_cast<const void *>(&rec_fwd_mc_kernel<CELL, KCW, R4, RL>),
+                               p.grid, p.threads, args, p.lds, s);
 }
 
 

@@ -946,8 +946,8 @@ hipError_t launch_bwd_wide2_t(const BwdArgs &m0, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     void *args[] = {&m};
-    return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(&rec_bwd_wide2_kernel<CELL>),
-                                      dim3(grid), dim3(kWideWaves * 64), args, 0, s);
+    return launch_all_resident(reinterpret_cast<const void *>(&rec_bwd_wide2_kernel<CELL>), grid,
+                               kWideWaves * 64, args, 0, s);
 }
 
 template <int CELL>

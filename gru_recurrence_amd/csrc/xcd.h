@@ -44,7 +44,7 @@ __device__ __forceinline__ void xcd_publish(unsigned *xcc) {
 // One whole wave: 1 if every member of `group` (xcd_map numbering) runs on
 // this workgroup's XCD, 0 if not, -1 if a member's entry did not appear
 // within spin_limit polls (the abort word is then raised).  Every member is
-// resident (cooperative launch), so the entries appear.
+// resident (checked on the host before the launch), so the entries appear.
 __device__ __forceinline__ int xcd_members_agree(const unsigned *xcc, unsigned *flag,
                                                  unsigned spin_limit, int group, int K) {
     const int lane = threadIdx.x & 63;

@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_util import dev, host, nerr
+from tests.gpu_util import check, dev, host, nerr
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -71,9 +71,7 @@ def test_lstm_backward_small(Dh, B, bt, final):
                           c.f64("c0"), c.f64("dH"), c.f64("dhT") if final else None,
                           c.f64("dcT") if final else None, NH=d.NH, Dh=d.Dh)
     for k in ("dx", "dW", "dR", "db", "dh0", "dc0"):
-        e = nerr(got[k], ref[k])
-        print("  %-4s nerr=%.3e" % (k, e), flush=True)
-        assert e <= TOL, (k, e)
+        check(k, got[k], ref[k], TOL)
 
 
 @pytest.mark.parametrize("wide", ["1", "0"])
@@ -86,54 +84,56 @@ def test_lstm_backward_bitwise_repeatable(wide):
         assert np.array_equal(a[k], b[k]), k
 
 
-def test_backward_workload_full_size_sampled():
-    """LSTM forward+BPTT, B=16, NH=4, Dh=256, T=1024, Din=1024 at full size.
-    The oracle recomputes 19 whole chains: every batch row of head 1 and
-    every head of batch row 3.  Compared: dh0/dc0 of those chains, db, dW
-    and dR entries of head 1's columns, dx entries of batch row 3."""
+def _head_param_grads(ref, c, n, G, want):
+    """dW and/or dR of head n alone, by the oracle's parameter-gradient sums
+    on that head's slices (the sums over t and b never mix heads)."""
+    d = c.dims
+    GD, sl = G * d.Dh, slice(n * d.Dh, (n + 1) * d.Dh)
+    dG = (ref["dA"] if G == 4 else ref["dGx"])[..., n * GD:(n + 1) * GD]
+    dS = (ref["dA"] if G == 4 else ref["dS"])[..., n * GD:(n + 1) * GD]
+    return oracle.param_grads(c.f64("x"), c.f64("W")[:, n * GD:(n + 1) * GD],
+                              c.f64("h0")[:, sl], ref["h_seq"][..., sl], dG, dS,
+                              NH=1, Dh=d.Dh, G=G, want=want)
+
+
+def _full_size_backward_checks(got, ref, c, G, heads_dW, n_t=64, seed=5):
+    """Every chain's dh0 (and dc0), all of db and dR, dW of the given heads,
+    dx of every batch row and input column at n_t sampled steps."""
+    d = c.dims
+    GD = G * d.Dh
+    for k in ("dh0", "dc0") if G == 4 else ("dh0",):
+        check(k, got[k], ref[k], TOL)
+    dG = ref["dA"] if G == 4 else ref["dGx"]
+    dS = ref["dA"] if G == 4 else ref["dS"]
+    full = oracle.param_grads(c.f64("x"), c.f64("W"), c.f64("h0"), ref["h_seq"], dG, dS,
+                              NH=d.NH, Dh=d.Dh, G=G, want=("db", "dR"))
+    check("db", got["db"], full["db"], TOL)
+    check("dR", got["dR"], full["dR"], TOL)
+    for n in heads_dW:
+        hd = _head_param_grads(ref, c, n, G, ("dW",))
+        check("dW[h%d]" % n, got["dW"][:, n * GD:(n + 1) * GD], hd["dW"], TOL)
+    rng = np.random.default_rng(seed)
+    tt = np.sort(rng.choice(d.T, size=min(n_t, d.T), replace=False))
+    tt[0], tt[-1] = 0, d.T - 1
+    m = (tt[:, None] * d.B + np.arange(d.B)[None, :]).reshape(-1)
+    idx = np.stack([np.repeat(m, d.Din), np.tile(np.arange(d.Din), m.size)], 1)
+    args = (c.f64("x"), c.f64("W"), c.f64("h0"), ref["h_seq"], dG, dS)
+    dx_ref = oracle.param_grad_entries("dx", idx, *args, NH=d.NH, Dh=d.Dh, G=G)
+    check("dx[%dt]" % tt.size, got["dx"][tt].reshape(-1), dx_ref, TOL)
+
+
+def test_backward_workload_full_size():
+    """LSTM forward+BPTT, B=16, NH=4, Dh=256, T=1024, Din=1024 at full size,
+    in the default plan.  The oracle runs BPTT on all 64 chains; compared:
+    dh0 and dc0 of every chain, all of db and dR, dW of two whole heads, dx of
+    every batch row at 64 steps (the first and last among them)."""
     w = synth.WORKLOADS["lstm_fwdbwd_b16_nh4_dh256"]
     c = synth.workload_case(w)
     d = w.dims
     got = gpu_bwd(c)
-    n1, b3 = 1, 3
-    mask = np.zeros((d.B, d.NH), bool)
-    mask[:, n1] = True
-    mask[b3, :] = True
     ref = oracle.lstm_bwd(c.f64("x"), c.f64("W"), c.f64("R"), c.f64("b"), c.f64("h0"),
-                          c.f64("c0"), c.f64("dH"), NH=d.NH, Dh=d.Dh, chain_mask=mask, grads=())
-    H, GD = d.NH * d.Dh, 4 * d.Dh
-    for b, n in [(0, n1), (15, n1), (b3, 0), (b3, 3)]:
-        sl = slice(n * d.Dh, (n + 1) * d.Dh)
-        for k in ("dh0", "dc0"):
-            e = nerr(got[k][b, sl], ref[k][b, sl])
-            print("  chain (b=%d,n=%d) %s nerr=%.3e" % (b, n, k, e), flush=True)
-            assert e <= TOL, (b, n, k, e)
-    rng = np.random.default_rng(5)
-    args = (c.f64("x"), c.f64("W"), c.f64("h0"), ref["h_seq"], ref["dA"], ref["dA"])
-    kw = dict(NH=d.NH, Dh=d.Dh, G=4)
-    cols = n1 * GD + np.arange(GD)
-    db_ref = oracle.param_grad_entries("db", cols[:, None], *args, **kw)
-    e = nerr(got["db"][cols], db_ref)
-    print("  db (head %d) nerr=%.3e" % (n1, e), flush=True)
-    assert e <= TOL
-    kk = rng.integers(0, d.Din, 256)
-    cc = n1 * GD + rng.integers(0, GD, 256)
-    dW_ref = oracle.param_grad_entries("dW", np.stack([kk, cc], 1), *args, **kw)
-    e = nerr(got["dW"][kk, cc], dW_ref)
-    print("  dW entries nerr=%.3e" % e, flush=True)
-    assert e <= TOL
-    ii = rng.integers(0, d.Dh, 256)
-    jj = rng.integers(0, GD, 256)
-    dR_ref = oracle.param_grad_entries("dR", np.stack([np.full(256, n1), ii, jj], 1), *args, **kw)
-    e = nerr(got["dR"][n1, ii, jj], dR_ref)
-    print("  dR entries nerr=%.3e" % e, flush=True)
-    assert e <= TOL
-    tt = rng.integers(0, d.T, 256)
-    kx = rng.integers(0, d.Din, 256)
-    dx_ref = oracle.param_grad_entries("dx", np.stack([tt * d.B + b3, kx], 1), *args, **kw)
-    e = nerr(got["dx"][tt, b3, kx], dx_ref)
-    print("  dx entries (row %d) nerr=%.3e" % (b3, e), flush=True)
-    assert e <= TOL
+                          c.f64("c0"), c.f64("dH"), NH=d.NH, Dh=d.Dh, grads=())
+    _full_size_backward_checks(got, ref, c, 4, heads_dW=(1, 3))
 
 
 def gpu_bwd_gru(c, final=False):
@@ -170,9 +170,7 @@ def test_gru_backward_small(Dh, B, bt, final):
     ref = oracle.gru_bwd(c.f64("x"), c.f64("W"), c.f64("R"), c.f64("b"), c.f64("h0"),
                          c.f64("dH"), c.f64("dhT") if final else None, NH=d.NH, Dh=d.Dh)
     for k in ("dx", "dW", "dR", "db", "dh0"):
-        e = nerr(got[k], ref[k])
-        print("  %-4s nerr=%.3e" % (k, e), flush=True)
-        assert e <= TOL, (k, e)
+        check(k, got[k], ref[k], TOL)
 
 
 @pytest.mark.parametrize("wide", ["1", "0"])
@@ -185,41 +183,18 @@ def test_gru_backward_bitwise_repeatable(wide):
         assert np.array_equal(a[k], b[k]), k
 
 
-def test_gru_backward_small_batch_workload_shape_sampled():
+def test_gru_backward_small_batch_workload_shape_full():
     """GRU BPTT at the shape of the small-batch GRU workload (B=4, NH=12,
-    Dh=64, T=2048, Din=768; dL/dh_t ~ N(0,1) for all t).  The oracle
-    recomputes 4 whole chains (head 5 of every batch row); compared: dh0 of
-    those chains, db and dW / dR entries of head 5's columns, dx entries."""
+    Dh=64, T=2048, Din=768; dL/dh_t ~ N(0,1) for all t).  The oracle runs
+    BPTT on all 48 chains; compared: dh0 of every chain, all of db and dR, dW
+    of two whole heads, dx of every batch row at 64 steps."""
     w = synth.WORKLOADS["gru_mh_b4_nh12_dh64"]
     d = w.dims
     c = synth.make_case("gru", d, "bf16", 9000, h0_var=0.1, backward=True)
     got = gpu_bwd_gru(c)
-    n5 = 5
-    mask = np.zeros((d.B, d.NH), bool)
-    mask[:, n5] = True
     ref = oracle.gru_bwd(c.f64("x"), c.f64("W"), c.f64("R"), c.f64("b"), c.f64("h0"),
-                         c.f64("dH"), NH=d.NH, Dh=d.Dh, chain_mask=mask, grads=())
-    GD = 3 * d.Dh
-    sl = slice(n5 * d.Dh, (n5 + 1) * d.Dh)
-    e = nerr(got["dh0"][:, sl], ref["dh0"][:, sl])
-    print("  dh0 (head %d) nerr=%.3e" % (n5, e), flush=True)
-    assert e <= TOL
-    args = (c.f64("x"), c.f64("W"), c.f64("h0"), ref["h_seq"], ref["dGx"], ref["dS"])
-    kw = dict(NH=d.NH, Dh=d.Dh, G=3)
-    cols = n5 * GD + np.arange(GD)
-    e = nerr(got["db"][cols], oracle.param_grad_entries("db", cols[:, None], *args, **kw))
-    print("  db nerr=%.3e" % e, flush=True)
-    assert e <= TOL
-    rng = np.random.default_rng(7)
-    kk, cc = rng.integers(0, d.Din, 256), n5 * GD + rng.integers(0, GD, 256)
-    e = nerr(got["dW"][kk, cc], oracle.param_grad_entries("dW", np.stack([kk, cc], 1), *args, **kw))
-    print("  dW entries nerr=%.3e" % e, flush=True)
-    assert e <= TOL
-    ii, jj = rng.integers(0, d.Dh, 256), rng.integers(0, GD, 256)
-    e = nerr(got["dR"][n5, ii, jj],
-             oracle.param_grad_entries("dR", np.stack([np.full(256, n5), ii, jj], 1), *args, **kw))
-    print("  dR entries nerr=%.3e" % e, flush=True)
-    assert e <= TOL
+                         c.f64("dH"), NH=d.NH, Dh=d.Dh, grads=())
+    _full_size_backward_checks(got, ref, c, 3, heads_dW=(0, 5))
 
 
 # 8 (head, row) groups of four workgroups in the exchange-based sweep
@@ -265,9 +240,7 @@ def test_backward_xcd_grouped_exchange(cell):
         ref = oracle.gru_bwd(c.f64("x"), c.f64("W"), c.f64("R"), c.f64("b"), c.f64("h0"),
                              c.f64("dH"), c.f64("dhT"), NH=d.NH, Dh=d.Dh)
     for k in got:
-        e = nerr(got[k], ref[k])
-        print("  %-4s nerr=%.3e" % (k, e), flush=True)
-        assert e <= TOL, (k, e)
+        check(k, got[k], ref[k], TOL)
 
 
 def _bwd_with_ws(c, ws, final=True):
@@ -314,9 +287,7 @@ def test_backward_two_cu_split_r(cell):
         ref = oracle.gru_bwd(c.f64("x"), c.f64("W"), c.f64("R"), c.f64("b"), c.f64("h0"),
                              c.f64("dH"), c.f64("dhT"), NH=d.NH, Dh=d.Dh)
     for k in got:
-        e = nerr(got[k], ref[k])
-        print("  %-4s nerr=%.3e" % (k, e), flush=True)
-        assert e <= TOL, (k, e)
+        check(k, got[k], ref[k], TOL)
     os.environ["RNN355_BWD_WIDE2"] = "0"
     one = _bwd_with_ws(c, ws)
     for k in got:

@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_util import dev, host, nerr
+from tests.gpu_util import check, dev, host, nerr
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -56,6 +56,4 @@ def test_searched_plan_parity(cell, B, NH, Dh, dtype, want):
         ref = oracle.gru_fwd(*[c.f64(k) for k in ("x", "W", "R", "b", "h0")], NH=NH, Dh=Dh)
     tol = 1e-5 if dtype == "f32" else 2e-2
     for k in got:
-        e = nerr(got[k], ref[k])
-        print("  %-6s nerr=%.3e" % (k, e), flush=True)
-        assert e <= tol, (k, e)
+        check(k, got[k], ref[k], tol)

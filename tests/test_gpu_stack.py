@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_util import dev, host, nerr
+from tests.gpu_util import check, dev, host, nerr
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -77,9 +77,7 @@ def test_stack_forward(cell, L, NH, Dh, dtype, Din):
     got, ref = run(cs), want(cs)
     tol = 1e-5 if dtype == "f32" else 2e-2
     for k in got:
-        e = nerr(got[k], ref[k])
-        print("  %-6s nerr=%.3e" % (k, e), flush=True)
-        assert e <= tol, (k, e)
+        check(k, got[k], ref[k], tol)
 
 
 def test_one_layer_stack_is_the_forward_bitwise():

@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_util import dev, host, nerr
+from tests.gpu_util import check, dev, host, nerr
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -75,9 +75,7 @@ def test_split_r_forward(cell, T, B, NH, Din):
     assert "split_R" in p
     got, ref = run(c), want(c)
     for key in got:
-        e = nerr(got[key], ref[key])
-        print("  %-6s nerr=%.3e" % (key, e), flush=True)
-        assert e <= TOL_BF16, (key, e)
+        check(key, got[key], ref[key], TOL_BF16)
 
 
 def test_split_r_bitwise_repeatable_resume_and_rec_entry():
