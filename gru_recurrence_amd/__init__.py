@@ -26,7 +26,7 @@ OP_FWD_LSTM, OP_FWD_GRU, OP_BWD_LSTM, OP_BWD_GRU, OP_REC_LSTM, OP_REC_GRU = rang
 
 EXPORTS = ("rnn_status_str", "rnn_workspace_size", "rnn_plan_describe", "rnn_input_proj",
            "rnn_input_proj_t",
-           "rnn_rec_lstm", "rnn_rec_gru", "rnn_fwd_lstm", "rnn_fwd_gru", "rnn_bwd_lstm",
+           "rnn_rec_lstm", "rnn_rec_lstm_noalloc", "rnn_rec_gru", "rnn_fwd_lstm", "rnn_fwd_gru", "rnn_bwd_lstm",
            "rnn_bwd_gru", "rnn_workspace_size_stack", "rnn_fwd_lstm_stack", "rnn_fwd_gru_stack",
            "rnn_workspace_size_chunked", "rnn_fwd_lstm_chunked", "rnn_fwd_gru_chunked",
            "rnn_bwd_lstm_ckpt", "rnn_bwd_gru_ckpt", "rnn_plan_search", "rnn_workspace_status")
@@ -81,6 +81,7 @@ def load(path: Optional[str] = None):
     lib.rnn_input_proj_t.argtypes = [I, I, I, I, P, P, P, P, P]
     lib.rnn_rec_lstm.argtypes = [D, I, P, P, P, P, P, P, P, P, P, S, P]
     lib.rnn_rec_gru.argtypes = [D, I, P, P, P, P, P, P, S, P]
+    lib.rnn_rec_lstm_noalloc.argtypes = [D, I, P, P, P, P, P, P, P, P, P, P]
     lib.rnn_fwd_lstm.argtypes = [D, I, P, P, P, P, P, P, P, P, P, P, P, S, P]
     lib.rnn_fwd_gru.argtypes = [D, I, P, P, P, P, P, P, P, P, S, P]
     lib.rnn_bwd_lstm.argtypes = [D, I] + [P] * 17 + [P, S, P]
@@ -386,6 +387,42 @@ def rec_lstm(gx, R, h0=None, c0=None, *, with_seq=True, ws=None, out=None, strea
                             _ptr(hT, "hT", f32), _ptr(cT, "cT", f32),
                             _ptr(ws, "ws"), ws.numel(), _stream(stream))
     _check(s, "rnn_rec_lstm")
+    return h_seq, c_seq, hT, cT
+
+
+def rec_lstm_noalloc(gx, R, h0=None, c0=None, *, with_seq=True, out=None, status=None,
+                     stream=None):
+    """rec_lstm through rnn_rec_lstm_noalloc: no workspace (the library's
+    own device scratch).  Outputs are allocated here unless given in `out`;
+    `status` (a 4-byte int32 device tensor) receives the device status word."""
+    torch = _torch()
+    T, B, N = gx.shape
+    NH, Dh = R.shape[0], R.shape[1]
+    d = Dims(T, B, 1, NH, Dh)
+    dt = _dtype_code(R)
+    H = NH * Dh
+    f32 = torch.float32
+    dev = gx.device
+    out = out or {}
+    h_seq = out.get("h_seq") if with_seq else None
+    c_seq = out.get("c_seq") if with_seq else None
+    if with_seq and h_seq is None:
+        h_seq = torch.empty((T, B, H), dtype=f32, device=dev)
+    if with_seq and c_seq is None:
+        c_seq = torch.empty((T, B, H), dtype=f32, device=dev)
+    hT = out.get("hT") if out.get("hT") is not None else torch.empty((B, H), dtype=f32, device=dev)
+    cT = out.get("cT") if out.get("cT") is not None else torch.empty((B, H), dtype=f32, device=dev)
+    s = load().rnn_rec_lstm_noalloc(ctypes.byref(d), dt,
+                                    _ptr(gx, "gx", f32, (T, B, NH * 4 * Dh)),
+                                    _ptr(R, "R", None, (NH, Dh, 4 * Dh)),
+                                    _ptr(h0, "h0", f32, (B, H), True),
+                                    _ptr(c0, "c0", f32, (B, H), True),
+                                    _ptr(h_seq, "h_seq", f32, None, True),
+                                    _ptr(c_seq, "c_seq", f32, None, True),
+                                    _ptr(hT, "hT", f32), _ptr(cT, "cT", f32),
+                                    _ptr(status, "status", torch.int32, (1,), True),
+                                    _stream(stream))
+    _check(s, "rnn_rec_lstm_noalloc")
     return h_seq, c_seq, hT, cT
 
 

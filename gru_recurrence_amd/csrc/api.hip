@@ -974,6 +974,45 @@ hipError_t launch_all_resident(const void *fn, int grid, int threads, void **arg
 
 }  // namespace rnn355
 
+// ---- the allocation-free recurrence (rnn_rec_lstm_noalloc)
+//
+// Its scratch (status word, XCD table, exchange slots, R^T of the split-R
+// plan: what rnn_rec_lstm keeps in the caller's workspace) is this
+// file-scope device array; each GPU the library runs on holds its own copy
+// until the process ends.  In host code `scratch` is only a stand-in for the
+// symbol: its device address, per device, comes from hipGetSymbolAddress
+// (scratch_ptr) and is what the kernels receive.
+constexpr size_t kScratchBytes = RNN_REC_NOALLOC_MAX_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+// out == nullptr: clear the status word; otherwise copy it to out.
+__global__ void status_word_kernel(unsigned *word, unsigned *out) {
+    if (threadIdx.x == 0) {
+        if (out) out[0] = word[0];
+        else word[0] = 0u;
+    }
+}
+
+// Device address of `scratch` on the current device, looked up on the first
+// call on that device (with the device current) and kept per device.
+void *scratch_ptr() {
+    static std::mutex mu;
+    static void *ptr[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> lk(mu);
+    if (!ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        ptr[dev] = p;
+    }
+    return ptr[dev];
+}
+
+}  // namespace
+
 extern "C" {
 
 const char *rnn_status_str(rnn_status s) {
@@ -1124,6 +1163,31 @@ rnn_status rnn_rec_lstm(const rnn_dims *d, rnn_dtype dt, const float *gx, const 
     if (!ws || ws_bytes < rnn_workspace_size(RNN_OP_REC_LSTM, d, dt)) return RNN_ERR_WORKSPACE;
     uint16_t *rt = (uint16_t *)((char *)ws + kHeader + xchg_bytes(d));
     return rec_fwd(kLSTM, d, dt, gx, R, h0, c0, h_seq, c_seq, hT, cT, ws, rt, stream);
+}
+
+rnn_status rnn_rec_lstm_noalloc(const rnn_dims *d, rnn_dtype dt, const float *gx, const void *R,
+                                const float *h0, const float *c0, float *h_seq, float *c_seq,
+                                float *hT, float *cT, unsigned *dev_status, hipStream_t stream) {
+    if (!dims_ok(d) || !dtype_ok(dt) || !gx || !R || !hT || !cT) return RNN_ERR_INVALID_ARG;
+    const void *ps[] = {gx, R, h0, c0, h_seq, c_seq, hT, cT, dev_status};
+    for (const void *p : ps)
+        if (!aligned16(p)) return RNN_ERR_INVALID_ARG;
+    if (!rec_supported(kLSTM, d, dt)) return RNN_ERR_UNSUPPORTED;
+    if (rnn_workspace_size(RNN_OP_REC_LSTM, d, dt) > kScratchBytes) return RNN_ERR_WORKSPACE;
+    void *ws = scratch_ptr();
+    if (!ws) return RNN_ERR_HIP;
+    // the array keeps the previous call's contents: the status word starts at
+    // zero for every call (the kernels clear their own exchange slots)
+    hipLaunchKernelGGL(status_word_kernel, dim3(1), dim3(64), 0, stream, (unsigned *)ws,
+                       (unsigned *)nullptr);
+    if (hipGetLastError() != hipSuccess) return RNN_ERR_HIP;
+    uint16_t *rt = (uint16_t *)((char *)ws + kHeader + xchg_bytes(d));
+    const rnn_status st = rec_fwd(kLSTM, d, dt, gx, R, h0, c0, h_seq, c_seq, hT, cT, ws, rt,
+                                  stream);
+    if (st != RNN_OK || !dev_status) return st;
+    hipLaunchKernelGGL(status_word_kernel, dim3(1), dim3(64), 0, stream, (unsigned *)ws,
+                       dev_status);
+    return hipGetLastError() == hipSuccess ? RNN_OK : RNN_ERR_HIP;
 }
 
 rnn_status rnn_rec_gru(const rnn_dims *d, rnn_dtype dt, const float *gx, const void *R,

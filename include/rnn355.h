@@ -145,6 +145,28 @@ rnn_status rnn_rec_lstm(const rnn_dims *d, rnn_dtype dt, const float *gx,
                         float *h_seq, float *c_seq, float *hT, float *cT,
                         void *ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the LSTM
+ * recurrence of rnn_rec_lstm, same arguments, same kernels and the same
+ * result bits, but with no workspace.  Its scratch (status word, exchange
+ * slots of the multi-CU plan, R^T of the split-R plan) is a device array
+ * inside the library of RNN_REC_NOALLOC_MAX_BYTES per GPU, held until the
+ * process ends; shapes whose rnn_workspace_size(RNN_OP_REC_LSTM, ...) is
+ * larger are rejected with RNN_ERR_WORKSPACE before anything is enqueued.
+ * The call makes no hipMalloc / hipFree and no allocating library call.
+ * dev_status (device memory, 4 bytes, 16-byte aligned, may be NULL)
+ * receives, in stream order, 0 or 1 if a step wait of this call gave up
+ * (what rnn_workspace_status reports as RNN_ERR_BARRIER_TIMEOUT).
+ * All calls on one GPU share its array: calls that overlap in time on one
+ * GPU (other streams, other host threads) race and their results are void.
+ */
+#define RNN_REC_NOALLOC_MAX_BYTES ((size_t)8 << 20)
+rnn_status rnn_rec_lstm_noalloc(const rnn_dims *d, rnn_dtype dt, const float *gx,
+                                const void *R, const float *h0, const float *c0,
+                                float *h_seq, float *c_seq, float *hT, float *cT,
+                                unsigned *dev_status, hipStream_t stream);
+
 /* The GRU recurrence alone, given gx (bias inside gx).  h_seq may be NULL. */
 rnn_status rnn_rec_gru(const rnn_dims *d, rnn_dtype dt, const float *gx,
                        const void *R, const float *h0,

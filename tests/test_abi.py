@@ -100,6 +100,18 @@ def test_invalid_arguments_are_rejected_before_launch():
     assert lib.rnn_rec_gru(ctypes.byref(d), g.RNN_BF16, None, ok[1], None, None, ok[2],
                            _p(FAKE), 1 << 20, None) == g.RNN_ERR_INVALID_ARG
     assert lib.rnn_workspace_status(None, 0, None) == g.RNN_ERR_INVALID_ARG
+    # the allocation-free recurrence: same argument checks, and shapes whose
+    # scratch would pass the library's fixed array are rejected up front
+    dn = g.Dims(8, 2, 1, 1, 32)
+    assert lib.rnn_rec_lstm_noalloc(ctypes.byref(dn), g.RNN_BF16, None, ok[1], None, None,
+                                    None, None, ok[2], ok[3], None, None) == g.RNN_ERR_INVALID_ARG
+    assert lib.rnn_rec_lstm_noalloc(ctypes.byref(dn), g.RNN_BF16, ok[0], ok[1], None, None,
+                                    None, None, ok[2], ok[3], _p(FAKE + 4),
+                                    None) == g.RNN_ERR_INVALID_ARG
+    big = g.Dims(8, 2, 1, 64, 256)    # R^T of 64 heads of Dh 256: 32 MiB of scratch
+    assert g.workspace_size(g.OP_REC_LSTM, big, g.RNN_BF16) > (8 << 20)
+    assert lib.rnn_rec_lstm_noalloc(ctypes.byref(big), g.RNN_BF16, ok[0], ok[1], None, None,
+                                    None, None, ok[2], ok[3], None, None) == g.RNN_ERR_WORKSPACE
 
 
 def test_backward_rejects_unsupported_and_invalid_before_launch():
