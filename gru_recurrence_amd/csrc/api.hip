@@ -111,6 +111,14 @@ BwdLayout bwd_layout(const rnn_dims *d, int G) {
     return L;
 }
 
+// out == nullptr: clear the status word; otherwise copy it to out.
+__global__ void status_word_kernel(unsigned *word, unsigned *out) {
+    if (threadIdx.x == 0) {
+        if (out) out[0] = word[0];
+        else word[0] = 0u;
+    }
+}
+
 // Compute-unit count of the current device, cached per device.
 int device_cus() {
     static std::mutex mu;
@@ -986,14 +994,6 @@ constexpr size_t kScratchBytes = RNN_REC_NOALLOC_MAX_BYTES;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
-
-// out == nullptr: clear the status word; otherwise copy it to out.
-__global__ void status_word_kernel(unsigned *word, unsigned *out) {
-    if (threadIdx.x == 0) {
-        if (out) out[0] = word[0];
-        else word[0] = 0u;
-    }
-}
 
 // Device address of `scratch` on the current device, looked up on the first
 // call on that device (with the device current) and kept per device.

@@ -21,11 +21,12 @@ struct CellTraits<kLSTM> { static constexpr int G = 4; };
 template <>
 struct CellTraits<kGRU> { static constexpr int G = 3; };
 
-// float -> bf16 bit pattern, round to nearest even (inputs are finite).
+// float -> bf16 bit pattern, round to nearest even (inputs are finite):
+// one v_cvt_pk_bf16_f32 on gfx950.  For every finite float it gives the bits
+// of the integer rule (u + 0x7FFF + ((u >> 16) & 1)) >> 16, checked on the
+// device over all 2^32 patterns.
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {

@@ -48,32 +48,51 @@ __device__ __forceinline__ float gate_rows_of(const f32x4 (&acc)[CellTraits<CELL
     }
 }
 
-// Cell update from the gate-row layout above, v = this lane's recurrent
-// sum and gx = the Gx of the lane's gate row.  One exp + rcp pass activates
-// every gate at once (tanh(x) = 2*sigmoid(2x) - 1 on the LSTM's z row), and
-// swaps hand every lane all the gates back.  The LSTM result is then valid
-// in every row (row 0 writes it), the GRU result in row 3 (row 3 writes it).
+// The exponent scale of the activation on gate row `row` of the row layout
+// above: sigmoid(x) = 1/(1 + 2^(x * -log2 e)); the LSTM's z row takes
+// tanh(x) = 2 sigmoid(2x) - 1, scale -2 log2 e.
 template <int CELL>
+__device__ __forceinline__ float gate_row_scale(int row) {
+    return (CELL == kLSTM && row == 2) ? -2.0f * kLog2e : -kLog2e;
+}
+
+// Cell update from the gate-row layout above, v = this lane's recurrent
+// sum and gx = the Gx of the lane's gate row (GXK: the LSTM's exponent is
+// fma(v, k, gx k), whose product gx k does not wait for the MFMAs, so one
+// fma follows them instead of an add and a multiply).  One
+// exp + rcp pass activates every gate at once, and swaps bring a unit's
+// gates together.  LSTM: h = o tanh(c) = 2 o sigmoid(2c) - o (one exp and
+// one rcp after c).  The LSTM result is valid in row 0 (row 0 writes it),
+// the GRU result in row 3 (row 3 writes it).
+template <int CELL, bool GXK = false>
 __device__ __forceinline__ void gate_rows_update(float v, float gx, float &st, float &hl,
                                                  float &h, float &c) {
     const int row = (threadIdx.x & 63) >> 4;
     const bool tanh_row = CELL == kLSTM && row == 2;
-    const float act_k = tanh_row ? -2.0f * kLog2e : -kLog2e;
-    const float x = v + gx;
-    const float sg = rcp_fast(1.0f + __builtin_amdgcn_exp2f(x * act_k));
+    const float act_k = gate_row_scale<CELL>(row);
+    const float arg = (GXK && CELL == kLSTM) ? fmaf(v, act_k, gx * act_k) : (v + gx) * act_k;
+    const float sg = rcp_fast(1.0f + __builtin_amdgcn_exp2f(arg));
     if constexpr (CELL == kLSTM) {
+        // rows i, f, z, o of `act`; row 0 gathers f and z with one swap each
+        // and o (needed last) with a second swap; only row 0's c and h are
+        // valid (the lanes that write them)
         const float act = tanh_row ? fmaf(sg, 2.0f, -1.0f) : sg;
-        const RowPair A = swap16(act, act);  // [i,i,z,z] [f,f,o,o]
-        const RowPair I = swap32(A.a, A.a);  // [i..] [z..]
-        const RowPair F = swap32(A.b, A.b);  // [f..] [o..]
-        const float cn = fmaf(F.a, st, I.a * I.b);
+        const float f = swap16(act, act).b;              // rows [f, f, o, o]
+        const RowPair Z = swap32(act, act);              // [i, f, i, f] [z, o, z, o]
+        const float o = swap16(Z.b, Z.b).b;              // rows [o, o, o, o]
+        const float o2 = o + o;
+        const float cn = fmaf(f, st, act * Z.b);
         st = cn;
         c = cn;
-        h = F.b * tanh_abs(cn);
+        const float s2 = rcp_fast(1.0f + __builtin_amdgcn_exp2f(cn * (-2.0f * kLog2e)));
+        h = fmaf(o2, s2, -o);
         hl = h;
     } else {
+        // tanh(x) = 2 sigmoid(2x) - 1 on the candidate row
         const RowPair W = swap32(sg, sg);                 // rows r, u, r, u
-        const float nn = tanh_abs(fmaf(W.a, v, gx));      // row 2: tanh(Gx_n + r S_n)
+        const float xn = fmaf(W.a, v, gx);                // row 2: Gx_n + r S_n
+        const float nn = fmaf(2.0f, rcp_fast(1.0f + __builtin_amdgcn_exp2f(xn * (-2.0f * kLog2e))),
+                              -1.0f);
         const float nn3 = swap16(nn, nn).a;               // row 3 <- row 2
         const float hn = fmaf(W.a, st - nn3, nn3);        // row 3: (1-u) nn + u h
         st = hn;
@@ -88,13 +107,14 @@ __device__ __forceinline__ void gate_rows_update(float v, float gx, float &st, f
 //   st[r]:    cell state c (LSTM) or h (GRU), updated in place.
 //   hl[r]:    last h (LSTM only; GRU keeps h in st).
 //   h[r], c[r]: this step's outputs.
-template <int CELL, int R4, int GL>
+template <int CELL, int R4, int GL, bool GXK = false>
 __device__ __forceinline__ void gate_update(const f32x4 (&acc)[CellTraits<CELL>::G],
                                             const float (&gx)[R4][GL], float (&st)[R4],
                                             float (&hl)[R4], float (&h)[R4], float (&c)[R4]) {
     constexpr int G = CellTraits<CELL>::G;
     if constexpr (R4 == 1) {
-        gate_rows_update<CELL>(gate_rows_of<CELL>(acc), gx[0][0], st[0], hl[0], h[0], c[0]);
+        gate_rows_update<CELL, GXK>(gate_rows_of<CELL>(acc), gx[0][0], st[0], hl[0], h[0],
+                                    c[0]);
     } else {
 #pragma unroll
         for (int r = 0; r < R4; ++r) {

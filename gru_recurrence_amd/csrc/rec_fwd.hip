@@ -125,6 +125,7 @@ __device__ __forceinline__ void rec_fwd_mfma_body(const RecArgs &a, const int bl
     static_assert(DH % 32 == 0, "Dh must be a multiple of 32");
     static_assert(PD % 2 == 0, "groups must keep the h double-buffer parity");
     static_assert(3 * PD < 64, "a group's stores must fit the vmcnt field");
+    constexpr bool GXK = ROWS1 && CELL == kLSTM;  // exponent as one fma (gate_rows_update)
 
     __shared__ __attribute__((aligned(16))) uint16_t hbuf[2][16 * HLD];
 
@@ -354,7 +355,7 @@ __device__ __forceinline__ void rec_fwd_mfma_body(const RecArgs &a, const int bl
                 }
             }
             float h[R4], c[R4];
-            gate_update<CELL, R4>(acc, use[s], st, hl, h, c);
+            gate_update<CELL, R4, GL, GXK>(acc, use[s], st, hl, h, c);
 #pragma unroll
             for (int r = 0; r < R4; ++r) {
                 oh[s][r] = h[r];
@@ -633,12 +634,13 @@ hipError_t launch_fused_t(const RecPlan &p, const RecArgs &a, const GemmArgs &g,
     static std::once_flag once;
     static hipError_t attr = hipSuccess;
     std::call_once(once, [] {
-        attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&fwd_fused_kernel<CELL, 128, R4, PD>),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)dma::LDS_BYTES);
+        attr = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(&fwd_fused_kernel<CELL, 128, R4, PD>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)dma::LDS_BYTES);
     });
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((fwd_fused_kernel<CELL, 128, R4, PD>), dim3(n_gemm + p.grid), dim3(512),
-                       dma::LDS_BYTES, s, a, g, n_gemm);
+    hipLaunchKernelGGL((fwd_fused_kernel<CELL, 128, R4, PD>), dim3(n_gemm + p.grid),
+                       dim3(512), dma::LDS_BYTES, s, a, g, n_gemm);
     return hipGetLastError();
 }
 

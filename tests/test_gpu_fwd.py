@@ -293,3 +293,4 @@ def test_pipelined_forward_reads_fresh_projection_after_reuse():
     serial = _with_env("RNN355_PIPELINE", "0", lambda: g.lstm_fwd(*ins[1]))
     torch.cuda.synchronize()
     assert torch.equal(h2, serial[0]) and torch.equal(cT2, serial[3])
+
