@@ -111,6 +111,28 @@ BwdLayout bwd_layout(const rnn_dims *d, int G) {
     return L;
 }
 
+// Float32 backward workspace after the header: pre-activations A (LSTM:
+// with the recurrent part; GRU: x W + b) and the GRU's recurrent sums S,
+// the gate-input gradients dA and the GRU's recurrent-sum gradients dS, and
+// h_{t-1}, all float32.
+struct BwdF32Layout {
+    size_t A, S, dA, dS, hprev, total;
+};
+BwdF32Layout bwd_f32_layout(const rnn_dims *d, int G) {
+    BwdF32Layout L{};
+    const bool gru = G == 3;
+    const size_t TB = (size_t)d->T * d->B, N = (size_t)d->NH * G * d->Dh;
+    const size_t H = (size_t)d->NH * d->Dh;
+    size_t off = 0;
+    L.A = off;     off += align_up(sizeof(float) * TB * N);
+    L.S = off;     off += gru ? align_up(sizeof(float) * TB * N) : 0;
+    L.dA = off;    off += align_up(sizeof(float) * TB * N);
+    L.dS = off;    off += gru ? align_up(sizeof(float) * TB * N) : 0;
+    L.hprev = off; off += align_up(sizeof(float) * TB * H);
+    L.total = off;
+    return L;
+}
+
 // out == nullptr: clear the status word; otherwise copy it to out.
 __global__ void status_word_kernel(unsigned *word, unsigned *out) {
     if (threadIdx.x == 0) {
@@ -569,12 +591,106 @@ rnn_status forward_stack(int cell, const rnn_dims *d, int L, rnn_dtype dt, const
 // 3. db, dW = x^T dA, dx = dA W^T, dR = h_{t-1}^T dS (dS = dA for the LSTM).
 // accumulate: add dW, dR and db to what they hold (a later segment of a
 // checkpointed backward); clear_status: zero the status word first.
+// Float32 BPTT: every step in float32 (rec_bwd_f32.hip for the sweep, the
+// float32 contraction for the recompute and the parameter gradients).
+rnn_status backward_f32(int cell, const rnn_dims *d, const float *x, const float *W,
+                        const float *R, const float *b, const float *h0, const float *c0,
+                        const float *h_seq, const float *c_seq, const float *dh_seq,
+                        const float *dhT, const float *dcT, float *dx, float *dW, float *dR,
+                        float *db, float *dh0, float *dc0, void *ws, size_t ws_bytes,
+                        hipStream_t s, bool accumulate, bool clear_status) {
+    const bool lstm = cell == kLSTM;
+    const int G = lstm ? 4 : 3, Dh = d->Dh, NH = d->NH, T = d->T, B = d->B, Din = d->Din;
+    const int GD = G * Dh, N = NH * GD, H = NH * Dh;
+    const long M = (long)T * B;
+    const BwdF32Plan p = plan_bwd_f32(cell, B, Dh);
+    if (!p.ok) return RNN_ERR_UNSUPPORTED;
+    const rnn_op op = lstm ? RNN_OP_BWD_LSTM : RNN_OP_BWD_GRU;
+    if (!ws || ws_bytes < rnn_workspace_size(op, d, RNN_F32)) return RNN_ERR_WORKSPACE;
+    char *base = (char *)ws + kHeader;
+    const BwdF32Layout L = bwd_f32_layout(d, G);
+    float *A = (float *)(base + L.A);
+    float *S = lstm ? A : (float *)(base + L.S);
+    float *dA = (float *)(base + L.dA);
+    float *dS = lstm ? dA : (float *)(base + L.dS);
+    float *hprev = (float *)(base + L.hprev);
+    auto ok = [](hipError_t e) { return e == hipSuccess; };
+    if (clear_status) {
+        hipLaunchKernelGGL(status_word_kernel, dim3(1), dim3(64), 0, s, (unsigned *)ws,
+                           (unsigned *)nullptr);
+        if (!ok(hipGetLastError())) return RNN_ERR_HIP;
+    }
+    // 1. h_{t-1}; A = x W + b, then + h_{t-1} R per head (LSTM) or S = h_{t-1} R (GRU)
+    if (!ok(launch_hprev_f32(h0, h_seq, hprev, (long)B * H, M * H, s))) return RNN_ERR_HIP;
+    {
+        GemmF32Args g{};
+        g.M = (int)M; g.N = N; g.K = Din;
+        g.A = x; g.sam = Din; g.sak = 1;
+        g.B = W; g.sbk = N; g.sbn = 1;
+        g.bias = b; g.C = A; g.ldc = N;
+        if (!ok(launch_gemm_f32(g, 1, s))) return RNN_ERR_HIP;
+    }
+    {
+        GemmF32Args g{};
+        g.M = (int)M; g.N = GD; g.K = Dh;
+        g.A = hprev; g.sam = H; g.sak = 1; g.strideA = Dh;
+        g.B = R; g.sbk = GD; g.sbn = 1; g.strideB = (long)Dh * GD;
+        g.C = S; g.ldc = N; g.strideC = GD;
+        g.accumulate = lstm ? 1 : 0;
+        if (!ok(launch_gemm_f32(g, NH, s))) return RNN_ERR_HIP;
+    }
+    // 2. the reverse-time sweep
+    {
+        BwdF32Args a{};
+        a.T = T; a.B = B; a.NH = NH; a.Dh = Dh; a.BT = p.BT;
+        a.A = A; a.S = lstm ? nullptr : S;
+        a.c_seq = c_seq; a.c0 = c0; a.hprev = hprev;
+        a.dh_seq = dh_seq; a.dhT = dhT; a.dcT = dcT;
+        a.R = R; a.dA = dA; a.dS = lstm ? nullptr : dS;
+        a.dh0 = dh0; a.dc0 = dc0;
+        if (!ok(launch_rec_bwd_f32(cell, p, a, s))) return RNN_ERR_HIP;
+    }
+    // 3. db = sum dA; dW = x^T dA; dx = dA W^T; dR_n = h_{t-1,n}^T dS_n
+    if (!ok(launch_colsum_f32(dA, M, N, db, accumulate, s))) return RNN_ERR_HIP;
+    {
+        GemmF32Args g{};
+        g.M = Din; g.N = N; g.K = (int)M;
+        g.A = x; g.sam = 1; g.sak = Din;
+        g.B = dA; g.sbk = N; g.sbn = 1;
+        g.C = dW; g.ldc = N;
+        g.accumulate = accumulate ? 1 : 0;
+        if (!ok(launch_gemm_f32(g, 1, s))) return RNN_ERR_HIP;
+    }
+    {
+        GemmF32Args g{};
+        g.M = (int)M; g.N = Din; g.K = N;
+        g.A = dA; g.sam = N; g.sak = 1;
+        g.B = W; g.sbk = 1; g.sbn = N;
+        g.C = dx; g.ldc = Din;
+        if (!ok(launch_gemm_f32(g, 1, s))) return RNN_ERR_HIP;
+    }
+    {
+        GemmF32Args g{};
+        g.M = Dh; g.N = GD; g.K = (int)M;
+        g.A = hprev; g.sam = 1; g.sak = H; g.strideA = Dh;
+        g.B = dS; g.sbk = N; g.sbn = 1; g.strideB = GD;
+        g.C = dR; g.ldc = GD; g.strideC = (long)Dh * GD;
+        g.accumulate = accumulate ? 1 : 0;
+        if (!ok(launch_gemm_f32(g, NH, s))) return RNN_ERR_HIP;
+    }
+    return RNN_OK;
+}
+
 rnn_status backward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, const void *W,
                     const void *R, const float *b, const float *h0, const float *c0,
                     const float *h_seq, const float *c_seq, const float *dh_seq,
                     const float *dhT, const float *dcT, float *dx, float *dW, float *dR,
                     float *db, float *dh0, float *dc0, void *ws, size_t ws_bytes,
                     hipStream_t stream, bool accumulate = false, bool clear_status = true) {
+    if (dt == RNN_F32)
+        return backward_f32(cell, d, (const float *)x, (const float *)W, (const float *)R, b, h0,
+                            c0, h_seq, c_seq, dh_seq, dhT, dcT, dx, dW, dR, db, dh0, dc0, ws,
+                            ws_bytes, stream, accumulate, clear_status);
     if (dt != RNN_BF16) return RNN_ERR_UNSUPPORTED;
     const bool lstm = cell == kLSTM;
     const int G = lstm ? 4 : 3, Dh = d->Dh, NH = d->NH, T = d->T, B = d->B, Din = d->Din;
@@ -916,7 +1032,8 @@ rnn_status backward_ckpt(int cell, const rnn_dims *d, rnn_dtype dt, int chunk, c
         const bool later = j == nseg - 1;  // the last segment, run first
         const float *hin = j == 0 ? h0 : h_ck + (j - 1) * BH;
         const float *cin = !lstm ? nullptr : j == 0 ? c0 : c_ck + (j - 1) * BH;
-        const void *xj = (const char *)x + (size_t)t0 * B * Din * sizeof(uint16_t);
+        const size_t esz = dt == RNN_BF16 ? sizeof(uint16_t) : sizeof(float);
+        const void *xj = (const char *)x + (size_t)t0 * B * Din * esz;
         rnn_status st = forward(cell, &dj, dt, xj, W, R, b, hin, cin, hseg, cseg, scr_h,
                                 lstm ? scr_c : nullptr, ws, s, later);
         if (st != RNN_OK) return st;
@@ -1040,7 +1157,7 @@ size_t rnn_workspace_size(rnn_op op, const rnn_dims *d, rnn_dtype dt) {
             return kHeader + xchg_bytes(d) + rt_fwd_bytes(d, dt, G);
         case RNN_OP_BWD_LSTM:
         case RNN_OP_BWD_GRU:
-            return kHeader + bwd_layout(d, G).total;
+            return kHeader + (dt == RNN_F32 ? bwd_f32_layout(d, G).total : bwd_layout(d, G).total);
         default:
             return 0;
     }
@@ -1341,8 +1458,9 @@ static rnn_status ckpt_args_ok(int cell, const rnn_dims *d, rnn_dtype dt, int ch
         if (!aligned16(all[i])) return RNN_ERR_INVALID_ARG;
     if (chunk < d->T && (!h_ckpt || (cell == kLSTM && !c_ckpt))) return RNN_ERR_INVALID_ARG;
     const int G = gates_of_cell(cell);
-    if (dt != RNN_BF16 || !gemm_shape_ok(d->Din, d->NH * G * d->Dh, dt) || d->Dh % 16 != 0 ||
-        !rec_supported(cell, d, dt))
+    const bool bwd_ok = dt == RNN_F32 ? plan_bwd_f32(cell, d->B, d->Dh).ok != 0
+                                      : d->Dh % 16 == 0;
+    if (!bwd_ok || !gemm_shape_ok(d->Din, d->NH * G * d->Dh, dt) || !rec_supported(cell, d, dt))
         return RNN_ERR_UNSUPPORTED;
     const rnn_op op = cell == kLSTM ? RNN_OP_BWD_LSTM : RNN_OP_BWD_GRU;
     if (!ws || ws_bytes < rnn_workspace_size_chunked(op, d, chunk, dt)) return RNN_ERR_WORKSPACE;

@@ -291,6 +291,36 @@ struct BwdArgs {
     int xcd_map;    // through this table of workgroup XCDs ([grid] words)
 };
 
+// Float32 backward (rec_bwd_f32.hip): float32 operands, pre-activations,
+// gate gradients and carries throughout.
+struct BwdF32Args {
+    int T, B, NH, Dh, BT;
+    const float *A;       // LSTM: x W + b + h_{t-1} R; GRU: x W + b   [T][B][N]
+    const float *S;       // GRU: h_{t-1} R                          [T][B][N]
+    const float *c_seq;   // LSTM [T][B][H]
+    const float *c0;      // LSTM [B][H] or null
+    const float *hprev;   // GRU: h_{t-1} [T][B][H]
+    const float *dh_seq;  // [T][B][H]
+    const float *dhT, *dcT;
+    const float *R;       // [NH][Dh][G Dh]
+    float *dA;            // gradients of the gate inputs (GRU: of Gx)  [T][B][N]
+    float *dS;            // GRU: gradients of the recurrent sums        [T][B][N]
+    float *dh0, *dc0;
+};
+struct BwdF32Plan {
+    int ok, BT, nbt;
+    size_t lds;
+};
+constexpr size_t kBwdF32MaxLds = 160u * 1024u;
+// Rows per workgroup such that the head's R (float32) and the tile's
+// gradients fit the LDS; ok == 0 if R alone does not.  Pure host function.
+BwdF32Plan plan_bwd_f32(int cell, int B, int Dh);
+hipError_t launch_rec_bwd_f32(int cell, const BwdF32Plan &p, const BwdF32Args &a, hipStream_t s);
+hipError_t launch_hprev_f32(const float *h0, const float *h_seq, float *hprev, long BH, long MH,
+                            hipStream_t s);
+hipError_t launch_colsum_f32(const float *X, long M, int N, float *out, bool accumulate,
+                             hipStream_t s);
+
 BwdPlan plan_bwd(int cell, int B, int NH, int Dh, int num_cu, int bt_override, int k_override);
 hipError_t launch_rec_bwd(int cell, const BwdPlan &p, const BwdArgs &m, hipStream_t s);
 // Reverse sweep of the backward for Dh = 256 on the same layout (one

@@ -308,7 +308,7 @@ rnn_status rnn_fwd_gru_stack(const rnn_dims *d, int L, rnn_dtype dt, const void 
  * over the segment with the gradients the later segment passes back.  dx,
  * dh0 and dc0 are the same bits as rnn_bwd_lstm; dW, dR and db are summed
  * segment by segment (float32 rounding differs).  h_ckpt and c_ckpt are
- * required when chunk < T.  bf16 only, like rnn_bwd_lstm.
+ * required when chunk < T.  dtype support as rnn_bwd_lstm.
  */
 size_t rnn_workspace_size_chunked(rnn_op op /* RNN_OP_FWD_* or RNN_OP_BWD_* */,
                                   const rnn_dims *d, int chunk, rnn_dtype dt);
@@ -348,6 +348,11 @@ rnn_status rnn_bwd_gru_ckpt(const rnn_dims *d, rnn_dtype dt, int chunk, const vo
  * card, abstract: the LSTM trained through its sequential recurrence; the
  * backward is the reverse-time recurrence of the same cell, with the same
  * block-diagonal R, held resident as R^T.)
+ * bf16 calls: Dh % 16 == 0; the gate gradients are rounded to bf16 only as
+ * operands of the dx, dW, dR contractions.  f32 calls: every intermediate
+ * stays float32 (pre-activations, gate gradients, carries, contractions);
+ * the head's R block in float32 must fit one CU's LDS (Dh <= 96 for the
+ * LSTM, else RNN_ERR_UNSUPPORTED), and the workspace is sized per dtype.
  */
 rnn_status rnn_bwd_lstm(const rnn_dims *d, rnn_dtype dt,
                         const void *x, const void *W, const void *R,
@@ -371,8 +376,9 @@ rnn_status rnn_bwd_lstm(const rnn_dims *d, rnn_dtype dt,
  *   dA_r = dA_n S_n r(1-r),
  *   dGx = (dA_r, dA_z, dA_n) -> dW, dx, db;  dS = (dA_r, dA_z, dA_n r) -> dR,
  *   carry = dh u + dS R^T (block-diagonal R).
- * bf16 only (f32 returns RNN_ERR_UNSUPPORTED); Dh % 16 == 0 and 3*Dh % 32
- * == 0.  Same workspace and stream rules as rnn_bwd_lstm.
+ * bf16 calls: Dh % 16 == 0 and 3*Dh % 32 == 0; f32 calls as for
+ * rnn_bwd_lstm (the float32 R block must fit one CU's LDS).  Same workspace
+ * and stream rules as rnn_bwd_lstm.
  */
 rnn_status rnn_bwd_gru(const rnn_dims *d, rnn_dtype dt,
                        const void *x, const void *W, const void *R,

@@ -118,9 +118,14 @@ def test_backward_rejects_unsupported_and_invalid_before_launch():
     lib = g.load()
     d = g.Dims(8, 2, 32, 2, 64)
     ptrs = [_p(FAKE + 256 * i) for i in range(17)]
-    # f32 backward has no kernel in this build
-    assert lib.rnn_bwd_lstm(ctypes.byref(d), g.RNN_F32, *ptrs, _p(FAKE), 1 << 30,
+    # f32 backward: a head whose float32 R block does not fit the sweep's LDS
+    # has no kernel; a supported one checks its (float32) workspace
+    dbig = g.Dims(8, 2, 32, 2, 256)
+    assert lib.rnn_bwd_lstm(ctypes.byref(dbig), g.RNN_F32, *ptrs, _p(FAKE), 1 << 30,
                             None) == g.RNN_ERR_UNSUPPORTED
+    assert lib.rnn_bwd_lstm(ctypes.byref(d), g.RNN_F32, *ptrs, _p(FAKE), 64,
+                            None) == g.RNN_ERR_WORKSPACE
+    assert g.workspace_size(g.OP_BWD_LSTM, d, g.RNN_F32) > 8 * 2 * (2 * 4 * 64) * 4 * 2
     # a required gradient output missing
     bad = list(ptrs)
     bad[11] = None  # dx
@@ -133,8 +138,10 @@ def test_backward_rejects_unsupported_and_invalid_before_launch():
     assert need > 8 * 2 * (2 * 4 * 64) * 4  # holds at least the recomputed pre-activations
     # GRU: 13 pointers (no c0, c_seq, dcT, dc0)
     gp = [_p(FAKE + 256 * i) for i in range(13)]
-    assert lib.rnn_bwd_gru(ctypes.byref(d), g.RNN_F32, *gp, _p(FAKE), 1 << 30,
+    assert lib.rnn_bwd_gru(ctypes.byref(dbig), g.RNN_F32, *gp, _p(FAKE), 1 << 30,
                            None) == g.RNN_ERR_UNSUPPORTED
+    assert lib.rnn_bwd_gru(ctypes.byref(d), g.RNN_F32, *gp, _p(FAKE), 64,
+                           None) == g.RNN_ERR_WORKSPACE
     bad = list(gp)
     bad[12] = None  # dh0
     assert lib.rnn_bwd_gru(ctypes.byref(d), g.RNN_BF16, *bad, _p(FAKE), 1 << 30,

@@ -314,3 +314,81 @@ def test_backward_two_cu_timeout_is_reported():
     ref = oracle.lstm_bwd(c.f64("x"), c.f64("W"), c.f64("R"), c.f64("b"), c.f64("h0"),
                           c.f64("c0"), c.f64("dH"), c.f64("dhT"), c.f64("dcT"), NH=d.NH, Dh=d.Dh)
     assert nerr(got["dh0"], ref["dh0"]) <= TOL
+
+
+TOL_F32 = 1e-5
+
+
+def _bwd_any(c, final):
+    x, W, R, b = dev(c, "x"), dev(c, "W"), dev(c, "R"), dev(c, "b")
+    h0 = dev(c, "h0")
+    if c.cell == "lstm":
+        c0 = dev(c, "c0")
+        h_seq, c_seq, _, _ = g.lstm_fwd(x, W, R, b, h0, c0)
+        grads = g.lstm_bwd(x, W, R, b, h0, c0, h_seq, c_seq, dev(c, "dH"),
+                           dev(c, "dhT") if final else None, dev(c, "dcT") if final else None)
+    else:
+        h_seq, _ = g.gru_fwd(x, W, R, b, h0)
+        grads = g.gru_bwd(x, W, R, b, h0, h_seq, dev(c, "dH"), dev(c, "dhT") if final else None)
+    torch.cuda.synchronize()
+    return {k: host(v) for k, v in grads.items()}
+
+
+def _bwd_oracle(c, final):
+    d = c.dims
+    if c.cell == "lstm":
+        return oracle.lstm_bwd(c.f64("x"), c.f64("W"), c.f64("R"), c.f64("b"), c.f64("h0"),
+                               c.f64("c0"), c.f64("dH"), c.f64("dhT") if final else None,
+                               c.f64("dcT") if final else None, NH=d.NH, Dh=d.Dh)
+    return oracle.gru_bwd(c.f64("x"), c.f64("W"), c.f64("R"), c.f64("b"), c.f64("h0"),
+                          c.f64("dH"), c.f64("dhT") if final else None, NH=d.NH, Dh=d.Dh)
+
+
+@pytest.mark.parametrize("cell,T,B,NH,Dh,Din,final", [
+    ("lstm", 64, 2, 1, 32, 32, False),   # the shape of the float32 tiny LSTM workload
+    ("lstm", 19, 3, 2, 24, 20, True),    # several heads, ragged sizes, final-state gradients
+    ("lstm", 9, 11, 3, 48, 16, True),    # three heads, two row tiles of the sweep
+    ("gru", 64, 2, 1, 32, 32, False),
+    ("gru", 23, 5, 2, 40, 12, True),
+])
+def test_backward_f32(cell, T, B, NH, Dh, Din, final):
+    """float32 BPTT (every intermediate float32) against the oracle at the
+    float32 bar, normwise 1e-5 on every gradient."""
+    d = synth.Dims(T=T, B=B, Din=Din, NH=NH, Dh=Dh)
+    bias = "forget+1" if cell == "lstm" else synth.normal(9800 + Dh, NH * 3 * Dh, 0.25)
+    c = synth.make_case(cell, d, "f32", 9900 + T + Dh, bias=bias, h0_var=0.2,
+                        c0_var=0.2 if cell == "lstm" else 0.0, backward=True, final_grads=final)
+    got = _bwd_any(c, final)
+    ref = _bwd_oracle(c, final)
+    keys = ("dx", "dW", "dR", "db", "dh0", "dc0") if cell == "lstm" else ("dx", "dW", "dR", "db", "dh0")
+    for k in keys:
+        check(k, got[k], ref[k], TOL_F32)
+
+
+@pytest.mark.parametrize("cell", ["lstm", "gru"])
+def test_backward_f32_from_checkpoints_matches_one_piece(cell):
+    """float32 BPTT from chunk checkpoints (segments recomputed, then their
+    BPTT with the carries of the later segment): dx and the initial-state
+    gradients are the bits of the one-piece call; dW, dR, db are sums over
+    segments (float32 order differs)."""
+    d = synth.Dims(T=40, B=3, Din=16, NH=2, Dh=32)
+    lstm = cell == "lstm"
+    c = synth.make_case(cell, d, "f32", 9990, bias="forget+1" if lstm else "zero", h0_var=0.2,
+                        c0_var=0.2 if lstm else 0.0, backward=True)
+    x, W, R, b, h0 = dev(c, "x"), dev(c, "W"), dev(c, "R"), dev(c, "b"), dev(c, "h0")
+    chunk = 16
+    if lstm:
+        c0 = dev(c, "c0")
+        fc = g.lstm_fwd_chunked(x, W, R, b, h0, c0, chunk=chunk, with_seq=False, ckpt=True)
+        ck = g.lstm_bwd_ckpt(x, W, R, b, h0, c0, fc[4], fc[5], dev(c, "dH"), chunk=chunk)
+    else:
+        fc = g.gru_fwd_chunked(x, W, R, b, h0, chunk=chunk, with_seq=False, ckpt=True)
+        ck = g.gru_bwd_ckpt(x, W, R, b, h0, fc[2], dev(c, "dH"), chunk=chunk)
+    torch.cuda.synchronize()
+    ck = {k: host(v) for k, v in ck.items()}
+    one = _bwd_any(c, False)
+    for k in ("dx", "dh0") + (("dc0",) if lstm else ()):
+        assert np.array_equal(ck[k], one[k]), k
+    ref = _bwd_oracle(c, False)
+    for k in ck:
+        check(k, ck[k], ref[k], TOL_F32)
