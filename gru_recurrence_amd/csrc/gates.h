@@ -68,32 +68,33 @@ template <int CELL, bool GXK = false>
 __device__ __forceinline__ void gate_rows_update(float v, float gx, float &st, float &hl,
                                                  float &h, float &c) {
     const int row = (threadIdx.x & 63) >> 4;
-    const bool tanh_row = CELL == kLSTM && row == 2;
     const float act_k = gate_row_scale<CELL>(row);
     const float arg = (GXK && CELL == kLSTM) ? fmaf(v, act_k, gx * act_k) : (v + gx) * act_k;
     const float sg = rcp_fast(1.0f + __builtin_amdgcn_exp2f(arg));
     if constexpr (CELL == kLSTM) {
-        // rows i, f, z, o of `act`; row 0 gathers f and z with one swap each
-        // and o (needed last) with a second swap; only row 0's c and h are
-        // valid (the lanes that write them)
-        const float act = tanh_row ? fmaf(sg, 2.0f, -1.0f) : sg;
-        const float f = swap16(act, act).b;              // rows [f, f, o, o]
-        const RowPair Z = swap32(act, act);              // [i, f, i, f] [z, o, z, o]
-        const float o = swap16(Z.b, Z.b).b;              // rows [o, o, o, o]
-        const float o2 = o + o;
-        const float cn = fmaf(f, st, act * Z.b);
+        // rows of sg: sigma(a_i), sigma(a_f), sigma(2 a_z), sigma(a_o).  Row 0
+        // gathers f and z with one swap each and o (needed last) with a
+        // second swap; only row 0's c and h are valid (the lanes that write
+        // them).  Each swap's partner register holds a constant set off the
+        // chain (its contents do not matter), so no copy of sg sits between
+        // the activation and c.
+        const float f = swap16(sg, 0.0f).b;   // rows [f, -, o, -]
+        const float zs = swap32(sg, 0.0f).b;  // rows [sigma(2 a_z), o, -, -]
+        const float o = swap16(zs, 0.0f).b;   // row 0: o
+        // i z = i (2 sigma(2 a_z) - 1)
+        const float cn = fmaf(f, st, fmaf(sg + sg, zs, -sg));
         st = cn;
         c = cn;
         const float s2 = rcp_fast(1.0f + __builtin_amdgcn_exp2f(cn * (-2.0f * kLog2e)));
-        h = fmaf(o2, s2, -o);
+        h = fmaf(o + o, s2, -o);
         hl = h;
     } else {
         // tanh(x) = 2 sigmoid(2x) - 1 on the candidate row
-        const RowPair W = swap32(sg, sg);                 // rows r, u, r, u
+        const RowPair W = swap32(0.0f, sg);               // W.a rows -, -, r, u
         const float xn = fmaf(W.a, v, gx);                // row 2: Gx_n + r S_n
         const float nn = fmaf(2.0f, rcp_fast(1.0f + __builtin_amdgcn_exp2f(xn * (-2.0f * kLog2e))),
                               -1.0f);
-        const float nn3 = swap16(nn, nn).a;               // row 3 <- row 2
+        const float nn3 = swap16(0.0f, nn).a;             // row 3 <- row 2
         const float hn = fmaf(W.a, st - nn3, nn3);        // row 3: (1-u) nn + u h
         st = hn;
         h = hn;

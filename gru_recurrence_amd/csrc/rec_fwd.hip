@@ -308,6 +308,46 @@ __device__ __forceinline__ void rec_fwd_mfma_body(const RecArgs &a, const int bl
     bf16x8 af[KC];
 #pragma unroll
     for (int c = 0; c < KC; ++c) af[c] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+    auto read_chunks = [&](const uint16_t *hb, int c0, int c1) {
+        if (lr < rows) {
+#pragma unroll
+            for (int c = c0; c < c1; ++c)
+                af[c] = *reinterpret_cast<const bf16x8 *>(hb + lr * HLD + 32 * c + 8 * lg);
+        }
+    };
+    // acc += h chunks [c0, c1) times this wave's R fragments, k-chunk after
+    // k-chunk (the first MFMAs need only the first LDS read)
+    f32x4 acc[G];
+    auto mfma_chunks = [&](int c0, int c1) {
+#pragma unroll
+        for (int c = c0; c < c1; ++c)
+#pragma unroll
+            for (int g = 0; g < G; ++g) acc[g] = mfma_16x16x32_bf16(af[c], rf[g][c], acc[g]);
+    };
+    // Group traffic at the first step of a group: the previous group's
+    // outputs stored, the next group's Gx requested.
+    auto group_traffic = [&](int tg, float (&nxt)[PD][R4][GL]) {
+        if constexpr (HB) {
+            wait_ready(tg + 2 * PD);
+            load_group(tg + PD, nxt);
+            if (tg > 0) store_group(tg - PD);
+        } else {
+            if (tg > 0) store_group(tg - PD);
+            wait_ready(tg + 2 * PD);
+            load_group(tg + PD, nxt);
+        }
+    };
+    // Cell update of step s of the group and h_t into the LDS buffer hn.
+    auto cell = [&](int s, float (&use)[PD][R4][GL], uint16_t *hn) {
+        float h[R4], c[R4];
+        gate_update<CELL, R4, GL, GXK>(acc, use[s], st, hl, h, c);
+#pragma unroll
+        for (int r = 0; r < R4; ++r) {
+            oh[s][r] = h[r];
+            oc[s][r] = c[r];
+            if (wr[r]) hn[(ROWS1 ? 0 : 4 * lg + r) * HLD + j] = f32_to_bf16_rne(h[r]);
+        }
+    };
     // PD steps starting at tg, reading Gx from `use`; at the first step the
     // previous group's outputs are stored and the next group's Gx requested.
     // FULL: every step of the group is < T (no per-step bound checks).
@@ -327,45 +367,21 @@ __device__ __forceinline__ void rec_fwd_mfma_body(const RecArgs &a, const int bl
             }
             const uint16_t *hc = hbuf[s & 1];
             uint16_t *hn = hbuf[(s + 1) & 1];
-            if (lr < rows) {
-#pragma unroll
-                for (int c = 0; c < KC; ++c)
-                    af[c] = *reinterpret_cast<const bf16x8 *>(hc + lr * HLD + 32 * c + 8 * lg);
-            }
-            f32x4 acc[G];
+            read_chunks(hc, 0, KC);
 #pragma unroll
             for (int g = 0; g < G; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int c = 0; c < KC; ++c)
-#pragma unroll
-                for (int g = 0; g < G; ++g) acc[g] = mfma_16x16x32_bf16(af[c], rf[g][c], acc[g]);
+            mfma_chunks(0, KC);
             // steps are unrolled: only a group's first step branches right
             // after the chain (the HBM traffic of the group), so only it needs
             // the pinned wait states
-            if (s == 0) mfma_chain_end();
             if (s == 0) {
-                if constexpr (HB) {
-                    wait_ready(tg + 2 * PD);
-                    load_group(tg + PD, nxt);
-                    if (tg > 0) store_group(tg - PD);
-                } else {
-                    if (tg > 0) store_group(tg - PD);
-                    wait_ready(tg + 2 * PD);
-                    load_group(tg + PD, nxt);
-                }
+                mfma_chain_end();
+                group_traffic(tg, nxt);
             }
-            float h[R4], c[R4];
-            gate_update<CELL, R4, GL, GXK>(acc, use[s], st, hl, h, c);
-#pragma unroll
-            for (int r = 0; r < R4; ++r) {
-                oh[s][r] = h[r];
-                oc[s][r] = c[r];
-                if (wr[r]) hn[(ROWS1 ? 0 : 4 * lg + r) * HLD + j] = f32_to_bf16_rne(h[r]);
-            }
+            cell(s, use, hn);
             lds_barrier();
         }
     };
-
     wait_ready(PD);
     load_group(0, bx0);
     using Full = std::integral_constant<bool, true>;
