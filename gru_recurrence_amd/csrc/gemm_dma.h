@@ -5,6 +5,8 @@
 // workgroups.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -28,24 +30,34 @@ static_assert(BM == kGemmRowTile && BN == kGemmColTile, "row-panel counters assu
 // 16-byte bank groups of a 256-byte (128-byte) LDS access phase.
 __device__ __forceinline__ int swz(int r) { return ((r >> 2) & 3) ^ (r & 2); }
 
-// Issue the loads of one operand tile (256 rows x 32 k) into `dst`: 1024
-// chunks of 16 bytes, two per thread; chunk q goes to LDS byte 16q, i.e.
-// row q/4, slot q%4, holding k chunk (q%4) ^ swz(row).  Rows past R read
-// row R-1 (their products only reach outputs that are not stored).
+// The loads of one operand tile (256 rows x 32 k): 1024 chunks of 16 bytes,
+// two per thread; chunk q goes to LDS byte 16q, i.e. row q/4, slot q%4,
+// holding k chunk (q%4) ^ swz(row).  Rows past R read row R-1 (their
+// products only reach outputs that are not stored).  `off` holds this
+// thread's two byte offsets from the tile's (row 0, k 0) element, set once
+// per output tile; a K tile only moves the wave-uniform base, so each load
+// is an SGPR base plus a 32-bit VGPR offset and the LDS destination (M0) is
+// wave-uniform too: no per-load vector arithmetic.
 // AUX is the loads' cache policy (16: device scope, for operands that other
 // workgroups of the same launch write).
-template <int AUX = 0>
-__device__ __forceinline__ void dma_tile(const uint16_t *__restrict__ P, long ld, int r0, int k0,
-                                         int R, lds_char *dst, int tid, int wave) {
+__device__ __forceinline__ void tile_offsets(long ld, int r0, int R, int tid, uint32_t (&off)[2]) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int q = tid + NTHR * i;
         const int r = q >> 2, slot = q & 3;
         const int chunk = slot ^ swz(r);
         const int gr = min(r0 + r, R - 1);
-        const uint16_t *src = P + (long)gr * ld + k0 + chunk * 8;
-        __builtin_amdgcn_global_load_lds(src, dst + (64 * wave + NTHR * i) * 16, 16, 0, AUX);
+        off[i] = (uint32_t)(((long)gr * ld + chunk * 8) * 2);
     }
+}
+template <int AUX = 0>
+__device__ __forceinline__ void dma_tile(const uint16_t *__restrict__ P, int k0, const uint32_t (&off)[2],
+                                         lds_char *dst, int wave_s) {
+    const char *base = reinterpret_cast<const char *>(P + k0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        __builtin_amdgcn_global_load_lds(base + off[i], dst + (64 * wave_s + NTHR * i) * 16, 16, 0,
+                                         AUX);
 }
 
 // vmcnt(4 * later): the loads of `later` later tiles may stay in flight.
@@ -73,6 +85,7 @@ __device__ __forceinline__ void gemm_dma_tiles_pre(const GemmArgs &g, int wg, in
     const uint16_t *B = g.B + (long)bz * g.strideB;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // in an SGPR: M0 from scalar code
     const int wm = wave >> 2, wn = wave & 3;
     const int l32 = lane & 31, lh = lane >> 5;
 
@@ -98,10 +111,11 @@ __device__ __forceinline__ void gemm_dma_tiles_pre(const GemmArgs &g, int wg, in
     // Workgroup i runs on XCD i % 8 (nwg is a multiple of 8 or the tile
     // count), so tile t goes to XCD t % 8.  Where the tile counts divide,
     // XCD x = 2 xr + xc takes the row tiles xr, xr + 4, ... in order and the
-    // column tiles of half xc: its share of W^T (half the columns) stays in its L2 while the row panels stream.  Otherwise runs
-    // of 8 row tiles, row tile 8q + x of a run on XCD x with all its column
-    // tiles, rows past the last whole run in order.  Either way each XCD
-    // finishes its row panels in time order.
+    // column tiles of half xc: its share of W^T (half the columns) stays in
+    // its L2 while the row panels stream.  Otherwise runs of 8 row tiles,
+    // row tile 8q + x of a run on XCD x with all its column tiles, rows past
+    // the last whole run in order.  Either way each XCD finishes its row
+    // panels in time order.
     const int tiles_n = (g.N + BN - 1) / BN;
     const int tiles_m = (g.M + BM - 1) / BM;
     const int tiles = tiles_m * tiles_n;
@@ -131,30 +145,49 @@ __device__ __forceinline__ void gemm_dma_tiles_pre(const GemmArgs &g, int wg, in
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 
+    // register r of lane l of block (i, j): row 32 i + 8 (r/4) + 4 (l/32) +
+    // r%4 of the wave's rows, column 32 j + l%32 of its columns
     f32x16 acc[4][2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     // the second segment's A columns of this tile's column block
     const uint16_t *A2 = SEG2 ? g.A2 + (long)(n0 / g.seg_n) * g.K2 : nullptr;
-    auto issue = [&](int kt) {
-        lds_char *st = lds + ((kt - kt0) % NS) * STB;
+    uint32_t goA[2], goB[2], goA2[2], goB2[2];
+    tile_offsets(g.lda, m0, g.M, tid, goA);
+    tile_offsets(g.ldb, n0, g.N, tid, goB);
+    if (SEG2) {
+        tile_offsets(g.lda2, m0, g.M, tid, goA2);
+        tile_offsets(g.ldb2, n0, g.N, tid, goB2);
+    }
+    // SEG2: the second segment's offsets replace the first's when its first
+    // K tile is issued (K tiles are issued in order)
+    auto issue = [&](int kt, int stage) {
+        lds_char *st = lds + stage * STB;
+        if (SEG2 && kt == ktiles1) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                goA[i] = goA2[i];
+                goB[i] = goB2[i];
+            }
+        }
         if (!SEG2 || kt < ktiles1) {
-            dma_tile<A_AUX>(A, g.lda, m0, kt * BK, g.M, st, tid, wave);
-            dma_tile(B, g.ldb, n0, kt * BK, g.N, st + OPB, tid, wave);
+            dma_tile<A_AUX>(A, kt * BK, goA, st, wave_s);
+            dma_tile(B, kt * BK, goB, st + OPB, wave_s);
         } else {
             const int k2 = (kt - ktiles1) * BK;
-            dma_tile<A_AUX>(A2, g.lda2, m0, k2, g.M, st, tid, wave);
-            dma_tile(g.B2, g.ldb2, n0, k2, g.N, st + OPB, tid, wave);
+            dma_tile<A_AUX>(A2, k2, goA, st, wave_s);
+            dma_tile(g.B2, k2, goB, st + OPB, wave_s);
         }
     };
+    if (SEG2 && kt0 > ktiles1) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            goA[i] = goA2[i];
+            goB[i] = goB2[i];
+        }
+    }
 #pragma unroll
     for (int p = 0; p < NS - 1; ++p)
-        if (kt0 + p < kt1) issue(kt0 + p);
+        if (kt0 + p < kt1) issue(kt0 + p, p);
 
     // Pipelined at k-step granularity (two 16-deep k-steps per tile): the
     // reads of the next k-step are in flight while the current one's MFMAs
@@ -162,9 +195,9 @@ __device__ __forceinline__ void gemm_dma_tiles_pre(const GemmArgs &g, int wg, in
     // kt's two k-steps, so its wait overlaps MFMAs already issued.  The
     // stage refilled at that barrier is the one tile kt-1 used: every wave's
     // reads of it completed before its MFMAs of kt-1, i.e. before the barrier.
-#define RNN355_READ_HALF(kt, kc, a0, a1, a2, a3, b0, b1)                                     \
+#define RNN355_READ_HALF(stage, kc, a0, a1, a2, a3, b0, b1)                                  \
     do {                                                                                     \
-        const uint32_t sb_ = lbase + (uint32_t)((((kt) - kt0) % NS) * STB);                  \
+        const uint32_t sb_ = lbase + (uint32_t)((stage) * STB);                              \
         asm volatile("ds_read_b128 %0, %6\n\t"                                              \
                      "ds_read_b128 %1, %6 offset:2048\n\t"                                  \
                      "ds_read_b128 %2, %6 offset:4096\n\t"                                  \
@@ -177,20 +210,18 @@ __device__ __forceinline__ void gemm_dma_tiles_pre(const GemmArgs &g, int wg, in
     } while (0)
 // the 8 MFMAs of one k-step once its reads are in (WAIT: the lgkmcnt that
 // leaves the six reads issued after them in flight, or 0); the wait is tied
-// to the fragment registers so that no use moves above it
-#define RNN355_MFMA_HALF(WAIT, a0, a1, a2, a3, b0, b1)                                       \
+// to the fragment registers so that no use moves above it.  ZERO: the
+// tile's first k-step, whose MFMAs start from 0 (no accumulator clearing).
+#define RNN355_MFMA_HALF(WAIT, ZERO, a0, a1, a2, a3, b0, b1)                                 \
     do {                                                                                     \
         asm volatile("s_waitcnt lgkmcnt(" #WAIT ")"                                          \
                      : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3), "+v"(b0), "+v"(b1));          \
-        acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0][0], 0, 0, 0);     \
-        acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[0][1], 0, 0, 0);     \
-        acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc[1][0], 0, 0, 0);     \
-        acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[1][1], 0, 0, 0);     \
-        acc[2][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, b0, acc[2][0], 0, 0, 0);     \
-        acc[2][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, b1, acc[2][1], 0, 0, 0);     \
-        acc[3][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a3, b0, acc[3][0], 0, 0, 0);     \
-        acc[3][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a3, b1, acc[3][1], 0, 0, 0);     \
-                                                                                             \
+        const bf16x8 *a_[4] = {&a0, &a1, &a2, &a3};                                          \
+        const bf16x8 *b_[2] = {&b0, &b1};                                                    \
+        _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                     \
+        _Pragma("unroll") for (int j_ = 0; j_ < 2; ++j_)                                     \
+            acc[i_][j_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                           \
+                *a_[i_], *b_[j_], (ZERO) ? f32x16{} : acc[i_][j_], 0, 0, 0);                 \
     } while (0)
 
     // tile kt0: landed for everyone
@@ -199,11 +230,15 @@ __device__ __forceinline__ void gemm_dma_tiles_pre(const GemmArgs &g, int wg, in
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     bf16x8 x0, x1, x2, x3, x4, x5, y0, y1, y2, y3, y4, y5;
-    RNN355_READ_HALF(kt0, 0, x0, x1, x2, x3, x4, x5);
-    for (int kt = kt0; kt < kt1; ++kt) {
-        RNN355_READ_HALF(kt, 1, y0, y1, y2, y3, y4, y5);
-        RNN355_MFMA_HALF(6, x0, x1, x2, x3, x4, x5);
+    // ring stages: `cur` holds tile kt, `prev` tile kt-1 (refilled with kt-1+NS)
+    int cur = 0, prev = NS - 1;
+    RNN355_READ_HALF(cur, 0, x0, x1, x2, x3, x4, x5);
+    auto ktile = [&](int kt, auto first) {
+        constexpr bool F = decltype(first)::value;
+        RNN355_READ_HALF(cur, 1, y0, y1, y2, y3, y4, y5);
+        RNN355_MFMA_HALF(6, F, x0, x1, x2, x3, x4, x5);
         const bool more = kt + 1 < kt1;
+        const int nxt = cur + 1 == NS ? 0 : cur + 1;
         if (more) {
             // this thread's loads of tile kt+1 landed (later tiles may fly);
             // after the barrier everyone's have
@@ -215,69 +250,88 @@ __device__ __forceinline__ void gemm_dma_tiles_pre(const GemmArgs &g, int wg, in
         }
         // the next tile's first k-step (the last tile re-reads its own, unused,
         // so that the count of reads behind y stays six on every path)
-        RNN355_READ_HALF(more ? kt + 1 : kt, 0, x0, x1, x2, x3, x4, x5);
-        RNN355_MFMA_HALF(6, y0, y1, y2, y3, y4, y5);
+        RNN355_READ_HALF(more ? nxt : cur, 0, x0, x1, x2, x3, x4, x5);
+        RNN355_MFMA_HALF(6, false, y0, y1, y2, y3, y4, y5);
         // refill the stage of tile kt-1 (at kt0: the stage the prologue
         // left empty) with tile kt-1+NS
-        if (more && kt - 1 + NS < kt1) issue(kt - 1 + NS);
+        if (more && kt - 1 + NS < kt1) issue(kt - 1 + NS, prev);
+        prev = cur;
+        cur = nxt;
+    };
+    if (kt0 < kt1) {
+        ktile(kt0, std::integral_constant<bool, true>{});
+        for (int kt = kt0 + 1; kt < kt1; ++kt) ktile(kt, std::integral_constant<bool, false>{});
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the unused reads
 #undef RNN355_READ_HALF
 #undef RNN355_MFMA_HALF
 
-    // epilogue: register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4, column l%32
-    float *C;
-    long ldc;
-    bool direct;
-    if (g.ksplit == 1) {
-        C = g.C + (long)bz * g.strideC;
-        ldc = g.ldc;
-        direct = true;
-    } else {
-        C = g.partial + ((long)bz * g.ksplit + slice) * (long)g.M * g.N;
-        ldc = g.N;
-        direct = false;
-    }
-    const bool acc_old = direct && g.accumulate;
-    // the bias of this lane's two columns, loaded before any store
-    float bv[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int n = n0 + wn * 64 + j * 32 + l32;
-        bv[j] = (direct && g.bias && n < g.N) ? g.bias[n] : 0.f;
-    }
-    if (m0 + BM <= g.M && n0 + BN <= g.N && !acc_old) {
-        // a whole tile and nothing to read back: stores only, without bounds
-        // checks or loads between them (with either, the compiler waits for
-        // every earlier store before the next -- a round trip per store)
-        float *base = C + (long)(m0 + wm * 128 + 4 * lh) * ldc + n0 + wn * 64 + l32;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float *row = base + (long)(i * 32 + 8 * (r >> 2) + (r & 3)) * ldc;
-#pragma unroll
-                for (int j = 0; j < 2; ++j) row[j * 32] = acc[i][j][r] + bv[j];
-            }
-    } else {
+    // epilogue (an empty K range, a split-K slice past the end, stores zeros)
+    auto store_tile = [&](const f32x16 (&acc)[4][2]) {
+        float *C;
+        long ldc;
+        bool direct;
+        if (g.ksplit == 1) {
+            C = g.C + (long)bz * g.strideC;
+            ldc = g.ldc;
+            direct = true;
+        } else {
+            C = g.partial + ((long)bz * g.ksplit + slice) * (long)g.M * g.N;
+            ldc = g.N;
+            direct = false;
+        }
+        const bool acc_old = direct && g.accumulate;
+        // the bias of this lane's two columns, loaded before any store
+        float bv[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int n = n0 + wn * 64 + j * 32 + l32;
-            if (n >= g.N) continue;
+            bv[j] = (direct && g.bias && n < g.N) ? g.bias[n] : 0.f;
+        }
+        if (m0 + BM <= g.M && n0 + BN <= g.N && !acc_old) {
+            // a whole tile and nothing to read back: stores only, without
+            // bounds checks or loads between them (with either, the compiler
+            // waits for every earlier store before the next -- a round trip
+            // per store); each store writes two 128-byte row segments
+            float *base = C + (long)(m0 + wm * 128 + 4 * lh) * ldc + n0 + wn * 64 + l32;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int m = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-                    if (m < g.M) {
-                        float v = acc[i][j][r] + bv[j];
-                        float *dst = C + (long)m * ldc + n;
-                        if (acc_old) v += *dst;
-                        *dst = v;
+                    float *row = base + (long)(i * 32 + 8 * (r >> 2) + (r & 3)) * ldc;
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) row[j * 32] = acc[i][j][r] + bv[j];
+                }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int n = n0 + wn * 64 + j * 32 + l32;
+                if (n >= g.N) continue;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int m = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                        if (m < g.M) {
+                            float v = acc[i][j][r] + bv[j];
+                            float *dst = C + (long)m * ldc + n;
+                            if (acc_old) v += *dst;
+                            *dst = v;
+                        }
                     }
                 }
             }
         }
+    };
+    if (kt0 < kt1) {
+        store_tile(acc);
+    } else {
+        f32x16 zero[4][2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) zero[i][j] = f32x16{};
+        store_tile(zero);
     }
     if (g.ready) {
         // publish the finished tile (see gemm.hip): stores reach L2, one
