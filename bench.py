@@ -71,17 +71,20 @@ def recurrent_flops(w: synth.Workload, T=None) -> float:
 
 def rec_kernel_name(w: synth.Workload, plan: str) -> str:
     """Name of the recurrence kernel the plan launches, as the profiler shows
-    it (template arguments: cell, Dh, row slots, steps per group, waits)."""
+    it (template arguments: cell, Dh, cell update passes, steps per group,
+    waits, rows in lane groups)."""
     if "multi_cu" in plan:
         return "rec_fwd_mc_kernel"
     if "split_R" in plan:
         return "rec_fwd_wide_kernel<%d>" % (0 if w.cell == "lstm" else 1)
     if "mfma" not in plan:
         return "rec_fwd_simple_kernel"
-    upt = int(plan.split("units_per_thread=")[1].split()[0])
-    pd = {1: 8, 2: 4, 4: 2}[upt]
-    return "rec_fwd_mfma_kernel<%d, %d, %d, %d, false>" % (0 if w.cell == "lstm" else 1,
-                                                          w.dims.Dh, upt, pd)
+    passes = int(plan.split("units_per_thread=")[1].split()[0])
+    rows = int(plan.split("rows_per_wg=")[1].split()[0])
+    lanes = 1 < rows <= 8
+    pd = {1: 8 if rows == 1 else 4, 2: 2, 4: 2}[passes]
+    return "rec_fwd_mfma_kernel<%d, %d, %d, %d, false, %s>" % (
+        0 if w.cell == "lstm" else 1, w.dims.Dh, passes, pd, "true" if lanes else "false")
 
 
 def traffic_per_launch():

@@ -102,6 +102,45 @@ __device__ __forceinline__ void gate_rows_update(float v, float gx, float &st, f
     }
 }
 
+// Batch rows in lane groups: the MFMA leaves row 4p + r of the tile in
+// register r of lane group p.  Two 16-lane and two 32-lane swaps per gate
+// transpose that 4 x 4 block, so that pass r holds row 4r + q in lane group
+// q and each pass of the cell update serves four rows: R4 passes cover 4 R4
+// rows (the register-slot layout runs one pass per register).
+//   gx[r][g]: the G gate inputs Gx of the lane's row in pass r.
+template <int CELL, int R4>
+__device__ __forceinline__ void gate_update_lanes(const f32x4 (&acc)[CellTraits<CELL>::G],
+                                                  const float (&gx)[R4][CellTraits<CELL>::G],
+                                                  float (&st)[R4], float (&hl)[R4], float (&h)[R4],
+                                                  float (&c)[R4]) {
+    constexpr int G = CellTraits<CELL>::G;
+    static_assert(R4 == 1 || R4 == 2 || R4 == 4, "one, two or four passes");
+    float v[R4][G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const RowPair p = swap16(acc[g][0], acc[g][1]);
+        const RowPair q = swap16(acc[g][2], acc[g][3]);
+        const RowPair x = swap32(p.a, q.a);  // passes 0, 2
+        v[0][g] = x.a;
+        if constexpr (R4 > 1) {
+            const RowPair y = swap32(p.b, q.b);  // passes 1, 3
+            v[1][g] = y.a;
+            if constexpr (R4 > 2) {
+                v[2][g] = x.b;
+                v[3][g] = y.b;
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < R4; ++r) {
+        float pre[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) pre[g] = (CELL == kGRU && g == 2) ? v[r][g] : v[r][g] + gx[r][g];
+        h[r] = unit_update<CELL>(pre, CELL == kGRU ? gx[r][2] : 0.f, st[r], c[r]);
+        hl[r] = h[r];
+    }
+}
+
 // The cell update of all row slots of one lane.
 //   gx[r][.]: for R4 > 1 the G gate inputs Gx of row slot r; for R4 == 1 a
 //             single value, the Gx of gate l/16 (the lane's row, see above).

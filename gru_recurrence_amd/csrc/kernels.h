@@ -106,7 +106,7 @@ struct RecPlan {
     int grid;        // workgroups
     int threads;     // per workgroup
     int waves;       // per workgroup
-    int upt;         // units per thread (MFMA kernel)
+    int upt;         // MFMA kernel: cell update passes per step (rows in lane groups; 1 at BT = 1)
     size_t lds;      // dynamic LDS bytes (simple kernel)
 };
 

@@ -57,8 +57,11 @@ namespace {
 // kernels; see the calibration in the design notes).
 constexpr double kMfmaNs = 7.95;          // one 16x16x32 bf16 MFMA issued per SIMD
 constexpr double kGateNs[3] = {61.5, 136.5, 261.5};  // cell update per gate, 1/2/4 row slots
+constexpr double kResLanesNs = 101.5;     // ... rows in lane groups (one CU), per gate
+constexpr double kResLanesPassNs = 50.0;  // ... per further pass of four rows
+constexpr double kResLanesRowNs = 8.4;    // ... per gate and row (Gx and outputs of a row)
 constexpr double kGateLanesNs = 100.0;    // ... rows in lane groups (multi-CU), per gate
-constexpr double kGateLanesPassNs = 120.0; // ... per further pass of four rows
+constexpr double kGateLanesPassNs = 150.0; // ... per further pass of four rows
 constexpr double kGatherRoundNs = 400.0;  // multi-CU: per further poll round of the gather
 constexpr double kWideRowsNs = 250.0;     // more than 8 rows of a tile: second row half
 constexpr double kExchangeNs = 1480.0;    // cross-CU step exchange (flag-in-data words)
@@ -88,9 +91,10 @@ constexpr int kWideWorkVgpr = 128;                // the split-R step's own VGPR
 int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 
 // Registers per wave (VGPRs + AGPRs) of the one-CU MFMA kernel as the
-// compiler reports them, [cell][Dh 32, 64, 128][row slots 1, 2, 4].
-constexpr int kResRegs[2][3][3] = {{{88, 226, 262}, {112, 240, 258}, {184, 244, 262}},
-                                   {{70, 210, 230}, {86, 224, 246}, {136, 216, 252}}};
+// compiler reports them, [cell][Dh 32, 64, 128][one row; rows in lane groups
+// with 1, 2 passes; four register row slots].
+constexpr int kResRegs[2][3][4] = {{{88, 172, 170, 262}, {112, 188, 190, 258}, {184, 205, 212, 262}},
+                                   {{70, 132, 136, 230}, {86, 146, 154, 246}, {138, 168, 174, 252}}};
 
 // Workgroups of `waves` waves, `regs` registers each, `lds` bytes, that fit
 // on one CU at once (at most 8).
@@ -141,8 +145,12 @@ void family_resident(int cell, int T, int B, int NH, int Dh, bool bf16, int cus,
     const int G = cell == kLSTM ? 4 : 3;
     for (int bt = 1; bt <= 16; ++bt) {
         PlanCand c = blank(kFamResident);
+        // one row: the gate-row cell update; two to eight rows: rows in lane
+        // groups, one pass per four rows (r4 passes); more: four register
+        // row slots
+        const bool lanes = bt > 1 && bt <= 8;
         c.BT = bt;
-        c.r4 = r4_of(bt);
+        c.r4 = bt <= 4 ? 1 : bt <= 8 ? 2 : 4;
         c.nb = Dh / 16;
         c.kcw = Dh / 32;
         c.waves = Dh / 16;
@@ -150,7 +158,8 @@ void family_resident(int cell, int T, int B, int NH, int Dh, bool bf16, int cus,
         c.r_vgpr = 4 * G * (Dh / 32);
         c.lds = 2L * 16 * (Dh + 8) * 2;
         const int di = Dh == 32 ? 0 : Dh == 64 ? 1 : 2;
-        c.wg_per_cu = fit_per_cu(c.waves, kResRegs[cell == kLSTM ? 0 : 1][di][r4_index(c.r4)], c.lds);
+        const int vi = bt == 1 ? 0 : lanes ? c.r4 : 3;
+        c.wg_per_cu = fit_per_cu(c.waves, kResRegs[cell == kLSTM ? 0 : 1][di][vi], c.lds);
         if (!bf16 || (Dh != 32 && Dh != 64 && Dh != 128)) fail(c, kPlanNotInstantiated);
         if (Dh % 32 != 0) fail(c, kPlanDivisibility);
         if (bt > B) fail(c, kPlanBatch);
@@ -158,7 +167,9 @@ void family_resident(int cell, int T, int B, int NH, int Dh, bool bf16, int cus,
             fail(c, kPlanRegisters);
         if (fix.bt > 0 && bt != std::min({fix.bt, 16, B})) fail(c, kPlanFixed);
         const int per_simd = ceil_div(c.waves, kSimds);
-        c.ns_step = kMfmaNs * G * (Dh / 32) * per_simd + G * kGateNs[r4_index(c.r4)] +
+        c.ns_step = kMfmaNs * G * (Dh / 32) * per_simd +
+                    G * (lanes ? kResLanesNs + kResLanesPassNs * (c.r4 - 1) + kResLanesRowNs * bt
+                               : kGateNs[bt == 1 ? 0 : 2]) +
                     (bt > 8 ? kWideRowsNs : 0.0);
         finish(c, T, cus);
         out.add(c);

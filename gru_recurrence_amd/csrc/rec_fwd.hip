@@ -110,7 +110,7 @@ __device__ __forceinline__ void lstm_or_gru_unit(const float *gpre, int DH, cons
 // s_waitcnt immediate for vmcnt(n), n < 64, other counters not waited on.
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
-template <int CELL, int DH, int R4, int PD, bool WAIT, bool HB = false>
+template <int CELL, int DH, int R4, int PD, bool WAIT, bool HB = false, bool LANES = false>
 __device__ __forceinline__ void rec_fwd_mfma_body(const RecArgs &a, const int blk,
                                                   uint16_t *h_bf = nullptr,
                                                   unsigned *done = nullptr) {
@@ -119,7 +119,7 @@ __device__ __forceinline__ void rec_fwd_mfma_body(const RecArgs &a, const int bl
     constexpr int NW = DH / 16;   // waves = 16-unit blocks
     constexpr int KC = DH / 32;   // k chunks of one MFMA
     constexpr int HLD = DH + 8;   // bf16 per h row in LDS (bank spread)
-    constexpr bool ROWS1 = R4 == 1;
+    constexpr bool ROWS1 = R4 == 1 && !LANES;  // one batch row (gate-row layout)
     constexpr int GL = ROWS1 ? 1 : G;          // Gx values per row slot per lane
     constexpr int OUT_ROW = CELL == kLSTM ? 0 : 3;  // R4 == 1: lanes that own the result
     static_assert(DH % 32 == 0, "Dh must be a multiple of 32");
@@ -171,15 +171,18 @@ __device__ __forceinline__ void rec_fwd_mfma_body(const RecArgs &a, const int bl
     const long gx_step = (long)B * N, o_step = (long)B * H;
     const long o_tile = (long)b0 * H + n * DH;
     const bool has_h = a.h_seq != nullptr, has_c = CELL == kLSTM && a.c_seq != nullptr;
-    // lane roles.  R4 > 1: row slot r is batch row 4*lg + r.  R4 == 1: batch
-    // row 0 only; lane row lg is gate lg for the Gx loads, and the lanes of
-    // row OUT_ROW write results.
+    // lane roles.  LANES: pass r holds batch row 4*r + lg (gate_update_lanes).
+    // Otherwise R4 > 1: row slot r is batch row 4*lg + r.  R4 == 1: batch row
+    // 0 only; lane row lg is gate lg for the Gx loads, and the lanes of row
+    // OUT_ROW write results.
     bool rv[R4], ld[R4], wr[R4];
     unsigned go[R4], oo[R4];
+    int brow[R4];
     float st[R4], hl[R4];
 #pragma unroll
     for (int r = 0; r < R4; ++r) {
-        const int b = ROWS1 ? 0 : 4 * lg + r;
+        const int b = ROWS1 ? 0 : LANES ? 4 * r + lg : 4 * lg + r;
+        brow[r] = b;
         rv[r] = b < rows;
         ld[r] = ROWS1 ? lg < G : rv[r];
         wr[r] = ROWS1 ? lg == OUT_ROW : rv[r];
@@ -340,12 +343,15 @@ __device__ __forceinline__ void rec_fwd_mfma_body(const RecArgs &a, const int bl
     // Cell update of step s of the group and h_t into the LDS buffer hn.
     auto cell = [&](int s, float (&use)[PD][R4][GL], uint16_t *hn) {
         float h[R4], c[R4];
-        gate_update<CELL, R4, GL, GXK>(acc, use[s], st, hl, h, c);
+        if constexpr (LANES)
+            gate_update_lanes<CELL, R4>(acc, use[s], st, hl, h, c);
+        else
+            gate_update<CELL, R4, GL, GXK>(acc, use[s], st, hl, h, c);
 #pragma unroll
         for (int r = 0; r < R4; ++r) {
             oh[s][r] = h[r];
             oc[s][r] = c[r];
-            if (wr[r]) hn[(ROWS1 ? 0 : 4 * lg + r) * HLD + j] = f32_to_bf16_rne(h[r]);
+            if (wr[r]) hn[brow[r] * HLD + j] = f32_to_bf16_rne(h[r]);
         }
     };
     // PD steps starting at tg, reading Gx from `use`; at the first step the
@@ -421,9 +427,9 @@ __device__ __forceinline__ void rec_fwd_mfma_body(const RecArgs &a, const int bl
     }
 }
 
-template <int CELL, int DH, int R4, int PD, bool WAIT>
+template <int CELL, int DH, int R4, int PD, bool WAIT, bool LANES>
 __global__ __launch_bounds__(DH / 16 * 64) void rec_fwd_mfma_kernel(RecArgs a) {
-    rec_fwd_mfma_body<CELL, DH, R4, PD, WAIT>(a, blockIdx.x);
+    rec_fwd_mfma_body<CELL, DH, R4, PD, WAIT, false, LANES>(a, blockIdx.x);
 }
 
 // The pipelined forward as one launch (Dh = 128: both roles run 512
@@ -434,7 +440,7 @@ __global__ __launch_bounds__(DH / 16 * 64) void rec_fwd_mfma_kernel(RecArgs a) {
 // is resident before any recurrence workgroup starts to wait, and the
 // projection waits on nothing: the launch cannot stall on itself, whatever
 // else shares the chip.
-template <int CELL, int DH, int R4, int PD>
+template <int CELL, int DH, int R4, int PD, bool LANES>
 __global__ __launch_bounds__(512) void fwd_fused_kernel(RecArgs a, GemmArgs g, int n_gemm) {
     static_assert(DH / 16 * 64 == 512, "both roles run 512 threads");
     extern __shared__ __attribute__((aligned(16))) char fused_lds[];
@@ -442,7 +448,7 @@ __global__ __launch_bounds__(512) void fwd_fused_kernel(RecArgs a, GemmArgs g, i
         dma::gemm_dma_tiles(g, blockIdx.x, n_gemm, (dma::lds_char *)fused_lds);
         return;
     }
-    rec_fwd_mfma_body<CELL, DH, R4, PD, true>(a, blockIdx.x - n_gemm);
+    rec_fwd_mfma_body<CELL, DH, R4, PD, true, false, LANES>(a, blockIdx.x - n_gemm);
 }
 
 // Two stacked layers in one launch (see StackSync): [0, R) layer l's
@@ -562,19 +568,26 @@ __global__ __launch_bounds__(256) void rec_fwd_simple_kernel(RecArgs a) {
     }
 }
 
-// Rows per lane in use and the matching prefetch group length (steps).
+// One batch row: the gate-row layout.  Two to eight rows: rows in lane
+// groups, one cell update pass per four rows (upt passes).  More: the
+// register-slot layout, four passes (the same count, with fewer live
+// registers).  Each with its prefetch group length (steps).
 template <int CELL, int DH, bool WAIT>
 void launch_mfma_rows_w(const RecPlan &p, const RecArgs &a, hipStream_t s) {
     const dim3 grid(p.grid), blk(DH / 16 * 64);
+    if (p.BT == 1) {
+        hipLaunchKernelGGL((rec_fwd_mfma_kernel<CELL, DH, 1, 8, WAIT, false>), grid, blk, 0, s, a);
+        return;
+    }
     switch (p.upt) {
         case 1:
-            hipLaunchKernelGGL((rec_fwd_mfma_kernel<CELL, DH, 1, 8, WAIT>), grid, blk, 0, s, a);
+            hipLaunchKernelGGL((rec_fwd_mfma_kernel<CELL, DH, 1, 4, WAIT, true>), grid, blk, 0, s, a);
             break;
         case 2:
-            hipLaunchKernelGGL((rec_fwd_mfma_kernel<CELL, DH, 2, 4, WAIT>), grid, blk, 0, s, a);
+            hipLaunchKernelGGL((rec_fwd_mfma_kernel<CELL, DH, 2, 2, WAIT, true>), grid, blk, 0, s, a);
             break;
         default:
-            hipLaunchKernelGGL((rec_fwd_mfma_kernel<CELL, DH, 4, 2, WAIT>), grid, blk, 0, s, a);
+            hipLaunchKernelGGL((rec_fwd_mfma_kernel<CELL, DH, 4, 2, WAIT, false>), grid, blk, 0, s, a);
             break;
     }
 }
@@ -617,7 +630,8 @@ RecPlan plan_rec(int cell, int T, int B, int NH, int Dh, bool bf16, int num_cu,
         p.grid = NH * p.nbt;
         p.waves = Dh / 16;
         p.threads = p.waves * 64;
-        p.upt = bt >= 4 ? 4 : bt == 3 ? 4 : bt;  // register row slots per lane
+        p.upt = bt <= 4 ? 1 : bt <= 8 ? 2 : 4;  // cell update passes per step
+        // (rows in lane groups up to 8 rows, register slots beyond)
         p.lds = 0;
         return p;
     }
@@ -644,18 +658,18 @@ RecPlan plan_rec(int cell, int T, int B, int NH, int Dh, bool bf16, int num_cu,
     return p;
 }
 
-template <int CELL, int R4, int PD>
+template <int CELL, int R4, int PD, bool LANES>
 hipError_t launch_fused_t(const RecPlan &p, const RecArgs &a, const GemmArgs &g, int n_gemm,
                           hipStream_t s) {
     static std::once_flag once;
     static hipError_t attr = hipSuccess;
     std::call_once(once, [] {
         attr = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&fwd_fused_kernel<CELL, 128, R4, PD>),
+            reinterpret_cast<const void *>(&fwd_fused_kernel<CELL, 128, R4, PD, LANES>),
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)dma::LDS_BYTES);
     });
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((fwd_fused_kernel<CELL, 128, R4, PD>), dim3(n_gemm + p.grid),
+    hipLaunchKernelGGL((fwd_fused_kernel<CELL, 128, R4, PD, LANES>), dim3(n_gemm + p.grid),
                        dim3(512), dma::LDS_BYTES, s, a, g, n_gemm);
     return hipGetLastError();
 }
@@ -666,13 +680,16 @@ hipError_t launch_fwd_fused(int cell, const RecPlan &p, const RecArgs &a, const 
     if (p.kind != kRecMfma || a.Dh != 128 || !a.ready || !g.ready || n_gemm <= 0 ||
         !gemm_dma_ok(g.K))
         return hipErrorInvalidValue;
+    if (p.BT == 1)
+        return cell == kLSTM ? launch_fused_t<kLSTM, 1, 8, false>(p, a, g, n_gemm, s)
+                             : launch_fused_t<kGRU, 1, 8, false>(p, a, g, n_gemm, s);
     switch (p.upt) {
-        case 1: return cell == kLSTM ? launch_fused_t<kLSTM, 1, 8>(p, a, g, n_gemm, s)
-                                     : launch_fused_t<kGRU, 1, 8>(p, a, g, n_gemm, s);
-        case 2: return cell == kLSTM ? launch_fused_t<kLSTM, 2, 4>(p, a, g, n_gemm, s)
-                                     : launch_fused_t<kGRU, 2, 4>(p, a, g, n_gemm, s);
-        default: return cell == kLSTM ? launch_fused_t<kLSTM, 4, 2>(p, a, g, n_gemm, s)
-                                      : launch_fused_t<kGRU, 4, 2>(p, a, g, n_gemm, s);
+        case 1: return cell == kLSTM ? launch_fused_t<kLSTM, 1, 4, true>(p, a, g, n_gemm, s)
+                                     : launch_fused_t<kGRU, 1, 4, true>(p, a, g, n_gemm, s);
+        case 2: return cell == kLSTM ? launch_fused_t<kLSTM, 2, 2, true>(p, a, g, n_gemm, s)
+                                     : launch_fused_t<kGRU, 2, 2, true>(p, a, g, n_gemm, s);
+        default: return cell == kLSTM ? launch_fused_t<kLSTM, 4, 2, false>(p, a, g, n_gemm, s)
+                                      : launch_fused_t<kGRU, 4, 2, false>(p, a, g, n_gemm, s);
     }
 }
 

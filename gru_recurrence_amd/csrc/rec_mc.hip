@@ -48,12 +48,9 @@ namespace rnn355 {
 
 namespace {
 
-// RL: batch rows in lane groups.  The MFMA leaves row 4p + r of the tile in
-// register r of lane group p; RL transposes that 4 x 4 block per gate (two
-// 16-lane and two 32-lane swaps) so that pass p holds row 4p + q in lane
-// group q, and each cell update pass serves four rows at once: R4 passes
-// cover 4 R4 rows (the slot layout runs one pass per register, four passes
-// for any tile of more than two rows).
+// RL: batch rows in lane groups (gate_update_lanes): each cell update pass
+// serves four rows at once, R4 passes cover 4 R4 rows (the slot layout runs
+// one pass per register, four passes for any tile of more than two rows).
 template <int CELL, int KCW, int R4, bool RL = false>
 __global__ __launch_bounds__(512) void rec_fwd_mc_kernel(McArgs m) {
     constexpr int G = CellTraits<CELL>::G;
@@ -220,32 +217,7 @@ __global__ __launch_bounds__(512) void rec_fwd_mc_kernel(McArgs m) {
         if (gate_wave) {
             float h[R4], c[R4];
             if constexpr (RL) {
-                // pass p, lane group q <- register q of lane group p (row 4p + q)
-                float v[R4][G];
-#pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    const RowPair p = swap16(acc[g][0], acc[g][1]);
-                    const RowPair q = swap16(acc[g][2], acc[g][3]);
-                    const RowPair x = swap32(p.a, q.a);  // passes 0, 2
-                    v[0][g] = x.a;
-                    if constexpr (R4 > 1) {
-                        const RowPair y = swap32(p.b, q.b);  // passes 1, 3
-                        v[1][g] = y.a;
-                        if constexpr (R4 > 2) {
-                            v[2][g] = x.b;
-                            v[3][g] = y.b;
-                        }
-                    }
-                }
-#pragma unroll
-                for (int r = 0; r < R4; ++r) {
-                    float pre[G];
-#pragma unroll
-                    for (int g = 0; g < G; ++g)
-                        pre[g] = (CELL == kGRU && g == 2) ? v[r][g] : v[r][g] + gxr[r][g];
-                    h[r] = unit_update<CELL>(pre, CELL == kGRU ? gxr[r][2] : 0.f, st[r], c[r]);
-                    hl[r] = h[r];
-                }
+                gate_update_lanes<CELL, R4>(acc, gxr, st, hl, h, c);
             } else {
                 gate_update<CELL, R4>(acc, gxr, st, hl, h, c);
             }

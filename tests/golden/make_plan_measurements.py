@@ -97,6 +97,14 @@ POINTS = [
                                        "RNN355_MC_ROWLANES": "0"}),
     ("lstm", 512, 16, 1, 384, "bf16", {"RNN355_REC_BT": "8"}),
     ("lstm", 512, 16, 1, 384, "bf16", {"RNN355_REC_BT": "8", "RNN355_MC_ROWLANES": "0"}),
+    # one CU per (head, rows), rows in lane groups (2 to 8 rows per workgroup)
+    ("lstm", 1024, 16, 6, 128, "bf16", {"RNN355_REC_BT": "8"}),
+    ("lstm", 512, 64, 12, 64, "bf16", {"RNN355_REC_BT": "8"}),
+    ("lstm", 512, 64, 12, 128, "bf16", {"RNN355_REC_BT": "8"}),
+    ("lstm", 512, 64, 12, 32, "bf16", {"RNN355_REC_BT": "2"}),
+    ("gru", 512, 64, 12, 64, "bf16", {"RNN355_REC_BT": "8"}),
+    ("gru", 512, 64, 12, 64, "bf16", {"RNN355_REC_BT": "1"}),
+    ("lstm", 512, 64, 12, 64, "bf16", {"RNN355_REC_BT": "1"}),
 ]
 
 ABOUT = (

@@ -125,6 +125,29 @@ def test_gru_bf16_tiles_and_ragged(Dh, bt):
     compare(run_gru(c), oracle_of(c), TOL_BF16, ("h_seq", "hT"))
 
 
+@pytest.mark.parametrize("cell", ["lstm", "gru"])
+@pytest.mark.parametrize("Dh", [32, 64, 128])
+@pytest.mark.parametrize("bt", [2, 4, 5, 8, 9, 16])
+def test_rows_per_workgroup_layouts(cell, Dh, bt):
+    """Batch tiles of the one-CU kernel in every row layout: 2 to 4 rows (one
+    cell update pass over rows in lane groups), 5 to 8 (two passes), 9 to 16
+    (four register row slots); B = 13 leaves a ragged last tile."""
+    os.environ["RNN355_REC_BT"] = str(bt)
+    d = synth.Dims(T=23, B=13, Din=64, NH=2, Dh=Dh)
+    op = g.OP_FWD_LSTM if cell == "lstm" else g.OP_FWD_GRU
+    plan = g.plan_describe(op, g.Dims(d.T, d.B, d.Din, d.NH, d.Dh), g.RNN_BF16)
+    print("  plan:", plan, flush=True)
+    rows = min(bt, d.B)
+    assert "mfma_resident_R rows_per_wg=%d " % rows in plan
+    passes = 1 if rows <= 4 else 2 if rows <= 8 else 4
+    assert "units_per_thread=%d " % passes in plan
+    c = synth.make_case(cell, d, "bf16", 5300 + 7 * bt + Dh, bias="forget+1" if cell == "lstm" else "zero",
+                        h0_var=0.2, c0_var=0.2 if cell == "lstm" else 0.0)
+    got = run_lstm(c) if cell == "lstm" else run_gru(c)
+    keys = ("h_seq", "c_seq", "hT", "cT") if cell == "lstm" else ("h_seq", "hT")
+    compare(got, oracle_of(c), TOL_BF16, keys)
+
+
 @pytest.mark.parametrize("cell,dtype,Dh", [("gru", "f32", 32), ("lstm", "f32", 48),
                                            ("lstm", "bf16", 48), ("gru", "bf16", 16)])
 def test_lds_kernel_shapes(cell, dtype, Dh):
@@ -294,3 +317,39 @@ def test_pipelined_forward_reads_fresh_projection_after_reuse():
     torch.cuda.synchronize()
     assert torch.equal(h2, serial[0]) and torch.equal(cT2, serial[3])
 
+
+
+@pytest.mark.parametrize("cell,B,NH,Dh,dtype,bt", [
+    ("lstm", 3, 2, 64, "bf16", None),    # one row per workgroup
+    ("gru", 8, 2, 64, "bf16", "4"),      # rows in lane groups
+    ("lstm", 3, 2, 32, "f32", None),     # LDS kernel
+])
+def test_recurrence_status_is_ok_on_a_workspace_holding_garbage(cell, B, NH, Dh, dtype, bt):
+    """The recurrence entry points clear the workspace status word
+    themselves: a workspace filled with nonzero bytes reports RNN_OK after a
+    call whose kernels never wait (regression: the one-CU and LDS paths left
+    the word as it was)."""
+    T = 9
+    G = synth.gates_of(cell)
+    old = os.environ.pop("RNN355_REC_BT", None)
+    if bt:
+        os.environ["RNN355_REC_BT"] = bt
+    try:
+        gen = torch.Generator(device="cuda").manual_seed(5)
+        gx = torch.randn((T, B, NH * G * Dh), device="cuda", generator=gen)
+        R = torch.randn((NH, Dh, G * Dh), device="cuda", generator=gen) / Dh ** 0.5
+        if dtype == "bf16":
+            R = R.to(torch.bfloat16)
+        op = g.OP_REC_LSTM if cell == "lstm" else g.OP_REC_GRU
+        dt = g.RNN_BF16 if dtype == "bf16" else g.RNN_F32
+        ws = torch.full((g.workspace_size(op, g.Dims(T, B, 64, NH, Dh), dt),), 0xA5,
+                        dtype=torch.uint8, device="cuda")
+        if cell == "lstm":
+            g.rec_lstm(gx, R, ws=ws)
+        else:
+            g.rec_gru(gx, R, ws=ws)
+        assert g.workspace_status(ws) == g.RNN_OK
+    finally:
+        os.environ.pop("RNN355_REC_BT", None)
+        if old is not None:
+            os.environ["RNN355_REC_BT"] = old
