@@ -330,13 +330,9 @@ rnn_status rec_fwd(int cell, const rnn_dims *d, rnn_dtype dt, const float *gx, c
         e = launch_rec_mc(cell, ch.mc, m, s, clear_status);
     } else {
         // these kernels never wait, so nothing else writes the status word:
-        // clear it here, or a fresh workspace would report what it held
-        if (clear_status) {
-            hipLaunchKernelGGL(status_word_kernel, dim3(1), dim3(64), 0, s, (unsigned *)ws,
-                               (unsigned *)nullptr);
-            e = hipGetLastError();
-            if (e != hipSuccess) return RNN_ERR_HIP;
-        }
+        // their workgroup 0 clears it, or a fresh workspace would report
+        // what it held
+        a.clear_word = clear_status ? (unsigned *)ws : nullptr;
         a.BT = ch.rec.BT;
         e = launch_rec_fwd(cell, ch.rec, a, dt == RNN_BF16, s);
     }

@@ -95,6 +95,10 @@ struct RecArgs {
     int panels;
     unsigned *flag;       // abort word, set when a wait runs out
     unsigned spin_limit;  // polls before a wait is declared lost
+    // Kernels that never wait: if set, workgroup 0 zeroes this status word
+    // at its start (no other workgroup writes it), so the call reports RNN_OK
+    // on a workspace that held anything.
+    unsigned *clear_word;
 };
 
 enum RecKind { kRecNone = 0, kRecMfma = 1, kRecSimple = 2 };

@@ -129,6 +129,7 @@ __device__ __forceinline__ void rec_fwd_mfma_body(const RecArgs &a, const int bl
 
     __shared__ __attribute__((aligned(16))) uint16_t hbuf[2][16 * HLD];
 
+    if (a.clear_word && blk == 0 && threadIdx.x == 0) *a.clear_word = 0u;
     const int n = blk % a.NH;
     const int b0 = (blk / a.NH) * a.BT;
     const int rows = min(a.BT, a.B - b0);
@@ -520,6 +521,7 @@ __global__ __launch_bounds__(256) void rec_fwd_simple_kernel(RecArgs a) {
     float *hs = cs + BT * DH;
     float *gs = hs + BT * DH;
 
+    if (a.clear_word && blockIdx.x == 0 && threadIdx.x == 0) *a.clear_word = 0u;
     const int n = blockIdx.x % a.NH;
     const int b0 = (blockIdx.x / a.NH) * BT;
     const int rows = min(BT, a.B - b0);
