@@ -271,6 +271,30 @@ def test_pipelined_forward_matches_serial_bitwise_and_oracle(cell, T, B, NH, Dh,
     compare(piped, oracle_of(c), TOL_BF16, keys)
 
 
+@pytest.mark.parametrize("cell", ["lstm", "gru"])
+@pytest.mark.parametrize("bt", [3, 8, 12])
+def test_pipelined_forward_row_layouts_match_serial_bitwise(cell, bt):
+    """The one-launch forward with several batch rows per recurrence
+    workgroup (rows in lane groups, one and two passes; register row slots)
+    gives bitwise the serial result, which matches the oracle."""
+    d = synth.Dims(T=70, B=24, Din=64, NH=2, Dh=128)
+    op = g.OP_FWD_LSTM if cell == "lstm" else g.OP_FWD_GRU
+    gd = g.Dims(d.T, d.B, d.Din, d.NH, d.Dh)
+    os.environ["RNN355_REC_BT"] = str(bt)
+    plan = _with_env("RNN355_PIPELINE", "1", lambda: g.plan_describe(op, gd, g.RNN_BF16))
+    print("  plan:", plan, flush=True)
+    assert "rows_per_wg=%d " % bt in plan and "input_proj=pipelined" in plan
+    c = synth.make_case(cell, d, "bf16", 7700 + bt, bias="forget+1" if cell == "lstm" else "zero",
+                        h0_var=0.1, c0_var=0.1 if cell == "lstm" else 0.0)
+    run = run_lstm if cell == "lstm" else run_gru
+    piped = _with_env("RNN355_PIPELINE", "1", lambda: run(c))
+    serial = _with_env("RNN355_PIPELINE", "0", lambda: run(c))
+    for k in piped:
+        assert np.array_equal(piped[k], serial[k]), k
+    keys = ("h_seq", "c_seq", "hT", "cT") if cell == "lstm" else ("h_seq", "hT")
+    compare(piped, oracle_of(c), TOL_BF16, keys)
+
+
 def test_pipelined_headline_forward_repeatable_and_equal_to_serial():
     """Full-size multi-head LSTM (B=16, NH=6, Dh=128, T=1024): three pipelined
     calls on one workspace (panel counters reused) and one serial call agree
