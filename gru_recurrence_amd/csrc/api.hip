@@ -4,6 +4,7 @@
 
 #include <cstdio>
 #include <cstdlib>
+#include <cmath>
 #include <cstring>
 #include <algorithm>
 #include <mutex>
@@ -76,7 +77,7 @@ size_t wt_bytes(const rnn_dims *d, int G) {
 // R staged transposed per head ([NH][G*Dh][Dh] bf16) for the Dh = 256
 // one-CU recurrence; sized for every bf16 shape with Dh = 256.
 size_t rt_fwd_bytes(const rnn_dims *d, rnn_dtype dt, int G) {
-    if (dt != RNN_BF16 || d->Dh != 256) return 0;
+    if (dt != RNN_BF16 || (d->Dh != 256 && d->Dh != 128)) return 0;
     return align_up(sizeof(uint16_t) * (size_t)d->NH * G * d->Dh * d->Dh);
 }
 
@@ -377,6 +378,48 @@ int proj_workgroups(const rnn_dims *d, const Choice &ch, int tiles_per_panel, in
     return std::max(8, std::min(cap, (int)((need + 4) / 8) * 8));
 }
 
+// Row panels of gx that the recurrence's workgroups of the pipelined
+// forward compute themselves before their first step (RecArgs::hs_*), so
+// that they start without waiting for the projection's first round of
+// tiles (about 40 ns per unit of K per tile, as in proj_workgroups): the
+// fewest panels whose head start and steps last that long at the plan's
+// step time, or as many as fit -- whole steps per panel run (kGemmRowTile *
+// P % B == 0), at
+// most kHeadStartRows rows per workgroup, x 16-byte aligned, and a panel
+// left to the projection.
+// RNN355_HEAD_START=P asks for P panels instead (0: none), within the same
+// limits.
+int head_start_panels(const Choice &ch, const rnn_dims *d, const void *x) {
+    const long panels = gx_panels(d);
+    if (x && ((uintptr_t)x & 15) != 0) return 0;
+    auto fits = [&](int p) {
+        if (p >= panels || ((long)kGemmRowTile * p) % d->B != 0) return false;
+        const long rows = (long)kGemmRowTile * p / d->B * std::min(ch.rec.BT, d->B);
+        return rows <= kHeadStartRows;
+    };
+    const char *e = getenv("RNN355_HEAD_START");
+    if (e && e[0]) {
+        const int want = atoi(e);
+        int best = 0;
+        for (int p = 1; p <= want && p < panels; ++p)
+            if (fits(p)) best = p;
+        return best;
+    }
+    // the head start itself takes ~22 ns per unit of K for one 32-row block,
+    // ~28 for two (measured at Din = 768 beside the projection)
+    const double first_round = 40.0 * d->Din, step = std::max(ch.cand.ns_step, 1.0);
+    int best = 0;
+    for (int p = 1; p < panels; ++p) {
+        if (!fits(p)) continue;
+        best = p;
+        const long steps = (long)kGemmRowTile * p / d->B;
+        const long rows = steps * std::min(ch.rec.BT, d->B);
+        const double hs_ns = (rows > 32 ? 28.0 : 22.0) * d->Din;
+        if (hs_ns + steps * step >= first_round) break;
+    }
+    return best;
+}
+
 // Forward = input projection + recurrence.  Pipelined (see pipelined()): one
 // launch whose first workgroups compute the projection in time order and
 // count finished 256-row panels of gx, while the recurrence's workgroups
@@ -399,28 +442,43 @@ rnn_status forward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, con
         auto ok = [](hipError_t e) { return e == hipSuccess; };
         // W^T for the k-major contraction; the same launch zeroes the status
         // words of the header and the panel counters
+        // and R^T per head (16-byte fragment loads in the recurrence)
+        uint16_t *rt = (uint16_t *)((char *)wt + wt_bytes(d, G));
         if (!ok(launch_transpose_bf16((const uint16_t *)W, wt, d->Din, N, 1, s,
-                                      clear_status ? (unsigned *)ws : nullptr, 64, ready, panels)))
+                                      clear_status ? (unsigned *)ws : nullptr, 64, ready, panels,
+                                      (const uint16_t *)R, rt, d->Dh, G * d->Dh, d->NH)))
             return RNN_ERR_HIP;
+        // the first hs panels come from the recurrence's workgroups
+        const int hs = head_start_panels(ch, d, x);
+        const long hs_rows = (long)hs * kGemmRowTile;
         GemmArgs g{};
-        g.M = M; g.N = N; g.K = d->Din;
-        g.A = (const uint16_t *)x; g.lda = d->Din;
+        g.M = (int)(M - hs_rows); g.N = N; g.K = d->Din;
+        g.A = (const uint16_t *)x + hs_rows * d->Din; g.lda = d->Din;
         g.B = wt; g.ldb = d->Din;
-        g.bias = b; g.C = gx; g.ldc = N;
+        g.bias = b; g.C = gx + hs_rows * N; g.ldc = N;
         g.ksplit = 1;
-        g.ready = ready;
+        g.ready = ready + hs;
         RecArgs a{};
         a.T = d->T; a.B = d->B; a.NH = d->NH; a.Dh = d->Dh; a.BT = ch.rec.BT;
         a.gx = gx;
         a.Rb = (const uint16_t *)R;
+        a.Rt = rt;
         a.h0 = h0; a.c0 = c0; a.h_seq = h_seq; a.c_seq = c_seq; a.hT = hT; a.cT = cT;
         a.ready = ready;
         a.ready_target = (unsigned)((N + kGemmColTile - 1) / kGemmColTile);  // tiles per panel
         a.panels = (int)panels;
         a.flag = (unsigned *)ws;
         a.spin_limit = spin_limit();
+        if (hs > 0) {
+            a.hs_panels = hs;
+            a.hs_steps = (int)(hs_rows / d->B);
+            a.hs_K = d->Din;
+            a.hs_x = (const uint16_t *)x;
+            a.hs_wt = wt;
+            a.hs_bias = b;
+        }
         // projection workgroups by rate (proj_workgroups), at most one per tile
-        const long tiles = panels * a.ready_target;
+        const long tiles = (panels - hs) * a.ready_target;
         int n_gemm = proj_workgroups(d, ch, (int)a.ready_target, cus - ch.rec.grid);
         if (n_gemm > tiles) n_gemm = (int)tiles;
         if (n_gemm < 8) n_gemm = (int)std::min<long>(8, tiles);
@@ -729,8 +787,9 @@ rnn_status backward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, co
     if (lstm && GD % kGemmColTile == 0 && gemm_dma_ok(Din) && gemm_dma_ok(Dh)) {
         // one contraction: the K tiles of x W^T, then for the column tiles of
         // head n those of h_{t-1}[:, n Dh:(n+1) Dh] R_n (R^T per head)
-        if (!ok(launch_transpose_bf16(Wb, wt, Din, N, 1, stream))) return RNN_ERR_HIP;
-        if (!ok(launch_transpose_bf16(Rb, rt, Dh, GD, NH, stream))) return RNN_ERR_HIP;
+        if (!ok(launch_transpose_bf16(Wb, wt, Din, N, 1, stream, nullptr, 0, nullptr, 0, Rb, rt,
+                                      Dh, GD, NH)))
+            return RNN_ERR_HIP;
         GemmArgs g{};
         g.M = M; g.N = N; g.K = Din;
         g.A = xb; g.lda = Din;
@@ -1178,10 +1237,12 @@ rnn_status rnn_plan_describe(rnn_op op, const rnn_dims *d, rnn_dtype dt, char *b
         return RNN_ERR_UNSUPPORTED;
     }
     const bool fwd = op == RNN_OP_FWD_LSTM || op == RNN_OP_FWD_GRU;
-    char proj[96];
-    snprintf(proj, sizeof proj, " predicted_ns_per_step=%.0f%s", ch.cand.ns_total / d->T,
-             !fwd ? "" : pipelined(ch, d, dt, device_cus()) ? " input_proj=pipelined"
-                                                            : " input_proj=serial");
+    char proj[128];
+    const bool piped = fwd && pipelined(ch, d, dt, device_cus());
+    char hs[32] = "";
+    if (piped) snprintf(hs, sizeof hs, " head_start_panels=%d", head_start_panels(ch, d, nullptr));
+    snprintf(proj, sizeof proj, " predicted_ns_per_step=%.0f%s%s", ch.cand.ns_total / d->T,
+             !fwd ? "" : piped ? " input_proj=pipelined" : " input_proj=serial", hs);
     if (ch.use_wide) {
         const WidePlan &p = ch.wide;
         snprintf(buf, len,

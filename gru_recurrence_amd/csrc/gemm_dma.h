@@ -21,8 +21,6 @@ constexpr int ROWB = BK * 2;                 // bytes per LDS row
 constexpr int OPB = BM * ROWB;               // bytes per operand per stage (16 KiB)
 constexpr int STB = 2 * OPB;                 // bytes per stage (32 KiB)
 constexpr size_t LDS_BYTES = (size_t)NST * STB;
-constexpr int NST_ALONE = 5;  // the stand-alone kernel: the whole 160 KiB
-constexpr size_t LDS_BYTES_ALONE = (size_t)NST_ALONE * STB;
 static_assert(BM == kGemmRowTile && BN == kGemmColTile, "row-panel counters assume the output tile");
 
 // Row r of a tile keeps its k chunk c (16 bytes) in slot c ^ swz(r): any 16
@@ -50,32 +48,55 @@ __device__ __forceinline__ void tile_offsets(long ld, int r0, int R, int tid, ui
         off[i] = (uint32_t)(((long)gr * ld + chunk * 8) * 2);
     }
 }
-template <int AUX = 0>
-__device__ __forceinline__ void dma_tile(const uint16_t *__restrict__ P, int k0, const uint32_t (&off)[2],
-                                         lds_char *dst, int wave_s) {
-    const char *base = reinterpret_cast<const char *>(P + k0);
+// The loads of a pair of K tiles: per operand and load slot, tile t0's
+// load (16 bytes at k0 of each of its rows) and at once tile t1's (the next
+// 64 bytes: with k0 a multiple of 64 elements, the other half of the same
+// 128-byte lines), so each line crosses from L2 once -- a tile's 64-byte
+// rows loaded a tile apart halve what the chip's L2 delivers per CU.  Order:
+// A t0, A t1, A t0, A t1, B t0, B t1, B t0, B t1 (t1's loads only if
+// `second`): one load follows the last of t0's.  A's source may differ
+// between the two tiles (a second K segment begins at t1).
+template <int AUX>
+__device__ __forceinline__ void dma_pair(const uint16_t *A0, const uint32_t (&oA0)[2],
+                                         const uint16_t *A1, const uint32_t (&oA1)[2],
+                                         const uint16_t *B0, const uint32_t (&oB0)[2],
+                                         const uint16_t *B1, const uint32_t (&oB1)[2],
+                                         lds_char *s0, lds_char *s1, bool second, int wave_s) {
+    const char *a0 = reinterpret_cast<const char *>(A0), *a1 = reinterpret_cast<const char *>(A1);
+    const char *b0 = reinterpret_cast<const char *>(B0), *b1 = reinterpret_cast<const char *>(B1);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-        __builtin_amdgcn_global_load_lds(base + off[i], dst + (64 * wave_s + NTHR * i) * 16, 16, 0,
-                                         AUX);
+    for (int i = 0; i < 2; ++i) {
+        const int d = (64 * wave_s + NTHR * i) * 16;
+        __builtin_amdgcn_global_load_lds(a0 + oA0[i], s0 + d, 16, 0, AUX);
+        if (second) __builtin_amdgcn_global_load_lds(a1 + oA1[i], s1 + d, 16, 0, AUX);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int d = OPB + (64 * wave_s + NTHR * i) * 16;
+        __builtin_amdgcn_global_load_lds(b0 + oB0[i], s0 + d, 16, 0, 0);
+        if (second) __builtin_amdgcn_global_load_lds(b1 + oB1[i], s1 + d, 16, 0, 0);
+    }
 }
 
-// vmcnt(4 * later): the loads of `later` later tiles may stay in flight.
-__device__ __forceinline__ void wait_tiles_after(int later) {
-    if (later >= 3) __builtin_amdgcn_s_waitcnt(0x0F7C);       // vmcnt(12)
-    else if (later == 2) __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
-    else if (later == 1) __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
-    else __builtin_amdgcn_s_waitcnt(0x0F70);                  // vmcnt(0)
+// vmcnt(n) for the counts the pair schedule needs (n in {0, 1, 4, 5, 8, 9});
+// any other n waits for everything.
+__device__ __forceinline__ void wait_vm(int n) {
+    if (n == 9) __builtin_amdgcn_s_waitcnt(0x0F79);
+    else if (n == 8) __builtin_amdgcn_s_waitcnt(0x0F78);
+    else if (n == 5) __builtin_amdgcn_s_waitcnt(0x0F75);
+    else if (n == 4) __builtin_amdgcn_s_waitcnt(0x0F74);
+    else if (n == 1) __builtin_amdgcn_s_waitcnt(0x0F71);
+    else __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
 // The contraction's work for workgroup `wg` of `nwg`: output tiles wg,
 // wg + nwg, ... of batch / split slice blockIdx.z (a persistent loop when
-// nwg is smaller than the tile count).  `lds` is NS * STB bytes of dynamic
-// LDS: a ring of NS K tiles (NS - 1 in flight).  Before each tile every
+// nwg is smaller than the tile count).  `lds` is LDS_BYTES of dynamic LDS:
+// a ring of four K tiles, loaded in pairs.  Before each tile every
 // thread calls pre(row tile), ahead of the barrier that starts the tile (a
 // wait for A's rows goes there); A_AUX is the cache policy of A's loads.
 // SEG2: the K tiles of the second segment (A2, B2) follow those of A, B.
-template <int A_AUX, int NS = NST, bool SEG2 = false, class PreTile>
+template <int A_AUX, bool SEG2 = false, class PreTile>
 __device__ __forceinline__ void gemm_dma_tiles_pre(const GemmArgs &g, int wg, int nwg,
                                                    lds_char *lds, PreTile &&pre) {
     const uint32_t lbase = (uint32_t)(uintptr_t)lds;
@@ -158,43 +179,32 @@ __device__ __forceinline__ void gemm_dma_tiles_pre(const GemmArgs &g, int wg, in
         tile_offsets(g.lda2, m0, g.M, tid, goA2);
         tile_offsets(g.ldb2, n0, g.N, tid, goB2);
     }
-    // SEG2: the second segment's offsets replace the first's when its first
-    // K tile is issued (K tiles are issued in order)
-    auto issue = [&](int kt, int stage) {
-        lds_char *st = lds + stage * STB;
-        if (SEG2 && kt == ktiles1) {
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                goA[i] = goA2[i];
-                goB[i] = goB2[i];
-            }
-        }
-        if (!SEG2 || kt < ktiles1) {
-            dma_tile<A_AUX>(A, kt * BK, goA, st, wave_s);
-            dma_tile(B, kt * BK, goB, st + OPB, wave_s);
-        } else {
-            const int k2 = (kt - ktiles1) * BK;
-            dma_tile<A_AUX>(A2, k2, goA, st, wave_s);
-            dma_tile(g.B2, k2, goB, st + OPB, wave_s);
-        }
+    // K tiles go out in pairs (tiles kt0 + j, kt0 + j + 1, j even) into a
+    // ring of four stages: tile kt0 + j in stage j % 4.  Pairs 0 and 1 go out
+    // before the loop, pair j/2 + 1 at the barrier of tile kt0 + j (j >= 2
+    // even), into the stages of tiles kt0 + j - 2 and kt0 + j - 1, which every
+    // wave has finished reading by then.
+    auto issue_pair = [&](int j) {
+        const int t0 = kt0 + j, t1 = t0 + 1;
+        const bool second = t1 < kt1;
+        lds_char *s0 = lds + (j & 3) * STB, *s1 = lds + ((j + 1) & 3) * STB;
+        // a tile's source: segment 1 (A, B at k = 32 kt) or segment 2
+        const bool g20 = SEG2 && t0 >= ktiles1, g21 = SEG2 && t1 >= ktiles1;
+        const int k0 = (g20 ? t0 - ktiles1 : t0) * BK, k1 = (g21 ? t1 - ktiles1 : t1) * BK;
+        const uint16_t *a0 = (g20 ? A2 : A) + k0, *a1 = (g21 ? A2 : A) + k1;
+        const uint16_t *b0 = (g20 ? g.B2 : B) + k0, *b1 = (g21 ? g.B2 : B) + k1;
+        dma_pair<A_AUX>(a0, g20 ? goA2 : goA, a1, g21 ? goA2 : goA, b0, g20 ? goB2 : goB, b1,
+                        g21 ? goB2 : goB, s0, s1, second, wave_s);
     };
-    if (SEG2 && kt0 > ktiles1) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            goA[i] = goA2[i];
-            goB[i] = goB2[i];
-        }
-    }
-#pragma unroll
-    for (int p = 0; p < NS - 1; ++p)
-        if (kt0 + p < kt1) issue(kt0 + p, p);
+    // loads a pair puts out (4 per tile and thread)
+    auto pair_loads = [&](int j) { return kt0 + j >= kt1 ? 0 : kt0 + j + 1 < kt1 ? 8 : 4; };
+    if (kt0 < kt1) issue_pair(0);
+    if (kt0 + 2 < kt1) issue_pair(2);
 
     // Pipelined at k-step granularity (two 16-deep k-steps per tile): the
     // reads of the next k-step are in flight while the current one's MFMAs
     // run, and the barrier that makes tile kt+1 visible sits between tile
-    // kt's two k-steps, so its wait overlaps MFMAs already issued.  The
-    // stage refilled at that barrier is the one tile kt-1 used: every wave's
-    // reads of it completed before its MFMAs of kt-1, i.e. before the barrier.
+    // kt's two k-steps, so its wait overlaps MFMAs already issued.
 #define RNN355_READ_HALF(stage, kc, a0, a1, a2, a3, b0, b1)                                  \
     do {                                                                                     \
         const uint32_t sb_ = lbase + (uint32_t)((stage) * STB);                              \
@@ -224,39 +234,35 @@ __device__ __forceinline__ void gemm_dma_tiles_pre(const GemmArgs &g, int wg, in
                 *a_[i_], *b_[j_], (ZERO) ? f32x16{} : acc[i_][j_], 0, 0, 0);                 \
     } while (0)
 
-    // tile kt0: landed for everyone
-    wait_tiles_after(min(NS - 2, kt1 - 1 - kt0));
+    // tile kt0 landed for everyone: after its last load, one of its pair's
+    // second tile and pair 1's may fly
+    wait_vm(pair_loads(0) == 8 ? 1 + pair_loads(2) : 0);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     bf16x8 x0, x1, x2, x3, x4, x5, y0, y1, y2, y3, y4, y5;
-    // ring stages: `cur` holds tile kt, `prev` tile kt-1 (refilled with kt-1+NS)
-    int cur = 0, prev = NS - 1;
-    RNN355_READ_HALF(cur, 0, x0, x1, x2, x3, x4, x5);
+    RNN355_READ_HALF(0, 0, x0, x1, x2, x3, x4, x5);
     auto ktile = [&](int kt, auto first) {
         constexpr bool F = decltype(first)::value;
+        const int j = kt - kt0, cur = j & 3, nxt = (j + 1) & 3;
         RNN355_READ_HALF(cur, 1, y0, y1, y2, y3, y4, y5);
         RNN355_MFMA_HALF(6, F, x0, x1, x2, x3, x4, x5);
         const bool more = kt + 1 < kt1;
-        const int nxt = cur + 1 == NS ? 0 : cur + 1;
         if (more) {
-            // this thread's loads of tile kt+1 landed (later tiles may fly);
-            // after the barrier everyone's have
-            const int later = min(NS - 3, kt1 - 2 - kt);
-            wait_tiles_after(later < 0 ? 0 : later);
+            // this thread's loads of tile kt+1 landed; after the barrier
+            // everyone's have.  Still in flight after them: at j = 0 pair 1;
+            // j odd (kt+1 opens pair (j+1)/2): that pair's last load; j even:
+            // nothing (the next pair goes out after the barrier)
+            wait_vm(j == 0 ? pair_loads(2) : (j & 1) ? (pair_loads(j + 1) == 8 ? 1 : 0) : 0);
             asm volatile("" ::: "memory");
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
+            if (j >= 2 && !(j & 1) && kt + 2 < kt1) issue_pair(j + 2);
         }
         // the next tile's first k-step (the last tile re-reads its own, unused,
         // so that the count of reads behind y stays six on every path)
         RNN355_READ_HALF(more ? nxt : cur, 0, x0, x1, x2, x3, x4, x5);
         RNN355_MFMA_HALF(6, false, y0, y1, y2, y3, y4, y5);
-        // refill the stage of tile kt-1 (at kt0: the stage the prologue
-        // left empty) with tile kt-1+NS
-        if (more && kt - 1 + NS < kt1) issue(kt - 1 + NS, prev);
-        prev = cur;
-        cur = nxt;
     };
     if (kt0 < kt1) {
         ktile(kt0, std::integral_constant<bool, true>{});
@@ -349,7 +355,7 @@ __device__ __forceinline__ void gemm_dma_tiles_pre(const GemmArgs &g, int wg, in
 // The ring of NST stages (LDS_BYTES): the kernels that share a CU's LDS
 // with a recurrence.
 __device__ __forceinline__ void gemm_dma_tiles(const GemmArgs &g, int wg, int nwg, lds_char *lds) {
-    gemm_dma_tiles_pre<0, NST>(g, wg, nwg, lds, [](int) {});
+    gemm_dma_tiles_pre<0>(g, wg, nwg, lds, [](int) {});
 }
 
 }  // namespace dma

@@ -10,15 +10,17 @@
 //
 // Block tile 256x256, K in tiles of 32, 512 threads = 8 waves in a 2 (m) x 4
 // (n) grid, each wave 128x64 = 4x2 tiles of v_mfma_f32_32x32x16_bf16.  LDS
-// holds a ring of K tiles (32 KiB each: five in this kernel, the whole 160
-// KiB; four where a recurrence shares the CU); the loads of tile kt+4 (kt+3)
-// are issued right after the barrier that starts tile kt, so four (three)
-// tiles are in flight and no register is spent on staging.  A load
-// instruction moves 16 bytes per lane and writes the wave's 64 lanes as one
-// contiguous KiB of LDS, so a tile is stored without padding: 64-byte rows
-// (32 k), and in row r the 16-byte chunk c of the k range sits in slot
-// c ^ swz(r) (gemm_dma.h): the 16 lanes of one access phase of a fragment
-// read (16 rows, one chunk) touch 16 different bank groups.
+// holds a ring of four K tiles (32 KiB each, 128 KiB).  K tiles are loaded
+// in pairs: a tile's rows are 64 bytes, half of a 128-byte cache line, and
+// the loads of the pair's two tiles go out interleaved from the same waves,
+// so each line crosses from L2 once (a line's halves requested a tile apart
+// are fetched twice, which halves what L2 delivers per CU when every CU
+// streams).  No register is spent on staging.  A load instruction moves 16
+// bytes per lane and writes the wave's 64 lanes as one contiguous KiB of LDS,
+// so a tile is stored without padding: 64-byte rows (32 k), and in row r
+// the 16-byte chunk c of the k range sits in slot c ^ swz(r) (gemm_dma.h):
+// the 16 lanes of one access phase of a fragment read (16 rows, one chunk)
+// touch 16 different bank groups.
 //
 // The fragment reads are inline assembly on purpose: the compiler tracks
 // loads into LDS only coarsely and would otherwise wait for every load in
@@ -39,38 +41,50 @@ namespace {
 
 __global__ __launch_bounds__(NTHR) void gemm_dma_kernel(GemmArgs g) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    gemm_dma_tiles_pre<0, NST_ALONE>(g, blockIdx.x, gridDim.x, (lds_char *)smem, [](int) {});
+    gemm_dma_tiles_pre<0>(g, blockIdx.x, gridDim.x, (lds_char *)smem, [](int) {});
 }
 
 // The same with a second K segment per column block (GemmArgs::A2, B2).
 __global__ __launch_bounds__(NTHR) void gemm_dma_seg2_kernel(GemmArgs g) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    gemm_dma_tiles_pre<0, NST_ALONE, true>(g, blockIdx.x, gridDim.x, (lds_char *)smem,
+    gemm_dma_tiles_pre<0, true>(g, blockIdx.x, gridDim.x, (lds_char *)smem,
                                            [](int) {});
 }
 
 // dst[b][c][r] = src[b][r][c] for bf16 matrices [R][C] (row pitch C), in
 // 64x64 tiles through LDS with 16-byte loads and stores where a row of the
-// tile is whole and aligned (C % 8 == 0 for loads, R % 8 == 0 for stores);
-// grid (ceil(C/64), ceil(R/64), batch).  Block (0,0,0) also zeroes the
-// `nclear` words at `clear` and the `nclear2` at `clear2` (the status words
-// and panel counters of the forward that follows), saving a launch.
-__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t *__restrict__ src,
-                                                             uint16_t *__restrict__ dst, int R,
-                                                             int C, long bstride, unsigned *clear,
+// tile is whole and aligned (C % 8 == 0 for loads, R % 8 == 0 for stores).
+// One launch serves up to two such jobs: a flat grid whose first blocks
+// cover job 0 (ceil(C/64) x ceil(R/64) x batch tiles) and the rest job 1.
+// Block 0 also zeroes the `nclear` words at `clear` and the `nclear2` at
+// `clear2` (the status words and panel counters of the forward that
+// follows), saving a launch.
+struct TJob {
+    const uint16_t *src;
+    uint16_t *dst;
+    int R, C, batch, tx, ty;  // tx, ty: tiles along C and R
+};
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(TJob j0, TJob j1, unsigned *clear,
                                                              long nclear, unsigned *clear2,
                                                              long nclear2) {
     __shared__ __attribute__((aligned(16))) uint16_t t[64][72];
-    const uint16_t *S = src + blockIdx.z * bstride;
-    uint16_t *D = dst + blockIdx.z * bstride;
-    const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
     const int tid = threadIdx.x;
-    if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) {
+    if (blockIdx.x == 0) {
         if (clear)
             for (long i = tid; i < nclear; i += 256) clear[i] = 0u;
         if (clear2)
             for (long i = tid; i < nclear2; i += 256) clear2[i] = 0u;
     }
+    const int n0 = j0.tx * j0.ty * j0.batch;
+    const bool second = (int)blockIdx.x >= n0;
+    const TJob &j = second ? j1 : j0;
+    const int f = second ? (int)blockIdx.x - n0 : (int)blockIdx.x;
+    const int bx = f % j.tx, by = (f / j.tx) % j.ty, bz = f / (j.tx * j.ty);
+    const int R = j.R, C = j.C;
+    const long bstride = (long)R * C;
+    const uint16_t *S = j.src + bz * bstride;
+    uint16_t *D = j.dst + bz * bstride;
+    const int c0 = bx * 64, r0 = by * 64;
     // load: 64 rows x 8 chunks of 8 columns, two chunks per thread
     for (int q = tid; q < 512; q += 256) {
         const int i = q >> 3, cc = (q & 7) * 8;
@@ -111,6 +125,12 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t *__r
     }
 }
 
+TJob tjob(const uint16_t *src, uint16_t *dst, int R, int C, int batch) {
+    TJob j{src, dst, R, C, batch, (C + 63) / 64, (R + 63) / 64};
+    if (!src || batch <= 0) j.batch = 0;
+    return j;
+}
+
 }  // namespace
 
 bool gemm_dma_ok(int K) { return K % BK == 0 && K > 0; }
@@ -129,20 +149,20 @@ hipError_t launch_gemm_dma(const GemmArgs &g0, int batch, hipStream_t s, int max
     static hipError_t attr = hipSuccess;
     std::call_once(once, [] {
         attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_dma_kernel),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES_ALONE);
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
         if (attr == hipSuccess)
             attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_dma_seg2_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)LDS_BYTES_ALONE);
+                                       (int)LDS_BYTES);
     });
     if (attr != hipSuccess) return attr;
     const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
     const int wgs = max_wg > 0 && max_wg < tiles ? max_wg : tiles;
     if (seg2)
-        hipLaunchKernelGGL(gemm_dma_seg2_kernel, dim3(wgs, 1, 1), dim3(NTHR), LDS_BYTES_ALONE, s, g);
+        hipLaunchKernelGGL(gemm_dma_seg2_kernel, dim3(wgs, 1, 1), dim3(NTHR), LDS_BYTES, s, g);
     else
         hipLaunchKernelGGL(gemm_dma_kernel, dim3(wgs, 1, batch * g.ksplit), dim3(NTHR),
-                           LDS_BYTES_ALONE, s, g);
+                           LDS_BYTES, s, g);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || g.ksplit == 1) return e;
     return launch_splitk_reduce(g, batch, s);
@@ -150,9 +170,12 @@ hipError_t launch_gemm_dma(const GemmArgs &g0, int batch, hipStream_t s, int max
 
 hipError_t launch_transpose_bf16(const uint16_t *src, uint16_t *dst, int R, int C, int batch,
                                  hipStream_t s, unsigned *clear, long nclear, unsigned *clear2,
-                                 long nclear2) {
-    dim3 grid((C + 63) / 64, (R + 63) / 64, batch);
-    hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, s, src, dst, R, C, (long)R * C,
+                                 long nclear2, const uint16_t *src1, uint16_t *dst1, int R1,
+                                 int C1, int batch1) {
+    const TJob j0 = tjob(src, dst, R, C, batch), j1 = tjob(src1, dst1, R1, C1, batch1);
+    const long blocks = (long)j0.tx * j0.ty * j0.batch + (long)j1.tx * j1.ty * j1.batch;
+    if (blocks <= 0 || blocks > 0x7fffffffL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, j0, j1,
                        clear, nclear, clear2, nclear2);
     return hipGetLastError();
 }

@@ -37,6 +37,12 @@ struct GemmArgs {
 };
 constexpr int kGemmRowTile = 256;  // rows per output tile of the bf16 contraction
 constexpr int kGemmColTile = 256;  // columns per output tile
+// Dynamic LDS of a workgroup of the pipelined forward: the projection's ring
+// of four 32 KiB K tiles, and more for the ring of a recurrence workgroup's
+// head start (with the recurrence's own 8.5 KiB, within the CU's 160 KiB).
+constexpr int kFusedLdsBytes = 144 * 1024;
+// Rows of gx a recurrence workgroup computes at most in its head start.
+constexpr int kHeadStartRows = 64;
 
 
 // Largest useful K split (a power of two <= what fills num_cu CUs, keeping
@@ -73,10 +79,13 @@ bool gemm_dma_ok(int K);
 // keeps a row tile's column tiles on one XCD).
 hipError_t launch_gemm_dma(const GemmArgs &g, int batch, hipStream_t s, int max_wg = 0);
 // dst[b][c][r] = src[b][r][c], bf16 [R][C] matrices, `batch` of them; the
-// same launch zeroes nclear words at `clear` and nclear2 at `clear2` (if set).
+// same launch zeroes nclear words at `clear` and nclear2 at `clear2` (if set)
+// and, if src1 is set, transposes a second batch (src1 -> dst1, [R1][C1]).
 hipError_t launch_transpose_bf16(const uint16_t *src, uint16_t *dst, int R, int C, int batch,
                                  hipStream_t s, unsigned *clear = nullptr, long nclear = 0,
-                                 unsigned *clear2 = nullptr, long nclear2 = 0);
+                                 unsigned *clear2 = nullptr, long nclear2 = 0,
+                                 const uint16_t *src1 = nullptr, uint16_t *dst1 = nullptr,
+                                 int R1 = 0, int C1 = 0, int batch1 = 0);
 hipError_t launch_gemm_f32(const GemmF32Args &g, int batch, hipStream_t s);
 
 // Forward recurrence (rec_fwd.hip).
@@ -84,6 +93,7 @@ struct RecArgs {
     int T, B, NH, Dh, BT;     // BT: batch rows per workgroup
     const float *gx;          // [T][B][NH*G*Dh]
     const uint16_t *Rb;       // bf16 R (MFMA kernel / bf16 simple kernel)
+    const uint16_t *Rt;       // optional, MFMA kernel: R^T per head [NH][G*Dh][Dh] bf16
     const float *Rf;          // f32 R (f32 simple kernel)
     const float *h0, *c0;
     float *h_seq, *c_seq, *hT, *cT;
@@ -95,6 +105,14 @@ struct RecArgs {
     int panels;
     unsigned *flag;       // abort word, set when a wait runs out
     unsigned spin_limit;  // polls before a wait is declared lost
+    // Head start of the pipelined forward (fused kernel only): each
+    // workgroup computes gx = x W + b itself for its own rows of the first
+    // hs_panels row panels (hs_steps = hs_panels * kGemmRowTile / B steps),
+    // which the projection's workgroups skip.  hs_wt: W^T [N][hs_K] bf16,
+    // hs_x: x [T*B][hs_K] bf16, hs_bias: b [N] or null.  0: none.
+    int hs_panels, hs_steps, hs_K;
+    const uint16_t *hs_x, *hs_wt;
+    const float *hs_bias;
     // Kernels that never wait: if set, workgroup 0 zeroes this status word
     // at its start (no other workgroup writes it), so the call reports RNN_OK
     // on a workspace that held anything.

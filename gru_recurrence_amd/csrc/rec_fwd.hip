@@ -67,6 +67,202 @@ __device__ __forceinline__ void lstm_or_gru_unit(const float *gpre, int DH, cons
     }
 }
 
+// s_waitcnt immediate for vmcnt(n), n < 64, other counters not waited on.
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+// 16 bytes per lane from src into the wave's contiguous KiB at dst (LDS).
+__device__ __forceinline__ void load_lds16(const char *src, dma::lds_char *dst) {
+    __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+
+// The head start's results + b into gx; register r of lane l in block (i,
+// mb) is row mb*32 + 8 (r/4) + 4 (l/32) + r%4, column l%32 of the block
+// (wave w: column blocks w and w + 8, or w twice).  Returns once every
+// wave's stores are complete in L2.
+template <int G, int MB>
+__device__ __forceinline__ void head_start_store(const RecArgs &a, int n, int b0, int rows,
+                                                 const dma::f32x16 (&acc)[2][MB]) {
+    constexpr int GD = G * 128, NB = GD / 32;
+    const int B = a.B, N = a.NH * GD, M = a.hs_steps * rows;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l32 = lane & 31, lh = lane >> 5;
+    const int nb1 = wave + 8;
+    const bool two = nb1 < NB;
+    auto grow = [&](int m) -> long {
+        return rows == 1 ? (long)m * B + b0 : (long)(m / rows) * B + b0 + m % rows;
+    };
+    float *gx = const_cast<float *>(a.gx);
+    const int col0 = n * GD + wave * 32 + l32;
+    const int col1 = two ? n * GD + nb1 * 32 + l32 : col0;  // GRU waves 4-7: block w again
+    const float bv0 = a.hs_bias ? a.hs_bias[col0] : 0.f;
+    const float bv1 = a.hs_bias ? a.hs_bias[col1] : 0.f;
+    if (M == 32 * MB && rows == 1) {
+        // whole blocks, one batch row: stores only, no bounds checks or
+        // branches between them (either makes the compiler wait for every
+        // earlier store first); the GRU's repeated block writes the same bits
+        float *base = gx + (long)b0 * N;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float *row = base + (long)(mb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3)) * B * N;
+                row[col0] = acc[0][mb][r] + bv0;
+                row[col1] = acc[1][mb][r] + bv1;
+            }
+    } else {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = mb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                if (m < M) {
+                    float *row = gx + grow(m) * N;
+                    row[col0] = acc[0][mb][r] + bv0;
+                    if (two) row[col1] = acc[1][mb][r] + bv1;
+                }
+            }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the stores are in L2
+    __syncthreads();
+}
+
+// Head start of the pipelined forward (RecArgs::hs_*; FlashRNN card,
+// abstract: the input part of every gate is one dense contraction over all
+// steps, so any part of it may be computed ahead).  The workgroup of head n
+// and batch rows [b0, b0 + rows), G gates of 128 units, computes gx for its
+// own rows (t, b0 + i), t < hs_steps, i < rows, over its head's G*128
+// columns before its first step: an M x G*128 tile, M = hs_steps * rows <=
+// 32 MB, MB row blocks of 32.  Each value is made as the projection's tile
+// would make it -- v_mfma_f32_32x32x16_bf16 over k-steps of 16 in increasing
+// k order starting from zero, then + b[n] (or + 0) -- so gx is bitwise what
+// the projection would have written.  As in the projection, K tiles of 32
+// (64 rows of x, G*128 rows of W^T, 64 bytes each, 16-byte chunks swizzled)
+// stream into a ring of LDS stages (four for LSTM, five for GRU) by the
+// direct global-to-LDS loads, all but one stage in flight; wave w owns the 32-column blocks w and w + 8 (GRU, 12
+// blocks: waves 4-7 compute block w twice and store it once).  Rows of x past
+// M repeat row M - 1 (their sums are never stored).  Returns once every
+// wave's stores are complete in L2, where the step loop's device-scope loads
+// read.
+template <int G, int MB>
+__device__ __forceinline__ void head_start(const RecArgs &a, int n, int b0, int rows,
+                                           char *smem) {
+    constexpr int GD = G * 128, NB = GD / 32;
+    constexpr int AB = 64 * 64, SB = AB + GD * 64;  // stage: x rows, then W^T rows
+    constexpr int NS = kFusedLdsBytes / SB;          // LSTM 4 stages, GRU 5
+    static_assert(NS >= 3, "the head start's ring needs three stages");
+    using dma::f32x16;
+    const int K = a.hs_K, B = a.B, KT = K >> 5;
+    const int M = a.hs_steps * rows;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    const int l32 = lane & 31, lh = lane >> 5;
+    dma::lds_char *lds = (dma::lds_char *)smem;
+    const uint32_t lbase = (uint32_t)(uintptr_t)lds;
+    // gx / x row of head-start row m: step m / rows, batch row b0 + m % rows
+    auto grow = [&](int m) -> long {
+        return rows == 1 ? (long)m * B + b0 : (long)(m / rows) * B + b0 + m % rows;
+    };
+    // Load sources: a wave's load instruction fills 64 consecutive 16-byte
+    // chunks of a stage; chunk q holds row q/4, k chunk (q%4) ^ swz(row).
+    // x: chunks [0, 256) by waves 0-3; W^T: G instructions per wave.
+    const char *pa;
+    {
+        const int q = 64 * (wave & 3) + lane, r = q >> 2;
+        pa = reinterpret_cast<const char *>(a.hs_x + grow(min(r, M - 1)) * K +
+                                            8 * ((q & 3) ^ dma::swz(r)));
+    }
+    const char *pb[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+        const int q = 64 * (wave * G + i) + lane, r = q >> 2;
+        pb[i] = reinterpret_cast<const char *>(a.hs_wt + (long)(n * GD + r) * K +
+                                               8 * ((q & 3) ^ dma::swz(r)));
+    }
+    auto issue = [&](int kt, int stage) {
+        dma::lds_char *st = lds + stage * SB;
+        const int kb = 64 * kt;
+        if (wave < 4) load_lds16(pa + kb, st + 1024 * wave_s);
+#pragma unroll
+        for (int i = 0; i < G; ++i) load_lds16(pb[i] + kb, st + AB + 1024 * (wave_s * G + i));
+    };
+    // fragment byte offsets in a stage: row l32 of block 0, k chunk 2 kc + lh
+    const int nb1 = wave + 8;
+    const bool two = nb1 < NB;
+    const int sw = dma::swz(l32);
+    uint32_t oa[2], ob[2];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+        const int slot = (2 * kc + lh) ^ sw;
+        oa[kc] = (uint32_t)(l32 * 64 + slot * 16);
+        ob[kc] = (uint32_t)(AB + (wave * 32 + l32) * 64 + slot * 16);
+    }
+    const uint32_t ob1 = (two ? 8 * 32 * 64 : 0);  // the second block's rows
+
+    f32x16 acc[2][MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[0][mb] = acc[1][mb] = f32x16{};
+#pragma unroll
+    for (int p = 0; p < NS - 1; ++p)
+        if (p < KT) issue(p, p);
+    for (int kt = 0; kt < KT; ++kt) {
+        // this wave's loads of tile kt landed, those of up to NS - 2 later
+        // tiles may fly (waves 0-3 issue G + 1 per tile, the others G:
+        // counting G per tile waits for at least as much)
+        const int later = min(NS - 2, KT - 1 - kt);
+        if (later >= 3) __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * G));
+        else if (later == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * G));
+        else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(G));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();  // everyone's tile kt landed; stage kt-1 free
+        asm volatile("" ::: "memory");
+        if (kt + NS - 1 < KT) issue(kt + NS - 1, (kt + NS - 1) % NS);
+        const uint32_t sb = lbase + (uint32_t)((kt % NS) * SB);
+        // the fragments of both k-steps, read and waited for in one block
+        bf16x8 fa[2][2], fb[2][2];
+        if constexpr (MB == 2)
+            asm volatile("ds_read_b128 %0, %8\n\t"
+                         "ds_read_b128 %1, %8 offset:2048\n\t"
+                         "ds_read_b128 %2, %9\n\t"
+                         "ds_read_b128 %3, %10\n\t"
+                         "ds_read_b128 %4, %11\n\t"
+                         "ds_read_b128 %5, %11 offset:2048\n\t"
+                         "ds_read_b128 %6, %12\n\t"
+                         "ds_read_b128 %7, %13\n\t"
+                         "s_waitcnt lgkmcnt(0)"
+                         : "=&v"(fa[0][0]), "=&v"(fa[0][1]), "=&v"(fb[0][0]), "=&v"(fb[0][1]),
+                           "=&v"(fa[1][0]), "=&v"(fa[1][1]), "=&v"(fb[1][0]), "=&v"(fb[1][1])
+                         : "v"(sb + oa[0]), "v"(sb + ob[0]), "v"(sb + ob[0] + ob1),
+                           "v"(sb + oa[1]), "v"(sb + ob[1]), "v"(sb + ob[1] + ob1)
+                         : "memory");
+        else
+            asm volatile("ds_read_b128 %0, %6\n\t"
+                         "ds_read_b128 %1, %7\n\t"
+                         "ds_read_b128 %2, %8\n\t"
+                         "ds_read_b128 %3, %9\n\t"
+                         "ds_read_b128 %4, %10\n\t"
+                         "ds_read_b128 %5, %11\n\t"
+                         "s_waitcnt lgkmcnt(0)"
+                         : "=&v"(fa[0][0]), "=&v"(fb[0][0]), "=&v"(fb[0][1]),
+                           "=&v"(fa[1][0]), "=&v"(fb[1][0]), "=&v"(fb[1][1])
+                         : "v"(sb + oa[0]), "v"(sb + ob[0]), "v"(sb + ob[0] + ob1),
+                           "v"(sb + oa[1]), "v"(sb + ob[1]), "v"(sb + ob[1] + ob1)
+                         : "memory");
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                acc[0][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kc][mb], fb[kc][0],
+                                                                     acc[0][mb], 0, 0, 0);
+                acc[1][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kc][mb], fb[kc][1],
+                                                                     acc[1][mb], 0, 0, 0);
+            }
+    }
+
+    head_start_store<G, MB>(a, n, b0, rows, acc);
+}
+
 // One workgroup = one head x one tile of up to 16 batch rows; DH/16 waves,
 // wave w owns hidden units [16w, 16w+16) with all G gate tiles, so after the
 // MFMA chain lane l holds every gate sum of unit 16w + l%16 for batch rows
@@ -107,13 +303,110 @@ __device__ __forceinline__ void lstm_or_gru_unit(const float *gpre, int DH, cons
 // earlier are then complete.  After the barrier of that step every wave
 // has passed its wait, and at the group's second step wave 0 counts the
 // steps those stores hold (the group three back).
-// s_waitcnt immediate for vmcnt(n), n < 64, other counters not waited on.
-constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+// The head start for one row block (M <= 32) where x's 32 rows of all K
+// fit in LDS beside a ring of at least three W^T stages: x's rows are each
+// read once, all loaded at the start (cold in the caches, they would
+// otherwise cost a memory latency in every K tile), and only W^T streams
+// through the ring.  Same MFMAs in the same order as head_start.
+inline constexpr int hs_ares_bytes(int K) { return 64 * K; }  // 32 rows x 2K bytes
+template <int G>
+__device__ __forceinline__ void head_start_ares(const RecArgs &a, int n, int b0, int rows,
+                                                char *smem) {
+    constexpr int GD = G * 128, NB = GD / 32, BS = GD * 64;  // W^T stage: GD rows x 32 k
+    using dma::f32x16;
+    const int K = a.hs_K, B = a.B, KT = K >> 5;
+    const int M = a.hs_steps * rows;
+    const int AR = hs_ares_bytes(K);              // x: K tile kt at 2048 kt
+    const int NS = (kFusedLdsBytes - AR) / BS;    // >= 3: the condition for this variant
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    const int l32 = lane & 31, lh = lane >> 5;
+    dma::lds_char *lds = (dma::lds_char *)smem;
+    const uint32_t lbase = (uint32_t)(uintptr_t)lds;
+    auto grow = [&](int m) -> long {
+        return rows == 1 ? (long)m * B + b0 : (long)(m / rows) * B + b0 + m % rows;
+    };
+    // x: 2 KT load instructions (K tile i/2, rows 16 (i%2) .. +16), wave w
+    // issues i = w, w + 8, ...; chunk q = 64 (i%2) + lane of the tile holds
+    // row q/4, k chunk (q%4) ^ swz(row).  Rows past M repeat row M - 1.
+    const char *pa[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int q = 64 * h + lane, r = q >> 2;
+        pa[h] = reinterpret_cast<const char *>(a.hs_x + grow(min(r, M - 1)) * K +
+                                               8 * ((q & 3) ^ dma::swz(r)));
+    }
+    for (int i = wave_s; i < 2 * KT; i += 8)
+        load_lds16(pa[i & 1] + 64 * (i >> 1), lds + 2048 * (i >> 1) + 1024 * (i & 1));
+    const char *pb[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+        const int q = 64 * (wave * G + i) + lane, r = q >> 2;
+        pb[i] = reinterpret_cast<const char *>(a.hs_wt + (long)(n * GD + r) * K +
+                                               8 * ((q & 3) ^ dma::swz(r)));
+    }
+    auto issue = [&](int kt, int stage) {
+        dma::lds_char *st = lds + AR + stage * BS;
+#pragma unroll
+        for (int i = 0; i < G; ++i) load_lds16(pb[i] + 64 * kt, st + 1024 * (wave_s * G + i));
+    };
+    const int nb1 = wave + 8;
+    const bool two = nb1 < NB;
+    const int sw = dma::swz(l32);
+    uint32_t oa[2], ob[2];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+        const int slot = (2 * kc + lh) ^ sw;
+        oa[kc] = (uint32_t)(l32 * 64 + slot * 16);
+        ob[kc] = (uint32_t)((wave * 32 + l32) * 64 + slot * 16);
+    }
+    const uint32_t ob1 = (two ? 8 * 32 * 64 : 0);
+
+    f32x16 acc[2][1];
+    acc[0][0] = acc[1][0] = f32x16{};
+    for (int p = 0; p < NS - 1 && p < KT; ++p) issue(p, p);
+    for (int kt = 0; kt < KT; ++kt) {
+        // this wave's loads of W^T tile kt landed (and, older, all of x's):
+        // those of up to NS - 2 later tiles may fly, G per tile
+        const int later = min(NS - 2, KT - 1 - kt);
+        if (later >= 3) __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * G));
+        else if (later == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * G));
+        else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(G));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();  // everyone's tile kt landed; stage kt-1 free
+        asm volatile("" ::: "memory");
+        if (kt + NS - 1 < KT) issue(kt + NS - 1, (kt + NS - 1) % NS);
+        const uint32_t sa = lbase + (uint32_t)(2048 * kt);
+        const uint32_t sb = lbase + (uint32_t)(AR + (kt % NS) * BS);
+        bf16x8 fa[2], fb[2][2];
+        asm volatile("ds_read_b128 %0, %6\n\t"
+                     "ds_read_b128 %1, %7\n\t"
+                     "ds_read_b128 %2, %8\n\t"
+                     "ds_read_b128 %3, %9\n\t"
+                     "ds_read_b128 %4, %10\n\t"
+                     "ds_read_b128 %5, %11\n\t"
+                     "s_waitcnt lgkmcnt(0)"
+                     : "=&v"(fa[0]), "=&v"(fb[0][0]), "=&v"(fb[0][1]), "=&v"(fa[1]),
+                       "=&v"(fb[1][0]), "=&v"(fb[1][1])
+                     : "v"(sa + oa[0]), "v"(sb + ob[0]), "v"(sb + ob[0] + ob1), "v"(sa + oa[1]),
+                       "v"(sb + ob[1]), "v"(sb + ob[1] + ob1)
+                     : "memory");
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+            acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kc], fb[kc][0], acc[0][0], 0, 0, 0);
+            acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kc], fb[kc][1], acc[1][0], 0, 0, 0);
+        }
+    }
+    head_start_store<G, 1>(a, n, b0, rows, acc);
+}
 
 template <int CELL, int DH, int R4, int PD, bool WAIT, bool HB = false, bool LANES = false>
 __device__ __forceinline__ void rec_fwd_mfma_body(const RecArgs &a, const int blk,
                                                   uint16_t *h_bf = nullptr,
-                                                  unsigned *done = nullptr) {
+                                                  unsigned *done = nullptr,
+                                                  char *dyn_lds = nullptr) {
     constexpr int G = CellTraits<CELL>::G;
     constexpr int GD = G * DH;
     constexpr int NW = DH / 16;   // waves = 16-unit blocks
@@ -130,18 +423,49 @@ __device__ __forceinline__ void rec_fwd_mfma_body(const RecArgs &a, const int bl
     __shared__ __attribute__((aligned(16))) uint16_t hbuf[2][16 * HLD];
 
     if (a.clear_word && blk == 0 && threadIdx.x == 0) *a.clear_word = 0u;
-    const int n = blk % a.NH;
-    const int b0 = (blk / a.NH) * a.BT;
+    // Head start: workgroup i runs on XCD i % 8; numbering the (head, batch
+    // tile) pairs head-major within each XCD's share keeps one or two heads'
+    // W^T per XCD, which its L2 then holds for all their batch tiles.
+    int wi = blk;
+    if constexpr (WAIT) {
+        const int grid = a.NH * ((a.B + a.BT - 1) / a.BT);
+        if (a.hs_steps > 0 && (grid & 7) == 0) {
+            const int nbt = grid / a.NH, lg8 = (blk & 7) * (grid >> 3) + (blk >> 3);
+            wi = (lg8 % nbt) * a.NH + lg8 / nbt;  // head lg8 / nbt, batch tile lg8 % nbt
+        }
+    }
+    const int n = wi % a.NH;
+    const int b0 = (wi / a.NH) * a.BT;
     const int rows = min(a.BT, a.B - b0);
     const int H = a.NH * DH, N = a.NH * GD;
     const int T = a.T, B = a.B;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
     const int j = 16 * wave + lr;  // this lane's hidden unit
+    // head start (pipelined forward, Dh = 128): gx of the first steps here
+    bool hs = false;
+    if constexpr (WAIT && DH == 128) {
+        hs = a.hs_steps > 0 && dyn_lds != nullptr;
+        if (hs) {
+            if (a.hs_steps * rows > 32) head_start<G, 2>(a, n, b0, rows, dyn_lds);
+            else if (kFusedLdsBytes - hs_ares_bytes(a.hs_K) >= 3 * G * 128 * 64)
+                head_start_ares<G>(a, n, b0, rows, dyn_lds);
+            else head_start<G, 1>(a, n, b0, rows, dyn_lds);
+        }
+    }
 
     // ---- R_n fragments of this wave's G tiles, resident for all T steps
     bf16x8 rf[G][KC];
-    {
+    if (a.Rt != nullptr) {
+        // R^T: a fragment's eight k of one column are 16 contiguous bytes
+        const uint16_t *Rn = a.Rt + (long)n * GD * DH;
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int c = 0; c < KC; ++c)
+                rf[g][c] = *reinterpret_cast<const bf16x8 *>(Rn + (long)(g * DH + j) * DH + 32 * c +
+                                                             8 * lg);
+    } else {
         const uint16_t *Rn = a.Rb + (long)n * DH * GD;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -207,7 +531,7 @@ __device__ __forceinline__ void rec_fwd_mfma_body(const RecArgs &a, const int bl
             for (int g = 0; g < GL; ++g) bx0[s][r][g] = bx1[s][r][g] = 0.f;
         }
     // Gx of steps [0, avail) is known complete and acquired (WAIT only).
-    int avail = WAIT ? 0 : T, panels_ok = 0;
+    int avail = WAIT ? (hs ? min(a.hs_steps, T) : 0) : T, panels_ok = hs ? a.hs_panels : 0;
     auto wait_ready = [&](int tend) {
         if constexpr (WAIT) {
             tend = min(tend, T);
@@ -441,6 +765,8 @@ __global__ __launch_bounds__(DH / 16 * 64) void rec_fwd_mfma_kernel(RecArgs a) {
 // is resident before any recurrence workgroup starts to wait, and the
 // projection waits on nothing: the launch cannot stall on itself, whatever
 // else shares the chip.
+static_assert(dma::LDS_BYTES <= (size_t)kFusedLdsBytes, "the projection's ring fits");
+static_assert(kHeadStartRows <= 64, "the head start holds at most two row blocks");
 template <int CELL, int DH, int R4, int PD, bool LANES>
 __global__ __launch_bounds__(512) void fwd_fused_kernel(RecArgs a, GemmArgs g, int n_gemm) {
     static_assert(DH / 16 * 64 == 512, "both roles run 512 threads");
@@ -449,7 +775,8 @@ __global__ __launch_bounds__(512) void fwd_fused_kernel(RecArgs a, GemmArgs g, i
         dma::gemm_dma_tiles(g, blockIdx.x, n_gemm, (dma::lds_char *)fused_lds);
         return;
     }
-    rec_fwd_mfma_body<CELL, DH, R4, PD, true, false, LANES>(a, blockIdx.x - n_gemm);
+    rec_fwd_mfma_body<CELL, DH, R4, PD, true, false, LANES>(a, blockIdx.x - n_gemm, nullptr,
+                                                            nullptr, fused_lds);
 }
 
 // Two stacked layers in one launch (see StackSync): [0, R) layer l's
@@ -668,11 +995,11 @@ hipError_t launch_fused_t(const RecPlan &p, const RecArgs &a, const GemmArgs &g,
     std::call_once(once, [] {
         attr = hipFuncSetAttribute(
             reinterpret_cast<const void *>(&fwd_fused_kernel<CELL, 128, R4, PD, LANES>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, (int)dma::LDS_BYTES);
+            hipFuncAttributeMaxDynamicSharedMemorySize, kFusedLdsBytes);
     });
     if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL((fwd_fused_kernel<CELL, 128, R4, PD, LANES>), dim3(n_gemm + p.grid),
-                       dim3(512), dma::LDS_BYTES, s, a, g, n_gemm);
+                       dim3(512), (size_t)kFusedLdsBytes, s, a, g, n_gemm);
     return hipGetLastError();
 }
 

@@ -23,7 +23,7 @@ TOL_BF16 = 2e-2
 
 @pytest.fixture(autouse=True)
 def _no_plan_override():
-    keys = ("RNN355_REC_BT", "RNN355_PIPELINE")
+    keys = ("RNN355_REC_BT", "RNN355_PIPELINE", "RNN355_HEAD_START")
     old = {k: os.environ.pop(k, None) for k in keys}
     yield
     for k in keys:
@@ -295,6 +295,39 @@ def test_pipelined_forward_row_layouts_match_serial_bitwise(cell, bt):
     compare(piped, oracle_of(c), TOL_BF16, keys)
 
 
+@pytest.mark.parametrize("cell,T,B,Din,bt,hs", [
+    ("lstm", 200, 16, 256, 1, 4),   # 64 steps x 1 row: two whole row blocks
+    ("gru", 150, 8, 128, 1, 1),     # 32 steps x 1 row: one row block
+    ("lstm", 120, 48, 128, 1, 3),   # 16 steps x 1 row: a partial row block
+    ("gru", 90, 32, 128, 3, 1),     # 8 steps x 3 rows; the last batch tile has 2
+    ("lstm", 100, 32, 256, 2, 4),   # 32 steps x 2 rows (rows in lane groups)
+    ("lstm", 120, 16, 96, 1, 2),    # three K tiles, fewer than the ring's stages
+])
+def test_pipelined_forward_head_start_matches_serial_bitwise(cell, T, B, Din, bt, hs):
+    """The one-launch forward whose recurrence workgroups compute the first
+    row panels of gx themselves (the projection skipping them) gives bitwise
+    the serial result, which matches the oracle: whole and partial 32-row
+    blocks, one to three batch rows per workgroup, LSTM and GRU."""
+    d = synth.Dims(T=T, B=B, Din=Din, NH=2, Dh=128)
+    op = g.OP_FWD_LSTM if cell == "lstm" else g.OP_FWD_GRU
+    gd = g.Dims(d.T, d.B, d.Din, d.NH, d.Dh)
+    os.environ["RNN355_REC_BT"] = str(bt)
+    os.environ["RNN355_HEAD_START"] = str(hs)
+    plan = _with_env("RNN355_PIPELINE", "1", lambda: g.plan_describe(op, gd, g.RNN_BF16))
+    print("  plan:", plan, flush=True)
+    assert "rows_per_wg=%d " % bt in plan and "input_proj=pipelined" in plan
+    assert "head_start_panels=%d" % hs in plan
+    c = synth.make_case(cell, d, "bf16", 7900 + T, bias="forget+1" if cell == "lstm" else "zero",
+                        h0_var=0.1, c0_var=0.1 if cell == "lstm" else 0.0)
+    run = run_lstm if cell == "lstm" else run_gru
+    piped = _with_env("RNN355_PIPELINE", "1", lambda: run(c))
+    serial = _with_env("RNN355_PIPELINE", "0", lambda: run(c))
+    for k in piped:
+        assert np.array_equal(piped[k], serial[k]), k
+    keys = ("h_seq", "c_seq", "hT", "cT") if cell == "lstm" else ("h_seq", "hT")
+    compare(piped, oracle_of(c), TOL_BF16, keys)
+
+
 def test_pipelined_headline_forward_repeatable_and_equal_to_serial():
     """Full-size multi-head LSTM (B=16, NH=6, Dh=128, T=1024): three pipelined
     calls on one workspace (panel counters reused) and one serial call agree
@@ -304,7 +337,9 @@ def test_pipelined_headline_forward_repeatable_and_equal_to_serial():
     x, W, R, b = dev(c, "x"), dev(c, "W"), dev(c, "R"), dev(c, "b")
     wd = w.dims
     d = g.Dims(wd.T, wd.B, wd.Din, wd.NH, wd.Dh)
-    assert "input_proj=pipelined" in g.plan_describe(g.OP_FWD_LSTM, d, g.RNN_BF16)
+    plan = g.plan_describe(g.OP_FWD_LSTM, d, g.RNN_BF16)
+    print("  plan:", plan, flush=True)
+    assert "input_proj=pipelined" in plan and "head_start_panels=0" not in plan
     ws = torch.empty(g.workspace_size(g.OP_FWD_LSTM, d, g.RNN_BF16), dtype=torch.uint8,
                      device="cuda")
     outs = []
