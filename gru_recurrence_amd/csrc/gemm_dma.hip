@@ -125,6 +125,59 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(TJob j0, TJob j1, u
     }
 }
 
+// The same transposition where every job has R % 8 == 0 and C % 8 == 0 and
+// 16-byte aligned rows: a thread moves one 8x8 block in registers (eight
+// 16-byte loads, 32 halfword recombinations, eight 16-byte stores), no LDS.
+// A workgroup covers 64 rows x 256 columns of the source, wave w columns
+// [64 w, 64 w + 64); lane 8 bi + bj takes block (bi, bj) of the wave's 64x64,
+// so each load instruction reads eight whole 128-byte row pieces and each
+// store writes eight.  Flat grid over both jobs as above, block 0 clears.
+__global__ __launch_bounds__(256) void transpose8_bf16_kernel(TJob j0, TJob j1, unsigned *clear,
+                                                              long nclear, unsigned *clear2,
+                                                              long nclear2) {
+    const int tid = threadIdx.x;
+    if (blockIdx.x == 0) {
+        if (clear)
+            for (long i = tid; i < nclear; i += 256) clear[i] = 0u;
+        if (clear2)
+            for (long i = tid; i < nclear2; i += 256) clear2[i] = 0u;
+    }
+    const int n0 = j0.tx * j0.ty * j0.batch;
+    const bool second = (int)blockIdx.x >= n0;
+    const TJob &j = second ? j1 : j0;
+    const int f = second ? (int)blockIdx.x - n0 : (int)blockIdx.x;
+    const int bx = f % j.tx, by = (f / j.tx) % j.ty, bz = f / (j.tx * j.ty);
+    const int R = j.R, C = j.C;
+    const long bstride = (long)R * C;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int r = by * 64 + 8 * (lane >> 3);             // the block's first source row
+    const int c = bx * 256 + 64 * wave + 8 * (lane & 7);  // and first source column
+    if (r >= R || c >= C) return;
+    const uint16_t *S = j.src + bz * bstride + (long)r * C + c;
+    uint16_t *D = j.dst + bz * bstride + (long)c * R + r;
+    uint32_t w[8][4];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(S + (long)k * C);
+        w[k][0] = v.x;
+        w[k][1] = v.y;
+        w[k][2] = v.z;
+        w[k][3] = v.w;
+    }
+    // output row e (source column c + e) holds source rows r..r+7 of column e:
+    // word m pairs rows 2m (low half) and 2m + 1 (high half)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        uint32_t o[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const uint32_t lo = w[2 * m][e >> 1], hi = w[2 * m + 1][e >> 1];
+            o[m] = (e & 1) ? (hi & 0xFFFF0000u) | (lo >> 16) : (hi << 16) | (lo & 0xFFFFu);
+        }
+        *reinterpret_cast<uint4 *>(D + (long)e * R) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+}
+
 TJob tjob(const uint16_t *src, uint16_t *dst, int R, int C, int batch) {
     TJob j{src, dst, R, C, batch, (C + 63) / 64, (R + 63) / 64};
     if (!src || batch <= 0) j.batch = 0;
@@ -172,6 +225,23 @@ hipError_t launch_transpose_bf16(const uint16_t *src, uint16_t *dst, int R, int 
                                  hipStream_t s, unsigned *clear, long nclear, unsigned *clear2,
                                  long nclear2, const uint16_t *src1, uint16_t *dst1, int R1,
                                  int C1, int batch1) {
+    // whole 8x8 blocks and 16-byte aligned rows in every job: the register kernel
+    auto fits8 = [](const uint16_t *a, const uint16_t *b, int r, int c) {
+        return r % 8 == 0 && c % 8 == 0 && ((uintptr_t)a & 15) == 0 && ((uintptr_t)b & 15) == 0;
+    };
+    if (fits8(src, dst, R, C) && (!src1 || batch1 <= 0 || fits8(src1, dst1, R1, C1))) {
+        auto tj8 = [](const uint16_t *a, uint16_t *b, int r, int c, int n) {
+            TJob j{a, b, r, c, n, (c + 255) / 256, (r + 63) / 64};
+            if (!a || n <= 0) j.batch = 0;
+            return j;
+        };
+        const TJob k0 = tj8(src, dst, R, C, batch), k1 = tj8(src1, dst1, R1, C1, batch1);
+        const long blocks8 = (long)k0.tx * k0.ty * k0.batch + (long)k1.tx * k1.ty * k1.batch;
+        if (blocks8 <= 0 || blocks8 > 0x7fffffffL) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(transpose8_bf16_kernel, dim3((unsigned)blocks8), dim3(256), 0, s, k0, k1,
+                           clear, nclear, clear2, nclear2);
+        return hipGetLastError();
+    }
     const TJob j0 = tjob(src, dst, R, C, batch), j1 = tjob(src1, dst1, R1, C1, batch1);
     const long blocks = (long)j0.tx * j0.ty * j0.batch + (long)j1.tx * j1.ty * j1.batch;
     if (blocks <= 0 || blocks > 0x7fffffffL) return hipErrorInvalidValue;
