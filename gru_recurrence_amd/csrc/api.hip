@@ -77,7 +77,7 @@ size_t wt_bytes(const rnn_dims *d, int G) {
 // R staged transposed per head ([NH][G*Dh][Dh] bf16) for the Dh = 256
 // one-CU recurrence; sized for every bf16 shape with Dh = 256.
 size_t rt_fwd_bytes(const rnn_dims *d, rnn_dtype dt, int G) {
-    if (dt != RNN_BF16 || (d->Dh != 256 && d->Dh != 128)) return 0;
+    if (dt != RNN_BF16 || (d->Dh != 256 && d->Dh != 128 && d->Dh != 64)) return 0;
     return align_up(sizeof(uint16_t) * (size_t)d->NH * G * d->Dh * d->Dh);
 }
 
@@ -293,7 +293,8 @@ rnn_status input_proj(int M, int K, int N, rnn_dtype dt, const void *x, const vo
     return e == hipSuccess ? RNN_OK : RNN_ERR_HIP;
 }
 
-// rt: workspace region for R^T (rt_fwd_bytes), used by the Dh = 256 kernel.
+// rt: workspace region for R^T (rt_fwd_bytes), used by the Dh = 256 kernel (and, at
+// Dh = 64 and 128, by the pipelined forward's recurrence).
 // clear_status: zero the status word first (a stacked layer after the
 // first keeps what earlier layers reported).
 rnn_status rec_fwd(int cell, const rnn_dims *d, rnn_dtype dt, const float *gx, const void *R,
@@ -344,21 +345,26 @@ bool rec_supported(int cell, const rnn_dims *d, rnn_dtype dt) {
     return choose(cell, d, dt, device_cus()).ok;
 }
 
+int head_start_panels(const Choice &ch, const rnn_dims *d, const void *x);
+
 // Whether the forward overlaps its two phases (see forward()): the one-CU
-// recurrence at Dh = 128 must leave at least half the CUs free, and the
-// projection (bf16, Din % 32 == 0) must take more than two waves of output
-// tiles on those CUs -- otherwise the first row panel is ready about when
-// the whole projection would be, and the overlap only adds the cost of
-// running the two side by side.
+// recurrence at Dh = 128 or 64 must leave at least half the CUs free, and
+// the projection (bf16, Din % 32 = 0) must take more than two waves of
+// output tiles on those CUs, or more than one where the recurrence can start
+// on a head start (head_start_panels) -- otherwise the first row panel is
+// ready about when the whole projection would be, and the overlap only adds
+// the cost of running the two side by side.
 bool pipelined(const Choice &ch, const rnn_dims *d, rnn_dtype dt, int cus) {
     const int force = pipeline_override();
-    if (dt != RNN_BF16 || ch.use_mc || ch.use_wide || ch.rec.kind != kRecMfma || d->Dh != 128 ||
-        !gemm_dma_ok(d->Din) || 2 * ch.rec.grid > cus || force == 0 || gx_panels(d) < 2)
+    if (dt != RNN_BF16 || ch.use_mc || ch.use_wide || ch.rec.kind != kRecMfma ||
+        (d->Dh != 128 && d->Dh != 64) || !gemm_dma_ok(d->Din) || 2 * ch.rec.grid > cus ||
+        force == 0 || gx_panels(d) < 2)
         return false;
     if (force == 1) return true;
     const int G = gates_of_cell(ch.cell);
     const long tiles = gx_panels(d) * (((long)d->NH * G * d->Dh + kGemmColTile - 1) / kGemmColTile);
-    return tiles > 2L * (cus - ch.rec.grid);
+    const long free = cus - ch.rec.grid;
+    return tiles > 2L * free || (tiles > free && head_start_panels(ch, d, nullptr) > 0);
 }
 
 // Workgroups for an input projection that runs beside the recurrence: enough
@@ -391,7 +397,7 @@ int proj_workgroups(const rnn_dims *d, const Choice &ch, int tiles_per_panel, in
 // limits.
 int head_start_panels(const Choice &ch, const rnn_dims *d, const void *x) {
     const long panels = gx_panels(d);
-    if (x && ((uintptr_t)x & 15) != 0) return 0;
+    if ((x && ((uintptr_t)x & 15) != 0) || (d->Dh != 128 && d->Dh != 64)) return 0;
     auto fits = [&](int p) {
         if (p >= panels || ((long)kGemmRowTile * p) % d->B != 0) return false;
         const long rows = (long)kGemmRowTile * p / d->B * std::min(ch.rec.BT, d->B);
@@ -443,10 +449,12 @@ rnn_status forward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, con
         // W^T for the k-major contraction; the same launch zeroes the status
         // words of the header and the panel counters
         // and R^T per head (16-byte fragment loads in the recurrence)
-        uint16_t *rt = (uint16_t *)((char *)wt + wt_bytes(d, G));
+        uint16_t *rt = rt_fwd_bytes(d, dt, G) > 0 ? (uint16_t *)((char *)wt + wt_bytes(d, G))
+                                                  : nullptr;
         if (!ok(launch_transpose_bf16((const uint16_t *)W, wt, d->Din, N, 1, s,
                                       clear_status ? (unsigned *)ws : nullptr, 64, ready, panels,
-                                      (const uint16_t *)R, rt, d->Dh, G * d->Dh, d->NH)))
+                                      rt ? (const uint16_t *)R : nullptr, rt, d->Dh, G * d->Dh,
+                                      rt ? d->NH : 0)))
             return RNN_ERR_HIP;
         // the first hs panels come from the recurrence's workgroups
         const int hs = head_start_panels(ch, d, x);

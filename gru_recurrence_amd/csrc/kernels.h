@@ -142,8 +142,8 @@ RecPlan plan_rec(int cell, int T, int B, int NH, int Dh, bool bf16, int num_cu,
 hipError_t launch_rec_fwd(int cell, const RecPlan &p, const RecArgs &a, bool bf16,
                           hipStream_t s);
 
-// Pipelined forward in one launch (MFMA plan, Dh = 128, bf16, Din % 32 ==
-// 0): n_gemm workgroups run the k-major input projection g (with g.ready),
+// Pipelined forward in one launch (MFMA plan, Dh = 128 or 64, bf16, Din %
+// 32 == 0): n_gemm workgroups run the k-major input projection g (with g.ready),
 // p.grid more run the recurrence a waiting on a.ready.  Dynamic LDS of the
 // contraction is set up here.
 hipError_t launch_fwd_fused(int cell, const RecPlan &p, const RecArgs &a, const GemmArgs &g,

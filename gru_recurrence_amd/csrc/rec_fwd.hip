@@ -77,23 +77,23 @@ __device__ __forceinline__ void load_lds16(const char *src, dma::lds_char *dst) 
 
 // The head start's results + b into gx; register r of lane l in block (i,
 // mb) is row mb*32 + 8 (r/4) + 4 (l/32) + r%4, column l%32 of the block
-// (wave w: column blocks w and w + 8, or w twice).  Returns once every
-// wave's stores are complete in L2.
-template <int G, int MB>
+// (wave w of the DH/16: column blocks w and w + DH/16, or w twice).  Returns
+// once every wave's stores are complete in L2.
+template <int G, int MB, int DH>
 __device__ __forceinline__ void head_start_store(const RecArgs &a, int n, int b0, int rows,
                                                  const dma::f32x16 (&acc)[2][MB]) {
-    constexpr int GD = G * 128, NB = GD / 32;
+    constexpr int GD = G * DH, NB = GD / 32;
     const int B = a.B, N = a.NH * GD, M = a.hs_steps * rows;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int l32 = lane & 31, lh = lane >> 5;
-    const int nb1 = wave + 8;
+    const int nb1 = wave + DH / 16;
     const bool two = nb1 < NB;
     auto grow = [&](int m) -> long {
         return rows == 1 ? (long)m * B + b0 : (long)(m / rows) * B + b0 + m % rows;
     };
     float *gx = const_cast<float *>(a.gx);
     const int col0 = n * GD + wave * 32 + l32;
-    const int col1 = two ? n * GD + nb1 * 32 + l32 : col0;  // GRU waves 4-7: block w again
+    const int col1 = two ? n * GD + nb1 * 32 + l32 : col0;  // GRU's last waves: block w again
     const float bv0 = a.hs_bias ? a.hs_bias[col0] : 0.f;
     const float bv1 = a.hs_bias ? a.hs_bias[col1] : 0.f;
     if (M == 32 * MB && rows == 1) {
@@ -144,10 +144,11 @@ __device__ __forceinline__ void head_start_store(const RecArgs &a, int n, int b0
 // M repeat row M - 1 (their sums are never stored).  Returns once every
 // wave's stores are complete in L2, where the step loop's device-scope loads
 // read.
-template <int G, int MB>
+template <int G, int MB, int DH>
 __device__ __forceinline__ void head_start(const RecArgs &a, int n, int b0, int rows,
                                            char *smem) {
-    constexpr int GD = G * 128, NB = GD / 32;
+    constexpr int GD = G * DH, NB = GD / 32, NWV = DH / 16;  // NWV waves
+    static_assert(NWV >= 4, "four waves load x's rows");
     constexpr int AB = 64 * 64, SB = AB + GD * 64;  // stage: x rows, then W^T rows
     constexpr int NS = kFusedLdsBytes / SB;          // LSTM 4 stages, GRU 5
     static_assert(NS >= 3, "the head start's ring needs three stages");
@@ -187,7 +188,7 @@ __device__ __forceinline__ void head_start(const RecArgs &a, int n, int b0, int 
         for (int i = 0; i < G; ++i) load_lds16(pb[i] + kb, st + AB + 1024 * (wave_s * G + i));
     };
     // fragment byte offsets in a stage: row l32 of block 0, k chunk 2 kc + lh
-    const int nb1 = wave + 8;
+    const int nb1 = wave + NWV;
     const bool two = nb1 < NB;
     const int sw = dma::swz(l32);
     uint32_t oa[2], ob[2];
@@ -197,7 +198,7 @@ __device__ __forceinline__ void head_start(const RecArgs &a, int n, int b0, int 
         oa[kc] = (uint32_t)(l32 * 64 + slot * 16);
         ob[kc] = (uint32_t)(AB + (wave * 32 + l32) * 64 + slot * 16);
     }
-    const uint32_t ob1 = (two ? 8 * 32 * 64 : 0);  // the second block's rows
+    const uint32_t ob1 = (two ? NWV * 32 * 64 : 0);  // the second block's rows
 
     f32x16 acc[2][MB];
 #pragma unroll
@@ -260,7 +261,7 @@ __device__ __forceinline__ void head_start(const RecArgs &a, int n, int b0, int 
             }
     }
 
-    head_start_store<G, MB>(a, n, b0, rows, acc);
+    head_start_store<G, MB, DH>(a, n, b0, rows, acc);
 }
 
 // One workgroup = one head x one tile of up to 16 batch rows; DH/16 waves,
@@ -310,10 +311,12 @@ __device__ __forceinline__ void head_start(const RecArgs &a, int n, int b0, int 
 // otherwise cost a memory latency in every K tile), and only W^T streams
 // through the ring.  Same MFMAs in the same order as head_start.
 inline constexpr int hs_ares_bytes(int K) { return 64 * K; }  // 32 rows x 2K bytes
-template <int G>
+template <int G, int DH>
 __device__ __forceinline__ void head_start_ares(const RecArgs &a, int n, int b0, int rows,
                                                 char *smem) {
-    constexpr int GD = G * 128, NB = GD / 32, BS = GD * 64;  // W^T stage: GD rows x 32 k
+    constexpr int GD = G * DH, NB = GD / 32, BS = GD * 64;  // W^T stage: GD rows x 32 k
+    constexpr int NWV = DH / 16;  // waves, >= 4
+    static_assert(NWV >= 4, "four waves load x's rows");
     using dma::f32x16;
     const int K = a.hs_K, B = a.B, KT = K >> 5;
     const int M = a.hs_steps * rows;
@@ -328,7 +331,7 @@ __device__ __forceinline__ void head_start_ares(const RecArgs &a, int n, int b0,
         return rows == 1 ? (long)m * B + b0 : (long)(m / rows) * B + b0 + m % rows;
     };
     // x: 2 KT load instructions (K tile i/2, rows 16 (i%2) .. +16), wave w
-    // issues i = w, w + 8, ...; chunk q = 64 (i%2) + lane of the tile holds
+    // issues i = w, w + NWV, ...; chunk q = 64 (i%2) + lane of the tile holds
     // row q/4, k chunk (q%4) ^ swz(row).  Rows past M repeat row M - 1.
     const char *pa[2];
 #pragma unroll
@@ -337,7 +340,7 @@ __device__ __forceinline__ void head_start_ares(const RecArgs &a, int n, int b0,
         pa[h] = reinterpret_cast<const char *>(a.hs_x + grow(min(r, M - 1)) * K +
                                                8 * ((q & 3) ^ dma::swz(r)));
     }
-    for (int i = wave_s; i < 2 * KT; i += 8)
+    for (int i = wave_s; i < 2 * KT; i += NWV)
         load_lds16(pa[i & 1] + 64 * (i >> 1), lds + 2048 * (i >> 1) + 1024 * (i & 1));
     const char *pb[G];
 #pragma unroll
@@ -351,7 +354,7 @@ __device__ __forceinline__ void head_start_ares(const RecArgs &a, int n, int b0,
 #pragma unroll
         for (int i = 0; i < G; ++i) load_lds16(pb[i] + 64 * kt, st + 1024 * (wave_s * G + i));
     };
-    const int nb1 = wave + 8;
+    const int nb1 = wave + NWV;
     const bool two = nb1 < NB;
     const int sw = dma::swz(l32);
     uint32_t oa[2], ob[2];
@@ -361,7 +364,7 @@ __device__ __forceinline__ void head_start_ares(const RecArgs &a, int n, int b0,
         oa[kc] = (uint32_t)(l32 * 64 + slot * 16);
         ob[kc] = (uint32_t)((wave * 32 + l32) * 64 + slot * 16);
     }
-    const uint32_t ob1 = (two ? 8 * 32 * 64 : 0);
+    const uint32_t ob1 = (two ? NWV * 32 * 64 : 0);
 
     f32x16 acc[2][1];
     acc[0][0] = acc[1][0] = f32x16{};
@@ -399,7 +402,7 @@ __device__ __forceinline__ void head_start_ares(const RecArgs &a, int n, int b0,
             acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kc], fb[kc][1], acc[1][0], 0, 0, 0);
         }
     }
-    head_start_store<G, 1>(a, n, b0, rows, acc);
+    head_start_store<G, 1, DH>(a, n, b0, rows, acc);
 }
 
 template <int CELL, int DH, int R4, int PD, bool WAIT, bool HB = false, bool LANES = false>
@@ -444,13 +447,13 @@ __device__ __forceinline__ void rec_fwd_mfma_body(const RecArgs &a, const int bl
     const int j = 16 * wave + lr;  // this lane's hidden unit
     // head start (pipelined forward, Dh = 128): gx of the first steps here
     bool hs = false;
-    if constexpr (WAIT && DH == 128) {
+    if constexpr (WAIT && DH >= 64) {
         hs = a.hs_steps > 0 && dyn_lds != nullptr;
         if (hs) {
-            if (a.hs_steps * rows > 32) head_start<G, 2>(a, n, b0, rows, dyn_lds);
-            else if (kFusedLdsBytes - hs_ares_bytes(a.hs_K) >= 3 * G * 128 * 64)
-                head_start_ares<G>(a, n, b0, rows, dyn_lds);
-            else head_start<G, 1>(a, n, b0, rows, dyn_lds);
+            if (a.hs_steps * rows > 32) head_start<G, 2, DH>(a, n, b0, rows, dyn_lds);
+            else if (kFusedLdsBytes - hs_ares_bytes(a.hs_K) >= 3 * G * DH * 64)
+                head_start_ares<G, DH>(a, n, b0, rows, dyn_lds);
+            else head_start<G, 1, DH>(a, n, b0, rows, dyn_lds);
         }
     }
 
@@ -757,8 +760,8 @@ __global__ __launch_bounds__(DH / 16 * 64) void rec_fwd_mfma_kernel(RecArgs a) {
     rec_fwd_mfma_body<CELL, DH, R4, PD, WAIT, false, LANES>(a, blockIdx.x);
 }
 
-// The pipelined forward as one launch (Dh = 128: both roles run 512
-// threads): workgroups [0, n_gemm) compute the input projection, output
+// The pipelined forward as one launch (512-thread workgroups; at Dh = 64 the
+// recurrence uses four of the eight waves): workgroups [0, n_gemm) compute the input projection, output
 // tiles in time order and each finished tile counted on its row panel;
 // the rest run the recurrence, waiting for the panels of their next steps.
 // Workgroups are dispatched in index order, so every projection workgroup
@@ -769,12 +772,16 @@ static_assert(dma::LDS_BYTES <= (size_t)kFusedLdsBytes, "the projection's ring f
 static_assert(kHeadStartRows <= 64, "the head start holds at most two row blocks");
 template <int CELL, int DH, int R4, int PD, bool LANES>
 __global__ __launch_bounds__(512) void fwd_fused_kernel(RecArgs a, GemmArgs g, int n_gemm) {
-    static_assert(DH / 16 * 64 == 512, "both roles run 512 threads");
+    static_assert(DH == 128 || DH == 64, "the recurrence takes all eight waves or the first four");
     extern __shared__ __attribute__((aligned(16))) char fused_lds[];
     if ((int)blockIdx.x < n_gemm) {
         dma::gemm_dma_tiles(g, blockIdx.x, n_gemm, (dma::lds_char *)fused_lds);
         return;
     }
+    // Dh = 64: the recurrence runs on four waves; the other four end here, on
+    // a scalar branch (a workgroup barrier waits only for the waves still
+    // running; a wave left running with no lanes active would take part)
+    if (DH < 128 && __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) >= DH / 16) return;
     rec_fwd_mfma_body<CELL, DH, R4, PD, true, false, LANES>(a, blockIdx.x - n_gemm, nullptr,
                                                             nullptr, fused_lds);
 }
@@ -987,39 +994,46 @@ RecPlan plan_rec(int cell, int T, int B, int NH, int Dh, bool bf16, int num_cu,
     return p;
 }
 
-template <int CELL, int R4, int PD, bool LANES>
+template <int CELL, int DH, int R4, int PD, bool LANES>
 hipError_t launch_fused_t(const RecPlan &p, const RecArgs &a, const GemmArgs &g, int n_gemm,
                           hipStream_t s) {
     static std::once_flag once;
     static hipError_t attr = hipSuccess;
     std::call_once(once, [] {
         attr = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&fwd_fused_kernel<CELL, 128, R4, PD, LANES>),
+            reinterpret_cast<const void *>(&fwd_fused_kernel<CELL, DH, R4, PD, LANES>),
             hipFuncAttributeMaxDynamicSharedMemorySize, kFusedLdsBytes);
     });
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((fwd_fused_kernel<CELL, 128, R4, PD, LANES>), dim3(n_gemm + p.grid),
+    hipLaunchKernelGGL((fwd_fused_kernel<CELL, DH, R4, PD, LANES>), dim3(n_gemm + p.grid),
                        dim3(512), (size_t)kFusedLdsBytes, s, a, g, n_gemm);
     return hipGetLastError();
+}
+
+template <int DH>
+hipError_t launch_fused_dh(int cell, const RecPlan &p, const RecArgs &a, const GemmArgs &g,
+                           int n_gemm, hipStream_t s) {
+    if (p.BT == 1)
+        return cell == kLSTM ? launch_fused_t<kLSTM, DH, 1, 8, false>(p, a, g, n_gemm, s)
+                             : launch_fused_t<kGRU, DH, 1, 8, false>(p, a, g, n_gemm, s);
+    switch (p.upt) {
+        case 1: return cell == kLSTM ? launch_fused_t<kLSTM, DH, 1, 4, true>(p, a, g, n_gemm, s)
+                                     : launch_fused_t<kGRU, DH, 1, 4, true>(p, a, g, n_gemm, s);
+        case 2: return cell == kLSTM ? launch_fused_t<kLSTM, DH, 2, 2, true>(p, a, g, n_gemm, s)
+                                     : launch_fused_t<kGRU, DH, 2, 2, true>(p, a, g, n_gemm, s);
+        default: return cell == kLSTM ? launch_fused_t<kLSTM, DH, 4, 2, false>(p, a, g, n_gemm, s)
+                                      : launch_fused_t<kGRU, DH, 4, 2, false>(p, a, g, n_gemm, s);
+    }
 }
 
 
 hipError_t launch_fwd_fused(int cell, const RecPlan &p, const RecArgs &a, const GemmArgs &g,
                             int n_gemm, hipStream_t s) {
-    if (p.kind != kRecMfma || a.Dh != 128 || !a.ready || !g.ready || n_gemm <= 0 ||
-        !gemm_dma_ok(g.K))
+    if (p.kind != kRecMfma || (a.Dh != 128 && a.Dh != 64) || !a.ready || !g.ready ||
+        n_gemm <= 0 || !gemm_dma_ok(g.K))
         return hipErrorInvalidValue;
-    if (p.BT == 1)
-        return cell == kLSTM ? launch_fused_t<kLSTM, 1, 8, false>(p, a, g, n_gemm, s)
-                             : launch_fused_t<kGRU, 1, 8, false>(p, a, g, n_gemm, s);
-    switch (p.upt) {
-        case 1: return cell == kLSTM ? launch_fused_t<kLSTM, 1, 4, true>(p, a, g, n_gemm, s)
-                                     : launch_fused_t<kGRU, 1, 4, true>(p, a, g, n_gemm, s);
-        case 2: return cell == kLSTM ? launch_fused_t<kLSTM, 2, 2, true>(p, a, g, n_gemm, s)
-                                     : launch_fused_t<kGRU, 2, 2, true>(p, a, g, n_gemm, s);
-        default: return cell == kLSTM ? launch_fused_t<kLSTM, 4, 2, false>(p, a, g, n_gemm, s)
-                                      : launch_fused_t<kGRU, 4, 2, false>(p, a, g, n_gemm, s);
-    }
+    return a.Dh == 128 ? launch_fused_dh<128>(cell, p, a, g, n_gemm, s)
+                       : launch_fused_dh<64>(cell, p, a, g, n_gemm, s);
 }
 
 template <int CELL, bool HB1>

@@ -162,9 +162,10 @@ def test_plans_of_the_workloads(monkeypatch):
     no device is visible): one-CU resident-R kernel for Dh <= 128, at Dh =
     256 four CUs per chain exchanging through an XCD's L2 (or one CU with R
     split over registers and LDS), multi-CU split above; the forward
-    overlaps projection and recurrence (one fused
-    launch, Dh = 128) only when the recurrence leaves half the chip free and
-    the projection is large."""
+    overlaps projection and recurrence (one fused launch, Dh = 128 or 64)
+    only when the recurrence leaves half the chip free and the projection is
+    large: more than two rounds of tiles on the free CUs, or more than one
+    where the recurrence starts on a head start of its own."""
     monkeypatch.delenv("RNN355_PIPELINE", raising=False)
     monkeypatch.delenv("RNN355_REC_BT", raising=False)
     monkeypatch.delenv("RNN355_REC_K", raising=False)
@@ -175,8 +176,11 @@ def test_plans_of_the_workloads(monkeypatch):
     head = g.Dims(1024, 16, 768, 6, 128)
     p = g.plan_describe(g.OP_FWD_LSTM, head, g.RNN_BF16)
     assert "mfma_resident_R" in p and " wg=96 " in p and "input_proj=pipelined" in p
+    assert "head_start_panels=2" in p
+    # 288 tiles on 208 free CUs: overlapped with a head start of one panel
     p = g.plan_describe(g.OP_FWD_GRU, g.Dims(2048, 4, 768, 12, 64), g.RNN_BF16)
-    assert "mfma_resident_R" in p and " wg=48 " in p and "input_proj=serial" in p
+    assert "mfma_resident_R" in p and " wg=48 " in p and "input_proj=pipelined" in p
+    assert "head_start_panels=1" in p
     p = g.plan_describe(g.OP_FWD_LSTM, g.Dims(1024, 16, 768, 1, 768), g.RNN_BF16)
     assert "mfma_multi_cu" in p and "input_proj=serial" in p
     # Dh = 256, 64 (head, row) chains: four CUs per chain, the 64 groups
@@ -209,9 +213,11 @@ def test_plans_of_the_workloads(monkeypatch):
     monkeypatch.setenv("RNN355_PIPELINE", "1")
     small = g.Dims(233, 5, 96, 2, 128)
     assert "input_proj=pipelined" in g.plan_describe(g.OP_FWD_LSTM, small, g.RNN_BF16)
-    # only the Dh = 128 one-CU kernel runs fused with the projection, and only
-    # with Din % 32 == 0
-    assert "input_proj=serial" in g.plan_describe(g.OP_FWD_LSTM, g.Dims(233, 5, 96, 2, 64),
+    # only the one-CU kernel at Dh = 128 or 64 runs fused with the projection,
+    # and only with Din % 32 == 0
+    assert "input_proj=pipelined" in g.plan_describe(g.OP_FWD_LSTM, g.Dims(233, 5, 96, 2, 64),
+                                                     g.RNN_BF16)
+    assert "input_proj=serial" in g.plan_describe(g.OP_FWD_LSTM, g.Dims(233, 5, 96, 2, 32),
                                                   g.RNN_BF16)
     assert "input_proj=serial" in g.plan_describe(g.OP_FWD_LSTM, g.Dims(233, 5, 40, 2, 128),
                                                   g.RNN_BF16)

@@ -295,20 +295,25 @@ def test_pipelined_forward_row_layouts_match_serial_bitwise(cell, bt):
     compare(piped, oracle_of(c), TOL_BF16, keys)
 
 
-@pytest.mark.parametrize("cell,T,B,Din,bt,hs", [
-    ("lstm", 200, 16, 256, 1, 4),   # 64 steps x 1 row: two whole row blocks
-    ("gru", 150, 8, 128, 1, 1),     # 32 steps x 1 row: one row block
-    ("lstm", 120, 48, 128, 1, 3),   # 16 steps x 1 row: a partial row block
-    ("gru", 90, 32, 128, 3, 1),     # 8 steps x 3 rows; the last batch tile has 2
-    ("lstm", 100, 32, 256, 2, 4),   # 32 steps x 2 rows (rows in lane groups)
-    ("lstm", 120, 16, 96, 1, 2),    # three K tiles, fewer than the ring's stages
+@pytest.mark.parametrize("cell,T,B,Din,bt,hs,Dh", [
+    ("lstm", 200, 16, 256, 1, 4, 128),   # 64 steps x 1 row: two whole row blocks
+    ("gru", 150, 8, 128, 1, 1, 128),     # 32 steps x 1 row: one row block
+    ("lstm", 120, 48, 128, 1, 3, 128),   # 16 steps x 1 row: a partial row block
+    ("gru", 90, 32, 128, 3, 1, 128),     # 8 steps x 3 rows; the last batch tile has 2
+    ("lstm", 100, 32, 256, 2, 4, 128),   # 32 steps x 2 rows (rows in lane groups)
+    ("lstm", 120, 16, 96, 1, 2, 128),    # three K tiles, fewer than the ring's stages
+    ("gru", 300, 4, 256, 1, 1, 64),      # Dh 64 (four waves): 64 steps x 1 row
+    ("lstm", 200, 8, 128, 1, 1, 64),     # Dh 64: 32 steps, x resident in LDS
+    ("lstm", 150, 16, 96, 2, 2, 64),     # Dh 64: 32 steps x 2 rows, three K tiles
+    ("gru", 200, 8, 64, 1, 0, 64),       # Dh 64 one-launch forward without a head start
 ])
-def test_pipelined_forward_head_start_matches_serial_bitwise(cell, T, B, Din, bt, hs):
+def test_pipelined_forward_head_start_matches_serial_bitwise(cell, T, B, Din, bt, hs, Dh):
     """The one-launch forward whose recurrence workgroups compute the first
     row panels of gx themselves (the projection skipping them) gives bitwise
     the serial result, which matches the oracle: whole and partial 32-row
-    blocks, one to three batch rows per workgroup, LSTM and GRU."""
-    d = synth.Dims(T=T, B=B, Din=Din, NH=2, Dh=128)
+    blocks, one to three batch rows per workgroup, LSTM and GRU, Dh 128 (eight
+    waves) and 64 (four of a workgroup's eight waves)."""
+    d = synth.Dims(T=T, B=B, Din=Din, NH=2, Dh=Dh)
     op = g.OP_FWD_LSTM if cell == "lstm" else g.OP_FWD_GRU
     gd = g.Dims(d.T, d.B, d.Din, d.NH, d.Dh)
     os.environ["RNN355_REC_BT"] = str(bt)
@@ -350,6 +355,32 @@ def test_pipelined_headline_forward_repeatable_and_equal_to_serial():
     serial = _with_env("RNN355_PIPELINE", "0", lambda: g.lstm_fwd(x, W, R, b, ws=ws))
     torch.cuda.synchronize()
     for o in outs[1:] + [(serial[0], serial[2], serial[3])]:
+        for a, e in zip(outs[0], o):
+            assert torch.equal(a, e)
+
+
+def test_pipelined_gru_b4_nh12_dh64_equal_to_serial():
+    """Full-size multi-head GRU (B=4, NH=12, Dh=64, T=2048): the one-launch
+    forward with its head start (four of eight waves per recurrence
+    workgroup) and the serial forward agree bitwise, twice on one workspace."""
+    w = synth.WORKLOADS["gru_mh_b4_nh12_dh64"]
+    c = synth.workload_case(w)
+    x, W, R, b, h0 = dev(c, "x"), dev(c, "W"), dev(c, "R"), dev(c, "b"), dev(c, "h0")
+    wd = w.dims
+    d = g.Dims(wd.T, wd.B, wd.Din, wd.NH, wd.Dh)
+    plan = g.plan_describe(g.OP_FWD_GRU, d, g.RNN_BF16)
+    print("  plan:", plan, flush=True)
+    assert "input_proj=pipelined" in plan and "head_start_panels=0" not in plan
+    ws = torch.empty(g.workspace_size(g.OP_FWD_GRU, d, g.RNN_BF16), dtype=torch.uint8,
+                     device="cuda")
+    outs = []
+    for _ in range(2):
+        h_seq, hT = g.gru_fwd(x, W, R, b, h0, ws=ws)
+        outs.append((h_seq.clone(), hT.clone()))
+    assert g.workspace_status(ws) == g.RNN_OK
+    serial = _with_env("RNN355_PIPELINE", "0", lambda: g.gru_fwd(x, W, R, b, h0, ws=ws))
+    torch.cuda.synchronize()
+    for o in outs[1:] + [serial]:
         for a, e in zip(outs[0], o):
             assert torch.equal(a, e)
 
