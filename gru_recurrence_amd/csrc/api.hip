@@ -85,9 +85,14 @@ size_t rt_fwd_bytes(const rnn_dims *d, rnn_dtype dt, int G) {
 // recomputed pre-activations A (LSTM: Gx + h_{t-1} R; GRU: Gx alone) and the
 // GRU's recurrent sums S (f32), the gate-input gradients dA and the GRU's
 // recurrent-sum gradients dS (bf16), h_{t-1} (bf16), the per-batch-tile bias
-// partials, split-K partials, W^T and R^T per head.
+// partials (per chunk of the sweep), split-K partials, W^T, R^T per head and
+// the carries between chunks of the sweep.
+// The reverse sweep runs in up to kBwdChunks time chunks (see backward()):
+// bias partials for each, and the carries between chunks.
+constexpr int kBwdChunks = 4;
+constexpr int kBwdMinChunk = 256;  // shortest chunk (steps)
 struct BwdLayout {
-    size_t xchg, A, S, dA, dS, hprev, dbp, part, wt, rt, total;
+    size_t xchg, A, S, dA, dS, hprev, dbp, part, wt, rt, car, total;
 };
 BwdLayout bwd_layout(const rnn_dims *d, int G) {
     BwdLayout L{};
@@ -101,13 +106,14 @@ BwdLayout bwd_layout(const rnn_dims *d, int G) {
     L.dA = off;   off += align_up(sizeof(uint16_t) * TB * N);
     L.dS = off;   off += gru ? align_up(sizeof(uint16_t) * TB * N) : 0;
     L.hprev = off; off += align_up(sizeof(uint16_t) * TB * H);
-    L.dbp = off;  off += align_up(sizeof(float) * (size_t)d->B * N);
+    L.dbp = off;  off += align_up(sizeof(float) * (size_t)kBwdChunks * d->B * N);
     // split-K partials of the dW and dR contractions (used one after the other)
     const size_t pw = gemm_partial_bytes(d->Din, (int)N, 1, kMaxSplitK);
     const size_t pr = gemm_partial_bytes(d->Dh, G * d->Dh, d->NH, kMaxSplitKdR);
     L.part = off; off += align_up(pw > pr ? pw : pr);
     L.wt = off;   off += wt_bytes(d, G);                                     // W^T [N][Din]
     L.rt = off;   off += align_up(sizeof(uint16_t) * (size_t)d->NH * G * d->Dh * d->Dh);  // R^T per head
+    L.car = off;  off += 4 * align_up(sizeof(float) * H * d->B);  // dh, dc carries, two of each
     L.total = off;
     return L;
 }
@@ -751,6 +757,47 @@ rnn_status backward_f32(int cell, const rnn_dims *d, const float *x, const float
     return RNN_OK;
 }
 
+// Streams of the current device (default priority) for work that runs
+// beside the caller's stream, two per device (i = 0, 1); created on first use.
+hipStream_t side_stream(int i = 0) {
+    static std::mutex mu;
+    static hipStream_t st[64][2];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64 || i < 0 || i > 1) return nullptr;
+    std::lock_guard<std::mutex> lk(mu);
+    if (!st[dev][i] && hipStreamCreateWithFlags(&st[dev][i], hipStreamNonBlocking) != hipSuccess)
+        st[dev][i] = nullptr;
+    return st[dev][i];
+}
+
+// Events of one call, destroyed when the call returns (the runtime keeps
+// a recorded event alive until its work is done).
+struct CallEvents {
+    hipEvent_t e[8] = {};
+    bool ok = true;
+    CallEvents() {
+        for (hipEvent_t &v : e)
+            if (hipEventCreateWithFlags(&v, hipEventDisableTiming) != hipSuccess) ok = false;
+    }
+    ~CallEvents() {
+        for (hipEvent_t v : e)
+            if (v) (void)hipEventDestroy(v);
+    }
+};
+
+// Chunk starts for a backward over T steps: starts[0] = 0 < ... <
+// starts[n] = T, n chunks of ceil(T / n) steps (the last one shorter when n
+// does not divide T), n = min(kBwdChunks or RNN355_BWD_CHUNKS, T /
+// kBwdMinChunk), at least 1; returns n.
+int bwd_chunk_starts(int T, int *starts) {
+    int n = std::min(kBwdChunks, env_int_or("RNN355_BWD_CHUNKS", kBwdChunks));
+    n = std::max(1, std::min(n, T / kBwdMinChunk));
+    const int ch = (T + n - 1) / n;
+    for (int c = 0; c < n; ++c) starts[c] = c * ch;
+    starts[n] = T;
+    return n;
+}
+
 rnn_status backward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, const void *W,
                     const void *R, const float *b, const float *h0, const float *c0,
                     const float *h_seq, const float *c_seq, const float *dh_seq,
@@ -825,26 +872,70 @@ rnn_status backward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, co
             if (!ok(launch_gemm_bf16(g, true, false, NH, stream))) return RNN_ERR_HIP;
         }
     }
-    // 2. the reverse-time sweep
-    {
+    // 2. the reverse-time sweep and 3. the parameter and input gradients.
+    // Where the sweep leaves at least 64 compute units free and T allows,
+    // the sweep runs in up to kBwdChunks time chunks, the last one first,
+    // each from the carries (dL/dh, dL/dc at its end) the later chunk left in
+    // the workspace -- the carries pass through memory as float32, so the
+    // sweep's values are the same bits as in one piece.  Once a chunk is
+    // swept, its dx rows (one stream) and its shares of dW, dR and db (sums
+    // over its time steps; another stream) run on half the free units each,
+    // beside the next chunk's sweep.  The first chunk's gradients, swept
+    // last, run on the caller's stream over the whole chip.  dW, dR and db
+    // add the chunks' shares in sweep order (deterministic, not the one-piece
+    // summation order).  RNN355_BWD_OVERLAP=0 keeps the sweep in one piece.
+    const bool two = pw.ok && env_int_or("RNN355_BWD_WIDE2", 1) != 0 && mc_xcd_enabled() &&
+                     mc_xcd_grouping(NH * B, 2 * NH * B) && 2 * NH * B <= device_cus();
+    const int cus = device_cus();
+    const int sweep_grid = two ? 2 * NH * B : pw.ok ? pw.grid : p.grid;
+    const int free_cus = (cus - sweep_grid) / 8 * 8;
+    int starts[kBwdChunks + 1];
+    const int nch = free_cus >= 64 && env_int_or("RNN355_BWD_OVERLAP", 1) != 0
+                        ? bwd_chunk_starts(T, starts)
+                        : 1;
+    // dx on one stream, dW, dR and db on the other, each on half the free units
+    hipStream_t side = nch > 1 ? side_stream(0) : nullptr, side2 = nch > 1 ? side_stream(1) : nullptr;
+    CallEvents ev;
+    const bool split = nch > 1 && side && side2 && ev.ok;
+    const int half = free_cus / 16 * 8;
+    if (!split) {
+        starts[0] = 0;
+        starts[1] = T;
+    }
+    const int nc = split ? nch : 1;
+    const long BHl = (long)B * H;
+    float *part = (float *)(base + L.part);
+    const size_t bh = align_up(sizeof(float) * (size_t)BHl);
+    float *car_h[2] = {(float *)(base + L.car), (float *)(base + L.car + bh)};
+    float *car_c[2] = {(float *)(base + L.car + 2 * bh), (float *)(base + L.car + 3 * bh)};
+
+    // the sweep over steps [t0, t0 + Tc)
+    auto sweep = [&](int c, int t0, int Tc) -> bool {
         BwdArgs m{};
-        m.T = T; m.B = B; m.NH = NH; m.Dh = Dh; m.BT = p.BT;
+        const bool last = c == nc - 1, first = c == 0;
+        m.T = Tc; m.B = B; m.NH = NH; m.Dh = Dh; m.BT = p.BT;
         m.K = p.K; m.KS = p.ks; m.NB = p.nb;
-        m.A = A; m.S = lstm ? nullptr : S;
-        m.c_seq = c_seq; m.c0 = c0; m.h_seq = h_seq; m.h0 = h0;
-        m.dh_seq = dh_seq; m.dhT = dhT; m.dcT = dcT;
-        m.Rb = Rb; m.dA = dA; m.dS = lstm ? nullptr : dS;
-        m.db_part = dbp; m.dh0 = dh0; m.dc0 = dc0;
+        m.A = A + (long)t0 * B * N; m.S = lstm ? nullptr : S + (long)t0 * B * N;
+        m.c_seq = c_seq ? c_seq + t0 * BHl : nullptr;
+        m.c0 = t0 == 0 ? c0 : c_seq ? c_seq + (t0 - 1) * BHl : nullptr;
+        m.h_seq = h_seq + t0 * BHl;
+        m.h0 = t0 == 0 ? h0 : h_seq + (t0 - 1) * BHl;
+        m.dh_seq = dh_seq + t0 * BHl;
+        m.dhT = last ? dhT : car_h[(c + 1) & 1];
+        m.dcT = !lstm ? nullptr : last ? dcT : car_c[(c + 1) & 1];
+        m.Rb = Rb; m.dA = dA + (long)t0 * B * N; m.dS = lstm ? nullptr : dS + (long)t0 * B * N;
+        m.db_part = dbp + (long)c * nbt * N;
+        m.dh0 = first ? dh0 : car_h[c & 1];
+        m.dc0 = !lstm ? nullptr : first ? dc0 : car_c[c & 1];
         m.xg = (unsigned long long *)(base + L.xchg);
         m.flag = (unsigned *)ws;
+        // the status word is cleared by the first sweep of a call that clears
+        // it; later pieces keep what the earlier ones reported
+        m.keep_flag = !clear_status || !last;
         if (!pw.ok && p.K > 1 && mc_xcd_enabled() && mc_xcd_grouping(p.groups, p.grid)) {
             m.xcd_map = 1;
             m.xcc = (unsigned *)((char *)ws + kXccOffset);
         }
-        // Dh = 256 on two CUs per (head, row) where the pairs can share an
-        // XCD's L2 and all of them fit the chip at once
-        const bool two = pw.ok && env_int_or("RNN355_BWD_WIDE2", 1) != 0 && mc_xcd_enabled() &&
-                         mc_xcd_grouping(NH * B, 2 * NH * B) && 2 * NH * B <= device_cus();
         m.spin_limit = spin_limit();
         hipError_t e;
         if (two) {
@@ -854,70 +945,70 @@ rnn_status backward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, co
         } else {
             e = pw.ok ? launch_rec_bwd_wide(cell, pw, m, stream) : launch_rec_bwd(cell, p, m, stream);
         }
-        if (!ok(e)) return RNN_ERR_HIP;
-    }
-    // 3. parameter and input gradients
-    if (!ok(launch_db_reduce(dbp, nbt, N, db, stream, accumulate))) return RNN_ERR_HIP;
-    float *part = (float *)(base + L.part);
-    const int cus = device_cus();
-    {
-        GemmArgs g{};  // dW[k][c] = sum_m x[m][k] dA[m][c]
-        g.M = Din; g.N = N; g.K = M;
-        g.A = xb; g.lda = Din; g.B = dA; g.ldb = N; g.C = dW; g.ldc = N;
-        g.accumulate = accumulate ? 1 : 0;
-        g.ksplit = std::min(gemm_splitk_for(Din, N, M, 1, cus), kMaxSplitK);
-        g.partial = part;
-        if (!ok(launch_gemm_bf16(g, false, false, 1, stream))) return RNN_ERR_HIP;
-    }
-    {
+        return ok(e);
+    };
+    // dx rows of steps [t0, t0 + Tc) on stream st; units > 0: at most that
+    // many workgroups (the dx rows of a chunk are written once: no order)
+    auto grad_x = [&](int t0, int Tc, hipStream_t st, int units) -> bool {
+        const long r0 = (long)t0 * B;
         GemmArgs g{};  // dx[m][k] = sum_c dA[m][c] W[k][c]
-        g.M = M; g.N = Din; g.K = N;
-        g.A = dA; g.lda = N; g.B = Wb; g.ldb = N; g.C = dx; g.ldc = Din;
-        const hipError_t e = gemm_dma_ok(N) ? launch_gemm_dma(g, 1, stream)
-                                            : launch_gemm_bf16(g, true, true, 1, stream);
-        if (!ok(e)) return RNN_ERR_HIP;
-    }
-    {
-        GemmArgs g{};  // dR[n][i][c] = sum_m h_{t-1}[m][n*Dh+i] dS[m][n*GD+c]
-        g.M = Dh; g.N = GD; g.K = M;
-        g.A = hprev; g.lda = H; g.strideA = Dh;
-        g.B = dS; g.ldb = N; g.strideB = GD;
-        g.C = dR; g.ldc = GD; g.strideC = (long)Dh * GD;
-        g.accumulate = accumulate ? 1 : 0;
-        g.ksplit = std::min(gemm_splitk_for(Dh, GD, M, NH, cus), kMaxSplitKdR);
-        g.partial = part;
-        if (!ok(launch_gemm_bf16(g, false, false, NH, stream))) return RNN_ERR_HIP;
+        g.M = Tc * B; g.N = Din; g.K = N;
+        g.A = dA + r0 * N; g.lda = N; g.B = Wb; g.ldb = N; g.C = dx + r0 * Din; g.ldc = Din;
+        return ok(gemm_dma_ok(N) ? launch_gemm_dma(g, 1, st, units)
+                                 : launch_gemm_bf16(g, true, true, 1, st));
+    };
+    // the dW, dR and db shares of chunk c, steps [t0, t0 + Tc), on stream
+    // st, split for `units` compute units (units < cus: every launch at
+    // most that many workgroups); acc: add to dW, dR and db
+    auto grad_w = [&](int c, int t0, int Tc, hipStream_t st, int units, bool acc) -> bool {
+        const long r0 = (long)t0 * B;
+        const int Mc = Tc * B;
+        {
+            GemmArgs g{};  // dW[k][c] (+)= sum_m x[m][k] dA[m][c]
+            g.M = Din; g.N = N; g.K = Mc;
+            g.A = xb + r0 * Din; g.lda = Din; g.B = dA + r0 * N; g.ldb = N; g.C = dW; g.ldc = N;
+            g.accumulate = acc ? 1 : 0;
+            g.ksplit = std::min(gemm_splitk_for(Din, N, Mc, 1, units), kMaxSplitK);
+            g.partial = part;
+            if (!ok(launch_gemm_bf16(g, false, false, 1, st))) return false;
+        }
+        {
+            GemmArgs g{};  // dR[n][i][c] (+)= sum_m h_{t-1}[m][n*Dh+i] dS[m][n*GD+c]
+            g.M = Dh; g.N = GD; g.K = Mc;
+            g.A = hprev + r0 * H; g.lda = H; g.strideA = Dh;
+            g.B = dS + r0 * N; g.ldb = N; g.strideB = GD;
+            g.C = dR; g.ldc = GD; g.strideC = (long)Dh * GD;
+            g.accumulate = acc ? 1 : 0;
+            g.ksplit = std::min(gemm_splitk_for(Dh, GD, Mc, NH, units), kMaxSplitKdR);
+            g.partial = part;
+            if (!ok(launch_gemm_bf16(g, false, false, NH, st))) return false;
+        }
+        return ok(launch_db_reduce(dbp + (long)c * nbt * N, nbt, N, db, st, acc));
+    };
+    for (int c = nc - 1; c >= 0; --c) {
+        const int t0 = starts[c], Tc = starts[c + 1] - t0;
+        if (!sweep(c, t0, Tc)) return RNN_ERR_HIP;
+        if (c > 0) {
+            // this chunk's gradients beside the next chunk's sweep
+            if (!ok(hipEventRecord(ev.e[c], stream)) || !ok(hipStreamWaitEvent(side, ev.e[c], 0)) ||
+                !ok(hipStreamWaitEvent(side2, ev.e[c], 0)) || !grad_x(t0, Tc, side, half) ||
+                !grad_w(c, t0, Tc, side2, half, accumulate || c != nc - 1))
+                return RNN_ERR_HIP;
+        } else {
+            // dx of the first chunk needs nothing from the other streams;
+            // dW, dR and db wait for their last shares (and the call's end
+            // for every dx)
+            if (!grad_x(t0, Tc, stream, 0)) return RNN_ERR_HIP;
+            if (nc > 1 && (!ok(hipEventRecord(ev.e[0], side)) ||
+                           !ok(hipEventRecord(ev.e[7], side2)) ||
+                           !ok(hipStreamWaitEvent(stream, ev.e[0], 0)) ||
+                           !ok(hipStreamWaitEvent(stream, ev.e[7], 0))))
+                return RNN_ERR_HIP;
+            if (!grad_w(0, t0, Tc, stream, cus, accumulate || nc > 1)) return RNN_ERR_HIP;
+        }
     }
     return RNN_OK;
 }
-
-// A second stream of the current device (default priority) for work that
-// runs beside the caller's stream; created on first use.
-hipStream_t side_stream() {
-    static std::mutex mu;
-    static hipStream_t st[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-    std::lock_guard<std::mutex> lk(mu);
-    if (!st[dev] && hipStreamCreateWithFlags(&st[dev], hipStreamNonBlocking) != hipSuccess)
-        st[dev] = nullptr;
-    return st[dev];
-}
-
-// Events of one call, destroyed when the call returns (the runtime keeps
-// a recorded event alive until its work is done).
-struct CallEvents {
-    hipEvent_t e[5] = {};
-    bool ok = true;
-    CallEvents() {
-        for (hipEvent_t &v : e)
-            if (hipEventCreateWithFlags(&v, hipEventDisableTiming) != hipSuccess) ok = false;
-    }
-    ~CallEvents() {
-        for (hipEvent_t v : e)
-            if (v) (void)hipEventDestroy(v);
-    }
-};
 
 // Long sequences in chunks of `chunk` steps (blog.hotdry.top 2025-09-21,
 // the list of framework-level optimisations, third item: memory for long

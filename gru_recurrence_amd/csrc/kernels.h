@@ -311,6 +311,7 @@ struct BwdArgs {
     unsigned spin_limit;
     unsigned *xcc;  // as McArgs: members of a group numbered by XCD, checked
     int xcd_map;    // through this table of workgroup XCDs ([grid] words)
+    int keep_flag;  // nonzero: the launch leaves the status word as it stands
 };
 
 // Float32 backward (rec_bwd_f32.hip): float32 operands, pre-activations,

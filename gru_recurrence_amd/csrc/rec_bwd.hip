@@ -485,7 +485,8 @@ hipError_t launch_rec_bwd(int cell, const BwdPlan &p, const BwdArgs &m, hipStrea
     if (m.xcd_map && (!m.xcc || p.groups % 8 != 0)) return hipErrorInvalidValue;
     // one launch: the status word, the XCD table, the exchange slots
     const long words = p.K > 1 ? 2L * p.groups * 2 * p.BT * (G * m.Dh / 2) : 0;
-    hipLaunchKernelGGL(clear_words_bwd_kernel, dim3(64), dim3(256), 0, s, m.flag, 1L,
+    hipLaunchKernelGGL(clear_words_bwd_kernel, dim3(64), dim3(256), 0, s,
+                       m.keep_flag ? (unsigned *)nullptr : m.flag, 1L,
                        m.xcd_map ? m.xcc : (unsigned *)nullptr, m.xcd_map ? (long)p.grid : 0L,
                        p.K > 1 ? reinterpret_cast<unsigned *>(m.xg) : (unsigned *)nullptr, words);
     const hipError_t e = hipGetLastError();

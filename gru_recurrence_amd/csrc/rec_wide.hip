@@ -940,7 +940,8 @@ hipError_t launch_bwd_wide2_t(const BwdArgs &m0, hipStream_t s) {
     BwdArgs m = m0;
     const int grid = 2 * m.NH * m.B;
     const long words = (long)m.NH * m.B * 2 * 2 * (kWideDh / 2) * 2;  // as 32-bit words
-    hipLaunchKernelGGL(clear_words_wide_kernel, dim3(64), dim3(256), 0, s, m.flag, 1L,
+    hipLaunchKernelGGL(clear_words_wide_kernel, dim3(64), dim3(256), 0, s,
+                       m.keep_flag ? (unsigned *)nullptr : m.flag, 1L,
                        m.xcd_map ? m.xcc : (unsigned *)nullptr, m.xcd_map ? (long)grid : 0L,
                        reinterpret_cast<unsigned *>(m.xg), words);
     hipError_t e = hipGetLastError();

@@ -24,7 +24,7 @@ TOL = 2e-2
 @pytest.fixture(autouse=True)
 def _clean_env():
     keys = ("RNN355_REC_BT", "RNN355_REC_K", "RNN355_REC_WIDE", "RNN355_MC_XCD",
-            "RNN355_BWD_WIDE2", "RNN355_SPIN_LIMIT")
+            "RNN355_BWD_WIDE2", "RNN355_SPIN_LIMIT", "RNN355_BWD_OVERLAP")
     old = {k: os.environ.pop(k, None) for k in keys}
     yield
     for k in keys:
@@ -134,6 +134,32 @@ def test_backward_workload_full_size():
     ref = oracle.lstm_bwd(c.f64("x"), c.f64("W"), c.f64("R"), c.f64("b"), c.f64("h0"),
                           c.f64("c0"), c.f64("dH"), NH=d.NH, Dh=d.Dh, grads=())
     _full_size_backward_checks(got, ref, c, 4, heads_dW=(1, 3))
+
+
+@pytest.mark.parametrize("cell,T,B,NH,Dh,Din,final", [
+    ("lstm", 1030, 8, 2, 256, 128, True),  # two CUs per (head, row); chunks 3 x 258 + 256
+    ("gru", 512, 4, 3, 128, 64, True),     # two chunks of 256
+    ("lstm", 600, 5, 2, 64, 96, False),    # two chunks of 300
+])
+def test_backward_chunked_sweep_matches_one_piece(cell, T, B, NH, Dh, Din, final):
+    """The backward whose sweep runs in time chunks, each chunk's dx, dW, dR
+    and db computed on two other streams beside the next chunk's sweep, against
+    the same call with the sweep in one piece (RNN355_BWD_OVERLAP=0): dx,
+    dh0 and dc0 bitwise (the carries pass between chunks as float32), dW, dR
+    and db to float32 rounding (the chunks' sums are added in chunk order)."""
+    d = synth.Dims(T=T, B=B, Din=Din, NH=NH, Dh=Dh)
+    c = synth.make_case(cell, d, "bf16", 9300 + T + Dh, bias="forget+1" if cell == "lstm" else "zero",
+                        h0_var=0.2, c0_var=0.2, backward=True, final_grads=final)
+    run = gpu_bwd if cell == "lstm" else gpu_bwd_gru
+    chunked = run(c, final)
+    os.environ["RNN355_BWD_OVERLAP"] = "0"
+    whole = run(c, final)
+    for k in ("dx", "dh0") + (("dc0",) if cell == "lstm" else ()):
+        assert np.array_equal(chunked[k], whole[k]), k
+    for k in ("dW", "dR", "db"):
+        e = nerr(chunked[k], whole[k])
+        print("  %s: %.2e" % (k, e), flush=True)
+        assert e <= 1e-5, k
 
 
 def gpu_bwd_gru(c, final=False):
