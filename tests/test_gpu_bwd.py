@@ -322,6 +322,27 @@ def test_backward_two_cu_split_r(cell):
         assert e <= 1e-2, (k, e)
 
 
+def test_chunked_backward_timeout_is_reported():
+    """The sweep in two chunks with a spin limit of one poll: every chunk's
+    launch ends normally, the status word the first sweep set survives the
+    second chunk's launch, and the next call (no limit) clears it."""
+    d = synth.Dims(T=512, B=4, Din=32, NH=2, Dh=256)
+    c = synth.make_case("lstm", d, "bf16", 9910, bias="forget+1", backward=True,
+                        final_grads=True)
+    ws = torch.empty(g.workspace_size(g.OP_BWD_LSTM, g.Dims(d.T, d.B, d.Din, d.NH, d.Dh),
+                                      g.RNN_BF16), dtype=torch.uint8, device="cuda")
+    os.environ["RNN355_SPIN_LIMIT"] = "1"
+    _bwd_with_ws(c, ws)
+    assert g.workspace_status(ws) == g.RNN_ERR_BARRIER_TIMEOUT
+    os.environ.pop("RNN355_SPIN_LIMIT")
+    got = _bwd_with_ws(c, ws)
+    assert g.workspace_status(ws) == g.RNN_OK
+    ref = oracle.lstm_bwd(c.f64("x"), c.f64("W"), c.f64("R"), c.f64("b"), c.f64("h0"),
+                          c.f64("c0"), c.f64("dH"), c.f64("dhT"), c.f64("dcT"), NH=d.NH, Dh=d.Dh)
+    for k in ("dx", "dW", "dR", "db", "dh0", "dc0"):
+        check(k, got[k], ref[k], TOL)
+
+
 def test_backward_two_cu_timeout_is_reported():
     """A spin limit of one poll (set from the host) makes the first swap of
     partial carries give up: both CUs stop, the kernel ends normally and the
