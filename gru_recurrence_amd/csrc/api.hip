@@ -881,7 +881,8 @@ rnn_status backward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, co
     // swept, its dx rows (one stream) and its shares of dW, dR and db (sums
     // over its time steps; another stream) run on half the free units each,
     // beside the next chunk's sweep.  The first chunk's gradients, swept
-    // last, run on the caller's stream over the whole chip.  dW, dR and db
+    // last, run over the whole chip: its dx on the dx stream beside its dW,
+    // dR and db on the caller's stream.  dW, dR and db
     // add the chunks' shares in sweep order (deterministic, not the one-piece
     // summation order).  RNN355_BWD_OVERLAP=0 keeps the sweep in one piece.
     const bool two = pw.ok && env_int_or("RNN355_BWD_WIDE2", 1) != 0 && mc_xcd_enabled() &&
@@ -994,17 +995,23 @@ rnn_status backward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, co
                 !ok(hipStreamWaitEvent(side2, ev.e[c], 0)) || !grad_x(t0, Tc, side, half) ||
                 !grad_w(c, t0, Tc, side2, half, accumulate || c != nc - 1))
                 return RNN_ERR_HIP;
-        } else {
-            // dx of the first chunk needs nothing from the other streams;
-            // dW, dR and db wait for their last shares (and the call's end
-            // for every dx)
-            if (!grad_x(t0, Tc, stream, 0)) return RNN_ERR_HIP;
-            if (nc > 1 && (!ok(hipEventRecord(ev.e[0], side)) ||
-                           !ok(hipEventRecord(ev.e[7], side2)) ||
-                           !ok(hipStreamWaitEvent(stream, ev.e[0], 0)) ||
-                           !ok(hipStreamWaitEvent(stream, ev.e[7], 0))))
+        } else if (nc == 1) {
+            if (!grad_x(t0, Tc, stream, 0) || !grad_w(0, t0, Tc, stream, cus, accumulate))
                 return RNN_ERR_HIP;
-            if (!grad_w(0, t0, Tc, stream, cus, accumulate || nc > 1)) return RNN_ERR_HIP;
+        } else {
+            // the first chunk: its dx on the dx stream (behind the other
+            // chunks' dx) beside its dW, dR and db on the caller's stream,
+            // which wait for the other chunks' shares; the call ends when
+            // every dx is done
+            const int xt = ((Tc * B + kGemmRowTile - 1) / kGemmRowTile) *
+                           ((Din + kGemmColTile - 1) / kGemmColTile);
+            const int wu = std::max(64, (cus - xt) / 8 * 8);  // CUs the dx tiles leave
+            if (!ok(hipEventRecord(ev.e[0], stream)) || !ok(hipStreamWaitEvent(side, ev.e[0], 0)) ||
+                !grad_x(t0, Tc, side, 0) || !ok(hipEventRecord(ev.e[7], side2)) ||
+                !ok(hipStreamWaitEvent(stream, ev.e[7], 0)) ||
+                !grad_w(0, t0, Tc, stream, wu, true) || !ok(hipEventRecord(ev.e[6], side)) ||
+                !ok(hipStreamWaitEvent(stream, ev.e[6], 0)))
+                return RNN_ERR_HIP;
         }
     }
     return RNN_OK;
