@@ -90,7 +90,7 @@ size_t rt_fwd_bytes(const rnn_dims *d, rnn_dtype dt, int G) {
 // The reverse sweep runs in up to kBwdChunks time chunks (see backward()):
 // bias partials for each, and the carries between chunks.
 constexpr int kBwdChunks = 4;
-constexpr int kBwdMinChunk = 256;  // shortest chunk (steps)
+constexpr int kBwdMinChunk = 128;  // shortest chunk (steps)
 struct BwdLayout {
     size_t xchg, A, S, dA, dS, hprev, dbp, part, wt, rt, car, total;
 };
@@ -773,7 +773,7 @@ hipStream_t side_stream(int i = 0) {
 // Events of one call, destroyed when the call returns (the runtime keeps
 // a recorded event alive until its work is done).
 struct CallEvents {
-    hipEvent_t e[8] = {};
+    hipEvent_t e[kBwdChunks + 3] = {};
     bool ok = true;
     CallEvents() {
         for (hipEvent_t &v : e)
@@ -1006,11 +1006,12 @@ rnn_status backward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, co
             const int xt = ((Tc * B + kGemmRowTile - 1) / kGemmRowTile) *
                            ((Din + kGemmColTile - 1) / kGemmColTile);
             const int wu = std::max(64, (cus - xt) / 8 * 8);  // CUs the dx tiles leave
-            if (!ok(hipEventRecord(ev.e[0], stream)) || !ok(hipStreamWaitEvent(side, ev.e[0], 0)) ||
-                !grad_x(t0, Tc, side, 0) || !ok(hipEventRecord(ev.e[7], side2)) ||
-                !ok(hipStreamWaitEvent(stream, ev.e[7], 0)) ||
-                !grad_w(0, t0, Tc, stream, wu, true) || !ok(hipEventRecord(ev.e[6], side)) ||
-                !ok(hipStreamWaitEvent(stream, ev.e[6], 0)))
+            hipEvent_t swept = ev.e[0], w_done = ev.e[kBwdChunks], x_done = ev.e[kBwdChunks + 1];
+            if (!ok(hipEventRecord(swept, stream)) || !ok(hipStreamWaitEvent(side, swept, 0)) ||
+                !grad_x(t0, Tc, side, 0) || !ok(hipEventRecord(w_done, side2)) ||
+                !ok(hipStreamWaitEvent(stream, w_done, 0)) ||
+                !grad_w(0, t0, Tc, stream, wu, true) || !ok(hipEventRecord(x_done, side)) ||
+                !ok(hipStreamWaitEvent(stream, x_done, 0)))
                 return RNN_ERR_HIP;
         }
     }

@@ -138,8 +138,8 @@ def test_backward_workload_full_size():
 
 @pytest.mark.parametrize("cell,T,B,NH,Dh,Din,final", [
     ("lstm", 1030, 8, 2, 256, 128, True),  # two CUs per (head, row); chunks 3 x 258 + 256
-    ("gru", 512, 4, 3, 128, 64, True),     # two chunks of 256
-    ("lstm", 600, 5, 2, 64, 96, False),    # two chunks of 300
+    ("gru", 512, 4, 3, 128, 64, True),     # four chunks of 128
+    ("lstm", 600, 5, 2, 64, 96, False),    # four chunks of 150
 ])
 def test_backward_chunked_sweep_matches_one_piece(cell, T, B, NH, Dh, Din, final):
     """The backward whose sweep runs in time chunks, each chunk's dx, dW, dR
@@ -323,9 +323,9 @@ def test_backward_two_cu_split_r(cell):
 
 
 def test_chunked_backward_timeout_is_reported():
-    """The sweep in two chunks with a spin limit of one poll: every chunk's
+    """The sweep in four chunks with a spin limit of one poll: every chunk's
     launch ends normally, the status word the first sweep set survives the
-    second chunk's launch, and the next call (no limit) clears it."""
+    later chunks' launches, and the next call (no limit) clears it."""
     d = synth.Dims(T=512, B=4, Din=32, NH=2, Dh=256)
     c = synth.make_case("lstm", d, "bf16", 9910, bias="forget+1", backward=True,
                         final_grads=True)
