@@ -26,7 +26,10 @@ import argparse
 import hashlib
 import json
 import os
+import shutil
+import subprocess
 import sys
+import threading
 import time
 
 import numpy as np
@@ -85,6 +88,46 @@ def rec_kernel_name(w: synth.Workload, plan: str) -> str:
     pd = {1: 8 if rows == 1 else 4, 2: 2, 4: 2}[passes]
     return "rec_fwd_mfma_kernel<%d, %d, %d, %d, false, %s>" % (
         0 if w.cell == "lstm" else 1, w.dims.Dh, passes, pd, "true" if lanes else "false")
+
+
+def gfx_clock_under_load(step, torch) -> float | None:
+    """GFX clock (MHz; mean over the XCDs and over two readings) as amd-smi
+    reports it while the workload's step runs in a loop, the first reading
+    after one second of it (amd-smi's figures lag the load); None where
+    amd-smi is missing or its output cannot be read.  The recurrence is bound
+    by its per-step latency, which scales with this clock."""
+    exe = shutil.which("amd-smi")
+    if exe is None:
+        return None
+    res = {"v": []}
+
+    def read():
+        r = subprocess.run([exe, "metric", "-g", "0", "--clock", "--json"],
+                           capture_output=True, text=True, timeout=20)
+        clk = json.loads(r.stdout)["gpu_data"][0]["clock"]
+        v = [c["clk"]["value"] for k, c in clk.items()
+             if k.startswith("gfx_") and isinstance(c, dict) and isinstance(c.get("clk"), dict)
+             and isinstance(c["clk"].get("value"), (int, float))]
+        if v:
+            res["v"].append(sum(v) / len(v))
+
+    def sample():
+        try:
+            time.sleep(1.0)
+            read()
+            time.sleep(0.5)
+            read()
+        except (OSError, ValueError, KeyError, IndexError, TypeError, subprocess.SubprocessError):
+            pass
+
+    th = threading.Thread(target=sample)
+    th.start()
+    while th.is_alive():
+        for _ in range(4):
+            step()
+        torch.cuda.synchronize()
+    th.join()
+    return round(sum(res["v"]) / len(res["v"]), 1) if res["v"] else None
 
 
 def traffic_per_launch():
@@ -326,14 +369,16 @@ def main():
                 evs[2].record(stream)
 
     def timed(fn, n):
-        """n calls of fn, each bracketed by events on `stream`; mean ms."""
+        """n calls of fn, each bracketed by events on `stream`; (mean, median,
+        min) ms."""
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
         for e in ev:
             e[0].record(stream)
             fn()
             e[1].record(stream)
         torch.cuda.synchronize()
-        return float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+        ms = [e[0].elapsed_time(e[1]) for e in ev]
+        return float(np.mean(ms)), float(np.median(ms)), float(np.min(ms))
 
     for _ in range(args.warmup):
         step()
@@ -346,6 +391,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    step_ms = [e[0].elapsed_time(e[2 if backward else 1]) for e in evs]
     for wsx in (ws_f,) + ((ws_b,) if backward else ()):
         st = g.workspace_status(wsx, stream)
         if st != g.RNN_OK:
@@ -371,8 +417,9 @@ def main():
 
     proj()
     rec()
-    proj_avg = timed(proj, args.steps)
-    rec_avg = timed(rec, args.steps)
+    proj_avg, proj_med, proj_min = timed(proj, args.steps)
+    rec_avg, rec_med, rec_min = timed(rec, args.steps)
+    clock = gfx_clock_under_load(step, torch)
     st = g.workspace_status(ws, stream)
     if st != g.RNN_OK:
         print("bench.py: kernel reported %s" % g.status_str(st), file=sys.stderr)
@@ -406,7 +453,11 @@ def main():
                    "parallelism": "single GPU"},
         "time_steps_per_s": round(d.T / (ms_step * 1e-3), 1),
         "forward_call": {"avg_ms": round(float(np.mean(fwd_ms)), 4), "plan": fplan},
-        "recurrence": {"avg_launch_ms": round(rec_avg, 4), "tflops": round(achieved, 3),
+        "step_event_ms": {"median": round(float(np.median(step_ms)), 4),
+                          "min": round(float(np.min(step_ms)), 4)},
+        "gfx_clock_mhz_under_load": clock,
+        "recurrence": {"avg_launch_ms": round(rec_avg, 4), "median_launch_ms": round(rec_med, 4),
+                       "min_launch_ms": round(rec_min, 4), "tflops": round(achieved, 3),
                        "ns_per_time_step": round(rec_avg * 1e6 / d.T, 1),
                        "time_steps_per_s": round(d.T / (rec_avg * 1e-3), 1),
                        "engaged_cus": ncu_engaged,
@@ -418,6 +469,8 @@ def main():
                                        "predicted_ns_per_step": predicted,
                                        "measured_ns_per_step": round(rec_avg * 1e6 / d.T, 1)}},
         "input_projection": {"avg_launch_ms": round(proj_avg, 4),
+                             "median_launch_ms": round(proj_med, 4),
+                             "min_launch_ms": round(proj_min, 4),
                              "tflops": round(gemm_flops / (proj_avg * 1e-3) / 1e12, 2),
                              "frac_of_peak": round(gemm_flops / (proj_avg * 1e-3) / 1e12
                                                    / PEAK_BF16_TFLOPS, 4)},
@@ -441,7 +494,8 @@ def main():
     if backward:
         bwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
         out["backward"] = {"avg_call_ms": round(float(np.mean(bwd_ms)), 4),
-                           "note": "rnn_bwd_lstm: recompute GEMMs, reverse sweep, dx/dW/dR GEMMs"}
+                           "note": "rnn_bwd_lstm: recompute GEMMs, reverse sweep in time chunks "
+                                   "with each chunk's dx/dW/dR GEMMs beside the next chunk's sweep"}
     if chunked:
         out["config"]["chunk"] = w.chunk
         out["workspace_bytes"] = {
