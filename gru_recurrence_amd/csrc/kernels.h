@@ -144,10 +144,12 @@ hipError_t launch_rec_fwd(int cell, const RecPlan &p, const RecArgs &a, bool bf1
 
 // Pipelined forward in one launch (MFMA plan, Dh = 128 or 64, bf16, Din %
 // 32 == 0): n_gemm workgroups run the k-major input projection g (with g.ready),
-// p.grid more run the recurrence a waiting on a.ready.  Dynamic LDS of the
-// contraction is set up here.
+// p.grid more run the recurrence a waiting on a.ready.  rows1 > 0 (a
+// multiple of the row tile) and n_gemm2 > 0 (a multiple of 8): the first
+// rows1 rows of g on all n_gemm projection workgroups, the rest on the
+// first n_gemm2 of them.  Dynamic LDS of the contraction is set up here.
 hipError_t launch_fwd_fused(int cell, const RecPlan &p, const RecArgs &a, const GemmArgs &g,
-                            int n_gemm, hipStream_t s);
+                            int n_gemm, hipStream_t s, int rows1 = 0, int n_gemm2 = 0);
 
 // Two stacked layers l, l+1 in one launch (MFMA plan with one batch row per
 // workgroup, Dh = 128, bf16): rec_grid workgroups run layer l on a finished

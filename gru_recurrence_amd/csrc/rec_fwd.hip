@@ -771,11 +771,29 @@ __global__ __launch_bounds__(DH / 16 * 64) void rec_fwd_mfma_kernel(RecArgs a) {
 static_assert(dma::LDS_BYTES <= (size_t)kFusedLdsBytes, "the projection's ring fits");
 static_assert(kHeadStartRows <= 64, "the head start holds at most two row blocks");
 template <int CELL, int DH, int R4, int PD, bool LANES>
-__global__ __launch_bounds__(512) void fwd_fused_kernel(RecArgs a, GemmArgs g, int n_gemm) {
+__global__ __launch_bounds__(512) void fwd_fused_kernel(RecArgs a, GemmArgs g, int n_gemm,
+                                                        int rows1, int n_gemm2) {
     static_assert(DH == 128 || DH == 64, "the recurrence takes all eight waves or the first four");
     extern __shared__ __attribute__((aligned(16))) char fused_lds[];
     if ((int)blockIdx.x < n_gemm) {
-        dma::gemm_dma_tiles(g, blockIdx.x, n_gemm, (dma::lds_char *)fused_lds);
+        const int wg = blockIdx.x;
+        if (rows1 > 0 && rows1 < g.M && n_gemm2 > 0) {
+            // the first rows1 rows (whole panels) on all n_gemm workgroups,
+            // the rest on the first n_gemm2 of them
+            GemmArgs g1 = g;
+            g1.M = rows1;
+            dma::gemm_dma_tiles(g1, wg, n_gemm, (dma::lds_char *)fused_lds);
+            if (wg < n_gemm2) {
+                GemmArgs g2 = g;
+                g2.M = g.M - rows1;
+                g2.A = g.A + (long)rows1 * g.lda;
+                g2.C = g.C + (long)rows1 * g.ldc;
+                g2.ready = g.ready + rows1 / kGemmRowTile;
+                dma::gemm_dma_tiles(g2, wg, n_gemm2, (dma::lds_char *)fused_lds);
+            }
+        } else {
+            dma::gemm_dma_tiles(g, wg, n_gemm, (dma::lds_char *)fused_lds);
+        }
         return;
     }
     // Dh = 64: the recurrence runs on four waves; the other four end here, on
@@ -996,7 +1014,7 @@ RecPlan plan_rec(int cell, int T, int B, int NH, int Dh, bool bf16, int num_cu,
 
 template <int CELL, int DH, int R4, int PD, bool LANES>
 hipError_t launch_fused_t(const RecPlan &p, const RecArgs &a, const GemmArgs &g, int n_gemm,
-                          hipStream_t s) {
+                          int rows1, int n_gemm2, hipStream_t s) {
     static std::once_flag once;
     static hipError_t attr = hipSuccess;
     std::call_once(once, [] {
@@ -1006,34 +1024,35 @@ hipError_t launch_fused_t(const RecPlan &p, const RecArgs &a, const GemmArgs &g,
     });
     if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL((fwd_fused_kernel<CELL, DH, R4, PD, LANES>), dim3(n_gemm + p.grid),
-                       dim3(512), (size_t)kFusedLdsBytes, s, a, g, n_gemm);
+                       dim3(512), (size_t)kFusedLdsBytes, s, a, g, n_gemm, rows1, n_gemm2);
     return hipGetLastError();
 }
 
 template <int DH>
 hipError_t launch_fused_dh(int cell, const RecPlan &p, const RecArgs &a, const GemmArgs &g,
-                           int n_gemm, hipStream_t s) {
+                           int n_gemm, int rows1, int n_gemm2, hipStream_t s) {
     if (p.BT == 1)
-        return cell == kLSTM ? launch_fused_t<kLSTM, DH, 1, 8, false>(p, a, g, n_gemm, s)
-                             : launch_fused_t<kGRU, DH, 1, 8, false>(p, a, g, n_gemm, s);
+        return cell == kLSTM ? launch_fused_t<kLSTM, DH, 1, 8, false>(p, a, g, n_gemm, rows1, n_gemm2, s)
+                             : launch_fused_t<kGRU, DH, 1, 8, false>(p, a, g, n_gemm, rows1, n_gemm2, s);
     switch (p.upt) {
-        case 1: return cell == kLSTM ? launch_fused_t<kLSTM, DH, 1, 4, true>(p, a, g, n_gemm, s)
-                                     : launch_fused_t<kGRU, DH, 1, 4, true>(p, a, g, n_gemm, s);
-        case 2: return cell == kLSTM ? launch_fused_t<kLSTM, DH, 2, 2, true>(p, a, g, n_gemm, s)
-                                     : launch_fused_t<kGRU, DH, 2, 2, true>(p, a, g, n_gemm, s);
-        default: return cell == kLSTM ? launch_fused_t<kLSTM, DH, 4, 2, false>(p, a, g, n_gemm, s)
-                                      : launch_fused_t<kGRU, DH, 4, 2, false>(p, a, g, n_gemm, s);
+        case 1: return cell == kLSTM ? launch_fused_t<kLSTM, DH, 1, 4, true>(p, a, g, n_gemm, rows1, n_gemm2, s)
+                                     : launch_fused_t<kGRU, DH, 1, 4, true>(p, a, g, n_gemm, rows1, n_gemm2, s);
+        case 2: return cell == kLSTM ? launch_fused_t<kLSTM, DH, 2, 2, true>(p, a, g, n_gemm, rows1, n_gemm2, s)
+                                     : launch_fused_t<kGRU, DH, 2, 2, true>(p, a, g, n_gemm, rows1, n_gemm2, s);
+        default: return cell == kLSTM ? launch_fused_t<kLSTM, DH, 4, 2, false>(p, a, g, n_gemm, rows1, n_gemm2, s)
+                                      : launch_fused_t<kGRU, DH, 4, 2, false>(p, a, g, n_gemm, rows1, n_gemm2, s);
     }
 }
 
 
 hipError_t launch_fwd_fused(int cell, const RecPlan &p, const RecArgs &a, const GemmArgs &g,
-                            int n_gemm, hipStream_t s) {
+                            int n_gemm, hipStream_t s, int rows1, int n_gemm2) {
     if (p.kind != kRecMfma || (a.Dh != 128 && a.Dh != 64) || !a.ready || !g.ready ||
-        n_gemm <= 0 || !gemm_dma_ok(g.K))
+        n_gemm <= 0 || !gemm_dma_ok(g.K) || rows1 % kGemmRowTile != 0 || n_gemm2 > n_gemm ||
+        (n_gemm2 > 0 && n_gemm2 % 8 != 0))
         return hipErrorInvalidValue;
-    return a.Dh == 128 ? launch_fused_dh<128>(cell, p, a, g, n_gemm, s)
-                       : launch_fused_dh<64>(cell, p, a, g, n_gemm, s);
+    return a.Dh == 128 ? launch_fused_dh<128>(cell, p, a, g, n_gemm, rows1, n_gemm2, s)
+                       : launch_fused_dh<64>(cell, p, a, g, n_gemm, rows1, n_gemm2, s);
 }
 
 template <int CELL, bool HB1>
