@@ -18,7 +18,7 @@ projection alone is timed the same way.
 
 Prints ONE JSON line (see the keys below).
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-clock]
 """
 from __future__ import annotations
 
@@ -231,6 +231,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(synth.WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the clock reading under load (a loop of steps; profiles use this)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="only run a plain device copy of this many MiB (5 times) and exit; "
@@ -419,7 +421,7 @@ def main():
     rec()
     proj_avg, proj_med, proj_min = timed(proj, args.steps)
     rec_avg, rec_med, rec_min = timed(rec, args.steps)
-    clock = gfx_clock_under_load(step, torch)
+    clock = None if args.no_clock else gfx_clock_under_load(step, torch)
     st = g.workspace_status(ws, stream)
     if st != g.RNN_OK:
         print("bench.py: kernel reported %s" % g.status_str(st), file=sys.stderr)
