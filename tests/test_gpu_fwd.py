@@ -23,7 +23,7 @@ TOL_BF16 = 2e-2
 
 @pytest.fixture(autouse=True)
 def _no_plan_override():
-    keys = ("RNN355_REC_BT", "RNN355_PIPELINE", "RNN355_HEAD_START")
+    keys = ("RNN355_REC_BT", "RNN355_PIPELINE", "RNN355_HEAD_START", "RNN355_FUSED_TAPER")
     old = {k: os.environ.pop(k, None) for k in keys}
     yield
     for k in keys:
@@ -335,8 +335,8 @@ def test_pipelined_forward_head_start_matches_serial_bitwise(cell, T, B, Din, bt
 
 def test_pipelined_headline_forward_repeatable_and_equal_to_serial():
     """Full-size multi-head LSTM (B=16, NH=6, Dh=128, T=1024): three pipelined
-    calls on one workspace (panel counters reused) and one serial call agree
-    bitwise."""
+    calls on one workspace (panel counters reused), one serial call and one
+    pipelined call without the projection's taper agree bitwise."""
     w = synth.WORKLOADS["lstm_mh_b16_nh6_dh128"]
     c = synth.workload_case(w)
     x, W, R, b = dev(c, "x"), dev(c, "W"), dev(c, "R"), dev(c, "b")
@@ -357,12 +357,18 @@ def test_pipelined_headline_forward_repeatable_and_equal_to_serial():
     for o in outs[1:] + [(serial[0], serial[2], serial[3])]:
         for a, e in zip(outs[0], o):
             assert torch.equal(a, e)
+    # every projection workgroup to the end (no taper): the same bits
+    flat = _with_env("RNN355_FUSED_TAPER", "0", lambda: g.lstm_fwd(x, W, R, b, ws=ws))
+    torch.cuda.synchronize()
+    for a, e in zip(outs[0], (flat[0], flat[2], flat[3])):
+        assert torch.equal(a, e)
 
 
 def test_pipelined_gru_b4_nh12_dh64_equal_to_serial():
     """Full-size multi-head GRU (B=4, NH=12, Dh=64, T=2048): the one-launch
     forward with its head start (four of eight waves per recurrence
-    workgroup) and the serial forward agree bitwise, twice on one workspace."""
+    workgroup), the serial forward and the one-launch forward without the
+    projection's taper agree bitwise, twice on one workspace."""
     w = synth.WORKLOADS["gru_mh_b4_nh12_dh64"]
     c = synth.workload_case(w)
     x, W, R, b, h0 = dev(c, "x"), dev(c, "W"), dev(c, "R"), dev(c, "b"), dev(c, "h0")
@@ -379,8 +385,9 @@ def test_pipelined_gru_b4_nh12_dh64_equal_to_serial():
         outs.append((h_seq.clone(), hT.clone()))
     assert g.workspace_status(ws) == g.RNN_OK
     serial = _with_env("RNN355_PIPELINE", "0", lambda: g.gru_fwd(x, W, R, b, h0, ws=ws))
+    flat = _with_env("RNN355_FUSED_TAPER", "0", lambda: g.gru_fwd(x, W, R, b, h0, ws=ws))
     torch.cuda.synchronize()
-    for o in outs[1:] + [serial]:
+    for o in outs[1:] + [serial, flat]:
         for a, e in zip(outs[0], o):
             assert torch.equal(a, e)
 
