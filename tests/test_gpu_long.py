@@ -128,6 +128,7 @@ def _bwd_both(c, chunk, final):
     ("gru", 17, 3, 1, 256, 6, False),
     ("lstm", 19, 16, 4, 256, 8, True),     # multi-CU forward recompute (every CU)
     ("lstm", 1100, 4, 2, 128, 550, True),  # each segment's sweep in four chunks
+    ("gru", 600, 3, 2, 64, 300, True),     # GRU segments swept in two chunks each
 ])
 def test_checkpointed_backward(cell, T, B, NH, Dh, chunk, final):
     d = synth.Dims(T=T, B=B, Din=64, NH=NH, Dh=Dh)
