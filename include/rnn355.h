@@ -40,11 +40,16 @@
  * Ownership and threading: every tensor pointer is DEVICE memory owned by the
  * caller; outputs are overwritten, never accumulated.  The library allocates
  * nothing: scratch comes from the caller's workspace of at least
- * rnn_workspace_size() bytes.  Calls only enqueue work on `stream` and return
- * (asynchronous, stream-ordered); they hold no global mutable state apart from
- * a lazily filled, lock-protected cache of device properties, so they may be
- * called from several host threads.  Two calls in flight at once must not
- * share a workspace.
+ * rnn_workspace_size() bytes.  Calls only enqueue work and return
+ * (asynchronous, stream-ordered on `stream`).  Some (the chunked forward and
+ * the bf16 backward) run part of their work on up to two streams the library
+ * creates per device on first use (default priority), forked from `stream`
+ * and joined back into it by events, so everything a call does is ordered
+ * after the work queued on `stream` before it and before the work queued on
+ * `stream` after it.  The library's only global mutable state is a lazily
+ * filled, lock-protected cache of device properties and those streams, so
+ * calls may come from several host threads.  Two calls in flight at once
+ * must not share a workspace.
  *
  * Errors: every function returns a status; nothing aborts and no C++
  * exception crosses this boundary.  Arguments are validated before anything
@@ -353,6 +358,13 @@ rnn_status rnn_bwd_gru_ckpt(const rnn_dims *d, rnn_dtype dt, int chunk, const vo
  * stays float32 (pre-activations, gate gradients, carries, contractions);
  * the head's R block in float32 must fit one CU's LDS (Dh <= 96 for the
  * LSTM, else RNN_ERR_UNSUPPORTED), and the workspace is sized per dtype.
+ * bf16 calls with T >= 256 whose reverse sweep leaves at least 64 CUs free
+ * run the sweep in up to four time chunks (of at least 128 steps), the last
+ * one first, and each chunk's dx, dW, dR and db contractions on the
+ * library's two streams beside the next chunk's sweep: dx, dh0 and dc0 are
+ * the same bits as with the sweep in one piece, dW, dR and db add the
+ * chunks' shares in chunk order (environment RNN355_BWD_OVERLAP=0: one
+ * piece).
  */
 rnn_status rnn_bwd_lstm(const rnn_dims *d, rnn_dtype dt,
                         const void *x, const void *W, const void *R,
