@@ -89,3 +89,67 @@ def test_random_shape_forward_and_backward(cell, T, B, NH, Dh, Din):
         e = nerr(host(v), ref_b[k])
         print("  bwd %-4s nerr=%.3e" % (k, e), flush=True)
         assert e <= TOL, (k, e)
+
+
+def _long_shapes(n=8, seed=20261203):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        cell = ["lstm", "gru"][int(rng.integers(0, 2))]
+        Dh = int(rng.choice([32, 64, 128, 256]))
+        NH = int(rng.integers(1, 5))
+        B = int(rng.integers(1, 9))
+        T = int(rng.integers(256, 701))
+        Din = int(rng.choice([32, 64, 96, 128]))
+        out.append((cell, T, B, NH, Dh, Din))
+    return out
+
+
+@pytest.mark.parametrize("cell,T,B,NH,Dh,Din", _long_shapes())
+def test_random_long_shape_chunked_against_one_piece(cell, T, B, NH, Dh, Din):
+    """Sequences of 256-700 steps, where the backward sweeps in time chunks
+    with the gradients on side streams and the forward may run pipelined:
+    the backward's dx, dh0 (dc0) are bitwise those of the sweep in one piece
+    and dW, dR, db agree to float32 rounding; the forward is bitwise the
+    serial one."""
+    import os
+    d = synth.Dims(T=T, B=B, Din=Din, NH=NH, Dh=Dh)
+    lstm = cell == "lstm"
+    c = synth.make_case(cell, d, "bf16", 12000 + 7 * T + 13 * B + 17 * NH + Dh + Din,
+                        bias="forget+1" if lstm else "zero", h0_var=0.2,
+                        c0_var=0.2 if lstm else 0.0, backward=True, final_grads=True)
+    x, W, R, b, h0 = (dev(c, k) for k in ("x", "W", "R", "b", "h0"))
+    c0 = dev(c, "c0") if lstm else None
+
+    def fwd():
+        return g.lstm_fwd(x, W, R, b, h0, c0) if lstm else g.gru_fwd(x, W, R, b, h0)
+
+    def bwd(f):
+        if lstm:
+            return g.lstm_bwd(x, W, R, b, h0, c0, f[0], f[1], dev(c, "dH"), dev(c, "dhT"),
+                              dev(c, "dcT"))
+        return g.gru_bwd(x, W, R, b, h0, f[0], dev(c, "dH"), dev(c, "dhT"))
+
+    keys = ("RNN355_PIPELINE", "RNN355_BWD_OVERLAP")
+    old = {k: os.environ.pop(k, None) for k in keys}
+    try:
+        f = fwd()
+        gch = {k: host(v) for k, v in bwd(f).items()}
+        os.environ["RNN355_PIPELINE"] = "0"
+        os.environ["RNN355_BWD_OVERLAP"] = "0"
+        fs = fwd()
+        g1 = {k: host(v) for k, v in bwd(fs).items()}
+    finally:
+        for k in keys:
+            os.environ.pop(k, None)
+            if old[k] is not None:
+                os.environ[k] = old[k]
+    torch.cuda.synchronize()
+    for a, e in zip(f, fs):
+        assert torch.equal(a, e)
+    for k in ("dx", "dh0") + (("dc0",) if lstm else ()):
+        assert np.array_equal(gch[k], g1[k]), k
+    for k in ("dW", "dR", "db"):
+        e = nerr(gch[k], g1[k])
+        print("  %-3s chunked vs one piece nerr=%.2e" % (k, e), flush=True)
+        assert e <= 1e-5, (k, e)
