@@ -8,7 +8,9 @@ resident; the two overlap when the recurrence leaves half the chip free),
 plus rnn_bwd_lstm for the forward+backward workload, on synthetic inputs
 already resident in HBM.  `value` is recurrent TFLOP/s: the algorithmic
 flops of the recurrent products (2*B*H*G*Dh per step, the block-diagonal R
-only; twice that with the backward) divided by the wall time of the step.
+only; twice that with the backward) divided by the wall time of the step,
+K steps back to back with nothing else on the stream between them.  K more
+steps with HIP events around each phase then give the per-phase figures.
 
 The roofline entry is for the dominant kernel, the recurrence: after the
 timed steps, K more launches of the recurrence alone (rnn_rec_lstm on the
@@ -227,8 +229,8 @@ def cpu_baseline(w: synth.Workload, c, budget_s: float):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(synth.WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-clock", action="store_true",
@@ -385,13 +387,19 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
+    # the timed steps back to back, nothing else on the stream between them
     t0 = time.perf_counter()
+    for k in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # then as many steps again with events around each phase, for the
+    # per-phase figures (the events themselves take a few microseconds of
+    # stream time per step, which is why the timed loop above has none)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     for k in range(args.steps):
         step(evs[k])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
     step_ms = [e[0].elapsed_time(e[2 if backward else 1]) for e in evs]
     for wsx in (ws_f,) + ((ws_b,) if backward else ()):
