@@ -13,10 +13,10 @@ K steps back to back with nothing else on the stream between them.  K more
 steps with HIP events around each phase then give the per-phase figures.
 
 The roofline entry is for the dominant kernel, the recurrence: after the
-timed steps, K more launches of the recurrence alone (rnn_rec_lstm on the
-projection's output) are bracketed one by one with HIP events on the stream
-they run on, and its average launch duration gives `achieved`.  The input
-projection alone is timed the same way.
+timed steps, min(K, 20) more launches of the recurrence alone (rnn_rec_lstm
+on the projection's output) are bracketed one by one with HIP events on the
+stream they run on, and its average launch duration gives `achieved`.  The
+input projection alone is timed the same way.
 
 Prints ONE JSON line (see the keys below).
 
@@ -48,6 +48,8 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
 NUM_CU = 256
 CU_BF16_TFLOPS = PEAK_BF16_TFLOPS / NUM_CU
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+# launches of the recurrence alone and of the projection alone, each timed
+KERNEL_LAUNCHES = 20
 KERNEL_SOURCES = [os.path.join(ROOT, "gru_recurrence_amd", "csrc", f)
                   for f in ("rec_fwd.hip", "gates.h", "common.h")]
 KERNEL_ARGS_HEADER = os.path.join(ROOT, "gru_recurrence_amd", "csrc", "kernels.h")
@@ -427,8 +429,11 @@ def main():
 
     proj()
     rec()
-    proj_avg, proj_med, proj_min = timed(proj, args.steps)
-    rec_avg, rec_med, rec_min = timed(rec, args.steps)
+    # each kernel alone: a fixed count of launches (a long run of the
+    # projection alone at 1.3-1.4 kW lowers the clock it runs at)
+    nk = min(args.steps, KERNEL_LAUNCHES)
+    proj_avg, proj_med, proj_min = timed(proj, nk)
+    rec_avg, rec_med, rec_min = timed(rec, nk)
     clock = None if args.no_clock else gfx_clock_under_load(step, torch)
     st = g.workspace_status(ws, stream)
     if st != g.RNN_OK:
