@@ -133,6 +133,30 @@ rnn_status rnn_plan_describe(rnn_op op, const rnn_dims *d, rnn_dtype dt, char *b
     if (!dims_ok(d) || !dtype_ok(dt) || !buf || len == 0) return RNN_ERR_INVALID_ARG;
     if (op < RNN_OP_FWD_LSTM || op > RNN_OP_REC_GRU) return RNN_ERR_INVALID_ARG;
     const int cell = cell_of_op(op);
+    if (op == RNN_OP_BWD_LSTM || op == RNN_OP_BWD_GRU) {
+        if (dt == RNN_F32) {
+            const BwdF32Plan p = plan_bwd_f32(cell, d->B, d->Dh);
+            if (!p.ok) {
+                snprintf(buf, len, "bwd_sweep=none");
+                return RNN_ERR_UNSUPPORTED;
+            }
+            snprintf(buf, len, "bwd_sweep=f32_lds rows_per_wg=%d wg=%d chunks=1", p.BT,
+                     p.nbt * d->NH);
+            return RNN_OK;
+        }
+        const BwdChoice b = choose_bwd(cell, d, device_cus());
+        if (!b.ok) {
+            snprintf(buf, len, "bwd_sweep=none");
+            return RNN_ERR_UNSUPPORTED;
+        }
+        snprintf(buf, len,
+                 "bwd_sweep=%s rows_per_wg=%d wg=%d wg_per_head_row_tile=%d chunks=%d "
+                 "free_cus=%d",
+                 b.two ? "split_R_two_cu" : b.pw.ok ? "split_R" : "exchange",
+                 b.pw.ok ? 1 : b.p.BT, b.sweep_grid, b.two ? 2 : b.pw.ok ? 1 : b.p.K, b.chunks,
+                 b.free_cus);
+        return RNN_OK;
+    }
     const Choice ch = choose(cell, d, dt, device_cus());
     if (!ch.ok) {
         snprintf(buf, len, "rec_kernel=none");

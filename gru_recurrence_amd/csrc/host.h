@@ -344,6 +344,18 @@ rnn_status forward_stack(int cell, const rnn_dims *d, int L, rnn_dtype dt, const
                          float *hT, float *cT, void *ws, hipStream_t s);
 
 // host_bwd.hip
+// The bf16 backward's sweep: the split-R plan (Dh = 256; on two CUs per
+// (head, row) where the pairs fit the XCD grouping) or the exchange-based
+// plan, its grid, the CUs it leaves free, and the time chunks it runs in
+// (1: one piece).  ok == false where no sweep fits.  Pure host function.
+struct BwdChoice {
+    WidePlan pw;
+    BwdPlan p;
+    bool two;
+    int sweep_grid, free_cus, chunks;
+    bool ok;
+};
+BwdChoice choose_bwd(int cell, const rnn_dims *d, int cus);
 rnn_status backward_f32(int cell, const rnn_dims *d, const float *x, const float *W,
                         const float *R, const float *b, const float *h0, const float *c0,
                         const float *h_seq, const float *c_seq, const float *dh_seq,

@@ -117,6 +117,24 @@ int bwd_chunk_starts(int T, int *starts) {
     return n;
 }
 
+BwdChoice choose_bwd(int cell, const rnn_dims *d, int cus) {
+    BwdChoice c{};
+    const int B = d->B, NH = d->NH, Dh = d->Dh;
+    c.pw = wide_enabled() ? plan_wide(cell, B, NH, Dh, true) : WidePlan{};
+    c.p = c.pw.ok ? BwdPlan{} : plan_bwd(cell, B, NH, Dh, cus, bt_override(), k_override());
+    c.ok = c.pw.ok || c.p.ok;
+    if (!c.ok) return c;
+    c.two = c.pw.ok && env_int_or("RNN355_BWD_WIDE2", 1) != 0 && mc_xcd_enabled() &&
+            mc_xcd_grouping(NH * B, 2 * NH * B) && 2 * NH * B <= cus;
+    c.sweep_grid = c.two ? 2 * NH * B : c.pw.ok ? c.pw.grid : c.p.grid;
+    c.free_cus = (cus - c.sweep_grid) / 8 * 8;
+    int starts[kBwdChunks + 1];
+    c.chunks = c.free_cus >= 64 && env_int_or("RNN355_BWD_OVERLAP", 1) != 0
+                   ? bwd_chunk_starts(d->T, starts)
+                   : 1;
+    return c;
+}
+
 rnn_status backward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, const void *W,
                     const void *R, const float *b, const float *h0, const float *c0,
                     const float *h_seq, const float *c_seq, const float *dh_seq,
@@ -133,11 +151,13 @@ rnn_status backward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, co
     const int GD = G * Dh, N = NH * GD, H = NH * Dh, M = T * B;
     if (!gemm_shape_ok(Din, N, dt) || Dh % 16 != 0) return RNN_ERR_UNSUPPORTED;
     // Dh = 256: one workgroup per (head, batch row) with R split over
-    // registers and LDS; otherwise the exchange-based sweep
-    const WidePlan pw = wide_enabled() ? plan_wide(cell, B, NH, Dh, true) : WidePlan{};
-    const BwdPlan p = pw.ok ? BwdPlan{} : plan_bwd(cell, B, NH, Dh, device_cus(), bt_override(),
-                                                   k_override());
-    if (!pw.ok && !p.ok) return RNN_ERR_UNSUPPORTED;
+    // registers and LDS (or two CUs per (head, row)); otherwise the
+    // exchange-based sweep
+    const int cus = device_cus();
+    const BwdChoice bc = choose_bwd(cell, d, cus);
+    if (!bc.ok) return RNN_ERR_UNSUPPORTED;
+    const WidePlan &pw = bc.pw;
+    const BwdPlan &p = bc.p;
     const int nbt = pw.ok ? B : p.nbt;  // rows of db partials
     const rnn_op op = lstm ? RNN_OP_BWD_LSTM : RNN_OP_BWD_GRU;
     if (!ws || ws_bytes < rnn_workspace_size(op, d, dt)) return RNN_ERR_WORKSPACE;
@@ -204,15 +224,10 @@ rnn_status backward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, co
     // dR and db on the caller's stream.  dW, dR and db
     // add the chunks' shares in sweep order (deterministic, not the one-piece
     // summation order).  RNN355_BWD_OVERLAP=0 keeps the sweep in one piece.
-    const bool two = pw.ok && env_int_or("RNN355_BWD_WIDE2", 1) != 0 && mc_xcd_enabled() &&
-                     mc_xcd_grouping(NH * B, 2 * NH * B) && 2 * NH * B <= device_cus();
-    const int cus = device_cus();
-    const int sweep_grid = two ? 2 * NH * B : pw.ok ? pw.grid : p.grid;
-    const int free_cus = (cus - sweep_grid) / 8 * 8;
+    const bool two = bc.two;
+    const int free_cus = bc.free_cus;
     int starts[kBwdChunks + 1];
-    const int nch = free_cus >= 64 && env_int_or("RNN355_BWD_OVERLAP", 1) != 0
-                        ? bwd_chunk_starts(T, starts)
-                        : 1;
+    const int nch = bc.chunks > 1 ? bwd_chunk_starts(T, starts) : 1;
     // dx on one stream, dW, dR and db on the other, each on half the free units
     hipStream_t side = nch > 1 ? side_stream(0) : nullptr, side2 = nch > 1 ? side_stream(1) : nullptr;
     CallEvents ev;

@@ -108,8 +108,11 @@ const char *rnn_status_str(rnn_status s);
 size_t rnn_workspace_size(rnn_op op, const rnn_dims *d, rnn_dtype dt);
 
 /* Write a one-line description of the kernel plan `op` would use (kernel,
- * rows per workgroup, workgroups, workgroups per head) into buf.  Pure host
- * function apart from reading the device's compute-unit count once. */
+ * rows per workgroup, workgroups, workgroups per head; for the forward
+ * whether the projection runs fused with the recurrence; for the backward
+ * the reverse sweep's kernel, the compute units it leaves free and the time
+ * chunks it runs in) into buf.  Pure host function apart from reading the
+ * device's compute-unit count once. */
 rnn_status rnn_plan_describe(rnn_op op, const rnn_dims *d, rnn_dtype dt,
                              char *buf, size_t len);
 

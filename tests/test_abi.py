@@ -227,6 +227,40 @@ def test_plans_of_the_workloads(monkeypatch):
     assert " wg=256 " in p and "input_proj=serial" in p
 
 
+def test_backward_plans(monkeypatch):
+    """The backward's sweep and its time chunks are host decisions too:
+    two CUs per (head, row) at Dh = 256 where the pairs fit the XCD
+    grouping, four chunks at T = 1024 and two at T = 256 (chunks of at
+    least 128 steps) where the sweep leaves at least 64 CUs free, one piece
+    with RNN355_BWD_OVERLAP=0, for short sequences and in float32."""
+    for k in ("RNN355_BWD_OVERLAP", "RNN355_BWD_CHUNKS", "RNN355_BWD_WIDE2", "RNN355_REC_WIDE",
+              "RNN355_MC_XCD", "RNN355_REC_BT", "RNN355_REC_K"):
+        monkeypatch.delenv(k, raising=False)
+    if g.plan_describe(g.OP_REC_LSTM, g.Dims(8, 16, 8, 6, 128), g.RNN_BF16).find(" wg=96 ") < 0:
+        pytest.skip("a device with other than 256 compute units is visible")
+    c5 = g.Dims(1024, 16, 1024, 4, 256)
+    p = g.plan_describe(g.OP_BWD_LSTM, c5, g.RNN_BF16)
+    assert "bwd_sweep=split_R_two_cu" in p and " wg=128 " in p and " chunks=4 " in p, p
+    assert "free_cus=128" in p
+    assert " chunks=2 " in g.plan_describe(g.OP_BWD_LSTM, g.Dims(256, 16, 1024, 4, 256),
+                                           g.RNN_BF16)
+    assert " chunks=1 " in g.plan_describe(g.OP_BWD_LSTM, g.Dims(255, 16, 1024, 4, 256),
+                                           g.RNN_BF16)
+    p = g.plan_describe(g.OP_BWD_GRU, g.Dims(600, 5, 96, 2, 64), g.RNN_BF16)
+    assert "bwd_sweep=exchange" in p and " chunks=4 " in p, p
+    monkeypatch.setenv("RNN355_BWD_CHUNKS", "3")
+    assert " chunks=3 " in g.plan_describe(g.OP_BWD_LSTM, c5, g.RNN_BF16)
+    monkeypatch.setenv("RNN355_BWD_OVERLAP", "0")
+    assert " chunks=1 " in g.plan_describe(g.OP_BWD_LSTM, c5, g.RNN_BF16)
+    monkeypatch.delenv("RNN355_BWD_OVERLAP")
+    monkeypatch.delenv("RNN355_BWD_CHUNKS")
+    monkeypatch.setenv("RNN355_BWD_WIDE2", "0")
+    p = g.plan_describe(g.OP_BWD_LSTM, c5, g.RNN_BF16)
+    assert "bwd_sweep=split_R " in p and " wg=64 " in p and " chunks=4 " in p, p
+    p = g.plan_describe(g.OP_BWD_LSTM, g.Dims(64, 2, 32, 1, 32), g.RNN_F32)
+    assert "bwd_sweep=f32_lds" in p and "chunks=1" in p, p
+
+
 def test_stack_entry_points_reject_before_launch():
     lib = g.load()
     d = g.Dims(8, 2, 32, 1, 32)

@@ -151,8 +151,14 @@ def test_backward_chunked_sweep_matches_one_piece(cell, T, B, NH, Dh, Din, final
     c = synth.make_case(cell, d, "bf16", 9300 + T + Dh, bias="forget+1" if cell == "lstm" else "zero",
                         h0_var=0.2, c0_var=0.2, backward=True, final_grads=final)
     run = gpu_bwd if cell == "lstm" else gpu_bwd_gru
+    op = g.OP_BWD_LSTM if cell == "lstm" else g.OP_BWD_GRU
+    gd = g.Dims(T, B, Din, NH, Dh)
+    plan = g.plan_describe(op, gd, g.RNN_BF16)
+    print("  plan:", plan, flush=True)
+    assert " chunks=1 " not in plan
     chunked = run(c, final)
     os.environ["RNN355_BWD_OVERLAP"] = "0"
+    assert " chunks=1 " in g.plan_describe(op, gd, g.RNN_BF16)
     whole = run(c, final)
     for k in ("dx", "dh0") + (("dc0",) if cell == "lstm" else ()):
         assert np.array_equal(chunked[k], whole[k]), k
