@@ -302,11 +302,14 @@ inline hipStream_t side_stream(int i = 0) {
 }
 
 // Events of one call, destroyed when the call returns (the runtime keeps
-// a recorded event alive until its work is done).
+// a recorded event alive until its work is done); make = false: none
+// (a call that turns out to need no second stream), ok stays false.
 struct CallEvents {
     hipEvent_t e[kBwdChunks + 3] = {};
-    bool ok = true;
-    CallEvents() {
+    bool ok = false;
+    explicit CallEvents(bool make = true) {
+        if (!make) return;
+        ok = true;
         for (hipEvent_t &v : e)
             if (hipEventCreateWithFlags(&v, hipEventDisableTiming) != hipSuccess) ok = false;
     }

@@ -230,7 +230,7 @@ rnn_status backward(int cell, const rnn_dims *d, rnn_dtype dt, const void *x, co
     const int nch = bc.chunks > 1 ? bwd_chunk_starts(T, starts) : 1;
     // dx on one stream, dW, dR and db on the other, each on half the free units
     hipStream_t side = nch > 1 ? side_stream(0) : nullptr, side2 = nch > 1 ? side_stream(1) : nullptr;
-    CallEvents ev;
+    CallEvents ev(nch > 1);
     const bool split = nch > 1 && side && side2 && ev.ok;
     const int half = free_cus / 16 * 8;
     if (!split) {
