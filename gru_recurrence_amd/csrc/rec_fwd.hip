@@ -925,12 +925,19 @@ __global__ __launch_bounds__(256) void rec_fwd_simple_kernel(RecArgs a) {
 // One batch row: the gate-row layout.  Two to eight rows: rows in lane
 // groups, one cell update pass per four rows (upt passes).  More: the
 // register-slot layout, four passes (the same count, with fewer live
-// registers).  Each with its prefetch group length (steps).
+// registers).  Each with its prefetch group length (steps).  One row with
+// nothing to wait on, LSTM with Dh=128: groups of two steps (groups of eight
+// cost about 4% more time per step, four or six about 2-3%); GRU with Dh=64
+// was 7% slower with two, so other shapes keep eight.  The launches that run
+// beside the projection or another layer and wait on its ready words keep
+// groups of eight too: with two, the fused forward took about 4% longer, the
+// stacked one about a third longer.
 template <int CELL, int DH, bool WAIT>
 void launch_mfma_rows_w(const RecPlan &p, const RecArgs &a, hipStream_t s) {
     const dim3 grid(p.grid), blk(DH / 16 * 64);
     if (p.BT == 1) {
-        hipLaunchKernelGGL((rec_fwd_mfma_kernel<CELL, DH, 1, 8, WAIT, false>), grid, blk, 0, s, a);
+        constexpr int PD1 = (CELL == kLSTM && DH == 128 && !WAIT) ? 2 : 8;
+        hipLaunchKernelGGL((rec_fwd_mfma_kernel<CELL, DH, 1, PD1, WAIT, false>), grid, blk, 0, s, a);
         return;
     }
     switch (p.upt) {
