@@ -928,10 +928,11 @@ __global__ __launch_bounds__(256) void rec_fwd_simple_kernel(RecArgs a) {
 // registers).  Each with its prefetch group length (steps).  One row with
 // nothing to wait on, LSTM with Dh=128: groups of two steps (groups of eight
 // cost about 4% more time per step, four or six about 2-3%); GRU with Dh=64
-// was 7% slower with two, so other shapes keep eight.  The launches that run
-// beside the projection or another layer and wait on its ready words keep
-// groups of eight too: with two, the fused forward took about 4% longer, the
-// stacked one about a third longer.
+// was 7% slower with two, so other shapes keep eight.  Launched beside the
+// projection and waiting on its ready words, the LSTM with Dh=128 takes
+// groups of six (per call: eight 0.539 ms, four 0.533, six 0.525, two 0.562);
+// the GRU with Dh=64 keeps eight there (four and six 2-5% slower), and so
+// does the stacked launch (per call: six 3% slower, four 11%, two a third).
 template <int CELL, int DH, bool WAIT>
 void launch_mfma_rows_w(const RecPlan &p, const RecArgs &a, hipStream_t s) {
     const dim3 grid(p.grid), blk(DH / 16 * 64);
@@ -1039,7 +1040,7 @@ template <int DH>
 hipError_t launch_fused_dh(int cell, const RecPlan &p, const RecArgs &a, const GemmArgs &g,
                            int n_gemm, int rows1, int n_gemm2, hipStream_t s) {
     if (p.BT == 1)
-        return cell == kLSTM ? launch_fused_t<kLSTM, DH, 1, 8, false>(p, a, g, n_gemm, rows1, n_gemm2, s)
+        return cell == kLSTM ? launch_fused_t<kLSTM, DH, 1, (DH == 128 ? 6 : 8), false>(p, a, g, n_gemm, rows1, n_gemm2, s)
                              : launch_fused_t<kGRU, DH, 1, 8, false>(p, a, g, n_gemm, rows1, n_gemm2, s);
     switch (p.upt) {
         case 1: return cell == kLSTM ? launch_fused_t<kLSTM, DH, 1, 4, true>(p, a, g, n_gemm, rows1, n_gemm2, s)
