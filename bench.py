@@ -89,7 +89,7 @@ def rec_kernel_name(w: synth.Workload, plan: str) -> str:
     passes = int(plan.split("units_per_thread=")[1].split()[0])
     rows = int(plan.split("rows_per_wg=")[1].split()[0])
     lanes = 1 < rows <= 8
-    one = 2 if (w.cell == "lstm" and w.dims.Dh == 128) else 8
+    one = {("lstm", 128): 2, ("gru", 64): 16}.get((w.cell, w.dims.Dh), 8)
     pd = {1: one if rows == 1 else 4, 2: 2, 4: 2}[passes]
     return "rec_fwd_mfma_kernel<%d, %d, %d, %d, false, %s>" % (
         0 if w.cell == "lstm" else 1, w.dims.Dh, passes, pd, "true" if lanes else "false")

@@ -927,17 +927,23 @@ __global__ __launch_bounds__(256) void rec_fwd_simple_kernel(RecArgs a) {
 // register-slot layout, four passes (the same count, with fewer live
 // registers).  Each with its prefetch group length (steps).  One row with
 // nothing to wait on, LSTM with Dh=128: groups of two steps (groups of eight
-// cost about 4% more time per step, four or six about 2-3%); GRU with Dh=64
-// was 7% slower with two, so other shapes keep eight.  Launched beside the
-// projection and waiting on its ready words, the LSTM with Dh=128 takes
-// groups of six (per call: eight 0.539 ms, four 0.533, six 0.525, two 0.562);
-// the GRU with Dh=64 keeps eight there (four and six 2-5% slower), and so
-// does the stacked launch (per call: six 3% slower, four 11%, two a third).
+// cost about 4% more time per step, four or six about 2-3%); GRU with Dh=64:
+// groups of sixteen (eight and twelve 0.7% slower, twenty 1.4%, two 7%).
+// Other shapes keep eight (longer groups hold more registers; not measured).
+// Launched beside the projection and waiting on its ready words, the LSTM
+// with Dh=128 takes groups of six (per call: eight 0.539 ms, four 0.533, six
+// 0.525, two 0.562) and the GRU with Dh=64 sixteen (eight 0.549, twelve
+// 0.542, sixteen 0.538, twenty 0.537, four and six 2-5% slower than eight);
+// the stacked launch keeps eight (per call: six 3% slower, four 11%, two a
+// third, ten and twelve no faster).
 template <int CELL, int DH, bool WAIT>
 void launch_mfma_rows_w(const RecPlan &p, const RecArgs &a, hipStream_t s) {
     const dim3 grid(p.grid), blk(DH / 16 * 64);
     if (p.BT == 1) {
-        constexpr int PD1 = (CELL == kLSTM && DH == 128 && !WAIT) ? 2 : 8;
+        constexpr int PD1 = WAIT                           ? 8
+                            : (CELL == kLSTM && DH == 128) ? 2
+                            : (CELL == kGRU && DH == 64)   ? 16
+                                                           : 8;
         hipLaunchKernelGGL((rec_fwd_mfma_kernel<CELL, DH, 1, PD1, WAIT, false>), grid, blk, 0, s, a);
         return;
     }
@@ -1041,7 +1047,7 @@ hipError_t launch_fused_dh(int cell, const RecPlan &p, const RecArgs &a, const G
                            int n_gemm, int rows1, int n_gemm2, hipStream_t s) {
     if (p.BT == 1)
         return cell == kLSTM ? launch_fused_t<kLSTM, DH, 1, (DH == 128 ? 6 : 8), false>(p, a, g, n_gemm, rows1, n_gemm2, s)
-                             : launch_fused_t<kGRU, DH, 1, 8, false>(p, a, g, n_gemm, rows1, n_gemm2, s);
+                             : launch_fused_t<kGRU, DH, 1, (DH == 64 ? 16 : 8), false>(p, a, g, n_gemm, rows1, n_gemm2, s);
     switch (p.upt) {
         case 1: return cell == kLSTM ? launch_fused_t<kLSTM, DH, 1, 4, true>(p, a, g, n_gemm, rows1, n_gemm2, s)
                                      : launch_fused_t<kGRU, DH, 1, 4, true>(p, a, g, n_gemm, rows1, n_gemm2, s);
