@@ -816,13 +816,13 @@ __global__ __launch_bounds__(512) void fwd_fused_kernel(RecArgs a, GemmArgs g, i
 // every workgroup of layer l (y.done_target), then the tile's barrier releases
 // the other waves.  A's loads are device-scope (they miss in the XCD's L2,
 // like the stores that wrote them); the weights load as usual.
-template <int CELL, int PD, bool HB1>
+template <int CELL, int PD0, int PD, bool HB1>
 __global__ __launch_bounds__(512) void fwd_stack2_kernel(RecArgs a0, RecArgs a1, GemmArgs g,
                                                          StackSync y) {
     extern __shared__ __attribute__((aligned(16))) char stack_lds[];
     const int blk = blockIdx.x;
     if (blk < y.rec_grid) {
-        rec_fwd_mfma_body<CELL, 128, 1, PD, false, true>(a0, blk, y.h_bf0, y.done);
+        rec_fwd_mfma_body<CELL, 128, 1, PD0, false, true>(a0, blk, y.h_bf0, y.done);
         return;
     }
     const int gb = blk - y.rec_grid;
@@ -934,8 +934,9 @@ __global__ __launch_bounds__(256) void rec_fwd_simple_kernel(RecArgs a) {
 // with Dh=128 takes groups of six (per call: eight 0.539 ms, four 0.533, six
 // 0.525, two 0.562) and the GRU with Dh=64 sixteen (eight 0.549, twelve
 // 0.542, sixteen 0.538, twenty 0.537, four and six 2-5% slower than eight);
-// the stacked launch keeps eight (per call: six 3% slower, four 11%, two a
-// third, ten and twelve no faster).
+// in the stacked launch, layer 0 (no waits, but a count published per group)
+// takes twelve and layer 1 eight (per call 0.747 ms; layer 0 at eight 0.753,
+// sixteen 0.756, six 0.775, two 1.03).
 template <int CELL, int DH, bool WAIT>
 void launch_mfma_rows_w(const RecPlan &p, const RecArgs &a, hipStream_t s) {
     const dim3 grid(p.grid), blk(DH / 16 * 64);
@@ -1075,11 +1076,11 @@ hipError_t launch_stack2_t(const RecArgs &a0, const RecArgs &a1, const GemmArgs 
     static std::once_flag once;
     static hipError_t attr = hipSuccess;
     std::call_once(once, [] {
-        attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&fwd_stack2_kernel<CELL, 8, HB1>),
+        attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&fwd_stack2_kernel<CELL, 12, 8, HB1>),
                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)dma::LDS_BYTES);
     });
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((fwd_stack2_kernel<CELL, 8, HB1>), dim3(2 * y.rec_grid + y.n_gemm),
+    hipLaunchKernelGGL((fwd_stack2_kernel<CELL, 12, 8, HB1>), dim3(2 * y.rec_grid + y.n_gemm),
                        dim3(512), dma::LDS_BYTES, s, a0, a1, g, y);
     return hipGetLastError();
 }
